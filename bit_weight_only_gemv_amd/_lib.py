@@ -1,0 +1,220 @@
+"""ctypes binding of ``libwq.so`` (include/wq.h).  Argument marshalling only:
+every step of the computation runs in the library.
+
+Host entry points take numpy arrays; device entry points take torch tensors
+that live on the GPU (torch is used only for device memory and streams) and
+enqueue on ``torch.cuda.current_stream()`` unless a stream is given.
+
+Importing torch before loading the library matters: torch ships its own HIP
+runtime under the same soname, and loading it first makes the library bind
+to that one runtime instead of a second copy.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libwq.so")
+
+WQ_OK = 0
+WQ_ERR_INVALID_ARG = -1
+WQ_ERR_UNSUPPORTED = -2
+WQ_ERR_HIP = -3
+WQ_FMT_W4 = 4
+WQ_FMT_W2 = 2
+WQ_FUSE_OUTLIERS = 1
+WQ_GROUP = 32
+WQ_MAX_K = 65536
+WQ_GEMM_MAX_M = 16
+
+# Every symbol include/wq.h declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_U32 = ctypes.c_uint32
+_INT = ctypes.c_int
+SIGNATURES = {
+    "wq_status_str": (ctypes.c_char_p, [_INT]),
+    "wq_last_error": (ctypes.c_char_p, []),
+    "wq_version": (ctypes.c_char_p, []),
+    "wq_quantize_w4": (_INT, [_P, _I64, _I64, _I32, _P, _P, _P]),
+    "wq_quantize_w2": (_INT, [_P, _I64, _I64, _I32, _P, _P, _P]),
+    "wq_select_outliers": (_INT, [_P, _I64, _I64, _P, ctypes.c_double, _P, _I64, _P]),
+    "wq_split_outliers": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P]),
+    "wq_dequant_host": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P]),
+    "wq_dequant_device": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _P]),
+    "wq_gemv_w4": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _P, _P]),
+    "wq_gemv_w2": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _P, _P]),
+    "wq_gemm_wq": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _I64, _P, _P]),
+    "wq_outlier_add": (_INT, [_P, _P, _I64, _I64, _P, _I64, _I64, _P, _P]),
+    "wq_read_probe": (_INT, [_P, _I64, _P, _P]),
+    "wq_read_probe_sink_words": (_I64, [_I64]),
+    "wq_copy_probe": (_INT, [_P, _P, _I64, _P]),
+}
+
+
+class WQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [{status}]")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads the library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m bit_weight_only_gemv_amd.build` "
+            "(there is no fallback implementation)")
+    import torch  # noqa: F401  (see module docstring)
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != WQ_OK:
+        raise WQError(status, load().wq_last_error().decode())
+
+
+def _np_ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+# ------------------------------------------------------------------ host
+
+
+def wq_quantize_w4(W: np.ndarray):
+    """W float32 [N, K] -> (codes uint8 [N, K/2], scales fp16 [N, K/32], zeros fp16 [N, K/32])."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    codes = np.empty((N, K // 2), np.uint8)
+    sc = np.empty((N, K // WQ_GROUP), np.uint16)
+    ze = np.empty((N, K // WQ_GROUP), np.uint16)
+    _check(load().wq_quantize_w4(_np_ptr(W), N, K, WQ_GROUP, _np_ptr(codes), _np_ptr(sc), _np_ptr(ze)))
+    return codes, sc.view(np.float16), ze.view(np.float16)
+
+
+def wq_quantize_w2(W: np.ndarray):
+    """W float32 [N, K] -> (codes uint8 [N, K/4], scales fp16 [N, K/32], zeros fp16 [N, K/32])."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    codes = np.empty((N, K // 4), np.uint8)
+    sc = np.empty((N, K // WQ_GROUP), np.uint16)
+    ze = np.empty((N, K // WQ_GROUP), np.uint16)
+    _check(load().wq_quantize_w2(_np_ptr(W), N, K, WQ_GROUP, _np_ptr(codes), _np_ptr(sc), _np_ptr(ze)))
+    return codes, sc.view(np.float16), ze.view(np.float16)
+
+
+def wq_select_outliers(W: np.ndarray, profile: np.ndarray, ratio: float) -> np.ndarray:
+    W = _c(W, np.float32)
+    N, K = W.shape
+    prof = _c(profile, np.float64)
+    cap = max(1, int(np.floor(ratio * K)) + 1)
+    idx = np.empty(cap, np.int32)
+    n = ctypes.c_int64(0)
+    _check(load().wq_select_outliers(_np_ptr(W), N, K, _np_ptr(prof), float(ratio), _np_ptr(idx),
+                                     cap, ctypes.byref(n)))
+    return idx[: n.value].copy()
+
+
+def wq_split_outliers(W: np.ndarray, idx: np.ndarray):
+    W = _c(W, np.float32)
+    N, K = W.shape
+    idx = _c(idx, np.int32)
+    dense = np.empty_like(W)
+    wout = np.empty((N, len(idx)), np.uint16)
+    _check(load().wq_split_outliers(_np_ptr(W), N, K, _np_ptr(idx), len(idx), _np_ptr(dense),
+                                    _np_ptr(wout)))
+    return dense, wout.view(np.float16)
+
+
+def wq_dequant_host(fmt: int, codes, scales, zeros, N: int, K: int) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    sc = _c(np.asarray(scales).view(np.uint16), np.uint16)
+    ze = _c(np.asarray(zeros).view(np.uint16), np.uint16)
+    out = np.empty((N, K), np.uint16)
+    _check(load().wq_dequant_host(fmt, _np_ptr(codes), _np_ptr(sc), _np_ptr(ze), N, K, _np_ptr(out)))
+    return out.view(np.float16)
+
+
+# ---------------------------------------------------------------- device
+
+
+def _dptr(t) -> int:
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("device arguments must be contiguous GPU tensors")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def wq_dequant_device(fmt, codes, scales, zeros, N, K, W_hat, stream=None):
+    _check(load().wq_dequant_device(fmt, _dptr(codes), _dptr(scales), _dptr(zeros), N, K,
+                                    _dptr(W_hat), _stream(stream)))
+
+
+def _gemv(fn, codes, scales, zeros, N, K, x, y, out_idx, out_w, n_out, flags, stream):
+    _check(fn(_dptr(codes), _dptr(scales), _dptr(zeros), N, K,
+              _dptr(out_idx) if n_out else None, _dptr(out_w) if n_out else None, n_out, flags,
+              _dptr(x), _dptr(y), _stream(stream)))
+
+
+def wq_gemv_w4(codes, scales, zeros, N, K, x, y, out_idx=None, out_w=None, n_out=0,
+               flags=WQ_FUSE_OUTLIERS, stream=None):
+    _gemv(load().wq_gemv_w4, codes, scales, zeros, N, K, x, y, out_idx, out_w, n_out, flags, stream)
+
+
+def wq_gemv_w2(codes, scales, zeros, N, K, x, y, out_idx=None, out_w=None, n_out=0,
+               flags=WQ_FUSE_OUTLIERS, stream=None):
+    _gemv(load().wq_gemv_w2, codes, scales, zeros, N, K, x, y, out_idx, out_w, n_out, flags, stream)
+
+
+def wq_gemm_wq(fmt, codes, scales, zeros, N, K, X, M, Y, out_idx=None, out_w=None, n_out=0,
+               flags=WQ_FUSE_OUTLIERS, stream=None):
+    _check(load().wq_gemm_wq(fmt, _dptr(codes), _dptr(scales), _dptr(zeros), N, K,
+                             _dptr(out_idx) if n_out else None, _dptr(out_w) if n_out else None,
+                             n_out, flags, _dptr(X), M, _dptr(Y), _stream(stream)))
+
+
+def wq_outlier_add(idx, out_w, n_out, N, X, M, K, Y, stream=None):
+    _check(load().wq_outlier_add(_dptr(idx) if n_out else None, _dptr(out_w) if n_out else None,
+                                 n_out, N, _dptr(X), M, K, _dptr(Y), _stream(stream)))
+
+
+def wq_read_probe_sink_words(nbytes: int) -> int:
+    return int(load().wq_read_probe_sink_words(nbytes))
+
+
+def wq_read_probe(src, nbytes, sink, stream=None):
+    _check(load().wq_read_probe(_dptr(src), nbytes, _dptr(sink), _stream(stream)))
+
+
+def wq_copy_probe(src, dst, nbytes, stream=None):
+    _check(load().wq_copy_probe(_dptr(src), _dptr(dst), nbytes, _stream(stream)))

@@ -1,0 +1,213 @@
+// Device dequantization (bit-identical to the host encoder's dequant), the
+// standalone outlier correction, and measurement probes for gfx950.
+
+#include "wq_common.cuh"
+#include "wq_device.h"
+
+namespace wqd {
+
+// ------------------------------------------------------------ dequantize
+// One thread per (row, group).  W4: w_hat = FP16((q - z) s); the decoder's
+// FP16 value 1024 + q (or 1024 + 16 q) minus 1024 + z (or 1024 + 16 z) is the
+// exact integer q - z (or 16 (q - z)), and float32 (q - z) * s is exact, so a
+// single rounding to FP16 remains.  W2: w_hat = FP16(float32(S C[q] + Z)); the
+// product S C[q] of two FP16 values is exact in float32, so the fused
+// multiply-add rounds exactly once, like a multiply followed by an add.
+template <int FMT>
+__global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ codes,
+                                                      const uint16_t* __restrict__ scales,
+                                                      const uint16_t* __restrict__ zeros, int64_t N,
+                                                      int64_t K, uint16_t* __restrict__ out) {
+  const int64_t G = K / kGroup;
+  const int64_t items = N * G;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items;
+       it += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = it / G, g = it % G;
+    const float s = h2f(scales[it]);
+    const float z = h2f(zeros[it]);
+    uint16_t w[32];
+    if constexpr (FMT == 4) {
+      const u4v c = *reinterpret_cast<const u4v*>(codes + n * (K / 2) + g * 16);
+      const uint32_t wv[4] = {c.x, c.y, c.z, c.w};
+      const float zlo = 1024.0f + z, zhi = 1024.0f + 16.0f * z;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t lo0, hi0, lo1, hi1;
+        w4_word_magic(wv[j], lo0, hi0, lo1, hi1);
+        const h2 a = as_h2(lo0), b = as_h2(hi0), c2 = as_h2(lo1), d = as_h2(hi1);
+        w[4 * j + 0] = f2h(((float)a[0] - zlo) * s);
+        w[4 * j + 2] = f2h(((float)a[1] - zlo) * s);
+        w[4 * j + 16] = f2h(((float)b[0] - zhi) * 0.0625f * s);
+        w[4 * j + 18] = f2h(((float)b[1] - zhi) * 0.0625f * s);
+        w[4 * j + 1] = f2h(((float)c2[0] - zlo) * s);
+        w[4 * j + 3] = f2h(((float)c2[1] - zlo) * s);
+        w[4 * j + 17] = f2h(((float)d[0] - zhi) * 0.0625f * s);
+        w[4 * j + 19] = f2h(((float)d[1] - zhi) * 0.0625f * s);
+      }
+    } else {
+      const u2 c = *reinterpret_cast<const u2*>(codes + n * (K / 4) + g * 8);
+      const uint32_t wv[2] = {c.x, c.y};
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const h2 cp = as_h2(w2_centroid_pair((wv[j] >> (2 * p + 8 * h)) & 0x00030003u));
+            const int k = 16 * j + 4 * h + p;
+            w[k] = f2h(__builtin_fmaf(s, (float)cp[0], z));
+            w[k + 8] = f2h(__builtin_fmaf(s, (float)cp[1], z));
+          }
+    }
+    u4v* dst = reinterpret_cast<u4v*>(out + n * K + g * 32);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      u4v t;
+      t.x = pack2(w[8 * v + 0], w[8 * v + 1]);
+      t.y = pack2(w[8 * v + 2], w[8 * v + 3]);
+      t.z = pack2(w[8 * v + 4], w[8 * v + 5]);
+      t.w = pack2(w[8 * v + 6], w[8 * v + 7]);
+      dst[v] = t;
+    }
+  }
+}
+
+// ----------------------------------------------------- outlier correction
+// One wave per output row n (grid-stride); lanes take outliers j, j+64, ...
+__global__ void __launch_bounds__(256) outlier_add_kernel(const int32_t* __restrict__ idx,
+                                                          const uint16_t* __restrict__ out_w,
+                                                          int n_out, int N,
+                                                          const uint16_t* __restrict__ X, int M,
+                                                          int K, uint16_t* __restrict__ Y) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int waves = blockDim.x >> 6;
+  for (int n = blockIdx.x * waves + wave; n < N; n += gridDim.x * waves) {
+    for (int m = 0; m < M; ++m) {
+      float acc = 0.f;
+      for (int j = lane; j < n_out; j += 64) {
+        const uint32_t c = (uint32_t)idx[j];
+        const float xv = c < (uint32_t)K ? h2f(X[(size_t)m * K + c]) : 0.f;
+        acc = __builtin_fmaf(h2f(out_w[(size_t)n * n_out + j]), xv, acc);
+      }
+      acc = row16_sum(acc);
+      acc += __shfl_xor(acc, 16);
+      acc += __shfl_xor(acc, 32);
+      if (lane == 0) {
+        uint16_t* yp = Y + (size_t)m * N + n;
+        *yp = f2h(h2f(*yp) + acc);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ probes
+constexpr int kProbeThreads = 256;
+constexpr int kProbeUnroll = 4;
+
+__host__ __device__ inline int64_t probe_blocks(int64_t bytes) {
+  const int64_t per_block = (int64_t)kProbeThreads * 16 * kProbeUnroll;
+  int64_t b = (bytes + per_block - 1) / per_block;
+  if (b > 8192) b = 8192;
+  if (b < 1) b = 1;
+  return b;
+}
+
+__global__ void __launch_bounds__(kProbeThreads) read_probe_kernel(const u4v* __restrict__ src,
+                                                                   int64_t n16,
+                                                                   uint32_t* __restrict__ sink) {
+  __shared__ uint32_t red[kProbeThreads / 64];
+  uint32_t acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + (kProbeUnroll - 1) * stride < n16; i += kProbeUnroll * stride) {
+    u4v v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u4v v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int w = 0; w < kProbeThreads / 64; ++w) r ^= red[w];
+    sink[blockIdx.x] = r;
+  }
+}
+
+__global__ void __launch_bounds__(kProbeThreads) copy_probe_kernel(const u4v* __restrict__ src,
+                                                                   u4v* __restrict__ dst,
+                                                                   int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    dst[i] = src[i];
+}
+
+}  // namespace wqd
+
+using namespace wqd;
+
+extern "C" int wq_dequant_device(int fmt, const uint8_t* codes, const uint16_t* scales,
+                                 const uint16_t* zeros, int64_t N, int64_t K, uint16_t* W_hat,
+                                 void* stream) {
+  const char* who = "wq_dequant_device";
+  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4 or WQ_FMT_W2", who);
+  if (int r = wq::check_shape(N, K, who)) return r;
+  if (!codes || !scales || !zeros || !W_hat) return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL", who);
+  if (!aligned16(codes) || !aligned16(W_hat))
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: device pointers must be 16-byte aligned", who);
+  const int64_t items = N * (K / kGroup);
+  int64_t blocks = (items + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipStream_t s = (hipStream_t)stream;
+  if (fmt == WQ_FMT_W4)
+    hipLaunchKernelGGL(dequant_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales,
+                       zeros, N, K, W_hat);
+  else
+    hipLaunchKernelGGL(dequant_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales,
+                       zeros, N, K, W_hat);
+  return check_launch(who);
+}
+
+extern "C" int wq_outlier_add(const int32_t* idx, const uint16_t* out_w, int64_t n_out, int64_t N,
+                              const uint16_t* X, int64_t M, int64_t K, uint16_t* Y, void* stream) {
+  const char* who = "wq_outlier_add";
+  if (int r = wq::check_shape(N, K, who)) return r;
+  if (int r = wq::check_outlier_args(idx, out_w, n_out, K, who)) return r;
+  if (M < 1 || M > (1 << 20)) return wq::fail(WQ_ERR_INVALID_ARG, "%s: bad M", who);
+  if (!X || !Y) return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (n_out == 0) return wq::ok();
+  int64_t blocks = (N + 3) / 4;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(outlier_add_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     idx, out_w, (int)n_out, (int)N, X, (int)M, (int)K, Y);
+  return check_launch(who);
+}
+
+extern "C" int64_t wq_read_probe_sink_words(int64_t bytes) { return probe_blocks(bytes); }
+
+extern "C" int wq_read_probe(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes <= 0 || bytes % 16)
+    return wq::fail(WQ_ERR_INVALID_ARG, "wq_read_probe: bytes must be a positive multiple of 16");
+  if (!aligned16(src)) return wq::fail(WQ_ERR_INVALID_ARG, "wq_read_probe: src not 16-byte aligned");
+  hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)probe_blocks(bytes)), dim3(kProbeThreads), 0,
+                     (hipStream_t)stream, (const u4v*)src, bytes / 16, sink);
+  return check_launch("wq_read_probe");
+}
+
+extern "C" int wq_copy_probe(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (!src || !dst || bytes <= 0 || bytes % 16)
+    return wq::fail(WQ_ERR_INVALID_ARG, "wq_copy_probe: bytes must be a positive multiple of 16");
+  if (!aligned16(src) || !aligned16(dst))
+    return wq::fail(WQ_ERR_INVALID_ARG, "wq_copy_probe: pointers not 16-byte aligned");
+  hipLaunchKernelGGL(copy_probe_kernel, dim3((unsigned)probe_blocks(bytes)), dim3(kProbeThreads), 0,
+                     (hipStream_t)stream, (const u4v*)src, (u4v*)dst, bytes / 16);
+  return check_launch("wq_copy_probe");
+}

@@ -1,0 +1,97 @@
+"""Packing a float32 weight matrix with the library's host encoder, and the
+packed arrays' home on the GPU.
+
+``pack_host`` is the offline path of the pages (OTF-LLM v4.0 quickstart:
+profile -> outlier selection -> split -> per-group quantization -> packing),
+entirely through ``libwq.so``'s host entry points.  ``DeviceLayer`` holds the
+same arrays in device memory and calls the device entry points on them.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+from . import _lib as L
+
+
+@dataclasses.dataclass
+class HostLayer:
+    fmt: int
+    N: int
+    K: int
+    codes: np.ndarray          # uint8 [N, K/2] (W4) or [N, K/4] (W2)
+    scales: np.ndarray         # float16 [N, K/32]
+    zeros: np.ndarray          # float16 [N, K/32]
+    idx: np.ndarray            # int32 [n_out], ascending
+    wout: np.ndarray           # float16 [N, n_out]
+
+    @property
+    def n_out(self) -> int:
+        return int(len(self.idx))
+
+
+def pack_host(fmt: int, W: np.ndarray, profile: Optional[np.ndarray] = None,
+              ratio: float = 0.0) -> HostLayer:
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    if profile is not None and ratio > 0:
+        idx = L.wq_select_outliers(W, profile, ratio)
+    else:
+        idx = np.zeros(0, np.int32)
+    if len(idx):
+        dense, wout = L.wq_split_outliers(W, idx)
+    else:
+        dense, wout = W, np.zeros((N, 0), np.float16)
+    if fmt == L.WQ_FMT_W4:
+        codes, sc, ze = L.wq_quantize_w4(dense)
+    elif fmt == L.WQ_FMT_W2:
+        codes, sc, ze = L.wq_quantize_w2(dense)
+    else:
+        raise ValueError("fmt must be 4 or 2")
+    return HostLayer(fmt, N, K, codes, sc, ze, idx, wout)
+
+
+class DeviceLayer:
+    """Packed arrays in device memory (torch tensors used as plain buffers)."""
+
+    def __init__(self, host: HostLayer, device="cuda"):
+        import torch
+        self.fmt, self.N, self.K, self.n_out = host.fmt, host.N, host.K, host.n_out
+
+        def up(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+
+        self.codes = up(host.codes, np.uint8)
+        self.scales = up(host.scales.view(np.int16), np.int16)
+        self.zeros = up(host.zeros.view(np.int16), np.int16)
+        if self.n_out:
+            self.idx = up(host.idx, np.int32)
+            self.wout = up(host.wout.view(np.int16), np.int16)
+        else:
+            self.idx = self.wout = None
+
+    def nbytes(self, M: int = 1) -> int:
+        """Algorithmic bytes of one product: codes, scales, zeros, outlier slab
+        and indices, X and Y."""
+        b = self.codes.numel() + 2 * self.scales.numel() + 2 * self.zeros.numel()
+        b += 2 * self.N * self.n_out + 4 * self.n_out
+        return b + 2 * M * self.K + 2 * M * self.N
+
+    def gemv(self, x, y, flags=L.WQ_FUSE_OUTLIERS, stream=None):
+        fn = L.wq_gemv_w4 if self.fmt == L.WQ_FMT_W4 else L.wq_gemv_w2
+        fn(self.codes, self.scales, self.zeros, self.N, self.K, x, y, self.idx, self.wout,
+           self.n_out, flags, stream)
+
+    def gemm(self, X, Y, flags=L.WQ_FUSE_OUTLIERS, stream=None):
+        L.wq_gemm_wq(self.fmt, self.codes, self.scales, self.zeros, self.N, self.K, X, X.shape[0],
+                     Y, self.idx, self.wout, self.n_out, flags, stream)
+
+    def outlier_add(self, X, Y, stream=None):
+        L.wq_outlier_add(self.idx, self.wout, self.n_out, self.N, X, X.shape[0], self.K, Y, stream)
+
+    def dequant(self, W_hat, stream=None):
+        L.wq_dequant_device(self.fmt, self.codes, self.scales, self.zeros, self.N, self.K, W_hat,
+                            stream)

@@ -1,0 +1,192 @@
+/*
+ * wq.h - C ABI of the MI355X (gfx950) group-wise low-bit weight-only GEMV library.
+ *
+ * Two weight formats, both grouped by 32 consecutive input channels (K):
+ *
+ *   W4: asymmetric uniform 4-bit grid, one FP16 scale s and one FP16 zero point
+ *       z (an integer 0..15 stored as FP16) per (row, group).  Reconstruction
+ *       w_hat = (q - z) * s.  Source: the SPECTRA page ("Compress Any LLM 3x in
+ *       One Click, Near-Lossless in Under 50 MB RAM"), section 3.4
+ *       "Microscaled Group-32 Quantization with Marlin-Interleaved Layout".
+ *   W2: 2-bit codes into the FP16 Lloyd-Max codebook C = {-1.52, -0.45, +0.45,
+ *       +1.52}, one FP16 scale S and zero Z per (row, group) fitted by ordinary
+ *       least squares.  Reconstruction w_hat = S * C[q] + Z.  Source: the
+ *       OTF-LLM v4.0 page (pypi otf-llm 4.0.0), sections 2, 3 and 5.
+ *
+ * In both formats a sorted set of n_out input channels (outlier columns) is kept
+ * exactly in FP16 and added in the same kernel launch (SPECTRA section 4.1,
+ * OTF-LLM "Architecture & Key Innovations": FP16 outliers plus quantized
+ * background).  The quantized background skips those columns.
+ *
+ * Layouts (row-major, N output rows, K input channels, G = K / 32 groups):
+ *   codes W4  uint8 [N][K/2]   byte 16g+k of row n = q[n][32g+k] | q[n][32g+16+k] << 4,
+ *                              k = 0..15 (in-group nibble interleave, SPECTRA 3.4)
+ *   codes W2  uint8 [N][K/4]   byte j of row n = q[4j] | q[4j+1]<<2 | q[4j+2]<<4 | q[4j+3]<<6
+ *                              (OTF-LLM section 5)
+ *   scales    uint16 (FP16 bits) [N][G]
+ *   zeros     uint16 (FP16 bits) [N][G]
+ *   out_idx   int32  [n_out], strictly increasing, each in [0, K)
+ *   out_w     uint16 (FP16 bits) [N][n_out]   out_w[n][j] = W[n][out_idx[j]]
+ *   x / X     uint16 (FP16 bits) [M][K];  y / Y  uint16 (FP16 bits) [M][N]
+ *
+ * Conventions
+ *   - Every function returns WQ_OK (0) or a negative WQ_ERR_* code; the message
+ *     of the last error on the calling thread is wq_last_error().  Nothing
+ *     aborts or throws across the ABI.
+ *   - The caller allocates and frees every buffer.  The library allocates no
+ *     device memory, keeps no workspace and no global state beyond its kernels.
+ *   - Device entry points take device pointers and a HIP stream (hipStream_t
+ *     passed as void*; NULL = the null stream).  They only enqueue work and never
+ *     synchronize; a launch failure is reported as WQ_ERR_HIP.  Host entry points
+ *     are synchronous and touch no GPU.
+ *   - Supported shapes: N >= 1, 32 <= K <= 65536, K % 32 == 0, group == 32
+ *     (any other group size is WQ_ERR_UNSUPPORTED), 0 <= n_out <= K.  Device
+ *     pointers must be 16-byte aligned.  A pointer may be NULL only when the
+ *     array it names is empty.
+ *   - Device results are bit-reproducible from run to run (no atomics).
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WQ_OK 0
+#define WQ_ERR_INVALID_ARG (-1)
+#define WQ_ERR_UNSUPPORTED (-2)
+#define WQ_ERR_HIP (-3)
+
+#define WQ_FMT_W4 4
+#define WQ_FMT_W2 2
+
+/* flags of the product entry points */
+#define WQ_FUSE_OUTLIERS 1u /* add the FP16 outlier columns inside the same launch */
+
+#define WQ_GROUP 32
+#define WQ_MAX_K 65536
+#define WQ_GEMM_MAX_M 16
+
+/* Text of a status code.  Never NULL. */
+const char* wq_status_str(int status);
+/* Message of the last failing call on this thread ("" if none).  Never NULL. */
+const char* wq_last_error(void);
+/* Library version string. */
+const char* wq_version(void);
+
+/* ------------------------------------------------------------------ host (CPU)
+ * All host functions are synchronous, single-threaded, deterministic, and are
+ * the reference encoders of the formats above.
+ */
+
+/* W4 quantize + pack (SPECTRA section 3.4, codes per Appendix A Proposition 2).
+ * W: float32 [N][K] (typically the dense residual from wq_split_outliers).
+ * Per (row, group), in float32 with round-half-to-even:
+ *   s = max((wmax - wmin) / 15, 1e-8);  z = clamp(round(-wmin / s), 0, 15);
+ *   q = clamp(round(w / s + z), 0, 15)   (codes use s before its FP16 rounding)
+ * Outputs: codes [N][K/2] (layout above), scales = FP16(s), zeros = FP16(z).
+ * Errors: WQ_ERR_INVALID_ARG for NULL pointers or bad N/K; WQ_ERR_UNSUPPORTED if
+ * group != 32 or K % 32 != 0. */
+int wq_quantize_w4(const float* W, int64_t N, int64_t K, int32_t group,
+                   uint8_t* codes, uint16_t* scales, uint16_t* zeros);
+
+/* W2 quantize + pack (OTF-LLM v4.0 sections 2, 3, 5), float64 per group of 32:
+ * mean mu, population std sigma, u = (w - mu) / sigma (0 if sigma == 0), code
+ * q = nearest FP16 centroid of u (ties to the lower code), c = C[q],
+ * S = sum((w - mu)(c - mean c)) / (sum((c - mean c)^2) + 1e-8), Z = mu - S mean(c).
+ * Sums run left to right over the 32 weights.  scales = FP16(S), zeros = FP16(Z).
+ * Errors as wq_quantize_w4. */
+int wq_quantize_w2(const float* W, int64_t N, int64_t K, int32_t group,
+                   uint8_t* codes, uint16_t* scales, uint16_t* zeros);
+
+/* Profile-guided outlier selection (OTF-LLM v4.0 section 4):
+ * score_c = sqrt(sum_n W[n][c]^2) * profile[c] (float64, rows summed in order);
+ * n_out = floor(ratio * K); the n_out highest scores (ties to the lower index),
+ * written ascending to idx (int32, SPECTRA section 3.3).  idx_cap is the
+ * capacity of idx; *n_out receives the count.
+ * Errors: WQ_ERR_INVALID_ARG if ratio is outside [0, 1], idx_cap < n_out, or a
+ * pointer is NULL. */
+int wq_select_outliers(const float* W, int64_t N, int64_t K, const double* profile,
+                       double ratio, int32_t* idx, int64_t idx_cap, int64_t* n_out);
+
+/* Outlier split (SPECTRA section 3.4 "dense residual"; section 3.6 payload):
+ * W_dense = W with columns idx[] set to 0 (W_dense may alias W), and
+ * W_out[n][j] = FP16(W[n][idx[j]]) (round to nearest even).
+ * Errors: WQ_ERR_INVALID_ARG if idx is not strictly increasing within [0, K). */
+int wq_split_outliers(const float* W, int64_t N, int64_t K, const int32_t* idx,
+                      int64_t n_out, float* W_dense, uint16_t* W_out);
+
+/* Dequantize on the host to FP16 [N][K]:
+ * W4  w_hat = FP16((q - z) * s)            (the float32 product is exact)
+ * W2  w_hat = FP16(float32(S * C[q] + Z))  (one float32 rounding, then FP16).
+ * fmt is WQ_FMT_W4 or WQ_FMT_W2. */
+int wq_dequant_host(int fmt, const uint8_t* codes, const uint16_t* scales,
+                    const uint16_t* zeros, int64_t N, int64_t K, uint16_t* W_hat);
+
+/* ------------------------------------------------------------- device (HIP)
+ * All device pointers; `stream` is a hipStream_t (NULL = null stream).
+ */
+
+/* Device dequantize, bit-identical to wq_dequant_host.  The unfused two-kernel
+ * baseline that SPECTRA section 4.1 argues against (dequantize to memory, then
+ * multiply) is built from this. */
+int wq_dequant_device(int fmt, const uint8_t* codes, const uint16_t* scales,
+                      const uint16_t* zeros, int64_t N, int64_t K, uint16_t* W_hat,
+                      void* stream);
+
+/* Fused M = 1 W4 GEMV (SPECTRA section 4.1):
+ *   y[n] = FP16( sum_{k not in out_idx} w_hat[n][k] x[k]
+ *                + sum_j out_w[n][j] x[out_idx[j]] )      with FP32 accumulation.
+ * With flags & WQ_FUSE_OUTLIERS the outlier sum is added in the same launch;
+ * without it the background still skips out_idx and the caller adds the
+ * outliers with wq_outlier_add.  n_out == 0 means no outliers (out_idx and
+ * out_w may be NULL).  x and y must not overlap. */
+int wq_gemv_w4(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+               int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
+               int64_t n_out, uint32_t flags, const uint16_t* x, uint16_t* y,
+               void* stream);
+
+/* Fused M = 1 W2 GEMV (OTF-LLM v4.0 section 5 and "continuous GEMM addition"),
+ * same contract as wq_gemv_w4 with w_hat = S * C[q] + Z. */
+int wq_gemv_w2(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+               int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
+               int64_t n_out, uint32_t flags, const uint16_t* x, uint16_t* y,
+               void* stream);
+
+/* Small-M batched product on matrix cores (SPECTRA section 4.2; M is a
+ * runtime argument): Y[m][n] = FP16(sum_k X[m][k] w_hat[n][k] + outliers) for
+ * 1 <= M <= WQ_GEMM_MAX_M, fmt WQ_FMT_W4 or WQ_FMT_W2.  X is [M][K], Y is [M][N].
+ * M > WQ_GEMM_MAX_M returns WQ_ERR_UNSUPPORTED. */
+int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+               int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
+               int64_t n_out, uint32_t flags, const uint16_t* X, int64_t M, uint16_t* Y,
+               void* stream);
+
+/* Standalone outlier correction (the add of SPECTRA section 4.1's outlier loop;
+ * the same arithmetic as the column refinement add of the StrataFlux page,
+ * section 3.2.1 Eq. 2, for a static column set):
+ *   Y[m][n] = FP16( Y[m][n] + sum_j out_w[n][j] X[m][idx[j]] ),  FP32 accumulation.
+ * Y is read and written in place. */
+int wq_outlier_add(const int32_t* idx, const uint16_t* out_w, int64_t n_out, int64_t N,
+                   const uint16_t* X, int64_t M, int64_t K, uint16_t* Y, void* stream);
+
+/* -------------------------------------------------- measurement support
+ * Not part of the method: kernels of known traffic that calibrate bandwidth
+ * figures and hardware byte counters. */
+
+/* Streams `bytes` (multiple of 16) from `src` and writes one uint32 per
+ * workgroup to `sink` (sink must hold wq_read_probe_sink_words(bytes) words). */
+int wq_read_probe(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+int64_t wq_read_probe_sink_words(int64_t bytes);
+
+/* Copies `bytes` (multiple of 16) from src to dst with 16-byte vector loads
+ * and stores. */
+int wq_copy_probe(const void* src, void* dst, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

@@ -1,0 +1,205 @@
+"""GPU parity: every device entry point of the C ABI against the CPU oracle on
+the same seeded inputs.
+
+* packed bytes and dequantized FP16 weights: bit-exact;
+* products: every output element within |y - y_ref| <= 2e-3 sum|w x| + 1e-5
+  (y_ref and sum|w x| in float64 from the oracle's own quantization).
+
+Small cases span several workgroup tiles and ragged tails in N, K and n_out;
+full-size cases use the workloads' real shapes in the launch configuration
+the benchmark times.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():   # collected but skipped off the GPU machine
+    pytest.skip("no GPU", allow_module_level=True)
+
+import bit_weight_only_gemv_amd as B  # noqa: E402
+from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def _bits(a):
+    return np.ascontiguousarray(a).view(np.uint16)
+
+
+def dev_fp16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16).view(np.int16)).cuda()
+
+
+def host_fp16(t):
+    return t.cpu().numpy().view(np.float16)
+
+
+def build(fmt, W, profile=None, ratio=0.0):
+    """Oracle layer, and the library's packing of the same W on the GPU (the
+    two are byte-identical; checked here too)."""
+    ref = O.quantize_layer(fmt, W, profile, ratio)
+    hl = pack_host(fmt, W, profile, ratio)
+    assert np.array_equal(hl.codes, ref.codes) and np.array_equal(hl.idx, ref.idx)
+    return ref, DeviceLayer(hl)
+
+
+def check_product(ref, y, x, label):
+    y_ref, a = O.matvec_ref(ref.w_hat(), x, ref.idx, ref.wout)
+    ok, worst = O.check_tolerance(host_fp16(y).astype(np.float64).reshape(y_ref.shape), y_ref, a)
+    say(f"  {label}: worst |err|/bound = {worst:.4f}")
+    assert ok, f"{label}: worst |err|/bound = {worst}"
+    return worst
+
+
+def run_gemv(dl, x, flags=B.WQ_FUSE_OUTLIERS):
+    xd = dev_fp16(x.reshape(-1))
+    y = torch.full((dl.N,), -1, dtype=torch.int16, device="cuda")
+    dl.gemv(xd, y, flags)
+    torch.cuda.synchronize()
+    return y, xd
+
+
+# --------------------------------------------------------------- dequant
+
+
+@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("N,K,scale", [(5, 96, 0.02), (37, 4096, 0.02), (130, 14336, 0.02),
+                                       (64, 1024, 1e-5), (16, 512, 300.0)])
+def test_dequant_device_bit_exact(fmt, N, K, scale):
+    say(f"dequant fmt={fmt} N={N} K={K} sigma={scale}")
+    W = synthetic.gaussian_weights(N, K, scale, 300, N, K)
+    ref, dl = build(fmt, W)
+    out = torch.empty((N, K), dtype=torch.int16, device="cuda")
+    dl.dequant(out)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(host_fp16(out)), _bits(ref.w_hat()))
+
+
+# ------------------------------------------------------------------ gemv
+
+SHAPES = [(1, 32), (7, 96), (129, 4096), (300, 14336), (77, 28672), (64, 8192), (33, 2080),
+          (1000, 1024), (17, 65536)]
+
+
+@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("outl", [False, True])
+def test_gemv_small(fmt, N, K, outl):
+    say(f"gemv fmt={fmt} N={N} K={K} outliers={outl}")
+    L = synthetic.small_layer(fmt, N, K, with_outliers=outl, seed=N % 17)
+    ref, dl = build(fmt, L.W, L.profile, L.ratio)
+    y, _ = run_gemv(dl, L.x)
+    check_product(ref, y, L.x, f"w{fmt} {N}x{K} n_out={ref.n_out}")
+
+
+@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("n_out", [1, 31, 32, 33, 64, 65, 129, 500])
+def test_gemv_outlier_counts(fmt, n_out):
+    K = 4096
+    say(f"gemv fmt={fmt} n_out={n_out}")
+    L = synthetic.small_layer(fmt, 200, K, with_outliers=True, seed=n_out,
+                              ratio=(n_out + 0.5) / K)
+    ref, dl = build(fmt, L.W, L.profile, L.ratio)
+    assert ref.n_out == n_out
+    y, _ = run_gemv(dl, L.x)
+    check_product(ref, y, L.x, f"w{fmt} n_out={n_out}")
+
+
+@pytest.mark.parametrize("fmt", [4, 2])
+def test_gemv_unfused_then_outlier_add(fmt):
+    say(f"gemv unfused + outlier_add fmt={fmt}")
+    L = synthetic.small_layer(fmt, 333, 4096, with_outliers=True, seed=5)
+    ref, dl = build(fmt, L.W, L.profile, L.ratio)
+    y, xd = run_gemv(dl, L.x, flags=0)
+    dl.outlier_add(xd.view(1, -1), y.view(1, -1))
+    torch.cuda.synchronize()
+    check_product(ref, y, L.x, "unfused")
+
+
+def test_gemv_deterministic():
+    L = synthetic.small_layer(2, 1500, 4096, with_outliers=True, seed=9)
+    ref, dl = build(2, L.W, L.profile, L.ratio)
+    y1, _ = run_gemv(dl, L.x)
+    y2, _ = run_gemv(dl, L.x)
+    assert torch.equal(y1, y2)
+
+
+def test_outlier_add_standalone():
+    say("outlier_add M=3")
+    L = synthetic.small_layer(4, 100, 2048, M=3, with_outliers=True, seed=2)
+    ref = O.quantize_layer(4, L.W, L.profile, L.ratio)
+    hl = pack_host(4, L.W, L.profile, L.ratio)
+    dl = DeviceLayer(hl)
+    rng = np.random.default_rng(0)
+    y0 = rng.standard_normal((3, 100)).astype(np.float16)
+    Y = dev_fp16(y0)
+    dl.outlier_add(dev_fp16(L.x), Y)
+    torch.cuda.synchronize()
+    Xo = L.x.astype(np.float64)[:, ref.idx]
+    exp = y0.astype(np.float64) + Xo @ ref.wout.astype(np.float64).T
+    bound = O.TOL_REL * (np.abs(y0.astype(np.float64)) + np.abs(Xo) @ np.abs(ref.wout.astype(np.float64)).T) + O.TOL_ABS
+    assert np.all(np.abs(host_fp16(Y).astype(np.float64) - exp) <= bound)
+
+
+# ------------------------------------------------------------------ gemm
+
+
+@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 13, 16])
+@pytest.mark.parametrize("N,K,outl", [(129, 4096, False), (200, 2080, True), (64, 14336, True)])
+def test_gemm_small(fmt, M, N, K, outl):
+    say(f"gemm fmt={fmt} M={M} N={N} K={K} outliers={outl}")
+    L = synthetic.small_layer(fmt, N, K, M=M, with_outliers=outl, seed=M)
+    ref, dl = build(fmt, L.W, L.profile, L.ratio)
+    X = dev_fp16(L.x)
+    Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
+    dl.gemm(X, Y)
+    torch.cuda.synchronize()
+    check_product(ref, Y, L.x, f"gemm w{fmt} M={M} {N}x{K} n_out={ref.n_out}")
+
+
+# ------------------------------------------------------- full-size layers
+
+
+def test_full_w4_4096x4096_m1():
+    L = synthetic.config1()
+    say("full W4 4096x4096 M=1")
+    ref, dl = build(4, L.W)
+    y, _ = run_gemv(dl, L.x)
+    check_product(ref, y, L.x, "W4 4096x4096")
+
+
+def test_full_w2_14336x4096_outliers_m1():
+    L = synthetic.config2()
+    say("full W2 14336x4096 + outliers M=1")
+    ref, dl = build(2, L.W, L.profile, L.ratio)
+    assert ref.n_out == 143
+    y, _ = run_gemv(dl, L.x)
+    check_product(ref, y, L.x, "W2 14336x4096")
+
+
+@pytest.mark.parametrize("N,K", [(14336, 4096), (4096, 14336)])
+@pytest.mark.parametrize("M", [2, 4, 8, 16])
+def test_full_w4_batched(N, K, M):
+    say(f"full W4 batched {N}x{K} M={M}")
+    L = synthetic.config4(M, N, K)
+    ref, dl = build(4, L.W)
+    X = dev_fp16(L.x)
+    Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    dl.gemm(X, Y)
+    torch.cuda.synchronize()
+    check_product(ref, Y, L.x, f"W4 {N}x{K} M={M}")
+    # M repeated GEMVs agree with the oracle too
+    for m in range(M):
+        y, _ = run_gemv(dl, L.x[m])
+        check_product(ref, y, L.x[m:m + 1], f"W4 {N}x{K} gemv row {m}")
