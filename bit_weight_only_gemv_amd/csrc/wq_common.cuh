@@ -56,20 +56,32 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
 // ------------------------------------------------------------- W4 decoder
 // A 32-bit word w of a W4 group holds bytes 4j..4j+3 (j = word index 0..3);
 // byte k carries code k in its low nibble and code k+16 in its high nibble.
-// OR-ing a nibble into the mantissa of FP16 1024.0 (0x6400) gives the exact
-// FP16 value 1024 + q (bits 3:0) or 1024 + 16 q (bits 7:4), two codes per
-// 32-bit operation:
-//   lo0 = (w      & 0x000F000F) | 0x64006400 -> 1024 + {q[4j],    q[4j+2]}
-//   hi0 = (w      & 0x00F000F0) | 0x64006400 -> 1024 + 16 {q[4j+16], q[4j+18]}
-//   lo1 = (w >> 8 & 0x000F000F) | 0x64006400 -> 1024 + {q[4j+1],  q[4j+3]}
-//   hi1 = (w >> 8 & 0x00F000F0) | 0x64006400 -> 1024 + 16 {q[4j+17], q[4j+19]}
+// Masking two nibbles into the two FP16 halves of a register yields FP16
+// subnormals: bits 3:0 hold q * 2^-24 and bits 7:4 hold 16 q * 2^-24, exactly.
+// gfx950's v_dot2 keeps FP16 subnormal inputs, so these feed the dot product
+// directly and the 2^-24 (and 1/16) come back as one float scale per group:
+//   lo0 = w      & 0x000F000F -> 2^-24 {q[4j],    q[4j+2]}
+//   hi0 = w      & 0x00F000F0 -> 2^-20 {q[4j+16], q[4j+18]}
+//   lo1 = w >> 8 & 0x000F000F -> 2^-24 {q[4j+1],  q[4j+3]}
+//   hi1 = w >> 8 & 0x00F000F0 -> 2^-20 {q[4j+17], q[4j+19]}
+__device__ __forceinline__ void w4_word_sub(uint32_t w, uint32_t& lo0, uint32_t& hi0,
+                                            uint32_t& lo1, uint32_t& hi1) {
+  const uint32_t w8 = w >> 8;
+  lo0 = w & 0x000F000Fu;
+  hi0 = w & 0x00F000F0u;
+  lo1 = w8 & 0x000F000Fu;
+  hi1 = w8 & 0x00F000F0u;
+}
+// The same four pairs as exact FP16 integers 1024 + q / 1024 + 16 q (the low
+// nibble OR-ed into the mantissa of 1024.0 = 0x6400); used where a normal
+// FP16 value is needed (device dequantization).
 __device__ __forceinline__ void w4_word_magic(uint32_t w, uint32_t& lo0, uint32_t& hi0,
                                               uint32_t& lo1, uint32_t& hi1) {
-  const uint32_t w8 = w >> 8;
-  lo0 = (w & 0x000F000Fu) | 0x64006400u;
-  hi0 = (w & 0x00F000F0u) | 0x64006400u;
-  lo1 = (w8 & 0x000F000Fu) | 0x64006400u;
-  hi1 = (w8 & 0x00F000F0u) | 0x64006400u;
+  w4_word_sub(w, lo0, hi0, lo1, hi1);
+  lo0 |= 0x64006400u;
+  hi0 |= 0x64006400u;
+  lo1 |= 0x64006400u;
+  hi1 |= 0x64006400u;
 }
 
 // ------------------------------------------------------------- W2 decoder
@@ -85,6 +97,13 @@ constexpr uint32_t kHiBytes = 0x3E37B7BEu;   // bytes {0xBE, 0xB7, 0x37, 0x3E}
 __device__ __forceinline__ uint32_t w2_centroid_pair(uint32_t t) {
   const uint32_t sel = t * 0x0101u + 0x04000400u;   // t < 2^18: one v_mad_u32_u24
   return __builtin_amdgcn_perm(kHiBytes, kLoBytes, sel);
+}
+
+// Workgroup barrier that only waits for this wave's LDS traffic (HIP's
+// __syncthreads also waits for every outstanding global load, which would
+// serialize a prologue behind the weight stream it is meant to overlap).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ------------------------------------------------------------ reductions

@@ -31,6 +31,8 @@
 #include "wq_common.cuh"
 #include "wq_device.h"
 
+#include <stdlib.h>
+
 namespace wqd {
 
 struct GemvArgs {
@@ -69,7 +71,19 @@ __device__ __forceinline__ uint16_t xh(const uint32_t (&xw)[16], uint32_t mask, 
   return ((mask >> k) & 1u) ? (uint16_t)0 : v;
 }
 
+constexpr int kOutRegs = 4;   // outlier columns per lane kept in registers
+constexpr uint32_t kOob = 0x80000000u;   // buffer offset past any range: loads return 0
+
+// One wave's loads for up to kRowsPerStep rows: codes, scale, zero of its
+// groups, and the outlier weights of the outlier columns it owns.
 template <int FMT, int GPL>
+struct RowBatch {
+  typename Fmt<FMT>::Codes cw[kRowsPerStep][GPL];
+  uint16_t sv[kRowsPerStep][GPL], zv[kRowsPerStep][GPL];
+  uint16_t ow[kRowsPerStep][kOutRegs];
+};
+
+template <int FMT, int GPL, bool HAS_OUT>
 __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
   typedef Fmt<FMT> F;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -77,7 +91,6 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
   const int RT = a.wr * a.rpw;
   uint32_t* s_mask = reinterpret_cast<uint32_t*>(smem);                 // [G] outlier bits
   float* s_part = reinterpret_cast<float*>(smem + 4 * G);               // [RT][wk][4]
-  _Float16* s_xo = reinterpret_cast<_Float16*>(smem + 4 * G + 16 * RT * a.wk);   // [n_out]
 
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -86,54 +99,124 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
   const int kw = wave % a.wk;
   const int rw = wave / a.wk;
   const int tile0 = blockIdx.x * RT;
+  const int rows_here = min(RT, a.N - tile0);
+  const int r_first = rw * a.rpw;                       // tile-local
+  const int r_end = min(r_first + a.rpw, rows_here);
+  const bool do_out = a.fuse && a.n_out > 0;
 
-  // ---- outlier bitmask and gathered outlier activations
-  for (int i = tid; i < G; i += nthr) s_mask[i] = 0u;
-  __syncthreads();
-  for (int j = tid; j < a.n_out; j += nthr) {
-    const uint32_t c = (uint32_t)a.out_idx[j];
-    if (c < (uint32_t)a.K) {
-      atomicOr(&s_mask[c >> 5], 1u << (c & 31));
-      s_xo[j] = __builtin_bit_cast(_Float16, a.x[c]);
-    } else {
-      s_xo[j] = (_Float16)0.0f;
+  // Outlier columns this lane owns: j_t = (kw + wk t) * 64 + lane.  Every
+  // column below n_cap has exactly one owner per row-wave; the rest (only when
+  // n_out > n_cap) go through a slower per-row loop.
+  const int jstride = a.wk * kWave;
+  const int n_cap = jstride * kOutRegs;
+  const int T = min(kOutRegs, (a.n_out + jstride - 1) / jstride);   // wave-uniform
+
+  // ---- (1) loads, issued in the order they are needed (loads return in order)
+  // All prologue loads are branch-free (invalid lanes read past the buffer and
+  // get 0), so the compiler's wait counters can let them overlap.
+  const __amdgpu_buffer_rsrc_t irs = make_rsrc(a.out_idx, (uint32_t)a.n_out * 4u);
+  uint32_t oraw[kOutRegs];
+  bool oval[kOutRegs];
+#pragma unroll
+  for (int t = 0; t < kOutRegs; ++t) {
+    const int j = (kw + a.wk * t) * kWave + lane;
+    oval[t] = HAS_OUT && t < T && j < a.n_out;
+    oraw[t] = HAS_OUT ? ld32(irs, oval[t] ? (uint32_t)j * 4u : kOob) : 0u;
+  }
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.K * 2u);
+  uint32_t xw[GPL][16];
+#pragma unroll
+  for (int i = 0; i < GPL; ++i) {
+    const uint32_t g = (uint32_t)((kw * GPL + i) * kWave + lane);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const u4v t = ld128(xrs, g * 64u + 16u * v);   // zero beyond K
+      xw[i][4 * v + 0] = t.x;
+      xw[i][4 * v + 1] = t.y;
+      xw[i][4 * v + 2] = t.z;
+      xw[i][4 * v + 3] = t.w;
     }
   }
-  __syncthreads();
-
-  // ---- this lane's activations, paired as the decoder emits weights
-  uint32_t xr[GPL][16];
-  float off[GPL], sx[GPL];
+  const uint64_t row_bytes = (uint64_t)a.K / F::kRowBytesPerK;
+  const __amdgpu_buffer_rsrc_t crs =
+      make_rsrc(a.codes + (uint64_t)tile0 * row_bytes, clamp_bytes((uint64_t)rows_here * row_bytes));
+  const __amdgpu_buffer_rsrc_t srs =
+      make_rsrc(a.scales + (uint64_t)tile0 * G, clamp_bytes((uint64_t)rows_here * G * 2));
+  const __amdgpu_buffer_rsrc_t zrs =
+      make_rsrc(a.zeros + (uint64_t)tile0 * G, clamp_bytes((uint64_t)rows_here * G * 2));
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(
+      do_out ? a.out_w + (uint64_t)tile0 * a.n_out : a.out_w,
+      do_out ? clamp_bytes((uint64_t)rows_here * a.n_out * 2) : 0u);
   bool gvalid[GPL];
-  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.K * 2u);
+#pragma unroll
+  for (int i = 0; i < GPL; ++i) gvalid[i] = (kw * GPL + i) * kWave + lane < G;
+
+  RowBatch<FMT, GPL> b;
+#pragma unroll
+  for (int u = 0; u < kRowsPerStep; ++u) {
+    const bool rv = r_first + u < r_end;
+    const uint32_t rl = (uint32_t)(r_first + u);
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const uint32_t g = (uint32_t)((kw * GPL + i) * kWave + lane);
+      const bool ok = rv && gvalid[i];
+      const uint32_t co = ok ? rl * (uint32_t)row_bytes + g * F::kGroupBytes : kOob;
+      const uint32_t mo = ok ? (rl * (uint32_t)G + g) * 2u : kOob;
+      if constexpr (FMT == 4)
+        b.cw[u][i] = ld128(crs, co);
+      else
+        b.cw[u][i] = ld64(crs, co);
+      b.sv[u][i] = ld16(srs, mo);
+      b.zv[u][i] = ld16(zrs, mo);
+    }
+    if constexpr (HAS_OUT) {
+#pragma unroll
+      for (int t = 0; t < kOutRegs; ++t) {
+        const int j = (kw + a.wk * t) * kWave + lane;
+        const bool ok = rv && oval[t];
+        b.ow[u][t] = ld16(ors, ok ? (rl * (uint32_t)a.n_out + (uint32_t)j) * 2u : kOob);
+      }
+    }
+  }
+
+  // ---- (2) outlier bitmask in LDS (the background skips these columns)
+  if constexpr (HAS_OUT) {
+    for (int i = tid; i < G; i += nthr) s_mask[i] = 0u;
+    lds_barrier();
+#pragma unroll
+    for (int t = 0; t < kOutRegs; ++t)
+      if (oval[t] && oraw[t] < (uint32_t)a.K) atomicOr(&s_mask[oraw[t] >> 5], 1u << (oraw[t] & 31));
+    for (int j = n_cap + tid; j < a.n_out; j += nthr) {
+      const uint32_t c = (uint32_t)a.out_idx[j];
+      if (c < (uint32_t)a.K) atomicOr(&s_mask[c >> 5], 1u << (c & 31));
+    }
+    lds_barrier();
+  }
+
+  // ---- (3) outlier activations (gathered now, used after the background)
+  uint16_t xo[kOutRegs];
+#pragma unroll
+  for (int t = 0; t < kOutRegs; ++t)
+    xo[t] = ld16(xrs, (HAS_OUT && oval[t] && oraw[t] < (uint32_t)a.K) ? oraw[t] * 2u : kOob);
+
+  // ---- (4) this lane's activations, masked and paired as the decoder emits weights
+  uint32_t xr[GPL][16];
+  float sx[GPL];
 #pragma unroll
   for (int i = 0; i < GPL; ++i) {
     const int g = (kw * GPL + i) * kWave + lane;
-    gvalid[i] = g < G;
-    uint32_t xw[16];
+    const uint32_t m = !gvalid[i] ? 0xFFFFFFFFu : (HAS_OUT ? s_mask[g] : 0u);
+    float sum = 0.f;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const u4v t = ld128(xrs, (uint32_t)g * 64u + 16u * v);   // zero beyond K
-      xw[4 * v + 0] = t.x;
-      xw[4 * v + 1] = t.y;
-      xw[4 * v + 2] = t.z;
-      xw[4 * v + 3] = t.w;
-    }
-    const uint32_t m = gvalid[i] ? s_mask[g] : 0xFFFFFFFFu;
-    float slo = 0.f, shi = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) slo += h2f(xh(xw, m, k));
-#pragma unroll
-    for (int k = 16; k < 32; ++k) shi += h2f(xh(xw, m, k));
-    sx[i] = slo + shi;
-    off[i] = 1024.0f * slo + 64.0f * shi;
-    if (FMT == 4) {
+    for (int k = 0; k < 32; ++k) sum += h2f(xh(xw[i], m, k));
+    sx[i] = sum;
+    if constexpr (FMT == 4) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        xr[i][4 * j + 0] = pack2(xh(xw, m, 4 * j), xh(xw, m, 4 * j + 2));
-        xr[i][4 * j + 1] = pack2(xh(xw, m, 4 * j + 16), xh(xw, m, 4 * j + 18));
-        xr[i][4 * j + 2] = pack2(xh(xw, m, 4 * j + 1), xh(xw, m, 4 * j + 3));
-        xr[i][4 * j + 3] = pack2(xh(xw, m, 4 * j + 17), xh(xw, m, 4 * j + 19));
+        xr[i][4 * j + 0] = pack2(xh(xw[i], m, 4 * j), xh(xw[i], m, 4 * j + 2));
+        xr[i][4 * j + 1] = pack2(xh(xw[i], m, 4 * j + 16), xh(xw[i], m, 4 * j + 18));
+        xr[i][4 * j + 2] = pack2(xh(xw[i], m, 4 * j + 1), xh(xw[i], m, 4 * j + 3));
+        xr[i][4 * j + 3] = pack2(xh(xw[i], m, 4 * j + 17), xh(xw[i], m, 4 * j + 19));
       }
     } else {
 #pragma unroll
@@ -143,74 +226,42 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
             const int k = 16 * j + 4 * h + p;
-            xr[i][8 * j + 4 * h + p] = pack2(xh(xw, m, k), xh(xw, m, k + 8));
+            xr[i][8 * j + 4 * h + p] = pack2(xh(xw[i], m, k), xh(xw[i], m, k + 8));
           }
     }
   }
 
-  // ---- this workgroup's rows
-  const int rows_here = min(RT, a.N - tile0);
-  const uint64_t row_bytes = (uint64_t)a.K / F::kRowBytesPerK;
-  const __amdgpu_buffer_rsrc_t crs =
-      make_rsrc(a.codes + (uint64_t)tile0 * row_bytes, clamp_bytes((uint64_t)rows_here * row_bytes));
-  const __amdgpu_buffer_rsrc_t srs =
-      make_rsrc(a.scales + (uint64_t)tile0 * G, clamp_bytes((uint64_t)rows_here * G * 2));
-  const __amdgpu_buffer_rsrc_t zrs =
-      make_rsrc(a.zeros + (uint64_t)tile0 * G, clamp_bytes((uint64_t)rows_here * G * 2));
-  const bool do_out = a.fuse && a.n_out > 0;
-  const __amdgpu_buffer_rsrc_t ors = make_rsrc(
-      do_out ? a.out_w + (uint64_t)tile0 * a.n_out : a.out_w,
-      do_out ? clamp_bytes((uint64_t)rows_here * a.n_out * 2) : 0u);
-
-  const int r_first = rw * a.rpw;                       // tile-local
-  const int r_end = min(r_first + a.rpw, rows_here);
-  for (int r0 = r_first; r0 < r_end; r0 += kRowsPerStep) {
-    typename F::Codes cw[kRowsPerStep][GPL];
-    uint16_t sv[kRowsPerStep][GPL], zv[kRowsPerStep][GPL];
+  // ---- (5) the rows
+  {
 #pragma unroll
     for (int u = 0; u < kRowsPerStep; ++u) {
-      const uint32_t rl = (uint32_t)min(r0 + u, r_end - 1);   // clamp: duplicate last row
-#pragma unroll
-      for (int i = 0; i < GPL; ++i) {
-        const uint32_t g = (uint32_t)((kw * GPL + i) * kWave + lane);
-        const uint32_t gi = gvalid[i] ? g : 0u;
-        const uint32_t co = rl * (uint32_t)row_bytes + gi * F::kGroupBytes;
-        if constexpr (FMT == 4)
-          cw[u][i] = ld128(crs, co);
-        else
-          cw[u][i] = ld64(crs, co);
-        sv[u][i] = ld16(srs, (rl * (uint32_t)G + gi) * 2u);
-        zv[u][i] = ld16(zrs, (rl * (uint32_t)G + gi) * 2u);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kRowsPerStep; ++u) {
-      const int rl = r0 + u;
+      const int rl = r_first + u;
       if (rl >= r_end) break;   // uniform across the wave
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < GPL; ++i) {
         if (!gvalid[i]) continue;
-        const float s = h2f(sv[u][i]);
-        const float z = h2f(zv[u][i]);
+        const float s = h2f(b.sv[u][i]);
+        const float z = h2f(b.zv[u][i]);
         if constexpr (FMT == 4) {
           float alo = 0.f, ahi = 0.f;
-          const uint32_t wv[4] = {cw[u][i].x, cw[u][i].y, cw[u][i].z, cw[u][i].w};
+          const uint32_t wv[4] = {b.cw[u][i].x, b.cw[u][i].y, b.cw[u][i].z, b.cw[u][i].w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             uint32_t lo0, hi0, lo1, hi1;
-            w4_word_magic(wv[j], lo0, hi0, lo1, hi1);
+            w4_word_sub(wv[j], lo0, hi0, lo1, hi1);
             alo = __builtin_amdgcn_fdot2(as_h2(lo0), as_h2(xr[i][4 * j + 0]), alo, false);
             ahi = __builtin_amdgcn_fdot2(as_h2(hi0), as_h2(xr[i][4 * j + 1]), ahi, false);
             alo = __builtin_amdgcn_fdot2(as_h2(lo1), as_h2(xr[i][4 * j + 2]), alo, false);
             ahi = __builtin_amdgcn_fdot2(as_h2(hi1), as_h2(xr[i][4 * j + 3]), ahi, false);
           }
-          float v = __builtin_fmaf(ahi, 0.0625f, alo) - off[i];
+          // sum q x = 2^24 (alo + ahi / 16); then (sum q x - z sum x) s
+          float v = __builtin_fmaf(ahi, 0.0625f, alo) * 16777216.0f;
           v = __builtin_fmaf(-z, sx[i], v);
           acc = __builtin_fmaf(s, v, acc);
         } else {
           float ac = 0.f;
-          const uint32_t wv[2] = {cw[u][i].x, cw[u][i].y};
+          const uint32_t wv[2] = {b.cw[u][i].x, b.cw[u][i].y};
 #pragma unroll
           for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -225,10 +276,14 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
           acc = __builtin_fmaf(z, sx[i], acc);
         }
       }
-      if (do_out) {
-        for (int j = (kw * kWave) + lane; j < a.n_out; j += a.wk * kWave) {
-          const uint16_t wo = ld16(ors, ((uint32_t)rl * (uint32_t)a.n_out + (uint32_t)j) * 2u);
-          acc = __builtin_fmaf(h2f(wo), (float)s_xo[j], acc);
+      if (HAS_OUT && do_out) {
+#pragma unroll
+        for (int t = 0; t < kOutRegs; ++t) acc = __builtin_fmaf(h2f(b.ow[u][t]), h2f(xo[t]), acc);
+        for (int j = n_cap + kw * kWave + lane; j < a.n_out; j += jstride) {
+          const uint32_t c = (uint32_t)a.out_idx[j];
+          const float xv = c < (uint32_t)a.K ? h2f(a.x[c]) : 0.f;
+          acc = __builtin_fmaf(h2f(ld16(ors, ((uint32_t)rl * (uint32_t)a.n_out + (uint32_t)j) * 2u)),
+                               xv, acc);
         }
       }
       acc = row16_sum(acc);
@@ -270,16 +325,17 @@ static GemvPlan plan_gemv(int64_t N, int64_t K, int64_t n_out) {
     }
   }
   p.wr = p.wk >= 4 ? 1 : 4 / p.wk;
-  p.rpw = 4;
-  // Larger tiles when there are many rows, so each workgroup's setup (mask,
-  // activation registers) is spread over more rows.
-  const int64_t waves_per_tile_rows = (int64_t)p.wr * p.rpw;
-  while (p.rpw < 16 && (N + waves_per_tile_rows * 2 - 1) / (waves_per_tile_rows * 2) >= 1024) {
-    p.rpw *= 2;
+  // One batch of at most 4 rows per wave; fewer rows per wave when that is
+  // what it takes to have ~1024 workgroups in flight.
+  p.rpw = kRowsPerStep;
+  while (p.rpw > 1 && (N + (int64_t)p.wr * p.rpw - 1) / ((int64_t)p.wr * p.rpw) < 1024) p.rpw /= 2;
+  if (const char* e = getenv("WQ_GEMV_ROWS_PER_WAVE")) {
+    const int v = atoi(e);
+    if (v >= 1 && v <= kRowsPerStep) p.rpw = v;
   }
   p.rt = p.wr * p.rpw;
   p.blocks = (int)((N + p.rt - 1) / p.rt);
-  p.lds = (size_t)4 * G + (size_t)16 * p.rt * p.wk + (size_t)2 * n_out + 16;
+  p.lds = (size_t)4 * G + (size_t)16 * p.rt * p.wk;
   return p;
 }
 
@@ -294,10 +350,14 @@ static int launch_gemv(const GemvArgs& a0, hipStream_t stream, const char* who) 
   a.wr = p.wr;
   a.rpw = p.rpw;
   const dim3 grid(p.blocks), block(p.wk * p.wr * kWave);
-  switch (p.gpl) {
-    case 1: hipLaunchKernelGGL((gemv_kernel<FMT, 1>), grid, block, p.lds, stream, a); break;
-    case 2: hipLaunchKernelGGL((gemv_kernel<FMT, 2>), grid, block, p.lds, stream, a); break;
-    default: hipLaunchKernelGGL((gemv_kernel<FMT, 4>), grid, block, p.lds, stream, a); break;
+  const bool out = a.n_out > 0;
+  switch (p.gpl * 2 + (out ? 1 : 0)) {
+    case 2: hipLaunchKernelGGL((gemv_kernel<FMT, 1, false>), grid, block, p.lds, stream, a); break;
+    case 3: hipLaunchKernelGGL((gemv_kernel<FMT, 1, true>), grid, block, p.lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((gemv_kernel<FMT, 2, false>), grid, block, p.lds, stream, a); break;
+    case 5: hipLaunchKernelGGL((gemv_kernel<FMT, 2, true>), grid, block, p.lds, stream, a); break;
+    case 8: hipLaunchKernelGGL((gemv_kernel<FMT, 4, false>), grid, block, p.lds, stream, a); break;
+    default: hipLaunchKernelGGL((gemv_kernel<FMT, 4, true>), grid, block, p.lds, stream, a); break;
   }
   return check_launch(who);
 }

@@ -76,6 +76,17 @@ float f16_to_f32(uint16_t h) {
   return (float)(sign ? -v : v);
 }
 
+// Round to nearest integer, ties to even, in the default rounding mode:
+// adding and subtracting 2^23 leaves an integer for |v| < 2^23, and every
+// float of larger magnitude is already an integer.  The sign is kept, so
+// values in (-0.5, 0) give -0 like any IEEE roundToIntegralTiesToEven.
+inline float round_half_even(float v) {
+  const float big = 8388608.0f;   // 2^23
+  const float a = std::fabs(v);
+  if (!(a < big)) return v;
+  return std::copysign((a + big) - big, v);
+}
+
 // The OTF-LLM codebook {-1.52, -0.45, +0.45, +1.52} at its FP16 values.
 const uint16_t kCodebookF16[4] = {0xBE14u, 0xB733u, 0x3733u, 0x3E14u};
 
@@ -158,13 +169,13 @@ int wq_quantize_w4(const float* W, int64_t N, int64_t K, int32_t group, uint8_t*
       }
       float s = (wmax - wmin) / 15.0f;
       if (!(s > 1e-8f)) s = 1e-8f;
-      float z = std::nearbyint(-wmin / s);
+      float z = round_half_even(-wmin / s);
       z = std::min(std::max(z, 0.0f), 15.0f);
       uint8_t q[WQ_GROUP];
       for (int k = 0; k < WQ_GROUP; ++k) {
         float t = w[k] / s;
         t = t + z;
-        t = std::nearbyint(t);
+        t = round_half_even(t);
         t = std::min(std::max(t, 0.0f), 15.0f);
         q[k] = (uint8_t)t;
       }
