@@ -42,7 +42,9 @@ def _parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="w2_14336",
-                   choices=["w2_14336", "w4_4096", "sweep", "batched", "w2_70b"])
+                   choices=["w2_14336", "w4_4096", "sweep", "batched", "w2_70b", "read"])
+    p.add_argument("--read-bytes", type=int, default=26157628,
+                   help="bytes per launch of the read-probe workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true", help="replay the timed launches as a HIP graph")
     return p.parse_args()
@@ -76,6 +78,8 @@ def main():
     dev = torch.cuda.get_device_name(0)
     stream = torch.cuda.current_stream()
 
+    if a.workload == "read":
+        return read_probe(a, torch, B)
     if a.workload == "w2_14336":
         L = synthetic.config2()
         label = "w2_14336x4096_outliers143_m1"
@@ -169,6 +173,42 @@ def main():
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(L, nbytes)
     print(json.dumps(out), flush=True)
+
+
+def read_probe(a, torch, B):
+    """Attainable HBM read rate: a plain streaming-read kernel over rotated
+    buffers of the given size (no decode, no arithmetic)."""
+    nb = (a.read_bytes + 15) // 16 * 16
+    ncopy = max(1, -(-ROTATE_BYTES // nb))
+    bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
+    for b in bufs:
+        b.fill_(1)
+    sink = torch.empty(B.wq_read_probe_sink_words(nb), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        B.wq_read_probe(bufs[i % ncopy], nb, sink)
+
+    for i in range(a.warmup):
+        step(i)
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(stream)
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for i in range(a.steps):
+                step(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / a.steps
+    print(json.dumps({"workload": "read_probe", "bytes": nb, "copies": ncopy, "ms_per_step": ms,
+                      "GB/s": round(nb / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(L, nbytes):

@@ -33,6 +33,8 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
+
 namespace wqd {
 
 struct GemvArgs {
@@ -71,6 +73,53 @@ __device__ __forceinline__ uint16_t xh(const uint32_t (&xw)[16], uint32_t mask, 
   return ((mask >> k) & 1u) ? (uint16_t)0 : v;
 }
 
+// Masks one group's 32 activations (bit k of `mask` set = column k is an
+// outlier, or the group is past K) and pairs them the way the decoder emits
+// weights: W4 word j gives (4j, 4j+2), (4j+16, 4j+18), (4j+1, 4j+3),
+// (4j+17, 4j+19); W2 word j, byte h, position p gives (16j+4h+p, +8).
+// Also returns the float sum of the masked activations.
+template <int FMT>
+__device__ __forceinline__ void pair_group(const uint32_t (&xw)[16], uint32_t m,
+                                           uint32_t (&out)[16], float& sum) {
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) s += h2f(xh(xw, m, k));
+  sum = s;
+  if constexpr (FMT == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      out[4 * j + 0] = pack2(xh(xw, m, 4 * j), xh(xw, m, 4 * j + 2));
+      out[4 * j + 1] = pack2(xh(xw, m, 4 * j + 16), xh(xw, m, 4 * j + 18));
+      out[4 * j + 2] = pack2(xh(xw, m, 4 * j + 1), xh(xw, m, 4 * j + 3));
+      out[4 * j + 3] = pack2(xh(xw, m, 4 * j + 17), xh(xw, m, 4 * j + 19));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int k = 16 * j + 4 * h + p;
+          out[8 * j + 4 * h + p] = pack2(xh(xw, m, k), xh(xw, m, k + 8));
+        }
+  }
+}
+
+__device__ __forceinline__ void load_group_x(__amdgpu_buffer_rsrc_t xrs, uint32_t off,
+                                             uint32_t (&xw)[16]) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const u4v t = ld128(xrs, off == 0x80000000u ? off : off + 16u * v);
+    xw[4 * v + 0] = t.x;
+    xw[4 * v + 1] = t.y;
+    xw[4 * v + 2] = t.z;
+    xw[4 * v + 3] = t.w;
+  }
+}
+
+constexpr int kPrepSlots = 2;   // groups of activations each thread prepares in LDS
+
 constexpr int kOutRegs = 4;   // outlier columns per lane kept in registers
 constexpr uint32_t kOob = 0x80000000u;   // buffer offset past any range: loads return 0
 
@@ -83,14 +132,21 @@ struct RowBatch {
   uint16_t ow[kRowsPerStep][kOutRegs];
 };
 
-template <int FMT, int GPL, bool HAS_OUT>
+// XLDS: the workgroup prepares the masked, paired activations once in LDS
+// and every wave reads its slice (otherwise each lane prepares its own).
+template <int FMT, int GPL, bool HAS_OUT, bool XLDS>
 __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
   typedef Fmt<FMT> F;
   extern __shared__ __align__(16) unsigned char smem[];
   const int G = a.K / kGroup;
   const int RT = a.wr * a.rpw;
+  // LDS: [mask / partial sums (aliased: the mask is dead before partials are
+  // written)] [per-group activation sums] [paired activations, 64 B a group]
+  const int head = max(4 * G, 16 * RT * a.wk);
   uint32_t* s_mask = reinterpret_cast<uint32_t*>(smem);                 // [G] outlier bits
-  float* s_part = reinterpret_cast<float*>(smem + 4 * G);               // [RT][wk][4]
+  float* s_part = reinterpret_cast<float*>(smem);                       // [RT][wk][4]
+  float* s_sx = reinterpret_cast<float*>(smem + head);                  // [G]
+  u4v* s_xp = reinterpret_cast<u4v*>(smem + ((head + 4 * G + 15) & ~15));   // [G][4]
 
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -124,18 +180,12 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
     oraw[t] = HAS_OUT ? ld32(irs, oval[t] ? (uint32_t)j * 4u : kOob) : 0u;
   }
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.K * 2u);
-  uint32_t xw[GPL][16];
+  constexpr int XS = XLDS ? kPrepSlots : GPL;
+  uint32_t xw[XS][16];
 #pragma unroll
-  for (int i = 0; i < GPL; ++i) {
-    const uint32_t g = (uint32_t)((kw * GPL + i) * kWave + lane);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const u4v t = ld128(xrs, g * 64u + 16u * v);   // zero beyond K
-      xw[i][4 * v + 0] = t.x;
-      xw[i][4 * v + 1] = t.y;
-      xw[i][4 * v + 2] = t.z;
-      xw[i][4 * v + 3] = t.w;
-    }
+  for (int i = 0; i < XS; ++i) {
+    const uint32_t g = XLDS ? (uint32_t)(tid + nthr * i) : (uint32_t)((kw * GPL + i) * kWave + lane);
+    load_group_x(xrs, g < (uint32_t)G ? g * 64u : kOob, xw[i]);
   }
   const uint64_t row_bytes = (uint64_t)a.K / F::kRowBytesPerK;
   const __amdgpu_buffer_rsrc_t crs =
@@ -199,39 +249,57 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
   for (int t = 0; t < kOutRegs; ++t)
     xo[t] = ld16(xrs, (HAS_OUT && oval[t] && oraw[t] < (uint32_t)a.K) ? oraw[t] * 2u : kOob);
 
-  // ---- (4) this lane's activations, masked and paired as the decoder emits weights
+  // ---- (4) activations, masked and paired as the decoder emits weights
   uint32_t xr[GPL][16];
   float sx[GPL];
+  if constexpr (XLDS) {
 #pragma unroll
-  for (int i = 0; i < GPL; ++i) {
-    const int g = (kw * GPL + i) * kWave + lane;
-    const uint32_t m = !gvalid[i] ? 0xFFFFFFFFu : (HAS_OUT ? s_mask[g] : 0u);
-    float sum = 0.f;
+    for (int i = 0; i < XS; ++i) {
+      const int g = tid + nthr * i;
+      if (g < G) {
+        uint32_t pr[16];
+        float sum;
+        pair_group<FMT>(xw[i], HAS_OUT ? s_mask[g] : 0u, pr, sum);
 #pragma unroll
-    for (int k = 0; k < 32; ++k) sum += h2f(xh(xw[i], m, k));
-    sx[i] = sum;
-    if constexpr (FMT == 4) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xr[i][4 * j + 0] = pack2(xh(xw[i], m, 4 * j), xh(xw[i], m, 4 * j + 2));
-        xr[i][4 * j + 1] = pack2(xh(xw[i], m, 4 * j + 16), xh(xw[i], m, 4 * j + 18));
-        xr[i][4 * j + 2] = pack2(xh(xw[i], m, 4 * j + 1), xh(xw[i], m, 4 * j + 3));
-        xr[i][4 * j + 3] = pack2(xh(xw[i], m, 4 * j + 17), xh(xw[i], m, 4 * j + 19));
+        for (int v = 0; v < 4; ++v) s_xp[g * 4 + v] = (u4v){pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]};
+        s_sx[g] = sum;
       }
-    } else {
+    }
+    for (int g = tid + nthr * XS; g < G; g += nthr) {   // only when K > 64 * 512 * ...
+      uint32_t w2[16], pr[16];
+      float sum;
+      load_group_x(xrs, (uint32_t)g * 64u, w2);
+      pair_group<FMT>(w2, HAS_OUT ? s_mask[g] : 0u, pr, sum);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int v = 0; v < 4; ++v) s_xp[g * 4 + v] = (u4v){pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]};
+      s_sx[g] = sum;
+    }
+    lds_barrier();
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+    for (int i = 0; i < GPL; ++i) {
+      const int g = (kw * GPL + i) * kWave + lane;
+      const int gg = gvalid[i] ? g : 0;
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int k = 16 * j + 4 * h + p;
-            xr[i][8 * j + 4 * h + p] = pack2(xh(xw[i], m, k), xh(xw[i], m, k + 8));
-          }
+      for (int v = 0; v < 4; ++v) {
+        const u4v t = s_xp[gg * 4 + v];
+        xr[i][4 * v + 0] = t.x;
+        xr[i][4 * v + 1] = t.y;
+        xr[i][4 * v + 2] = t.z;
+        xr[i][4 * v + 3] = t.w;
+      }
+      sx[i] = s_sx[gg];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const int g = (kw * GPL + i) * kWave + lane;
+      const uint32_t m = !gvalid[i] ? 0xFFFFFFFFu : (HAS_OUT ? s_mask[g] : 0u);
+      pair_group<FMT>(xw[i], m, xr[i], sx[i]);
     }
   }
 
-  // ---- (5) the rows
+  // ---- (5) the rows (s_part aliases s_mask: wait until every wave has read its mask)
+  if constexpr (HAS_OUT && !XLDS) lds_barrier();
   {
 #pragma unroll
     for (int u = 0; u < kRowsPerStep; ++u) {
@@ -305,7 +373,8 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
 
 struct GemvPlan {
   int gpl, wk, wr, rpw, rt, blocks;
-  size_t lds;
+  size_t lds, lds_reg;
+  bool xlds;
 };
 
 static GemvPlan plan_gemv(int64_t N, int64_t K, int64_t n_out) {
@@ -335,7 +404,12 @@ static GemvPlan plan_gemv(int64_t N, int64_t K, int64_t n_out) {
   }
   p.rt = p.wr * p.rpw;
   p.blocks = (int)((N + p.rt - 1) / p.rt);
-  p.lds = (size_t)4 * G + (size_t)16 * p.rt * p.wk;
+  const size_t head = std::max((size_t)4 * G, (size_t)16 * p.rt * p.wk);
+  p.lds_reg = head;
+  p.lds = ((head + (size_t)4 * G + 15) & ~(size_t)15) + (size_t)64 * G;
+  p.xlds = p.lds <= kMaxLdsBytes;
+  if (const char* e = getenv("WQ_GEMV_XLDS")) p.xlds = p.xlds && atoi(e) != 0;
+  if (!p.xlds) p.lds = p.lds_reg;
   return p;
 }
 
@@ -351,14 +425,16 @@ static int launch_gemv(const GemvArgs& a0, hipStream_t stream, const char* who) 
   a.rpw = p.rpw;
   const dim3 grid(p.blocks), block(p.wk * p.wr * kWave);
   const bool out = a.n_out > 0;
-  switch (p.gpl * 2 + (out ? 1 : 0)) {
-    case 2: hipLaunchKernelGGL((gemv_kernel<FMT, 1, false>), grid, block, p.lds, stream, a); break;
-    case 3: hipLaunchKernelGGL((gemv_kernel<FMT, 1, true>), grid, block, p.lds, stream, a); break;
-    case 4: hipLaunchKernelGGL((gemv_kernel<FMT, 2, false>), grid, block, p.lds, stream, a); break;
-    case 5: hipLaunchKernelGGL((gemv_kernel<FMT, 2, true>), grid, block, p.lds, stream, a); break;
-    case 8: hipLaunchKernelGGL((gemv_kernel<FMT, 4, false>), grid, block, p.lds, stream, a); break;
-    default: hipLaunchKernelGGL((gemv_kernel<FMT, 4, true>), grid, block, p.lds, stream, a); break;
+#define WQ_GEMV_CASE(G_, O_, X_)                                                           \
+  if (p.gpl == G_ && out == O_ && p.xlds == X_) {                                          \
+    hipLaunchKernelGGL((gemv_kernel<FMT, G_, O_, X_>), grid, block, p.lds, stream, a);     \
+    return check_launch(who);                                                              \
   }
+  WQ_GEMV_CASE(1, false, true) WQ_GEMV_CASE(1, true, true) WQ_GEMV_CASE(1, false, false)
+  WQ_GEMV_CASE(1, true, false) WQ_GEMV_CASE(2, false, true) WQ_GEMV_CASE(2, true, true)
+  WQ_GEMV_CASE(2, false, false) WQ_GEMV_CASE(2, true, false) WQ_GEMV_CASE(4, false, true)
+  WQ_GEMV_CASE(4, true, true) WQ_GEMV_CASE(4, false, false) WQ_GEMV_CASE(4, true, false)
+#undef WQ_GEMV_CASE
   return check_launch(who);
 }
 
