@@ -118,8 +118,6 @@ __device__ __forceinline__ void load_group_x(__amdgpu_buffer_rsrc_t xrs, uint32_
   }
 }
 
-constexpr int kPrepSlots = 2;   // groups of activations each thread prepares in LDS
-
 constexpr int kOutRegs = 4;   // outlier columns per lane kept in registers
 constexpr uint32_t kOob = 0x80000000u;   // buffer offset past any range: loads return 0
 
@@ -132,21 +130,338 @@ struct RowBatch {
   uint16_t ow[kRowsPerStep][kOutRegs];
 };
 
-// XLDS: the workgroup prepares the masked, paired activations once in LDS
-// and every wave reads its slice (otherwise each lane prepares its own).
-template <int FMT, int GPL, bool HAS_OUT, bool XLDS>
-__global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
+// Contiguous byte range [b0, b0 + len) of a global array staged into LDS by
+// the whole workgroup with 16-byte loads (at most kStageSlots per thread;
+// larger ranges fall back to a loop).  Loads are issued first (issue) and
+// written to LDS later (commit), so the wait for them can come after other
+// loads were issued.  Data starts at dst + shift in LDS.
+constexpr int kStageSlots = 2;
+struct Stage {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t shift, nchunks;
+  u4v v[kStageSlots];
+  __device__ __forceinline__ void issue(const void* base, uint64_t b0, uint64_t len,
+                                        uint64_t total, int tid, int nthr) {
+    const uint64_t a0 = b0 & ~(uint64_t)15;
+    shift = (uint32_t)(b0 - a0);
+    nchunks = (uint32_t)((shift + len + 15) / 16);
+    // A 16-byte load that reaches past the record count returns all zeros, so
+    // the count is rounded up to whole chunks: the few bytes past the array end
+    // stay inside the 16-byte block (and page) of its last element, and are
+    // never used.
+    rs = make_rsrc(static_cast<const unsigned char*>(base) + a0,
+                   clamp_bytes((total - a0 + 15) & ~(uint64_t)15));
+#pragma unroll
+    for (int i = 0; i < kStageSlots; ++i) {
+      const uint32_t c = (uint32_t)(tid + nthr * i);
+      v[i] = ld128(rs, c < nchunks ? c * 16u : 0x80000000u);
+    }
+  }
+  __device__ __forceinline__ void commit(unsigned char* dst, int tid, int nthr) const {
+    u4v* d = reinterpret_cast<u4v*>(dst);
+#pragma unroll
+    for (int i = 0; i < kStageSlots; ++i) {
+      const uint32_t c = (uint32_t)(tid + nthr * i);
+      if (c < nchunks) d[c] = v[i];
+    }
+    for (uint32_t c = (uint32_t)(tid + nthr * kStageSlots); c < nchunks; c += (uint32_t)nthr)
+      d[c] = ld128(rs, c * 16u);
+  }
+};
+
+__device__ __forceinline__ size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+// Bytes of LDS the main kernel needs (host and device agree on this layout).
+__host__ __device__ inline size_t gemv_lds_bytes(int K, int RT, int wk, int n_out, bool has_out) {
+  const size_t G = (size_t)K / kGroup;
+  size_t off = ((size_t)16 * RT * wk + 15) & ~(size_t)15;              // partial sums
+  off += ((size_t)RT * G * 2 + 16 + 15) & ~(size_t)15;                 // scales
+  off += ((size_t)RT * G * 2 + 16 + 15) & ~(size_t)15;                 // zeros
+  if (has_out) {
+    off += ((size_t)RT * n_out * 2 + 16 + 15) & ~(size_t)15;           // outlier slab rows
+    off += ((size_t)n_out * 4 + 16 + 15) & ~(size_t)15;                // outlier indices
+  }
+  return off + (size_t)K * 2;                                          // activations
+}
+
+template <int FMT, int GPL, bool HAS_OUT>
+__device__ __forceinline__ void load_rows(RowBatch<FMT, GPL>& b, __amdgpu_buffer_rsrc_t crs,
+                                          __amdgpu_buffer_rsrc_t srs, __amdgpu_buffer_rsrc_t zrs,
+                                          __amdgpu_buffer_rsrc_t ors, int r_first, int r_end,
+                                          uint32_t row_bytes, uint32_t G, int kw, int lane,
+                                          const bool (&gvalid)[GPL], const bool (&oval)[kOutRegs],
+                                          int wk, int n_out) {
+  typedef Fmt<FMT> F;
+#pragma unroll
+  for (int u = 0; u < kRowsPerStep; ++u) {
+    const bool rv = r_first + u < r_end;
+    const uint32_t rl = (uint32_t)(r_first + u);
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const uint32_t g = (uint32_t)((kw * GPL + i) * kWave + lane);
+      const bool ok = rv && gvalid[i];
+      const uint32_t co = ok ? rl * row_bytes + g * F::kGroupBytes : kOob;
+      const uint32_t mo = ok ? (rl * G + g) * 2u : kOob;
+      if constexpr (FMT == 4)
+        b.cw[u][i] = ld128(crs, co);
+      else
+        b.cw[u][i] = ld64(crs, co);
+      b.sv[u][i] = ld16(srs, mo);
+      b.zv[u][i] = ld16(zrs, mo);
+    }
+    if constexpr (HAS_OUT) {
+#pragma unroll
+      for (int t = 0; t < kOutRegs; ++t) {
+        const int j = (kw + wk * t) * kWave + lane;
+        const bool ok = rv && oval[t];
+        b.ow[u][t] = ld16(ors, ok ? (rl * (uint32_t)n_out + (uint32_t)j) * 2u : kOob);
+      }
+    }
+  }
+}
+
+// One W4 group: codes enter v_dot2 as FP16 subnormals q * 2^-24 (low nibbles)
+// and 16 q * 2^-24 (high nibbles); sum (q - z) s x = s (2^24 (lo + hi / 16) - z sum x).
+__device__ __forceinline__ float w4_group_dot(const u4v& cw, const uint32_t (&xr)[16], float s,
+                                              float z, float sx, float acc) {
+  float alo = 0.f, ahi = 0.f;
+  const uint32_t wv[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t lo0, hi0, lo1, hi1;
+    w4_word_sub(wv[j], lo0, hi0, lo1, hi1);
+    alo = __builtin_amdgcn_fdot2(as_h2(lo0), as_h2(xr[4 * j + 0]), alo, false);
+    ahi = __builtin_amdgcn_fdot2(as_h2(hi0), as_h2(xr[4 * j + 1]), ahi, false);
+    alo = __builtin_amdgcn_fdot2(as_h2(lo1), as_h2(xr[4 * j + 2]), alo, false);
+    ahi = __builtin_amdgcn_fdot2(as_h2(hi1), as_h2(xr[4 * j + 3]), ahi, false);
+  }
+  float v = __builtin_fmaf(ahi, 0.0625f, alo) * 16777216.0f;
+  v = __builtin_fmaf(-z, sx, v);
+  return __builtin_fmaf(s, v, acc);
+}
+
+// Main kernel.  Per workgroup (RT rows): the scales, zeros and outlier
+// weights of its rows, the outlier indices and x are each one contiguous
+// range and are staged into LDS with 16-byte loads by the whole workgroup;
+// x is masked in LDS (one 16-bit store per outlier column).  The packed codes
+// are the only per-lane global loads.  Each wave then reads its K-slice of x,
+// pairs it the way the decoder emits weights, and sweeps its rows.
+template <int FMT, int GPL, bool HAS_OUT, int XC>
+__global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
   typedef Fmt<FMT> F;
   extern __shared__ __align__(16) unsigned char smem[];
   const int G = a.K / kGroup;
   const int RT = a.wr * a.rpw;
-  // LDS: [mask / partial sums (aliased: the mask is dead before partials are
-  // written)] [per-group activation sums] [paired activations, 64 B a group]
-  const int head = max(4 * G, 16 * RT * a.wk);
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int kw = wave % a.wk;
+  const int rw = wave / a.wk;
+  const int tile0 = blockIdx.x * RT;
+  const int rows_here = min(RT, a.N - tile0);
+  const int r_first = rw * a.rpw;
+  const int r_end = min(r_first + a.rpw, rows_here);
+  const bool do_out = a.fuse && a.n_out > 0;
+  const int jstride = a.wk * kWave;
+  const int n_cap = jstride * kOutRegs;
+  const int T = min(kOutRegs, (a.n_out + jstride - 1) / jstride);
+  const int nch = a.K / 8;   // 16-byte chunks of x
+
+  size_t off = align16((size_t)16 * RT * a.wk);
+  float* s_part = reinterpret_cast<float*>(smem);
+  unsigned char* s_sc = smem + off;
+  off += align16((size_t)RT * G * 2 + 16);
+  unsigned char* s_zr = smem + off;
+  off += align16((size_t)RT * G * 2 + 16);
+  unsigned char* s_ow = smem + off;
+  if (HAS_OUT) off += align16((size_t)RT * a.n_out * 2 + 16);
+  int32_t* s_idx = reinterpret_cast<int32_t*>(smem + off);
+  if (HAS_OUT) off += align16((size_t)a.n_out * 4 + 16);
+  uint16_t* s_x = reinterpret_cast<uint16_t*>(smem + off);
+  u4v* s_x16 = reinterpret_cast<u4v*>(smem + off);
+
+  // ---- (1) loads, in the order they are needed; all branch-free
+  Stage st_idx, st_sc, st_zr, st_ow;
+  if constexpr (HAS_OUT) st_idx.issue(a.out_idx, 0, (uint64_t)a.n_out * 4, (uint64_t)a.n_out * 4, tid, nthr);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.K * 2u);
+  u4v xc[XC];
+#pragma unroll
+  for (int i = 0; i < XC; ++i) {
+    const int c = tid + nthr * i;
+    xc[i] = ld128(xrs, c < nch ? (uint32_t)c * 16u : kOob);
+  }
+  const uint64_t meta_total = (uint64_t)a.N * G * 2;
+  st_sc.issue(a.scales, (uint64_t)tile0 * G * 2, (uint64_t)rows_here * G * 2, meta_total, tid, nthr);
+  st_zr.issue(a.zeros, (uint64_t)tile0 * G * 2, (uint64_t)rows_here * G * 2, meta_total, tid, nthr);
+  if constexpr (HAS_OUT)
+    st_ow.issue(a.out_w, (uint64_t)tile0 * a.n_out * 2, (uint64_t)rows_here * a.n_out * 2,
+                (uint64_t)a.N * a.n_out * 2, tid, nthr);
+  const uint64_t row_bytes = (uint64_t)a.K / F::kRowBytesPerK;
+  const __amdgpu_buffer_rsrc_t crs =
+      make_rsrc(a.codes + (uint64_t)tile0 * row_bytes, clamp_bytes((uint64_t)rows_here * row_bytes));
+  bool gvalid[GPL];
+#pragma unroll
+  for (int i = 0; i < GPL; ++i) gvalid[i] = (kw * GPL + i) * kWave + lane < G;
+  typename F::Codes cw[kRowsPerStep][GPL];
+#pragma unroll
+  for (int u = 0; u < kRowsPerStep; ++u) {
+    const bool rv = r_first + u < r_end;
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const uint32_t g = (uint32_t)((kw * GPL + i) * kWave + lane);
+      const uint32_t co = (rv && gvalid[i]) ? (uint32_t)(r_first + u) * (uint32_t)row_bytes + g * F::kGroupBytes : kOob;
+      if constexpr (FMT == 4)
+        cw[u][i] = ld128(crs, co);
+      else
+        cw[u][i] = ld64(crs, co);
+    }
+  }
+
+  // ---- (2) staged ranges into LDS
+  if constexpr (HAS_OUT) st_idx.commit(reinterpret_cast<unsigned char*>(s_idx), tid, nthr);
+#pragma unroll
+  for (int i = 0; i < XC; ++i) {
+    const int c = tid + nthr * i;
+    if (c < nch) s_x16[c] = xc[i];
+  }
+  for (int c = tid + nthr * XC; c < nch; c += nthr) s_x16[c] = ld128(xrs, (uint32_t)c * 16u);
+  st_sc.commit(s_sc, tid, nthr);
+  st_zr.commit(s_zr, tid, nthr);
+  if constexpr (HAS_OUT) st_ow.commit(s_ow, tid, nthr);
+  lds_barrier();
+
+  // ---- (3) outlier activations, then the outlier columns of x zeroed
+  float xo[kOutRegs];
+  if constexpr (HAS_OUT) {
+#pragma unroll
+    for (int t = 0; t < kOutRegs; ++t) {
+      const int j = (kw + a.wk * t) * kWave + lane;
+      const uint32_t c = (t < T && j < a.n_out) ? (uint32_t)s_idx[j] : 0xFFFFFFFFu;
+      xo[t] = c < (uint32_t)a.K ? h2f(s_x[c]) : 0.f;
+    }
+    lds_barrier();
+    for (int j = tid; j < a.n_out; j += nthr) {
+      const uint32_t c = (uint32_t)s_idx[j];
+      if (c < (uint32_t)a.K) s_x[c] = 0;
+    }
+    lds_barrier();
+  }
+
+  // ---- (4) this wave's activations, paired as the decoder emits weights
+  uint32_t xr[GPL][16];
+  float sx[GPL];
+  const uint32_t one2 = 0x3C003C00u;   // FP16 (1, 1)
+#pragma unroll
+  for (int i = 0; i < GPL; ++i) {
+    const int g = gvalid[i] ? (kw * GPL + i) * kWave + lane : 0;
+    uint32_t xw[16];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const u4v t = s_x16[g * 4 + v];
+      xw[4 * v + 0] = t.x;
+      xw[4 * v + 1] = t.y;
+      xw[4 * v + 2] = t.z;
+      xw[4 * v + 3] = t.w;
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) sum = __builtin_amdgcn_fdot2(as_h2(xw[m]), as_h2(one2), sum, false);
+    sx[i] = sum;
+    if constexpr (FMT == 4) {
+      // (4j, 4j+2), (4j+16, 4j+18), (4j+1, 4j+3), (4j+17, 4j+19)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xr[i][4 * j + 0] = __builtin_amdgcn_perm(xw[2 * j + 1], xw[2 * j], 0x05040100u);
+        xr[i][4 * j + 1] = __builtin_amdgcn_perm(xw[2 * j + 9], xw[2 * j + 8], 0x05040100u);
+        xr[i][4 * j + 2] = __builtin_amdgcn_perm(xw[2 * j + 1], xw[2 * j], 0x07060302u);
+        xr[i][4 * j + 3] = __builtin_amdgcn_perm(xw[2 * j + 9], xw[2 * j + 8], 0x07060302u);
+      }
+    } else {
+      // (k, k + 8) for k = 16 j + 4 h + p
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int k = 16 * j + 4 * h + p;
+            xr[i][8 * j + 4 * h + p] =
+                __builtin_amdgcn_perm(xw[(k >> 1) + 4], xw[k >> 1], (k & 1) ? 0x07060302u : 0x05040100u);
+          }
+    }
+  }
+
+  // ---- (5) the rows
+  const uint16_t* sc16 = reinterpret_cast<const uint16_t*>(s_sc + st_sc.shift);
+  const uint16_t* zr16 = reinterpret_cast<const uint16_t*>(s_zr + st_zr.shift);
+  const uint16_t* ow16 = reinterpret_cast<const uint16_t*>(s_ow + (HAS_OUT ? st_ow.shift : 0));
+#pragma unroll
+  for (int u = 0; u < kRowsPerStep; ++u) {
+    const int rl = r_first + u;
+    if (rl >= r_end) break;   // uniform across the wave
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      if (!gvalid[i]) continue;
+      const int g = (kw * GPL + i) * kWave + lane;
+      const float s = h2f(sc16[rl * G + g]);
+      const float z = h2f(zr16[rl * G + g]);
+      if constexpr (FMT == 4) {
+        acc = w4_group_dot(cw[u][i], xr[i], s, z, sx[i], acc);
+      } else {
+        float ac = 0.f;
+        const uint32_t wv[2] = {cw[u][i].x, cw[u][i].y};
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const uint32_t t = (wv[j] >> (2 * p + 8 * h)) & 0x00030003u;
+              ac = __builtin_amdgcn_fdot2(as_h2(w2_centroid_pair(t)),
+                                          as_h2(xr[i][8 * j + 4 * h + p]), ac, false);
+            }
+        acc = __builtin_fmaf(s, ac, acc);
+        acc = __builtin_fmaf(z, sx[i], acc);
+      }
+    }
+    if (HAS_OUT && do_out) {
+#pragma unroll
+      for (int t = 0; t < kOutRegs; ++t) {
+        const int j = (kw + a.wk * t) * kWave + lane;
+        if (t < T && j < a.n_out) acc = __builtin_fmaf(h2f(ow16[rl * a.n_out + j]), xo[t], acc);
+      }
+      for (int j = n_cap + kw * kWave + lane; j < a.n_out; j += jstride) {
+        const uint32_t c = (uint32_t)s_idx[j];
+        acc = __builtin_fmaf(h2f(ow16[rl * a.n_out + j]),
+                             c < (uint32_t)a.K ? h2f(a.x[c]) : 0.f, acc);
+      }
+    }
+    acc = row16_sum(acc);
+    if ((lane & 15) == 0) s_part[(rl * a.wk + kw) * 4 + (lane >> 4)] = acc;
+  }
+  __syncthreads();
+  for (int t = tid; t < rows_here; t += nthr) {
+    float sum = 0.f;
+    for (int k = 0; k < a.wk; ++k) {
+      const float* p = s_part + (t * a.wk + k) * 4;
+      sum += (p[0] + p[1]) + (p[2] + p[3]);
+    }
+    a.y[tile0 + t] = f2h(sum);
+  }
+}
+
+template <int FMT, int GPL, bool HAS_OUT>
+__global__ void __launch_bounds__(512) gemv_reg_kernel(GemvArgs a) {
+  typedef Fmt<FMT> F;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int G = a.K / kGroup;
+  const int RT = a.wr * a.rpw;
+  // LDS: outlier bitmask, later reused for the partial sums (every wave has
+  // read its mask words before the first partial is written)
   uint32_t* s_mask = reinterpret_cast<uint32_t*>(smem);                 // [G] outlier bits
   float* s_part = reinterpret_cast<float*>(smem);                       // [RT][wk][4]
-  float* s_sx = reinterpret_cast<float*>(smem + head);                  // [G]
-  u4v* s_xp = reinterpret_cast<u4v*>(smem + ((head + 4 * G + 15) & ~15));   // [G][4]
 
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -180,11 +495,10 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
     oraw[t] = HAS_OUT ? ld32(irs, oval[t] ? (uint32_t)j * 4u : kOob) : 0u;
   }
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.K * 2u);
-  constexpr int XS = XLDS ? kPrepSlots : GPL;
-  uint32_t xw[XS][16];
+  uint32_t xw[GPL][16];
 #pragma unroll
-  for (int i = 0; i < XS; ++i) {
-    const uint32_t g = XLDS ? (uint32_t)(tid + nthr * i) : (uint32_t)((kw * GPL + i) * kWave + lane);
+  for (int i = 0; i < GPL; ++i) {
+    const uint32_t g = (uint32_t)((kw * GPL + i) * kWave + lane);
     load_group_x(xrs, g < (uint32_t)G ? g * 64u : kOob, xw[i]);
   }
   const uint64_t row_bytes = (uint64_t)a.K / F::kRowBytesPerK;
@@ -202,32 +516,8 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
   for (int i = 0; i < GPL; ++i) gvalid[i] = (kw * GPL + i) * kWave + lane < G;
 
   RowBatch<FMT, GPL> b;
-#pragma unroll
-  for (int u = 0; u < kRowsPerStep; ++u) {
-    const bool rv = r_first + u < r_end;
-    const uint32_t rl = (uint32_t)(r_first + u);
-#pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      const uint32_t g = (uint32_t)((kw * GPL + i) * kWave + lane);
-      const bool ok = rv && gvalid[i];
-      const uint32_t co = ok ? rl * (uint32_t)row_bytes + g * F::kGroupBytes : kOob;
-      const uint32_t mo = ok ? (rl * (uint32_t)G + g) * 2u : kOob;
-      if constexpr (FMT == 4)
-        b.cw[u][i] = ld128(crs, co);
-      else
-        b.cw[u][i] = ld64(crs, co);
-      b.sv[u][i] = ld16(srs, mo);
-      b.zv[u][i] = ld16(zrs, mo);
-    }
-    if constexpr (HAS_OUT) {
-#pragma unroll
-      for (int t = 0; t < kOutRegs; ++t) {
-        const int j = (kw + a.wk * t) * kWave + lane;
-        const bool ok = rv && oval[t];
-        b.ow[u][t] = ld16(ors, ok ? (rl * (uint32_t)a.n_out + (uint32_t)j) * 2u : kOob);
-      }
-    }
-  }
+  load_rows<FMT, GPL, HAS_OUT>(b, crs, srs, zrs, ors, r_first, r_end, (uint32_t)row_bytes,
+                               (uint32_t)G, kw, lane, gvalid, oval, a.wk, a.n_out);
 
   // ---- (2) outlier bitmask in LDS (the background skips these columns)
   if constexpr (HAS_OUT) {
@@ -252,54 +542,15 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
   // ---- (4) activations, masked and paired as the decoder emits weights
   uint32_t xr[GPL][16];
   float sx[GPL];
-  if constexpr (XLDS) {
 #pragma unroll
-    for (int i = 0; i < XS; ++i) {
-      const int g = tid + nthr * i;
-      if (g < G) {
-        uint32_t pr[16];
-        float sum;
-        pair_group<FMT>(xw[i], HAS_OUT ? s_mask[g] : 0u, pr, sum);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) s_xp[g * 4 + v] = (u4v){pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]};
-        s_sx[g] = sum;
-      }
-    }
-    for (int g = tid + nthr * XS; g < G; g += nthr) {   // only when K > 64 * 512 * ...
-      uint32_t w2[16], pr[16];
-      float sum;
-      load_group_x(xrs, (uint32_t)g * 64u, w2);
-      pair_group<FMT>(w2, HAS_OUT ? s_mask[g] : 0u, pr, sum);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) s_xp[g * 4 + v] = (u4v){pr[4 * v], pr[4 * v + 1], pr[4 * v + 2], pr[4 * v + 3]};
-      s_sx[g] = sum;
-    }
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      const int g = (kw * GPL + i) * kWave + lane;
-      const int gg = gvalid[i] ? g : 0;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const u4v t = s_xp[gg * 4 + v];
-        xr[i][4 * v + 0] = t.x;
-        xr[i][4 * v + 1] = t.y;
-        xr[i][4 * v + 2] = t.z;
-        xr[i][4 * v + 3] = t.w;
-      }
-      sx[i] = s_sx[gg];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      const int g = (kw * GPL + i) * kWave + lane;
-      const uint32_t m = !gvalid[i] ? 0xFFFFFFFFu : (HAS_OUT ? s_mask[g] : 0u);
-      pair_group<FMT>(xw[i], m, xr[i], sx[i]);
-    }
+  for (int i = 0; i < GPL; ++i) {
+    const int g = (kw * GPL + i) * kWave + lane;
+    const uint32_t m = !gvalid[i] ? 0xFFFFFFFFu : (HAS_OUT ? s_mask[g] : 0u);
+    pair_group<FMT>(xw[i], m, xr[i], sx[i]);
   }
 
   // ---- (5) the rows (s_part aliases s_mask: wait until every wave has read its mask)
-  if constexpr (HAS_OUT && !XLDS) lds_barrier();
+  if constexpr (HAS_OUT) lds_barrier();
   {
 #pragma unroll
     for (int u = 0; u < kRowsPerStep; ++u) {
@@ -312,21 +563,7 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
         const float s = h2f(b.sv[u][i]);
         const float z = h2f(b.zv[u][i]);
         if constexpr (FMT == 4) {
-          float alo = 0.f, ahi = 0.f;
-          const uint32_t wv[4] = {b.cw[u][i].x, b.cw[u][i].y, b.cw[u][i].z, b.cw[u][i].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            uint32_t lo0, hi0, lo1, hi1;
-            w4_word_sub(wv[j], lo0, hi0, lo1, hi1);
-            alo = __builtin_amdgcn_fdot2(as_h2(lo0), as_h2(xr[i][4 * j + 0]), alo, false);
-            ahi = __builtin_amdgcn_fdot2(as_h2(hi0), as_h2(xr[i][4 * j + 1]), ahi, false);
-            alo = __builtin_amdgcn_fdot2(as_h2(lo1), as_h2(xr[i][4 * j + 2]), alo, false);
-            ahi = __builtin_amdgcn_fdot2(as_h2(hi1), as_h2(xr[i][4 * j + 3]), ahi, false);
-          }
-          // sum q x = 2^24 (alo + ahi / 16); then (sum q x - z sum x) s
-          float v = __builtin_fmaf(ahi, 0.0625f, alo) * 16777216.0f;
-          v = __builtin_fmaf(-z, sx[i], v);
-          acc = __builtin_fmaf(s, v, acc);
+          acc = w4_group_dot(b.cw[u][i], xr[i], s, z, sx[i], acc);
         } else {
           float ac = 0.f;
           const uint32_t wv[2] = {b.cw[u][i].x, b.cw[u][i].y};
@@ -372,9 +609,9 @@ __global__ void __launch_bounds__(512) gemv_kernel(GemvArgs a) {
 // ------------------------------------------------------------- launch plan
 
 struct GemvPlan {
-  int gpl, wk, wr, rpw, rt, blocks;
-  size_t lds, lds_reg;
-  bool xlds;
+  int gpl, wk, wr, rpw, rt, blocks, xc;
+  size_t lds;
+  bool lds_path;   // gemv_lds_kernel (x and the W2 table in LDS) or gemv_reg_kernel
 };
 
 static GemvPlan plan_gemv(int64_t N, int64_t K, int64_t n_out) {
@@ -394,22 +631,22 @@ static GemvPlan plan_gemv(int64_t N, int64_t K, int64_t n_out) {
     }
   }
   p.wr = p.wk >= 4 ? 1 : 4 / p.wk;
-  // One batch of at most 4 rows per wave; fewer rows per wave when that is
-  // what it takes to have ~1024 workgroups in flight.
   p.rpw = kRowsPerStep;
-  while (p.rpw > 1 && (N + (int64_t)p.wr * p.rpw - 1) / ((int64_t)p.wr * p.rpw) < 1024) p.rpw /= 2;
   if (const char* e = getenv("WQ_GEMV_ROWS_PER_WAVE")) {
     const int v = atoi(e);
     if (v >= 1 && v <= kRowsPerStep) p.rpw = v;
   }
   p.rt = p.wr * p.rpw;
   p.blocks = (int)((N + p.rt - 1) / p.rt);
-  const size_t head = std::max((size_t)4 * G, (size_t)16 * p.rt * p.wk);
-  p.lds_reg = head;
-  p.lds = ((head + (size_t)4 * G + 15) & ~(size_t)15) + (size_t)64 * G;
-  p.xlds = p.lds <= kMaxLdsBytes;
-  if (const char* e = getenv("WQ_GEMV_XLDS")) p.xlds = p.xlds && atoi(e) != 0;
-  if (!p.xlds) p.lds = p.lds_reg;
+  const size_t part = (size_t)16 * p.rt * p.wk;
+  p.lds = gemv_lds_bytes((int)K, p.rt, p.wk, (int)n_out, n_out > 0);
+  p.lds_path = p.lds <= kMaxLdsBytes;
+  if (const char* e = getenv("WQ_GEMV_LDS_PATH")) p.lds_path = p.lds_path && atoi(e) != 0;
+  if (!p.lds_path) p.lds = std::max((size_t)4 * G, part);
+  // 16-byte chunks of x per thread, loaded before the weights
+  const int nthr = p.wk * p.wr * kWave;
+  const int64_t chunks = (K / 8 + nthr - 1) / nthr;
+  p.xc = chunks <= 2 ? 2 : chunks <= 4 ? 4 : 8;
   return p;
 }
 
@@ -419,23 +656,28 @@ static int launch_gemv(const GemvArgs& a0, hipStream_t stream, const char* who) 
   const GemvPlan p = plan_gemv(a.N, a.K, a.n_out);
   if (p.gpl == 0) return wq::fail(WQ_ERR_UNSUPPORTED, "%s: K=%d not supported", who, a.K);
   if (p.lds > kMaxLdsBytes)
-    return wq::fail(WQ_ERR_UNSUPPORTED, "%s: %zu bytes of LDS needed (n_out too large)", who, p.lds);
+    return wq::fail(WQ_ERR_UNSUPPORTED, "%s: %zu bytes of LDS needed", who, p.lds);
   a.wk = p.wk;
   a.wr = p.wr;
   a.rpw = p.rpw;
   const dim3 grid(p.blocks), block(p.wk * p.wr * kWave);
   const bool out = a.n_out > 0;
-#define WQ_GEMV_CASE(G_, O_, X_)                                                           \
-  if (p.gpl == G_ && out == O_ && p.xlds == X_) {                                          \
-    hipLaunchKernelGGL((gemv_kernel<FMT, G_, O_, X_>), grid, block, p.lds, stream, a);     \
-    return check_launch(who);                                                              \
+#define WQ_GEMV_CASE(G_, O_)                                                                 \
+  if (p.gpl == G_ && out == O_) {                                                            \
+    if (!p.lds_path)                                                                         \
+      hipLaunchKernelGGL((gemv_reg_kernel<FMT, G_, O_>), grid, block, p.lds, stream, a);     \
+    else if (p.xc == 2)                                                                      \
+      hipLaunchKernelGGL((gemv_lds_kernel<FMT, G_, O_, 2>), grid, block, p.lds, stream, a);  \
+    else if (p.xc == 4)                                                                      \
+      hipLaunchKernelGGL((gemv_lds_kernel<FMT, G_, O_, 4>), grid, block, p.lds, stream, a);  \
+    else                                                                                     \
+      hipLaunchKernelGGL((gemv_lds_kernel<FMT, G_, O_, 8>), grid, block, p.lds, stream, a);  \
+    return check_launch(who);                                                                \
   }
-  WQ_GEMV_CASE(1, false, true) WQ_GEMV_CASE(1, true, true) WQ_GEMV_CASE(1, false, false)
-  WQ_GEMV_CASE(1, true, false) WQ_GEMV_CASE(2, false, true) WQ_GEMV_CASE(2, true, true)
-  WQ_GEMV_CASE(2, false, false) WQ_GEMV_CASE(2, true, false) WQ_GEMV_CASE(4, false, true)
-  WQ_GEMV_CASE(4, true, true) WQ_GEMV_CASE(4, false, false) WQ_GEMV_CASE(4, true, false)
+  WQ_GEMV_CASE(1, false) WQ_GEMV_CASE(1, true) WQ_GEMV_CASE(2, false) WQ_GEMV_CASE(2, true)
+  WQ_GEMV_CASE(4, false) WQ_GEMV_CASE(4, true)
 #undef WQ_GEMV_CASE
-  return check_launch(who);
+  return wq::fail(WQ_ERR_UNSUPPORTED, "%s: no kernel for this shape", who);
 }
 
 }  // namespace wqd
