@@ -8,9 +8,18 @@
 
 namespace wqd {
 
-// LDS one workgroup may request (gfx950 has 160 KB per CU; we stay within the
-// 64 KB that every launch may take without attributes).
-constexpr size_t kMaxLdsBytes = 64 * 1024;
+// LDS one workgroup may request: gfx950 gives a workgroup up to the whole
+// 160 KB of a CU (launches above 64 KB raise the kernel's dynamic-LDS limit
+// first, see allow_lds).
+constexpr size_t kMaxLdsBytes = 160 * 1024;
+constexpr size_t kDefaultLdsBytes = 64 * 1024;
+
+// Raises a kernel's dynamic-LDS limit when a launch needs more than 64 KB.
+inline bool allow_lds(const void* kernel, size_t bytes) {
+  if (bytes <= kDefaultLdsBytes) return true;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) ==
+         hipSuccess;
+}
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 

@@ -245,6 +245,9 @@ extern "C" int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales,
     return wq::fail(WQ_ERR_UNSUPPORTED, "%s: %zu bytes of LDS needed (n_out too large)", who, lds);
   const dim3 grid((unsigned)((N + kGemmRows - 1) / kGemmRows)), block(kGemmWaves * 64);
   hipStream_t s = (hipStream_t)stream;
+  const void* k = fmt == WQ_FMT_W4 ? reinterpret_cast<const void*>(&gemm_kernel<4>)
+                                   : reinterpret_cast<const void*>(&gemm_kernel<2>);
+  if (!allow_lds(k, lds)) return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit", who);
   if (fmt == WQ_FMT_W4)
     hipLaunchKernelGGL(gemm_kernel<4>, grid, block, lds, s, a);
   else

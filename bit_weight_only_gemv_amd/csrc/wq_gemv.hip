@@ -172,9 +172,12 @@ struct Stage {
 __device__ __forceinline__ size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
 // Bytes of LDS the main kernel needs (host and device agree on this layout).
-__host__ __device__ inline size_t gemv_lds_bytes(int K, int RT, int wk, int n_out, bool has_out) {
+constexpr int kLutCopies = 32;   // W2 nibble table: 16 entries x 32 lane-sliced copies
+__host__ __device__ inline size_t gemv_lds_bytes(int K, int RT, int wk, int n_out, bool has_out,
+                                                 int fmt) {
   const size_t G = (size_t)K / kGroup;
   size_t off = ((size_t)16 * RT * wk + 15) & ~(size_t)15;              // partial sums
+  if (fmt == 2) off += (size_t)16 * kLutCopies * 4;                     // W2 centroid table
   off += ((size_t)RT * G * 2 + 16 + 15) & ~(size_t)15;                 // scales
   off += ((size_t)RT * G * 2 + 16 + 15) & ~(size_t)15;                 // zeros
   if (has_out) {
@@ -270,6 +273,8 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
 
   size_t off = align16((size_t)16 * RT * a.wk);
   float* s_part = reinterpret_cast<float*>(smem);
+  uint32_t* s_lut = reinterpret_cast<uint32_t*>(smem + off);   // W2: [16][kLutCopies]
+  if (FMT == 2) off += (size_t)16 * kLutCopies * 4;
   unsigned char* s_sc = smem + off;
   off += align16((size_t)RT * G * 2 + 16);
   unsigned char* s_zr = smem + off;
@@ -329,6 +334,14 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
   st_sc.commit(s_sc, tid, nthr);
   st_zr.commit(s_zr, tid, nthr);
   if constexpr (HAS_OUT) st_ow.commit(s_ow, tid, nthr);
+  if constexpr (FMT == 2) {
+    // entry e = two consecutive codes (e & 3, e >> 2) -> their two FP16 centroids;
+    // lane l reads copy l % 32, so a 32-lane half of the wave hits 32 banks
+    for (int i = tid; i < 16 * kLutCopies; i += nthr) {
+      const uint32_t e = (uint32_t)i / kLutCopies;
+      s_lut[i] = w2_centroid_pair((e & 3u) | ((e >> 2) << 16));
+    }
+  }
   lds_barrier();
 
   // ---- (3) outlier activations, then the outlier columns of x zeroed
@@ -378,19 +391,12 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
         xr[i][4 * j + 3] = __builtin_amdgcn_perm(xw[2 * j + 9], xw[2 * j + 8], 0x07060302u);
       }
     } else {
-      // (k, k + 8) for k = 16 j + 4 h + p
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int k = 16 * j + 4 * h + p;
-            xr[i][8 * j + 4 * h + p] =
-                __builtin_amdgcn_perm(xw[(k >> 1) + 4], xw[k >> 1], (k & 1) ? 0x07060302u : 0x05040100u);
-          }
+      for (int m = 0; m < 16; ++m) xr[i][m] = xw[m];   // natural pairs (2m, 2m + 1)
     }
   }
+  const uint32_t lut_lane = (uint32_t)(lane & (kLutCopies - 1)) * 4u;
+  const unsigned char* lut8 = reinterpret_cast<const unsigned char*>(s_lut);
 
   // ---- (5) the rows
   const uint16_t* sc16 = reinterpret_cast<const uint16_t*>(s_sc + st_sc.shift);
@@ -410,18 +416,17 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
       if constexpr (FMT == 4) {
         acc = w4_group_dot(cw[u][i], xr[i], s, z, sx[i], acc);
       } else {
+        // nibble n of code word j = codes (16 j + 2 n, 16 j + 2 n + 1)
         float ac = 0.f;
         const uint32_t wv[2] = {cw[u][i].x, cw[u][i].y};
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              const uint32_t t = (wv[j] >> (2 * p + 8 * h)) & 0x00030003u;
-              ac = __builtin_amdgcn_fdot2(as_h2(w2_centroid_pair(t)),
-                                          as_h2(xr[i][8 * j + 4 * h + p]), ac, false);
-            }
+          for (int n = 0; n < 8; ++n) {
+            const uint32_t e = (wv[j] >> (4 * n)) & 0xFu;
+            const uint32_t c2 = *reinterpret_cast<const uint32_t*>(lut8 + ((e << 7) | lut_lane));
+            ac = __builtin_amdgcn_fdot2(as_h2(c2), as_h2(xr[i][8 * j + n]), ac, false);
+          }
         acc = __builtin_fmaf(s, ac, acc);
         acc = __builtin_fmaf(z, sx[i], acc);
       }
@@ -614,7 +619,7 @@ struct GemvPlan {
   bool lds_path;   // gemv_lds_kernel (x and the W2 table in LDS) or gemv_reg_kernel
 };
 
-static GemvPlan plan_gemv(int64_t N, int64_t K, int64_t n_out) {
+static GemvPlan plan_gemv(int fmt, int64_t N, int64_t K, int64_t n_out) {
   const int G = (int)(K / kGroup);
   GemvPlan p{};
   // Fewest idle lanes, at most 8 K-waves; on a tie prefer 2 groups per lane,
@@ -639,7 +644,7 @@ static GemvPlan plan_gemv(int64_t N, int64_t K, int64_t n_out) {
   p.rt = p.wr * p.rpw;
   p.blocks = (int)((N + p.rt - 1) / p.rt);
   const size_t part = (size_t)16 * p.rt * p.wk;
-  p.lds = gemv_lds_bytes((int)K, p.rt, p.wk, (int)n_out, n_out > 0);
+  p.lds = gemv_lds_bytes((int)K, p.rt, p.wk, (int)n_out, n_out > 0, fmt);
   p.lds_path = p.lds <= kMaxLdsBytes;
   if (const char* e = getenv("WQ_GEMV_LDS_PATH")) p.lds_path = p.lds_path && atoi(e) != 0;
   if (!p.lds_path) p.lds = std::max((size_t)4 * G, part);
@@ -653,7 +658,7 @@ static GemvPlan plan_gemv(int64_t N, int64_t K, int64_t n_out) {
 template <int FMT>
 static int launch_gemv(const GemvArgs& a0, hipStream_t stream, const char* who) {
   GemvArgs a = a0;
-  const GemvPlan p = plan_gemv(a.N, a.K, a.n_out);
+  const GemvPlan p = plan_gemv(FMT, a.N, a.K, a.n_out);
   if (p.gpl == 0) return wq::fail(WQ_ERR_UNSUPPORTED, "%s: K=%d not supported", who, a.K);
   if (p.lds > kMaxLdsBytes)
     return wq::fail(WQ_ERR_UNSUPPORTED, "%s: %zu bytes of LDS needed", who, p.lds);
@@ -662,21 +667,28 @@ static int launch_gemv(const GemvArgs& a0, hipStream_t stream, const char* who) 
   a.rpw = p.rpw;
   const dim3 grid(p.blocks), block(p.wk * p.wr * kWave);
   const bool out = a.n_out > 0;
+#define WQ_GEMV_LAUNCH(KERNEL)                                                                \
+  do {                                                                                       \
+    if (!allow_lds(reinterpret_cast<const void*>(&KERNEL), p.lds))                          \
+      return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds); \
+    hipLaunchKernelGGL(KERNEL, grid, block, p.lds, stream, a);                               \
+  } while (0)
 #define WQ_GEMV_CASE(G_, O_)                                                                 \
   if (p.gpl == G_ && out == O_) {                                                            \
     if (!p.lds_path)                                                                         \
-      hipLaunchKernelGGL((gemv_reg_kernel<FMT, G_, O_>), grid, block, p.lds, stream, a);     \
+      WQ_GEMV_LAUNCH((gemv_reg_kernel<FMT, G_, O_>));                                        \
     else if (p.xc == 2)                                                                      \
-      hipLaunchKernelGGL((gemv_lds_kernel<FMT, G_, O_, 2>), grid, block, p.lds, stream, a);  \
+      WQ_GEMV_LAUNCH((gemv_lds_kernel<FMT, G_, O_, 2>));                                     \
     else if (p.xc == 4)                                                                      \
-      hipLaunchKernelGGL((gemv_lds_kernel<FMT, G_, O_, 4>), grid, block, p.lds, stream, a);  \
+      WQ_GEMV_LAUNCH((gemv_lds_kernel<FMT, G_, O_, 4>));                                     \
     else                                                                                     \
-      hipLaunchKernelGGL((gemv_lds_kernel<FMT, G_, O_, 8>), grid, block, p.lds, stream, a);  \
+      WQ_GEMV_LAUNCH((gemv_lds_kernel<FMT, G_, O_, 8>));                                     \
     return check_launch(who);                                                                \
   }
   WQ_GEMV_CASE(1, false) WQ_GEMV_CASE(1, true) WQ_GEMV_CASE(2, false) WQ_GEMV_CASE(2, true)
   WQ_GEMV_CASE(4, false) WQ_GEMV_CASE(4, true)
 #undef WQ_GEMV_CASE
+#undef WQ_GEMV_LAUNCH
   return wq::fail(WQ_ERR_UNSUPPORTED, "%s: no kernel for this shape", who);
 }
 
