@@ -172,12 +172,12 @@ struct Stage {
 __device__ __forceinline__ size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
 // Bytes of LDS the main kernel needs (host and device agree on this layout).
-constexpr int kLutCopies = 32;   // W2 nibble table: 16 entries x 32 lane-sliced copies
+constexpr int kLutCopies = 4;   // W2 byte table: 256 entries x 4 lane-sliced copies
 __host__ __device__ inline size_t gemv_lds_bytes(int K, int RT, int wk, int n_out, bool has_out,
                                                  int fmt) {
   const size_t G = (size_t)K / kGroup;
   size_t off = ((size_t)16 * RT * wk + 15) & ~(size_t)15;              // partial sums
-  if (fmt == 2) off += (size_t)16 * kLutCopies * 4;                     // W2 centroid table
+  if (fmt == 2) off += (size_t)256 * kLutCopies * 8;                    // W2 centroid table
   off += ((size_t)RT * G * 2 + 16 + 15) & ~(size_t)15;                 // scales
   off += ((size_t)RT * G * 2 + 16 + 15) & ~(size_t)15;                 // zeros
   if (has_out) {
@@ -243,6 +243,19 @@ __device__ __forceinline__ float w4_group_dot(const u4v& cw, const uint32_t (&xr
   return __builtin_fmaf(s, v, acc);
 }
 
+// Group g of slot i of lane `lane` in K-wave kw.  W4 (and W2 with one group
+// per lane): slot i covers 64 consecutive groups, one per lane, so a wave's
+// load of a slot is one contiguous stretch of the row.  W2 with an even count:
+// a lane owns GPL consecutive groups, so two W2 groups (16 bytes) are one
+// 16-byte load.
+template <int FMT, int GPL>
+__device__ __forceinline__ int group_of(int kw, int i, int lane) {
+  if constexpr (FMT == 2 && GPL % 2 == 0)
+    return kw * GPL * kWave + GPL * lane + i;
+  else
+    return (kw * GPL + i) * kWave + lane;
+}
+
 // Main kernel.  Per workgroup (RT rows): the scales, zeros and outlier
 // weights of its rows, the outlier indices and x are each one contiguous
 // range and are staged into LDS with 16-byte loads by the whole workgroup;
@@ -273,8 +286,8 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
 
   size_t off = align16((size_t)16 * RT * a.wk);
   float* s_part = reinterpret_cast<float*>(smem);
-  uint32_t* s_lut = reinterpret_cast<uint32_t*>(smem + off);   // W2: [16][kLutCopies]
-  if (FMT == 2) off += (size_t)16 * kLutCopies * 4;
+  u2* s_lut = reinterpret_cast<u2*>(smem + off);   // W2: [256][kLutCopies]
+  if (FMT == 2) off += (size_t)256 * kLutCopies * 8;
   unsigned char* s_sc = smem + off;
   off += align16((size_t)RT * G * 2 + 16);
   unsigned char* s_zr = smem + off;
@@ -307,19 +320,31 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
       make_rsrc(a.codes + (uint64_t)tile0 * row_bytes, clamp_bytes((uint64_t)rows_here * row_bytes));
   bool gvalid[GPL];
 #pragma unroll
-  for (int i = 0; i < GPL; ++i) gvalid[i] = (kw * GPL + i) * kWave + lane < G;
+  for (int i = 0; i < GPL; ++i) gvalid[i] = group_of<FMT, GPL>(kw, i, lane) < G;
   typename F::Codes cw[kRowsPerStep][GPL];
 #pragma unroll
   for (int u = 0; u < kRowsPerStep; ++u) {
     const bool rv = r_first + u < r_end;
+    const uint32_t rb = (uint32_t)(r_first + u) * (uint32_t)row_bytes;
+    if constexpr (FMT == 2 && GPL % 2 == 0) {
 #pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      const uint32_t g = (uint32_t)((kw * GPL + i) * kWave + lane);
-      const uint32_t co = (rv && gvalid[i]) ? (uint32_t)(r_first + u) * (uint32_t)row_bytes + g * F::kGroupBytes : kOob;
-      if constexpr (FMT == 4)
-        cw[u][i] = ld128(crs, co);
-      else
-        cw[u][i] = ld64(crs, co);
+      for (int i = 0; i < GPL; i += 2) {
+        const uint32_t g = (uint32_t)group_of<FMT, GPL>(kw, i, lane);
+        // G is even here (K % 64 == 0), so both groups of the pair are valid or neither
+        const u4v v = ld128(crs, (rv && gvalid[i]) ? rb + g * 8u : kOob);
+        cw[u][i] = (u2){v.x, v.y};
+        cw[u][i + 1] = (u2){v.z, v.w};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < GPL; ++i) {
+        const uint32_t g = (uint32_t)group_of<FMT, GPL>(kw, i, lane);
+        const uint32_t co = (rv && gvalid[i]) ? rb + g * F::kGroupBytes : kOob;
+        if constexpr (FMT == 4)
+          cw[u][i] = ld128(crs, co);
+        else
+          cw[u][i] = ld64(crs, co);
+      }
     }
   }
 
@@ -335,11 +360,12 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
   st_zr.commit(s_zr, tid, nthr);
   if constexpr (HAS_OUT) st_ow.commit(s_ow, tid, nthr);
   if constexpr (FMT == 2) {
-    // entry e = two consecutive codes (e & 3, e >> 2) -> their two FP16 centroids;
-    // lane l reads copy l % 32, so a 32-lane half of the wave hits 32 banks
-    for (int i = tid; i < 16 * kLutCopies; i += nthr) {
+    // entry e = one code byte (four codes) -> their four FP16 centroids; lane l
+    // reads copy l % kLutCopies, which spreads a wave's reads over more banks
+    for (int i = tid; i < 256 * kLutCopies; i += nthr) {
       const uint32_t e = (uint32_t)i / kLutCopies;
-      s_lut[i] = w2_centroid_pair((e & 3u) | ((e >> 2) << 16));
+      s_lut[i] = (u2){w2_centroid_pair((e & 3u) | (((e >> 2) & 3u) << 16)),
+                      w2_centroid_pair(((e >> 4) & 3u) | ((e >> 6) << 16))};
     }
   }
   lds_barrier();
@@ -367,7 +393,7 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
   const uint32_t one2 = 0x3C003C00u;   // FP16 (1, 1)
 #pragma unroll
   for (int i = 0; i < GPL; ++i) {
-    const int g = gvalid[i] ? (kw * GPL + i) * kWave + lane : 0;
+    const int g = gvalid[i] ? group_of<FMT, GPL>(kw, i, lane) : 0;
     uint32_t xw[16];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -395,7 +421,7 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
       for (int m = 0; m < 16; ++m) xr[i][m] = xw[m];   // natural pairs (2m, 2m + 1)
     }
   }
-  const uint32_t lut_lane = (uint32_t)(lane & (kLutCopies - 1)) * 4u;
+  const uint32_t lut_lane = (uint32_t)(lane & (kLutCopies - 1)) * 8u;
   const unsigned char* lut8 = reinterpret_cast<const unsigned char*>(s_lut);
 
   // ---- (5) the rows
@@ -410,22 +436,23 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
       if (!gvalid[i]) continue;
-      const int g = (kw * GPL + i) * kWave + lane;
+      const int g = group_of<FMT, GPL>(kw, i, lane);
       const float s = h2f(sc16[rl * G + g]);
       const float z = h2f(zr16[rl * G + g]);
       if constexpr (FMT == 4) {
         acc = w4_group_dot(cw[u][i], xr[i], s, z, sx[i], acc);
       } else {
-        // nibble n of code word j = codes (16 j + 2 n, 16 j + 2 n + 1)
+        // byte b of the group = codes 4b .. 4b + 3 = activation words 2b, 2b + 1
         float ac = 0.f;
         const uint32_t wv[2] = {cw[u][i].x, cw[u][i].y};
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int n = 0; n < 8; ++n) {
-            const uint32_t e = (wv[j] >> (4 * n)) & 0xFu;
-            const uint32_t c2 = *reinterpret_cast<const uint32_t*>(lut8 + ((e << 7) | lut_lane));
-            ac = __builtin_amdgcn_fdot2(as_h2(c2), as_h2(xr[i][8 * j + n]), ac, false);
+          for (int by = 0; by < 4; ++by) {
+            const uint32_t e = (wv[j] >> (8 * by)) & 0xFFu;
+            const u2 c4 = *reinterpret_cast<const u2*>(lut8 + e * (kLutCopies * 8u) + lut_lane);
+            ac = __builtin_amdgcn_fdot2(as_h2(c4.x), as_h2(xr[i][8 * j + 2 * by]), ac, false);
+            ac = __builtin_amdgcn_fdot2(as_h2(c4.y), as_h2(xr[i][8 * j + 2 * by + 1]), ac, false);
           }
         acc = __builtin_fmaf(s, ac, acc);
         acc = __builtin_fmaf(z, sx[i], acc);
@@ -646,6 +673,8 @@ static GemvPlan plan_gemv(int fmt, int64_t N, int64_t K, int64_t n_out) {
   const size_t part = (size_t)16 * p.rt * p.wk;
   p.lds = gemv_lds_bytes((int)K, p.rt, p.wk, (int)n_out, n_out > 0, fmt);
   p.lds_path = p.lds <= kMaxLdsBytes;
+  // the W2 pairing of consecutive groups needs an even group count
+  if (fmt == 2 && p.gpl % 2 == 0 && G % 2 != 0) p.lds_path = false;
   if (const char* e = getenv("WQ_GEMV_LDS_PATH")) p.lds_path = p.lds_path && atoi(e) != 0;
   if (!p.lds_path) p.lds = std::max((size_t)4 * G, part);
   // 16-byte chunks of x per thread, loaded before the weights
