@@ -1,29 +1,35 @@
 #!/usr/bin/env python3
 """Benchmark of the fused low-bit weight-only GEMV on one MI355X.
 
-Default workload (one JSON line): M = 1 W2 GEMV of a 14336 x 4096 layer
-(Llama-3-8B MLP gate/up shape), Lloyd-Max 2-bit codes with OLS group-32
-scale/zero and 143 (3.5%) FP16 outlier columns, x FP16 with 1% of channels
-x100.  One step = one launch of the whole fused path (stream codes, scales,
-zeros and the outlier slab; decode; multiply; reduce; add outliers; store y).
+Default workload (one JSON line): the M = 1 W2 GEMV of a 14336 x 4096 layer
+(Llama-3-8B MLP gate/up shape): Lloyd-Max 2-bit codes with OLS group-32
+scale/zero, 143 (3.5%) FP16 outlier columns, x FP16 with 1% of channels x100.
+One step = one launch of the whole fused path (stream codes, scales, zeros and
+the outlier slab; decode; multiply; reduce; add the outlier columns; store y).
 
-Weights are rotated through >= 512 MB of distinct device copies so that
-neither the 256 MB Infinity Cache nor the L2s serve repeats; inputs are
-resident in HBM before the timed region.  Timing: hipEvents on the stream
-the kernels run on, around exactly --steps launches, bracketed by device
-synchronization.
+Measurement:
+* weights are rotated through >= 512 MB of distinct device copies so neither
+  the 256 MB Infinity Cache nor the L2s serve repeats; inputs sit in HBM
+  before the timed region;
+* the timed launches are captured once into a HIP graph (the kernels are
+  launched through the library's C ABI during capture) and replayed; hipEvents
+  on the replay stream bracket exactly --steps launches, with device
+  synchronization on both sides (--eager times Python-side launches instead,
+  which measures the interpreter, not the GPU);
+* value = algorithmic bytes per step (codes + FP16 scales + FP16 zeros + FP16
+  outlier slab + int32 indices + x + y) / time per step.
 
-``value`` is GB/s of algorithmic bytes (codes + FP16 scales + FP16 zeros +
-FP16 outlier slab + int32 indices + x + y) per second of wall time per step.
-
-Other workloads (``--workload``): w4_4096 (W4 4096x4096), sweep (Llama-3-8B
-shaped decode: 225 W4 GEMVs replayed as one HIP graph, tokens/s), batched
-(W4 small-M MFMA path), w2_70b (W2 + outliers 28672x8192 / 8192x28672).
+Other workloads (--workload): w4_4096 (W4 4096x4096), sweep (Llama-3-8B-shaped
+decode: 225 W4 GEMVs per step in one graph -> tokens/s), batched (W4 small-M
+matrix-core path vs M repeated GEMVs), w2_70b (W2 + outliers at 28672x8192 and
+8192x28672, M = 1 and 8), read / copy (plain streaming kernels: the attainable
+HBM rate and the byte-counter calibration).
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,9 +37,12 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "M=1 dequant-GEMV effective HBM GB/s (% of MI355X peak); eq. tokens/s"
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["wq_gemv.hip", "wq_common.cuh", "wq_device.h"]
 
 
 def _parse():
@@ -42,12 +51,20 @@ def _parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="w2_14336",
-                   choices=["w2_14336", "w4_4096", "sweep", "batched", "w2_70b", "read"])
-    p.add_argument("--read-bytes", type=int, default=26157628,
-                   help="bytes per launch of the read-probe workload")
+                   choices=["w2_14336", "w4_4096", "sweep", "batched", "w2_70b", "read", "copy"])
+    p.add_argument("--bytes", type=int, default=26157628,
+                   help="bytes per launch of the read / copy workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--graph", action="store_true", help="replay the timed launches as a HIP graph")
+    p.add_argument("--eager", action="store_true", help="time Python-side launches, no graph")
     return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_weight_only_gemv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def sweep_bytes_per_token(fmt: int, ratio: float) -> int:
@@ -62,48 +79,86 @@ def sweep_bytes_per_token(fmt: int, ratio: float) -> int:
     return tot
 
 
-def main():
-    a = _parse()
-    if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path is a "
-              "single-GPU kernel and multi-GPU sharding is not built.", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import synthetic
+class Timer:
+    """Times `steps` calls of fn(i): captured once into a HIP graph and replayed
+    (or launched eagerly), bracketed by events on the launching stream."""
+
+    def __init__(self, torch, eager=False):
+        self.torch, self.eager = torch, eager
+
+    def __call__(self, fn, steps, warmup, reps=3):
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        graph = None
+        if not self.eager:
+            graph = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(stream)
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(graph, stream=s):
+                    for i in range(steps):
+                        fn(i)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            if graph is not None:
+                graph.replay()
+            else:
+                for i in range(steps):
+                    fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            best = ms if best is None else min(best, ms)
+        return best
+
+
+def clone_layer(DeviceLayer, base):
+    c = DeviceLayer.__new__(DeviceLayer)
+    c.__dict__.update(base.__dict__)
+    c.codes, c.scales, c.zeros = base.codes.clone(), base.scales.clone(), base.zeros.clone()
+    if base.n_out:
+        c.idx, c.wout = base.idx.clone(), base.wout.clone()
+    return c
+
+
+def rotated(DeviceLayer, base, nbytes):
+    ncopy = max(1, -(-ROTATE_BYTES // nbytes))
+    return [base] + [clone_layer(DeviceLayer, base) for _ in range(ncopy - 1)]
+
+
+def traffic_for(label):
+    """HBM bytes per launch from stored counter runs, if they were taken on the
+    current kernel sources (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(label)
+    if not e or e.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def gemv_workload(a, torch, L, label, timer):
     import bit_weight_only_gemv_amd as B
     from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
-
-    B.load()
-    torch.cuda.init()
-    dev = torch.cuda.get_device_name(0)
-    stream = torch.cuda.current_stream()
-
-    if a.workload == "read":
-        return read_probe(a, torch, B)
-    if a.workload == "w2_14336":
-        L = synthetic.config2()
-        label = "w2_14336x4096_outliers143_m1"
-    elif a.workload == "w4_4096":
-        L = synthetic.config1()
-        label = "w4_4096x4096_m1"
-    else:
-        print("workload not implemented yet", file=sys.stderr)
-        sys.exit(3)
-
     t0 = time.time()
     hl = pack_host(L.fmt, L.W, L.profile, L.ratio)
     pack_s = time.time() - t0
     base = DeviceLayer(hl)
     nbytes = base.nbytes(1)
-    ncopy = max(1, -(-ROTATE_BYTES // nbytes))
-    layers = [base]
-    for _ in range(ncopy - 1):
-        c = DeviceLayer.__new__(DeviceLayer)
-        c.__dict__.update(base.__dict__)
-        c.codes, c.scales, c.zeros = base.codes.clone(), base.scales.clone(), base.zeros.clone()
-        if base.n_out:
-            c.idx, c.wout = base.idx.clone(), base.wout.clone()
-        layers.append(c)
+    layers = rotated(DeviceLayer, base, nbytes)
+    ncopy = len(layers)
     x = torch.from_numpy(L.x.reshape(-1).view(np.int16)).cuda()
     ys = [torch.empty(base.N, dtype=torch.int16, device="cuda") for _ in range(ncopy)]
     torch.cuda.synchronize()
@@ -111,39 +166,10 @@ def main():
     def step(i):
         layers[i % ncopy].gemv(x, ys[i % ncopy])
 
-    for i in range(a.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    graph = None
-    if a.graph:
-        graph = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(stream)
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(graph, stream=s):
-                for i in range(a.steps):
-                    step(i)
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(a.steps):
-            step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / a.steps
-    gbs = nbytes / (ms_step * 1e-3) / 1e9
-
+    ms = timer(step, a.steps, a.warmup)
+    gbs = nbytes / (ms * 1e-3) / 1e9
     bpt = sweep_bytes_per_token(L.fmt, L.ratio)
+    traffic = traffic_for(label)
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -151,69 +177,141 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "data": "synthetic (seeded Gaussian weights and activations, no checkpoint)",
+        "data": "synthetic (seeded Gaussian weights and activations; no checkpoint)",
         "config": {"workload": label, "N": base.N, "K": base.K, "M": 1, "n_out": base.n_out,
                    "format": f"W{L.fmt} group-32", "accumulate": "f32",
                    "bytes_per_step": nbytes, "rotated_copies": ncopy,
-                   "timing": "hip graph replay" if graph is not None else "eager launches"},
+                   "timing": "eager launches" if a.eager else "hip graph replay"},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "eq_tokens_per_s": round(gbs * 1e9 / bpt, 1),
         "eq_tokens_basis_bytes_per_token": bpt,
-        "device": dev,
         "host_pack_s": round(pack_s, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
     }
-
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(L, nbytes)
-    print(json.dumps(out), flush=True)
+    return out
 
 
-def read_probe(a, torch, B):
-    """Attainable HBM read rate: a plain streaming-read kernel over rotated
-    buffers of the given size (no decode, no arithmetic)."""
-    nb = (a.read_bytes + 15) // 16 * 16
-    ncopy = max(1, -(-ROTATE_BYTES // nb))
-    bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
-    for b in bufs:
-        b.fill_(1)
-    sink = torch.empty(B.wq_read_probe_sink_words(nb), dtype=torch.int32, device="cuda")
-    stream = torch.cuda.current_stream()
+def sweep_workload(a, torch, timer):
+    """225 W4 GEMVs of a Llama-3-8B-shaped decode step, one graph per token."""
+    import synthetic
+    from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
+    shapes = synthetic.config3_shapes()
+    proto = {}
+    for (layer, proj, name, N, K) in shapes:
+        key = (name if name in ("lm_head",) else {"q": "sq", "o": "sq", "k": "kv", "v": "kv",
+                                                    "gate": "mlp", "up": "mlp", "down": "down"}[name])
+        if key not in proto:
+            L = synthetic.config3_layer(layer, proj, N, K, name)
+            proto[key] = DeviceLayer(pack_host(4, L.W))
+    layers, xs, ys = [], [], []
+    total = 0
+    for (layer, proj, name, N, K) in shapes:
+        key = name if name == "lm_head" else {"q": "sq", "o": "sq", "k": "kv", "v": "kv",
+                                              "gate": "mlp", "up": "mlp", "down": "down"}[name]
+        d = clone_layer(DeviceLayer, proto[key]) if key != "lm_head" else proto[key]
+        layers.append(d)
+        x = synthetic.gaussian_x_fp16(1, K, 3, layer, proj)
+        xs.append(torch.from_numpy(x.reshape(-1).view(np.int16)).cuda())
+        ys.append(torch.empty(N, dtype=torch.int16, device="cuda"))
+        total += d.nbytes(1)
+    torch.cuda.synchronize()
 
     def step(i):
-        B.wq_read_probe(bufs[i % ncopy], nb, sink)
+        for d, x, y in zip(layers, xs, ys):
+            d.gemv(x, y)
 
-    for i in range(a.warmup):
-        step(i)
-    graph = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(stream)
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(graph, stream=s):
-            for i in range(a.steps):
-                step(i)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    graph.replay()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / a.steps
-    print(json.dumps({"workload": "read_probe", "bytes": nb, "copies": ncopy, "ms_per_step": ms,
-                      "GB/s": round(nb / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    steps = max(1, min(a.steps, 50))
+    ms = timer(step, steps, min(a.warmup, 5))
+    gbs = total / (ms * 1e-3) / 1e9
+    return {"workload": "w4_llama3_8b_sweep_225_gemv", "bytes_per_token": total,
+            "ms_per_token": ms, "tokens_per_s": round(1e3 / ms, 1), "GB/s": round(gbs, 1),
+            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "roofline_tokens_per_s": round(HBM_PEAK_GBS * 1e9 / total, 1), "steps": steps}
+
+
+def batched_workload(a, torch, timer):
+    import synthetic
+    from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
+    rows = []
+    for (N, K) in ((14336, 4096), (4096, 14336)):
+        Lb = synthetic.config4(16, N, K)
+        base = DeviceLayer(pack_host(4, Lb.W))
+        for M in (2, 4, 8, 16):
+            nbytes = base.nbytes(M)
+            layers = rotated(DeviceLayer, base, nbytes)
+            nc = len(layers)
+            X = torch.from_numpy(np.ascontiguousarray(Lb.x[:M]).view(np.int16)).cuda()
+            Y = [torch.empty((M, N), dtype=torch.int16, device="cuda") for _ in range(nc)]
+            xrow = [X[m].contiguous() for m in range(M)]
+            ms_gemm = timer(lambda i: layers[i % nc].gemm(X, Y[i % nc]), a.steps // 4, a.warmup // 4)
+
+            def rep(i):
+                for m in range(M):
+                    layers[i % nc].gemv(xrow[m], Y[i % nc][m])
+            ms_rep = timer(rep, max(1, a.steps // (4 * M)), max(1, a.warmup // (4 * M)))
+            flops = 2.0 * M * N * K
+            rows.append({"workload": f"w4_{N}x{K}_m{M}", "bytes": nbytes,
+                         "gemm_us": round(ms_gemm * 1e3, 3),
+                         "gemm_GB/s": round(nbytes / (ms_gemm * 1e-3) / 1e9, 1),
+                         "gemm_TFLOP/s": round(flops / (ms_gemm * 1e-3) / 1e12, 2),
+                         "repeated_gemv_us": round(ms_rep * 1e3, 3),
+                         "speedup_vs_repeated_gemv": round(ms_rep / ms_gemm, 2)})
+    return rows
+
+
+def w2_70b_workload(a, torch, timer):
+    import synthetic
+    from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
+    rows = []
+    for (N, K) in ((28672, 8192), (8192, 28672)):
+        L8 = synthetic.config5(N, K, 8)
+        base = DeviceLayer(pack_host(2, L8.W, L8.profile, L8.ratio))
+        for M in (1, 8):
+            nbytes = base.nbytes(M)
+            layers = rotated(DeviceLayer, base, nbytes)
+            nc = len(layers)
+            X = torch.from_numpy(np.ascontiguousarray(L8.x[:M]).view(np.int16)).cuda()
+            Y = [torch.empty((M, N), dtype=torch.int16, device="cuda") for _ in range(nc)]
+            if M == 1:
+                fn = lambda i: layers[i % nc].gemv(X[0], Y[i % nc][0])  # noqa: E731
+            else:
+                fn = lambda i: layers[i % nc].gemm(X, Y[i % nc])  # noqa: E731
+            ms = timer(fn, a.steps // 4, a.warmup // 4)
+            rows.append({"workload": f"w2_{N}x{K}_outliers{base.n_out}_m{M}", "bytes": nbytes,
+                         "us": round(ms * 1e3, 3), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                         "pct_of_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)})
+    return rows
+
+
+def stream_workload(a, torch, timer, copy):
+    import bit_weight_only_gemv_amd as B
+    nb = (a.bytes + 15) // 16 * 16
+    ncopy = max(1, -(-ROTATE_BYTES // nb))
+    bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
+    if copy:
+        dsts = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
+        fn = lambda i: B.wq_copy_probe(bufs[i % ncopy], dsts[i % ncopy], nb)  # noqa: E731
+    else:
+        sink = torch.empty(B.wq_read_probe_sink_words(nb), dtype=torch.int32, device="cuda")
+        fn = lambda i: B.wq_read_probe(bufs[i % ncopy], nb, sink)  # noqa: E731
+    ms = timer(fn, a.steps, a.warmup)
+    moved = nb * (2 if copy else 1)
+    return {"workload": "copy_probe" if copy else "read_probe", "bytes": nb, "copies": ncopy,
+            "us": round(ms * 1e3, 3), "GB/s": round(moved / (ms * 1e-3) / 1e9, 1)}
 
 
 def cpu_baseline(L, nbytes):
-    """The oracle, as it stands, on the same layer: float64 dequantization of
-    the packed weights followed by the float64 product (median of 3)."""
+    """The oracle, as it stands, on the same layer: dequantization of the packed
+    weights followed by the float64 product (median of 3)."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -230,8 +328,40 @@ def cpu_baseline(L, nbytes):
     t = float(np.median(times))
     return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": f"whole {ref.N}x{ref.K} layer: oracle dequant + float64 product, median of 3 "
-                      f"({t:.2f} s each); host has {len(os.sched_getaffinity(0))} cores"}
+            "sample": (f"the whole {ref.N}x{ref.K} layer: oracle dequantization + float64 product, "
+                       f"median of 3 runs ({t:.2f} s each); numpy elementwise work is single-threaded, "
+                       f"the BLAS product used {blas_threads} threads of "
+                       f"{len(os.sched_getaffinity(0))} host cores")}
+
+
+def main():
+    a = _parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): the path is a "
+              "single-GPU kernel; sharding across GPUs is described, not built.", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, ROOT)
+    import torch
+    import synthetic
+    import bit_weight_only_gemv_amd as B
+
+    B.load()
+    torch.cuda.init()
+    timer = Timer(torch, eager=a.eager)
+    if a.workload == "w2_14336":
+        out = gemv_workload(a, torch, synthetic.config2(), "w2_14336x4096_outliers143_m1", timer)
+    elif a.workload == "w4_4096":
+        out = gemv_workload(a, torch, synthetic.config1(), "w4_4096x4096_m1", timer)
+    elif a.workload == "sweep":
+        out = sweep_workload(a, torch, timer)
+    elif a.workload == "batched":
+        out = batched_workload(a, torch, timer)
+    elif a.workload == "w2_70b":
+        out = w2_70b_workload(a, torch, timer)
+    else:
+        out = stream_workload(a, torch, timer, copy=(a.workload == "copy"))
+    for o in (out if isinstance(out, list) else [out]):
+        print(json.dumps(o), flush=True)
 
 
 if __name__ == "__main__":

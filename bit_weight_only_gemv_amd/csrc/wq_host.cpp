@@ -30,6 +30,17 @@ thread_local std::string g_last_error;
 
 // ------------------------------------------------------------------ FP16 bits
 
+// Round to nearest integer, ties to even, for doubles of magnitude below 2^52
+// (adding and subtracting 2^52 leaves the rounded value in the default rounding
+// mode); larger doubles are already integers.  Avoids nearbyint, whose
+// floating-point-environment handling is slow in some C libraries.
+inline double round_half_even_d(double v) {
+  const double big = 4503599627370496.0;   // 2^52
+  const double a = std::fabs(v);
+  if (!(a < big)) return v;
+  return std::copysign((a + big) - big, v);
+}
+
 // IEEE binary16 from binary64, round to nearest, ties to even.  Written from
 // the format's definition: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
 // bits; subnormals are multiples of 2^-24.
@@ -45,13 +56,13 @@ uint16_t f64_to_f16(double v) {
   if (a < 0x1p-14) {
     // subnormal (or zero): count of 2^-24 units, rounded to nearest even.  A
     // result of 1024 is the smallest normal, whose bit pattern is the same.
-    const double m = std::nearbyint(std::ldexp(a, 24));
+    const double m = round_half_even_d(std::ldexp(a, 24));
     return (uint16_t)(sign | (uint16_t)m);
   }
   int e2;
   (void)std::frexp(a, &e2);        // a = f * 2^e2, f in [0.5, 1)
   int e = e2 - 1;                  // a in [2^e, 2^(e+1))
-  double m = std::nearbyint(std::ldexp(a, 10 - e));   // in [1024, 2048]
+  double m = round_half_even_d(std::ldexp(a, 10 - e));   // in [1024, 2048]
   if (m == 2048.0) {
     m = 1024.0;
     e += 1;
