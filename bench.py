@@ -42,7 +42,7 @@ METRIC = "M=1 dequant-GEMV effective HBM GB/s (% of MI355X peak); eq. tokens/s"
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["wq_gemv.hip", "wq_common.cuh", "wq_device.h"]
+KERNEL_SOURCES = ["wq_gemv.hip", "wq_mma.hip", "wq_mma.h", "wq_common.cuh", "wq_device.h"]
 
 
 def _parse():

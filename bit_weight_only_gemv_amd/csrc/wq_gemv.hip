@@ -30,6 +30,7 @@
 
 #include "wq_common.cuh"
 #include "wq_device.h"
+#include "wq_mma.h"
 
 #include <stdlib.h>
 
@@ -749,6 +750,16 @@ static int gemv_entry(int fmt, const uint8_t* codes, const uint16_t* scales, con
   a.n_out = (int)n_out;
   a.fuse = (flags & WQ_FUSE_OUTLIERS) ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
+  // the matrix-core kernel fuses the outlier pass; an unfused call with
+  // outlier columns stays on the VALU kernels
+  if (a.fuse || n_out == 0) {
+    int mode = 1;
+    if (const char* e = getenv("WQ_GEMV_MMA")) mode = atoi(e);
+    bool launched = false;
+    const int r = wqd_gemv_mma(fmt, codes, scales, zeros, N, K, out_idx, out_w,
+                               a.fuse ? n_out : 0, x, y, s, who, mode, &launched);
+    if (r != WQ_OK || launched) return r;
+  }
   return fmt == 4 ? launch_gemv<4>(a, s, who) : launch_gemv<2>(a, s, who);
 }
 

@@ -1,0 +1,15 @@
+// Matrix-core GEMV launcher (wq_mma.hip), called by the GEMV entry points.
+// Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Launches the matrix-core M = 1 kernel when the shape suits it and sets
+// *launched; otherwise returns WQ_OK with *launched = false and the caller
+// uses the VALU kernels.  `mode`: 0 = never, 1 = when the plan prefers it,
+// 2 = whenever the shape is supported.
+int wqd_gemv_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                 int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
+                 int64_t n_out, const uint16_t* x, uint16_t* y, hipStream_t stream,
+                 const char* who, int mode, bool* launched);

@@ -1,0 +1,688 @@
+// M = 1 dequantize-and-multiply on the matrix cores of gfx950
+// (v_mfma_f32_16x16x32_f16), persistent over row blocks.
+//
+// What is computed is the same as the VALU kernels of wq_gemv.hip (SPECTRA
+// page, section 4.1; OTF-LLM v4.0 page, section 5):
+//   y[n] = FP16( sum_{k not in outliers} w_hat[n][k] x[k]
+//                + sum_j out_w[n][j] x[out_idx[j]] ),   FP32 accumulation.
+//
+// Layout of the work:
+//  * A workgroup owns row blocks of 16 rows (blockIdx.x, + gridDim.x, ...) and
+//    has nw waves; wave w owns the K-slices of 512 channels w, w + nw, ...
+//    A wave prepares each of its slices by itself, in an LDS region of its
+//    own (x of the slice, masked at the outlier columns; per-group sums of x;
+//    the slice's outlier activations), so no workgroup barrier sits between
+//    the weight loads and the first products.  Only the W2 centroid table is
+//    shared: it is written at entry, before the bulk of the loads.
+//  * One MFMA multiplies a 16 x 32 A block by a 32 x 16 B block.  B holds
+//    decoded weights: lane (n, r) = (lane % 16, lane / 16) gives 8 weights of
+//    row n from its own 16-byte load (W4: one group; W2: two groups).  The
+//    four lane quarters read different groups, so a plain product would mix
+//    groups that carry different scales.  The 16 rows of A keep them apart:
+//    A row m ("slot") holds x only in the k-quarter and step that belong to
+//    group m of the slice, zero elsewhere, so D[m][n] = sum over group m of
+//    x * code value.  After the 16 steps of a row block, lane (n, r) holds
+//    D[4r + j][n], the sums of the 4 consecutive groups 4r .. 4r + 3, and
+//    applies their scales and zeros:
+//      W4: s (sum q x - z sum x), codes entering as FP16 subnormals q 2^-24;
+//      W2: S sum C[q] x + Z sum x, centroids from an LDS table.
+//  * W2 table: 256 entries (one code byte -> its four FP16 centroids), 32
+//    copies, copy c at byte 8c of each 256-byte entry row, lane l reading copy
+//    l % 32.  Every lane thus reads its own bank pair (no bank conflicts), and
+//    the address (entry << 8 | 8 (l % 32)) is one byte permute of the code word.
+//  * Outlier columns: the indices are ascending, so the columns inside a
+//    slice are one contiguous run j_lo .. j_lo + nin of the FP16 slab.  The
+//    wave that owns the slice gathers their activations from its copy of x,
+//    zeroes them there, and dots the slab run with them (v_dot2) for each row
+//    block, 32 columns per step.
+//  * Row-block loads go through a ring of DEPTH register buffers, so that
+//    while one row block is multiplied, the next ones are in flight.
+//  * Per row block each wave reduces its 4 lane quarters and adds its row
+//    sums into an LDS slot of its own; the slots are summed in a fixed order
+//    at the end (deterministic, no atomics).
+
+#include "wq_common.cuh"
+#include "wq_device.h"
+#include "wq_mma.h"
+
+#include <stdlib.h>
+
+#include <algorithm>
+
+namespace wqd {
+
+constexpr int kSliceCh = 512;      // channels per K-slice
+constexpr int kSliceGroups = 16;   // groups per K-slice = MFMA slots
+constexpr int kLutRow = 256;       // bytes per W2 table entry (32 copies x 8 bytes)
+constexpr int kMaxWaves = 8;
+constexpr uint32_t kOob = 0x80000000u;   // buffer offset past any range: loads return 0
+
+struct MmaArgs {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* zeros;
+  const int32_t* out_idx;
+  const uint16_t* out_w;
+  const uint16_t* x;
+  uint16_t* y;
+  int N, K, n_out;   // n_out = 0 when there are no outlier columns
+  int nw;            // waves per workgroup
+  int nks;           // K-slices
+  int nsw;           // K-slices per wave, at most
+  int nrb;           // row blocks (16 rows)
+  int rbl;           // row blocks per workgroup, at most
+};
+
+// Per-wave LDS region: for each of its slices, x (1 KB, masked) and the 16
+// group sums (64 B); then the outlier activations of its slices, each run
+// followed by zeros up to the next multiple of 32 (at least 32 entries per
+// slice, so that every lane's first-step read is defined).
+__host__ __device__ inline int mma_run_pad(int nin) { return ((nin + 32) / 32) * 32; }
+__host__ __device__ inline uint32_t mma_xo_cap(int n_out, int nsw) {
+  return n_out > 0 ? (uint32_t)(((n_out + 31) / 32) * 32 + 32 * nsw) : 0u;
+}
+__host__ __device__ inline uint32_t mma_wave_bytes(int n_out, int nsw) {
+  return (uint32_t)nsw * 1088u + mma_xo_cap(n_out, nsw) * 2u;
+}
+
+// LDS layout (byte offsets), identical on host and device.
+struct MmaLds {
+  uint32_t lut, wave, part, total;
+};
+__host__ __device__ inline MmaLds mma_lds_layout(int fmt, int n_out, int nw, int nsw, int rbl) {
+  MmaLds L{};
+  uint32_t off = 0;
+  L.lut = off;
+  if (fmt == 2) off += 256u * kLutRow;
+  L.wave = off;
+  off += (uint32_t)nw * mma_wave_bytes(n_out, nsw);
+  L.part = off;
+  off += (uint32_t)rbl * (uint32_t)nw * 64u;
+  L.total = off;
+  return L;
+}
+
+template <int FMT>
+struct MmaFmt;
+template <>
+struct MmaFmt<4> {
+  static constexpr int kLoads = 4;       // 16-byte code loads per lane per row block
+  static constexpr int kSliceBytes = 256;
+  static constexpr int kRowBytesDiv = 2;
+};
+template <>
+struct MmaFmt<2> {
+  static constexpr int kLoads = 2;
+  static constexpr int kSliceBytes = 128;
+  static constexpr int kRowBytesDiv = 4;
+};
+
+// 8-byte LDS load at a byte address of the kernel's LDS (the kernel declares
+// no static LDS, so its dynamic LDS window starts at address 0).
+__device__ __forceinline__ u2 lds_ld64(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) u2*)(size_t)addr;
+}
+
+// Loads of one row block of one K-slice: codes, scales, zeros, and the first
+// 32 outlier columns of the slice (5 dwords per lane: 8 FP16 values that may
+// start at an odd index).
+template <int FMT, bool OUT>
+struct Item {
+  u4v cw[MmaFmt<FMT>::kLoads];
+  u2 sv, zv;
+  uint32_t od[OUT ? 5 : 1];
+};
+
+// Dots 8 FP16 slab values (5 dwords starting at an even or odd FP16 index,
+// sh = 0 or 16) with 4 pairs of FP16 activations.
+__device__ __forceinline__ float slab_dot(const uint32_t (&od)[5], const uint32_t (&xw)[4],
+                                          uint32_t sh, float v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t wv = __builtin_amdgcn_alignbit(od[i + 1], od[i], sh);
+    v = __builtin_amdgcn_fdot2(as_h2(wv), as_h2(xw[i]), v, false);
+  }
+  return v;
+}
+
+template <int FMT, int IV, int DEPTH, int NSW>
+__global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
+  typedef MmaFmt<FMT> F;
+  constexpr bool OUT = IV > 0;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int n_out = OUT ? a.n_out : 0;
+  const MmaLds L = mma_lds_layout(FMT, n_out, a.nw, a.nsw, a.rbl);
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int n16 = lane & 15;
+  const int r = lane >> 4;
+  const int G = a.K >> 5;
+  const uint32_t row_bytes = (uint32_t)a.K / F::kRowBytesDiv;
+  const int nrb_wg = (a.nrb - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int ns_w = (a.nks - w + a.nw - 1) / a.nw;   // 1 .. NSW (nw <= nks)
+  const int T = ns_w * nrb_wg;                       // items of this wave
+  const uint32_t wreg = L.wave + (uint32_t)w * mma_wave_bytes(n_out, a.nsw);
+  const uint32_t wxo = wreg + (uint32_t)a.nsw * 1088u;
+  auto slice_x = [&](int s) { return wreg + (uint32_t)s * 1088u; };        // 1 KB of x
+  auto slice_sx = [&](int s) { return wreg + (uint32_t)s * 1088u + 1024u; };
+
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(a.codes, clamp_bytes((uint64_t)a.N * row_bytes));
+  const uint64_t meta = (uint64_t)a.N * G * 2;
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.scales, clamp_bytes(meta));
+  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(a.zeros, clamp_bytes(meta));
+  // The slab is read with 4-byte loads at 4-byte-aligned offsets and the
+  // indices with 16-byte loads; each record count is rounded up to that size,
+  // which stays inside the 16-byte block (and page) of the last element.
+  const __amdgpu_buffer_rsrc_t ors =
+      make_rsrc(a.out_w, clamp_bytes(((uint64_t)a.N * n_out * 2 + 3) & ~(uint64_t)3));
+  const __amdgpu_buffer_rsrc_t irs = make_rsrc(a.out_idx, ((uint32_t)n_out * 4u + 15u) & ~15u);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.K * 2u);
+
+  // ---- (0) outlier indices (lane l holds idx[256 v + 4 l + k]; entries past
+  //      n_out are set, once they arrive, to a value that lies in no slice)
+  //      and x of every slice of this wave: issued before the weight stream,
+  //      so that waiting for them never waits for weights
+  int32_t oidx[IV > 0 ? IV : 1][4];
+  if constexpr (OUT) {
+#pragma unroll
+    for (int v = 0; v < IV; ++v) {
+      const u4v t = ld128(irs, (uint32_t)(256 * v + 4 * lane) * 4u);
+      oidx[v][0] = (int32_t)t.x;
+      oidx[v][1] = (int32_t)t.y;
+      oidx[v][2] = (int32_t)t.z;
+      oidx[v][3] = (int32_t)t.w;
+    }
+  }
+  u4v xr[NSW];
+  const __amdgpu_buffer_rsrc_t xnul = make_rsrc(a.x, 0u);
+#pragma unroll
+  for (int s = 0; s < NSW; ++s) {   // lane l: channels 512 ks + 8 l .. + 8 (past K: 0)
+    const uint32_t c = (uint32_t)((w + a.nw * s) * kSliceCh + 8 * lane);
+    xr[s] = ld128(s < ns_w ? xrs : xnul, c * 2u);
+  }
+  asm volatile("" ::: "memory");   // these loads stay ahead of the weight stream
+  // outlier run of slice ks: j_lo = number of indices below it, nin inside it
+  auto jrange = [&](int ks, int& j_lo, int& nin) {
+    j_lo = 0;
+    nin = 0;
+    if constexpr (OUT) {
+      const int lo = ks * kSliceCh, hi = lo + kSliceCh;
+#pragma unroll
+      for (int v = 0; v < IV; ++v)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int c = oidx[v][k];
+          j_lo += __builtin_popcountll(__ballot(c < lo));
+          nin += __builtin_popcountll(__ballot(c >= lo && c < hi));
+        }
+    }
+  };
+
+  // ---- (1) W2 centroid table: entry e (a code byte) -> its four FP16
+  //      centroids, 32 copies; slot s = 32 e + copy is written by consecutive
+  //      lanes (consecutive banks).  Shared by the workgroup: one barrier,
+  //      taken before the weight loads are issued.
+  if constexpr (FMT == 2) {
+    u2* lut = reinterpret_cast<u2*>(smem + L.lut);
+    for (int sl = tid; sl < 256 * 32; sl += nthr) {
+      const uint32_t e = (uint32_t)sl >> 5;
+      lut[sl] = (u2){w2_centroid_pair((e & 3u) | (((e >> 2) & 3u) << 16)),
+                     w2_centroid_pair(((e >> 4) & 3u) | ((e >> 6) << 16))};
+    }
+    lds_barrier();
+  }
+
+  // ---- (2) the first DEPTH row blocks' loads (every load is issued
+  //      unconditionally; an item past the end reads nothing)
+  // Offsets need no per-lane checks: rows past N and the bytes past the end
+  // of a short last slice lie past the arrays (the loads return 0) or in the
+  // next row, where the activations are zero; an item past the end of the
+  // wave's list reads through descriptors of zero records.
+  const __amdgpu_buffer_rsrc_t nul = make_rsrc(a.codes, 0u);
+  auto load_main = [&](Item<FMT, OUT>& it, bool valid, int ks, int rb) {
+    const __amdgpu_buffer_rsrc_t c_ = valid ? crs : nul;
+    const __amdgpu_buffer_rsrc_t s_ = valid ? srs : nul;
+    const __amdgpu_buffer_rsrc_t z_ = valid ? zrs : nul;
+    const uint32_t row = (uint32_t)(rb * 16 + n16);
+    const uint32_t rbase = row * row_bytes + (uint32_t)(ks * F::kSliceBytes + 16 * r);
+#pragma unroll
+    for (int u = 0; u < F::kLoads; ++u) it.cw[u] = ld128(c_, rbase + 64u * u);
+    const uint32_t mo = (row * (uint32_t)G + (uint32_t)(ks * kSliceGroups + 4 * r)) * 2u;
+    it.sv = ld64(s_, mo);
+    it.zv = ld64(z_, mo);
+  };
+  auto load_slab = [&](Item<FMT, OUT>& it, bool valid, int ks, int rb) {
+    if constexpr (OUT) {
+      int j_lo, nin;
+      jrange(ks, j_lo, nin);
+      const __amdgpu_buffer_rsrc_t o_ = valid ? ors : nul;
+      const uint32_t row = (uint32_t)(rb * 16 + n16);
+      const uint32_t e0 = row * (uint32_t)n_out + (uint32_t)(j_lo + 8 * r);
+      const uint32_t b0 = (e0 * 2u) & ~3u;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) it.od[i] = ld32(o_, b0 + 4u * i);
+    }
+  };
+  int ls = 0, lr = 0;   // slice / row-block counters of the next item to load
+  auto advance = [&](int& s_, int& q_) {
+    if (++q_ == nrb_wg) {
+      q_ = 0;
+      ++s_;
+    }
+  };
+  Item<FMT, OUT> buf[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    load_main(buf[d], d < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
+    advance(ls, lr);
+  }
+  // slab runs of these items: their offsets need the indices, whose wait is
+  // pinned here, after the weight loads went out
+  if constexpr (OUT) {
+#pragma unroll
+    for (int v = 0; v < IV; ++v)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        asm volatile("" : "+v"(oidx[v][k])::"memory");
+        const uint32_t j = (uint32_t)(256 * v + 4 * lane + k);
+        if (j >= (uint32_t)n_out) oidx[v][k] = 0x7FFFFFFF;
+      }
+  }
+  {
+    int s2 = 0, r2 = 0;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      load_slab(buf[d], d < T, w + a.nw * s2, blockIdx.x + r2 * gridDim.x);
+      advance(s2, r2);
+    }
+  }
+
+  // ---- (3) every slice of this wave set up in its LDS region: x masked at
+  //      the outlier columns, their activations gathered, group sums of x
+  //      (W4: scaled by 2^-24 like the code values)
+  uint16_t* wxo16 = reinterpret_cast<uint16_t*>(smem + wxo);
+  {
+    int xo_off = 0;
+#pragma unroll
+    for (int s = 0; s < NSW; ++s) {
+      if (s < ns_w) {
+        const int ks = w + a.nw * s;
+        reinterpret_cast<u4v*>(smem + slice_x(s))[lane] = xr[s];
+        uint16_t* x16 = reinterpret_cast<uint16_t*>(smem + slice_x(s));
+        if constexpr (OUT) {
+          int j_lo, nin;
+          jrange(ks, j_lo, nin);
+          const int lo = ks * kSliceCh;
+          const int nz = mma_run_pad(nin);
+          for (int j = lane; j < nz; j += kWave) wxo16[xo_off + j] = 0;
+#pragma unroll
+          for (int v = 0; v < IV; ++v)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int c = oidx[v][k] - lo;
+              if (c >= 0 && c < kSliceCh) wxo16[xo_off + 256 * v + 4 * lane + k - j_lo] = x16[c];
+            }
+#pragma unroll
+          for (int v = 0; v < IV; ++v)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int c = oidx[v][k] - lo;
+              if (c >= 0 && c < kSliceCh) x16[c] = 0;
+            }
+          xo_off += nz;
+        }
+        if (lane < kSliceGroups) {
+          float sum = 0.f;
+          const u4v* src = reinterpret_cast<const u4v*>(smem + slice_x(s) + (uint32_t)lane * 64u);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const u4v t = src[v];
+            const uint32_t tw[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sum = __builtin_amdgcn_fdot2(as_h2(tw[i]), as_h2(0x3C003C00u), sum, false);
+          }
+          reinterpret_cast<float*>(smem + slice_sx(s))[lane] =
+              FMT == 4 ? sum * 5.9604644775390625e-8f : sum;
+        }
+      }
+    }
+  }
+
+  // ---- A fragments, group sums and first-run outlier activations of slice s
+  h8 afr[16];
+  f4 sx4 = {0.f, 0.f, 0.f, 0.f};
+  uint32_t xo0[4] = {0u, 0u, 0u, 0u};
+  int cur_jlo = 0, cur_nin = 0, cur_xo = 0;
+  auto enter_slice = [&](int s) {
+    const int ks = w + a.nw * s;
+    if constexpr (OUT) {
+      if (s > 0) cur_xo += mma_run_pad(cur_nin);
+      jrange(ks, cur_jlo, cur_nin);
+      const u4v v = *reinterpret_cast<const u4v*>(smem + wxo + (uint32_t)(cur_xo + 8 * r) * 2u);
+      xo0[0] = v.x;
+      xo0[1] = v.y;
+      xo0[2] = v.z;
+      xo0[3] = v.w;
+    }
+    sx4 = *reinterpret_cast<const f4*>(smem + slice_sx(s) + (uint32_t)r * 16u);
+    // A: the lane of slot m = lane % 16 whose k-quarter holds group m carries
+    // that group's 32 activations in the 4 steps of the group; all else is 0
+    const int m = n16;
+    bool act;
+    int u_m, t0;
+    if constexpr (FMT == 2) {   // group m: load m / 8, quarter (m / 2) % 4, half m % 2
+      act = r == ((m >> 1) & 3);
+      u_m = m >> 3;
+      t0 = 4 * (m & 1);
+    } else {                    // group m: load m / 4, quarter m % 4
+      act = r == (m & 3);
+      u_m = m >> 2;
+      t0 = 0;
+    }
+    uint32_t gv[16];
+    {
+      const u4v* src = reinterpret_cast<const u4v*>(smem + slice_x(s) + (uint32_t)m * 64u);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const u4v t = src[v];
+        gv[4 * v + 0] = act ? t.x : 0u;
+        gv[4 * v + 1] = act ? t.y : 0u;
+        gv[4 * v + 2] = act ? t.z : 0u;
+        gv[4 * v + 3] = act ? t.w : 0u;
+      }
+    }
+    uint32_t fr[4][4];   // the group's 4 fragments (W4: in decode order)
+    if constexpr (FMT == 2) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fr[t][i] = gv[4 * t + i];
+    } else {
+      // step t, word i: codes k0 = 16 (t & 1) + 4 i + (t >> 1) and k0 + 2
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k0 = 16 * (t & 1) + 4 * i;
+          fr[t][i] = __builtin_amdgcn_perm(gv[k0 / 2 + 1], gv[k0 / 2],
+                                           (t >> 1) ? 0x07060302u : 0x05040100u);
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+      const int u = FMT == 2 ? (f >> 3) : (f >> 2);
+      const int t = FMT == 2 ? (f & 7) : (f & 3);
+      const int tt = FMT == 2 ? (t & 3) : t;
+      const bool on = u == u_m && (FMT == 2 ? (t & 4) == t0 : true);
+      const u4v v = on ? (u4v){fr[tt][0], fr[tt][1], fr[tt][2], fr[tt][3]}
+                       : (u4v){0u, 0u, 0u, 0u};
+      afr[f] = __builtin_bit_cast(h8, v);
+    }
+  };
+
+  // ---- one row block of one slice: products, slot scales, the first 32
+  //      outlier columns of the slice, reduction of the lane quarters
+  float* s_part = reinterpret_cast<float*>(smem + L.part);
+  const uint32_t lut_lane = (uint32_t)(lane & 31) * 8u;
+  auto compute = [&](const Item<FMT, OUT>& it, int ri, int si) {
+    const int row = (int)(blockIdx.x + (unsigned)ri * gridDim.x) * 16 + n16;
+    f4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (FMT == 4) {
+      // c0: low-nibble steps (values q 2^-24), c1: high-nibble steps (16 q 2^-24)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t d[4] = {it.cw[u].x, it.cw[u].y, it.cw[u].z, it.cw[u].w};
+        uint32_t d8[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d8[i] = d[i] >> 8;
+        const u4v b0 = {d[0] & 0x000F000Fu, d[1] & 0x000F000Fu, d[2] & 0x000F000Fu,
+                        d[3] & 0x000F000Fu};
+        const u4v b1 = {d[0] & 0x00F000F0u, d[1] & 0x00F000F0u, d[2] & 0x00F000F0u,
+                        d[3] & 0x00F000F0u};
+        const u4v b2 = {d8[0] & 0x000F000Fu, d8[1] & 0x000F000Fu, d8[2] & 0x000F000Fu,
+                        d8[3] & 0x000F000Fu};
+        const u4v b3 = {d8[0] & 0x00F000F0u, d8[1] & 0x00F000F0u, d8[2] & 0x00F000F0u,
+                        d8[3] & 0x00F000F0u};
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[4 * u + 0], __builtin_bit_cast(h8, b0), c0,
+                                                    0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[4 * u + 1], __builtin_bit_cast(h8, b1), c1,
+                                                    0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[4 * u + 2], __builtin_bit_cast(h8, b2), c0,
+                                                    0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[4 * u + 3], __builtin_bit_cast(h8, b3), c1,
+                                                    0, 0, 0);
+      }
+    } else {
+      // byte b of a code word -> LDS address (b << 8) | 8 (lane % 32); the 16
+      // table reads of a load are issued before its 8 products
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t d[4] = {it.cw[u].x, it.cw[u].y, it.cw[u].z, it.cw[u].w};
+        u2 lv[16];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const uint32_t word = d[t >> 1];
+          const uint32_t bsel = (uint32_t)(2 * (t & 1));
+          lv[2 * t] =
+              lds_ld64(L.lut + __builtin_amdgcn_perm(word, lut_lane, 0x0C0C0400u + (bsel << 8)));
+          lv[2 * t + 1] =
+              lds_ld64(L.lut + __builtin_amdgcn_perm(word, lut_lane, 0x0C0C0500u + (bsel << 8)));
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const u4v bv = {lv[2 * t].x, lv[2 * t].y, lv[2 * t + 1].x, lv[2 * t + 1].y};
+          if (t & 1)
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[8 * u + t], __builtin_bit_cast(h8, bv),
+                                                        c1, 0, 0, 0);
+          else
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[8 * u + t], __builtin_bit_cast(h8, bv),
+                                                        c0, 0, 0, 0);
+        }
+      }
+    }
+    // slots 4r + j = groups ks*16 + 4r + j of row n16
+    const uint32_t sw[2] = {it.sv.x, it.sv.y};
+    const uint32_t zw[2] = {it.zv.x, it.zv.y};
+    float v = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float s = h2f((uint16_t)(sw[j >> 1] >> (16 * (j & 1))));
+      const float z = h2f((uint16_t)(zw[j >> 1] >> (16 * (j & 1))));
+      if constexpr (FMT == 4) {
+        float t = __builtin_fmaf(c1[j], 0.0625f, c0[j]);
+        t = __builtin_fmaf(-z, sx4[j], t);
+        v = __builtin_fmaf(s, t, v);
+      } else {
+        v = __builtin_fmaf(s, c0[j] + c1[j], v);
+        v = __builtin_fmaf(z, sx4[j], v);
+      }
+    }
+    if constexpr (FMT == 4) v *= 16777216.0f;
+    if constexpr (OUT) {
+      const uint32_t sh = (((uint32_t)row * (uint32_t)n_out + (uint32_t)cur_jlo) & 1u) * 16u;
+      v = slab_dot(it.od, xo0, sh, v);
+    }
+    // the four lane quarters hold the same row: add them
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    if (r == 0) {
+      float* p = s_part + ((uint32_t)ri * (uint32_t)a.nw + (uint32_t)w) * 16u + (uint32_t)n16;
+      *p = si == 0 ? v : *p + v;
+    }
+  };
+
+  // ---- (4) the items: compute one, refill its buffer with the one DEPTH
+  //      ahead.  Only the ring's loads are in this loop.
+  int si = 0, ri = 0;   // slice / row-block counters of the item being computed
+  for (int base = 0; base < T; base += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      if (base + d < T) {
+        if (ri == 0) enter_slice(si);
+        compute(buf[d], ri, si);
+        advance(si, ri);
+      }
+      load_main(buf[d], base + d + DEPTH < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
+      load_slab(buf[d], base + d + DEPTH < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
+      advance(ls, lr);
+    }
+  }
+
+  // ---- (5) outlier runs longer than 32 columns: the remaining columns, row
+  //      block by row block, after the weight stream
+  if constexpr (OUT) {
+    int xo_off = 0;
+    for (int s = 0; s < ns_w; ++s) {
+      int j_lo, nin;
+      jrange(w + a.nw * s, j_lo, nin);
+      for (int c = 32; c < nin; c += 32) {
+        const u4v xv = *reinterpret_cast<const u4v*>(smem + wxo + (uint32_t)(xo_off + c + 8 * r) * 2u);
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        for (int q = 0; q < nrb_wg; ++q) {
+          const int row = (int)(blockIdx.x + (unsigned)q * gridDim.x) * 16 + n16;
+          const bool ok = row < a.N && c + 8 * r < nin;
+          const uint32_t e0 = (uint32_t)row * (uint32_t)n_out + (uint32_t)(j_lo + c + 8 * r);
+          const uint32_t b0 = (e0 * 2u) & ~3u;
+          uint32_t od[5];
+#pragma unroll
+          for (int i = 0; i < 5; ++i) od[i] = ld32(ors, ok ? b0 + 4u * i : kOob);
+          float v = slab_dot(od, xw, (e0 & 1u) * 16u, 0.f);
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          if (r == 0) s_part[((uint32_t)q * (uint32_t)a.nw + (uint32_t)w) * 16u + (uint32_t)n16] += v;
+        }
+      }
+      xo_off += mma_run_pad(nin);
+    }
+  }
+
+  // ---- (6) fixed-order sum of the waves' row sums
+  __syncthreads();
+  for (int t = tid; t < nrb_wg * 16; t += nthr) {
+    const int ri2 = t >> 4, n = t & 15;
+    const int row = (int)(blockIdx.x + (unsigned)ri2 * gridDim.x) * 16 + n;
+    if (row >= a.N) continue;
+    float s = 0.f;
+    for (int k = 0; k < a.nw; ++k) s += s_part[((uint32_t)ri2 * a.nw + k) * 16u + n];
+    a.y[row] = f2h(s);
+  }
+}
+
+// ------------------------------------------------------------- launch plan
+
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+struct MmaPlan {
+  bool ok, preferred;
+  int nw, nks, nsw, nswt, nrb, grid, rbl, iv, depth;
+  size_t lds;
+};
+
+static MmaPlan plan_mma1(int fmt, int64_t N, int64_t K, int64_t n_out) {
+  MmaPlan p{};
+  if (K % 128 != 0 || K > 65536 || n_out > 1024) return p;
+  const int64_t row_bytes = fmt == 4 ? K / 2 : K / 4;
+  if (N * row_bytes > 0xFFFFFFF0ll || N * (K / 32) * 2 > 0xFFFFFFF0ll ||
+      N * n_out * 2 > 0xFFFFFFF0ll)
+    return p;
+  p.nks = (int)((K + kSliceCh - 1) / kSliceCh);
+  if (p.nks <= kMaxWaves) {
+    p.nw = p.nks;
+  } else {
+    int best = -1;
+    for (int nw = kMaxWaves; nw >= 4; --nw) {
+      const int waste = ((p.nks + nw - 1) / nw) * nw - p.nks;
+      if (best < 0 || waste < best) {
+        best = waste;
+        p.nw = nw;
+      }
+    }
+  }
+  p.nsw = (p.nks + p.nw - 1) / p.nw;
+  if (p.nsw > 8) return p;
+  p.nswt = p.nsw <= 1 ? 1 : p.nsw <= 2 ? 2 : p.nsw <= 4 ? 4 : 8;
+  p.nrb = (int)((N + 15) / 16);
+  const int cus = device_cus();
+  if (cus <= 0) return p;
+  p.grid = std::min(p.nrb, cus);
+  p.rbl = (p.nrb + p.grid - 1) / p.grid;
+  p.iv = n_out == 0 ? 0 : n_out <= 256 ? 1 : n_out <= 512 ? 2 : 4;
+  const MmaLds L = mma_lds_layout(fmt, (int)n_out, p.nw, p.nsw, p.rbl);
+  p.lds = L.total;
+  if (p.lds > kMaxLdsBytes) return p;
+  p.depth = 2;
+  if (const char* e = getenv("WQ_MMA_DEPTH")) {
+    const int v = atoi(e);
+    if (v == 2 || v == 4) p.depth = v;
+  }
+  p.ok = true;
+  // One workgroup per compute unit: worth it once every unit has a row block.
+  // Measured on MI355X: ahead of the VALU kernels for W2 (the centroid table
+  // and the v_dot2 work leave the VALU path compute-bound); behind them for
+  // W4, whose VALU decode is cheap and whose loads are fully contiguous.
+  p.preferred = fmt == 2 && p.nrb >= cus;
+  return p;
+}
+
+}  // namespace wqd
+
+using namespace wqd;
+
+int wqd_gemv_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                 int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
+                 int64_t n_out, const uint16_t* x, uint16_t* y, hipStream_t stream,
+                 const char* who, int mode, bool* launched) {
+  *launched = false;
+  if (mode == 0) return WQ_OK;
+  const MmaPlan p = plan_mma1(fmt, N, K, n_out);
+  if (!p.ok || (mode == 1 && !p.preferred)) return WQ_OK;
+  MmaArgs a{};
+  a.codes = codes;
+  a.scales = scales;
+  a.zeros = zeros;
+  a.out_idx = out_idx;
+  a.out_w = out_w;
+  a.x = x;
+  a.y = y;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.n_out = (int)n_out;
+  a.nw = p.nw;
+  a.nks = p.nks;
+  a.nsw = p.nsw;
+  a.nrb = p.nrb;
+  a.rbl = p.rbl;
+  const dim3 grid(p.grid), block(p.nw * kWave);
+#define WQ_MMA_LAUNCH(F_, IV_, D_, S_)                                                       \
+  if (fmt == F_ && p.iv == IV_ && p.depth == D_ && p.nswt == S_) {                           \
+    if (!allow_lds(reinterpret_cast<const void*>(&mma1d_kernel<F_, IV_, D_, S_>), p.lds))   \
+      return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds); \
+    hipLaunchKernelGGL((mma1d_kernel<F_, IV_, D_, S_>), grid, block, p.lds, stream, a);      \
+    *launched = true;                                                                        \
+    return check_launch(who);                                                                \
+  }
+#define WQ_MMA_SLICES(F_, IV_, D_) \
+  WQ_MMA_LAUNCH(F_, IV_, D_, 1) WQ_MMA_LAUNCH(F_, IV_, D_, 2) WQ_MMA_LAUNCH(F_, IV_, D_, 4) \
+  WQ_MMA_LAUNCH(F_, IV_, D_, 8)
+#define WQ_MMA_DEPTHS(F_, IV_) WQ_MMA_SLICES(F_, IV_, 2) WQ_MMA_SLICES(F_, IV_, 4)
+  WQ_MMA_DEPTHS(4, 0) WQ_MMA_DEPTHS(4, 1) WQ_MMA_DEPTHS(4, 2) WQ_MMA_DEPTHS(4, 4)
+  WQ_MMA_DEPTHS(2, 0) WQ_MMA_DEPTHS(2, 1) WQ_MMA_DEPTHS(2, 2) WQ_MMA_DEPTHS(2, 4)
+#undef WQ_MMA_SLICES
+#undef WQ_MMA_DEPTHS
+#undef WQ_MMA_LAUNCH
+  return WQ_OK;
+}

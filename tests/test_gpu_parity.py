@@ -88,14 +88,23 @@ def test_dequant_device_bit_exact(fmt, N, K, scale):
 # ------------------------------------------------------------------ gemv
 
 SHAPES = [(1, 32), (7, 96), (129, 4096), (300, 14336), (77, 28672), (64, 8192), (33, 2080),
-          (1000, 1024), (17, 65536)]
+          (1000, 1024), (17, 65536), (5000, 4224)]
+
+
+@pytest.fixture(params=["valu", "mfma"])
+def gemv_path(request, monkeypatch):
+    """Runs a GEMV test on the VALU kernels and again with the matrix-core
+    kernel forced wherever it supports the shape (K % 128 == 0 and its LDS
+    fits); the library otherwise picks it only for large N."""
+    monkeypatch.setenv("WQ_GEMV_MMA", "0" if request.param == "valu" else "2")
+    return request.param
 
 
 @pytest.mark.parametrize("fmt", [4, 2])
 @pytest.mark.parametrize("N,K", SHAPES)
 @pytest.mark.parametrize("outl", [False, True])
-def test_gemv_small(fmt, N, K, outl):
-    say(f"gemv fmt={fmt} N={N} K={K} outliers={outl}")
+def test_gemv_small(fmt, N, K, outl, gemv_path):
+    say(f"gemv fmt={fmt} N={N} K={K} outliers={outl} path={gemv_path}")
     L = synthetic.small_layer(fmt, N, K, with_outliers=outl, seed=N % 17)
     ref, dl = build(fmt, L.W, L.profile, L.ratio)
     y, _ = run_gemv(dl, L.x)
@@ -104,9 +113,9 @@ def test_gemv_small(fmt, N, K, outl):
 
 @pytest.mark.parametrize("fmt", [4, 2])
 @pytest.mark.parametrize("n_out", [1, 31, 32, 33, 64, 65, 129, 500])
-def test_gemv_outlier_counts(fmt, n_out):
+def test_gemv_outlier_counts(fmt, n_out, gemv_path):
     K = 4096
-    say(f"gemv fmt={fmt} n_out={n_out}")
+    say(f"gemv fmt={fmt} n_out={n_out} path={gemv_path}")
     L = synthetic.small_layer(fmt, 200, K, with_outliers=True, seed=n_out,
                               ratio=(n_out + 0.5) / K)
     ref, dl = build(fmt, L.W, L.profile, L.ratio)
@@ -126,7 +135,7 @@ def test_gemv_unfused_then_outlier_add(fmt):
     check_product(ref, y, L.x, "unfused")
 
 
-def test_gemv_deterministic():
+def test_gemv_deterministic(gemv_path):
     L = synthetic.small_layer(2, 1500, 4096, with_outliers=True, seed=9)
     ref, dl = build(2, L.W, L.profile, L.ratio)
     y1, _ = run_gemv(dl, L.x)
