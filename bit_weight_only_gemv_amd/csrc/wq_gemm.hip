@@ -21,6 +21,9 @@
 
 #include "wq_common.cuh"
 #include "wq_device.h"
+#include "wq_mma.h"
+
+#include <stdlib.h>
 
 namespace wqd {
 
@@ -237,6 +240,23 @@ extern "C" int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales,
     return wq::fail(WQ_ERR_UNSUPPORTED, "%s: X larger than 4 GB", who);
   GemmArgs a{codes, scales, zeros, out_idx, out_w, X, Y, (int)N, (int)K, (int)M, (int)n_out,
              (flags & WQ_FUSE_OUTLIERS) ? 1 : 0};
+  hipStream_t s = (hipStream_t)stream;
+  // M = 1 is the GEMV; 2 <= M <= 16 goes to the persistent matrix-core kernel
+  // when its plan fits (it fuses the outlier pass; an unfused call with
+  // outlier columns stays here)
+  if (M == 1)
+    return fmt == WQ_FMT_W4 ? wq_gemv_w4(codes, scales, zeros, N, K, out_idx, out_w, n_out, flags,
+                                         X, Y, stream)
+                            : wq_gemv_w2(codes, scales, zeros, N, K, out_idx, out_w, n_out, flags,
+                                         X, Y, stream);
+  if (a.fuse || n_out == 0) {
+    int mode = 1;
+    if (const char* e = getenv("WQ_GEMM_MMA")) mode = atoi(e);
+    bool launched = false;
+    const int r = wqd_gemm_mma(fmt, codes, scales, zeros, N, K, out_idx, out_w, a.fuse ? n_out : 0,
+                               X, M, Y, s, who, mode, &launched);
+    if (r != WQ_OK || launched) return r;
+  }
   const int G = (int)(K / kGroup);
   const int n_chunks = (a.fuse && n_out > 0) ? (int)((n_out + 31) / 32) : 0;
   const size_t lds = (size_t)((4 * G + 15) & ~15) + (size_t)kKB * 64 * 16 + (size_t)kKB * 16 * 4 +
@@ -244,7 +264,6 @@ extern "C" int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales,
   if (lds > kMaxLdsBytes)
     return wq::fail(WQ_ERR_UNSUPPORTED, "%s: %zu bytes of LDS needed (n_out too large)", who, lds);
   const dim3 grid((unsigned)((N + kGemmRows - 1) / kGemmRows)), block(kGemmWaves * 64);
-  hipStream_t s = (hipStream_t)stream;
   const void* k = fmt == WQ_FMT_W4 ? reinterpret_cast<const void*>(&gemm_kernel<4>)
                                    : reinterpret_cast<const void*>(&gemm_kernel<2>);
   if (!allow_lds(k, lds)) return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit", who);

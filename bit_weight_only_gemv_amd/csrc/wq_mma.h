@@ -13,3 +13,10 @@ int wqd_gemv_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
                  int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
                  int64_t n_out, const uint16_t* x, uint16_t* y, hipStream_t stream,
                  const char* who, int mode, bool* launched);
+
+// Launches the matrix-core batched kernel (2 <= M <= 16) when the shape suits
+// it (same contract and `mode` values as wqd_gemv_mma).
+int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                 int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
+                 int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream,
+                 const char* who, int mode, bool* launched);

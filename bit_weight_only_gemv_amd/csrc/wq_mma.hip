@@ -571,6 +571,484 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   }
 }
 
+// ====================================================== batched (2 <= M <= 16)
+//
+// Same persistent layout (waves own K-slices, now of 256 channels; the
+// workgroup's row blocks stream through a ring), but A holds the M activation
+// rows (rows M..15 zero) and B holds the dequantized weights themselves, so
+// each MFMA adds 16 rows x M activation rows x 32 channels into one tile:
+//   W4: w_hat = (q - z) s exactly: (1024 + q) - (1024 + z) in FP16 is the
+//       exact integer q - z, and its product with the FP16 scale rounds once,
+//       to the dequantized weight itself;
+//   W2: w_hat = S C[q] + Z as one FP16 fused multiply-add of the table's
+//       centroids (one rounding).
+// Lane (n, q) reads bytes 32 q .. 32 q + 31 (W4) or 16 q .. 16 q + 15 (W2) of
+// row n's slice, i.e. the two consecutive groups 2q, 2q + 1 of the slice,
+// whose scales and zeros are one 4-byte load each.  The activation rows of the
+// next slice are loaded one slice ahead.  W2 zeroes the outlier columns in the
+// activation fragments (W4 needs no mask: a column zeroed before
+// quantization decodes to exactly 0); the slice's run of the outlier slab is
+// one more MFMA per row block, against the gathered outlier activations.
+
+constexpr int kSliceChB = 256;
+constexpr int kSliceGroupsB = 8;
+
+template <int FMT>
+struct MmbFmt;
+template <>
+struct MmbFmt<4> {
+  static constexpr int kLoads = 2;
+  static constexpr int kSliceBytes = 128;
+  static constexpr int kRowBytesDiv = 2;
+};
+template <>
+struct MmbFmt<2> {
+  static constexpr int kLoads = 1;
+  static constexpr int kSliceBytes = 64;
+  static constexpr int kRowBytesDiv = 4;
+};
+
+struct MmbArgs {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint16_t* zeros;
+  const int32_t* out_idx;
+  const uint16_t* out_w;
+  const uint16_t* X;
+  uint16_t* Y;
+  int N, K, M, n_out;
+  int nw, nks, nrb, rbl;
+};
+
+// LDS: W2 table; per wave two slice areas (outlier-column mask, 8 words, and
+// the run's column offsets, up to 256); partial tiles [rbl][nw][M][16].
+constexpr uint32_t kMmbWaveArea = 32u + 1024u;
+struct MmbLds {
+  uint32_t lut, wave, part, total;
+};
+__host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl) {
+  MmbLds L{};
+  uint32_t off = 0;
+  L.lut = off;
+  if (fmt == 2) off += 256u * kLutRow;
+  L.wave = off;
+  off += (uint32_t)nw * 2u * kMmbWaveArea;
+  L.part = off;
+  off += (uint32_t)rbl * (uint32_t)nw * (uint32_t)M * 64u;
+  L.total = off;
+  return L;
+}
+
+template <int FMT, bool OUT>
+struct ItemB {
+  u4v cw[MmbFmt<FMT>::kLoads];
+  uint32_t sv, zv;
+  uint32_t od[OUT ? 5 : 1];
+};
+
+__device__ __forceinline__ uint32_t splat_lo(uint32_t v) { return __builtin_amdgcn_perm(v, v, 0x01000100u); }
+__device__ __forceinline__ uint32_t splat_hi(uint32_t v) { return __builtin_amdgcn_perm(v, v, 0x03020302u); }
+
+template <int FMT, int IV, int DEPTH>
+__global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
+  typedef MmbFmt<FMT> F;
+  constexpr bool OUT = IV > 0;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int n_out = OUT ? a.n_out : 0;
+  const MmbLds L = mmb_lds_layout(FMT, a.M, a.nw, a.rbl);
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15;   // weight row of B / activation row of A
+  const int q = lane >> 4;     // k-quarter
+  const int G = a.K >> 5;
+  const uint32_t row_bytes = (uint32_t)a.K / F::kRowBytesDiv;
+  const int nrb_wg = (a.nrb - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int ns_w = (a.nks - w + a.nw - 1) / a.nw;
+  const int T = ns_w * nrb_wg;
+
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(a.codes, clamp_bytes((uint64_t)a.N * row_bytes));
+  const uint64_t meta = (uint64_t)a.N * G * 2;
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.scales, clamp_bytes(meta));
+  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(a.zeros, clamp_bytes(meta));
+  const __amdgpu_buffer_rsrc_t ors =
+      make_rsrc(a.out_w, clamp_bytes(((uint64_t)a.N * n_out * 2 + 3) & ~(uint64_t)3));
+  const __amdgpu_buffer_rsrc_t irs = make_rsrc(a.out_idx, ((uint32_t)n_out * 4u + 15u) & ~15u);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.X, clamp_bytes((uint64_t)a.M * a.K * 2));
+  const __amdgpu_buffer_rsrc_t nul = make_rsrc(a.codes, 0u);
+
+  // ---- (0) outlier indices (as in the M = 1 kernel), then the activation
+  //      rows of this wave's first slice
+  int32_t oidx[IV > 0 ? IV : 1][4];
+  if constexpr (OUT) {
+#pragma unroll
+    for (int v = 0; v < IV; ++v) {
+      const u4v t = ld128(irs, (uint32_t)(256 * v + 4 * lane) * 4u);
+      oidx[v][0] = (int32_t)t.x;
+      oidx[v][1] = (int32_t)t.y;
+      oidx[v][2] = (int32_t)t.z;
+      oidx[v][3] = (int32_t)t.w;
+    }
+  }
+  // lane (m, q) of slice ks: W2 channels 256 ks + 64 q + 8 t (t < 8); W4 the
+  // two groups 8 ks + 2 q + u, 32 channels each; past K they read 0 (fixed up
+  // when the fragments are built)
+  auto x_load = [&](int ks, u4v (&xv)[8]) {
+    const uint32_t rowoff = (uint32_t)n16 * (uint32_t)a.K;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t c = (uint32_t)(ks * kSliceChB + 64 * q + 8 * t);
+      xv[t] = ld128(xrs, (rowoff + c) * 2u);
+    }
+  };
+  u4v xpre[8];
+  x_load(w, xpre);
+  asm volatile("" ::: "memory");   // these loads stay ahead of the weight stream
+
+  auto jrange = [&](int ks, int& j_lo, int& nin) {
+    j_lo = 0;
+    nin = 0;
+    if constexpr (OUT) {
+      const int lo = ks * kSliceChB, hi = lo + kSliceChB;
+#pragma unroll
+      for (int v = 0; v < IV; ++v)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int c = oidx[v][k];
+          j_lo += __builtin_popcountll(__ballot(c < lo));
+          nin += __builtin_popcountll(__ballot(c >= lo && c < hi));
+        }
+    }
+  };
+
+  // ---- (1) W2 centroid table (one barrier, before the weight loads)
+  if constexpr (FMT == 2) {
+    u2* lut = reinterpret_cast<u2*>(smem + L.lut);
+    for (int sl = tid; sl < 256 * 32; sl += nthr) {
+      const uint32_t e = (uint32_t)sl >> 5;
+      lut[sl] = (u2){w2_centroid_pair((e & 3u) | (((e >> 2) & 3u) << 16)),
+                     w2_centroid_pair(((e >> 4) & 3u) | ((e >> 6) << 16))};
+    }
+    lds_barrier();
+  }
+
+  // ---- (2) the ring
+  auto load_main = [&](ItemB<FMT, OUT>& it, bool valid, int ks, int rb) {
+    const __amdgpu_buffer_rsrc_t c_ = valid ? crs : nul;
+    const __amdgpu_buffer_rsrc_t s_ = valid ? srs : nul;
+    const __amdgpu_buffer_rsrc_t z_ = valid ? zrs : nul;
+    const uint32_t row = (uint32_t)(rb * 16 + n16);
+    const uint32_t rbase = row * row_bytes + (uint32_t)(ks * F::kSliceBytes + 16 * F::kLoads * q);
+#pragma unroll
+    for (int u = 0; u < F::kLoads; ++u) it.cw[u] = ld128(c_, rbase + 16u * u);
+    const uint32_t mo = (row * (uint32_t)G + (uint32_t)(ks * kSliceGroupsB + 2 * q)) * 2u;
+    it.sv = ld32(s_, mo);
+    it.zv = ld32(z_, mo);
+  };
+  auto load_slab = [&](ItemB<FMT, OUT>& it, bool valid, int ks, int rb) {
+    if constexpr (OUT) {
+      int j_lo, nin;
+      jrange(ks, j_lo, nin);
+      const __amdgpu_buffer_rsrc_t o_ = valid ? ors : nul;
+      const uint32_t row = (uint32_t)(rb * 16 + n16);
+      const uint32_t e0 = row * (uint32_t)n_out + (uint32_t)(j_lo + 8 * q);
+      const uint32_t b0 = (e0 * 2u) & ~3u;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) it.od[i] = ld32(o_, b0 + 4u * i);
+    }
+  };
+  int ls = 0, lr = 0;
+  auto advance = [&](int& s_, int& q_) {
+    if (++q_ == nrb_wg) {
+      q_ = 0;
+      ++s_;
+    }
+  };
+  ItemB<FMT, OUT> buf[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    load_main(buf[d], d < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
+    advance(ls, lr);
+  }
+  if constexpr (OUT) {
+#pragma unroll
+    for (int v = 0; v < IV; ++v)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        asm volatile("" : "+v"(oidx[v][k])::"memory");
+        const uint32_t j = (uint32_t)(256 * v + 4 * lane + k);
+        if (j >= (uint32_t)n_out) oidx[v][k] = 0x7FFFFFFF;
+      }
+  }
+  {
+    int s2 = 0, r2 = 0;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      load_slab(buf[d], d < T, w + a.nw * s2, blockIdx.x + r2 * gridDim.x);
+      advance(s2, r2);
+    }
+  }
+
+  // ---- per-slice activation work: outlier-column mask and run list in this
+  //      wave's LDS area (parity p), then the run's outlier activations
+  const uint32_t warea0 = L.wave + (uint32_t)w * 2u * kMmbWaveArea;
+  uint32_t xopre[4] = {0u, 0u, 0u, 0u};
+  auto prep_slice = [&](int ks, int p) {
+    if constexpr (OUT) {
+      uint32_t* mask = reinterpret_cast<uint32_t*>(smem + warea0 + (uint32_t)p * kMmbWaveArea);
+      int32_t* list = reinterpret_cast<int32_t*>(smem + warea0 + (uint32_t)p * kMmbWaveArea + 32u);
+      int j_lo, nin;
+      jrange(ks, j_lo, nin);
+      const int lo = ks * kSliceChB;
+      if (lane < 8) mask[lane] = 0u;
+      for (int j = lane; j < 32; j += kWave) list[j] = -1;   // first run step padded
+#pragma unroll
+      for (int v = 0; v < IV; ++v)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int c = oidx[v][k] - lo;
+          if (c >= 0 && c < kSliceChB) {
+            __hip_atomic_fetch_or(&mask[c >> 5], 1u << (c & 31), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+            list[256 * v + 4 * lane + k - j_lo] = c;
+          }
+        }
+      // outlier activations of the first 32 columns of the run: X[m][lo + c]
+      const int4 l0 = *reinterpret_cast<const int4*>(list + 8 * q);
+      const int4 l1 = *reinterpret_cast<const int4*>(list + 8 * q + 4);
+      const int cl[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+      uint32_t hv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {   // every lane loads (a valid column when idle)
+        const bool ok = 8 * q + e < nin && cl[e] >= 0;
+        const uint32_t col = (uint32_t)(lo + __builtin_amdgcn_ubfe(ok ? cl[e] : 0, 0, 8));
+        const uint32_t v = ld16(xrs, ((uint32_t)n16 * (uint32_t)a.K + col) * 2u);
+        hv[e] = ok ? v : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xopre[i] = hv[2 * i] | (hv[2 * i + 1] << 16);
+    }
+  };
+  prep_slice(w, 0);
+
+  h8 afr[8];
+  uint32_t xo[4] = {0u, 0u, 0u, 0u};
+  int cur_jlo = 0, cur_nin = 0;
+  auto enter_slice = [&](int s) {
+    const int ks = w + a.nw * s;
+    const int p = s & 1;
+    // fragments of this slice from the prefetched rows (channels past K: 0)
+    uint32_t fr[8][4];
+    if constexpr (FMT == 2) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const bool ok = ks * kSliceChB + 64 * q + 8 * t < a.K;
+        fr[t][0] = ok ? xpre[t].x : 0u;
+        fr[t][1] = ok ? xpre[t].y : 0u;
+        fr[t][2] = ok ? xpre[t].z : 0u;
+        fr[t][3] = ok ? xpre[t].w : 0u;
+      }
+      if constexpr (OUT) {
+        // zero the outlier columns: bits 2i, 2i + 1 of step t's byte
+        const uint32_t* mask =
+            reinterpret_cast<const uint32_t*>(smem + warea0 + (uint32_t)p * kMmbWaveArea);
+        const uint32_t m0 = mask[2 * q], m1 = mask[2 * q + 1];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const uint32_t byte = ((t < 4 ? m0 : m1) >> (8 * (t & 3))) & 0xFFu;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t b2 = (byte >> (2 * i)) & 3u;
+            const uint32_t keep = (b2 & 1u ? 0u : 0x0000FFFFu) | (b2 & 2u ? 0u : 0xFFFF0000u);
+            fr[t][i] &= keep;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bool ok = ks * kSliceGroupsB + 2 * q + u < G;
+        uint32_t gv[16];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const u4v t = xpre[4 * u + v];
+          gv[4 * v + 0] = ok ? t.x : 0u;
+          gv[4 * v + 1] = ok ? t.y : 0u;
+          gv[4 * v + 2] = ok ? t.z : 0u;
+          gv[4 * v + 3] = ok ? t.w : 0u;
+        }
+        // step t, word i: codes k0 = 16 (t & 1) + 4 i + (t >> 1) and k0 + 2
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int k0 = 16 * (t & 1) + 4 * i;
+            fr[4 * u + t][i] = __builtin_amdgcn_perm(gv[k0 / 2 + 1], gv[k0 / 2],
+                                                     (t >> 1) ? 0x07060302u : 0x05040100u);
+          }
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < 8; ++f)
+      afr[f] = __builtin_bit_cast(h8, (u4v){fr[f][0], fr[f][1], fr[f][2], fr[f][3]});
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xo[i] = xopre[i];
+    jrange(ks, cur_jlo, cur_nin);
+    // the next slice's rows and outlier activations, one slice ahead
+    if (s + 1 < ns_w) {
+      x_load(ks + a.nw, xpre);
+      prep_slice(ks + a.nw, p ^ 1);
+    }
+  };
+
+  float* s_part = reinterpret_cast<float*>(smem + L.part);
+  const uint32_t lut_lane = (uint32_t)(lane & 31) * 8u;
+  auto add_tile = [&](const f4& c, int ri, int si) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int m = 4 * q + jj;
+      if (m < a.M) {
+        float* p = s_part + (((uint32_t)ri * (uint32_t)a.nw + (uint32_t)w) * (uint32_t)a.M +
+                             (uint32_t)m) * 16u + (uint32_t)n16;
+        *p = si == 0 ? c[jj] : *p + c[jj];
+      }
+    }
+  };
+  auto compute = [&](const ItemB<FMT, OUT>& it, int ri, int si) {
+    f4 c = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (FMT == 4) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t sp = u ? splat_hi(it.sv) : splat_lo(it.sv);
+        // -(1024 + z) in both halves: the zero is an exact small integer
+        const _Float16 zf = __builtin_bit_cast(_Float16, (uint16_t)(it.zv >> (16 * u)));
+        const uint32_t nz = splat_lo((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(-1024.0f16 - zf)));
+        const uint32_t d[4] = {it.cw[u].x, it.cw[u].y, it.cw[u].z, it.cw[u].w};
+        uint32_t b[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t v0 = (d[i] & 0x000F000Fu) | 0x64006400u;
+          const uint32_t v1 = ((d[i] >> 4) & 0x000F000Fu) | 0x64006400u;
+          const uint32_t v2 = ((d[i] >> 8) & 0x000F000Fu) | 0x64006400u;
+          const uint32_t v3 = ((d[i] >> 12) & 0x000F000Fu) | 0x64006400u;
+          const uint32_t vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const h2 qz = as_h2(vv[t]) + as_h2(nz);   // exact q - z
+            b[t][i] = as_u32(qz * as_h2(sp));         // one rounding: w_hat
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              afr[4 * u + t], __builtin_bit_cast(h8, (u4v){b[t][0], b[t][1], b[t][2], b[t][3]}), c,
+              0, 0, 0);
+      }
+    } else {
+      const uint32_t sp[2] = {splat_lo(it.sv), splat_hi(it.sv)};
+      const uint32_t zp[2] = {splat_lo(it.zv), splat_hi(it.zv)};
+      const uint32_t d[4] = {it.cw[0].x, it.cw[0].y, it.cw[0].z, it.cw[0].w};
+      u2 lv[16];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t word = d[t >> 1];
+        const uint32_t bsel = (uint32_t)(2 * (t & 1));
+        lv[2 * t] = lds_ld64(L.lut + __builtin_amdgcn_perm(word, lut_lane, 0x0C0C0400u + (bsel << 8)));
+        lv[2 * t + 1] =
+            lds_ld64(L.lut + __builtin_amdgcn_perm(word, lut_lane, 0x0C0C0500u + (bsel << 8)));
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int g = t >> 2;
+        const uint32_t cv[4] = {lv[2 * t].x, lv[2 * t].y, lv[2 * t + 1].x, lv[2 * t + 1].y};
+        uint32_t b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          b[i] = as_u32(__builtin_elementwise_fma(as_h2(cv[i]), as_h2(sp[g]), as_h2(zp[g])));
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            afr[t], __builtin_bit_cast(h8, (u4v){b[0], b[1], b[2], b[3]}), c, 0, 0, 0);
+      }
+    }
+    if constexpr (OUT) {
+      const uint32_t row = (uint32_t)(((int)blockIdx.x + ri * (int)gridDim.x) * 16 + n16);
+      const uint32_t sh = ((row * (uint32_t)n_out + (uint32_t)cur_jlo) & 1u) * 16u;
+      uint32_t bw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bw[i] = __builtin_amdgcn_alignbit(it.od[i + 1], it.od[i], sh);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          __builtin_bit_cast(h8, (u4v){xo[0], xo[1], xo[2], xo[3]}),
+          __builtin_bit_cast(h8, (u4v){bw[0], bw[1], bw[2], bw[3]}), c, 0, 0, 0);
+    }
+    add_tile(c, ri, si);
+  };
+
+  int si = 0, ri = 0;
+  for (int base = 0; base < T; base += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      if (base + d < T) {
+        if (ri == 0) enter_slice(si);
+        compute(buf[d], ri, si);
+        advance(si, ri);
+      }
+      load_main(buf[d], base + d + DEPTH < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
+      load_slab(buf[d], base + d + DEPTH < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
+      advance(ls, lr);
+    }
+  }
+
+  // ---- outlier runs longer than 32 columns, after the weight stream
+  if constexpr (OUT) {
+    for (int s = 0; s < ns_w; ++s) {
+      const int ks = w + a.nw * s;
+      int j_lo, nin;
+      jrange(ks, j_lo, nin);
+      for (int c0 = 32; c0 < nin; c0 += 32) {
+        // activations of columns j_lo + c0 + 8q + e
+        uint32_t hv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j_lo + c0 + 8 * q + e;
+          const bool ok = c0 + 8 * q + e < nin;
+          const int col = ok ? (int)ld32(irs, (uint32_t)j * 4u) : 0;
+          hv[e] = ok ? (uint32_t)ld16(xrs, ((uint32_t)n16 * (uint32_t)a.K + (uint32_t)col) * 2u) : 0u;
+        }
+        const u4v xv = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
+                        hv[6] | (hv[7] << 16)};
+        for (int r2 = 0; r2 < nrb_wg; ++r2) {
+          const uint32_t row = (uint32_t)(((int)blockIdx.x + r2 * (int)gridDim.x) * 16 + n16);
+          const uint32_t e0 = row * (uint32_t)n_out + (uint32_t)(j_lo + c0 + 8 * q);
+          const uint32_t b0 = (e0 * 2u) & ~3u;
+          uint32_t od[5];
+#pragma unroll
+          for (int i = 0; i < 5; ++i) od[i] = ld32(ors, b0 + 4u * i);
+          uint32_t bw[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bw[i] = __builtin_amdgcn_alignbit(od[i + 1], od[i], (e0 & 1u) * 16u);
+          f4 c = {0.f, 0.f, 0.f, 0.f};
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(h8, xv), __builtin_bit_cast(h8, (u4v){bw[0], bw[1], bw[2], bw[3]}), c,
+              0, 0, 0);
+          add_tile(c, r2, 1);
+        }
+      }
+    }
+  }
+
+  // ---- fixed-order sum of the waves' tiles
+  __syncthreads();
+  for (int t = tid; t < nrb_wg * a.M * 16; t += nthr) {
+    const int n = t & 15, m = (t >> 4) % a.M, ri2 = (t >> 4) / a.M;
+    const int row = ((int)blockIdx.x + ri2 * (int)gridDim.x) * 16 + n;
+    if (row >= a.N) continue;
+    float s = 0.f;
+    for (int k = 0; k < a.nw; ++k)
+      s += s_part[(((uint32_t)ri2 * a.nw + k) * (uint32_t)a.M + (uint32_t)m) * 16u + (uint32_t)n];
+    a.Y[(size_t)m * a.N + row] = f2h(s);
+  }
+}
+
 // ------------------------------------------------------------- launch plan
 
 static int device_cus() {
@@ -638,6 +1116,46 @@ static MmaPlan plan_mma1(int fmt, int64_t N, int64_t K, int64_t n_out) {
   return p;
 }
 
+
+struct MmbPlan {
+  bool ok;
+  int nw, nks, nrb, grid, rbl, iv, depth;
+  size_t lds;
+};
+
+static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M) {
+  MmbPlan p{};
+  if (K % 128 != 0 || K > 65536 || n_out > 1024 || M < 2 || M > 16) return p;
+  const int64_t row_bytes = fmt == 4 ? K / 2 : K / 4;
+  if (N * row_bytes > 0xFFFFFFF0ll || N * (K / 32) * 2 > 0xFFFFFFF0ll ||
+      N * n_out * 2 > 0xFFFFFFF0ll || M * K * 2 > 0xFFFFFFF0ll)
+    return p;
+  p.nks = (int)((K + kSliceChB - 1) / kSliceChB);
+  if (p.nks <= kMaxWaves) {
+    p.nw = p.nks;
+  } else {
+    int best = -1;
+    for (int nw = kMaxWaves; nw >= 4; --nw) {
+      const int waste = ((p.nks + nw - 1) / nw) * nw - p.nks;
+      if (best < 0 || waste < best) {
+        best = waste;
+        p.nw = nw;
+      }
+    }
+  }
+  p.nrb = (int)((N + 15) / 16);
+  const int cus = device_cus();
+  if (cus <= 0) return p;
+  p.grid = std::min(p.nrb, cus);
+  p.rbl = (p.nrb + p.grid - 1) / p.grid;
+  p.iv = n_out == 0 ? 0 : n_out <= 256 ? 1 : n_out <= 512 ? 2 : 4;
+  p.lds = mmb_lds_layout(fmt, (int)M, p.nw, p.rbl).total;
+  if (p.lds > kMaxLdsBytes) return p;
+  p.depth = 2;
+  p.ok = true;
+  return p;
+}
+
 }  // namespace wqd
 
 using namespace wqd;
@@ -684,5 +1202,44 @@ int wqd_gemv_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
 #undef WQ_MMA_SLICES
 #undef WQ_MMA_DEPTHS
 #undef WQ_MMA_LAUNCH
+  return WQ_OK;
+}
+
+int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                 int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
+                 int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream,
+                 const char* who, int mode, bool* launched) {
+  *launched = false;
+  if (mode == 0) return WQ_OK;
+  const MmbPlan p = plan_mmb(fmt, N, K, n_out, M);
+  if (!p.ok) return WQ_OK;
+  MmbArgs a{};
+  a.codes = codes;
+  a.scales = scales;
+  a.zeros = zeros;
+  a.out_idx = out_idx;
+  a.out_w = out_w;
+  a.X = X;
+  a.Y = Y;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.M = (int)M;
+  a.n_out = (int)n_out;
+  a.nw = p.nw;
+  a.nks = p.nks;
+  a.nrb = p.nrb;
+  a.rbl = p.rbl;
+  const dim3 grid(p.grid), block(p.nw * kWave);
+#define WQ_MMB_LAUNCH(F_, IV_)                                                               \
+  if (fmt == F_ && p.iv == IV_) {                                                            \
+    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2>), p.lds))          \
+      return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds); \
+    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2>), grid, block, p.lds, stream, a);             \
+    *launched = true;                                                                        \
+    return check_launch(who);                                                                \
+  }
+  WQ_MMB_LAUNCH(4, 0) WQ_MMB_LAUNCH(4, 1) WQ_MMB_LAUNCH(4, 2) WQ_MMB_LAUNCH(4, 4)
+  WQ_MMB_LAUNCH(2, 0) WQ_MMB_LAUNCH(2, 1) WQ_MMB_LAUNCH(2, 2) WQ_MMB_LAUNCH(2, 4)
+#undef WQ_MMB_LAUNCH
   return WQ_OK;
 }

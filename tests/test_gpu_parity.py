@@ -163,11 +163,21 @@ def test_outlier_add_standalone():
 # ------------------------------------------------------------------ gemm
 
 
+@pytest.fixture(params=["tile", "mfma"])
+def gemm_path(request, monkeypatch):
+    """Runs a batched test on the per-group tile kernel and on the persistent
+    matrix-core kernel (the library's choice wherever the latter supports the
+    shape: K % 128 == 0, fused outliers, its LDS fits)."""
+    monkeypatch.setenv("WQ_GEMM_MMA", "0" if request.param == "tile" else "1")
+    return request.param
+
+
 @pytest.mark.parametrize("fmt", [4, 2])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 13, 16])
-@pytest.mark.parametrize("N,K,outl", [(129, 4096, False), (200, 2080, True), (64, 14336, True)])
-def test_gemm_small(fmt, M, N, K, outl):
-    say(f"gemm fmt={fmt} M={M} N={N} K={K} outliers={outl}")
+@pytest.mark.parametrize("N,K,outl", [(129, 4096, False), (200, 2080, True), (64, 14336, True),
+                                      (5000, 4224, True), (300, 8192, True), (40, 28672, True)])
+def test_gemm_small(fmt, M, N, K, outl, gemm_path):
+    say(f"gemm fmt={fmt} M={M} N={N} K={K} outliers={outl} path={gemm_path}")
     L = synthetic.small_layer(fmt, N, K, M=M, with_outliers=outl, seed=M)
     ref, dl = build(fmt, L.W, L.profile, L.ratio)
     X = dev_fp16(L.x)
