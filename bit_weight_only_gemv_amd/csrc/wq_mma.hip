@@ -220,21 +220,7 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     }
   };
 
-  // ---- (1) W2 centroid table: entry e (a code byte) -> its four FP16
-  //      centroids, 32 copies; slot s = 32 e + copy is written by consecutive
-  //      lanes (consecutive banks).  Shared by the workgroup: one barrier,
-  //      taken before the weight loads are issued.
-  if constexpr (FMT == 2) {
-    u2* lut = reinterpret_cast<u2*>(smem + L.lut);
-    for (int sl = tid; sl < 256 * 32; sl += nthr) {
-      const uint32_t e = (uint32_t)sl >> 5;
-      lut[sl] = (u2){w2_centroid_pair((e & 3u) | (((e >> 2) & 3u) << 16)),
-                     w2_centroid_pair(((e >> 4) & 3u) | ((e >> 6) << 16))};
-    }
-    lds_barrier();
-  }
-
-  // ---- (2) the first DEPTH row blocks' loads (every load is issued
+  // ---- (1) the first DEPTH row blocks' loads (every load is issued
   //      unconditionally; an item past the end reads nothing)
   // Offsets need no per-lane checks: rows past N and the bytes past the end
   // of a short last slice lie past the arrays (the loads return 0) or in the
@@ -277,6 +263,19 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   for (int d = 0; d < DEPTH; ++d) {
     load_main(buf[d], d < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
     advance(ls, lr);
+    if (d == 0 && FMT == 2) {
+      // W2 centroid table, written while the first row block is in flight:
+      // entry e (a code byte) -> its four FP16 centroids, 32 copies; slot
+      // s = 32 e + copy is written by consecutive lanes (consecutive banks).
+      // Shared by the workgroup: one barrier.
+      u2* lut = reinterpret_cast<u2*>(smem + L.lut);
+      for (int sl = tid; sl < 256 * 32; sl += nthr) {
+        const uint32_t e = (uint32_t)sl >> 5;
+        lut[sl] = (u2){w2_centroid_pair((e & 3u) | (((e >> 2) & 3u) << 16)),
+                       w2_centroid_pair(((e >> 4) & 3u) | ((e >> 6) << 16))};
+      }
+      lds_barrier();
+    }
   }
   // slab runs of these items: their offsets need the indices, whose wait is
   // pinned here, after the weight loads went out
@@ -299,7 +298,7 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     }
   }
 
-  // ---- (3) every slice of this wave set up in its LDS region: x masked at
+  // ---- (2) every slice of this wave set up in its LDS region: x masked at
   //      the outlier columns, their activations gathered, group sums of x
   //      (W4: scaled by 2^-24 like the code values)
   uint16_t* wxo16 = reinterpret_cast<uint16_t*>(smem + wxo);
@@ -514,7 +513,7 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     }
   };
 
-  // ---- (4) the items: compute one, refill its buffer with the one DEPTH
+  // ---- (3) the items: compute one, refill its buffer with the one DEPTH
   //      ahead.  Only the ring's loads are in this loop.
   int si = 0, ri = 0;   // slice / row-block counters of the item being computed
   for (int base = 0; base < T; base += DEPTH) {
@@ -531,7 +530,7 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     }
   }
 
-  // ---- (5) outlier runs longer than 32 columns: the remaining columns, row
+  // ---- (4) outlier runs longer than 32 columns: the remaining columns, row
   //      block by row block, after the weight stream
   if constexpr (OUT) {
     int xo_off = 0;
@@ -559,7 +558,7 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     }
   }
 
-  // ---- (6) fixed-order sum of the waves' row sums
+  // ---- (5) fixed-order sum of the waves' row sums
   __syncthreads();
   for (int t = tid; t < nrb_wg * 16; t += nthr) {
     const int ri2 = t >> 4, n = t & 15;
@@ -722,18 +721,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     }
   };
 
-  // ---- (1) W2 centroid table (one barrier, before the weight loads)
-  if constexpr (FMT == 2) {
-    u2* lut = reinterpret_cast<u2*>(smem + L.lut);
-    for (int sl = tid; sl < 256 * 32; sl += nthr) {
-      const uint32_t e = (uint32_t)sl >> 5;
-      lut[sl] = (u2){w2_centroid_pair((e & 3u) | (((e >> 2) & 3u) << 16)),
-                     w2_centroid_pair(((e >> 4) & 3u) | ((e >> 6) << 16))};
-    }
-    lds_barrier();
-  }
-
-  // ---- (2) the ring
+  // ---- (1) the ring
   auto load_main = [&](ItemB<FMT, OUT>& it, bool valid, int ks, int rb) {
     const __amdgpu_buffer_rsrc_t c_ = valid ? crs : nul;
     const __amdgpu_buffer_rsrc_t s_ = valid ? srs : nul;
@@ -770,6 +758,15 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   for (int d = 0; d < DEPTH; ++d) {
     load_main(buf[d], d < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
     advance(ls, lr);
+    if (d == 0 && FMT == 2) {   // W2 centroid table (as in the M = 1 kernel)
+      u2* lut = reinterpret_cast<u2*>(smem + L.lut);
+      for (int sl = tid; sl < 256 * 32; sl += nthr) {
+        const uint32_t e = (uint32_t)sl >> 5;
+        lut[sl] = (u2){w2_centroid_pair((e & 3u) | (((e >> 2) & 3u) << 16)),
+                       w2_centroid_pair(((e >> 4) & 3u) | ((e >> 6) << 16))};
+      }
+      lds_barrier();
+    }
   }
   if constexpr (OUT) {
 #pragma unroll
