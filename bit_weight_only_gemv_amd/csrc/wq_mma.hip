@@ -9,11 +9,11 @@
 // Layout of the work:
 //  * A workgroup owns row blocks of 16 rows (blockIdx.x, + gridDim.x, ...) and
 //    has nw waves; wave w owns the K-slices of 512 channels w, w + nw, ...
-//    A wave prepares each of its slices by itself, in an LDS region of its
-//    own (x of the slice, masked at the outlier columns; per-group sums of x;
-//    the slice's outlier activations), so no workgroup barrier sits between
-//    the weight loads and the first products.  Only the W2 centroid table is
-//    shared: it is written at entry, before the bulk of the loads.
+//    Each wave keeps its slices' x in an LDS region of its own (masked at the
+//    outlier columns, with per-group sums of x and the slice's outlier
+//    activations).  The set-up (W2 centroid table, x, outlier gather) runs
+//    while the first row blocks are in flight; its two workgroup barriers wait
+//    for LDS traffic only, never for the weight stream.
 //  * One MFMA multiplies a 16 x 32 A block by a 32 x 16 B block.  B holds
 //    decoded weights: lane (n, r) = (lane % 16, lane / 16) gives 8 weights of
 //    row n from its own 16-byte load (W4: one group; W2: two groups).  The
@@ -30,11 +30,13 @@
 //    copies, copy c at byte 8c of each 256-byte entry row, lane l reading copy
 //    l % 32.  Every lane thus reads its own bank pair (no bank conflicts), and
 //    the address (entry << 8 | 8 (l % 32)) is one byte permute of the code word.
-//  * Outlier columns: the indices are ascending, so the columns inside a
-//    slice are one contiguous run j_lo .. j_lo + nin of the FP16 slab.  The
-//    wave that owns the slice gathers their activations from its copy of x,
-//    zeroes them there, and dots the slab run with them (v_dot2) for each row
-//    block, 32 columns per step.
+//  * Outlier columns: slice ks owns the slab positions J(ks) .. J(ks + 1) - 1,
+//    J(ks) = floor(ks n_out / nks), at most 32 of them; lane quarter r takes
+//    8 consecutive positions.  The positions, not the columns they name, are
+//    split, so every slab load address is known at entry and the slab streams
+//    with the codes.  At set-up the lanes gather the outlier activations of
+//    their share from the workgroup's copy of x and zero those columns there;
+//    per row block the slab values are dotted with them (v_dot2).
 //  * Row-block loads go through a ring of DEPTH register buffers, so that
 //    while one row block is multiplied, the next ones are in flight.
 //  * Per row block each wave reduces its 4 lane quarters and adds its row
@@ -73,29 +75,23 @@ struct MmaArgs {
   int rbl;           // row blocks per workgroup, at most
 };
 
-// Per-wave LDS region: for each of its slices, x (1 KB, masked) and the 16
-// group sums (64 B); then the outlier activations of its slices, each run
-// followed by zeros up to the next multiple of 32 (at least 32 entries per
-// slice, so that every lane's first-step read is defined).
-__host__ __device__ inline int mma_run_pad(int nin) { return ((nin + 32) / 32) * 32; }
-__host__ __device__ inline uint32_t mma_xo_cap(int n_out, int nsw) {
-  return n_out > 0 ? (uint32_t)(((n_out + 31) / 32) * 32 + 32 * nsw) : 0u;
-}
-__host__ __device__ inline uint32_t mma_wave_bytes(int n_out, int nsw) {
-  return (uint32_t)nsw * 1088u + mma_xo_cap(n_out, nsw) * 2u;
-}
+// Per-wave LDS region: for each of its slices, x (1 KB, masked at the outlier
+// columns), the 16 group sums of x (64 B) and the 32 outlier activations of the
+// slice's share of the slab (64 B, zero past the share).
+constexpr uint32_t kSliceLds = 1024u + 64u + 64u;
+constexpr int kShareMax = 32;   // slab positions per slice, at most
 
 // LDS layout (byte offsets), identical on host and device.
 struct MmaLds {
   uint32_t lut, wave, part, total;
 };
-__host__ __device__ inline MmaLds mma_lds_layout(int fmt, int n_out, int nw, int nsw, int rbl) {
+__host__ __device__ inline MmaLds mma_lds_layout(int fmt, int nw, int nsw, int rbl) {
   MmaLds L{};
   uint32_t off = 0;
   L.lut = off;
   if (fmt == 2) off += 256u * kLutRow;
   L.wave = off;
-  off += (uint32_t)nw * mma_wave_bytes(n_out, nsw);
+  off += (uint32_t)nw * (uint32_t)nsw * kSliceLds;
   L.part = off;
   off += (uint32_t)rbl * (uint32_t)nw * 64u;
   L.total = off;
@@ -123,9 +119,9 @@ __device__ __forceinline__ u2 lds_ld64(uint32_t addr) {
   return *(const __attribute__((address_space(3))) u2*)(size_t)addr;
 }
 
-// Loads of one row block of one K-slice: codes, scales, zeros, and the first
-// 32 outlier columns of the slice (5 dwords per lane: 8 FP16 values that may
-// start at an odd index).
+// Loads of one row block of one K-slice: codes, scales, zeros, and the
+// slice's share of the outlier slab (5 dwords per lane: the 8 FP16 values of
+// the lane's positions, which may start at an odd index).
 template <int FMT, bool OUT>
 struct Item {
   u4v cw[MmaFmt<FMT>::kLoads];
@@ -134,24 +130,25 @@ struct Item {
 };
 
 // Dots 8 FP16 slab values (5 dwords starting at an even or odd FP16 index,
-// sh = 0 or 16) with 4 pairs of FP16 activations.
+// sh = 0 or 16) with 4 pairs of FP16 activations; keep clears the values past
+// the lane's share (they belong to other positions or rows, and an infinite
+// one must not meet a zero activation).
 __device__ __forceinline__ float slab_dot(const uint32_t (&od)[5], const uint32_t (&xw)[4],
-                                          uint32_t sh, float v) {
+                                          const uint32_t (&keep)[4], uint32_t sh, float v) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t wv = __builtin_amdgcn_alignbit(od[i + 1], od[i], sh);
+    const uint32_t wv = __builtin_amdgcn_alignbit(od[i + 1], od[i], sh) & keep[i];
     v = __builtin_amdgcn_fdot2(as_h2(wv), as_h2(xw[i]), v, false);
   }
   return v;
 }
 
-template <int FMT, int IV, int DEPTH, int NSW>
+template <int FMT, bool OUT, int DEPTH, int NSW>
 __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   typedef MmaFmt<FMT> F;
-  constexpr bool OUT = IV > 0;
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_out = OUT ? a.n_out : 0;
-  const MmaLds L = mma_lds_layout(FMT, n_out, a.nw, a.nsw, a.rbl);
+  const MmaLds L = mma_lds_layout(FMT, a.nw, a.nsw, a.rbl);
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int lane = tid & 63;
@@ -163,38 +160,30 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   const int nrb_wg = (a.nrb - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const int ns_w = (a.nks - w + a.nw - 1) / a.nw;   // 1 .. NSW (nw <= nks)
   const int T = ns_w * nrb_wg;                       // items of this wave
-  const uint32_t wreg = L.wave + (uint32_t)w * mma_wave_bytes(n_out, a.nsw);
-  const uint32_t wxo = wreg + (uint32_t)a.nsw * 1088u;
-  auto slice_x = [&](int s) { return wreg + (uint32_t)s * 1088u; };        // 1 KB of x
-  auto slice_sx = [&](int s) { return wreg + (uint32_t)s * 1088u + 1024u; };
+  const uint32_t wave_bytes = (uint32_t)a.nsw * kSliceLds;
+  const uint32_t wreg = L.wave + (uint32_t)w * wave_bytes;
+  auto slice_x = [&](int s) { return wreg + (uint32_t)s * kSliceLds; };   // 1 KB of x
+  auto slice_sx = [&](int s) { return wreg + (uint32_t)s * kSliceLds + 1024u; };
+  auto slice_xo = [&](int s) { return wreg + (uint32_t)s * kSliceLds + 1088u; };
+  // first slab position of slice ks (ks n_out < 2^31: the plan bounds both)
+  auto share_lo = [&](int ks) { return (uint32_t)(ks * n_out) / (uint32_t)a.nks; };
 
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(a.codes, clamp_bytes((uint64_t)a.N * row_bytes));
   const uint64_t meta = (uint64_t)a.N * G * 2;
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.scales, clamp_bytes(meta));
   const __amdgpu_buffer_rsrc_t zrs = make_rsrc(a.zeros, clamp_bytes(meta));
-  // The slab is read with 4-byte loads at 4-byte-aligned offsets and the
-  // indices with 16-byte loads; each record count is rounded up to that size,
-  // which stays inside the 16-byte block (and page) of the last element.
+  // The slab is read with 4-byte loads at 4-byte-aligned offsets; its record
+  // count is rounded up to that size, which stays inside the 16-byte block
+  // (and page) of the last element.
   const __amdgpu_buffer_rsrc_t ors =
       make_rsrc(a.out_w, clamp_bytes(((uint64_t)a.N * n_out * 2 + 3) & ~(uint64_t)3));
-  const __amdgpu_buffer_rsrc_t irs = make_rsrc(a.out_idx, ((uint32_t)n_out * 4u + 15u) & ~15u);
+  const __amdgpu_buffer_rsrc_t irs = make_rsrc(a.out_idx, (uint32_t)n_out * 4u);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.K * 2u);
 
-  // ---- (0) outlier indices (lane l holds idx[256 v + 4 l + k]; entries past
-  //      n_out are set, once they arrive, to a value that lies in no slice)
-  //      and x of every slice of this wave: issued before the weight stream,
-  //      so that waiting for them never waits for weights
-  int32_t oidx[IV > 0 ? IV : 1][4];
-  if constexpr (OUT) {
-#pragma unroll
-    for (int v = 0; v < IV; ++v) {
-      const u4v t = ld128(irs, (uint32_t)(256 * v + 4 * lane) * 4u);
-      oidx[v][0] = (int32_t)t.x;
-      oidx[v][1] = (int32_t)t.y;
-      oidx[v][2] = (int32_t)t.z;
-      oidx[v][3] = (int32_t)t.w;
-    }
-  }
+  // ---- (0) x of every slice of this wave and the outlier indices of its
+  //      slices' shares (lane l: slice 2p + l / 32, position l % 32 of the
+  //      share), issued before the weight stream so that waiting for them
+  //      never waits for weights
   u4v xr[NSW];
   const __amdgpu_buffer_rsrc_t xnul = make_rsrc(a.x, 0u);
 #pragma unroll
@@ -202,32 +191,29 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     const uint32_t c = (uint32_t)((w + a.nw * s) * kSliceCh + 8 * lane);
     xr[s] = ld128(s < ns_w ? xrs : xnul, c * 2u);
   }
-  asm volatile("" ::: "memory");   // these loads stay ahead of the weight stream
-  // outlier run of slice ks: j_lo = number of indices below it, nin inside it
-  auto jrange = [&](int ks, int& j_lo, int& nin) {
-    j_lo = 0;
-    nin = 0;
-    if constexpr (OUT) {
-      const int lo = ks * kSliceCh, hi = lo + kSliceCh;
+  constexpr int NIP = OUT ? (NSW + 1) / 2 : 1;
+  uint32_t oi[NIP];
+  bool oval[NIP];
+  if constexpr (OUT) {
 #pragma unroll
-      for (int v = 0; v < IV; ++v)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int c = oidx[v][k];
-          j_lo += __builtin_popcountll(__ballot(c < lo));
-          nin += __builtin_popcountll(__ballot(c >= lo && c < hi));
-        }
+    for (int p = 0; p < NIP; ++p) {
+      const int s = 2 * p + (lane >> 5);
+      const int ks = w + a.nw * s;
+      const uint32_t j = share_lo(ks) + (uint32_t)(lane & 31);
+      oval[p] = s < ns_w && j < share_lo(ks + 1);
+      oi[p] = ld32(irs, oval[p] ? j * 4u : kOob);
     }
-  };
+  }
+  asm volatile("" ::: "memory");   // these loads stay ahead of the weight stream
 
-  // ---- (1) the first DEPTH row blocks' loads (every load is issued
+  // ---- (1) loads of one row block of one slice (every load is issued
   //      unconditionally; an item past the end reads nothing)
   // Offsets need no per-lane checks: rows past N and the bytes past the end
   // of a short last slice lie past the arrays (the loads return 0) or in the
   // next row, where the activations are zero; an item past the end of the
   // wave's list reads through descriptors of zero records.
   const __amdgpu_buffer_rsrc_t nul = make_rsrc(a.codes, 0u);
-  auto load_main = [&](Item<FMT, OUT>& it, bool valid, int ks, int rb) {
+  auto load_item = [&](Item<FMT, OUT>& it, bool valid, int ks, int rb) {
     const __amdgpu_buffer_rsrc_t c_ = valid ? crs : nul;
     const __amdgpu_buffer_rsrc_t s_ = valid ? srs : nul;
     const __amdgpu_buffer_rsrc_t z_ = valid ? zrs : nul;
@@ -238,14 +224,9 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     const uint32_t mo = (row * (uint32_t)G + (uint32_t)(ks * kSliceGroups + 4 * r)) * 2u;
     it.sv = ld64(s_, mo);
     it.zv = ld64(z_, mo);
-  };
-  auto load_slab = [&](Item<FMT, OUT>& it, bool valid, int ks, int rb) {
     if constexpr (OUT) {
-      int j_lo, nin;
-      jrange(ks, j_lo, nin);
       const __amdgpu_buffer_rsrc_t o_ = valid ? ors : nul;
-      const uint32_t row = (uint32_t)(rb * 16 + n16);
-      const uint32_t e0 = row * (uint32_t)n_out + (uint32_t)(j_lo + 8 * r);
+      const uint32_t e0 = row * (uint32_t)n_out + share_lo(ks) + 8u * (uint32_t)r;
       const uint32_t b0 = (e0 * 2u) & ~3u;
 #pragma unroll
       for (int i = 0; i < 5; ++i) it.od[i] = ld32(o_, b0 + 4u * i);
@@ -258,113 +239,105 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
       ++s_;
     }
   };
-  Item<FMT, OUT> buf[DEPTH];
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    load_main(buf[d], d < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
-    advance(ls, lr);
-    if (d == 0 && FMT == 2) {
-      // W2 centroid table, written while the first row block is in flight:
-      // entry e (a code byte) -> its four FP16 centroids, 32 copies; slot
-      // s = 32 e + copy is written by consecutive lanes (consecutive banks).
-      // Shared by the workgroup: one barrier.
-      u2* lut = reinterpret_cast<u2*>(smem + L.lut);
-      for (int sl = tid; sl < 256 * 32; sl += nthr) {
-        const uint32_t e = (uint32_t)sl >> 5;
-        lut[sl] = (u2){w2_centroid_pair((e & 3u) | (((e >> 2) & 3u) << 16)),
-                       w2_centroid_pair(((e >> 4) & 3u) | ((e >> 6) << 16))};
+  // W2 centroid table: entry e (a code byte) -> its four FP16 centroids, 32
+  // copies in a 256-byte row; 16-byte chunk ch holds copies 2 (ch % 16) and
+  // 2 (ch % 16) + 1 of entry ch / 16, and consecutive lanes write consecutive
+  // chunks.
+  auto build_lut = [&]() {
+    if constexpr (FMT == 2) {
+      u4v* lut = reinterpret_cast<u4v*>(smem + L.lut);
+      for (int ch = tid; ch < 256 * 16; ch += nthr) {
+        const uint32_t e = (uint32_t)ch >> 4;
+        const uint32_t lo = w2_centroid_pair((e & 3u) | (((e >> 2) & 3u) << 16));
+        const uint32_t hi = w2_centroid_pair(((e >> 4) & 3u) | ((e >> 6) << 16));
+        lut[ch] = (u4v){lo, hi, lo, hi};
       }
-      lds_barrier();
     }
-  }
-  // slab runs of these items: their offsets need the indices, whose wait is
-  // pinned here, after the weight loads went out
-  if constexpr (OUT) {
-#pragma unroll
-    for (int v = 0; v < IV; ++v)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        asm volatile("" : "+v"(oidx[v][k])::"memory");
-        const uint32_t j = (uint32_t)(256 * v + 4 * lane + k);
-        if (j >= (uint32_t)n_out) oidx[v][k] = 0x7FFFFFFF;
-      }
-  }
-  {
-    int s2 = 0, r2 = 0;
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      load_slab(buf[d], d < T, w + a.nw * s2, blockIdx.x + r2 * gridDim.x);
-      advance(s2, r2);
-    }
-  }
+  };
 
-  // ---- (2) every slice of this wave set up in its LDS region: x masked at
-  //      the outlier columns, their activations gathered, group sums of x
-  //      (W4: scaled by 2^-24 like the code values)
-  uint16_t* wxo16 = reinterpret_cast<uint16_t*>(smem + wxo);
-  {
-    int xo_off = 0;
+  // ---- (2) set-up: every wave stores x of its slices; after a barrier each
+  //      lane gathers the activations of its outlier positions (from whichever
+  //      wave holds the column) and zeroes the column there; after a second
+  //      barrier each wave sums the groups of its masked slices (W4: scaled by
+  //      2^-24 like the code values)
+  auto setup = [&]() {
+#pragma unroll
+    for (int s = 0; s < NSW; ++s)
+      if (s < ns_w) reinterpret_cast<u4v*>(smem + slice_x(s))[lane] = xr[s];
+    lds_barrier();   // x of every wave, and the W2 table, visible
+    if constexpr (OUT) {
+#pragma unroll
+      for (int p = 0; p < NIP; ++p) {
+        const int s = 2 * p + (lane >> 5);
+        const uint32_t c = oi[p];
+        const bool v = oval[p] && c < (uint32_t)a.K;
+        uint16_t xv = 0;
+        if (v) {   // column c: slice c / 512, held by wave (c / 512) % nw as its slice (c / 512) / nw
+          const uint32_t kc = c >> 9;
+          const uint32_t wc = kc % (uint32_t)a.nw, sc = kc / (uint32_t)a.nw;
+          uint16_t* xp = reinterpret_cast<uint16_t*>(smem + L.wave + wc * wave_bytes +
+                                                     sc * kSliceLds + (c & 511u) * 2u);
+          xv = *xp;
+          *xp = 0;
+        }
+        if (s < ns_w) reinterpret_cast<uint16_t*>(smem + slice_xo(s))[lane & 31] = xv;
+      }
+      lds_barrier();   // every outlier column of x zeroed
+    }
 #pragma unroll
     for (int s = 0; s < NSW; ++s) {
-      if (s < ns_w) {
-        const int ks = w + a.nw * s;
-        reinterpret_cast<u4v*>(smem + slice_x(s))[lane] = xr[s];
-        uint16_t* x16 = reinterpret_cast<uint16_t*>(smem + slice_x(s));
-        if constexpr (OUT) {
-          int j_lo, nin;
-          jrange(ks, j_lo, nin);
-          const int lo = ks * kSliceCh;
-          const int nz = mma_run_pad(nin);
-          for (int j = lane; j < nz; j += kWave) wxo16[xo_off + j] = 0;
+      if (s < ns_w && lane < kSliceGroups) {
+        float sum = 0.f;
+        const u4v* src = reinterpret_cast<const u4v*>(smem + slice_x(s) + (uint32_t)lane * 64u);
 #pragma unroll
-          for (int v = 0; v < IV; ++v)
+        for (int v = 0; v < 4; ++v) {
+          const u4v t = src[v];
+          const uint32_t tw[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const int c = oidx[v][k] - lo;
-              if (c >= 0 && c < kSliceCh) wxo16[xo_off + 256 * v + 4 * lane + k - j_lo] = x16[c];
-            }
-#pragma unroll
-          for (int v = 0; v < IV; ++v)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const int c = oidx[v][k] - lo;
-              if (c >= 0 && c < kSliceCh) x16[c] = 0;
-            }
-          xo_off += nz;
+          for (int i = 0; i < 4; ++i)
+            sum = __builtin_amdgcn_fdot2(as_h2(tw[i]), as_h2(0x3C003C00u), sum, false);
         }
-        if (lane < kSliceGroups) {
-          float sum = 0.f;
-          const u4v* src = reinterpret_cast<const u4v*>(smem + slice_x(s) + (uint32_t)lane * 64u);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const u4v t = src[v];
-            const uint32_t tw[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              sum = __builtin_amdgcn_fdot2(as_h2(tw[i]), as_h2(0x3C003C00u), sum, false);
-          }
-          reinterpret_cast<float*>(smem + slice_sx(s))[lane] =
-              FMT == 4 ? sum * 5.9604644775390625e-8f : sum;
-        }
+        reinterpret_cast<float*>(smem + slice_sx(s))[lane] =
+            FMT == 4 ? sum * 5.9604644775390625e-8f : sum;
       }
     }
+  };
+
+  // ---- (3) the prologue: the first row block's loads go out, the table is
+  //      written and the set-up runs while they are in flight, and only then
+  //      is the rest of the ring issued (measured on MI355X: issuing the
+  //      whole ring at entry delays the first row block behind the others
+  //      and costs more than the overlap gains)
+  Item<FMT, OUT> buf[DEPTH];
+  load_item(buf[0], 0 < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
+  advance(ls, lr);
+  build_lut();
+  setup();
+#pragma unroll
+  for (int d = 1; d < DEPTH; ++d) {
+    load_item(buf[d], d < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
+    advance(ls, lr);
   }
 
-  // ---- A fragments, group sums and first-run outlier activations of slice s
+  // ---- A fragments, group sums and outlier activations of slice s
   h8 afr[16];
   f4 sx4 = {0.f, 0.f, 0.f, 0.f};
   uint32_t xo0[4] = {0u, 0u, 0u, 0u};
-  int cur_jlo = 0, cur_nin = 0, cur_xo = 0;
+  uint32_t keep[4] = {0u, 0u, 0u, 0u};
+  uint32_t cur_j = 0;
   auto enter_slice = [&](int s) {
     const int ks = w + a.nw * s;
     if constexpr (OUT) {
-      if (s > 0) cur_xo += mma_run_pad(cur_nin);
-      jrange(ks, cur_jlo, cur_nin);
-      const u4v v = *reinterpret_cast<const u4v*>(smem + wxo + (uint32_t)(cur_xo + 8 * r) * 2u);
+      cur_j = share_lo(ks);
+      const int cnt = (int)(share_lo(ks + 1) - cur_j) - 8 * r;   // valid positions of the lane
+      const u4v v = *reinterpret_cast<const u4v*>(smem + slice_xo(s) + (uint32_t)r * 16u);
       xo0[0] = v.x;
       xo0[1] = v.y;
       xo0[2] = v.z;
       xo0[3] = v.w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        keep[i] = 2 * i + 1 < cnt ? 0xFFFFFFFFu : 2 * i < cnt ? 0x0000FFFFu : 0u;
     }
     sx4 = *reinterpret_cast<const f4*>(smem + slice_sx(s) + (uint32_t)r * 16u);
     // A: the lane of slot m = lane % 16 whose k-quarter holds group m carries
@@ -422,8 +395,8 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     }
   };
 
-  // ---- one row block of one slice: products, slot scales, the first 32
-  //      outlier columns of the slice, reduction of the lane quarters
+  // ---- one row block of one slice: products, slot scales, the slice's share
+  //      of the outlier slab, reduction of the lane quarters
   float* s_part = reinterpret_cast<float*>(smem + L.part);
   const uint32_t lut_lane = (uint32_t)(lane & 31) * 8u;
   auto compute = [&](const Item<FMT, OUT>& it, int ri, int si) {
@@ -501,8 +474,8 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     }
     if constexpr (FMT == 4) v *= 16777216.0f;
     if constexpr (OUT) {
-      const uint32_t sh = (((uint32_t)row * (uint32_t)n_out + (uint32_t)cur_jlo) & 1u) * 16u;
-      v = slab_dot(it.od, xo0, sh, v);
+      const uint32_t sh = (((uint32_t)row * (uint32_t)n_out + cur_j) & 1u) * 16u;
+      v = slab_dot(it.od, xo0, keep, sh, v);
     }
     // the four lane quarters hold the same row: add them
     v += __shfl_xor(v, 16);
@@ -513,7 +486,7 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     }
   };
 
-  // ---- (3) the items: compute one, refill its buffer with the one DEPTH
+  // ---- (4) the items: compute one, refill its buffer with the one DEPTH
   //      ahead.  Only the ring's loads are in this loop.
   int si = 0, ri = 0;   // slice / row-block counters of the item being computed
   for (int base = 0; base < T; base += DEPTH) {
@@ -524,37 +497,8 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
         compute(buf[d], ri, si);
         advance(si, ri);
       }
-      load_main(buf[d], base + d + DEPTH < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
-      load_slab(buf[d], base + d + DEPTH < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
+      load_item(buf[d], base + d + DEPTH < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
       advance(ls, lr);
-    }
-  }
-
-  // ---- (4) outlier runs longer than 32 columns: the remaining columns, row
-  //      block by row block, after the weight stream
-  if constexpr (OUT) {
-    int xo_off = 0;
-    for (int s = 0; s < ns_w; ++s) {
-      int j_lo, nin;
-      jrange(w + a.nw * s, j_lo, nin);
-      for (int c = 32; c < nin; c += 32) {
-        const u4v xv = *reinterpret_cast<const u4v*>(smem + wxo + (uint32_t)(xo_off + c + 8 * r) * 2u);
-        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-        for (int q = 0; q < nrb_wg; ++q) {
-          const int row = (int)(blockIdx.x + (unsigned)q * gridDim.x) * 16 + n16;
-          const bool ok = row < a.N && c + 8 * r < nin;
-          const uint32_t e0 = (uint32_t)row * (uint32_t)n_out + (uint32_t)(j_lo + c + 8 * r);
-          const uint32_t b0 = (e0 * 2u) & ~3u;
-          uint32_t od[5];
-#pragma unroll
-          for (int i = 0; i < 5; ++i) od[i] = ld32(ors, ok ? b0 + 4u * i : kOob);
-          float v = slab_dot(od, xw, (e0 & 1u) * 16u, 0.f);
-          v += __shfl_xor(v, 16);
-          v += __shfl_xor(v, 32);
-          if (r == 0) s_part[((uint32_t)q * (uint32_t)a.nw + (uint32_t)w) * 16u + (uint32_t)n16] += v;
-        }
-      }
-      xo_off += mma_run_pad(nin);
     }
   }
 
@@ -677,8 +621,8 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.X, clamp_bytes((uint64_t)a.M * a.K * 2));
   const __amdgpu_buffer_rsrc_t nul = make_rsrc(a.codes, 0u);
 
-  // ---- (0) outlier indices (as in the M = 1 kernel), then the activation
-  //      rows of this wave's first slice
+  // ---- (0) outlier indices (lane l holds idx[256 v + 4 l + k]), then the
+  //      activation rows of this wave's first slice
   int32_t oidx[IV > 0 ? IV : 1][4];
   if constexpr (OUT) {
 #pragma unroll
@@ -1063,18 +1007,20 @@ static int device_cus() {
 
 struct MmaPlan {
   bool ok, preferred;
-  int nw, nks, nsw, nswt, nrb, grid, rbl, iv, depth;
+  int nw, nks, nsw, nswt, nrb, grid, rbl, depth;
   size_t lds;
 };
 
 static MmaPlan plan_mma1(int fmt, int64_t N, int64_t K, int64_t n_out) {
   MmaPlan p{};
-  if (K % 128 != 0 || K > 65536 || n_out > 1024) return p;
+  if (K % 128 != 0 || K > 65536) return p;
   const int64_t row_bytes = fmt == 4 ? K / 2 : K / 4;
   if (N * row_bytes > 0xFFFFFFF0ll || N * (K / 32) * 2 > 0xFFFFFFF0ll ||
       N * n_out * 2 > 0xFFFFFFF0ll)
     return p;
   p.nks = (int)((K + kSliceCh - 1) / kSliceCh);
+  // every slice's share of the outlier slab fits one lane quarter each (8 x 4)
+  if (n_out > (int64_t)kShareMax * p.nks) return p;
   if (p.nks <= kMaxWaves) {
     p.nw = p.nks;
   } else {
@@ -1095,8 +1041,7 @@ static MmaPlan plan_mma1(int fmt, int64_t N, int64_t K, int64_t n_out) {
   if (cus <= 0) return p;
   p.grid = std::min(p.nrb, cus);
   p.rbl = (p.nrb + p.grid - 1) / p.grid;
-  p.iv = n_out == 0 ? 0 : n_out <= 256 ? 1 : n_out <= 512 ? 2 : 4;
-  const MmaLds L = mma_lds_layout(fmt, (int)n_out, p.nw, p.nsw, p.rbl);
+  const MmaLds L = mma_lds_layout(fmt, p.nw, p.nsw, p.rbl);
   p.lds = L.total;
   if (p.lds > kMaxLdsBytes) return p;
   p.depth = 2;
@@ -1182,20 +1127,19 @@ int wqd_gemv_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
   a.nrb = p.nrb;
   a.rbl = p.rbl;
   const dim3 grid(p.grid), block(p.nw * kWave);
-#define WQ_MMA_LAUNCH(F_, IV_, D_, S_)                                                       \
-  if (fmt == F_ && p.iv == IV_ && p.depth == D_ && p.nswt == S_) {                           \
-    if (!allow_lds(reinterpret_cast<const void*>(&mma1d_kernel<F_, IV_, D_, S_>), p.lds))   \
+#define WQ_MMA_LAUNCH(F_, O_, D_, S_)                                                        \
+  if (fmt == F_ && (n_out > 0) == O_ && p.depth == D_ && p.nswt == S_) {                     \
+    if (!allow_lds(reinterpret_cast<const void*>(&mma1d_kernel<F_, O_, D_, S_>), p.lds))    \
       return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds); \
-    hipLaunchKernelGGL((mma1d_kernel<F_, IV_, D_, S_>), grid, block, p.lds, stream, a);      \
+    hipLaunchKernelGGL((mma1d_kernel<F_, O_, D_, S_>), grid, block, p.lds, stream, a);       \
     *launched = true;                                                                        \
     return check_launch(who);                                                                \
   }
-#define WQ_MMA_SLICES(F_, IV_, D_) \
-  WQ_MMA_LAUNCH(F_, IV_, D_, 1) WQ_MMA_LAUNCH(F_, IV_, D_, 2) WQ_MMA_LAUNCH(F_, IV_, D_, 4) \
-  WQ_MMA_LAUNCH(F_, IV_, D_, 8)
-#define WQ_MMA_DEPTHS(F_, IV_) WQ_MMA_SLICES(F_, IV_, 2) WQ_MMA_SLICES(F_, IV_, 4)
-  WQ_MMA_DEPTHS(4, 0) WQ_MMA_DEPTHS(4, 1) WQ_MMA_DEPTHS(4, 2) WQ_MMA_DEPTHS(4, 4)
-  WQ_MMA_DEPTHS(2, 0) WQ_MMA_DEPTHS(2, 1) WQ_MMA_DEPTHS(2, 2) WQ_MMA_DEPTHS(2, 4)
+#define WQ_MMA_SLICES(F_, O_, D_) \
+  WQ_MMA_LAUNCH(F_, O_, D_, 1) WQ_MMA_LAUNCH(F_, O_, D_, 2) WQ_MMA_LAUNCH(F_, O_, D_, 4) \
+  WQ_MMA_LAUNCH(F_, O_, D_, 8)
+#define WQ_MMA_DEPTHS(F_, O_) WQ_MMA_SLICES(F_, O_, 2) WQ_MMA_SLICES(F_, O_, 4)
+  WQ_MMA_DEPTHS(4, false) WQ_MMA_DEPTHS(4, true) WQ_MMA_DEPTHS(2, false) WQ_MMA_DEPTHS(2, true)
 #undef WQ_MMA_SLICES
 #undef WQ_MMA_DEPTHS
 #undef WQ_MMA_LAUNCH
