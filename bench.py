@@ -56,6 +56,9 @@ def _parse():
                    help="bytes per launch of the read / copy workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true", help="time Python-side launches, no graph")
+    p.add_argument("--layout", default="tiled", choices=["tiled", "rowmajor"],
+                   help="packed-array layout the M = 1 GEMV workloads time for `value` (the "
+                        "other one is timed too and reported beside it)")
     return p.parse_args()
 
 
@@ -127,6 +130,8 @@ def clone_layer(DeviceLayer, base):
     c.codes, c.scales, c.zeros = base.codes.clone(), base.scales.clone(), base.zeros.clone()
     if base.n_out:
         c.idx, c.wout = base.idx.clone(), base.wout.clone()
+    if base.tiled is not None:
+        c.tiled = base.tiled.clone()
     return c
 
 
@@ -155,7 +160,7 @@ def gemv_workload(a, torch, L, label, timer):
     t0 = time.time()
     hl = pack_host(L.fmt, L.W, L.profile, L.ratio)
     pack_s = time.time() - t0
-    base = DeviceLayer(hl)
+    base = DeviceLayer(hl, tiled=True)
     nbytes = base.nbytes(1)
     layers = rotated(DeviceLayer, base, nbytes)
     ncopy = len(layers)
@@ -163,13 +168,19 @@ def gemv_workload(a, torch, L, label, timer):
     ys = [torch.empty(base.N, dtype=torch.int16, device="cuda") for _ in range(ncopy)]
     torch.cuda.synchronize()
 
-    def step(i):
+    def step_rowmajor(i):
         layers[i % ncopy].gemv(x, ys[i % ncopy])
 
-    ms = timer(step, a.steps, a.warmup)
+    def step_tiled(i):
+        layers[i % ncopy].gemv_tiled(x, ys[i % ncopy])
+
+    other = "rowmajor" if a.layout == "tiled" else "tiled"
+    steps = {"rowmajor": step_rowmajor, "tiled": step_tiled}
+    ms_other = timer(steps[other], a.steps, a.warmup)
+    ms = timer(steps[a.layout], a.steps, a.warmup)
     gbs = nbytes / (ms * 1e-3) / 1e9
     bpt = sweep_bytes_per_token(L.fmt, L.ratio)
-    traffic = traffic_for(label)
+    traffic = traffic_for(f"{label}_{a.layout}")
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -185,12 +196,14 @@ def gemv_workload(a, torch, L, label, timer):
         "data": "synthetic (seeded Gaussian weights and activations; no checkpoint)",
         "config": {"workload": label, "N": base.N, "K": base.K, "M": 1, "n_out": base.n_out,
                    "format": f"W{L.fmt} group-32", "accumulate": "f32",
-                   "bytes_per_step": nbytes, "rotated_copies": ncopy,
+                   "bytes_per_step": nbytes, "rotated_copies": ncopy, "layout": a.layout,
                    "timing": "eager launches" if a.eager else "hip graph replay"},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "eq_tokens_per_s": round(gbs * 1e9 / bpt, 1),
         "eq_tokens_basis_bytes_per_token": bpt,
         "host_pack_s": round(pack_s, 2),
+        f"{other}_layout": {"us": round(ms_other * 1e3, 3),
+                            "GB/s": round(nbytes / (ms_other * 1e-3) / 1e9, 2)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
@@ -274,21 +287,25 @@ def w2_70b_workload(a, torch, timer):
     rows = []
     for (N, K) in ((28672, 8192), (8192, 28672)):
         L8 = synthetic.config5(N, K, 8)
-        base = DeviceLayer(pack_host(2, L8.W, L8.profile, L8.ratio))
-        for M in (1, 8):
+        base = DeviceLayer(pack_host(2, L8.W, L8.profile, L8.ratio), tiled=True)
+        for M, layout in ((1, "rowmajor"), (1, "tiled"), (8, "rowmajor")):
             nbytes = base.nbytes(M)
             layers = rotated(DeviceLayer, base, nbytes)
             nc = len(layers)
             X = torch.from_numpy(np.ascontiguousarray(L8.x[:M]).view(np.int16)).cuda()
             Y = [torch.empty((M, N), dtype=torch.int16, device="cuda") for _ in range(nc)]
-            if M == 1:
+            if M == 1 and layout == "tiled":
+                fn = lambda i: layers[i % nc].gemv_tiled(X[0], Y[i % nc][0])  # noqa: E731
+            elif M == 1:
                 fn = lambda i: layers[i % nc].gemv(X[0], Y[i % nc][0])  # noqa: E731
             else:
                 fn = lambda i: layers[i % nc].gemm(X, Y[i % nc])  # noqa: E731
             ms = timer(fn, a.steps // 4, a.warmup // 4)
-            rows.append({"workload": f"w2_{N}x{K}_outliers{base.n_out}_m{M}", "bytes": nbytes,
-                         "us": round(ms * 1e3, 3), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            rows.append({"workload": f"w2_{N}x{K}_outliers{base.n_out}_m{M}", "layout": layout,
+                         "bytes": nbytes, "us": round(ms * 1e3, 3),
+                         "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                          "pct_of_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)})
+            del layers
     return rows
 
 

@@ -52,6 +52,9 @@ SIGNATURES = {
     "wq_gemv_w2": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _P, _P]),
     "wq_gemm_wq": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _I64, _P, _P]),
     "wq_outlier_add": (_INT, [_P, _P, _I64, _I64, _P, _I64, _I64, _P, _P]),
+    "wq_tiled_bytes": (_I64, [_INT, _I64, _I64, _I64]),
+    "wq_tile_host": (_INT, [_INT, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64]),
+    "wq_gemv_tiled": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
     "wq_read_probe": (_INT, [_P, _I64, _P, _P]),
     "wq_read_probe_sink_words": (_I64, [_I64]),
     "wq_copy_probe": (_INT, [_P, _P, _I64, _P]),
@@ -157,6 +160,27 @@ def wq_dequant_host(fmt: int, codes, scales, zeros, N: int, K: int) -> np.ndarra
     return out.view(np.float16)
 
 
+def wq_tiled_bytes(fmt: int, N: int, K: int, n_out: int) -> int:
+    n = int(load().wq_tiled_bytes(fmt, N, K, n_out))
+    if n < 0:
+        _check(n)
+    return n
+
+
+def wq_tile_host(fmt: int, codes, scales, zeros, out_w, N: int, K: int) -> np.ndarray:
+    """Row-major packed arrays -> the tiled M = 1 layout (uint8 array)."""
+    n_out = 0 if out_w is None else int(np.asarray(out_w).shape[1])
+    codes = _c(codes, np.uint8)
+    sc = _c(np.asarray(scales).view(np.uint16), np.uint16)
+    ze = _c(np.asarray(zeros).view(np.uint16), np.uint16)
+    ow = _c(np.asarray(out_w).view(np.uint16), np.uint16) if n_out else None
+    nb = wq_tiled_bytes(fmt, N, K, n_out)
+    out = np.empty(nb, np.uint8)
+    _check(load().wq_tile_host(fmt, _np_ptr(codes), _np_ptr(sc), _np_ptr(ze),
+                               _np_ptr(ow) if n_out else None, N, K, n_out, _np_ptr(out), nb))
+    return out
+
+
 # ---------------------------------------------------------------- device
 
 
@@ -201,6 +225,11 @@ def wq_gemm_wq(fmt, codes, scales, zeros, N, K, X, M, Y, out_idx=None, out_w=Non
     _check(load().wq_gemm_wq(fmt, _dptr(codes), _dptr(scales), _dptr(zeros), N, K,
                              _dptr(out_idx) if n_out else None, _dptr(out_w) if n_out else None,
                              n_out, flags, _dptr(X), M, _dptr(Y), _stream(stream)))
+
+
+def wq_gemv_tiled(fmt, tiled, N, K, x, y, out_idx=None, n_out=0, stream=None):
+    _check(load().wq_gemv_tiled(fmt, _dptr(tiled), N, K, _dptr(out_idx) if n_out else None, n_out,
+                                _dptr(x), _dptr(y), _stream(stream)))
 
 
 def wq_outlier_add(idx, out_w, n_out, N, X, M, K, Y, stream=None):

@@ -756,7 +756,7 @@ static int gemv_entry(int fmt, const uint8_t* codes, const uint16_t* scales, con
     int mode = 1;
     if (const char* e = getenv("WQ_GEMV_MMA")) mode = atoi(e);
     bool launched = false;
-    const int r = wqd_gemv_mma(fmt, codes, scales, zeros, N, K, out_idx, out_w,
+    const int r = wqd_gemv_mma(fmt, false, codes, scales, zeros, N, K, out_idx, out_w,
                                a.fuse ? n_out : 0, x, y, s, who, mode, &launched);
     if (r != WQ_OK || launched) return r;
   }
@@ -777,4 +777,29 @@ extern "C" int wq_gemv_w2(const uint8_t* codes, const uint16_t* scales, const ui
                           void* stream) {
   return gemv_entry(2, codes, scales, zeros, N, K, out_idx, out_w, n_out, flags, x, y, stream,
                     "wq_gemv_w2");
+}
+
+extern "C" int wq_gemv_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
+                             const int32_t* out_idx, int64_t n_out, const uint16_t* x,
+                             uint16_t* y, void* stream) {
+  const char* who = "wq_gemv_tiled";
+  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4 or WQ_FMT_W2", who);
+  if (int r = wq::check_shape(N, K, who)) return r;
+  if (n_out < 0 || n_out > K)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: n_out must be in [0, K] (got %lld)", who,
+                    (long long)n_out);
+  if (!tiled || !x || !y || (n_out > 0 && !out_idx))
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (!aligned16(tiled) || !aligned16(x) || !aligned16(y) || (n_out > 0 && !aligned16(out_idx)))
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: device pointers must be 16-byte aligned", who);
+  bool launched = false;
+  const int r = wqd_gemv_mma(fmt, true, tiled, nullptr, nullptr, N, K, out_idx, nullptr, n_out, x,
+                             y, (hipStream_t)stream, who, 2, &launched);
+  if (r != WQ_OK) return r;
+  if (!launched)
+    return wq::fail(WQ_ERR_UNSUPPORTED,
+                    "%s: shape not supported by the tiled kernel (K <= 32768 and at most 32 "
+                    "outlier positions per 512-channel slice)", who);
+  return WQ_OK;
 }

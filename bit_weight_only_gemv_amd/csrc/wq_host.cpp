@@ -339,4 +339,69 @@ int wq_dequant_host(int fmt, const uint8_t* codes, const uint16_t* scales, const
   return wq::ok();
 }
 
+int64_t wq_tiled_bytes(int fmt, int64_t N, int64_t K, int64_t n_out) {
+  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2)
+    return fail(WQ_ERR_INVALID_ARG, "wq_tiled_bytes: fmt must be WQ_FMT_W4 or WQ_FMT_W2");
+  if (int r = wq::check_shape(N, K, "wq_tiled_bytes")) return r;
+  if (n_out < 0 || n_out > K)
+    return fail(WQ_ERR_INVALID_ARG, "wq_tiled_bytes: n_out must be in [0, K]");
+  wq::ok();
+  return wq::tiled_geometry(fmt, N, K, n_out).total;
+}
+
+int wq_tile_host(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                 const uint16_t* out_w, int64_t N, int64_t K, int64_t n_out, uint8_t* tiled,
+                 int64_t tiled_bytes) {
+  const int64_t need = wq_tiled_bytes(fmt, N, K, n_out);
+  if (need < 0) return (int)need;
+  if (!codes || !scales || !zeros || !tiled || (n_out > 0 && !out_w))
+    return fail(WQ_ERR_INVALID_ARG, "wq_tile_host: NULL pointer");
+  if (tiled_bytes < need)
+    return fail(WQ_ERR_INVALID_ARG, "wq_tile_host: tiled buffer holds %lld bytes, %lld needed",
+                (long long)tiled_bytes, (long long)need);
+  const wq::TiledGeometry g = wq::tiled_geometry(fmt, N, K, n_out);
+  const int64_t row_bytes = fmt == WQ_FMT_W4 ? K / 2 : K / 4;
+  const int64_t G = K / WQ_GROUP;
+  const int64_t SB = g.slice_bytes;
+  std::memset(tiled, 0, (size_t)g.total);
+  auto put16 = [](uint8_t* dst, uint16_t v) { std::memcpy(dst, &v, 2); };
+  for (int64_t b = 0; b < g.nrb; ++b) {
+    for (int64_t s = 0; s < g.nks; ++s) {
+      const int64_t tile = b * g.nks + s;
+      uint8_t* ct = tiled + g.codes_off + tile * 16 * SB;
+      uint8_t* mt = tiled + g.meta_off + tile * 1024;
+      for (int64_t n = 0; n < 16; ++n) {
+        const int64_t row = 16 * b + n;
+        if (row >= N) break;
+        for (int64_t r = 0; r < 4; ++r) {
+          const int64_t lane = n + 16 * r;
+          for (int64_t u = 0; u < SB / 64; ++u)
+            for (int64_t c = 0; c < 16; ++c) {
+              const int64_t col = s * SB + 64 * u + 16 * r + c;
+              if (col < row_bytes) ct[1024 * u + 16 * lane + c] = codes[row * row_bytes + col];
+            }
+          for (int64_t i = 0; i < 4; ++i) {
+            const int64_t grp = 16 * s + 4 * r + i;
+            if (grp >= G) continue;
+            put16(mt + 2 * (8 * lane + i), scales[row * G + grp]);
+            put16(mt + 2 * (8 * lane + 4 + i), zeros[row * G + grp]);
+          }
+        }
+      }
+    }
+    for (int64_t c = 0; c < g.nch; ++c) {
+      uint8_t* ot = tiled + g.slab_off + (b * g.nch + c) * 256;
+      for (int64_t n = 0; n < 16; ++n) {
+        const int64_t row = 16 * b + n;
+        if (row >= N) break;
+        for (int64_t i = 0; i < 8; ++i) {
+          const int64_t j = 8 * c + i;
+          if (j < n_out) put16(ot + 2 * (8 * n + i), out_w[row * n_out + j]);
+        }
+      }
+    }
+  }
+  return wq::ok();
+}
+
 }  // extern "C"

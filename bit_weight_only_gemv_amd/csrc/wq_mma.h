@@ -8,11 +8,12 @@
 // Launches the matrix-core M = 1 kernel when the shape suits it and sets
 // *launched; otherwise returns WQ_OK with *launched = false and the caller
 // uses the VALU kernels.  `mode`: 0 = never, 1 = when the plan prefers it,
-// 2 = whenever the shape is supported.
-int wqd_gemv_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
-                 int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
-                 int64_t n_out, const uint16_t* x, uint16_t* y, hipStream_t stream,
-                 const char* who, int mode, bool* launched);
+// 2 = whenever the shape is supported.  With `tiled`, `codes` is the tiled
+// layer (wq.h "Tiled layout") and scales / zeros / out_w are not used.
+int wqd_gemv_mma(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scales,
+                 const uint16_t* zeros, int64_t N, int64_t K, const int32_t* out_idx,
+                 const uint16_t* out_w, int64_t n_out, const uint16_t* x, uint16_t* y,
+                 hipStream_t stream, const char* who, int mode, bool* launched);
 
 // Launches the matrix-core batched kernel (2 <= M <= 16) when the shape suits
 // it (same contract and `mode` values as wqd_gemv_mma).

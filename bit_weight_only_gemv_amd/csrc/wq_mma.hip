@@ -30,13 +30,18 @@
 //    copies, copy c at byte 8c of each 256-byte entry row, lane l reading copy
 //    l % 32.  Every lane thus reads its own bank pair (no bank conflicts), and
 //    the address (entry << 8 | 8 (l % 32)) is one byte permute of the code word.
-//  * Outlier columns: slice ks owns the slab positions J(ks) .. J(ks + 1) - 1,
-//    J(ks) = floor(ks n_out / nks), at most 32 of them; lane quarter r takes
-//    8 consecutive positions.  The positions, not the columns they name, are
-//    split, so every slab load address is known at entry and the slab streams
-//    with the codes.  At set-up the lanes gather the outlier activations of
-//    their share from the workgroup's copy of x and zero those columns there;
-//    per row block the slab values are dotted with them (v_dot2).
+//  * Outlier columns: the slab positions are cut into chunks of 8, and slice
+//    ks owns chunks C(ks) .. C(ks + 1) - 1, C(ks) = floor(ks nch / nks), at
+//    most 4 of them; lane quarter r takes chunk C(ks) + r.  The positions, not
+//    the columns they name, are split, so every slab load address is known at
+//    entry and the slab streams with the codes.  At set-up the lanes gather
+//    the outlier activations of their share from the workgroup's copy of x and
+//    zero those columns there; per row block the slab values are dotted with
+//    them (v_dot2).
+//  * Two layouts of the packed arrays: the row-major one of the C ABI, and the
+//    tiled one (TILED), in which every load of a wave is one contiguous 1 KB
+//    block: codes and scale/zero tiles per (row block, slice), slab chunks of
+//    16 rows x 8 positions.
 //  * Row-block loads go through a ring of DEPTH register buffers, so that
 //    while one row block is multiplied, the next ones are in flight.
 //  * Per row block each wave reduces its 4 lane quarters and adds its row
@@ -73,6 +78,7 @@ struct MmaArgs {
   int nsw;           // K-slices per wave, at most
   int nrb;           // row blocks (16 rows)
   int rbl;           // row blocks per workgroup, at most
+  int nch;           // outlier chunks of 8 slab positions, ceil(n_out / 8)
 };
 
 // Per-wave LDS region: for each of its slices, x (1 KB, masked at the outlier
@@ -143,9 +149,10 @@ __device__ __forceinline__ float slab_dot(const uint32_t (&od)[5], const uint32_
   return v;
 }
 
-template <int FMT, bool OUT, int DEPTH, int NSW>
+template <int FMT, bool OUT, bool TILED, int NSW>
 __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   typedef MmaFmt<FMT> F;
+  constexpr int DEPTH = 2;
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_out = OUT ? a.n_out : 0;
   const MmaLds L = mma_lds_layout(FMT, a.nw, a.nsw, a.rbl);
@@ -165,18 +172,27 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   auto slice_x = [&](int s) { return wreg + (uint32_t)s * kSliceLds; };   // 1 KB of x
   auto slice_sx = [&](int s) { return wreg + (uint32_t)s * kSliceLds + 1024u; };
   auto slice_xo = [&](int s) { return wreg + (uint32_t)s * kSliceLds + 1088u; };
-  // first slab position of slice ks (ks n_out < 2^31: the plan bounds both)
-  auto share_lo = [&](int ks) { return (uint32_t)(ks * n_out) / (uint32_t)a.nks; };
+  // first outlier chunk of slice ks (ks nch < 2^31: the plan bounds both),
+  // and the slice's share of slab positions, 8 C(ks) .. min(8 C(ks + 1), n_out)
+  auto chunk_lo = [&](int ks) { return (uint32_t)(ks * a.nch) / (uint32_t)a.nks; };
+  auto share_end = [&](int ks) { return min(8u * chunk_lo(ks + 1), (uint32_t)n_out); };
 
-  const __amdgpu_buffer_rsrc_t crs = make_rsrc(a.codes, clamp_bytes((uint64_t)a.N * row_bytes));
-  const uint64_t meta = (uint64_t)a.N * G * 2;
+  // Row-major: codes [N][K/div], scales / zeros [N][G], slab [N][n_out].
+  // Tiled: codes tiles of 16 kSliceBytes and scale/zero tiles of 1 KB per
+  // (row block, slice), slab chunks of 256 bytes per (row block, chunk); the
+  // arrays are padded to whole tiles, so the record counts cover them.
+  const uint64_t tiles = (uint64_t)a.nrb * a.nks;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(
+      a.codes, clamp_bytes(TILED ? tiles * 16 * F::kSliceBytes : (uint64_t)a.N * row_bytes));
+  const uint64_t meta = TILED ? tiles * 1024 : (uint64_t)a.N * G * 2;
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.scales, clamp_bytes(meta));
-  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(a.zeros, clamp_bytes(meta));
-  // The slab is read with 4-byte loads at 4-byte-aligned offsets; its record
-  // count is rounded up to that size, which stays inside the 16-byte block
-  // (and page) of the last element.
-  const __amdgpu_buffer_rsrc_t ors =
-      make_rsrc(a.out_w, clamp_bytes(((uint64_t)a.N * n_out * 2 + 3) & ~(uint64_t)3));
+  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(TILED ? a.scales : a.zeros, clamp_bytes(meta));
+  // The row-major slab is read with 4-byte loads at 4-byte-aligned offsets;
+  // its record count is rounded up to that size, which stays inside the
+  // 16-byte block (and page) of the last element.
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(
+      a.out_w, clamp_bytes(TILED ? (uint64_t)a.nrb * a.nch * 256
+                                 : ((uint64_t)a.N * n_out * 2 + 3) & ~(uint64_t)3));
   const __amdgpu_buffer_rsrc_t irs = make_rsrc(a.out_idx, (uint32_t)n_out * 4u);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.K * 2u);
 
@@ -199,8 +215,8 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     for (int p = 0; p < NIP; ++p) {
       const int s = 2 * p + (lane >> 5);
       const int ks = w + a.nw * s;
-      const uint32_t j = share_lo(ks) + (uint32_t)(lane & 31);
-      oval[p] = s < ns_w && j < share_lo(ks + 1);
+      const uint32_t j = 8u * chunk_lo(ks) + (uint32_t)(lane & 31);
+      oval[p] = s < ns_w && j < share_end(ks);
       oi[p] = ld32(irs, oval[p] ? j * 4u : kOob);
     }
   }
@@ -209,27 +225,49 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   // ---- (1) loads of one row block of one slice (every load is issued
   //      unconditionally; an item past the end reads nothing)
   // Offsets need no per-lane checks: rows past N and the bytes past the end
-  // of a short last slice lie past the arrays (the loads return 0) or in the
-  // next row, where the activations are zero; an item past the end of the
-  // wave's list reads through descriptors of zero records.
+  // of a short last slice lie past the arrays (the loads return 0) or, in the
+  // row-major layout, in the next row, where the activations are zero; an
+  // item past the end of the wave's list reads through descriptors of zero
+  // records.  A lane quarter past its slice's chunks reads at kOob (zero).
   const __amdgpu_buffer_rsrc_t nul = make_rsrc(a.codes, 0u);
   auto load_item = [&](Item<FMT, OUT>& it, bool valid, int ks, int rb) {
     const __amdgpu_buffer_rsrc_t c_ = valid ? crs : nul;
     const __amdgpu_buffer_rsrc_t s_ = valid ? srs : nul;
     const __amdgpu_buffer_rsrc_t z_ = valid ? zrs : nul;
     const uint32_t row = (uint32_t)(rb * 16 + n16);
-    const uint32_t rbase = row * row_bytes + (uint32_t)(ks * F::kSliceBytes + 16 * r);
+    if constexpr (TILED) {
+      const uint32_t tile = (uint32_t)(rb * a.nks + ks);
+      const uint32_t cbase = tile * (16u * F::kSliceBytes) + 16u * (uint32_t)lane;
 #pragma unroll
-    for (int u = 0; u < F::kLoads; ++u) it.cw[u] = ld128(c_, rbase + 64u * u);
-    const uint32_t mo = (row * (uint32_t)G + (uint32_t)(ks * kSliceGroups + 4 * r)) * 2u;
-    it.sv = ld64(s_, mo);
-    it.zv = ld64(z_, mo);
+      for (int u = 0; u < F::kLoads; ++u) it.cw[u] = ld128(c_, cbase + 1024u * u);
+      const u4v m = ld128(s_, tile * 1024u + 16u * (uint32_t)lane);
+      it.sv = (u2){m.x, m.y};
+      it.zv = (u2){m.z, m.w};
+    } else {
+      const uint32_t rbase = row * row_bytes + (uint32_t)(ks * F::kSliceBytes + 16 * r);
+#pragma unroll
+      for (int u = 0; u < F::kLoads; ++u) it.cw[u] = ld128(c_, rbase + 64u * u);
+      const uint32_t mo = (row * (uint32_t)G + (uint32_t)(ks * kSliceGroups + 4 * r)) * 2u;
+      it.sv = ld64(s_, mo);
+      it.zv = ld64(z_, mo);
+    }
     if constexpr (OUT) {
       const __amdgpu_buffer_rsrc_t o_ = valid ? ors : nul;
-      const uint32_t e0 = row * (uint32_t)n_out + share_lo(ks) + 8u * (uint32_t)r;
-      const uint32_t b0 = (e0 * 2u) & ~3u;
+      const uint32_t c0 = chunk_lo(ks);
+      const bool on = (uint32_t)r < chunk_lo(ks + 1) - c0;
+      if constexpr (TILED) {
+        const uint32_t off = ((uint32_t)rb * (uint32_t)a.nch + c0) * 256u + 16u * (uint32_t)lane;
+        const u4v t = ld128(o_, on ? off : kOob);
+        it.od[0] = t.x;
+        it.od[1] = t.y;
+        it.od[2] = t.z;
+        it.od[3] = t.w;
+      } else {
+        const uint32_t e0 = row * (uint32_t)n_out + 8u * (c0 + (uint32_t)r);
+        const uint32_t b0 = on ? (e0 * 2u) & ~3u : kOob;
 #pragma unroll
-      for (int i = 0; i < 5; ++i) it.od[i] = ld32(o_, b0 + 4u * i);
+        for (int i = 0; i < 5; ++i) it.od[i] = ld32(o_, b0 + 4u * i);
+      }
     }
   };
   int ls = 0, lr = 0;   // slice / row-block counters of the next item to load
@@ -324,12 +362,12 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   f4 sx4 = {0.f, 0.f, 0.f, 0.f};
   uint32_t xo0[4] = {0u, 0u, 0u, 0u};
   uint32_t keep[4] = {0u, 0u, 0u, 0u};
-  uint32_t cur_j = 0;
   auto enter_slice = [&](int s) {
     const int ks = w + a.nw * s;
     if constexpr (OUT) {
-      cur_j = share_lo(ks);
-      const int cnt = (int)(share_lo(ks + 1) - cur_j) - 8 * r;   // valid positions of the lane
+      // valid positions of the lane's chunk (row-major slab: the values past
+      // them are other positions or rows, and are masked off)
+      const int cnt = (int)share_end(ks) - (int)(8u * (chunk_lo(ks) + (uint32_t)r));
       const u4v v = *reinterpret_cast<const u4v*>(smem + slice_xo(s) + (uint32_t)r * 16u);
       xo0[0] = v.x;
       xo0[1] = v.y;
@@ -474,8 +512,13 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     }
     if constexpr (FMT == 4) v *= 16777216.0f;
     if constexpr (OUT) {
-      const uint32_t sh = (((uint32_t)row * (uint32_t)n_out + cur_j) & 1u) * 16u;
-      v = slab_dot(it.od, xo0, keep, sh, v);
+      if constexpr (TILED) {   // zero-padded chunks: no alignment, no mask
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = __builtin_amdgcn_fdot2(as_h2(it.od[i]), as_h2(xo0[i]), v, false);
+      } else {
+        const uint32_t sh = (((uint32_t)row * (uint32_t)n_out) & 1u) * 16u;
+        v = slab_dot(it.od, xo0, keep, sh, v);
+      }
     }
     // the four lane quarters hold the same row: add them
     v += __shfl_xor(v, 16);
@@ -1007,20 +1050,31 @@ static int device_cus() {
 
 struct MmaPlan {
   bool ok, preferred;
-  int nw, nks, nsw, nswt, nrb, grid, rbl, depth;
+  int nw, nks, nsw, nswt, nrb, nch, grid, rbl;
   size_t lds;
 };
 
-static MmaPlan plan_mma1(int fmt, int64_t N, int64_t K, int64_t n_out) {
+static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_out) {
   MmaPlan p{};
-  if (K % 128 != 0 || K > 65536) return p;
-  const int64_t row_bytes = fmt == 4 ? K / 2 : K / 4;
-  if (N * row_bytes > 0xFFFFFFF0ll || N * (K / 32) * 2 > 0xFFFFFFF0ll ||
-      N * n_out * 2 > 0xFFFFFFF0ll)
-    return p;
+  // the row-major layout reads whole 128-channel quarters of a slice from
+  // each row; the tiled one is padded to whole slices
+  if (K % (tiled ? 32 : 128) != 0 || K > 65536) return p;
   p.nks = (int)((K + kSliceCh - 1) / kSliceCh);
-  // every slice's share of the outlier slab fits one lane quarter each (8 x 4)
-  if (n_out > (int64_t)kShareMax * p.nks) return p;
+  p.nch = (int)((n_out + 7) / 8);
+  p.nrb = (int)((N + 15) / 16);
+  // every slice's share of the outlier slab fits the four lane quarters
+  if (p.nch > 4 * p.nks) return p;
+  if (tiled) {
+    const wq::TiledGeometry g = wq::tiled_geometry(fmt, N, K, n_out);
+    if (g.meta_off > 0xFFFFFFF0ll || g.slab_off - g.meta_off > 0xFFFFFFF0ll ||
+        g.total - g.slab_off > 0xFFFFFFF0ll)
+      return p;
+  } else {
+    const int64_t row_bytes = fmt == 4 ? K / 2 : K / 4;
+    if (N * row_bytes > 0xFFFFFFF0ll || N * (K / 32) * 2 > 0xFFFFFFF0ll ||
+        N * n_out * 2 > 0xFFFFFFF0ll)
+      return p;
+  }
   if (p.nks <= kMaxWaves) {
     p.nw = p.nks;
   } else {
@@ -1036,7 +1090,6 @@ static MmaPlan plan_mma1(int fmt, int64_t N, int64_t K, int64_t n_out) {
   p.nsw = (p.nks + p.nw - 1) / p.nw;
   if (p.nsw > 8) return p;
   p.nswt = p.nsw <= 1 ? 1 : p.nsw <= 2 ? 2 : p.nsw <= 4 ? 4 : 8;
-  p.nrb = (int)((N + 15) / 16);
   const int cus = device_cus();
   if (cus <= 0) return p;
   p.grid = std::min(p.nrb, cus);
@@ -1044,11 +1097,6 @@ static MmaPlan plan_mma1(int fmt, int64_t N, int64_t K, int64_t n_out) {
   const MmaLds L = mma_lds_layout(fmt, p.nw, p.nsw, p.rbl);
   p.lds = L.total;
   if (p.lds > kMaxLdsBytes) return p;
-  p.depth = 2;
-  if (const char* e = getenv("WQ_MMA_DEPTH")) {
-    const int v = atoi(e);
-    if (v == 2 || v == 4) p.depth = v;
-  }
   p.ok = true;
   // One workgroup per compute unit: worth it once every unit has a row block.
   // Measured on MI355X: ahead of the VALU kernels for W2 (the centroid table
@@ -1102,20 +1150,28 @@ static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M)
 
 using namespace wqd;
 
-int wqd_gemv_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
-                 int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
-                 int64_t n_out, const uint16_t* x, uint16_t* y, hipStream_t stream,
-                 const char* who, int mode, bool* launched) {
+int wqd_gemv_mma(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scales,
+                 const uint16_t* zeros, int64_t N, int64_t K, const int32_t* out_idx,
+                 const uint16_t* out_w, int64_t n_out, const uint16_t* x, uint16_t* y,
+                 hipStream_t stream, const char* who, int mode, bool* launched) {
   *launched = false;
   if (mode == 0) return WQ_OK;
-  const MmaPlan p = plan_mma1(fmt, N, K, n_out);
+  const MmaPlan p = plan_mma1(fmt, tiled, N, K, n_out);
   if (!p.ok || (mode == 1 && !p.preferred)) return WQ_OK;
   MmaArgs a{};
-  a.codes = codes;
-  a.scales = scales;
-  a.zeros = zeros;
+  if (tiled) {
+    const wq::TiledGeometry g = wq::tiled_geometry(fmt, N, K, n_out);
+    a.codes = codes + g.codes_off;
+    a.scales = reinterpret_cast<const uint16_t*>(codes + g.meta_off);
+    a.zeros = a.scales;
+    a.out_w = reinterpret_cast<const uint16_t*>(codes + g.slab_off);
+  } else {
+    a.codes = codes;
+    a.scales = scales;
+    a.zeros = zeros;
+    a.out_w = out_w;
+  }
   a.out_idx = out_idx;
-  a.out_w = out_w;
   a.x = x;
   a.y = y;
   a.N = (int)N;
@@ -1126,22 +1182,23 @@ int wqd_gemv_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
   a.nsw = p.nsw;
   a.nrb = p.nrb;
   a.rbl = p.rbl;
+  a.nch = p.nch;
   const dim3 grid(p.grid), block(p.nw * kWave);
-#define WQ_MMA_LAUNCH(F_, O_, D_, S_)                                                        \
-  if (fmt == F_ && (n_out > 0) == O_ && p.depth == D_ && p.nswt == S_) {                     \
-    if (!allow_lds(reinterpret_cast<const void*>(&mma1d_kernel<F_, O_, D_, S_>), p.lds))    \
+#define WQ_MMA_LAUNCH(F_, O_, T_, S_)                                                        \
+  if (fmt == F_ && (n_out > 0) == O_ && tiled == T_ && p.nswt == S_) {                       \
+    if (!allow_lds(reinterpret_cast<const void*>(&mma1d_kernel<F_, O_, T_, S_>), p.lds))    \
       return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds); \
-    hipLaunchKernelGGL((mma1d_kernel<F_, O_, D_, S_>), grid, block, p.lds, stream, a);       \
+    hipLaunchKernelGGL((mma1d_kernel<F_, O_, T_, S_>), grid, block, p.lds, stream, a);       \
     *launched = true;                                                                        \
     return check_launch(who);                                                                \
   }
-#define WQ_MMA_SLICES(F_, O_, D_) \
-  WQ_MMA_LAUNCH(F_, O_, D_, 1) WQ_MMA_LAUNCH(F_, O_, D_, 2) WQ_MMA_LAUNCH(F_, O_, D_, 4) \
-  WQ_MMA_LAUNCH(F_, O_, D_, 8)
-#define WQ_MMA_DEPTHS(F_, O_) WQ_MMA_SLICES(F_, O_, 2) WQ_MMA_SLICES(F_, O_, 4)
-  WQ_MMA_DEPTHS(4, false) WQ_MMA_DEPTHS(4, true) WQ_MMA_DEPTHS(2, false) WQ_MMA_DEPTHS(2, true)
+#define WQ_MMA_SLICES(F_, O_, T_) \
+  WQ_MMA_LAUNCH(F_, O_, T_, 1) WQ_MMA_LAUNCH(F_, O_, T_, 2) WQ_MMA_LAUNCH(F_, O_, T_, 4) \
+  WQ_MMA_LAUNCH(F_, O_, T_, 8)
+#define WQ_MMA_LAYOUTS(F_, O_) WQ_MMA_SLICES(F_, O_, false) WQ_MMA_SLICES(F_, O_, true)
+  WQ_MMA_LAYOUTS(4, false) WQ_MMA_LAYOUTS(4, true) WQ_MMA_LAYOUTS(2, false) WQ_MMA_LAYOUTS(2, true)
 #undef WQ_MMA_SLICES
-#undef WQ_MMA_DEPTHS
+#undef WQ_MMA_LAYOUTS
 #undef WQ_MMA_LAUNCH
   return WQ_OK;
 }

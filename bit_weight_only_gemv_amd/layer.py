@@ -55,9 +55,11 @@ def pack_host(fmt: int, W: np.ndarray, profile: Optional[np.ndarray] = None,
 
 
 class DeviceLayer:
-    """Packed arrays in device memory (torch tensors used as plain buffers)."""
+    """Packed arrays in device memory (torch tensors used as plain buffers).
+    With ``tiled=True`` the layer also holds the tiled M = 1 layout (built by
+    the library's host rearrangement), which ``gemv_tiled`` reads."""
 
-    def __init__(self, host: HostLayer, device="cuda"):
+    def __init__(self, host: HostLayer, device="cuda", tiled: bool = False):
         import torch
         self.fmt, self.N, self.K, self.n_out = host.fmt, host.N, host.K, host.n_out
 
@@ -72,6 +74,11 @@ class DeviceLayer:
             self.wout = up(host.wout.view(np.int16), np.int16)
         else:
             self.idx = self.wout = None
+        self.tiled = None
+        if tiled:
+            t = L.wq_tile_host(self.fmt, host.codes, host.scales, host.zeros,
+                               host.wout if self.n_out else None, self.N, self.K)
+            self.tiled = up(t, np.uint8)
 
     def nbytes(self, M: int = 1) -> int:
         """Algorithmic bytes of one product: codes, scales, zeros, outlier slab
@@ -84,6 +91,11 @@ class DeviceLayer:
         fn = L.wq_gemv_w4 if self.fmt == L.WQ_FMT_W4 else L.wq_gemv_w2
         fn(self.codes, self.scales, self.zeros, self.N, self.K, x, y, self.idx, self.wout,
            self.n_out, flags, stream)
+
+    def gemv_tiled(self, x, y, stream=None):
+        if self.tiled is None:
+            raise ValueError("layer built without tiled=True")
+        L.wq_gemv_tiled(self.fmt, self.tiled, self.N, self.K, x, y, self.idx, self.n_out, stream)
 
     def gemm(self, X, Y, flags=L.WQ_FUSE_OUTLIERS, stream=None):
         L.wq_gemm_wq(self.fmt, self.codes, self.scales, self.zeros, self.N, self.K, X, X.shape[0],

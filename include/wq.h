@@ -172,6 +172,49 @@ int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales, const uint
 int wq_outlier_add(const int32_t* idx, const uint16_t* out_w, int64_t n_out, int64_t N,
                    const uint16_t* X, int64_t M, int64_t K, uint16_t* Y, void* stream);
 
+/* ------------------------------------------------------ tiled M = 1 layout
+ * A second device layout of the same packed layer, read by the matrix-core
+ * M = 1 kernel so that every 64-lane load is one contiguous 1 KB block (the
+ * row-major arrays above make each load touch 16 rows).  It holds the bytes of
+ * codes / scales / zeros / out_w, rearranged and zero-padded; the outlier
+ * indices stay a separate int32 array.  SPECTRA section 3.4 names an
+ * interleaved, hardware-tiled layout for its kernel; this is the gfx950 one.
+ *
+ * Geometry: nrb = ceil(N / 16) row blocks, nks = ceil(K / 512) slices,
+ * nch = ceil(n_out / 8) outlier chunks, SB = 256 (W4) or 128 (W2) code bytes
+ * per row and slice.  Three sections, each starting at a multiple of 256 bytes
+ * (codes at 0, then meta, then slab); every entry past N, K or n_out is 0.
+ *   codes: tile (b, s) of 16 SB bytes at (b nks + s) 16 SB; its byte
+ *          1024 u + 16 (n + 16 r) + c   (u < SB / 64, n < 16, r < 4, c < 16)
+ *          = codes[16 b + n][s SB + 64 u + 16 r + c]
+ *   meta:  tile (b, s) of 512 FP16 entries at (b nks + s) 1024 bytes; entry
+ *          8 (n + 16 r) + i     = scales[16 b + n][16 s + 4 r + i]  (i < 4)
+ *          8 (n + 16 r) + 4 + i = zeros [16 b + n][16 s + 4 r + i]
+ *   slab:  chunk (b, c) of 128 FP16 entries at (b nch + c) 256 bytes; entry
+ *          8 n + i = out_w[16 b + n][8 c + i]                       (i < 8)
+ */
+
+/* Bytes of the tiled layout of an N x K layer with n_out outlier columns, or a
+ * negative WQ_ERR_* code for invalid arguments (fmt, shape as above). */
+int64_t wq_tiled_bytes(int fmt, int64_t N, int64_t K, int64_t n_out);
+
+/* Host rearrangement of row-major packed arrays (layouts above; out_w may be
+ * NULL when n_out == 0) into the tiled layout.  `tiled` holds `tiled_bytes`
+ * bytes, at least wq_tiled_bytes(...); every byte of the layout is written.
+ * Errors: WQ_ERR_INVALID_ARG for NULL pointers, bad shapes or a short buffer. */
+int wq_tile_host(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                 const uint16_t* out_w, int64_t N, int64_t K, int64_t n_out, uint8_t* tiled,
+                 int64_t tiled_bytes);
+
+/* Fused M = 1 GEMV on a tiled layer (device pointer `tiled`), outliers always
+ * in the same launch; the same result contract as wq_gemv_w4 / wq_gemv_w2
+ * with WQ_FUSE_OUTLIERS.  WQ_ERR_UNSUPPORTED for shapes the kernel cannot hold:
+ * K > 32768, more than 32 outlier positions per 512-channel slice
+ * (n_out > 32 ceil(K / 512)), or partial sums beyond the 160 KB of LDS
+ * (N above about 200 000 rows at K = 32768). */
+int wq_gemv_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K, const int32_t* out_idx,
+                  int64_t n_out, const uint16_t* x, uint16_t* y, void* stream);
+
 /* -------------------------------------------------- measurement support
  * Not part of the method: kernels of known traffic that calibrate bandwidth
  * figures and hardware byte counters. */

@@ -135,6 +135,73 @@ def test_gemv_unfused_then_outlier_add(fmt):
     check_product(ref, y, L.x, "unfused")
 
 
+# ------------------------------------------------------------- tiled gemv
+
+TILED_SHAPES = [(1, 32), (7, 96), (129, 4096), (300, 14336), (77, 28672), (33, 2080),
+                (1000, 1024), (5000, 4224), (16, 512), (40, 32768)]
+
+
+def build_tiled(fmt, W, profile=None, ratio=0.0):
+    ref = O.quantize_layer(fmt, W, profile, ratio)
+    hl = pack_host(fmt, W, profile, ratio)
+    assert np.array_equal(hl.codes, ref.codes) and np.array_equal(hl.idx, ref.idx)
+    return ref, DeviceLayer(hl, tiled=True)
+
+
+def run_gemv_tiled(dl, x):
+    xd = dev_fp16(x.reshape(-1))
+    y = torch.full((dl.N,), -1, dtype=torch.int16, device="cuda")
+    dl.gemv_tiled(xd, y)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("N,K", TILED_SHAPES)
+@pytest.mark.parametrize("outl", [False, True])
+def test_gemv_tiled(fmt, N, K, outl, monkeypatch):
+    say(f"gemv tiled fmt={fmt} N={N} K={K} outliers={outl}")
+    L = synthetic.small_layer(fmt, N, K, with_outliers=outl, seed=N % 17)
+    ref, dl = build_tiled(fmt, L.W, L.profile, L.ratio)
+    y = run_gemv_tiled(dl, L.x)
+    check_product(ref, y, L.x, f"tiled w{fmt} {N}x{K} n_out={ref.n_out}")
+    if K % 128 == 0:
+        # the row-major matrix-core kernel performs the same operations in the
+        # same order on the same values: identical bits
+        monkeypatch.setenv("WQ_GEMV_MMA", "2")
+        y2, _ = run_gemv(dl, L.x)
+        assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("n_out", [1, 7, 8, 9, 31, 33, 64, 65, 129, 256])
+def test_gemv_tiled_outlier_counts(fmt, n_out):
+    K = 4096
+    say(f"gemv tiled fmt={fmt} n_out={n_out}")
+    L = synthetic.small_layer(fmt, 200, K, with_outliers=True, seed=n_out,
+                              ratio=(n_out + 0.5) / K)
+    ref, dl = build_tiled(fmt, L.W, L.profile, L.ratio)
+    assert ref.n_out == n_out
+    y = run_gemv_tiled(dl, L.x)
+    check_product(ref, y, L.x, f"tiled w{fmt} n_out={n_out}")
+
+
+def test_gemv_tiled_unsupported_shapes():
+    # 257 outlier positions over 8 slices of 512 channels: one slice would need 5 chunks
+    L = synthetic.small_layer(2, 64, 4096, with_outliers=True, seed=3, ratio=257.5 / 4096)
+    _, dl = build_tiled(2, L.W, L.profile, L.ratio)
+    assert dl.n_out == 257
+    y = torch.empty(64, dtype=torch.int16, device="cuda")
+    with pytest.raises(B.WQError) as e:
+        dl.gemv_tiled(dev_fp16(L.x.reshape(-1)), y)
+    assert e.value.status == -2
+    L = synthetic.small_layer(4, 16, 65536, seed=1)
+    _, dl = build_tiled(4, L.W)
+    with pytest.raises(B.WQError) as e:
+        dl.gemv_tiled(dev_fp16(L.x.reshape(-1)), torch.empty(16, dtype=torch.int16, device="cuda"))
+    assert e.value.status == -2
+
+
 def test_gemv_deterministic(gemv_path):
     L = synthetic.small_layer(2, 1500, 4096, with_outliers=True, seed=9)
     ref, dl = build(2, L.W, L.profile, L.ratio)
@@ -201,10 +268,13 @@ def test_full_w4_4096x4096_m1():
 def test_full_w2_14336x4096_outliers_m1():
     L = synthetic.config2()
     say("full W2 14336x4096 + outliers M=1")
-    ref, dl = build(2, L.W, L.profile, L.ratio)
+    ref = O.quantize_layer(2, L.W, L.profile, L.ratio)
+    dl = DeviceLayer(pack_host(2, L.W, L.profile, L.ratio), tiled=True)
     assert ref.n_out == 143
     y, _ = run_gemv(dl, L.x)
     check_product(ref, y, L.x, "W2 14336x4096")
+    yt = run_gemv_tiled(dl, L.x)
+    check_product(ref, yt, L.x, "W2 14336x4096 tiled")
 
 
 @pytest.mark.parametrize("N,K", [(14336, 4096), (4096, 14336)])

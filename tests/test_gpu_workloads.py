@@ -1,7 +1,8 @@
 """GPU parity at the full sizes of the larger workloads, in the launch
 configuration the benchmark times, on outputs the oracle computes row by row:
 
-* 70B-class W2 + outlier layers (28672 x 8192 and 8192 x 28672, M = 1 and 8):
+* 70B-class W2 + outlier layers (28672 x 8192 and 8192 x 28672, M = 1 on both
+  layouts and M = 8):
   the oracle selects the outlier columns from the whole matrix, then splits,
   quantizes and multiplies only a sample of rows (the encoding of a row does
   not depend on other rows once the outlier columns are fixed);
@@ -66,7 +67,7 @@ def sample_rows(N, n=192, seed=0):
 def test_w2_70b_class_outliers(N, K):
     say(f"W2 70B-class {N}x{K} + outliers")
     L = synthetic.config5(N, K, 8)
-    dl = DeviceLayer(pack_host(2, L.W, L.profile, L.ratio))
+    dl = DeviceLayer(pack_host(2, L.W, L.profile, L.ratio), tiled=True)
     assert dl.n_out == int(np.floor(0.035 * K))
     rows = sample_rows(N)
     w_hat, idx, wout = oracle_rows(2, L.W, L.profile, L.ratio, rows)
@@ -77,11 +78,15 @@ def test_w2_70b_class_outliers(N, K):
     X = torch.from_numpy(np.ascontiguousarray(L.x).view(np.int16)).cuda()
     y1 = torch.empty(N, dtype=torch.int16, device="cuda")
     dl.gemv(X[0].contiguous(), y1)
+    yt = torch.empty(N, dtype=torch.int16, device="cuda")
+    dl.gemv_tiled(X[0].contiguous(), yt)
     Y8 = torch.empty((8, N), dtype=torch.int16, device="cuda")
     dl.gemm(X, Y8)
     torch.cuda.synchronize()
     check_rows(y1.cpu().numpy().view(np.float16)[None, :], rows, w_hat, L.x[:1], idx, wout,
                f"M=1 {N}x{K}")
+    check_rows(yt.cpu().numpy().view(np.float16)[None, :], rows, w_hat, L.x[:1], idx, wout,
+               f"M=1 tiled {N}x{K}")
     check_rows(Y8.cpu().numpy().view(np.float16), rows, w_hat, L.x, idx, wout, f"M=8 {N}x{K}")
 
 
