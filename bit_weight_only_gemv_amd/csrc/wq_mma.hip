@@ -62,7 +62,11 @@ constexpr int kSliceCh = 512;      // channels per K-slice
 constexpr int kSliceGroups = 16;   // groups per K-slice = MFMA slots
 constexpr int kLutRow = 256;       // bytes per W2 table entry (32 copies x 8 bytes)
 constexpr int kMaxWaves = 8;
-constexpr uint32_t kOob = 0x80000000u;   // buffer offset past any range: loads return 0
+// Buffer offset past every range the kernels read (the plans keep each
+// array below kMaxArrayBytes, and instruction offsets of up to 3 KB cannot
+// wrap it): loads from it return 0.
+constexpr uint32_t kOob = 0xFFFFF000u;
+constexpr int64_t kMaxArrayBytes = 0xFFFFE000ll;
 
 struct MmaArgs {
   const uint8_t* codes;
@@ -1066,13 +1070,13 @@ static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_ou
   if (p.nch > 4 * p.nks) return p;
   if (tiled) {
     const wq::TiledGeometry g = wq::tiled_geometry(fmt, N, K, n_out);
-    if (g.meta_off > 0xFFFFFFF0ll || g.slab_off - g.meta_off > 0xFFFFFFF0ll ||
-        g.total - g.slab_off > 0xFFFFFFF0ll)
+    if (g.meta_off > kMaxArrayBytes || g.slab_off - g.meta_off > kMaxArrayBytes ||
+        g.total - g.slab_off > kMaxArrayBytes)
       return p;
   } else {
     const int64_t row_bytes = fmt == 4 ? K / 2 : K / 4;
-    if (N * row_bytes > 0xFFFFFFF0ll || N * (K / 32) * 2 > 0xFFFFFFF0ll ||
-        N * n_out * 2 > 0xFFFFFFF0ll)
+    if (N * row_bytes > kMaxArrayBytes || N * (K / 32) * 2 > kMaxArrayBytes ||
+        N * n_out * 2 > kMaxArrayBytes)
       return p;
   }
   if (p.nks <= kMaxWaves) {

@@ -137,8 +137,10 @@ def test_gemv_unfused_then_outlier_add(fmt):
 
 # ------------------------------------------------------------- tiled gemv
 
+# row blocks vs 256 compute units: 5000 rows -> 313 blocks (57 left over, cut in 4 row ranges);
+# 5376 -> 336 (80 left, cut in 3); 300 -> 19 (fewer blocks than units, each cut in 4)
 TILED_SHAPES = [(1, 32), (7, 96), (129, 4096), (300, 14336), (77, 28672), (33, 2080),
-                (1000, 1024), (5000, 4224), (16, 512), (40, 32768)]
+                (1000, 1024), (5000, 4224), (16, 512), (40, 32768), (5376, 1024)]
 
 
 def build_tiled(fmt, W, profile=None, ratio=0.0):
