@@ -20,7 +20,8 @@ Measurement:
   outlier slab + int32 indices + x + y) / time per step.
 
 Other workloads (--workload): w4_4096 (W4 4096x4096), sweep (Llama-3-8B-shaped
-decode: 225 W4 GEMVs per step in one graph -> tokens/s), batched (W4 small-M
+decode in one graph -> tokens/s: 225 separate W4 GEMVs per token, and 129 with
+q|k|v and gate|up stacked along N), batched (W4 small-M
 matrix-core path vs M repeated GEMVs), w2_70b (W2 + outliers at 28672x8192 and
 8192x28672, M = 1 and 8), read / copy (plain streaming kernels: the attainable
 HBM rate and the byte-counter calibration).
@@ -213,42 +214,85 @@ def gemv_workload(a, torch, L, label, timer):
     return out
 
 
+SWEEP_GROUPS = {
+    # one GEMV per projection: 7 per layer + the LM head = 225 per token
+    "unfused": [("q",), ("k",), ("v",), ("o",), ("gate",), ("up",), ("down",)],
+    # projections that read the same activation stacked along N into one GEMV
+    # (q|k|v 6144 x 4096, gate|up 28672 x 4096): 4 per layer + the head = 129
+    "fused": [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)],
+}
+
+
 def sweep_workload(a, torch, timer):
-    """225 W4 GEMVs of a Llama-3-8B-shaped decode step, one graph per token."""
+    """One Llama-3-8B-shaped W4 decode step per graph replay, two ways:
+    225 separate GEMVs, and 129 GEMVs with q|k|v and gate|up stacked along N
+    (same weights, same bytes, fewer launches).  Each group of GEMVs runs on
+    the layout (row-major or tiled) measured faster for it over its 32 layers;
+    tokens_per_s is the fused step's rate."""
     import synthetic
     from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
     shapes = synthetic.config3_shapes()
-    proto = {}
-    for (layer, proj, name, N, K) in shapes:
-        key = (name if name in ("lm_head",) else {"q": "sq", "o": "sq", "k": "kv", "v": "kv",
-                                                    "gate": "mlp", "up": "mlp", "down": "down"}[name])
-        if key not in proto:
-            L = synthetic.config3_layer(layer, proj, N, K, name)
-            proto[key] = DeviceLayer(pack_host(4, L.W))
-    layers, xs, ys = [], [], []
-    total = 0
-    for (layer, proj, name, N, K) in shapes:
-        key = name if name == "lm_head" else {"q": "sq", "o": "sq", "k": "kv", "v": "kv",
-                                              "gate": "mlp", "up": "mlp", "down": "down"}[name]
-        d = clone_layer(DeviceLayer, proto[key]) if key != "lm_head" else proto[key]
-        layers.append(d)
-        x = synthetic.gaussian_x_fp16(1, K, 3, layer, proj)
-        xs.append(torch.from_numpy(x.reshape(-1).view(np.int16)).cuda())
-        ys.append(torch.empty(N, dtype=torch.int16, device="cuda"))
-        total += d.nbytes(1)
+    nlayers = shapes[-1][0]
+    proj = {}
+    for (layer, p, name, N, K) in shapes:
+        if layer == 0:
+            proj[name] = (p, N, K)
+    head = shapes[-1]
+    protos = {}
+    for groups in SWEEP_GROUPS.values():
+        for g in groups:
+            if g not in protos:
+                Ws = [synthetic.config3_layer(0, proj[n][0], proj[n][1], proj[n][2], n).W for n in g]
+                protos[g] = DeviceLayer(pack_host(4, np.concatenate(Ws, axis=0)), tiled=True)
+    hL = synthetic.config3_layer(head[0], head[1], head[3], head[4], head[2])
+    head_layer = DeviceLayer(pack_host(4, hL.W), tiled=True)
     torch.cuda.synchronize()
-
-    def step(i):
-        for d, x, y in zip(layers, xs, ys):
-            d.gemv(x, y)
-
     steps = max(1, min(a.steps, 50))
-    ms = timer(step, steps, min(a.warmup, 5))
-    gbs = total / (ms * 1e-3) / 1e9
-    return {"workload": "w4_llama3_8b_sweep_225_gemv", "bytes_per_token": total,
-            "ms_per_token": ms, "tokens_per_s": round(1e3 / ms, 1), "GB/s": round(gbs, 1),
-            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-            "roofline_tokens_per_s": round(HBM_PEAK_GBS * 1e9 / total, 1), "steps": steps}
+    out = {"workload": "w4_llama3_8b_decode_step", "steps": steps}
+    for label, groups in SWEEP_GROUPS.items():
+        layers = {g: [protos[g]] + [clone_layer(DeviceLayer, protos[g]) for _ in range(nlayers - 1)]
+                  for g in groups}
+        xs = {g: torch.from_numpy(synthetic.gaussian_x_fp16(1, protos[g].K, 3, 0, i).reshape(-1)
+                                  .view(np.int16)).cuda() for i, g in enumerate(groups)}
+        ys = {g: torch.empty(protos[g].N, dtype=torch.int16, device="cuda") for g in groups}
+        xh = torch.from_numpy(hL.x.reshape(-1).view(np.int16)).cuda()
+        yh = torch.empty(head_layer.N, dtype=torch.int16, device="cuda")
+        # layout per group: the faster one over the group's 32 (cold) layers
+        pick = {}
+        for g in list(groups) + ["head"]:
+            ls = [head_layer] if g == "head" else layers[g]
+            x, y = (xh, yh) if g == "head" else (xs[g], ys[g])
+            t = {}
+            for lay in ("rowmajor", "tiled"):
+                def run(i, ls=ls, x=x, y=y, lay=lay):
+                    for d in ls:
+                        (d.gemv_tiled if lay == "tiled" else d.gemv)(x, y)
+                t[lay] = timer(run, 5, 2)
+            pick[g] = min(t, key=t.get)
+        calls = []
+        for li in range(nlayers):
+            for g in groups:
+                d = layers[g][li]
+                calls.append((d.gemv_tiled if pick[g] == "tiled" else d.gemv, xs[g], ys[g]))
+        calls.append((head_layer.gemv_tiled if pick["head"] == "tiled" else head_layer.gemv, xh, yh))
+        total = sum(layers[g][0].nbytes(1) for g in groups) * nlayers + head_layer.nbytes(1)
+
+        def step(i, calls=calls):
+            for fn, x, y in calls:
+                fn(x, y)
+
+        ms = timer(step, steps, min(a.warmup, 5))
+        out[label] = {"gemvs_per_token": len(calls), "ms_per_token": round(ms, 4),
+                      "tokens_per_s": round(1e3 / ms, 1), "bytes_per_token": total,
+                      "GB/s": round(total / (ms * 1e-3) / 1e9, 1),
+                      "layouts": {("|".join(g) if g != "head" else g): pick[g] for g in pick}}
+        del layers, calls
+        torch.cuda.synchronize()
+    best = out["fused"]
+    out.update({"ms_per_token": best["ms_per_token"], "tokens_per_s": best["tokens_per_s"],
+                "pct_of_hbm_peak": round(100 * best["GB/s"] / HBM_PEAK_GBS, 2),
+                "roofline_tokens_per_s": round(HBM_PEAK_GBS * 1e9 / best["bytes_per_token"], 1)})
+    return out
 
 
 def batched_workload(a, torch, timer):

@@ -8,7 +8,9 @@ configuration the benchmark times, on outputs the oracle computes row by row:
   not depend on other rows once the outlier columns are fixed);
 * the Llama-3-8B-shaped W4 decode sweep (225 GEMVs) captured in one HIP
   graph: every replay (with eager work in between) equals the eager result
-  bit for bit, and sampled GEMVs match the oracle.
+  bit for bit, and sampled GEMVs match the oracle;
+* the stacked projections the fused sweep runs (q|k|v 6144 x 4096, gate|up
+  28672 x 4096), on both layouts, on rows sampled from every part.
 """
 
 import sys
@@ -143,3 +145,29 @@ def test_llama_sweep_graph_replay_and_samples():
         w_hat, idx, wout = oracle_rows(4, W, None, 0.0, rows)
         check_rows(eager[i].cpu().numpy().view(np.float16)[None, :], rows, w_hat, xs[i], idx, wout,
                    f"sweep GEMV {i} ({name} {N}x{K})")
+
+
+@pytest.mark.parametrize("names", [("q", "k", "v"), ("gate", "up")])
+def test_stacked_projections_both_layouts(names):
+    shapes = {name: (p, N, K) for (layer, p, name, N, K) in synthetic.config3_shapes() if layer == 0}
+    Ws = [synthetic.config3_layer(0, shapes[n][0], shapes[n][1], shapes[n][2], n).W for n in names]
+    W = np.concatenate(Ws, axis=0)
+    N, K = W.shape
+    say(f"stacked {'|'.join(names)} {N}x{K}")
+    dl = DeviceLayer(pack_host(4, W), tiled=True)
+    x = synthetic.gaussian_x_fp16(1, K, 3, 0, 0)
+    xd = torch.from_numpy(x.reshape(-1).view(np.int16)).cuda()
+    y1 = torch.empty(N, dtype=torch.int16, device="cuda")
+    y2 = torch.empty(N, dtype=torch.int16, device="cuda")
+    dl.gemv(xd, y1)
+    dl.gemv_tiled(xd, y2)
+    torch.cuda.synchronize()
+    # rows from every stacked part, including each part's first and last row
+    edges = np.cumsum([0] + [w.shape[0] for w in Ws])
+    rows = np.unique(np.concatenate([sample_rows(N, 160, seed=len(names)), edges[1:-1] - 1,
+                                     edges[1:-1]])).astype(np.int64)
+    w_hat, idx, wout = oracle_rows(4, W, None, 0.0, rows)
+    check_rows(y1.cpu().numpy().view(np.float16)[None, :], rows, w_hat, x, idx, wout,
+               f"stacked {N}x{K} row-major")
+    check_rows(y2.cpu().numpy().view(np.float16)[None, :], rows, w_hat, x, idx, wout,
+               f"stacked {N}x{K} tiled")
