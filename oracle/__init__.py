@@ -13,7 +13,7 @@ exhaustive or brute-force checks); none is "parity unpinned".
 
 from .wq_oracle import (  # noqa: F401
     GROUP, CODEBOOK_DECIMAL, CODEBOOK_FP16, CODEBOOK_F64, THRESHOLDS_F64, OLS_EPS,
-    quantize_w4, pack_w4, unpack_w4, dequant_w4,
+    quantize_w4, pack_w4, unpack_w4, dequant_w4, pack_zeros_w4, unpack_zeros_w4,
     quantize_w2, pack_w2, unpack_w2, dequant_w2,
     outlier_count, outlier_scores, select_outliers, split_outliers,
     QuantLayer, quantize_layer, background_mask, matvec_ref,

@@ -136,6 +136,32 @@ def dequant_w4(q: np.ndarray, scale: np.ndarray, zero: np.ndarray) -> np.ndarray
     return w.astype(np.float16).reshape(N, K)
 
 
+def pack_zeros_w4(zero: np.ndarray) -> np.ndarray:
+    """Packed zero points of [SPECTRA] section 3.4: the zero points of the two
+    adjacent groups 2m and 2m + 1 of a row share byte m, group 2m in bits 3:0
+    and group 2m + 1 in bits 7:4 (with an odd group count the last byte's high
+    nibble is 0).  ``zero`` holds the FP16 zero points, which the W4 quantizer
+    makes integers 0..15; anything else is rejected."""
+    z = np.asarray(zero).astype(np.float32)
+    if z.size and not (np.all(z == np.rint(z)) and z.min() >= 0 and z.max() <= W4_LEVELS):
+        raise ValueError("zero points must be integers in 0..15")
+    zi = z.astype(np.uint8)
+    N, G = zi.shape
+    if G % 2:
+        zi = np.concatenate([zi, np.zeros((N, 1), np.uint8)], axis=1)
+    return (zi[:, 0::2] | (zi[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_zeros_w4(zpk: np.ndarray, G: int) -> np.ndarray:
+    """Inverse of ``pack_zeros_w4``: FP16 zero points [N, G]."""
+    zpk = np.asarray(zpk, dtype=np.uint8)
+    N = zpk.shape[0]
+    z = np.empty((N, 2 * zpk.shape[1]), np.uint8)
+    z[:, 0::2] = zpk & 0x0F
+    z[:, 1::2] = zpk >> 4
+    return z[:, :G].astype(np.float16)
+
+
 # --------------------------------------------------------------------------- W2
 
 
@@ -249,8 +275,13 @@ class QuantLayer:
     def n_out(self) -> int:
         return int(len(self.idx))
 
+    @property
+    def zero_packed(self) -> np.ndarray:
+        """W4 zero points packed two per byte ([SPECTRA] section 3.4)."""
+        return pack_zeros_w4(self.zero)
+
     def w_hat(self) -> np.ndarray:
-        if self.fmt == 4:
+        if self.fmt in (4, 5):
             return dequant_w4(self.q, self.scale, self.zero)
         return dequant_w2(self.q, self.scale, self.zero)
 
@@ -266,14 +297,14 @@ def quantize_layer(fmt: int, W: np.ndarray, profile=None, ratio: float = 0.0) ->
     else:
         idx = np.zeros(0, np.int32)
         dense, wout = W, np.zeros((N, 0), np.float16)
-    if fmt == 4:
+    if fmt in (4, 5):   # 5: W4 whose zero points are stored packed (same values)
         q, sc, ze, _ = quantize_w4(dense)
         codes = pack_w4(q)
     elif fmt == 2:
         q, sc, ze = quantize_w2(dense)
         codes = pack_w2(q)
     else:
-        raise ValueError("fmt must be 4 or 2")
+        raise ValueError("fmt must be 4, 5 or 2")
     return QuantLayer(fmt, codes, sc, ze, q, idx, wout, N, K)
 
 

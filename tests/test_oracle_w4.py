@@ -137,3 +137,40 @@ def test_pack_hand_example():
     g = load_golden("w4_pack_example.json")
     q = np.array(g["codes"], np.uint8)[None, :]
     assert O.pack_w4(q)[0].tobytes().hex() == g["bytes_hex"]
+
+
+# ------------------------------------------------------- packed zero points
+
+
+def test_packed_zero_hand_example():
+    g = load_golden("w4_packed_zero_example.json")
+    z = np.array(g["zeros"], np.float16)[None, :]
+    zpk = O.pack_zeros_w4(z)
+    assert zpk[0].tobytes().hex() == g["bytes_hex"]
+    assert np.array_equal(O.unpack_zeros_w4(zpk, z.shape[1]), z)
+
+
+def test_packed_zero_exhaustive_roundtrip():
+    # every byte value decodes to two zero points and packs back to itself
+    b = np.arange(256, dtype=np.uint8)[:, None]
+    z = O.unpack_zeros_w4(b, 2)
+    assert sorted(set(z.ravel().tolist())) == list(range(16))
+    assert np.array_equal(z[:, 0], (b[:, 0] & 15).astype(np.float16))
+    assert np.array_equal(z[:, 1], (b[:, 0] >> 4).astype(np.float16))
+    assert np.array_equal(O.pack_zeros_w4(z), b)
+
+
+def test_packed_zero_layer_and_rejects():
+    # the zero points the quantizer makes always pack, and packing loses nothing
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((9, 32 * 7)).astype(np.float32)
+    W[:, :32] -= 5.0                 # an all-negative group: z clamps to 15
+    W[:, 32:64] += 5.0               # an all-positive group: z = 0
+    _, _, zero, _ = O.quantize_w4(W)
+    zpk = O.pack_zeros_w4(zero)
+    assert zpk.shape == (9, 4) and np.all(zpk[:, 3] >> 4 == 0)
+    assert np.array_equal(O.unpack_zeros_w4(zpk, 7), zero)
+    assert np.all(zero[:, 0] == 15) and np.all(zero[:, 1] == 0)
+    for bad in (np.array([[16.0]]), np.array([[-1.0]]), np.array([[2.5]])):
+        with pytest.raises(ValueError):
+            O.pack_zeros_w4(bad.astype(np.float16))
