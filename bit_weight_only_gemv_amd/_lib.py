@@ -27,6 +27,7 @@ WQ_ERR_UNSUPPORTED = -2
 WQ_ERR_HIP = -3
 WQ_FMT_W4 = 4
 WQ_FMT_W2 = 2
+WQ_FMT_W4P = 5
 WQ_FUSE_OUTLIERS = 1
 WQ_GROUP = 32
 WQ_MAX_K = 65536
@@ -44,12 +45,14 @@ SIGNATURES = {
     "wq_version": (ctypes.c_char_p, []),
     "wq_quantize_w4": (_INT, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "wq_quantize_w2": (_INT, [_P, _I64, _I64, _I32, _P, _P, _P]),
+    "wq_pack_zeros_w4": (_INT, [_P, _I64, _I64, _P]),
     "wq_select_outliers": (_INT, [_P, _I64, _I64, _P, ctypes.c_double, _P, _I64, _P]),
     "wq_split_outliers": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P]),
     "wq_dequant_host": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P]),
     "wq_dequant_device": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _P]),
     "wq_gemv_w4": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _P, _P]),
     "wq_gemv_w2": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _P, _P]),
+    "wq_gemv_w4p": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _P, _P]),
     "wq_gemm_wq": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _I64, _P, _P]),
     "wq_outlier_add": (_INT, [_P, _P, _I64, _I64, _P, _I64, _I64, _P, _P]),
     "wq_tiled_bytes": (_I64, [_INT, _I64, _I64, _I64]),
@@ -128,6 +131,14 @@ def wq_quantize_w2(W: np.ndarray):
     return codes, sc.view(np.float16), ze.view(np.float16)
 
 
+def wq_pack_zeros_w4(zeros, N: int, K: int) -> np.ndarray:
+    """FP16 W4 zero points [N, K/32] -> packed bytes uint8 [N, ceil(K/64)]."""
+    ze = _c(np.asarray(zeros).view(np.uint16), np.uint16)
+    out = np.empty((N, (K // WQ_GROUP + 1) // 2), np.uint8)
+    _check(load().wq_pack_zeros_w4(_np_ptr(ze), N, K, _np_ptr(out)))
+    return out
+
+
 def wq_select_outliers(W: np.ndarray, profile: np.ndarray, ratio: float) -> np.ndarray:
     W = _c(W, np.float32)
     N, K = W.shape
@@ -151,10 +162,17 @@ def wq_split_outliers(W: np.ndarray, idx: np.ndarray):
     return dense, wout.view(np.float16)
 
 
+def _zeros_arg(fmt, zeros):
+    """FP16 zero points (uint16 bits), or the packed bytes of W4P."""
+    if fmt == WQ_FMT_W4P:
+        return _c(zeros, np.uint8)
+    return _c(np.asarray(zeros).view(np.uint16), np.uint16)
+
+
 def wq_dequant_host(fmt: int, codes, scales, zeros, N: int, K: int) -> np.ndarray:
     codes = _c(codes, np.uint8)
     sc = _c(np.asarray(scales).view(np.uint16), np.uint16)
-    ze = _c(np.asarray(zeros).view(np.uint16), np.uint16)
+    ze = _zeros_arg(fmt, zeros)
     out = np.empty((N, K), np.uint16)
     _check(load().wq_dequant_host(fmt, _np_ptr(codes), _np_ptr(sc), _np_ptr(ze), N, K, _np_ptr(out)))
     return out.view(np.float16)
@@ -172,7 +190,7 @@ def wq_tile_host(fmt: int, codes, scales, zeros, out_w, N: int, K: int) -> np.nd
     n_out = 0 if out_w is None else int(np.asarray(out_w).shape[1])
     codes = _c(codes, np.uint8)
     sc = _c(np.asarray(scales).view(np.uint16), np.uint16)
-    ze = _c(np.asarray(zeros).view(np.uint16), np.uint16)
+    ze = _zeros_arg(fmt, zeros)
     ow = _c(np.asarray(out_w).view(np.uint16), np.uint16) if n_out else None
     nb = wq_tiled_bytes(fmt, N, K, n_out)
     out = np.empty(nb, np.uint8)
@@ -218,6 +236,12 @@ def wq_gemv_w4(codes, scales, zeros, N, K, x, y, out_idx=None, out_w=None, n_out
 def wq_gemv_w2(codes, scales, zeros, N, K, x, y, out_idx=None, out_w=None, n_out=0,
                flags=WQ_FUSE_OUTLIERS, stream=None):
     _gemv(load().wq_gemv_w2, codes, scales, zeros, N, K, x, y, out_idx, out_w, n_out, flags, stream)
+
+
+def wq_gemv_w4p(codes, scales, zeros_packed, N, K, x, y, out_idx=None, out_w=None, n_out=0,
+                flags=WQ_FUSE_OUTLIERS, stream=None):
+    _gemv(load().wq_gemv_w4p, codes, scales, zeros_packed, N, K, x, y, out_idx, out_w, n_out, flags,
+          stream)
 
 
 def wq_gemm_wq(fmt, codes, scales, zeros, N, K, X, M, Y, out_idx=None, out_w=None, n_out=0,

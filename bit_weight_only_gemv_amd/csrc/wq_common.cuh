@@ -40,6 +40,15 @@ __device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ uint16_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
+__device__ __forceinline__ uint8_t ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+// W4P: zero point of group g from the packed bytes of its row (group 2m in
+// bits 3:0 of byte m, group 2m + 1 in bits 7:4), as a float (exact integer).
+__device__ __forceinline__ float packed_zero(uint32_t byte, uint32_t g) {
+  return (float)((byte >> (4u * (g & 1u))) & 0x0Fu);
+}
 
 __device__ __forceinline__ float h2f(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);

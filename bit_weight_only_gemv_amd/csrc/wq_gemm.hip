@@ -45,7 +45,7 @@ constexpr int kKB = 16;                      // groups per staged block
 // Channel (0..31) of the group held in element e (0..7) of quarter q's fragment.
 template <int FMT>
 __device__ __forceinline__ int frag_channel(int q, int e) {
-  if (FMT == 4) {
+  if (FMT != 2) {
     // lo0 = (4q, 4q+2), hi0 = (4q+16, 4q+18), lo1 = (4q+1, 4q+3), hi1 = (4q+17, 4q+19)
     const int base[8] = {0, 2, 16, 18, 1, 3, 17, 19};
     return 4 * q + base[e];
@@ -98,13 +98,16 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
     s_xo[it] = f;
   }
 
-  const uint32_t row_bytes = (uint32_t)(FMT == 4 ? a.K / 2 : a.K / 4);
+  const uint32_t row_bytes = (uint32_t)(FMT != 2 ? a.K / 2 : a.K / 4);
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(a.codes + (uint64_t)row0 * row_bytes,
                                                clamp_bytes((uint64_t)rows_here * row_bytes));
   const __amdgpu_buffer_rsrc_t srs =
       make_rsrc(a.scales + (uint64_t)row0 * G, clamp_bytes((uint64_t)rows_here * G * 2));
+  // W4P (FMT 5): zero points packed two per byte, (G + 1) / 2 bytes per row
+  const uint64_t zrow = FMT == 5 ? (uint64_t)(G + 1) / 2 : (uint64_t)G * 2;
   const __amdgpu_buffer_rsrc_t zrs =
-      make_rsrc(a.zeros + (uint64_t)row0 * G, clamp_bytes((uint64_t)rows_here * G * 2));
+      make_rsrc(reinterpret_cast<const unsigned char*>(a.zeros) + (uint64_t)row0 * zrow,
+                clamp_bytes((uint64_t)rows_here * zrow));
   const __amdgpu_buffer_rsrc_t xrs =
       make_rsrc(a.X, clamp_bytes((uint64_t)a.M * a.K * 2));
 
@@ -154,9 +157,10 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
       const uint32_t g = (uint32_t)(kb + gl);
       const uint32_t mo = ((uint32_t)my_row * (uint32_t)G + g) * 2u;
       const float s = h2f(ld16(srs, mo));
-      const float z = h2f(ld16(zrs, mo));
+      const float z = FMT == 5 ? packed_zero(ld8(zrs, (uint32_t)my_row * (uint32_t)zrow + g / 2u), g)
+                               : h2f(ld16(zrs, mo));
       h8 b;
-      if constexpr (FMT == 4) {
+      if constexpr (FMT != 2) {
         const uint32_t w = ld32(crs, (uint32_t)my_row * row_bytes + g * 16u + 4u * fq);
         const uint32_t zz = (uint32_t)f2h(1024.0f + z);
         const h2 nz = as_h2(zz | (zz << 16)) * (_Float16)(-1.0f);
@@ -176,7 +180,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
       }
       const h8 av = s_xa[(gl * 16 + fn) * 4 + fq];
       const f4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b, zero4, 0, 0, 0);
-      if constexpr (FMT == 4) {
+      if constexpr (FMT != 2) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) acc[jj] = __builtin_fmaf(s, p[jj], acc[jj]);
       } else {
@@ -224,8 +228,8 @@ extern "C" int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales,
                           const uint16_t* out_w, int64_t n_out, uint32_t flags, const uint16_t* X,
                           int64_t M, uint16_t* Y, void* stream) {
   const char* who = "wq_gemm_wq";
-  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2)
-    return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4 or WQ_FMT_W2", who);
+  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2 && fmt != WQ_FMT_W4P)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2", who);
   if (int r = wq::check_shape(N, K, who)) return r;
   if (int r = wq::check_outlier_args(out_idx, out_w, n_out, K, who)) return r;
   if (M < 1) return wq::fail(WQ_ERR_INVALID_ARG, "%s: M must be >= 1", who);
@@ -244,11 +248,15 @@ extern "C" int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales,
   // M = 1 is the GEMV; 2 <= M <= 16 goes to the persistent matrix-core kernel
   // when its plan fits (it fuses the outlier pass; an unfused call with
   // outlier columns stays here)
-  if (M == 1)
+  if (M == 1) {
+    if (fmt == WQ_FMT_W4P)
+      return wq_gemv_w4p(codes, scales, reinterpret_cast<const uint8_t*>(zeros), N, K, out_idx,
+                         out_w, n_out, flags, X, Y, stream);
     return fmt == WQ_FMT_W4 ? wq_gemv_w4(codes, scales, zeros, N, K, out_idx, out_w, n_out, flags,
                                          X, Y, stream)
                             : wq_gemv_w2(codes, scales, zeros, N, K, out_idx, out_w, n_out, flags,
                                          X, Y, stream);
+  }
   if (a.fuse || n_out == 0) {
     int mode = 1;
     if (const char* e = getenv("WQ_GEMM_MMA")) mode = atoi(e);
@@ -264,11 +272,14 @@ extern "C" int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales,
   if (lds > kMaxLdsBytes)
     return wq::fail(WQ_ERR_UNSUPPORTED, "%s: %zu bytes of LDS needed (n_out too large)", who, lds);
   const dim3 grid((unsigned)((N + kGemmRows - 1) / kGemmRows)), block(kGemmWaves * 64);
-  const void* k = fmt == WQ_FMT_W4 ? reinterpret_cast<const void*>(&gemm_kernel<4>)
-                                   : reinterpret_cast<const void*>(&gemm_kernel<2>);
+  const void* k = fmt == WQ_FMT_W4    ? reinterpret_cast<const void*>(&gemm_kernel<4>)
+                  : fmt == WQ_FMT_W4P ? reinterpret_cast<const void*>(&gemm_kernel<5>)
+                                      : reinterpret_cast<const void*>(&gemm_kernel<2>);
   if (!allow_lds(k, lds)) return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit", who);
   if (fmt == WQ_FMT_W4)
     hipLaunchKernelGGL(gemm_kernel<4>, grid, block, lds, s, a);
+  else if (fmt == WQ_FMT_W4P)
+    hipLaunchKernelGGL(gemm_kernel<5>, grid, block, lds, s, a);
   else
     hipLaunchKernelGGL(gemm_kernel<2>, grid, block, lds, s, a);
   return check_launch(who);

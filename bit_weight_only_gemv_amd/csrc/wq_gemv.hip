@@ -67,6 +67,9 @@ struct Fmt<2> {
   static constexpr int kRowBytesPerK = 4;   // row bytes = K / 4
   typedef u2 Codes;
 };
+// W4P: the W4 codes; only the zero points are stored differently (packed).
+template <>
+struct Fmt<5> : Fmt<4> {};
 
 // Masked FP16 activation k of a group whose 32 values sit in 16 packed words.
 __device__ __forceinline__ uint16_t xh(const uint32_t (&xw)[16], uint32_t mask, int k) {
@@ -86,7 +89,7 @@ __device__ __forceinline__ void pair_group(const uint32_t (&xw)[16], uint32_t m,
 #pragma unroll
   for (int k = 0; k < 32; ++k) s += h2f(xh(xw, m, k));
   sum = s;
-  if constexpr (FMT == 4) {
+  if constexpr (FMT != 2) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       out[4 * j + 0] = pack2(xh(xw, m, 4 * j), xh(xw, m, 4 * j + 2));
@@ -180,7 +183,7 @@ __host__ __device__ inline size_t gemv_lds_bytes(int K, int RT, int wk, int n_ou
   size_t off = ((size_t)16 * RT * wk + 15) & ~(size_t)15;              // partial sums
   if (fmt == 2) off += (size_t)256 * kLutCopies * 8;                    // W2 centroid table
   off += ((size_t)RT * G * 2 + 16 + 15) & ~(size_t)15;                 // scales
-  off += ((size_t)RT * G * 2 + 16 + 15) & ~(size_t)15;                 // zeros
+  off += ((size_t)RT * (fmt == 5 ? (G + 1) / 2 : G * 2) + 16 + 15) & ~(size_t)15;   // zeros
   if (has_out) {
     off += ((size_t)RT * n_out * 2 + 16 + 15) & ~(size_t)15;           // outlier slab rows
     off += ((size_t)n_out * 4 + 16 + 15) & ~(size_t)15;                // outlier indices
@@ -206,12 +209,15 @@ __device__ __forceinline__ void load_rows(RowBatch<FMT, GPL>& b, __amdgpu_buffer
       const bool ok = rv && gvalid[i];
       const uint32_t co = ok ? rl * row_bytes + g * F::kGroupBytes : kOob;
       const uint32_t mo = ok ? (rl * G + g) * 2u : kOob;
-      if constexpr (FMT == 4)
+      if constexpr (FMT != 2)
         b.cw[u][i] = ld128(crs, co);
       else
         b.cw[u][i] = ld64(crs, co);
       b.sv[u][i] = ld16(srs, mo);
-      b.zv[u][i] = ld16(zrs, mo);
+      if constexpr (FMT == 5)   // the byte holding the zero point (rows of (G + 1) / 2 bytes)
+        b.zv[u][i] = ld8(zrs, ok ? rl * ((G + 1u) / 2u) + g / 2u : kOob);
+      else
+        b.zv[u][i] = ld16(zrs, mo);
     }
     if constexpr (HAS_OUT) {
 #pragma unroll
@@ -292,7 +298,8 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
   unsigned char* s_sc = smem + off;
   off += align16((size_t)RT * G * 2 + 16);
   unsigned char* s_zr = smem + off;
-  off += align16((size_t)RT * G * 2 + 16);
+  const int Gz = FMT == 5 ? (G + 1) / 2 : G * 2;   // bytes of zero points per row
+  off += align16((size_t)RT * Gz + 16);
   unsigned char* s_ow = smem + off;
   if (HAS_OUT) off += align16((size_t)RT * a.n_out * 2 + 16);
   int32_t* s_idx = reinterpret_cast<int32_t*>(smem + off);
@@ -312,7 +319,8 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
   }
   const uint64_t meta_total = (uint64_t)a.N * G * 2;
   st_sc.issue(a.scales, (uint64_t)tile0 * G * 2, (uint64_t)rows_here * G * 2, meta_total, tid, nthr);
-  st_zr.issue(a.zeros, (uint64_t)tile0 * G * 2, (uint64_t)rows_here * G * 2, meta_total, tid, nthr);
+  st_zr.issue(a.zeros, (uint64_t)tile0 * Gz, (uint64_t)rows_here * Gz, (uint64_t)a.N * Gz, tid,
+              nthr);
   if constexpr (HAS_OUT)
     st_ow.issue(a.out_w, (uint64_t)tile0 * a.n_out * 2, (uint64_t)rows_here * a.n_out * 2,
                 (uint64_t)a.N * a.n_out * 2, tid, nthr);
@@ -341,7 +349,7 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
       for (int i = 0; i < GPL; ++i) {
         const uint32_t g = (uint32_t)group_of<FMT, GPL>(kw, i, lane);
         const uint32_t co = (rv && gvalid[i]) ? rb + g * F::kGroupBytes : kOob;
-        if constexpr (FMT == 4)
+        if constexpr (FMT != 2)
           cw[u][i] = ld128(crs, co);
         else
           cw[u][i] = ld64(crs, co);
@@ -408,7 +416,7 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
 #pragma unroll
     for (int m = 0; m < 16; ++m) sum = __builtin_amdgcn_fdot2(as_h2(xw[m]), as_h2(one2), sum, false);
     sx[i] = sum;
-    if constexpr (FMT == 4) {
+    if constexpr (FMT != 2) {
       // (4j, 4j+2), (4j+16, 4j+18), (4j+1, 4j+3), (4j+17, 4j+19)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -439,8 +447,9 @@ __global__ void __launch_bounds__(512) gemv_lds_kernel(GemvArgs a) {
       if (!gvalid[i]) continue;
       const int g = group_of<FMT, GPL>(kw, i, lane);
       const float s = h2f(sc16[rl * G + g]);
-      const float z = h2f(zr16[rl * G + g]);
-      if constexpr (FMT == 4) {
+      const float z = FMT == 5 ? packed_zero(s_zr[st_zr.shift + rl * Gz + (g >> 1)], (uint32_t)g)
+                               : h2f(zr16[rl * G + g]);
+      if constexpr (FMT != 2) {
         acc = w4_group_dot(cw[u][i], xr[i], s, z, sx[i], acc);
       } else {
         // byte b of the group = codes 4b .. 4b + 3 = activation words 2b, 2b + 1
@@ -539,8 +548,10 @@ __global__ void __launch_bounds__(512) gemv_reg_kernel(GemvArgs a) {
       make_rsrc(a.codes + (uint64_t)tile0 * row_bytes, clamp_bytes((uint64_t)rows_here * row_bytes));
   const __amdgpu_buffer_rsrc_t srs =
       make_rsrc(a.scales + (uint64_t)tile0 * G, clamp_bytes((uint64_t)rows_here * G * 2));
+  const uint64_t zrow = FMT == 5 ? (uint64_t)(G + 1) / 2 : (uint64_t)G * 2;   // bytes per row
   const __amdgpu_buffer_rsrc_t zrs =
-      make_rsrc(a.zeros + (uint64_t)tile0 * G, clamp_bytes((uint64_t)rows_here * G * 2));
+      make_rsrc(reinterpret_cast<const unsigned char*>(a.zeros) + (uint64_t)tile0 * zrow,
+                clamp_bytes((uint64_t)rows_here * zrow));
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(
       do_out ? a.out_w + (uint64_t)tile0 * a.n_out : a.out_w,
       do_out ? clamp_bytes((uint64_t)rows_here * a.n_out * 2) : 0u);
@@ -594,8 +605,9 @@ __global__ void __launch_bounds__(512) gemv_reg_kernel(GemvArgs a) {
       for (int i = 0; i < GPL; ++i) {
         if (!gvalid[i]) continue;
         const float s = h2f(b.sv[u][i]);
-        const float z = h2f(b.zv[u][i]);
-        if constexpr (FMT == 4) {
+        const float z = FMT == 5 ? packed_zero(b.zv[u][i], (uint32_t)((kw * GPL + i) * kWave + lane))
+                                 : h2f(b.zv[u][i]);
+        if constexpr (FMT != 2) {
           acc = w4_group_dot(b.cw[u][i], xr[i], s, z, sx[i], acc);
         } else {
           float ac = 0.f;
@@ -760,7 +772,8 @@ static int gemv_entry(int fmt, const uint8_t* codes, const uint16_t* scales, con
                                a.fuse ? n_out : 0, x, y, s, who, mode, &launched);
     if (r != WQ_OK || launched) return r;
   }
-  return fmt == 4 ? launch_gemv<4>(a, s, who) : launch_gemv<2>(a, s, who);
+  return fmt == 4 ? launch_gemv<4>(a, s, who)
+                  : fmt == 5 ? launch_gemv<5>(a, s, who) : launch_gemv<2>(a, s, who);
 }
 
 extern "C" int wq_gemv_w4(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
@@ -769,6 +782,14 @@ extern "C" int wq_gemv_w4(const uint8_t* codes, const uint16_t* scales, const ui
                           void* stream) {
   return gemv_entry(4, codes, scales, zeros, N, K, out_idx, out_w, n_out, flags, x, y, stream,
                     "wq_gemv_w4");
+}
+
+extern "C" int wq_gemv_w4p(const uint8_t* codes, const uint16_t* scales,
+                           const uint8_t* zeros_packed, int64_t N, int64_t K,
+                           const int32_t* out_idx, const uint16_t* out_w, int64_t n_out,
+                           uint32_t flags, const uint16_t* x, uint16_t* y, void* stream) {
+  return gemv_entry(5, codes, scales, reinterpret_cast<const uint16_t*>(zeros_packed), N, K,
+                    out_idx, out_w, n_out, flags, x, y, stream, "wq_gemv_w4p");
 }
 
 extern "C" int wq_gemv_w2(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
@@ -783,8 +804,8 @@ extern "C" int wq_gemv_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K
                              const int32_t* out_idx, int64_t n_out, const uint16_t* x,
                              uint16_t* y, void* stream) {
   const char* who = "wq_gemv_tiled";
-  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2)
-    return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4 or WQ_FMT_W2", who);
+  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2 && fmt != WQ_FMT_W4P)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2", who);
   if (int r = wq::check_shape(N, K, who)) return r;
   if (n_out < 0 || n_out > K)
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: n_out must be in [0, K] (got %lld)", who,

@@ -281,6 +281,27 @@ int wq_select_outliers(const float* W, int64_t N, int64_t K, const double* profi
   return wq::ok();
 }
 
+int wq_pack_zeros_w4(const uint16_t* zeros, int64_t N, int64_t K, uint8_t* zeros_packed) {
+  if (int r = wq::check_shape(N, K, "wq_pack_zeros_w4")) return r;
+  if (!zeros || !zeros_packed) return fail(WQ_ERR_INVALID_ARG, "wq_pack_zeros_w4: NULL pointer");
+  const int64_t G = K / WQ_GROUP, Gp = (G + 1) / 2;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t m = 0; m < Gp; ++m) {
+      uint32_t b = 0;
+      for (int64_t h = 0; h < 2 && 2 * m + h < G; ++h) {
+        const float z = f16_to_f32(zeros[n * G + 2 * m + h]);
+        if (!(z >= 0.f && z <= 15.f && z == (float)(int)z))
+          return fail(WQ_ERR_INVALID_ARG,
+                      "wq_pack_zeros_w4: zero point of row %lld group %lld is not an integer "
+                      "in 0..15", (long long)n, (long long)(2 * m + h));
+        b |= (uint32_t)z << (4 * h);
+      }
+      zeros_packed[n * Gp + m] = (uint8_t)b;
+    }
+  }
+  return wq::ok();
+}
+
 int wq_split_outliers(const float* W, int64_t N, int64_t K, const int32_t* idx, int64_t n_out,
                       float* W_dense, uint16_t* W_out) {
   if (int r = wq::check_shape(N, K, "wq_split_outliers")) return r;
@@ -304,8 +325,9 @@ int wq_split_outliers(const float* W, int64_t N, int64_t K, const int32_t* idx, 
 
 int wq_dequant_host(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
                     int64_t N, int64_t K, uint16_t* W_hat) {
-  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2)
-    return fail(WQ_ERR_INVALID_ARG, "wq_dequant_host: fmt must be WQ_FMT_W4 or WQ_FMT_W2");
+  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2 && fmt != WQ_FMT_W4P)
+    return fail(WQ_ERR_INVALID_ARG,
+                "wq_dequant_host: fmt must be WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2");
   if (int r = wq::check_shape(N, K, "wq_dequant_host")) return r;
   if (!codes || !scales || !zeros || !W_hat)
     return fail(WQ_ERR_INVALID_ARG, "wq_dequant_host: NULL pointer");
@@ -315,9 +337,15 @@ int wq_dequant_host(int fmt, const uint8_t* codes, const uint16_t* scales, const
   for (int64_t n = 0; n < N; ++n) {
     for (int64_t g = 0; g < G; ++g) {
       const float s = f16_to_f32(scales[n * G + g]);
-      const float z = f16_to_f32(zeros[n * G + g]);
+      float z;
+      if (fmt == WQ_FMT_W4P) {
+        const uint8_t* zp = reinterpret_cast<const uint8_t*>(zeros) + n * ((G + 1) / 2);
+        z = (float)((zp[g / 2] >> (4 * (g % 2))) & 0x0F);
+      } else {
+        z = f16_to_f32(zeros[n * G + g]);
+      }
       uint16_t* out = W_hat + n * K + g * WQ_GROUP;
-      if (fmt == WQ_FMT_W4) {
+      if (fmt == WQ_FMT_W4 || fmt == WQ_FMT_W4P) {
         const uint8_t* c = codes + n * (K / 2) + g * 16;
         for (int k = 0; k < 16; ++k) {
           const float lo = (float)(c[k] & 0x0F) - z;
@@ -340,8 +368,9 @@ int wq_dequant_host(int fmt, const uint8_t* codes, const uint16_t* scales, const
 }
 
 int64_t wq_tiled_bytes(int fmt, int64_t N, int64_t K, int64_t n_out) {
-  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2)
-    return fail(WQ_ERR_INVALID_ARG, "wq_tiled_bytes: fmt must be WQ_FMT_W4 or WQ_FMT_W2");
+  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2 && fmt != WQ_FMT_W4P)
+    return fail(WQ_ERR_INVALID_ARG,
+                "wq_tiled_bytes: fmt must be WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2");
   if (int r = wq::check_shape(N, K, "wq_tiled_bytes")) return r;
   if (n_out < 0 || n_out > K)
     return fail(WQ_ERR_INVALID_ARG, "wq_tiled_bytes: n_out must be in [0, K]");
@@ -360,7 +389,7 @@ int wq_tile_host(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
     return fail(WQ_ERR_INVALID_ARG, "wq_tile_host: tiled buffer holds %lld bytes, %lld needed",
                 (long long)tiled_bytes, (long long)need);
   const wq::TiledGeometry g = wq::tiled_geometry(fmt, N, K, n_out);
-  const int64_t row_bytes = fmt == WQ_FMT_W4 ? K / 2 : K / 4;
+  const int64_t row_bytes = fmt == WQ_FMT_W2 ? K / 4 : K / 2;
   const int64_t G = K / WQ_GROUP;
   const int64_t SB = g.slice_bytes;
   std::memset(tiled, 0, (size_t)g.total);
@@ -369,7 +398,7 @@ int wq_tile_host(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
     for (int64_t s = 0; s < g.nks; ++s) {
       const int64_t tile = b * g.nks + s;
       uint8_t* ct = tiled + g.codes_off + tile * 16 * SB;
-      uint8_t* mt = tiled + g.meta_off + tile * 1024;
+      uint8_t* mt = tiled + g.meta_off + tile * g.meta_tile;
       for (int64_t n = 0; n < 16; ++n) {
         const int64_t row = 16 * b + n;
         if (row >= N) break;
@@ -380,11 +409,23 @@ int wq_tile_host(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
               const int64_t col = s * SB + 64 * u + 16 * r + c;
               if (col < row_bytes) ct[1024 * u + 16 * lane + c] = codes[row * row_bytes + col];
             }
-          for (int64_t i = 0; i < 4; ++i) {
-            const int64_t grp = 16 * s + 4 * r + i;
-            if (grp >= G) continue;
-            put16(mt + 2 * (8 * lane + i), scales[row * G + grp]);
-            put16(mt + 2 * (8 * lane + 4 + i), zeros[row * G + grp]);
+          if (fmt == WQ_FMT_W4P) {
+            const uint8_t* zp = reinterpret_cast<const uint8_t*>(zeros) + row * ((G + 1) / 2);
+            for (int64_t i = 0; i < 4; ++i) {
+              const int64_t grp = 16 * s + 4 * r + i;
+              if (grp < G) put16(mt + 2 * (4 * lane + i), scales[row * G + grp]);
+            }
+            for (int64_t j = 0; j < 2; ++j) {
+              const int64_t m = 8 * s + 2 * r + j;
+              if (m < (G + 1) / 2) mt[512 + 2 * lane + j] = zp[m];
+            }
+          } else {
+            for (int64_t i = 0; i < 4; ++i) {
+              const int64_t grp = 16 * s + 4 * r + i;
+              if (grp >= G) continue;
+              put16(mt + 2 * (8 * lane + i), scales[row * G + grp]);
+              put16(mt + 2 * (8 * lane + 4 + i), zeros[row * G + grp]);
+            }
           }
         }
       }

@@ -13,6 +13,7 @@ namespace wqd {
 // single rounding to FP16 remains.  W2: w_hat = FP16(float32(S C[q] + Z)); the
 // product S C[q] of two FP16 values is exact in float32, so the fused
 // multiply-add rounds exactly once, like a multiply followed by an add.
+// FMT 5 (W4P) is W4 with the zero point read from its packed nibble.
 template <int FMT>
 __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint16_t* __restrict__ scales,
@@ -24,9 +25,15 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict_
        it += (int64_t)gridDim.x * blockDim.x) {
     const int64_t n = it / G, g = it % G;
     const float s = h2f(scales[it]);
-    const float z = h2f(zeros[it]);
+    float z;
+    if constexpr (FMT == 5) {
+      const uint8_t* zp = reinterpret_cast<const uint8_t*>(zeros) + n * ((G + 1) / 2);
+      z = (float)((zp[g >> 1] >> (4 * (g & 1))) & 0x0Fu);
+    } else {
+      z = h2f(zeros[it]);
+    }
     uint16_t w[32];
-    if constexpr (FMT == 4) {
+    if constexpr (FMT == 4 || FMT == 5) {
       const u4v c = *reinterpret_cast<const u4v*>(codes + n * (K / 2) + g * 16);
       const uint32_t wv[4] = {c.x, c.y, c.z, c.w};
       const float zlo = 1024.0f + z, zhi = 1024.0f + 16.0f * z;
@@ -157,8 +164,8 @@ extern "C" int wq_dequant_device(int fmt, const uint8_t* codes, const uint16_t* 
                                  const uint16_t* zeros, int64_t N, int64_t K, uint16_t* W_hat,
                                  void* stream) {
   const char* who = "wq_dequant_device";
-  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2)
-    return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4 or WQ_FMT_W2", who);
+  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2 && fmt != WQ_FMT_W4P)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2", who);
   if (int r = wq::check_shape(N, K, who)) return r;
   if (!codes || !scales || !zeros || !W_hat) return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL", who);
   if (!aligned16(codes) || !aligned16(W_hat))
@@ -169,6 +176,9 @@ extern "C" int wq_dequant_device(int fmt, const uint8_t* codes, const uint16_t* 
   hipStream_t s = (hipStream_t)stream;
   if (fmt == WQ_FMT_W4)
     hipLaunchKernelGGL(dequant_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales,
+                       zeros, N, K, W_hat);
+  else if (fmt == WQ_FMT_W4P)
+    hipLaunchKernelGGL(dequant_kernel<5>, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales,
                        zeros, N, K, W_hat);
   else
     hipLaunchKernelGGL(dequant_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales,

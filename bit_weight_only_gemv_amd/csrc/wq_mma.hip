@@ -117,6 +117,8 @@ struct MmaFmt<4> {
   static constexpr int kRowBytesDiv = 2;
 };
 template <>
+struct MmaFmt<5> : MmaFmt<4> {};   // W4P: W4 codes, packed zero points
+template <>
 struct MmaFmt<2> {
   static constexpr int kLoads = 2;
   static constexpr int kSliceBytes = 128;
@@ -188,9 +190,11 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   const uint64_t tiles = (uint64_t)a.nrb * a.nks;
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(
       a.codes, clamp_bytes(TILED ? tiles * 16 * F::kSliceBytes : (uint64_t)a.N * row_bytes));
-  const uint64_t meta = TILED ? tiles * 1024 : (uint64_t)a.N * G * 2;
+  const uint64_t meta = TILED ? tiles * (FMT == 5 ? 640 : 1024) : (uint64_t)a.N * G * 2;
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.scales, clamp_bytes(meta));
-  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(TILED ? a.scales : a.zeros, clamp_bytes(meta));
+  const __amdgpu_buffer_rsrc_t zrs =
+      make_rsrc(TILED ? a.scales : a.zeros,
+                clamp_bytes(TILED ? meta : FMT == 5 ? (uint64_t)a.N * (G / 2) : meta));
   // The row-major slab is read with 4-byte loads at 4-byte-aligned offsets;
   // its record count is rounded up to that size, which stays inside the
   // 16-byte block (and page) of the last element.
@@ -244,16 +248,24 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
       const uint32_t cbase = tile * (16u * F::kSliceBytes) + 16u * (uint32_t)lane;
 #pragma unroll
       for (int u = 0; u < F::kLoads; ++u) it.cw[u] = ld128(c_, cbase + 1024u * u);
-      const u4v m = ld128(s_, tile * 1024u + 16u * (uint32_t)lane);
-      it.sv = (u2){m.x, m.y};
-      it.zv = (u2){m.z, m.w};
+      if constexpr (FMT == 5) {   // 640-byte tile: 4 scales per lane, then 4 packed zeros
+        it.sv = ld64(s_, tile * 640u + 8u * (uint32_t)lane);
+        it.zv = (u2){ld16(s_, tile * 640u + 512u + 2u * (uint32_t)lane), 0u};
+      } else {
+        const u4v m = ld128(s_, tile * 1024u + 16u * (uint32_t)lane);
+        it.sv = (u2){m.x, m.y};
+        it.zv = (u2){m.z, m.w};
+      }
     } else {
       const uint32_t rbase = row * row_bytes + (uint32_t)(ks * F::kSliceBytes + 16 * r);
 #pragma unroll
       for (int u = 0; u < F::kLoads; ++u) it.cw[u] = ld128(c_, rbase + 64u * u);
       const uint32_t mo = (row * (uint32_t)G + (uint32_t)(ks * kSliceGroups + 4 * r)) * 2u;
       it.sv = ld64(s_, mo);
-      it.zv = ld64(z_, mo);
+      if constexpr (FMT == 5)   // groups 16 ks + 4 r .. + 3: two bytes of the packed row
+        it.zv = (u2){ld16(z_, row * (uint32_t)(G / 2) + (uint32_t)(8 * ks + 2 * r)), 0u};
+      else
+        it.zv = ld64(z_, mo);
     }
     if constexpr (OUT) {
       const __amdgpu_buffer_rsrc_t o_ = valid ? ors : nul;
@@ -340,7 +352,7 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
             sum = __builtin_amdgcn_fdot2(as_h2(tw[i]), as_h2(0x3C003C00u), sum, false);
         }
         reinterpret_cast<float*>(smem + slice_sx(s))[lane] =
-            FMT == 4 ? sum * 5.9604644775390625e-8f : sum;
+            FMT != 2 ? sum * 5.9604644775390625e-8f : sum;
       }
     }
   };
@@ -444,7 +456,7 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   auto compute = [&](const Item<FMT, OUT>& it, int ri, int si) {
     const int row = (int)(blockIdx.x + (unsigned)ri * gridDim.x) * 16 + n16;
     f4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (FMT == 4) {
+    if constexpr (FMT != 2) {
       // c0: low-nibble steps (values q 2^-24), c1: high-nibble steps (16 q 2^-24)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -504,8 +516,9 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float s = h2f((uint16_t)(sw[j >> 1] >> (16 * (j & 1))));
-      const float z = h2f((uint16_t)(zw[j >> 1] >> (16 * (j & 1))));
-      if constexpr (FMT == 4) {
+      const float z = FMT == 5 ? (float)((zw[0] >> (4 * j)) & 0x0Fu)
+                               : h2f((uint16_t)(zw[j >> 1] >> (16 * (j & 1))));
+      if constexpr (FMT != 2) {
         float t = __builtin_fmaf(c1[j], 0.0625f, c0[j]);
         t = __builtin_fmaf(-z, sx4[j], t);
         v = __builtin_fmaf(s, t, v);
@@ -514,7 +527,7 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
         v = __builtin_fmaf(z, sx4[j], v);
       }
     }
-    if constexpr (FMT == 4) v *= 16777216.0f;
+    if constexpr (FMT != 2) v *= 16777216.0f;
     if constexpr (OUT) {
       if constexpr (TILED) {   // zero-padded chunks: no alignment, no mask
 #pragma unroll
@@ -592,6 +605,8 @@ struct MmbFmt<4> {
   static constexpr int kRowBytesDiv = 2;
 };
 template <>
+struct MmbFmt<5> : MmbFmt<4> {};   // W4P: W4 codes, packed zero points
+template <>
 struct MmbFmt<2> {
   static constexpr int kLoads = 1;
   static constexpr int kSliceBytes = 64;
@@ -661,7 +676,9 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   const __amdgpu_buffer_rsrc_t crs = make_rsrc(a.codes, clamp_bytes((uint64_t)a.N * row_bytes));
   const uint64_t meta = (uint64_t)a.N * G * 2;
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.scales, clamp_bytes(meta));
-  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(a.zeros, clamp_bytes(meta));
+  // W4P: zero points packed two per byte, (G / 2) bytes per row (G is even here)
+  const __amdgpu_buffer_rsrc_t zrs =
+      make_rsrc(a.zeros, clamp_bytes(FMT == 5 ? (uint64_t)a.N * (G / 2) : meta));
   const __amdgpu_buffer_rsrc_t ors =
       make_rsrc(a.out_w, clamp_bytes(((uint64_t)a.N * n_out * 2 + 3) & ~(uint64_t)3));
   const __amdgpu_buffer_rsrc_t irs = make_rsrc(a.out_idx, ((uint32_t)n_out * 4u + 15u) & ~15u);
@@ -723,7 +740,10 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     for (int u = 0; u < F::kLoads; ++u) it.cw[u] = ld128(c_, rbase + 16u * u);
     const uint32_t mo = (row * (uint32_t)G + (uint32_t)(ks * kSliceGroupsB + 2 * q)) * 2u;
     it.sv = ld32(s_, mo);
-    it.zv = ld32(z_, mo);
+    if constexpr (FMT == 5)   // groups 8 ks + 2 q, + 1: one byte of the packed row
+      it.zv = ld8(z_, row * (uint32_t)(G / 2) + (uint32_t)(4 * ks + q));
+    else
+      it.zv = ld32(z_, mo);
   };
   auto load_slab = [&](ItemB<FMT, OUT>& it, bool valid, int ks, int rb) {
     if constexpr (OUT) {
@@ -905,13 +925,18 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   };
   auto compute = [&](const ItemB<FMT, OUT>& it, int ri, int si) {
     f4 c = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (FMT == 4) {
+    if constexpr (FMT != 2) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const uint32_t sp = u ? splat_hi(it.sv) : splat_lo(it.sv);
         // -(1024 + z) in both halves: the zero is an exact small integer
-        const _Float16 zf = __builtin_bit_cast(_Float16, (uint16_t)(it.zv >> (16 * u)));
-        const uint32_t nz = splat_lo((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(-1024.0f16 - zf)));
+        uint32_t nz;
+        if constexpr (FMT == 5) {   // FP16 -(1024 + z) = 0xE400 | z for z in 0..15
+          nz = splat_lo(0xE400u | ((it.zv >> (4 * u)) & 0x0Fu));
+        } else {
+          const _Float16 zf = __builtin_bit_cast(_Float16, (uint16_t)(it.zv >> (16 * u)));
+          nz = splat_lo((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(-1024.0f16 - zf)));
+        }
         const uint32_t d[4] = {it.cw[u].x, it.cw[u].y, it.cw[u].z, it.cw[u].w};
         uint32_t b[4][4];
 #pragma unroll
@@ -1074,7 +1099,7 @@ static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_ou
         g.total - g.slab_off > kMaxArrayBytes)
       return p;
   } else {
-    const int64_t row_bytes = fmt == 4 ? K / 2 : K / 4;
+    const int64_t row_bytes = fmt == 2 ? K / 4 : K / 2;
     if (N * row_bytes > kMaxArrayBytes || N * (K / 32) * 2 > kMaxArrayBytes ||
         N * n_out * 2 > kMaxArrayBytes)
       return p;
@@ -1120,7 +1145,7 @@ struct MmbPlan {
 static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M) {
   MmbPlan p{};
   if (K % 128 != 0 || K > 65536 || n_out > 1024 || M < 2 || M > 16) return p;
-  const int64_t row_bytes = fmt == 4 ? K / 2 : K / 4;
+  const int64_t row_bytes = fmt == 2 ? K / 4 : K / 2;
   if (N * row_bytes > 0xFFFFFFF0ll || N * (K / 32) * 2 > 0xFFFFFFF0ll ||
       N * n_out * 2 > 0xFFFFFFF0ll || M * K * 2 > 0xFFFFFFF0ll)
     return p;
@@ -1201,6 +1226,7 @@ int wqd_gemv_mma(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scal
   WQ_MMA_LAUNCH(F_, O_, T_, 8)
 #define WQ_MMA_LAYOUTS(F_, O_) WQ_MMA_SLICES(F_, O_, false) WQ_MMA_SLICES(F_, O_, true)
   WQ_MMA_LAYOUTS(4, false) WQ_MMA_LAYOUTS(4, true) WQ_MMA_LAYOUTS(2, false) WQ_MMA_LAYOUTS(2, true)
+  WQ_MMA_LAYOUTS(5, false) WQ_MMA_LAYOUTS(5, true)
 #undef WQ_MMA_SLICES
 #undef WQ_MMA_LAYOUTS
 #undef WQ_MMA_LAUNCH
@@ -1242,6 +1268,7 @@ int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
   }
   WQ_MMB_LAUNCH(4, 0) WQ_MMB_LAUNCH(4, 1) WQ_MMB_LAUNCH(4, 2) WQ_MMB_LAUNCH(4, 4)
   WQ_MMB_LAUNCH(2, 0) WQ_MMB_LAUNCH(2, 1) WQ_MMB_LAUNCH(2, 2) WQ_MMB_LAUNCH(2, 4)
+  WQ_MMB_LAUNCH(5, 0) WQ_MMB_LAUNCH(5, 1) WQ_MMB_LAUNCH(5, 2) WQ_MMB_LAUNCH(5, 4)
 #undef WQ_MMB_LAUNCH
   return WQ_OK;
 }

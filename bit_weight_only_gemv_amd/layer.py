@@ -22,9 +22,9 @@ class HostLayer:
     fmt: int
     N: int
     K: int
-    codes: np.ndarray          # uint8 [N, K/2] (W4) or [N, K/4] (W2)
+    codes: np.ndarray          # uint8 [N, K/2] (W4, W4P) or [N, K/4] (W2)
     scales: np.ndarray         # float16 [N, K/32]
-    zeros: np.ndarray          # float16 [N, K/32]
+    zeros: np.ndarray          # float16 [N, K/32]; W4P: packed uint8 [N, ceil(K/64)]
     idx: np.ndarray            # int32 [n_out], ascending
     wout: np.ndarray           # float16 [N, n_out]
 
@@ -45,12 +45,14 @@ def pack_host(fmt: int, W: np.ndarray, profile: Optional[np.ndarray] = None,
         dense, wout = L.wq_split_outliers(W, idx)
     else:
         dense, wout = W, np.zeros((N, 0), np.float16)
-    if fmt == L.WQ_FMT_W4:
+    if fmt in (L.WQ_FMT_W4, L.WQ_FMT_W4P):
         codes, sc, ze = L.wq_quantize_w4(dense)
+        if fmt == L.WQ_FMT_W4P:
+            ze = L.wq_pack_zeros_w4(ze, N, K)
     elif fmt == L.WQ_FMT_W2:
         codes, sc, ze = L.wq_quantize_w2(dense)
     else:
-        raise ValueError("fmt must be 4 or 2")
+        raise ValueError("fmt must be 4, 5 (W4P) or 2")
     return HostLayer(fmt, N, K, codes, sc, ze, idx, wout)
 
 
@@ -68,7 +70,10 @@ class DeviceLayer:
 
         self.codes = up(host.codes, np.uint8)
         self.scales = up(host.scales.view(np.int16), np.int16)
-        self.zeros = up(host.zeros.view(np.int16), np.int16)
+        if self.fmt == L.WQ_FMT_W4P:
+            self.zeros = up(host.zeros, np.uint8)
+        else:
+            self.zeros = up(host.zeros.view(np.int16), np.int16)
         if self.n_out:
             self.idx = up(host.idx, np.int32)
             self.wout = up(host.wout.view(np.int16), np.int16)
@@ -83,12 +88,13 @@ class DeviceLayer:
     def nbytes(self, M: int = 1) -> int:
         """Algorithmic bytes of one product: codes, scales, zeros, outlier slab
         and indices, X and Y."""
-        b = self.codes.numel() + 2 * self.scales.numel() + 2 * self.zeros.numel()
+        b = self.codes.numel() + 2 * self.scales.numel() + self.zeros.numel() * self.zeros.element_size()
         b += 2 * self.N * self.n_out + 4 * self.n_out
         return b + 2 * M * self.K + 2 * M * self.N
 
     def gemv(self, x, y, flags=L.WQ_FUSE_OUTLIERS, stream=None):
-        fn = L.wq_gemv_w4 if self.fmt == L.WQ_FMT_W4 else L.wq_gemv_w2
+        fn = {L.WQ_FMT_W4: L.wq_gemv_w4, L.WQ_FMT_W2: L.wq_gemv_w2,
+              L.WQ_FMT_W4P: L.wq_gemv_w4p}[self.fmt]
         fn(self.codes, self.scales, self.zeros, self.N, self.K, x, y, self.idx, self.wout,
            self.n_out, flags, stream)
 

@@ -13,6 +13,10 @@
  *       least squares.  Reconstruction w_hat = S * C[q] + Z.  Source: the
  *       OTF-LLM v4.0 page (pypi otf-llm 4.0.0), sections 2, 3 and 5.
  *
+ *   W4P: W4 with its zero points stored packed, two 4-bit zero points of
+ *       adjacent groups per byte (SPECTRA section 3.4, "PackedZero"), 4.625
+ *       instead of 5 bits per weight.  Same codes, scales and values as W4.
+ *
  * In both formats a sorted set of n_out input channels (outlier columns) is kept
  * exactly in FP16 and added in the same kernel launch (SPECTRA section 4.1,
  * OTF-LLM "Architecture & Key Innovations": FP16 outliers plus quantized
@@ -24,7 +28,11 @@
  *   codes W2  uint8 [N][K/4]   byte j of row n = q[4j] | q[4j+1]<<2 | q[4j+2]<<4 | q[4j+3]<<6
  *                              (OTF-LLM section 5)
  *   scales    uint16 (FP16 bits) [N][G]
- *   zeros     uint16 (FP16 bits) [N][G]
+ *   zeros     uint16 (FP16 bits) [N][G]   (W4, W2)
+ *   zeros W4P uint8 [N][ceil(G/2)]   byte m of row n = z[n][2m] | z[n][2m+1] << 4
+ *                              (the high nibble of the last byte is 0 when G is odd);
+ *                              entry points that take `const uint16_t* zeros` read
+ *                              these bytes through that pointer when fmt is WQ_FMT_W4P
  *   out_idx   int32  [n_out], strictly increasing, each in [0, K)
  *   out_w     uint16 (FP16 bits) [N][n_out]   out_w[n][j] = W[n][out_idx[j]]
  *   x / X     uint16 (FP16 bits) [M][K];  y / Y  uint16 (FP16 bits) [M][N]
@@ -61,6 +69,7 @@ extern "C" {
 
 #define WQ_FMT_W4 4
 #define WQ_FMT_W2 2
+#define WQ_FMT_W4P 5 /* W4 with packed 4-bit zero points */
 
 /* flags of the product entry points */
 #define WQ_FUSE_OUTLIERS 1u /* add the FP16 outlier columns inside the same launch */
@@ -101,6 +110,12 @@ int wq_quantize_w4(const float* W, int64_t N, int64_t K, int32_t group,
 int wq_quantize_w2(const float* W, int64_t N, int64_t K, int32_t group,
                    uint8_t* codes, uint16_t* scales, uint16_t* zeros);
 
+/* Packs FP16 W4 zero points [N][G] (as wq_quantize_w4 writes them) two per
+ * byte (SPECTRA section 3.4): zeros_packed[n][m] = z[n][2m] | z[n][2m+1] << 4,
+ * [N][ceil(G/2)].  Errors: WQ_ERR_INVALID_ARG for NULL pointers, bad N/K, or a
+ * zero point that is not an integer in 0..15. */
+int wq_pack_zeros_w4(const uint16_t* zeros, int64_t N, int64_t K, uint8_t* zeros_packed);
+
 /* Profile-guided outlier selection (OTF-LLM v4.0 section 4):
  * score_c = sqrt(sum_n W[n][c]^2) * profile[c] (float64, rows summed in order);
  * n_out = floor(ratio * K); the n_out highest scores (ties to the lower index),
@@ -119,9 +134,9 @@ int wq_split_outliers(const float* W, int64_t N, int64_t K, const int32_t* idx,
                       int64_t n_out, float* W_dense, uint16_t* W_out);
 
 /* Dequantize on the host to FP16 [N][K]:
- * W4  w_hat = FP16((q - z) * s)            (the float32 product is exact)
- * W2  w_hat = FP16(float32(S * C[q] + Z))  (one float32 rounding, then FP16).
- * fmt is WQ_FMT_W4 or WQ_FMT_W2. */
+ * W4, W4P  w_hat = FP16((q - z) * s)            (the float32 product is exact)
+ * W2       w_hat = FP16(float32(S * C[q] + Z))  (one float32 rounding, then FP16).
+ * fmt is WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2. */
 int wq_dequant_host(int fmt, const uint8_t* codes, const uint16_t* scales,
                     const uint16_t* zeros, int64_t N, int64_t K, uint16_t* W_hat);
 
@@ -155,9 +170,16 @@ int wq_gemv_w2(const uint8_t* codes, const uint16_t* scales, const uint16_t* zer
                int64_t n_out, uint32_t flags, const uint16_t* x, uint16_t* y,
                void* stream);
 
+/* Fused M = 1 GEMV of a W4P layer: wq_gemv_w4 with the zero points read from
+ * their packed bytes ([N][ceil(G/2)], layout above); identical results. */
+int wq_gemv_w4p(const uint8_t* codes, const uint16_t* scales, const uint8_t* zeros_packed,
+                int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
+                int64_t n_out, uint32_t flags, const uint16_t* x, uint16_t* y,
+                void* stream);
+
 /* Small-M batched product on matrix cores (SPECTRA section 4.2; M is a
  * runtime argument): Y[m][n] = FP16(sum_k X[m][k] w_hat[n][k] + outliers) for
- * 1 <= M <= WQ_GEMM_MAX_M, fmt WQ_FMT_W4 or WQ_FMT_W2.  X is [M][K], Y is [M][N].
+ * 1 <= M <= WQ_GEMM_MAX_M, fmt WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2.  X is [M][K], Y is [M][N].
  * M > WQ_GEMM_MAX_M returns WQ_ERR_UNSUPPORTED. */
 int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
                int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
@@ -190,6 +212,9 @@ int wq_outlier_add(const int32_t* idx, const uint16_t* out_w, int64_t n_out, int
  *   meta:  tile (b, s) of 512 FP16 entries at (b nks + s) 1024 bytes; entry
  *          8 (n + 16 r) + i     = scales[16 b + n][16 s + 4 r + i]  (i < 4)
  *          8 (n + 16 r) + 4 + i = zeros [16 b + n][16 s + 4 r + i]
+ *          W4P: tile (b, s) of 640 bytes at (b nks + s) 640; FP16 entry
+ *          4 (n + 16 r) + i = scales[16 b + n][16 s + 4 r + i], and bytes
+ *          512 + 2 (n + 16 r) + j (j < 2) = zeros_packed[16 b + n][8 s + 2 r + j]
  *   slab:  chunk (b, c) of 128 FP16 entries at (b nch + c) 256 bytes; entry
  *          8 n + i = out_w[16 b + n][8 c + i]                       (i < 8)
  */

@@ -2,6 +2,7 @@
 the same seeded inputs.
 
 * packed bytes and dequantized FP16 weights: bit-exact;
+* formats W4, W2 and W4P (W4 with its zero points packed two per byte);
 * products: every output element within |y - y_ref| <= 2e-3 sum|w x| + 1e-5
   (y_ref and sum|w x| in float64 from the oracle's own quantization).
 
@@ -50,6 +51,8 @@ def build(fmt, W, profile=None, ratio=0.0):
     ref = O.quantize_layer(fmt, W, profile, ratio)
     hl = pack_host(fmt, W, profile, ratio)
     assert np.array_equal(hl.codes, ref.codes) and np.array_equal(hl.idx, ref.idx)
+    if fmt == 5:
+        assert np.array_equal(hl.zeros, ref.zero_packed)
     return ref, DeviceLayer(hl)
 
 
@@ -72,7 +75,7 @@ def run_gemv(dl, x, flags=B.WQ_FUSE_OUTLIERS):
 # --------------------------------------------------------------- dequant
 
 
-@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("N,K,scale", [(5, 96, 0.02), (37, 4096, 0.02), (130, 14336, 0.02),
                                        (64, 1024, 1e-5), (16, 512, 300.0)])
 def test_dequant_device_bit_exact(fmt, N, K, scale):
@@ -100,7 +103,7 @@ def gemv_path(request, monkeypatch):
     return request.param
 
 
-@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("N,K", SHAPES)
 @pytest.mark.parametrize("outl", [False, True])
 def test_gemv_small(fmt, N, K, outl, gemv_path):
@@ -111,7 +114,7 @@ def test_gemv_small(fmt, N, K, outl, gemv_path):
     check_product(ref, y, L.x, f"w{fmt} {N}x{K} n_out={ref.n_out}")
 
 
-@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("n_out", [1, 31, 32, 33, 64, 65, 129, 500])
 def test_gemv_outlier_counts(fmt, n_out, gemv_path):
     K = 4096
@@ -124,7 +127,7 @@ def test_gemv_outlier_counts(fmt, n_out, gemv_path):
     check_product(ref, y, L.x, f"w{fmt} n_out={n_out}")
 
 
-@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("fmt", [4, 2, 5])
 def test_gemv_unfused_then_outlier_add(fmt):
     say(f"gemv unfused + outlier_add fmt={fmt}")
     L = synthetic.small_layer(fmt, 333, 4096, with_outliers=True, seed=5)
@@ -158,7 +161,7 @@ def run_gemv_tiled(dl, x):
     return y
 
 
-@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("N,K", TILED_SHAPES)
 @pytest.mark.parametrize("outl", [False, True])
 def test_gemv_tiled(fmt, N, K, outl, monkeypatch):
@@ -175,7 +178,7 @@ def test_gemv_tiled(fmt, N, K, outl, monkeypatch):
         assert torch.equal(y, y2)
 
 
-@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("n_out", [1, 7, 8, 9, 31, 33, 64, 65, 129, 256])
 def test_gemv_tiled_outlier_counts(fmt, n_out):
     K = 4096
@@ -241,7 +244,7 @@ def gemm_path(request, monkeypatch):
     return request.param
 
 
-@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 13, 16])
 @pytest.mark.parametrize("N,K,outl", [(129, 4096, False), (200, 2080, True), (64, 14336, True),
                                       (5000, 4224, True), (300, 8192, True), (40, 28672, True)])
@@ -259,12 +262,13 @@ def test_gemm_small(fmt, M, N, K, outl, gemm_path):
 # ------------------------------------------------------- full-size layers
 
 
-def test_full_w4_4096x4096_m1():
+@pytest.mark.parametrize("fmt", [4, 5])
+def test_full_w4_4096x4096_m1(fmt):
     L = synthetic.config1()
-    say("full W4 4096x4096 M=1")
-    ref, dl = build(4, L.W)
+    say(f"full W{'4P' if fmt == 5 else '4'} 4096x4096 M=1")
+    ref, dl = build(fmt, L.W)
     y, _ = run_gemv(dl, L.x)
-    check_product(ref, y, L.x, "W4 4096x4096")
+    check_product(ref, y, L.x, f"fmt {fmt} 4096x4096")
 
 
 def test_full_w2_14336x4096_outliers_m1():

@@ -149,3 +149,32 @@ def test_error_codes():
     assert lib.wq_gemm_wq(3, fake, fake, fake, 8, 64, None, None, 0, 1, fake, 2, fake, None) == -1
     assert lib.wq_gemv_w4(fake, fake, fake, 8, 65536 + 32, None, None, 0, 1, fake, fake, None) == -2
     assert lib.wq_read_probe(fake, 15, fake, None) == -1
+
+
+# ------------------------------------------------- W4P packed zero points
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (37, 4096), (5, 224)])
+def test_packed_zeros_match_oracle(N, K):
+    W = synthetic.gaussian_weights(N, K, 0.02, 201, N, K)
+    W[:, :32] -= 1.0     # all-negative first group: its zero point clamps to 15
+    ref = O.quantize_layer(5, W)
+    from bit_weight_only_gemv_amd.layer import pack_host
+    lib = pack_host(5, W)
+    assert np.array_equal(lib.codes, ref.codes)
+    assert np.array_equal(lib.zeros, ref.zero_packed)
+    assert lib.zeros.shape == (N, (K // 32 + 1) // 2)
+    wh = B.wq_dequant_host(5, lib.codes, lib.scales, lib.zeros, N, K)
+    assert np.array_equal(_bits(wh), _bits(ref.w_hat()))
+    # and the same values as the W4 layer with FP16 zero points
+    w4 = B.wq_dequant_host(4, ref.codes, ref.scale, ref.zero, N, K)
+    assert np.array_equal(_bits(wh), _bits(w4))
+
+
+def test_packed_zeros_reject_non_integer():
+    z = np.array([[3.0, 2.5]], np.float16)
+    with pytest.raises(B.WQError):
+        B.wq_pack_zeros_w4(z, 1, 64)
+    with pytest.raises(B.WQError):
+        B.wq_pack_zeros_w4(np.array([[16.0, 0.0]], np.float16), 1, 64)
+    assert B.wq_pack_zeros_w4(np.array([[15.0, 0.0]], np.float16), 1, 64).tolist() == [[15]]
