@@ -57,9 +57,13 @@ def _parse():
                    help="bytes per launch of the read / copy workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true", help="time Python-side launches, no graph")
-    p.add_argument("--layout", default="tiled", choices=["tiled", "rowmajor"],
-                   help="packed-array layout the M = 1 GEMV workloads time for `value` (the "
-                        "other one is timed too and reported beside it)")
+    p.add_argument("--w4-zeros", default="fp16", choices=["fp16", "packed"],
+                   help="zero points of the W4 workloads (w4_4096, sweep, batched): FP16, or "
+                        "packed two per byte (the W4P format)")
+    p.add_argument("--layout", default="best", choices=["best", "tiled", "rowmajor"],
+                   help="packed-array layout whose time the M = 1 GEMV workloads report as "
+                        "`value` (best: the faster of the two; the other one is timed too and "
+                        "reported beside it)")
     return p.parse_args()
 
 
@@ -78,8 +82,10 @@ def sweep_bytes_per_token(fmt: int, ratio: float) -> int:
     tot = 0
     for (_, _, _, N, K) in synthetic.config3_shapes():
         n_out = int(np.floor(ratio * K)) if ratio > 0 else 0
-        codes = N * K // (2 if fmt == 4 else 4)
-        tot += codes + 4 * N * (K // 32) + 2 * N * n_out + 4 * n_out + 2 * K + 2 * N
+        G = K // 32
+        codes = N * K // (4 if fmt == 2 else 2)
+        zeros = N * ((G + 1) // 2) if fmt == 5 else 2 * N * G   # W4P: packed, else FP16
+        tot += codes + 2 * N * G + zeros + 2 * N * n_out + 4 * n_out + 2 * K + 2 * N
     return tot
 
 
@@ -175,13 +181,14 @@ def gemv_workload(a, torch, L, label, timer):
     def step_tiled(i):
         layers[i % ncopy].gemv_tiled(x, ys[i % ncopy])
 
-    other = "rowmajor" if a.layout == "tiled" else "tiled"
     steps = {"rowmajor": step_rowmajor, "tiled": step_tiled}
-    ms_other = timer(steps[other], a.steps, a.warmup)
-    ms = timer(steps[a.layout], a.steps, a.warmup)
+    times = {k: timer(fn, a.steps, a.warmup) for k, fn in steps.items()}
+    layout = min(times, key=times.get) if a.layout == "best" else a.layout
+    other = "rowmajor" if layout == "tiled" else "tiled"
+    ms, ms_other = times[layout], times[other]
     gbs = nbytes / (ms * 1e-3) / 1e9
     bpt = sweep_bytes_per_token(L.fmt, L.ratio)
-    traffic = traffic_for(f"{label}_{a.layout}")
+    traffic = traffic_for(f"{label}_{layout}")
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -196,8 +203,9 @@ def gemv_workload(a, torch, L, label, timer):
         "dtype": "f16",
         "data": "synthetic (seeded Gaussian weights and activations; no checkpoint)",
         "config": {"workload": label, "N": base.N, "K": base.K, "M": 1, "n_out": base.n_out,
-                   "format": f"W{L.fmt} group-32", "accumulate": "f32",
-                   "bytes_per_step": nbytes, "rotated_copies": ncopy, "layout": a.layout,
+                   "format": {4: "W4", 2: "W2", 5: "W4P (packed zero points)"}[L.fmt] + " group-32",
+                   "accumulate": "f32",
+                   "bytes_per_step": nbytes, "rotated_copies": ncopy, "layout": layout,
                    "timing": "eager launches" if a.eager else "hip graph replay"},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "eq_tokens_per_s": round(gbs * 1e9 / bpt, 1),
@@ -223,6 +231,15 @@ SWEEP_GROUPS = {
 }
 
 
+def _with_fmt(L, fmt):
+    import dataclasses
+    return dataclasses.replace(L, fmt=fmt)
+
+
+def w4_fmt(a) -> int:
+    return 5 if a.w4_zeros == "packed" else 4
+
+
 def sweep_workload(a, torch, timer):
     """One Llama-3-8B-shaped W4 decode step per graph replay, two ways:
     225 separate GEMVs, and 129 GEMVs with q|k|v and gate|up stacked along N
@@ -243,12 +260,13 @@ def sweep_workload(a, torch, timer):
         for g in groups:
             if g not in protos:
                 Ws = [synthetic.config3_layer(0, proj[n][0], proj[n][1], proj[n][2], n).W for n in g]
-                protos[g] = DeviceLayer(pack_host(4, np.concatenate(Ws, axis=0)), tiled=True)
+                protos[g] = DeviceLayer(pack_host(w4_fmt(a), np.concatenate(Ws, axis=0)), tiled=True)
     hL = synthetic.config3_layer(head[0], head[1], head[3], head[4], head[2])
-    head_layer = DeviceLayer(pack_host(4, hL.W), tiled=True)
+    head_layer = DeviceLayer(pack_host(w4_fmt(a), hL.W), tiled=True)
     torch.cuda.synchronize()
     steps = max(1, min(a.steps, 50))
-    out = {"workload": "w4_llama3_8b_decode_step", "steps": steps}
+    out = {"workload": "w4_llama3_8b_decode_step" + ("_w4p" if w4_fmt(a) == 5 else ""),
+           "steps": steps}
     for label, groups in SWEEP_GROUPS.items():
         layers = {g: [protos[g]] + [clone_layer(DeviceLayer, protos[g]) for _ in range(nlayers - 1)]
                   for g in groups}
@@ -301,7 +319,7 @@ def batched_workload(a, torch, timer):
     rows = []
     for (N, K) in ((14336, 4096), (4096, 14336)):
         Lb = synthetic.config4(16, N, K)
-        base = DeviceLayer(pack_host(4, Lb.W))
+        base = DeviceLayer(pack_host(w4_fmt(a), Lb.W))
         for M in (2, 4, 8, 16):
             nbytes = base.nbytes(M)
             layers = rotated(DeviceLayer, base, nbytes)
@@ -412,7 +430,10 @@ def main():
     if a.workload == "w2_14336":
         out = gemv_workload(a, torch, synthetic.config2(), "w2_14336x4096_outliers143_m1", timer)
     elif a.workload == "w4_4096":
-        out = gemv_workload(a, torch, synthetic.config1(), "w4_4096x4096_m1", timer)
+        L1 = synthetic.config1()
+        if a.w4_zeros == "packed":
+            L1 = _with_fmt(L1, 5)
+        out = gemv_workload(a, torch, L1, "w4_4096x4096_m1" + ("_w4p" if L1.fmt == 5 else ""), timer)
     elif a.workload == "sweep":
         out = sweep_workload(a, torch, timer)
     elif a.workload == "batched":
