@@ -23,7 +23,8 @@ Other workloads (--workload): w4_4096 (W4 4096x4096), sweep (Llama-3-8B-shaped
 decode in one graph -> tokens/s: 225 separate W4 GEMVs per token, and 129 with
 q|k|v and gate|up stacked along N), batched (W4 small-M
 matrix-core path vs M repeated GEMVs), w2_70b (W2 + outliers at 28672x8192 and
-8192x28672, M = 1 and 8), read / copy (plain streaming kernels: the attainable
+8192x28672, M = 1 and 8), embed (row gather from a 131072 x 4096 W4 table),
+read / copy (plain streaming kernels: the attainable
 HBM rate and the byte-counter calibration).
 """
 
@@ -52,7 +53,8 @@ def _parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="w2_14336",
-                   choices=["w2_14336", "w4_4096", "sweep", "batched", "w2_70b", "read", "copy"])
+                   choices=["w2_14336", "w4_4096", "sweep", "batched", "w2_70b", "embed", "read",
+                            "copy"])
     p.add_argument("--bytes", type=int, default=26157628,
                    help="bytes per launch of the read / copy workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -371,6 +373,38 @@ def w2_70b_workload(a, torch, timer):
     return rows
 
 
+def embed_workload(a, torch, timer):
+    """Embedding row gather (SPECTRA section 4.3) from a W4 (or W4P) table of
+    131072 x 4096 (the page's example vocabulary): n_ids uniformly drawn token
+    ids per launch, a fresh id set each launch (rotated), rows dequantized
+    straight into FP16 output rows.  Bytes = the gathered rows' codes, scales,
+    zeros and ids read plus the FP16 rows written."""
+    import synthetic
+    from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
+    V, K = 131072, 4096
+    fmt = w4_fmt(a)
+    W = synthetic.gaussian_weights(V, K, 0.02, 6, 0, fmt)
+    dl = DeviceLayer(pack_host(fmt, W))
+    del W
+    G = K // 32
+    zrow = (G + 1) // 2 if fmt == 5 else 2 * G
+    rows = []
+    for n_ids in (1, 64, 4096):
+        nsets = 64
+        rng = np.random.default_rng(n_ids)
+        ids = [torch.from_numpy(rng.integers(0, V, n_ids).astype(np.int32)).cuda()
+               for _ in range(nsets)]
+        outs = [torch.empty((n_ids, K), dtype=torch.int16, device="cuda") for _ in range(4)]
+        fn = lambda i: dl.embed(ids[i % nsets], outs[i % 4])  # noqa: E731
+        ms = timer(fn, a.steps // 4, a.warmup // 4)
+        nbytes = n_ids * (K // 2 + 2 * G + zrow + 4) + n_ids * K * 2
+        rows.append({"workload": f"embed_gather_{V}x{K}_w{'4p' if fmt == 5 else '4'}_ids{n_ids}",
+                     "bytes": nbytes, "us": round(ms * 1e3, 3),
+                     "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "pct_of_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)})
+    return rows
+
+
 def stream_workload(a, torch, timer, copy):
     import bit_weight_only_gemv_amd as B
     nb = (a.bytes + 15) // 16 * 16
@@ -440,6 +474,8 @@ def main():
         out = batched_workload(a, torch, timer)
     elif a.workload == "w2_70b":
         out = w2_70b_workload(a, torch, timer)
+    elif a.workload == "embed":
+        out = embed_workload(a, torch, timer)
     else:
         out = stream_workload(a, torch, timer, copy=(a.workload == "copy"))
     for o in (out if isinstance(out, list) else [out]):

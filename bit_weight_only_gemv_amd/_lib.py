@@ -55,6 +55,7 @@ SIGNATURES = {
     "wq_gemv_w4p": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _P, _P]),
     "wq_gemm_wq": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _I64, _P, _P]),
     "wq_outlier_add": (_INT, [_P, _P, _I64, _I64, _P, _I64, _I64, _P, _P]),
+    "wq_embed_gather": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _I64, _P, _P]),
     "wq_tiled_bytes": (_I64, [_INT, _I64, _I64, _I64]),
     "wq_tile_host": (_INT, [_INT, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64]),
     "wq_gemv_tiled": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
@@ -254,6 +255,12 @@ def wq_gemm_wq(fmt, codes, scales, zeros, N, K, X, M, Y, out_idx=None, out_w=Non
 def wq_gemv_tiled(fmt, tiled, N, K, x, y, out_idx=None, n_out=0, stream=None):
     _check(load().wq_gemv_tiled(fmt, _dptr(tiled), N, K, _dptr(out_idx) if n_out else None, n_out,
                                 _dptr(x), _dptr(y), _stream(stream)))
+
+
+def wq_embed_gather(fmt, codes, scales, zeros, V, K, ids, n_ids, out, stream=None):
+    _check(load().wq_embed_gather(fmt, _dptr(codes), _dptr(scales), _dptr(zeros), V, K,
+                                  _dptr(ids) if n_ids else None, n_ids,
+                                  _dptr(out) if n_ids else None, _stream(stream)))
 
 
 def wq_outlier_add(idx, out_w, n_out, N, X, M, K, Y, stream=None):

@@ -15,6 +15,66 @@ namespace wqd {
 // multiply-add rounds exactly once, like a multiply followed by an add.
 // FMT 5 (W4P) is W4 with the zero point read from its packed nibble.
 template <int FMT>
+__device__ __forceinline__ void dequant_group(const uint8_t* __restrict__ codes,
+                                              const uint16_t* __restrict__ scales,
+                                              const uint16_t* __restrict__ zeros, int64_t n,
+                                              int64_t g, int64_t K, uint16_t* __restrict__ dst_row) {
+  const int64_t G = K / kGroup;
+  const float s = h2f(scales[n * G + g]);
+  float z;
+  if constexpr (FMT == 5) {
+    const uint8_t* zp = reinterpret_cast<const uint8_t*>(zeros) + n * ((G + 1) / 2);
+    z = (float)((zp[g >> 1] >> (4 * (g & 1))) & 0x0Fu);
+  } else {
+    z = h2f(zeros[n * G + g]);
+  }
+  uint16_t w[32];
+  if constexpr (FMT == 4 || FMT == 5) {
+    const u4v c = *reinterpret_cast<const u4v*>(codes + n * (K / 2) + g * 16);
+    const uint32_t wv[4] = {c.x, c.y, c.z, c.w};
+    const float zlo = 1024.0f + z, zhi = 1024.0f + 16.0f * z;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t lo0, hi0, lo1, hi1;
+      w4_word_magic(wv[j], lo0, hi0, lo1, hi1);
+      const h2 a = as_h2(lo0), b = as_h2(hi0), c2 = as_h2(lo1), d = as_h2(hi1);
+      w[4 * j + 0] = f2h(((float)a[0] - zlo) * s);
+      w[4 * j + 2] = f2h(((float)a[1] - zlo) * s);
+      w[4 * j + 16] = f2h(((float)b[0] - zhi) * 0.0625f * s);
+      w[4 * j + 18] = f2h(((float)b[1] - zhi) * 0.0625f * s);
+      w[4 * j + 1] = f2h(((float)c2[0] - zlo) * s);
+      w[4 * j + 3] = f2h(((float)c2[1] - zlo) * s);
+      w[4 * j + 17] = f2h(((float)d[0] - zhi) * 0.0625f * s);
+      w[4 * j + 19] = f2h(((float)d[1] - zhi) * 0.0625f * s);
+    }
+  } else {
+    const u2 c = *reinterpret_cast<const u2*>(codes + n * (K / 4) + g * 8);
+    const uint32_t wv[2] = {c.x, c.y};
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const h2 cp = as_h2(w2_centroid_pair((wv[j] >> (2 * p + 8 * h)) & 0x00030003u));
+          const int k = 16 * j + 4 * h + p;
+          w[k] = f2h(__builtin_fmaf(s, (float)cp[0], z));
+          w[k + 8] = f2h(__builtin_fmaf(s, (float)cp[1], z));
+        }
+  }
+  u4v* dst = reinterpret_cast<u4v*>(dst_row + g * 32);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    u4v t;
+    t.x = pack2(w[8 * v + 0], w[8 * v + 1]);
+    t.y = pack2(w[8 * v + 2], w[8 * v + 3]);
+    t.z = pack2(w[8 * v + 4], w[8 * v + 5]);
+    t.w = pack2(w[8 * v + 6], w[8 * v + 7]);
+    dst[v] = t;
+  }
+}
+
+template <int FMT>
 __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint16_t* __restrict__ scales,
                                                       const uint16_t* __restrict__ zeros, int64_t N,
@@ -24,57 +84,34 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict_
   for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items;
        it += (int64_t)gridDim.x * blockDim.x) {
     const int64_t n = it / G, g = it % G;
-    const float s = h2f(scales[it]);
-    float z;
-    if constexpr (FMT == 5) {
-      const uint8_t* zp = reinterpret_cast<const uint8_t*>(zeros) + n * ((G + 1) / 2);
-      z = (float)((zp[g >> 1] >> (4 * (g & 1))) & 0x0Fu);
+    dequant_group<FMT>(codes, scales, zeros, n, g, K, out + n * K);
+  }
+}
+
+// --------------------------------------------------- embedding row gather
+// SPECTRA section 4.3: only the rows of the token ids in the batch are read
+// and dequantized, straight into the FP16 output rows; the same per-group
+// arithmetic as the dequantization above, so the rows are bit-identical to
+// it.  One thread per (token, group); an id outside [0, V) gives a zero row.
+template <int FMT>
+__global__ void __launch_bounds__(256) embed_kernel(const uint8_t* __restrict__ codes,
+                                                    const uint16_t* __restrict__ scales,
+                                                    const uint16_t* __restrict__ zeros, int64_t V,
+                                                    int64_t K, const int32_t* __restrict__ ids,
+                                                    int64_t n_ids, uint16_t* __restrict__ out) {
+  const int64_t G = K / kGroup;
+  const int64_t items = n_ids * G;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items;
+       it += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = it / G, g = it % G;
+    const int64_t n = ids[t];
+    uint16_t* row = out + t * K;
+    if (n >= 0 && n < V) {
+      dequant_group<FMT>(codes, scales, zeros, n, g, K, row);
     } else {
-      z = h2f(zeros[it]);
-    }
-    uint16_t w[32];
-    if constexpr (FMT == 4 || FMT == 5) {
-      const u4v c = *reinterpret_cast<const u4v*>(codes + n * (K / 2) + g * 16);
-      const uint32_t wv[4] = {c.x, c.y, c.z, c.w};
-      const float zlo = 1024.0f + z, zhi = 1024.0f + 16.0f * z;
+      u4v* dst = reinterpret_cast<u4v*>(row + g * 32);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t lo0, hi0, lo1, hi1;
-        w4_word_magic(wv[j], lo0, hi0, lo1, hi1);
-        const h2 a = as_h2(lo0), b = as_h2(hi0), c2 = as_h2(lo1), d = as_h2(hi1);
-        w[4 * j + 0] = f2h(((float)a[0] - zlo) * s);
-        w[4 * j + 2] = f2h(((float)a[1] - zlo) * s);
-        w[4 * j + 16] = f2h(((float)b[0] - zhi) * 0.0625f * s);
-        w[4 * j + 18] = f2h(((float)b[1] - zhi) * 0.0625f * s);
-        w[4 * j + 1] = f2h(((float)c2[0] - zlo) * s);
-        w[4 * j + 3] = f2h(((float)c2[1] - zlo) * s);
-        w[4 * j + 17] = f2h(((float)d[0] - zhi) * 0.0625f * s);
-        w[4 * j + 19] = f2h(((float)d[1] - zhi) * 0.0625f * s);
-      }
-    } else {
-      const u2 c = *reinterpret_cast<const u2*>(codes + n * (K / 4) + g * 8);
-      const uint32_t wv[2] = {c.x, c.y};
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const h2 cp = as_h2(w2_centroid_pair((wv[j] >> (2 * p + 8 * h)) & 0x00030003u));
-            const int k = 16 * j + 4 * h + p;
-            w[k] = f2h(__builtin_fmaf(s, (float)cp[0], z));
-            w[k + 8] = f2h(__builtin_fmaf(s, (float)cp[1], z));
-          }
-    }
-    u4v* dst = reinterpret_cast<u4v*>(out + n * K + g * 32);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      u4v t;
-      t.x = pack2(w[8 * v + 0], w[8 * v + 1]);
-      t.y = pack2(w[8 * v + 2], w[8 * v + 3]);
-      t.z = pack2(w[8 * v + 4], w[8 * v + 5]);
-      t.w = pack2(w[8 * v + 6], w[8 * v + 7]);
-      dst[v] = t;
+      for (int v = 0; v < 4; ++v) dst[v] = (u4v){0u, 0u, 0u, 0u};
     }
   }
 }
@@ -183,6 +220,36 @@ extern "C" int wq_dequant_device(int fmt, const uint8_t* codes, const uint16_t* 
   else
     hipLaunchKernelGGL(dequant_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales,
                        zeros, N, K, W_hat);
+  return check_launch(who);
+}
+
+extern "C" int wq_embed_gather(int fmt, const uint8_t* codes, const uint16_t* scales,
+                               const uint16_t* zeros, int64_t V, int64_t K, const int32_t* ids,
+                               int64_t n_ids, uint16_t* out, void* stream) {
+  const char* who = "wq_embed_gather";
+  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2 && fmt != WQ_FMT_W4P)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2", who);
+  if (int r = wq::check_shape(V, K, who)) return r;
+  if (n_ids < 0 || n_ids > ((int64_t)1 << 31))
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: n_ids must be in [0, 2^31]", who);
+  if (n_ids == 0) return wq::ok();
+  if (!codes || !scales || !zeros || !ids || !out)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (!aligned16(codes) || !aligned16(out))
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: device pointers must be 16-byte aligned", who);
+  const int64_t items = n_ids * (K / kGroup);
+  int64_t blocks = (items + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipStream_t s = (hipStream_t)stream;
+  if (fmt == WQ_FMT_W4)
+    hipLaunchKernelGGL(embed_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales,
+                       zeros, V, K, ids, n_ids, out);
+  else if (fmt == WQ_FMT_W4P)
+    hipLaunchKernelGGL(embed_kernel<5>, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales,
+                       zeros, V, K, ids, n_ids, out);
+  else
+    hipLaunchKernelGGL(embed_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales,
+                       zeros, V, K, ids, n_ids, out);
   return check_launch(who);
 }
 

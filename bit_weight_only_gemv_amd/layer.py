@@ -110,6 +110,11 @@ class DeviceLayer:
     def outlier_add(self, X, Y, stream=None):
         L.wq_outlier_add(self.idx, self.wout, self.n_out, self.N, X, X.shape[0], self.K, Y, stream)
 
+    def embed(self, ids, out, stream=None):
+        """Rows ids of the dequantized table into out (FP16 [len(ids), K])."""
+        L.wq_embed_gather(self.fmt, self.codes, self.scales, self.zeros, self.N, self.K, ids,
+                          ids.numel(), out, stream)
+
     def dequant(self, W_hat, stream=None):
         L.wq_dequant_device(self.fmt, self.codes, self.scales, self.zeros, self.N, self.K, W_hat,
                             stream)

@@ -186,6 +186,15 @@ int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales, const uint
                int64_t n_out, uint32_t flags, const uint16_t* X, int64_t M, uint16_t* Y,
                void* stream);
 
+/* Embedding row gather (SPECTRA section 4.3): out[t][k] = w_hat[ids[t]][k] for
+ * t < n_ids, FP16 [n_ids][K], bit-identical to wq_dequant_device of those rows
+ * (W4 / W4P / W2 table [V][K] in the layouts above; ids int32 on the device).
+ * Only the rows named by ids are read.  An id outside [0, V) yields a row of
+ * zeros (the ids are not checked on the host).  n_ids == 0 does nothing. */
+int wq_embed_gather(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                    int64_t V, int64_t K, const int32_t* ids, int64_t n_ids, uint16_t* out,
+                    void* stream);
+
 /* Standalone outlier correction (the add of SPECTRA section 4.1's outlier loop;
  * the same arithmetic as the column refinement add of the StrataFlux page,
  * section 3.2.1 Eq. 2, for a static column set):

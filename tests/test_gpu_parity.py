@@ -298,3 +298,28 @@ def test_full_w4_batched(N, K, M):
     for m in range(M):
         y, _ = run_gemv(dl, L.x[m])
         check_product(ref, y, L.x[m:m + 1], f"W4 {N}x{K} gemv row {m}")
+
+
+# ------------------------------------------------------ embedding row gather
+
+
+@pytest.mark.parametrize("fmt", [4, 2, 5])
+@pytest.mark.parametrize("V,K", [(1000, 4096), (77, 96), (300, 2080)])
+def test_embed_gather_bit_exact(fmt, V, K):
+    say(f"embed gather fmt={fmt} V={V} K={K}")
+    W = synthetic.gaussian_weights(V, K, 0.02, 310, V, K)
+    ref, dl = build(fmt, W)
+    w_hat = ref.w_hat()
+    rng = np.random.default_rng(V + K + fmt)
+    ids = np.concatenate([[0, V - 1, 5, 5], rng.integers(0, V, 200), [-1, V, 2**31 - 1]])
+    ids = ids.astype(np.int32)
+    idd = torch.from_numpy(ids).cuda()
+    out = torch.full((len(ids), K), -1, dtype=torch.int16, device="cuda")
+    dl.embed(idd, out)
+    torch.cuda.synchronize()
+    got = _bits(host_fp16(out))
+    valid = (ids >= 0) & (ids < V)
+    assert np.array_equal(got[valid], _bits(w_hat[ids[valid]]))
+    assert np.all(got[~valid] == 0)
+    # an empty batch is a no-op
+    dl.embed(idd[:0], out[:0])

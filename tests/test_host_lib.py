@@ -149,6 +149,11 @@ def test_error_codes():
     assert lib.wq_gemm_wq(3, fake, fake, fake, 8, 64, None, None, 0, 1, fake, 2, fake, None) == -1
     assert lib.wq_gemv_w4(fake, fake, fake, 8, 65536 + 32, None, None, 0, 1, fake, fake, None) == -2
     assert lib.wq_read_probe(fake, 15, fake, None) == -1
+    assert lib.wq_embed_gather(3, fake, fake, fake, 8, 64, fake, 1, fake, None) == -1
+    assert lib.wq_embed_gather(4, fake, fake, fake, 8, 40, fake, 1, fake, None) == -2
+    assert lib.wq_embed_gather(4, fake, fake, fake, 8, 64, fake, -1, fake, None) == -1
+    assert lib.wq_embed_gather(4, fake, fake, fake, 8, 64, None, 0, None, None) == 0
+    assert lib.wq_embed_gather(4, fake, fake, fake, 8, 64, None, 2, fake, None) == -1
 
 
 # ------------------------------------------------- W4P packed zero points
