@@ -16,6 +16,8 @@ from .wq_oracle import (  # noqa: F401
     quantize_w4, pack_w4, unpack_w4, dequant_w4, pack_zeros_w4, unpack_zeros_w4,
     quantize_w2, pack_w2, unpack_w2, dequant_w2,
     outlier_count, outlier_scores, select_outliers, split_outliers,
+    channel_saliency, saliency_kurtosis, kurtosis_ratio, select_outliers_kurtosis,
+    KURT_R_BASE, KURT_R_MIN, KURT_R_MAX,
     QuantLayer, quantize_layer, background_mask, matvec_ref,
     TOL_REL, TOL_ABS, check_tolerance, fidelity,
 )

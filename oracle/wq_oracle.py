@@ -250,6 +250,60 @@ def select_outliers(W: np.ndarray, profile: np.ndarray, ratio: float) -> np.ndar
     return np.sort(order[:n]).astype(np.int32)
 
 
+# ------------------------------------------ kurtosis-adaptive outlier policy
+
+KURT_R_BASE = 0.01      # [SPECTRA] 3.3: r stays 0.01 for mesokurtic saliencies
+KURT_R_MIN = 0.005      # [SPECTRA] 3.3: clamp(..., 0.005, 0.03)
+KURT_R_MAX = 0.03
+KURT_SLOPE = 0.15       # [SPECTRA] 3.3: r_base (1 + 0.15 ln(1 + kappa_excess))
+
+
+def channel_saliency(W: np.ndarray, gamma=None) -> np.ndarray:
+    """[SPECTRA] 3.1-3.2: S_j = |gamma_j| ||W[:, j]||_2 (float64, the column norm
+    summed over rows in order).  Without a preceding normalization gain the page
+    sets gamma_j = 1, the plain column norm."""
+    K = W.shape[1]
+    g = np.ones(K) if gamma is None else np.abs(np.asarray(gamma, dtype=np.float64))
+    return outlier_scores(W, g)
+
+
+def saliency_kurtosis(S: np.ndarray) -> float:
+    """Population kurtosis of the saliencies ([SPECTRA] 3.3, Appendix A Prop. 1):
+    mu = (1/K) sum S, sigma^2 = (1/K) sum (S - mu)^2, z = (S - mu) / sigma,
+    kappa = (1/K) sum z^4, every sum left to right in float64.  A constant
+    vector has no spread; its kappa is taken as 0 (reading)."""
+    S = np.asarray(S, dtype=np.float64)
+    K = S.size
+    mu = float(_seqsum(S)) / K
+    d = S - mu
+    var = float(_seqsum(d * d)) / K
+    if var == 0.0:
+        return 0.0
+    z = d / np.sqrt(var)
+    z2 = z * z
+    return float(_seqsum(z2 * z2)) / K
+
+
+def kurtosis_ratio(kappa: float, r_base: float = KURT_R_BASE) -> float:
+    """[SPECTRA] 3.3: r = clamp(r_base (1 + 0.15 ln(1 + max(0, kappa - 3))), 0.005, 0.03)."""
+    ex = max(0.0, kappa - 3.0)
+    r = r_base * (1.0 + KURT_SLOPE * float(np.log1p(ex)))
+    return min(max(r, KURT_R_MIN), KURT_R_MAX)
+
+
+def select_outliers_kurtosis(W: np.ndarray, gamma=None, r_base: float = KURT_R_BASE):
+    """The kurtosis-adaptive outlier policy of [SPECTRA] 3.1-3.3: saliencies,
+    their kurtosis, the ratio r, then the floor(r K) most salient columns (ties
+    to the lower index), ascending int32.  Returns (idx, r, kappa)."""
+    K = W.shape[1]
+    S = channel_saliency(W, gamma)
+    kappa = saliency_kurtosis(S)
+    r = kurtosis_ratio(kappa, r_base)
+    n = outlier_count(K, r)
+    order = np.lexsort((np.arange(K), -S))
+    return np.sort(order[:n]).astype(np.int32), r, kappa
+
+
 def split_outliers(W: np.ndarray, idx: np.ndarray):
     """Dense residual with the outlier columns zeroed, and the outlier columns
     kept in FP16 as a row-major [N, n_out] slab ([SPECTRA] 3.4 first sentence,
