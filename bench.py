@@ -24,6 +24,7 @@ decode in one graph -> tokens/s: 225 separate W4 GEMVs per token, and 129 with
 q|k|v and gate|up stacked along N), batched (W4 small-M
 matrix-core path vs M repeated GEMVs), w2_70b (W2 + outliers at 28672x8192 and
 8192x28672, M = 1 and 8), embed (row gather from a 131072 x 4096 W4 table),
+kurtosis (the kurtosis-adaptive outlier policy on the W2 layers),
 read / copy (plain streaming kernels: the attainable
 HBM rate and the byte-counter calibration).
 """
@@ -53,8 +54,8 @@ def _parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="w2_14336",
-                   choices=["w2_14336", "w4_4096", "sweep", "batched", "w2_70b", "embed", "read",
-                            "copy"])
+                   choices=["w2_14336", "w4_4096", "sweep", "batched", "w2_70b", "embed",
+                            "kurtosis", "read", "copy"])
     p.add_argument("--bytes", type=int, default=26157628,
                    help="bytes per launch of the read / copy workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -405,6 +406,40 @@ def embed_workload(a, torch, timer):
     return rows
 
 
+def kurtosis_workload(a, torch, timer):
+    """The kurtosis-adaptive outlier policy (SPECTRA sections 3.1-3.3) on the W2
+    layers of the other workloads: kappa, the ratio and n_out it picks (host
+    time), and the tiled W2 GEMV with those outliers next to the profile-guided
+    3.5% of the default workloads."""
+    import synthetic
+    from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
+    import bit_weight_only_gemv_amd as B
+    rows = []
+    for label, L in (("w2_14336x4096", synthetic.config2()),
+                     ("w2_28672x8192", synthetic.config5(28672, 8192, 1))):
+        t0 = time.time()
+        idx, r, kappa = B.wq_select_outliers_kurtosis(L.W)
+        t_sel = time.time() - t0
+        row = {"workload": f"kurtosis_policy_{label}", "kappa": round(kappa, 4), "ratio": round(r, 5),
+               "n_out": int(len(idx)), "host_select_s": round(t_sel, 3)}
+        for pol in ("kurtosis", "profile_3.5pct"):
+            hl = pack_host(2, L.W, kurtosis=True) if pol == "kurtosis" else \
+                pack_host(2, L.W, L.profile, L.ratio)
+            base = DeviceLayer(hl, tiled=True)
+            nbytes = base.nbytes(1)
+            layers = rotated(DeviceLayer, base, nbytes)
+            nc = len(layers)
+            x = torch.from_numpy(L.x[:1].reshape(-1).view(np.int16)).cuda()
+            ys = [torch.empty(base.N, dtype=torch.int16, device="cuda") for _ in range(nc)]
+            ms = timer(lambda i: layers[i % nc].gemv_tiled(x, ys[i % nc]), a.steps // 4,
+                       a.warmup // 4)
+            row[pol] = {"n_out": base.n_out, "bytes": nbytes, "us": round(ms * 1e3, 3),
+                        "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            del layers
+        rows.append(row)
+    return rows
+
+
 def stream_workload(a, torch, timer, copy):
     import bit_weight_only_gemv_amd as B
     nb = (a.bytes + 15) // 16 * 16
@@ -476,6 +511,8 @@ def main():
         out = w2_70b_workload(a, torch, timer)
     elif a.workload == "embed":
         out = embed_workload(a, torch, timer)
+    elif a.workload == "kurtosis":
+        out = kurtosis_workload(a, torch, timer)
     else:
         out = stream_workload(a, torch, timer, copy=(a.workload == "copy"))
     for o in (out if isinstance(out, list) else [out]):

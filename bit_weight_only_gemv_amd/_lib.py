@@ -47,6 +47,8 @@ SIGNATURES = {
     "wq_quantize_w2": (_INT, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "wq_pack_zeros_w4": (_INT, [_P, _I64, _I64, _P]),
     "wq_select_outliers": (_INT, [_P, _I64, _I64, _P, ctypes.c_double, _P, _I64, _P]),
+    "wq_select_outliers_kurtosis": (_INT, [_P, _I64, _I64, _P, ctypes.c_double, _P, _I64, _P,
+                                           _P, _P]),
     "wq_split_outliers": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P]),
     "wq_dequant_host": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P]),
     "wq_dequant_device": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _P]),
@@ -150,6 +152,23 @@ def wq_select_outliers(W: np.ndarray, profile: np.ndarray, ratio: float) -> np.n
     _check(load().wq_select_outliers(_np_ptr(W), N, K, _np_ptr(prof), float(ratio), _np_ptr(idx),
                                      cap, ctypes.byref(n)))
     return idx[: n.value].copy()
+
+
+def wq_select_outliers_kurtosis(W: np.ndarray, gamma: Optional[np.ndarray] = None,
+                                r_base: float = 0.01):
+    """Kurtosis-adaptive selection -> (idx int32 ascending, ratio r, kurtosis)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    g = _c(gamma, np.float64) if gamma is not None else None
+    cap = max(1, int(np.floor(0.03 * K)) + 1)
+    idx = np.empty(cap, np.int32)
+    n = ctypes.c_int64(0)
+    r = ctypes.c_double(0.0)
+    k = ctypes.c_double(0.0)
+    _check(load().wq_select_outliers_kurtosis(_np_ptr(W), N, K, _np_ptr(g) if g is not None else None,
+                                              float(r_base), _np_ptr(idx), cap, ctypes.byref(n),
+                                              ctypes.byref(r), ctypes.byref(k)))
+    return idx[: n.value].copy(), r.value, k.value
 
 
 def wq_split_outliers(W: np.ndarray, idx: np.ndarray):

@@ -281,6 +281,64 @@ int wq_select_outliers(const float* W, int64_t N, int64_t K, const double* profi
   return wq::ok();
 }
 
+int wq_select_outliers_kurtosis(const float* W, int64_t N, int64_t K, const double* gamma,
+                                double r_base, int32_t* idx, int64_t idx_cap, int64_t* n_out,
+                                double* ratio, double* kappa) {
+  const char* who = "wq_select_outliers_kurtosis";
+  if (int r = wq::check_shape(N, K, who)) return r;
+  if (!W || !n_out) return fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (!(r_base > 0.0 && r_base <= 1.0))
+    return fail(WQ_ERR_INVALID_ARG, "%s: r_base must be in (0, 1]", who);
+  // saliency S_c = |gamma_c| ||W[:, c]||_2, the column norm summed over rows in order
+  std::vector<double> acc((size_t)K, 0.0);
+  for (int64_t r = 0; r < N; ++r) {
+    const float* row = W + r * K;
+    for (int64_t c = 0; c < K; ++c) {
+      const double v = (double)row[c];
+      acc[c] = acc[c] + v * v;
+    }
+  }
+  std::vector<double> S((size_t)K);
+  for (int64_t c = 0; c < K; ++c) S[c] = std::sqrt(acc[c]) * (gamma ? std::fabs(gamma[c]) : 1.0);
+  // population kurtosis, every sum left to right; no spread -> 0
+  double sum = 0.0;
+  for (int64_t c = 0; c < K; ++c) sum = sum + S[c];
+  const double mu = sum / (double)K;
+  double var = 0.0;
+  for (int64_t c = 0; c < K; ++c) {
+    const double d = S[c] - mu;
+    var = var + d * d;
+  }
+  var = var / (double)K;
+  double kap = 0.0;
+  if (var != 0.0) {
+    const double sd = std::sqrt(var);
+    double m4 = 0.0;
+    for (int64_t c = 0; c < K; ++c) {
+      const double z = (S[c] - mu) / sd;
+      const double z2 = z * z;
+      m4 = m4 + z2 * z2;
+    }
+    kap = m4 / (double)K;
+  }
+  const double ex = kap - 3.0 > 0.0 ? kap - 3.0 : 0.0;
+  double rr = r_base * (1.0 + 0.15 * std::log1p(ex));
+  rr = std::min(std::max(rr, 0.005), 0.03);
+  const int64_t n = (int64_t)std::floor(rr * (double)K);
+  if (n > idx_cap || (n > 0 && !idx))
+    return fail(WQ_ERR_INVALID_ARG, "%s: idx holds %lld entries, %lld needed", who,
+                (long long)idx_cap, (long long)n);
+  std::vector<int32_t> order((size_t)K);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return S[a] > S[b]; });
+  std::sort(order.begin(), order.begin() + n);
+  for (int64_t j = 0; j < n; ++j) idx[j] = order[j];
+  *n_out = n;
+  if (ratio) *ratio = rr;
+  if (kappa) *kappa = kap;
+  return wq::ok();
+}
+
 int wq_pack_zeros_w4(const uint16_t* zeros, int64_t N, int64_t K, uint8_t* zeros_packed) {
   if (int r = wq::check_shape(N, K, "wq_pack_zeros_w4")) return r;
   if (!zeros || !zeros_packed) return fail(WQ_ERR_INVALID_ARG, "wq_pack_zeros_w4: NULL pointer");

@@ -34,10 +34,16 @@ class HostLayer:
 
 
 def pack_host(fmt: int, W: np.ndarray, profile: Optional[np.ndarray] = None,
-              ratio: float = 0.0) -> HostLayer:
+              ratio: float = 0.0, *, kurtosis_gamma: Optional[np.ndarray] = None,
+              kurtosis: bool = False) -> HostLayer:
+    """Outlier selection, split, quantization and packing.  Outliers come from
+    the profile-guided rule (profile, ratio), or with kurtosis=True from the
+    kurtosis-adaptive rule (optional normalization gains kurtosis_gamma)."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     N, K = W.shape
-    if profile is not None and ratio > 0:
+    if kurtosis:
+        idx, _, _ = L.wq_select_outliers_kurtosis(W, kurtosis_gamma)
+    elif profile is not None and ratio > 0:
         idx = L.wq_select_outliers(W, profile, ratio)
     else:
         idx = np.zeros(0, np.int32)

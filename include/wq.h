@@ -126,6 +126,24 @@ int wq_pack_zeros_w4(const uint16_t* zeros, int64_t N, int64_t K, uint8_t* zeros
 int wq_select_outliers(const float* W, int64_t N, int64_t K, const double* profile,
                        double ratio, int32_t* idx, int64_t idx_cap, int64_t* n_out);
 
+/* Kurtosis-adaptive outlier selection (SPECTRA sections 3.1-3.3), a host
+ * policy that picks n_out itself:
+ *   saliency S_c = |gamma_c| * sqrt(sum_n W[n][c]^2)  (float64, rows in order;
+ *                  gamma NULL means gamma_c = 1, the page's fallback for
+ *                  projections with no preceding normalization gain);
+ *   kappa = population kurtosis of S (mean, variance and fourth moment summed
+ *           left to right; 0 when all S are equal);
+ *   r = clamp(r_base * (1 + 0.15 * log1p(max(0, kappa - 3))), 0.005, 0.03);
+ *   n_out = floor(r * K) columns of highest S (ties to the lower index), written
+ *           ascending to idx.
+ * r_base is 0.01 on the page.  idx_cap >= floor(0.03 K) always suffices.
+ * *ratio and *kappa receive r and kappa (either may be NULL).
+ * Errors: WQ_ERR_INVALID_ARG for NULL W / n_out, r_base outside (0, 1], or a
+ * short idx. */
+int wq_select_outliers_kurtosis(const float* W, int64_t N, int64_t K, const double* gamma,
+                                double r_base, int32_t* idx, int64_t idx_cap, int64_t* n_out,
+                                double* ratio, double* kappa);
+
 /* Outlier split (SPECTRA section 3.4 "dense residual"; section 3.6 payload):
  * W_dense = W with columns idx[] set to 0 (W_dense may alias W), and
  * W_out[n][j] = FP16(W[n][idx[j]]) (round to nearest even).

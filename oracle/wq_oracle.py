@@ -340,12 +340,16 @@ class QuantLayer:
         return dequant_w2(self.q, self.scale, self.zero)
 
 
-def quantize_layer(fmt: int, W: np.ndarray, profile=None, ratio: float = 0.0) -> QuantLayer:
-    """Outlier split (if a profile is given) followed by W4 or W2 quantization
-    of the dense residual and packing."""
+def quantize_layer(fmt: int, W: np.ndarray, profile=None, ratio: float = 0.0,
+                   idx=None) -> QuantLayer:
+    """Outlier split (columns ``idx`` if given, else from the profile rule)
+    followed by W4 or W2 quantization of the dense residual and packing."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     N, K = W.shape
-    if profile is not None and outlier_count(K, ratio) > 0:
+    if idx is not None and len(idx) > 0:
+        idx = np.asarray(idx, dtype=np.int32)
+        dense, wout = split_outliers(W, idx)
+    elif profile is not None and outlier_count(K, ratio) > 0:
         idx = select_outliers(W, profile, ratio)
         dense, wout = split_outliers(W, idx)
     else:

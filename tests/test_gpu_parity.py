@@ -323,3 +323,25 @@ def test_embed_gather_bit_exact(fmt, V, K):
     assert np.all(got[~valid] == 0)
     # an empty batch is a no-op
     dl.embed(idd[:0], out[:0])
+
+
+# --------------------------------------- kurtosis-adaptive outlier policy
+
+
+@pytest.mark.parametrize("fmt", [2, 4])
+def test_gemv_kurtosis_policy_layer(fmt):
+    say(f"gemv with kurtosis-selected outliers fmt={fmt}")
+    rng = np.random.default_rng(12)
+    N, K = 700, 4096
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    W[:, rng.choice(K, 60, replace=False)] *= 20.0      # leptokurtic column norms
+    idx, r, kappa = O.select_outliers_kurtosis(W)
+    assert r > 0.01 and len(idx) == int(np.floor(r * K))
+    ref = O.quantize_layer(fmt, W, idx=idx)
+    hl = pack_host(fmt, W, kurtosis=True)
+    assert np.array_equal(hl.idx, ref.idx) and np.array_equal(hl.codes, ref.codes)
+    dl = DeviceLayer(hl, tiled=True)
+    x = synthetic.gaussian_x_fp16(1, K, 12, 0, fmt)
+    y, _ = run_gemv(dl, x)
+    check_product(ref, y, x, f"kurtosis policy w{fmt} n_out={ref.n_out} (row-major)")
+    check_product(ref, run_gemv_tiled(dl, x), x, f"kurtosis policy w{fmt} (tiled)")

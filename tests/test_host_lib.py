@@ -183,3 +183,51 @@ def test_packed_zeros_reject_non_integer():
     with pytest.raises(B.WQError):
         B.wq_pack_zeros_w4(np.array([[16.0, 0.0]], np.float16), 1, 64)
     assert B.wq_pack_zeros_w4(np.array([[15.0, 0.0]], np.float16), 1, 64).tolist() == [[15]]
+
+
+# ------------------------------------------ kurtosis-adaptive outlier policy
+
+
+@pytest.mark.parametrize("case", ["gaussian", "heavy", "gamma", "tiny", "constant"])
+def test_kurtosis_policy_matches_oracle(case):
+    rng = np.random.default_rng(11)
+    N, K = 48, 2048
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    gamma = None
+    if case == "heavy":
+        W[:, rng.choice(K, 30, replace=False)] *= 25.0
+    elif case == "gamma":
+        gamma = np.abs(rng.standard_normal(K)) + 0.1
+        gamma[rng.choice(K, 8, replace=False)] = 60.0
+    elif case == "tiny":
+        W = W[:3, :64].copy()
+    elif case == "constant":
+        W = np.ones((5, 256), np.float32)    # equal saliencies: kappa 0, r = r_base
+    idx, r, kappa = B.wq_select_outliers_kurtosis(W, gamma)
+    ridx, rr, rk = O.select_outliers_kurtosis(W, gamma)
+    assert np.array_equal(idx, ridx)
+    assert r == rr and kappa == rk        # the same float64 operations in the same order
+    # and a layer packed with it equals the oracle's layer with those columns
+    from bit_weight_only_gemv_amd.layer import pack_host
+    lib = pack_host(2, W, kurtosis=True, kurtosis_gamma=gamma)
+    ref = O.quantize_layer(2, W, idx=ridx)
+    assert np.array_equal(lib.idx, ref.idx) and np.array_equal(lib.codes, ref.codes)
+    assert np.array_equal(_bits(lib.wout), _bits(ref.wout))
+
+
+def test_kurtosis_policy_errors():
+    W = np.zeros((4, 64), np.float32)
+    with pytest.raises(B.WQError):
+        B.wq_select_outliers_kurtosis(W, None, r_base=0.0)
+    lib = B.load()
+    n = ctypes.c_int64(0)
+    p = W.ctypes.data_as(ctypes.c_void_p)
+    assert lib.wq_select_outliers_kurtosis(None, 4, 64, None, 0.01, None, 0, ctypes.byref(n),
+                                           None, None) == -1
+    # a capacity below floor(r K) is rejected (r >= 0.01 -> at least 10 of 1024 columns)
+    W2 = np.random.default_rng(0).standard_normal((4, 1024)).astype(np.float32)
+    idx = np.zeros(4, np.int32)
+    assert lib.wq_select_outliers_kurtosis(W2.ctypes.data_as(ctypes.c_void_p), 4, 1024, None,
+                                           0.01, idx.ctypes.data_as(ctypes.c_void_p), 4,
+                                           ctypes.byref(n), None, None) == -1
+    assert p is not None
