@@ -19,5 +19,6 @@ from .wq_oracle import (  # noqa: F401
     channel_saliency, saliency_kurtosis, kurtosis_ratio, select_outliers_kurtosis,
     KURT_R_BASE, KURT_R_MIN, KURT_R_MAX,
     QuantLayer, quantize_layer, background_mask, matvec_ref,
+    REFINE_CHUNK, topk_chunks, refinement_w4, refine_ref,
     TOL_REL, TOL_ABS, check_tolerance, fidelity,
 )

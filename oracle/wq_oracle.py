@@ -401,6 +401,51 @@ def matvec_ref(w_hat: np.ndarray, x: np.ndarray, idx=None, wout=None):
     return y, a
 
 
+# ------------------------------------------------ runtime top-k refinement
+
+REFINE_CHUNK = 1024     # [StrataFlux] 3.2.1: input channels in chunks of 1,024
+
+
+def topk_chunks(x: np.ndarray, k: int, chunk: int = REFINE_CHUNK) -> np.ndarray:
+    """S(x) of [StrataFlux] 3.2.1 "Channel selection": the input channels cut
+    into chunks of ``chunk``, and in each chunk the k channels of largest |x_i|
+    (all of a chunk shorter than k).  Readings: |x| of the FP16 value, ties go to
+    the lower index, each chunk's picks are listed in ascending order, chunks in
+    order."""
+    x = np.asarray(x, dtype=np.float16).reshape(-1)
+    K = x.size
+    mag = np.abs(x.astype(np.float64))
+    out = []
+    for c0 in range(0, K, chunk):
+        m = mag[c0:c0 + chunk]
+        order = np.lexsort((np.arange(m.size), -m))
+        out.append(np.sort(order[:min(k, m.size)]) + c0)
+    return np.concatenate(out).astype(np.int32) if out else np.zeros(0, np.int32)
+
+
+def refinement_w4(W: np.ndarray, w_hat: np.ndarray):
+    """Refinement columns: the residual R = W - w_hat of the resident layer,
+    stored per input channel (R transposed, [K, N]) in the W4 format along N
+    ([StrataFlux] 3.2.1: refinement values as integers with their own scale
+    factors; DecDEC's 4-bit encoding of the weight residual).  Returns the W4
+    quantization of R^T: (q, scale, zero) with groups of 32 output rows."""
+    R = np.asarray(W, dtype=np.float32) - np.asarray(w_hat, dtype=np.float16).astype(np.float32)
+    q, sc, ze, _ = quantize_w4(np.ascontiguousarray(R.T))
+    return q, sc, ze
+
+
+def refine_ref(y0: np.ndarray, x: np.ndarray, sel: np.ndarray, c_hat: np.ndarray):
+    """[StrataFlux] Eq. 2: y' = y0 + sum_{i in S(x)} x_i C[:, i] in float64, with
+    C^T = ``c_hat`` [K, N] the dequantized refinement.  Returns (y', abs_sum)
+    with abs_sum = |y0| + sum |x_i C[:, i]| (the scale of the acceptance bound)."""
+    x64 = np.asarray(x, dtype=np.float16).astype(np.float64).reshape(-1)
+    C = np.asarray(c_hat, dtype=np.float16).astype(np.float64)
+    y0 = np.asarray(y0, dtype=np.float16).astype(np.float64)
+    sel = np.asarray(sel, dtype=np.int64)
+    terms = x64[sel][:, None] * C[sel]
+    return y0 + terms.sum(axis=0), np.abs(y0) + np.abs(terms).sum(axis=0)
+
+
 # Acceptance bound per output element: |y_gpu - y_ref| <= REL * sum|w x| + ABS.
 TOL_REL = 2e-3
 TOL_ABS = 1e-5
