@@ -55,7 +55,7 @@ def _parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="w2_14336",
                    choices=["w2_14336", "w4_4096", "sweep", "batched", "w2_70b", "embed",
-                            "kurtosis", "read", "copy"])
+                            "kurtosis", "refine", "read", "copy"])
     p.add_argument("--bytes", type=int, default=26157628,
                    help="bytes per launch of the read / copy workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -440,6 +440,65 @@ def kurtosis_workload(a, torch, timer):
     return rows
 
 
+def refine_workload(a, torch, timer):
+    """Runtime top-k refinement (StrataFlux section 3.2.1, Eq. 2) after the tiled
+    GEMV: per 1024-channel chunk the k = 32 largest |x_i| are selected on the GPU
+    and their 4-bit residual columns added to y.  Each launch times the
+    selection, the add, the GEMV, and the three in sequence; the layer and its
+    refinement columns are rotated like the GEMV's.  Refinement bytes = the
+    selected columns' codes, scales and zeros, the indices and x entries read,
+    and y read and written."""
+    import synthetic
+    import bit_weight_only_gemv_amd as B
+    from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host, refinement_host
+    rows = []
+    k, chunk = 32, 1024
+    for label, L in (("w2_14336x4096_outliers143", synthetic.config2()),
+                     ("w4_4096x14336", synthetic.config3_layer(0, 6, 4096, 14336, "down"))):
+        hl = pack_host(L.fmt, L.W, L.profile, L.ratio)
+        rf = refinement_host(L.W, hl)
+        base = DeviceLayer(hl, tiled=True)
+        base.set_refinement(rf)
+        nbytes = base.nbytes(1)
+        rbytes_table = base.r_codes.numel() + 2 * base.r_scales.numel() + 2 * base.r_zeros.numel()
+        layers = rotated(DeviceLayer, base, nbytes + rbytes_table)
+        for c in layers[1:]:
+            c.r_codes, c.r_scales, c.r_zeros = (base.r_codes.clone(), base.r_scales.clone(),
+                                                base.r_zeros.clone())
+        nc = len(layers)
+        N, K = base.N, base.K
+        n_sel = B.wq_topk_count(K, chunk, k)
+        x = torch.from_numpy(L.x[:1].reshape(-1).view(np.int16)).cuda()
+        ys = [torch.empty(N, dtype=torch.int16, device="cuda") for _ in range(nc)]
+        sels = [torch.empty(n_sel, dtype=torch.int32, device="cuda") for _ in range(nc)]
+        for i in range(nc):
+            B.wq_topk_chunks(x, K, chunk, k, sels[i])
+        st = a.steps // 4
+        wu = a.warmup // 4
+        t_topk = timer(lambda i: B.wq_topk_chunks(x, K, chunk, k, sels[i % nc]), st, wu)
+        t_ref = timer(lambda i: layers[i % nc].refine(x, ys[i % nc], sels[i % nc], n_sel), st, wu)
+        t_gemv = timer(lambda i: layers[i % nc].gemv_tiled(x, ys[i % nc]), st, wu)
+
+        def chain(i):
+            lay, y, sel = layers[i % nc], ys[i % nc], sels[i % nc]
+            lay.gemv_tiled(x, y)
+            B.wq_topk_chunks(x, K, chunk, k, sel)
+            lay.refine(x, y, sel, n_sel)
+
+        t_all = timer(chain, st, wu)
+        Gn = N // 32
+        rbytes = n_sel * (N // 2 + 4 * Gn) + 4 * n_sel + 2 * n_sel + 4 * N
+        rows.append({"workload": f"refine_topk{k}_per{chunk}_{label}", "N": N, "K": K,
+                     "n_sel": n_sel, "topk_us": round(t_topk * 1e3, 3),
+                     "refine_us": round(t_ref * 1e3, 3), "refine_bytes": rbytes,
+                     "refine_GB/s": round(rbytes / (t_ref * 1e-3) / 1e9, 1),
+                     "gemv_us": round(t_gemv * 1e3, 3),
+                     "gemv_topk_refine_us": round(t_all * 1e3, 3),
+                     "overhead_pct": round(100 * (t_all - t_gemv) / t_gemv, 1)})
+        del layers
+    return rows
+
+
 def stream_workload(a, torch, timer, copy):
     import bit_weight_only_gemv_amd as B
     nb = (a.bytes + 15) // 16 * 16
@@ -513,6 +572,8 @@ def main():
         out = embed_workload(a, torch, timer)
     elif a.workload == "kurtosis":
         out = kurtosis_workload(a, torch, timer)
+    elif a.workload == "refine":
+        out = refine_workload(a, torch, timer)
     else:
         out = stream_workload(a, torch, timer, copy=(a.workload == "copy"))
     for o in (out if isinstance(out, list) else [out]):

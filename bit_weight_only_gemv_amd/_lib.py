@@ -58,6 +58,9 @@ SIGNATURES = {
     "wq_gemm_wq": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _I64, _P, _P]),
     "wq_outlier_add": (_INT, [_P, _P, _I64, _I64, _P, _I64, _I64, _P, _P]),
     "wq_embed_gather": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _I64, _P, _P]),
+    "wq_topk_count": (_I64, [_I64, _I64, _I64]),
+    "wq_topk_chunks": (_INT, [_P, _I64, _I64, _I64, _P, _P]),
+    "wq_refine_add": (_INT, [_P, _P, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
     "wq_tiled_bytes": (_I64, [_INT, _I64, _I64, _I64]),
     "wq_tile_host": (_INT, [_INT, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64]),
     "wq_gemv_tiled": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
@@ -280,6 +283,24 @@ def wq_embed_gather(fmt, codes, scales, zeros, V, K, ids, n_ids, out, stream=Non
     _check(load().wq_embed_gather(fmt, _dptr(codes), _dptr(scales), _dptr(zeros), V, K,
                                   _dptr(ids) if n_ids else None, n_ids,
                                   _dptr(out) if n_ids else None, _stream(stream)))
+
+
+def wq_topk_count(K: int, chunk: int, k: int) -> int:
+    n = int(load().wq_topk_count(K, chunk, k))
+    if n < 0:
+        _check(n)
+    return n
+
+
+def wq_topk_chunks(x, K, chunk, k, sel, stream=None):
+    _check(load().wq_topk_chunks(_dptr(x), K, chunk, k, _dptr(sel) if k else None,
+                                 _stream(stream)))
+
+
+def wq_refine_add(rcodes, rscales, rzeros, N, K, sel, n_sel, x, y, stream=None):
+    _check(load().wq_refine_add(_dptr(rcodes), _dptr(rscales), _dptr(rzeros), N, K,
+                                _dptr(sel) if n_sel else None, n_sel, _dptr(x), _dptr(y),
+                                _stream(stream)))
 
 
 def wq_outlier_add(idx, out_w, n_out, N, X, M, K, Y, stream=None):

@@ -24,7 +24,7 @@ LIB = os.path.join(HERE, "libwq.so")
 
 ARCH = "gfx950"
 HOST_SOURCES = ["wq_host.cpp"]
-HIP_SOURCES = ["wq_gemv.hip", "wq_mma.hip", "wq_gemm.hip", "wq_misc.hip"]
+HIP_SOURCES = ["wq_gemv.hip", "wq_mma.hip", "wq_gemm.hip", "wq_misc.hip", "wq_refine.hip"]
 
 
 def _hipcc() -> str:

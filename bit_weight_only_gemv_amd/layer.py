@@ -62,6 +62,31 @@ def pack_host(fmt: int, W: np.ndarray, profile: Optional[np.ndarray] = None,
     return HostLayer(fmt, N, K, codes, sc, ze, idx, wout)
 
 
+@dataclasses.dataclass
+class HostRefinement:
+    """4-bit refinement columns of a layer, per input channel: the W4 format of
+    the residual transposed ([K, N], groups of 32 output rows)."""
+    N: int
+    K: int
+    codes: np.ndarray          # uint8 [K, N/2]
+    scales: np.ndarray         # float16 [K, N/32]
+    zeros: np.ndarray          # float16 [K, N/32]
+
+
+def refinement_host(W: np.ndarray, host: "HostLayer") -> HostRefinement:
+    """The residual of the packed layer, R = W_dense - w_hat (outlier columns 0:
+    they are exact already), transposed and packed with the library's W4
+    encoder (StrataFlux section 3.2.1, DecDEC's 4-bit residual encoding)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    w_hat = L.wq_dequant_host(host.fmt, host.codes, host.scales, host.zeros, N, K)
+    R = W - w_hat.astype(np.float32)
+    if host.n_out:
+        R[:, host.idx] = 0.0
+    codes, sc, ze = L.wq_quantize_w4(np.ascontiguousarray(R.T))
+    return HostRefinement(N, K, codes, sc, ze)
+
+
 class DeviceLayer:
     """Packed arrays in device memory (torch tensors used as plain buffers).
     With ``tiled=True`` the layer also holds the tiled M = 1 layout (built by
@@ -120,6 +145,21 @@ class DeviceLayer:
         """Rows ids of the dequantized table into out (FP16 [len(ids), K])."""
         L.wq_embed_gather(self.fmt, self.codes, self.scales, self.zeros, self.N, self.K, ids,
                           ids.numel(), out, stream)
+
+    def set_refinement(self, ref: HostRefinement, device="cuda"):
+        import torch
+
+        def up(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+
+        self.r_codes = up(ref.codes, np.uint8)
+        self.r_scales = up(ref.scales.view(np.int16), np.int16)
+        self.r_zeros = up(ref.zeros.view(np.int16), np.int16)
+
+    def refine(self, x, y, sel, n_sel, stream=None):
+        """y += sum over the selected channels of x_i C[:, i] (StrataFlux Eq. 2)."""
+        L.wq_refine_add(self.r_codes, self.r_scales, self.r_zeros, self.N, self.K, sel, n_sel,
+                        x, y, stream)
 
     def dequant(self, W_hat, stream=None):
         L.wq_dequant_device(self.fmt, self.codes, self.scales, self.zeros, self.N, self.K, W_hat,

@@ -213,6 +213,33 @@ int wq_embed_gather(int fmt, const uint8_t* codes, const uint16_t* scales, const
                     int64_t V, int64_t K, const int32_t* ids, int64_t n_ids, uint16_t* out,
                     void* stream);
 
+/* ------------------------------------------- runtime top-k refinement
+ * StrataFlux page, section 3.2.1: channel selection per chunk of input channels
+ * and the refinement add of Eq. 2.  The refinement columns C are given per
+ * input channel, i.e. C transposed [K][N], in the W4 format along N (codes
+ * [K][N/2], FP16 scales and zeros [K][N/32], groups of 32 output rows); the
+ * plain reading is the 4-bit residual W - w_hat of the resident layer. */
+
+/* Number of channels wq_topk_chunks selects: per full chunk min(k, chunk), and
+ * min(k, K % chunk) for a short last chunk.  Negative WQ_ERR_* on bad sizes. */
+int64_t wq_topk_count(int64_t K, int64_t chunk, int64_t k);
+
+/* S(x): in each chunk of `chunk` consecutive channels of x (FP16 [K]), the k
+ * channels of largest |x| (ties to the lower index), exact.  Chunk c's picks are
+ * written ascending to sel[c * min(k, chunk) ...]; sel (int32, device) holds
+ * wq_topk_count(K, chunk, k) entries.  chunk: a multiple of 64 in [64, 1024]
+ * (the page uses 1024).  K % 32 == 0.  k == 0 does nothing. */
+int wq_topk_chunks(const uint16_t* x, int64_t K, int64_t chunk, int64_t k, int32_t* sel,
+                   void* stream);
+
+/* Eq. 2: y[n] = FP16( y[n] + sum_j x[sel[j]] C[n][sel[j]] ), FP32 accumulation,
+ * j < n_sel, with C[n][i] = (q - z) s of the W4 refinement row i (values as
+ * dequantized, without their FP16 rounding).  Entries of sel outside [0, K)
+ * are skipped.  N % 32 == 0.  y is read and written in place. */
+int wq_refine_add(const uint8_t* rcodes, const uint16_t* rscales, const uint16_t* rzeros,
+                  int64_t N, int64_t K, const int32_t* sel, int64_t n_sel, const uint16_t* x,
+                  uint16_t* y, void* stream);
+
 /* Standalone outlier correction (the add of SPECTRA section 4.1's outlier loop;
  * the same arithmetic as the column refinement add of the StrataFlux page,
  * section 3.2.1 Eq. 2, for a static column set):

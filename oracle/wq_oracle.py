@@ -423,13 +423,16 @@ def topk_chunks(x: np.ndarray, k: int, chunk: int = REFINE_CHUNK) -> np.ndarray:
     return np.concatenate(out).astype(np.int32) if out else np.zeros(0, np.int32)
 
 
-def refinement_w4(W: np.ndarray, w_hat: np.ndarray):
+def refinement_w4(W: np.ndarray, w_hat: np.ndarray, idx=None):
     """Refinement columns: the residual R = W - w_hat of the resident layer,
     stored per input channel (R transposed, [K, N]) in the W4 format along N
     ([StrataFlux] 3.2.1: refinement values as integers with their own scale
-    factors; DecDEC's 4-bit encoding of the weight residual).  Returns the W4
+    factors; DecDEC's 4-bit encoding of the weight residual).  Outlier columns
+    ``idx`` are exact already: their residual is 0 (reading).  Returns the W4
     quantization of R^T: (q, scale, zero) with groups of 32 output rows."""
     R = np.asarray(W, dtype=np.float32) - np.asarray(w_hat, dtype=np.float16).astype(np.float32)
+    if idx is not None and len(idx):
+        R[:, np.asarray(idx, dtype=np.int64)] = 0.0
     q, sc, ze, _ = quantize_w4(np.ascontiguousarray(R.T))
     return q, sc, ze
 

@@ -345,3 +345,66 @@ def test_gemv_kurtosis_policy_layer(fmt):
     y, _ = run_gemv(dl, x)
     check_product(ref, y, x, f"kurtosis policy w{fmt} n_out={ref.n_out} (row-major)")
     check_product(ref, run_gemv_tiled(dl, x), x, f"kurtosis policy w{fmt} (tiled)")
+
+
+# ---------------------------------------------- runtime top-k refinement
+
+
+@pytest.mark.parametrize("K,chunk,k", [(4096, 1024, 32), (14336, 1024, 32), (4096, 1024, 1),
+                                       (2080, 1024, 64), (1024, 256, 255), (96, 64, 200),
+                                       (4096, 512, 0), (28672, 1024, 128)])
+def test_topk_chunks_exact(K, chunk, k):
+    say(f"topk K={K} chunk={chunk} k={k}")
+    rng = np.random.default_rng(K + k)
+    x = rng.standard_normal(K).astype(np.float16)
+    x[rng.choice(K, K // 8)] = x[1]        # exact ties in |x|
+    x[rng.choice(K, K // 16)] = -x[1]
+    x[::37] *= -40                          # large negative values
+    n = B.wq_topk_count(K, chunk, k)
+    exp = O.topk_chunks(x, k, chunk)
+    assert n == len(exp)
+    sel = torch.full((max(n, 1),), -7, dtype=torch.int32, device="cuda")
+    B.wq_topk_chunks(dev_fp16(x), K, chunk, k, sel)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy()[:n], exp)
+
+
+@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("N,K,k", [(14336 // 4, 4096, 32), (512, 2048, 8), (96, 1088, 100)])
+def test_gemv_then_refine(fmt, N, K, k):
+    say(f"gemv + top-k refinement fmt={fmt} N={N} K={K} k={k}")
+    from bit_weight_only_gemv_amd.layer import refinement_host
+    L = synthetic.small_layer(fmt, N, K, with_outliers=True, seed=k)
+    ref, dl = build(fmt, L.W, L.profile, L.ratio)
+    hl = pack_host(fmt, L.W, L.profile, L.ratio)
+    rf = refinement_host(L.W, hl)
+    rq, rs, rz = O.refinement_w4(L.W, ref.w_hat(), ref.idx)
+    assert np.array_equal(rf.codes, O.pack_w4(rq))
+    assert np.array_equal(_bits(rf.scales), _bits(rs)) and np.array_equal(_bits(rf.zeros), _bits(rz))
+    dl.set_refinement(rf)
+    x = L.x.reshape(-1)
+    y, xd = run_gemv(dl, x)
+    y_base = host_fp16(y).astype(np.float64).copy()
+    n = B.wq_topk_count(K, 1024, k)
+    sel = torch.empty(n, dtype=torch.int32, device="cuda")
+    B.wq_topk_chunks(xd, K, 1024, k, sel)
+    dl.refine(xd, y, sel, n)
+    torch.cuda.synchronize()
+    S = O.topk_chunks(x, k)
+    assert np.array_equal(sel.cpu().numpy(), S)
+    c_hat = O.dequant_w4(rq, rs, rz)
+    # the add itself, on top of the GPU's own base output
+    y_ref, a = O.refine_ref(y_base.astype(np.float16), x, S, c_hat)
+    ok, worst = O.check_tolerance(host_fp16(y).astype(np.float64), y_ref, a)
+    say(f"  refine add: worst |err|/bound = {worst:.4f}")
+    assert ok
+    # and the whole refined product against the oracle's
+    y0, a0 = O.matvec_ref(ref.w_hat(), x, ref.idx, ref.wout)
+    terms = x.astype(np.float64)[S][:, None] * c_hat.astype(np.float64)[S]
+    ok2, worst2 = O.check_tolerance(host_fp16(y).astype(np.float64), y0[0] + terms.sum(0),
+                                    a0[0] + np.abs(terms).sum(0))
+    say(f"  refined product: worst |err|/bound = {worst2:.4f}")
+    assert ok2
+    # refinement moves the product toward the unquantized layer
+    exact = L.W.astype(np.float64) @ x.astype(np.float64)
+    assert np.abs(host_fp16(y) - exact).mean() < np.abs(y_base - exact).mean()

@@ -154,6 +154,18 @@ def test_error_codes():
     assert lib.wq_embed_gather(4, fake, fake, fake, 8, 64, fake, -1, fake, None) == -1
     assert lib.wq_embed_gather(4, fake, fake, fake, 8, 64, None, 0, None, None) == 0
     assert lib.wq_embed_gather(4, fake, fake, fake, 8, 64, None, 2, fake, None) == -1
+    # top-k selection and refinement add
+    assert B.wq_topk_count(4096, 1024, 32) == 128 and B.wq_topk_count(2080, 1024, 64) == 160
+    assert B.wq_topk_count(100, 64, 200) == 100 and B.wq_topk_count(64, 64, 0) == 0
+    assert lib.wq_topk_count(10, 0, 1) < 0
+    assert lib.wq_topk_chunks(fake, 4096, 1000, 8, fake, None) == -2
+    assert lib.wq_topk_chunks(fake, 4096, 2048, 8, fake, None) == -2
+    assert lib.wq_topk_chunks(fake, 4010, 1024, 8, fake, None) == -2
+    assert lib.wq_topk_chunks(fake, 4096, 1024, -1, fake, None) == -1
+    assert lib.wq_topk_chunks(None, 4096, 1024, 0, None, None) == 0
+    assert lib.wq_refine_add(fake, fake, fake, 48, 64, fake, 1, fake, fake, None) == -2
+    assert lib.wq_refine_add(fake, fake, fake, 64, 64, fake, 65, fake, fake, None) == -1
+    assert lib.wq_refine_add(None, None, None, 64, 64, None, 0, None, None, None) == 0
 
 
 # ------------------------------------------------- W4P packed zero points
