@@ -486,6 +486,13 @@ def refine_workload(a, torch, timer):
             lay.refine(x, y, sel, n_sel)
 
         t_all = timer(chain, st, wu)
+        t_fused = timer(lambda i: layers[i % nc].refine_topk(x, ys[i % nc], k, chunk), st, wu)
+
+        def chain_fused(i):
+            layers[i % nc].gemv_tiled(x, ys[i % nc])
+            layers[i % nc].refine_topk(x, ys[i % nc], k, chunk)
+
+        t_all_fused = timer(chain_fused, st, wu)
         Gn = N // 32
         rbytes = n_sel * (N // 2 + 4 * Gn) + 4 * n_sel + 2 * n_sel + 4 * N
         rows.append({"workload": f"refine_topk{k}_per{chunk}_{label}", "N": N, "K": K,
@@ -493,8 +500,10 @@ def refine_workload(a, torch, timer):
                      "refine_us": round(t_ref * 1e3, 3), "refine_bytes": rbytes,
                      "refine_GB/s": round(rbytes / (t_ref * 1e-3) / 1e9, 1),
                      "gemv_us": round(t_gemv * 1e3, 3),
+                     "fused_topk_refine_us": round(t_fused * 1e3, 3),
                      "gemv_topk_refine_us": round(t_all * 1e3, 3),
-                     "overhead_pct": round(100 * (t_all - t_gemv) / t_gemv, 1)})
+                     "gemv_fused_refine_us": round(t_all_fused * 1e3, 3),
+                     "overhead_pct": round(100 * (t_all_fused - t_gemv) / t_gemv, 1)})
         del layers
     return rows
 

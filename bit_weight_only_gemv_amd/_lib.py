@@ -61,6 +61,7 @@ SIGNATURES = {
     "wq_topk_count": (_I64, [_I64, _I64, _I64]),
     "wq_topk_chunks": (_INT, [_P, _I64, _I64, _I64, _P, _P]),
     "wq_refine_add": (_INT, [_P, _P, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
+    "wq_refine_topk": (_INT, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P]),
     "wq_tiled_bytes": (_I64, [_INT, _I64, _I64, _I64]),
     "wq_tile_host": (_INT, [_INT, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64]),
     "wq_gemv_tiled": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
@@ -301,6 +302,12 @@ def wq_refine_add(rcodes, rscales, rzeros, N, K, sel, n_sel, x, y, stream=None):
     _check(load().wq_refine_add(_dptr(rcodes), _dptr(rscales), _dptr(rzeros), N, K,
                                 _dptr(sel) if n_sel else None, n_sel, _dptr(x), _dptr(y),
                                 _stream(stream)))
+
+
+def wq_refine_topk(rcodes, rscales, rzeros, N, K, chunk, k, x, y, sel_out=None, stream=None):
+    _check(load().wq_refine_topk(_dptr(rcodes), _dptr(rscales), _dptr(rzeros), N, K, chunk, k,
+                                 _dptr(x), _dptr(y), _dptr(sel_out) if sel_out is not None else None,
+                                 _stream(stream)))
 
 
 def wq_outlier_add(idx, out_w, n_out, N, X, M, K, Y, stream=None):

@@ -23,6 +23,20 @@ inline bool allow_lds(const void* kernel, size_t bytes) {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+inline int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
 // Turns a failed launch into WQ_ERR_HIP with the runtime's message.
 inline int check_launch(const char* who) {
   const hipError_t e = hipGetLastError();

@@ -1064,19 +1064,6 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
 
 // ------------------------------------------------------------- launch plan
 
-static int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    cached[dev] = v;
-  }
-  return cached[dev];
-}
-
 struct MmaPlan {
   bool ok, preferred;
   int nw, nks, nsw, nswt, nrb, nch, grid, rbl;

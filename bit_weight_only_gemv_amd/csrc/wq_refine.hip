@@ -9,208 +9,371 @@
 // stored per input channel (C transposed, [K][N]) in the W4 format along N
 // (groups of 32 output rows, FP16 scale and zero, in-group nibble interleave).
 //
-// topk_kernel: one workgroup per chunk.  The selection is an exact radix
-// select on 26-bit keys ((|x| bits << 10 | 1023 - local index) + 1, unique
-// per chunk, so ties go to the lower index); the kept channels are then
-// written in index order through a block-wide prefix count.
+// Selection (wave_chunk_topk): one wave per chunk, lane l holding channels
+// 16l .. 16l + 15.  The k-th largest FP16 magnitude T comes from two histogram
+// passes in the wave's own LDS (the top 7 bits of the 15-bit magnitude, then
+// the low 8 bits inside the chosen bin); every channel above T is kept, and of
+// those equal to T the lowest-indexed ones, counted by a wave prefix sum, fill
+// the rest.  The picks are written in index order.  No block barrier is
+// needed.
 //
-// refine_kernel: a workgroup owns 64 output rows (2 groups of 32) and splits
-// the selected columns over 32 slots of 8 threads; thread (slot, group,
-// quarter) decodes 4 code bytes, 8 rows, of columns j = slot, slot + 32, ...
-// with four columns' loads in flight at a time.  The slots' partial sums are
-// added in a fixed order and added once into the FP16 output.
+// Refinement add (refine_groups): a workgroup of 512 threads owns GPW groups of
+// 32 output rows and splits the selected columns over 128 slots of 4 threads;
+// thread (slot, quarter) decodes 4 code bytes, 8 rows, of each of its groups
+// for columns j = slot, slot + 128, ... with four columns' loads in flight at
+// a time.  The slots' partial sums are added in a fixed order and added once
+// into the FP16 output.
+//
+// topk_kernel runs the selection alone (one wave per chunk), refine_kernel the
+// add alone from a given selection, and topk_refine_kernel both in one launch:
+// each workgroup selects for every chunk into LDS (8 waves, chunks w, w + 8,
+// ...) and then adds for its own group.  The two paths sum in the same order,
+// so their outputs agree bit for bit.
 
 #include "wq_common.cuh"
 #include "wq_device.h"
 
 namespace wqd {
 
-constexpr int kTopkThreads = 256;
-constexpr int kRadixBits = 7;
-constexpr int kRadixBins = 1 << kRadixBits;   // 128
-constexpr int kRefineThreads = 256;
-constexpr int kRefineRows = 64;               // 2 groups of 32 rows per workgroup
-constexpr int kRefineSlots = kRefineThreads / 8;   // columns in flight per workgroup
-constexpr int kRefineUnroll = 4;              // columns per slot with loads in flight
 constexpr uint32_t kOobR = 0xFFFFF000u;       // past every buffer: loads return 0
+constexpr int kSelBins1 = 128;                // magnitude bits 14..8
+constexpr int kSelBins2 = 256;                // magnitude bits 7..0
+constexpr int kSelWords = kSelBins1 + kSelBins2 + 4;   // per wave: both histograms + state
+constexpr int kRefineThreads = 512;
+constexpr int kRefineSlots = kRefineThreads / 4;       // column slots per workgroup
+constexpr int kRefineUnroll = 4;              // columns per slot with loads in flight
+constexpr int kRefineRuns = kRefineThreads / kGroup;   // 16 runs of 8 slots in the sum
+constexpr int kFusedMaxSel = 4096;            // selections the fused kernel holds in LDS
 
-// Per wave: inclusive suffix sums over lanes (lane l gets the sum of lanes >= l).
-__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t t = __shfl_down(v, d);
-    if (lane + d < kWave) v += t;
-  }
-  return v;
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Per wave: inclusive prefix sums over lanes.
-__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t t = __shfl_up(v, d);
-    if (lane >= d) v += t;
-  }
-  return v;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 
-__global__ void __launch_bounds__(kTopkThreads) topk_kernel(const uint16_t* __restrict__ x,
-                                                           int K, int chunk, int k,
-                                                           int32_t* __restrict__ sel) {
-  __shared__ uint32_t hist[kRadixBins];
-  __shared__ uint32_t s_state[2];            // [0] key prefix, [1] rank still wanted
-  __shared__ uint32_t s_wave[kTopkThreads / kWave];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid >> 6;
+// Per wave (all 64 lanes active): the sum of v over the lanes below this one,
+// and over all lanes in `total`.  Inclusive scan with DPP: shifts by 1, 2, 4, 8
+// inside each row of 16 lanes, then the row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ uint32_t wave_excl_sum(uint32_t v, uint32_t& total) {
+  const int lane = (int)__lane_id();
+  const int rl = lane & 15;
+  uint32_t r = v, t;
+  t = dpp_mov<0x111>(r);   // row_shr:1
+  if (rl >= 1) r += t;
+  t = dpp_mov<0x112>(r);   // row_shr:2
+  if (rl >= 2) r += t;
+  t = dpp_mov<0x114>(r);   // row_shr:4
+  if (rl >= 4) r += t;
+  t = dpp_mov<0x118>(r);   // row_shr:8
+  if (rl >= 8) r += t;
+  t = dpp_mov<0x142>(r);   // row_bcast:15
+  if ((lane & 31) >= 16) r += t;
+  t = dpp_mov<0x143>(r);   // row_bcast:31
+  if (lane >= 32) r += t;
+  total = (uint32_t)__builtin_amdgcn_readlane((int)r, 63);
+  return r - v;
+}
+
+// One wave: of the csize channels c0 .. c0 + csize - 1 (csize a multiple of 32,
+// at most 1024), the kk of largest |x| with ties to the lower index, written
+// ascending to out[0 .. kk).  hist: this wave's kSelWords words of LDS.
+__device__ __forceinline__ void wave_chunk_topk(__amdgpu_buffer_rsrc_t xrs, int c0, int csize, int kk,
+                                uint32_t* hist, int32_t* out, int lane) {
+  const bool valid = 16 * lane < csize;
+  uint32_t m[16];
+  {
+    const uint32_t off = valid ? (uint32_t)(c0 + 16 * lane) * 2u : kOobR;
+    const u4v a = ld128(xrs, off), b = ld128(xrs, off + 16u);
+    const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      m[2 * i] = wv[i] & 0x7FFFu;
+      m[2 * i + 1] = (wv[i] >> 16) & 0x7FFFu;
+    }
+  }
+  const bool all = kk >= csize;
+  uint32_t T = 0u, keq = 0u;   // keep |x| > T, and the first keq channels with |x| == T
+  if (!all && kk > 0) {
+    uint32_t* h1 = hist;
+    uint32_t* h2 = hist + kSelBins1;
+    uint32_t* st = hist + kSelBins1 + kSelBins2;
+    h1[lane] = 0u;
+    h1[lane + kWave] = 0u;
+#pragma unroll
+    for (int i = 0; i < kSelBins2 / kWave; ++i) h2[lane + kWave * i] = 0u;
+    wave_sync();
+    if (valid) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) atomicAdd(&h1[m[e] >> 8], 1u);
+    }
+    wave_sync();
+    {
+      // lane l holds bins 2l (lower) and 2l + 1 (higher); exactly one bin holds
+      // the kk-th largest (1 <= kk < number of valid channels)
+      const uint32_t rem = (uint32_t)kk;
+      const uint32_t lo = h1[2 * lane], hi = h1[2 * lane + 1];
+      uint32_t tot;
+      const uint32_t below = wave_excl_sum(lo + hi, tot);
+      const uint32_t suf = tot - below;                     // bins >= 2l
+      const uint32_t above = suf - lo - hi;                 // bins >= 2l + 2
+      if (above < rem && rem <= above + hi) {
+        st[0] = 2u * lane + 1u;
+        st[1] = rem - above;
+      } else if (above + hi < rem && rem <= suf) {
+        st[0] = 2u * lane;
+        st[1] = rem - above - hi;
+      }
+    }
+    wave_sync();
+    const uint32_t b1 = st[0];
+    const uint32_t rem = st[1];
+    if (valid) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if ((m[e] >> 8) == b1) atomicAdd(&h2[m[e] & 0xFFu], 1u);
+    }
+    wave_sync();
+    {
+      uint32_t hb[4], sum = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hb[i] = h2[4 * lane + i];
+        sum += hb[i];
+      }
+      uint32_t tot;
+      const uint32_t below = wave_excl_sum(sum, tot);
+      uint32_t cum = tot - below - sum;                     // bins >= 4l + 4
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (cum < rem && rem <= cum + hb[i]) {
+          st[2] = (b1 << 8) | (uint32_t)(4 * lane + i);
+          st[3] = rem - cum;
+        }
+        cum += hb[i];
+      }
+    }
+    wave_sync();
+    T = st[2];
+    keq = st[3];
+  }
+  uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const bool g = valid && (all || (kk > 0 && m[e] > T));
+    const bool q = valid && !all && kk > 0 && m[e] == T;
+    gt |= (uint32_t)g << e;
+    eq |= (uint32_t)q << e;
+  }
+  const uint32_t neq = (uint32_t)__builtin_popcount(eq);
+  uint32_t tot;
+  const uint32_t eq_before = wave_excl_sum(neq, tot);
+  uint32_t keep = gt;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t rank = eq_before + (uint32_t)__builtin_popcount(eq & ((1u << e) - 1u));
+    if (((eq >> e) & 1u) && rank < keq) keep |= 1u << e;
+  }
+  const uint32_t cnt = (uint32_t)__builtin_popcount(keep);
+  uint32_t pos = wave_excl_sum(cnt, tot);
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if ((keep >> e) & 1u) {
+      if (pos < (uint32_t)kk) out[pos] = c0 + 16 * lane + e;   // never past the chunk's picks
+      ++pos;
+    }
+}
+
+// One chunk per workgroup of one wave.
+__global__ void __launch_bounds__(kWave) topk_kernel(const uint16_t* __restrict__ x, int K,
+                                                    int chunk, int k, int32_t* __restrict__ sel) {
+  __shared__ uint32_t hist[kSelWords];
   const int c = blockIdx.x;
   const int c0 = c * chunk;
   const int csize = min(chunk, K - c0);
-  const int kk = min(k, csize);
-
-  // four consecutive channels per thread; past the chunk or K: key 0
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (uint32_t)K * 2u);
-  const int j0 = 4 * tid;
-  const u2 xv = ld64(xrs, j0 < csize ? (uint32_t)(c0 + j0) * 2u : kOobR);
-  const uint32_t h[4] = {xv.x & 0xFFFFu, xv.x >> 16, xv.y & 0xFFFFu, xv.y >> 16};
-  uint32_t key[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int j = j0 + e;
-    key[e] = j < csize ? (((h[e] & 0x7FFFu) << 10) | (uint32_t)(1023 - j)) + 1u : 0u;
-  }
-
-  // ---- radix select of the kk-th largest key: 4 passes of 7 bits (bits 27..0)
-  uint32_t thr = 1u;   // kk == csize: every valid key (>= 1) is kept
-  if (kk > 0 && kk < csize) {
-    if (tid == 0) {
-      s_state[0] = 0u;
-      s_state[1] = (uint32_t)kk;
-    }
-    uint32_t pmask = 0u;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 21 - kRadixBits * pass;
-      if (tid < kRadixBins) hist[tid] = 0u;
-      __syncthreads();
-      const uint32_t prefix = s_state[0];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (key[e] != 0u && (key[e] & pmask) == prefix)
-          atomicAdd(&hist[(key[e] >> shift) & (kRadixBins - 1)], 1u);
-      __syncthreads();
-      if (wave == 0) {
-        // lane l holds bins 2l (lower) and 2l + 1 (higher); find the bin that
-        // holds the wanted rank counting from the largest key
-        const uint32_t rem = s_state[1];
-        const uint32_t lo = hist[2 * lane], hi = hist[2 * lane + 1];
-        const uint32_t suf = wave_suffix_sum(lo + hi, lane);   // bins >= 2l
-        const uint32_t above = suf - lo - hi;                 // bins >= 2l + 2
-        int bin = -1;
-        uint32_t left = 0u;
-        if (above < rem && rem <= above + hi) {
-          bin = 2 * lane + 1;
-          left = rem - above;
-        } else if (above + hi < rem && rem <= suf) {
-          bin = 2 * lane;
-          left = rem - above - hi;
-        }
-        if (bin >= 0) {
-          s_state[0] = prefix | ((uint32_t)bin << shift);
-          s_state[1] = left;
-        }
-      }
-      __syncthreads();
-      pmask |= (uint32_t)(kRadixBins - 1) << shift;
-    }
-    thr = s_state[0];   // keys are unique: exactly kk keys are >= thr
-  }
-
-  // ---- keep key >= thr (and k > 0), written in index order
-  uint32_t keep[4], cnt = 0u;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    keep[e] = (kk > 0 && key[e] != 0u && key[e] >= thr) ? 1u : 0u;
-    cnt += keep[e];
-  }
-  const uint32_t incl = wave_prefix_sum(cnt, lane);
-  if (lane == kWave - 1) s_wave[wave] = incl;
-  __syncthreads();
-  uint32_t base = 0u;
-  for (int w = 0; w < wave; ++w) base += s_wave[w];
-  uint32_t pos = base + incl - cnt;
-  int32_t* out = sel + (size_t)c * (size_t)k;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (keep[e]) out[pos++] = c0 + j0 + e;
+  wave_chunk_topk(xrs, c0, csize, min(k, csize), hist, sel + (size_t)c * (size_t)k,
+                  (int)threadIdx.x);
 }
 
-__global__ void __launch_bounds__(kRefineThreads) refine_kernel(
-    const uint8_t* __restrict__ rcodes, const uint16_t* __restrict__ rscales,
-    const uint16_t* __restrict__ rzeros, int N, int K, const int32_t* __restrict__ sel, int n_sel,
-    const uint16_t* __restrict__ x, uint16_t* __restrict__ y) {
-  __shared__ float s_part[kRefineSlots][kRefineRows];
+// y[32 g .. 32 g + 31] += sum_{j < n_sel} x[sel[j]] C[rows][sel[j]] for the
+// workgroup's GPW groups g = g0 .. g0 + GPW - 1 (those below Gn), 512 threads.
+// Every group is summed in the same order whatever GPW is.  sel may sit in LDS
+// or global memory; s_part holds GPW * 128 * 32 floats, s_red GPW * 16 * 32.
+template <int GPW>
+__device__ __forceinline__ void refine_groups(const __amdgpu_buffer_rsrc_t& crs,
+                                              const __amdgpu_buffer_rsrc_t& srs,
+                                              const __amdgpu_buffer_rsrc_t& zrs,
+                                              const __amdgpu_buffer_rsrc_t& xrs, uint32_t row_bytes,
+                                              int Gn, int K, int g0, const int32_t* sel, int n_sel,
+                                              uint16_t y0, uint16_t* __restrict__ y, float* s_part,
+                                              float* s_red) {
   const int tid = threadIdx.x;
-  const int p = tid & 7, slot = tid >> 3;             // part of the row block, column slot
-  const int q = p & 3;                                // quarter of the group
-  const int Gn = N / kGroup;                          // groups along N
-  const int g = blockIdx.x * (kRefineRows / kGroup) + (p >> 2);
-  const bool gv = g < Gn;
-  const uint32_t row_bytes = (uint32_t)N / 2u;
-  const __amdgpu_buffer_rsrc_t crs = make_rsrc(rcodes, clamp_bytes((uint64_t)K * row_bytes));
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(rscales, clamp_bytes((uint64_t)K * Gn * 2));
-  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(rzeros, clamp_bytes((uint64_t)K * Gn * 2));
-  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, (uint32_t)K * 2u);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int q = tid & 3, slot = tid >> 2;             // quarter of a group, column slot
+  float acc[GPW][8];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[gi][i] = 0.f;
   constexpr int kStep = kRefineSlots * kRefineUnroll;
   for (int j0 = slot; j0 < n_sel; j0 += kStep) {
     // kRefineUnroll columns of this slot, all loads issued before any use; a
-    // column past n_sel or out of [0, K) reads zeros everywhere and adds 0
-    uint32_t co[kRefineUnroll], mo[kRefineUnroll], xo[kRefineUnroll];
+    // column past n_sel or out of [0, K), or a group past Gn, reads zeros
+    // everywhere and adds 0
+    int ch[kRefineUnroll];
 #pragma unroll
     for (int u = 0; u < kRefineUnroll; ++u) {
       const int j = j0 + u * kRefineSlots;
-      const int ch = j < n_sel ? sel[j] : -1;
-      const bool cv = ch >= 0 && ch < K;
-      xo[u] = cv ? (uint32_t)ch * 2u : kOobR;
-      co[u] = cv && gv ? (uint32_t)ch * row_bytes + (uint32_t)g * 16u + 4u * (uint32_t)q : kOobR;
-      mo[u] = cv && gv ? ((uint32_t)ch * (uint32_t)Gn + (uint32_t)g) * 2u : kOobR;
+      const int c = j < n_sel ? sel[j] : -1;
+      ch[u] = c >= 0 && c < K ? c : -1;
     }
-    uint32_t w[kRefineUnroll];
-    uint16_t sv[kRefineUnroll], zv[kRefineUnroll], xv[kRefineUnroll];
+    uint32_t w[kRefineUnroll][GPW];
+    uint16_t sv[kRefineUnroll][GPW], zv[kRefineUnroll][GPW], xv[kRefineUnroll];
 #pragma unroll
     for (int u = 0; u < kRefineUnroll; ++u) {
-      w[u] = ld32(crs, co[u]);
-      sv[u] = ld16(srs, mo[u]);
-      zv[u] = ld16(zrs, mo[u]);
-      xv[u] = ld16(xrs, xo[u]);
+      const bool cv = ch[u] >= 0;
+      xv[u] = ld16(xrs, cv ? (uint32_t)ch[u] * 2u : kOobR);
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        const int g = g0 + gi;
+        const bool ok = cv && g < Gn;
+        w[u][gi] = ld32(crs, ok ? (uint32_t)ch[u] * row_bytes + (uint32_t)g * 16u + 4u * (uint32_t)q
+                                : kOobR);
+        const uint32_t mo = ok ? ((uint32_t)ch[u] * (uint32_t)Gn + (uint32_t)g) * 2u : kOobR;
+        sv[u][gi] = ld16(srs, mo);
+        zv[u][gi] = ld16(zrs, mo);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kRefineUnroll; ++u) {
-      const float z = h2f(zv[u]);
-      const float xsv = h2f(xv[u]) * h2f(sv[u]);
-      // byte b of the quarter: rows 4q + b (low nibble) and 4q + b + 16 (high nibble)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float lo = (float)((w[u] >> (8 * b)) & 0x0Fu) - z;
-        const float hi = (float)((w[u] >> (8 * b + 4)) & 0x0Fu) - z;
-        acc[b] = __builtin_fmaf(lo, xsv, acc[b]);
-        acc[4 + b] = __builtin_fmaf(hi, xsv, acc[4 + b]);
+      for (int gi = 0; gi < GPW; ++gi) {
+        const float z = h2f(zv[u][gi]);
+        const float xsv = h2f(xv[u]) * h2f(sv[u][gi]);
+        // byte b of the quarter: rows 4q + b (low nibble) and 4q + b + 16 (high nibble)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float lo = (float)((w[u][gi] >> (8 * b)) & 0x0Fu) - z;
+          const float hi = (float)((w[u][gi] >> (8 * b + 4)) & 0x0Fu) - z;
+          acc[gi][b] = __builtin_fmaf(lo, xsv, acc[gi][b]);
+          acc[gi][4 + b] = __builtin_fmaf(hi, xsv, acc[gi][4 + b]);
+        }
       }
     }
   }
-  const int rb = (p >> 2) * kGroup + 4 * q;           // first row of this thread in the block
 #pragma unroll
-  for (int i = 0; i < 8; ++i) s_part[slot][rb + (i & 3) + (i >= 4 ? 16 : 0)] = acc[i];
+  for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      s_part[(gi * kRefineSlots + slot) * kGroup + 4 * q + (i & 3) + (i >= 4 ? 16 : 0)] =
+          acc[gi][i];
   __syncthreads();
-  if (tid < kRefineRows) {
-    const int row = blockIdx.x * kRefineRows + tid;
-    if (row < N) {
-      float t = s_part[0][tid];
+  // fixed-order sums per group: 16 runs of 8 slots, then the 16 run sums
+  {
+    const int r = tid & (kGroup - 1), run = tid >> 5;
 #pragma unroll
-      for (int s = 1; s < kRefineSlots; ++s) t += s_part[s][tid];   // fixed order
-      y[row] = f2h(h2f(y[row]) + t);
+    for (int gi = 0; gi < GPW; ++gi) {
+      const float* p = s_part + (gi * kRefineSlots + run * 8) * kGroup + r;
+      float t = p[0];
+#pragma unroll
+      for (int s = 1; s < 8; ++s) t += p[s * kGroup];
+      s_red[(gi * kRefineRuns + run) * kGroup + r] = t;
     }
   }
+  __syncthreads();
+  if (tid < GPW * kGroup && g0 + tid / kGroup < Gn) {
+    const int gi = tid / kGroup, r = tid & (kGroup - 1);
+    const float* p = s_red + gi * kRefineRuns * kGroup + r;
+    float t = p[0];
+#pragma unroll
+    for (int s = 1; s < kRefineRuns; ++s) t += p[s * kGroup];
+    y[g0 * kGroup + tid] = f2h(h2f(y0) + t);
+  }
+}
+
+struct RefineArgs {
+  const uint8_t* rcodes;
+  const uint16_t* rscales;
+  const uint16_t* rzeros;
+  const uint16_t* x;
+  uint16_t* y;
+  const int32_t* sel;   // refine_kernel: the selection; topk_refine_kernel: unused
+  int32_t* sel_out;     // topk_refine_kernel: optional copy of the selection
+  int N, K, n_sel, chunk, k;
+};
+
+template <int GPW>
+__global__ void __launch_bounds__(kRefineThreads) refine_kernel(RefineArgs a) {
+  __shared__ float s_part[GPW * kRefineSlots * kGroup];
+  __shared__ float s_red[GPW * kRefineRuns * kGroup];
+  const int Gn = a.N / kGroup;
+  const int g0 = blockIdx.x * GPW;
+  const uint32_t row_bytes = (uint32_t)a.N / 2u;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(a.rcodes, clamp_bytes((uint64_t)a.K * row_bytes));
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.rscales, clamp_bytes((uint64_t)a.K * Gn * 2));
+  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(a.rzeros, clamp_bytes((uint64_t)a.K * Gn * 2));
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.K * 2u);
+  // the output rows are read up front, off the selection's critical path
+  const int tid = threadIdx.x;
+  const uint16_t y0 =
+      tid < GPW * kGroup && g0 + tid / kGroup < Gn ? a.y[g0 * kGroup + tid] : (uint16_t)0;
+  refine_groups<GPW>(crs, srs, zrs, xrs, row_bytes, Gn, a.K, g0, a.sel, a.n_sel, y0, a.y, s_part,
+                     s_red);
+}
+
+template <int GPW>
+__global__ void __launch_bounds__(kRefineThreads) topk_refine_kernel(RefineArgs a) {
+  constexpr int kWaves = kRefineThreads / kWave;
+  // the selection's histograms live in the partial-sum area until it is used
+  constexpr int kPartFloats = GPW * kRefineSlots * kGroup;
+  static_assert(kPartFloats >= kWaves * kSelWords, "histograms must fit the partial sums");
+  __shared__ int32_t s_sel[kFusedMaxSel];
+  __shared__ float s_part[kPartFloats];
+  __shared__ float s_red[GPW * kRefineRuns * kGroup];
+  uint32_t* s_hist = reinterpret_cast<uint32_t*>(s_part);
+  const int Gn = a.N / kGroup;
+  const int g0 = blockIdx.x * GPW;
+  const uint32_t row_bytes = (uint32_t)a.N / 2u;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(a.rcodes, clamp_bytes((uint64_t)a.K * row_bytes));
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.rscales, clamp_bytes((uint64_t)a.K * Gn * 2));
+  const __amdgpu_buffer_rsrc_t zrs = make_rsrc(a.rzeros, clamp_bytes((uint64_t)a.K * Gn * 2));
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.K * 2u);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid >> 6;
+  const uint16_t y0 =
+      tid < GPW * kGroup && g0 + tid / kGroup < Gn ? a.y[g0 * kGroup + tid] : (uint16_t)0;
+  const int nch = (a.K + a.chunk - 1) / a.chunk;
+  for (int c = wave; c < nch; c += kWaves) {
+    const int c0 = c * a.chunk;
+    const int csize = min(a.chunk, a.K - c0);
+    wave_chunk_topk(xrs, c0, csize, min(a.k, csize), s_hist + wave * kSelWords, s_sel + c * a.k,
+                    lane);
+  }
+  __syncthreads();
+  if (a.sel_out != nullptr && blockIdx.x == 0)
+    for (int j = tid; j < a.n_sel; j += kRefineThreads) a.sel_out[j] = s_sel[j];
+  refine_groups<GPW>(crs, srs, zrs, xrs, row_bytes, Gn, a.K, g0, s_sel, a.n_sel, y0, a.y, s_part,
+                     s_red);
+}
+
+// Groups per workgroup: enough workgroups to spread the loads, few enough that
+// the fused kernel's per-workgroup selection is not repeated far beyond one
+// workgroup per compute unit.
+static int refine_gpw(int Gn, bool fused) {
+  int gpw = 1;
+  if (fused) {
+    const int cus = device_cus() > 0 ? device_cus() : 256;
+    while (gpw < 4 && (Gn + gpw - 1) / gpw > cus) gpw *= 2;
+  }
+  if (const char* e = getenv("WQ_REFINE_GPW")) {
+    const int v = atoi(e);
+    if (v == 1 || v == 2 || v == 4) gpw = v;
+  }
+  return gpw;
 }
 
 }  // namespace wqd
@@ -237,8 +400,8 @@ extern "C" int wq_topk_chunks(const uint16_t* x, int64_t K, int64_t chunk, int64
   if (!x || !sel) return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
   if (!aligned16(x)) return wq::fail(WQ_ERR_INVALID_ARG, "%s: x must be 16-byte aligned", who);
   const int nch = (int)((K + chunk - 1) / chunk);
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)nch), dim3(kTopkThreads), 0, (hipStream_t)stream,
-                     x, (int)K, (int)chunk, (int)std::min<int64_t>(k, chunk), sel);
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)nch), dim3(kWave), 0, (hipStream_t)stream, x,
+                     (int)K, (int)chunk, (int)std::min<int64_t>(k, chunk), sel);
   return check_launch(who);
 }
 
@@ -254,9 +417,67 @@ extern "C" int wq_refine_add(const uint8_t* rcodes, const uint16_t* rscales,
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
   if ((uint64_t)K * (uint64_t)N / 2 > 0xFFFFE000ull)
     return wq::fail(WQ_ERR_UNSUPPORTED, "%s: refinement larger than 4 GB", who);
-  const int blocks = (int)((N + kRefineRows - 1) / kRefineRows);
-  hipLaunchKernelGGL(refine_kernel, dim3((unsigned)blocks), dim3(kRefineThreads), 0,
-                     (hipStream_t)stream, rcodes, rscales, rzeros, (int)N, (int)K, sel, (int)n_sel,
-                     x, y);
+  RefineArgs a{};
+  a.rcodes = rcodes;
+  a.rscales = rscales;
+  a.rzeros = rzeros;
+  a.x = x;
+  a.y = y;
+  a.sel = sel;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.n_sel = (int)n_sel;
+  const int Gn = (int)(N / kGroup), gpw = refine_gpw(Gn, false);
+  const dim3 grid((unsigned)((Gn + gpw - 1) / gpw)), block(kRefineThreads);
+  if (gpw == 1)
+    hipLaunchKernelGGL(refine_kernel<1>, grid, block, 0, (hipStream_t)stream, a);
+  else if (gpw == 2)
+    hipLaunchKernelGGL(refine_kernel<2>, grid, block, 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(refine_kernel<4>, grid, block, 0, (hipStream_t)stream, a);
+  return check_launch(who);
+}
+
+extern "C" int wq_refine_topk(const uint8_t* rcodes, const uint16_t* rscales,
+                              const uint16_t* rzeros, int64_t N, int64_t K, int64_t chunk,
+                              int64_t k, const uint16_t* x, uint16_t* y, int32_t* sel_out,
+                              void* stream) {
+  const char* who = "wq_refine_topk";
+  if (int r = wq::check_shape(N, K, who)) return r;
+  if (N % 32) return wq::fail(WQ_ERR_UNSUPPORTED, "%s: N must be a multiple of 32", who);
+  if (chunk < 64 || chunk > 1024 || chunk % 64)
+    return wq::fail(WQ_ERR_UNSUPPORTED, "%s: chunk must be a multiple of 64 in [64, 1024]", who);
+  if (k < 0) return wq::fail(WQ_ERR_INVALID_ARG, "%s: k must be >= 0", who);
+  if (k == 0) return wq::ok();
+  const int64_t kk = std::min(k, chunk);
+  const int64_t n_sel = (K / chunk) * kk + std::min(kk, K % chunk);
+  if (n_sel > kFusedMaxSel)
+    return wq::fail(WQ_ERR_UNSUPPORTED, "%s: %lld selected channels exceed %d (use "
+                    "wq_topk_chunks + wq_refine_add)", who, (long long)n_sel, kFusedMaxSel);
+  if (!rcodes || !rscales || !rzeros || !x || !y)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (!aligned16(x)) return wq::fail(WQ_ERR_INVALID_ARG, "%s: x must be 16-byte aligned", who);
+  if ((uint64_t)K * (uint64_t)N / 2 > 0xFFFFE000ull)
+    return wq::fail(WQ_ERR_UNSUPPORTED, "%s: refinement larger than 4 GB", who);
+  RefineArgs a{};
+  a.rcodes = rcodes;
+  a.rscales = rscales;
+  a.rzeros = rzeros;
+  a.x = x;
+  a.y = y;
+  a.sel_out = sel_out;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.n_sel = (int)n_sel;
+  a.chunk = (int)chunk;
+  a.k = (int)kk;
+  const int Gn = (int)(N / kGroup), gpw = refine_gpw(Gn, true);
+  const dim3 grid((unsigned)((Gn + gpw - 1) / gpw)), block(kRefineThreads);
+  if (gpw == 1)
+    hipLaunchKernelGGL(topk_refine_kernel<1>, grid, block, 0, (hipStream_t)stream, a);
+  else if (gpw == 2)
+    hipLaunchKernelGGL(topk_refine_kernel<2>, grid, block, 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(topk_refine_kernel<4>, grid, block, 0, (hipStream_t)stream, a);
   return check_launch(who);
 }

@@ -161,6 +161,11 @@ class DeviceLayer:
         L.wq_refine_add(self.r_codes, self.r_scales, self.r_zeros, self.N, self.K, sel, n_sel,
                         x, y, stream)
 
+    def refine_topk(self, x, y, k, chunk=1024, sel_out=None, stream=None):
+        """Selection and add of StrataFlux Eq. 2 in one launch."""
+        L.wq_refine_topk(self.r_codes, self.r_scales, self.r_zeros, self.N, self.K, chunk, k, x, y,
+                         sel_out, stream)
+
     def dequant(self, W_hat, stream=None):
         L.wq_dequant_device(self.fmt, self.codes, self.scales, self.zeros, self.N, self.K, W_hat,
                             stream)

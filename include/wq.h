@@ -240,6 +240,19 @@ int wq_refine_add(const uint8_t* rcodes, const uint16_t* rscales, const uint16_t
                   int64_t N, int64_t K, const int32_t* sel, int64_t n_sel, const uint16_t* x,
                   uint16_t* y, void* stream);
 
+/* Selection and add in one launch: y += sum over S(x) of x_i C[:, i], with S(x)
+ * exactly as wq_topk_chunks makes it, and the sums in the same order as
+ * wq_topk_chunks followed by wq_refine_add (the two give identical y).  Every
+ * workgroup selects for itself from x, so the selection never goes through
+ * global memory; sel_out (int32, device, wq_topk_count(K, chunk, k) entries)
+ * receives S(x) if not NULL.  Holds at most 4096 selected channels (larger
+ * selections return WQ_ERR_UNSUPPORTED: use the two calls).  N % 32 == 0,
+ * chunk a multiple of 64 in [64, 1024], x 16-byte aligned; k == 0 does
+ * nothing. */
+int wq_refine_topk(const uint8_t* rcodes, const uint16_t* rscales, const uint16_t* rzeros,
+                   int64_t N, int64_t K, int64_t chunk, int64_t k, const uint16_t* x, uint16_t* y,
+                   int32_t* sel_out, void* stream);
+
 /* Standalone outlier correction (the add of SPECTRA section 4.1's outlier loop;
  * the same arithmetic as the column refinement add of the StrataFlux page,
  * section 3.2.1 Eq. 2, for a static column set):

@@ -408,3 +408,81 @@ def test_gemv_then_refine(fmt, N, K, k):
     # refinement moves the product toward the unquantized layer
     exact = L.W.astype(np.float64) @ x.astype(np.float64)
     assert np.abs(host_fp16(y) - exact).mean() < np.abs(y_base - exact).mean()
+
+
+@pytest.mark.parametrize("fmt", [4, 2])
+@pytest.mark.parametrize("N,K,chunk,k", [(14336 // 4, 4096, 1024, 32), (4096, 14336, 1024, 32),
+                                         (512, 2048, 1024, 8), (96, 1088, 1024, 100),
+                                         (64, 1024, 64, 64), (128, 4096, 1024, 1024)])
+def test_refine_topk_fused(fmt, N, K, chunk, k):
+    """One-launch selection + add: the same selection as wq_topk_chunks (copied
+    out) and bit-identical y to wq_topk_chunks followed by wq_refine_add."""
+    say(f"fused top-k refinement fmt={fmt} N={N} K={K} chunk={chunk} k={k}")
+    from bit_weight_only_gemv_amd.layer import refinement_host
+    L = synthetic.small_layer(fmt, N, K, with_outliers=True, seed=k + 1)
+    hl = pack_host(fmt, L.W, L.profile, L.ratio)
+    rf = refinement_host(L.W, hl)
+    dl = DeviceLayer(hl)
+    dl.set_refinement(rf)
+    x = L.x.reshape(-1)
+    y1, xd = run_gemv(dl, x)
+    y2 = y1.clone()
+    y_base = host_fp16(y1).astype(np.float64).copy()
+    n = B.wq_topk_count(K, chunk, k)
+    sel_out = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    dl.refine_topk(xd, y1, k, chunk, sel_out)
+    sel = torch.empty(n, dtype=torch.int32, device="cuda")
+    B.wq_topk_chunks(xd, K, chunk, k, sel)
+    dl.refine(xd, y2, sel, n)
+    torch.cuda.synchronize()
+    S = O.topk_chunks(x, k, chunk)
+    assert np.array_equal(sel_out.cpu().numpy(), S)
+    assert np.array_equal(y1.cpu().numpy(), y2.cpu().numpy())
+    rq, rs, rz = O.refinement_w4(L.W, O.quantize_layer(fmt, L.W, L.profile, L.ratio).w_hat(),
+                                 hl.idx)
+    y_ref, a = O.refine_ref(y_base.astype(np.float16), x, S, O.dequant_w4(rq, rs, rz))
+    ok, worst = O.check_tolerance(host_fp16(y1).astype(np.float64), y_ref, a)
+    say(f"  fused refine add: worst |err|/bound = {worst:.4f}")
+    assert ok
+
+
+def test_refine_topk_limits():
+    """More than 4096 selected channels is refused before any launch; k = 0 is a no-op."""
+    x = torch.zeros(8192, dtype=torch.int16, device="cuda")
+    y = torch.zeros(64, dtype=torch.int16, device="cuda")
+    c = torch.zeros(8192 * 32, dtype=torch.uint8, device="cuda")
+    m = torch.zeros(8192 * 2, dtype=torch.int16, device="cuda")
+    with pytest.raises(B.WQError):
+        B.wq_refine_topk(c, m, m, 64, 8192, 64, 64, x, y)
+    B.wq_refine_topk(c, m, m, 64, 8192, 1024, 0, x, y)
+    B.wq_refine_topk(c, m, m, 64, 8192, 1024, 32, x, y)   # 256 channels of x = 0: adds 0
+    torch.cuda.synchronize()
+    assert int(y.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("gpw", ["1", "2", "4"])
+@pytest.mark.parametrize("N,K", [(96, 2048), (14336 // 4, 4096), (4096, 14336 // 2)])
+def test_refine_groups_per_workgroup(gpw, N, K, monkeypatch):
+    """Workgroups of 1, 2 or 4 row groups (a ragged last workgroup included) sum
+    every group in the same order: the fused and two-call paths stay
+    bit-identical to each other and to the one-group default."""
+    say(f"refinement with {gpw} groups per workgroup N={N} K={K}")
+    from bit_weight_only_gemv_amd.layer import refinement_host
+    L = synthetic.small_layer(4, N, K, with_outliers=True, seed=3)
+    hl = pack_host(4, L.W, L.profile, L.ratio)
+    dl = DeviceLayer(hl)
+    dl.set_refinement(refinement_host(L.W, hl))
+    x = L.x.reshape(-1)
+    y0, xd = run_gemv(dl, x)
+    n = B.wq_topk_count(K, 1024, 32)
+    sel = torch.empty(n, dtype=torch.int32, device="cuda")
+    B.wq_topk_chunks(xd, K, 1024, 32, sel)
+    ya = y0.clone()
+    dl.refine(xd, ya, sel, n)                  # default grouping
+    monkeypatch.setenv("WQ_REFINE_GPW", gpw)
+    yb, yc = y0.clone(), y0.clone()
+    dl.refine(xd, yb, sel, n)
+    dl.refine_topk(xd, yc, 32)
+    torch.cuda.synchronize()
+    assert np.array_equal(ya.cpu().numpy(), yb.cpu().numpy())
+    assert np.array_equal(ya.cpu().numpy(), yc.cpu().numpy())

@@ -166,6 +166,12 @@ def test_error_codes():
     assert lib.wq_refine_add(fake, fake, fake, 48, 64, fake, 1, fake, fake, None) == -2
     assert lib.wq_refine_add(fake, fake, fake, 64, 64, fake, 65, fake, fake, None) == -1
     assert lib.wq_refine_add(None, None, None, 64, 64, None, 0, None, None, None) == 0
+    assert lib.wq_refine_topk(fake, fake, fake, 48, 64, 64, 1, fake, fake, None, None) == -2
+    assert lib.wq_refine_topk(fake, fake, fake, 64, 64, 32, 1, fake, fake, None, None) == -2
+    assert lib.wq_refine_topk(fake, fake, fake, 64, 8192, 64, 64, fake, fake, None, None) == -2
+    assert lib.wq_refine_topk(fake, fake, fake, 64, 64, 64, -1, fake, fake, None, None) == -1
+    assert lib.wq_refine_topk(None, None, None, 64, 64, 64, 0, None, None, None, None) == 0
+    assert lib.wq_refine_topk(fake, fake, fake, 64, 64, 64, 1, None, fake, None, None) == -1
 
 
 # ------------------------------------------------- W4P packed zero points
