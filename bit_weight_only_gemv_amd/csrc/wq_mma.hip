@@ -626,7 +626,8 @@ struct MmbArgs {
 };
 
 // LDS: W2 table; per wave two slice areas (outlier-column mask, 8 words, and
-// the run's column offsets, up to 256); partial tiles [rbl][nw][M][16].
+// the run's column offsets, up to 256); partial tiles [rbl][nw][Mp][16] with
+// Mp = M rounded up to the lane quarter's 4 rows (rows M..Mp-1 stay unread).
 constexpr uint32_t kMmbWaveArea = 32u + 1024u;
 struct MmbLds {
   uint32_t lut, wave, part, total;
@@ -639,7 +640,7 @@ __host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl
   L.wave = off;
   off += (uint32_t)nw * 2u * kMmbWaveArea;
   L.part = off;
-  off += (uint32_t)rbl * (uint32_t)nw * (uint32_t)M * 64u;
+  off += (uint32_t)rbl * (uint32_t)nw * (uint32_t)((M + 3) & ~3) * 64u;
   L.total = off;
   return L;
 }
@@ -910,17 +911,29 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     }
   };
 
+  // Each lane owns its entries of the partial tiles: they start at 0 and each
+  // slice's tile is added in program order (a fixed summation order); the four
+  // reads go out together, so an item waits for LDS once.
   float* s_part = reinterpret_cast<float*>(smem + L.part);
   const uint32_t lut_lane = (uint32_t)(lane & 31) * 8u;
-  auto add_tile = [&](const f4& c, int ri, int si) {
+  const uint32_t Mp = (uint32_t)((a.M + 3) & ~3);
+  const bool qrows = 4 * q < a.M;   // this lane quarter holds activation rows
+  auto part_at = [&](int ri, int jj) {
+    return s_part + (((uint32_t)ri * (uint32_t)a.nw + (uint32_t)w) * Mp + (uint32_t)(4 * q + jj)) *
+                        16u + (uint32_t)n16;
+  };
+  if (qrows)
+    for (int ri = 0; ri < nrb_wg; ++ri)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int m = 4 * q + jj;
-      if (m < a.M) {
-        float* p = s_part + (((uint32_t)ri * (uint32_t)a.nw + (uint32_t)w) * (uint32_t)a.M +
-                             (uint32_t)m) * 16u + (uint32_t)n16;
-        *p = si == 0 ? c[jj] : *p + c[jj];
-      }
+      for (int jj = 0; jj < 4; ++jj) *part_at(ri, jj) = 0.f;
+  auto add_tile = [&](const f4& c, int ri, int si) {
+    (void)si;
+    if (qrows) {
+      float old[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) old[jj] = *part_at(ri, jj);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) *part_at(ri, jj) = old[jj] + c[jj];
     }
   };
   auto compute = [&](const ItemB<FMT, OUT>& it, int ri, int si) {
@@ -939,12 +952,16 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         }
         const uint32_t d[4] = {it.cw[u].x, it.cw[u].y, it.cw[u].z, it.cw[u].w};
         uint32_t b[4][4];
+        // the FP16 exponent of 1024 held in a register, so that mask and OR
+        // fuse into one v_and_or_b32 (a VOP3 instruction takes no literal here)
+        uint32_t magic = 0x64006400u;
+        asm volatile("" : "+v"(magic));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t v0 = (d[i] & 0x000F000Fu) | 0x64006400u;
-          const uint32_t v1 = ((d[i] >> 4) & 0x000F000Fu) | 0x64006400u;
-          const uint32_t v2 = ((d[i] >> 8) & 0x000F000Fu) | 0x64006400u;
-          const uint32_t v3 = ((d[i] >> 12) & 0x000F000Fu) | 0x64006400u;
+          const uint32_t v0 = (d[i] & 0x000F000Fu) | magic;
+          const uint32_t v1 = ((d[i] >> 4) & 0x000F000Fu) | magic;
+          const uint32_t v2 = ((d[i] >> 8) & 0x000F000Fu) | magic;
+          const uint32_t v3 = ((d[i] >> 12) & 0x000F000Fu) | magic;
           const uint32_t vv[4] = {v0, v1, v2, v3};
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
@@ -1057,7 +1074,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     if (row >= a.N) continue;
     float s = 0.f;
     for (int k = 0; k < a.nw; ++k)
-      s += s_part[(((uint32_t)ri2 * a.nw + k) * (uint32_t)a.M + (uint32_t)m) * 16u + (uint32_t)n];
+      s += s_part[(((uint32_t)ri2 * a.nw + k) * Mp + (uint32_t)m) * 16u + (uint32_t)n];
     a.Y[(size_t)m * a.N + row] = f2h(s);
   }
 }
