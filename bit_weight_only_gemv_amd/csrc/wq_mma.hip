@@ -576,8 +576,8 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
 
 // ====================================================== batched (2 <= M <= 16)
 //
-// Same persistent layout (waves own K-slices, now of 256 channels; the
-// workgroup's row blocks stream through a ring), but A holds the M activation
+// Same persistent layout (waves own K-slices, here of 256 or 512 channels;
+// the workgroup's row blocks stream through a ring), but A holds the M activation
 // rows (rows M..15 zero) and B holds the dequantized weights themselves, so
 // each MFMA adds 16 rows x M activation rows x 32 channels into one tile:
 //   W4: w_hat = (q - z) s exactly: (1024 + q) - (1024 + z) in FP16 is the
@@ -585,32 +585,25 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
 //       to the dequantized weight itself;
 //   W2: w_hat = S C[q] + Z as one FP16 fused multiply-add of the table's
 //       centroids (one rounding).
-// Lane (n, q) reads bytes 32 q .. 32 q + 31 (W4) or 16 q .. 16 q + 15 (W2) of
-// row n's slice, i.e. the two consecutive groups 2q, 2q + 1 of the slice,
-// whose scales and zeros are one 4-byte load each.  The activation rows of the
+// Lane (n, q) reads the QG consecutive groups QG q .. QG q + QG - 1 of row n's
+// slice (W4: 16 QG bytes, W2: 8 QG bytes), whose scales and zeros are one
+// 2 QG-byte load each.  The activation rows of the
 // next slice are loaded one slice ahead.  W2 zeroes the outlier columns in the
 // activation fragments (W4 needs no mask: a column zeroed before
 // quantization decodes to exactly 0); the slice's run of the outlier slab is
 // one more MFMA per row block, against the gathered outlier activations.
 
-constexpr int kSliceChB = 256;
-constexpr int kSliceGroupsB = 8;
-
-template <int FMT>
-struct MmbFmt;
-template <>
-struct MmbFmt<4> {
-  static constexpr int kLoads = 2;
-  static constexpr int kSliceBytes = 128;
-  static constexpr int kRowBytesDiv = 2;
-};
-template <>
-struct MmbFmt<5> : MmbFmt<4> {};   // W4P: W4 codes, packed zero points
-template <>
-struct MmbFmt<2> {
-  static constexpr int kLoads = 1;
-  static constexpr int kSliceBytes = 64;
-  static constexpr int kRowBytesDiv = 4;
+// Slice geometry: QG groups of 32 channels per lane quarter, so a slice is
+// 128 QG channels (QG = 2: 256, QG = 4: 512).  W4 (and W4P) lanes read one
+// 16-byte load per group, W2 lanes one per two groups.
+template <int FMT, int QG>
+struct MmbFmt {
+  static constexpr int kSliceCh = 128 * QG;
+  static constexpr int kSliceGroups = 4 * QG;
+  static constexpr int kLoads = FMT == 2 ? QG / 2 : QG;
+  static constexpr int kSliceBytes = FMT == 2 ? 32 * QG : 64 * QG;
+  static constexpr int kRowBytesDiv = FMT == 2 ? 4 : 2;
+  static constexpr int kSteps = 4 * QG;   // MFMA steps (and x loads) per lane per slice
 };
 
 struct MmbArgs {
@@ -625,43 +618,48 @@ struct MmbArgs {
   int nw, nks, nrb, rbl;
 };
 
-// LDS: W2 table; per wave two slice areas (outlier-column mask, 8 words, and
-// the run's column offsets, up to 256); partial tiles [rbl][nw][Mp][16] with
-// Mp = M rounded up to the lane quarter's 4 rows (rows M..Mp-1 stay unread).
-constexpr uint32_t kMmbWaveArea = 32u + 1024u;
+// LDS: W2 table; per wave two slice areas (outlier-column mask, one bit per
+// channel of the slice, and the run's column offsets, up to one per channel);
+// partial tiles [rbl][nw][Mp][16] with Mp = M rounded up to the lane quarter's
+// 4 rows (rows M..Mp-1 stay unread).
+__host__ __device__ constexpr uint32_t mmb_wave_area(int qg) { return 16u * qg + 512u * qg; }
 struct MmbLds {
   uint32_t lut, wave, part, total;
 };
-__host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl) {
+__host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl, int qg) {
   MmbLds L{};
   uint32_t off = 0;
   L.lut = off;
   if (fmt == 2) off += 256u * kLutRow;
   L.wave = off;
-  off += (uint32_t)nw * 2u * kMmbWaveArea;
+  off += (uint32_t)nw * 2u * mmb_wave_area(qg);
   L.part = off;
   off += (uint32_t)rbl * (uint32_t)nw * (uint32_t)((M + 3) & ~3) * 64u;
   L.total = off;
   return L;
 }
 
-template <int FMT, bool OUT>
+template <int FMT, bool OUT, int QG>
 struct ItemB {
-  u4v cw[MmbFmt<FMT>::kLoads];
-  uint32_t sv, zv;
+  u4v cw[MmbFmt<FMT, QG>::kLoads];
+  u2 sv, zv;   // QG FP16 scales / zeros (W4P: QG packed nibbles in zv.x)
   uint32_t od[OUT ? 5 : 1];
 };
 
 __device__ __forceinline__ uint32_t splat_lo(uint32_t v) { return __builtin_amdgcn_perm(v, v, 0x01000100u); }
 __device__ __forceinline__ uint32_t splat_hi(uint32_t v) { return __builtin_amdgcn_perm(v, v, 0x03020302u); }
 
-template <int FMT, int IV, int DEPTH>
+template <int FMT, int IV, int DEPTH, int QG>
 __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
-  typedef MmbFmt<FMT> F;
+  typedef MmbFmt<FMT, QG> F;
+  constexpr int kSliceChB = F::kSliceCh;
+  constexpr int kSliceGroupsB = F::kSliceGroups;
+  constexpr int XS = F::kSteps;
+  constexpr uint32_t kMmbWaveArea = mmb_wave_area(QG);
   constexpr bool OUT = IV > 0;
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_out = OUT ? a.n_out : 0;
-  const MmbLds L = mmb_lds_layout(FMT, a.M, a.nw, a.rbl);
+  const MmbLds L = mmb_lds_layout(FMT, a.M, a.nw, a.rbl, QG);
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int lane = tid & 63;
@@ -699,18 +697,18 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
       oidx[v][3] = (int32_t)t.w;
     }
   }
-  // lane (m, q) of slice ks: W2 channels 256 ks + 64 q + 8 t (t < 8); W4 the
-  // two groups 8 ks + 2 q + u, 32 channels each; past K they read 0 (fixed up
-  // when the fragments are built)
-  auto x_load = [&](int ks, u4v (&xv)[8]) {
+  // lane (m, q) of slice ks: channels 128 QG ks + 32 QG q + 8 t (t < 4 QG),
+  // i.e. the QG groups 4 QG ks + QG q + u, 32 channels each; past K they read
+  // 0 (fixed up when the fragments are built)
+  auto x_load = [&](int ks, u4v (&xv)[XS]) {
     const uint32_t rowoff = (uint32_t)n16 * (uint32_t)a.K;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t c = (uint32_t)(ks * kSliceChB + 64 * q + 8 * t);
+    for (int t = 0; t < XS; ++t) {
+      const uint32_t c = (uint32_t)(ks * kSliceChB + 32 * QG * q + 8 * t);
       xv[t] = ld128(xrs, (rowoff + c) * 2u);
     }
   };
-  u4v xpre[8];
+  u4v xpre[XS];
   x_load(w, xpre);
   asm volatile("" ::: "memory");   // these loads stay ahead of the weight stream
 
@@ -731,7 +729,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   };
 
   // ---- (1) the ring
-  auto load_main = [&](ItemB<FMT, OUT>& it, bool valid, int ks, int rb) {
+  auto load_main = [&](ItemB<FMT, OUT, QG>& it, bool valid, int ks, int rb) {
     const __amdgpu_buffer_rsrc_t c_ = valid ? crs : nul;
     const __amdgpu_buffer_rsrc_t s_ = valid ? srs : nul;
     const __amdgpu_buffer_rsrc_t z_ = valid ? zrs : nul;
@@ -739,14 +737,21 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     const uint32_t rbase = row * row_bytes + (uint32_t)(ks * F::kSliceBytes + 16 * F::kLoads * q);
 #pragma unroll
     for (int u = 0; u < F::kLoads; ++u) it.cw[u] = ld128(c_, rbase + 16u * u);
-    const uint32_t mo = (row * (uint32_t)G + (uint32_t)(ks * kSliceGroupsB + 2 * q)) * 2u;
-    it.sv = ld32(s_, mo);
-    if constexpr (FMT == 5)   // groups 8 ks + 2 q, + 1: one byte of the packed row
-      it.zv = ld8(z_, row * (uint32_t)(G / 2) + (uint32_t)(4 * ks + q));
+    const uint32_t mo = (row * (uint32_t)G + (uint32_t)(ks * kSliceGroupsB + QG * q)) * 2u;
+    if constexpr (QG == 4)
+      it.sv = ld64(s_, mo);
     else
-      it.zv = ld32(z_, mo);
+      it.sv = (u2){ld32(s_, mo), 0u};
+    if constexpr (FMT == 5) {   // the QG groups' nibbles: QG / 2 bytes of the packed row
+      const uint32_t zo = row * (uint32_t)(G / 2) + (uint32_t)((kSliceGroupsB * ks + QG * q) / 2);
+      it.zv = (u2){QG == 4 ? (uint32_t)ld16(z_, zo) : (uint32_t)ld8(z_, zo), 0u};
+    } else if constexpr (QG == 4) {
+      it.zv = ld64(z_, mo);
+    } else {
+      it.zv = (u2){ld32(z_, mo), 0u};
+    }
   };
-  auto load_slab = [&](ItemB<FMT, OUT>& it, bool valid, int ks, int rb) {
+  auto load_slab = [&](ItemB<FMT, OUT, QG>& it, bool valid, int ks, int rb) {
     if constexpr (OUT) {
       int j_lo, nin;
       jrange(ks, j_lo, nin);
@@ -765,7 +770,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
       ++s_;
     }
   };
-  ItemB<FMT, OUT> buf[DEPTH];
+  ItemB<FMT, OUT, QG> buf[DEPTH];
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
     load_main(buf[d], d < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
@@ -806,11 +811,12 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   auto prep_slice = [&](int ks, int p) {
     if constexpr (OUT) {
       uint32_t* mask = reinterpret_cast<uint32_t*>(smem + warea0 + (uint32_t)p * kMmbWaveArea);
-      int32_t* list = reinterpret_cast<int32_t*>(smem + warea0 + (uint32_t)p * kMmbWaveArea + 32u);
+      int32_t* list =
+          reinterpret_cast<int32_t*>(smem + warea0 + (uint32_t)p * kMmbWaveArea + 16u * QG);
       int j_lo, nin;
       jrange(ks, j_lo, nin);
       const int lo = ks * kSliceChB;
-      if (lane < 8) mask[lane] = 0u;
+      if (lane < 4 * QG) mask[lane] = 0u;
       for (int j = lane; j < 32; j += kWave) list[j] = -1;   // first run step padded
 #pragma unroll
       for (int v = 0; v < IV; ++v)
@@ -831,7 +837,8 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {   // every lane loads (a valid column when idle)
         const bool ok = 8 * q + e < nin && cl[e] >= 0;
-        const uint32_t col = (uint32_t)(lo + __builtin_amdgcn_ubfe(ok ? cl[e] : 0, 0, 8));
+        const uint32_t col =
+            (uint32_t)(lo + __builtin_amdgcn_ubfe(ok ? cl[e] : 0, 0, QG == 4 ? 9 : 8));
         const uint32_t v = ld16(xrs, ((uint32_t)n16 * (uint32_t)a.K + col) * 2u);
         hv[e] = ok ? v : 0u;
       }
@@ -841,18 +848,18 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   };
   prep_slice(w, 0);
 
-  h8 afr[8];
+  h8 afr[XS];
   uint32_t xo[4] = {0u, 0u, 0u, 0u};
   int cur_jlo = 0, cur_nin = 0;
   auto enter_slice = [&](int s) {
     const int ks = w + a.nw * s;
     const int p = s & 1;
     // fragments of this slice from the prefetched rows (channels past K: 0)
-    uint32_t fr[8][4];
+    uint32_t fr[XS][4];
     if constexpr (FMT == 2) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const bool ok = ks * kSliceChB + 64 * q + 8 * t < a.K;
+      for (int t = 0; t < XS; ++t) {
+        const bool ok = ks * kSliceChB + 32 * QG * q + 8 * t < a.K;
         fr[t][0] = ok ? xpre[t].x : 0u;
         fr[t][1] = ok ? xpre[t].y : 0u;
         fr[t][2] = ok ? xpre[t].z : 0u;
@@ -862,10 +869,12 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         // zero the outlier columns: bits 2i, 2i + 1 of step t's byte
         const uint32_t* mask =
             reinterpret_cast<const uint32_t*>(smem + warea0 + (uint32_t)p * kMmbWaveArea);
-        const uint32_t m0 = mask[2 * q], m1 = mask[2 * q + 1];
+        uint32_t mw[QG];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const uint32_t byte = ((t < 4 ? m0 : m1) >> (8 * (t & 3))) & 0xFFu;
+        for (int i = 0; i < QG; ++i) mw[i] = mask[QG * q + i];
+#pragma unroll
+        for (int t = 0; t < XS; ++t) {
+          const uint32_t byte = (mw[t >> 2] >> (8 * (t & 3))) & 0xFFu;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint32_t b2 = (byte >> (2 * i)) & 3u;
@@ -876,8 +885,8 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bool ok = ks * kSliceGroupsB + 2 * q + u < G;
+      for (int u = 0; u < QG; ++u) {
+        const bool ok = ks * kSliceGroupsB + QG * q + u < G;
         uint32_t gv[16];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -899,7 +908,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
       }
     }
 #pragma unroll
-    for (int f = 0; f < 8; ++f)
+    for (int f = 0; f < XS; ++f)
       afr[f] = __builtin_bit_cast(h8, (u4v){fr[f][0], fr[f][1], fr[f][2], fr[f][3]});
 #pragma unroll
     for (int i = 0; i < 4; ++i) xo[i] = xopre[i];
@@ -936,18 +945,19 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
       for (int jj = 0; jj < 4; ++jj) *part_at(ri, jj) = old[jj] + c[jj];
     }
   };
-  auto compute = [&](const ItemB<FMT, OUT>& it, int ri, int si) {
+  auto compute = [&](const ItemB<FMT, OUT, QG>& it, int ri, int si) {
     f4 c = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t svw[2] = {it.sv.x, it.sv.y}, zvw[2] = {it.zv.x, it.zv.y};
     if constexpr (FMT != 2) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint32_t sp = u ? splat_hi(it.sv) : splat_lo(it.sv);
+      for (int u = 0; u < QG; ++u) {
+        const uint32_t sp = (u & 1) ? splat_hi(svw[u >> 1]) : splat_lo(svw[u >> 1]);
         // -(1024 + z) in both halves: the zero is an exact small integer
         uint32_t nz;
         if constexpr (FMT == 5) {   // FP16 -(1024 + z) = 0xE400 | z for z in 0..15
-          nz = splat_lo(0xE400u | ((it.zv >> (4 * u)) & 0x0Fu));
+          nz = splat_lo(0xE400u | ((zvw[0] >> (4 * u)) & 0x0Fu));
         } else {
-          const _Float16 zf = __builtin_bit_cast(_Float16, (uint16_t)(it.zv >> (16 * u)));
+          const _Float16 zf = __builtin_bit_cast(_Float16, (uint16_t)(zvw[u >> 1] >> (16 * (u & 1))));
           nz = splat_lo((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(-1024.0f16 - zf)));
         }
         const uint32_t d[4] = {it.cw[u].x, it.cw[u].y, it.cw[u].z, it.cw[u].w};
@@ -976,28 +986,32 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
               0, 0, 0);
       }
     } else {
-      const uint32_t sp[2] = {splat_lo(it.sv), splat_hi(it.sv)};
-      const uint32_t zp[2] = {splat_lo(it.zv), splat_hi(it.zv)};
-      const uint32_t d[4] = {it.cw[0].x, it.cw[0].y, it.cw[0].z, it.cw[0].w};
-      u2 lv[16];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t word = d[t >> 1];
-        const uint32_t bsel = (uint32_t)(2 * (t & 1));
-        lv[2 * t] = lds_ld64(L.lut + __builtin_amdgcn_perm(word, lut_lane, 0x0C0C0400u + (bsel << 8)));
-        lv[2 * t + 1] =
-            lds_ld64(L.lut + __builtin_amdgcn_perm(word, lut_lane, 0x0C0C0500u + (bsel << 8)));
-      }
+      for (int uu = 0; uu < F::kLoads; ++uu) {   // one load: 64 codes, two groups
+        const uint32_t sp[2] = {splat_lo(svw[uu]), splat_hi(svw[uu])};
+        const uint32_t zp[2] = {splat_lo(zvw[uu]), splat_hi(zvw[uu])};
+        const uint32_t d[4] = {it.cw[uu].x, it.cw[uu].y, it.cw[uu].z, it.cw[uu].w};
+        u2 lv[16];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int g = t >> 2;
-        const uint32_t cv[4] = {lv[2 * t].x, lv[2 * t].y, lv[2 * t + 1].x, lv[2 * t + 1].y};
-        uint32_t b[4];
+        for (int t = 0; t < 8; ++t) {
+          const uint32_t word = d[t >> 1];
+          const uint32_t bsel = (uint32_t)(2 * (t & 1));
+          lv[2 * t] =
+              lds_ld64(L.lut + __builtin_amdgcn_perm(word, lut_lane, 0x0C0C0400u + (bsel << 8)));
+          lv[2 * t + 1] =
+              lds_ld64(L.lut + __builtin_amdgcn_perm(word, lut_lane, 0x0C0C0500u + (bsel << 8)));
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          b[i] = as_u32(__builtin_elementwise_fma(as_h2(cv[i]), as_h2(sp[g]), as_h2(zp[g])));
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            afr[t], __builtin_bit_cast(h8, (u4v){b[0], b[1], b[2], b[3]}), c, 0, 0, 0);
+        for (int t = 0; t < 8; ++t) {
+          const int g = t >> 2;
+          const uint32_t cv[4] = {lv[2 * t].x, lv[2 * t].y, lv[2 * t + 1].x, lv[2 * t + 1].y};
+          uint32_t b[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            b[i] = as_u32(__builtin_elementwise_fma(as_h2(cv[i]), as_h2(sp[g]), as_h2(zp[g])));
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              afr[8 * uu + t], __builtin_bit_cast(h8, (u4v){b[0], b[1], b[2], b[3]}), c, 0, 0, 0);
+        }
       }
     }
     if constexpr (OUT) {
@@ -1142,7 +1156,7 @@ static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_ou
 
 struct MmbPlan {
   bool ok;
-  int nw, nks, nrb, grid, rbl, iv, depth;
+  int nw, nks, nrb, grid, rbl, iv, depth, qg;
   size_t lds;
 };
 
@@ -1153,7 +1167,15 @@ static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M)
   if (N * row_bytes > 0xFFFFFFF0ll || N * (K / 32) * 2 > 0xFFFFFFF0ll ||
       N * n_out * 2 > 0xFFFFFFF0ll || M * K * 2 > 0xFFFFFFF0ll)
     return p;
-  p.nks = (int)((K + kSliceChB - 1) / kSliceChB);
+  // 512-channel slices (QG = 4) halve the items and slice changes of layers up
+  // to K = 8192 without outliers (measured faster there); longer rows, and the
+  // outlier variants (whose registers would spill at QG = 4), keep 256.
+  // WQ_MMB_QG=2|4 overrides the choice for the variants without outliers.
+  p.qg = n_out == 0 && K <= 8192 ? 4 : 2;
+  if (const char* e = getenv("WQ_MMB_QG"))
+    if (n_out == 0) p.qg = atoi(e) == 4 ? 4 : 2;
+  const int slice_ch = 128 * p.qg;
+  p.nks = (int)((K + slice_ch - 1) / slice_ch);
   if (p.nks <= kMaxWaves) {
     p.nw = p.nks;
   } else {
@@ -1172,7 +1194,7 @@ static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M)
   p.grid = std::min(p.nrb, cus);
   p.rbl = (p.nrb + p.grid - 1) / p.grid;
   p.iv = n_out == 0 ? 0 : n_out <= 256 ? 1 : n_out <= 512 ? 2 : 4;
-  p.lds = mmb_lds_layout(fmt, (int)M, p.nw, p.rbl).total;
+  p.lds = mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg).total;
   if (p.lds > kMaxLdsBytes) return p;
   p.depth = 2;
   p.ok = true;
@@ -1262,17 +1284,20 @@ int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
   a.nrb = p.nrb;
   a.rbl = p.rbl;
   const dim3 grid(p.grid), block(p.nw * kWave);
-#define WQ_MMB_LAUNCH(F_, IV_)                                                               \
-  if (fmt == F_ && p.iv == IV_) {                                                            \
-    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2>), p.lds))          \
+#define WQ_MMB_LAUNCH_Q(F_, IV_, Q_)                                                         \
+  if (fmt == F_ && p.iv == IV_ && p.qg == Q_) {                                              \
+    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, Q_>), p.lds))      \
       return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds); \
-    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2>), grid, block, p.lds, stream, a);             \
+    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, Q_>), grid, block, p.lds, stream, a);         \
     *launched = true;                                                                        \
     return check_launch(who);                                                                \
   }
+#define WQ_MMB_LAUNCH(F_, IV_) WQ_MMB_LAUNCH_Q(F_, IV_, 2)
+  WQ_MMB_LAUNCH_Q(4, 0, 4) WQ_MMB_LAUNCH_Q(2, 0, 4) WQ_MMB_LAUNCH_Q(5, 0, 4)
   WQ_MMB_LAUNCH(4, 0) WQ_MMB_LAUNCH(4, 1) WQ_MMB_LAUNCH(4, 2) WQ_MMB_LAUNCH(4, 4)
   WQ_MMB_LAUNCH(2, 0) WQ_MMB_LAUNCH(2, 1) WQ_MMB_LAUNCH(2, 2) WQ_MMB_LAUNCH(2, 4)
   WQ_MMB_LAUNCH(5, 0) WQ_MMB_LAUNCH(5, 1) WQ_MMB_LAUNCH(5, 2) WQ_MMB_LAUNCH(5, 4)
+#undef WQ_MMB_LAUNCH_Q
 #undef WQ_MMB_LAUNCH
   return WQ_OK;
 }

@@ -259,6 +259,26 @@ def test_gemm_small(fmt, M, N, K, outl, gemm_path):
     check_product(ref, Y, L.x, f"gemm w{fmt} M={M} {N}x{K} n_out={ref.n_out}")
 
 
+@pytest.mark.parametrize("qg", ["2", "4"])
+@pytest.mark.parametrize("fmt", [4, 2, 5])
+@pytest.mark.parametrize("M", [2, 5, 16])
+@pytest.mark.parametrize("N,K", [(129, 4096), (300, 8192), (5000, 4224), (64, 2176), (48, 384)])
+def test_gemm_slice_widths(fmt, M, N, K, qg, monkeypatch):
+    """The matrix-core batched kernel with 256- and 512-channel slices (no
+    outliers), including a short last slice (K % 512 = 128) and K below one
+    slice."""
+    monkeypatch.setenv("WQ_GEMM_MMA", "1")
+    monkeypatch.setenv("WQ_MMB_QG", qg)
+    say(f"gemm slices of {128 * int(qg)} fmt={fmt} M={M} N={N} K={K}")
+    L = synthetic.small_layer(fmt, N, K, M=M, seed=M + N)
+    ref, dl = build(fmt, L.W)
+    X = dev_fp16(L.x)
+    Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
+    dl.gemm(X, Y)
+    torch.cuda.synchronize()
+    check_product(ref, Y, L.x, f"gemm w{fmt} M={M} {N}x{K} slices {128 * int(qg)}")
+
+
 # ------------------------------------------------------- full-size layers
 
 
