@@ -115,6 +115,14 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Orders one wave's own LDS traffic: a wave's LDS operations complete in
+// order, and this keeps the compiler from moving them across the point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ------------------------------------------------------------ reductions
 // Sum over each row of 16 lanes with DPP; every lane of the row ends up with
 // the row's sum.

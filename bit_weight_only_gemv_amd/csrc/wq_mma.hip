@@ -624,15 +624,22 @@ struct MmbArgs {
 // 4 rows (rows M..Mp-1 stay unread).
 __host__ __device__ constexpr uint32_t mmb_wave_area(int qg) { return 16u * qg + 512u * qg; }
 struct MmbLds {
-  uint32_t lut, wave, part, total;
+  uint32_t lut, wave, runs, idx, part, total;
 };
-__host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl, int qg) {
+// With outliers also: the run table (slice ks's run of the sorted indices
+// starts at runs[ks], nks + 1 words) and a copy of the indices (256 iv words).
+__host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl, int qg, int nks,
+                                                 int iv) {
   MmbLds L{};
   uint32_t off = 0;
   L.lut = off;
   if (fmt == 2) off += 256u * kLutRow;
   L.wave = off;
   off += (uint32_t)nw * 2u * mmb_wave_area(qg);
+  L.runs = off;
+  if (iv > 0) off += ((uint32_t)(nks + 1) * 4u + 15u) & ~15u;
+  L.idx = off;
+  off += (uint32_t)iv * 1024u;
   L.part = off;
   off += (uint32_t)rbl * (uint32_t)nw * (uint32_t)((M + 3) & ~3) * 64u;
   L.total = off;
@@ -659,7 +666,9 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   constexpr bool OUT = IV > 0;
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_out = OUT ? a.n_out : 0;
-  const MmbLds L = mmb_lds_layout(FMT, a.M, a.nw, a.rbl, QG);
+  const MmbLds L = mmb_lds_layout(FMT, a.M, a.nw, a.rbl, QG, a.nks, IV);
+  uint32_t* s_runs = reinterpret_cast<uint32_t*>(smem + L.runs);
+  const int32_t* s_idx = reinterpret_cast<const int32_t*>(smem + L.idx);
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int lane = tid & 63;
@@ -684,13 +693,14 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.X, clamp_bytes((uint64_t)a.M * a.K * 2));
   const __amdgpu_buffer_rsrc_t nul = make_rsrc(a.codes, 0u);
 
-  // ---- (0) outlier indices (lane l holds idx[256 v + 4 l + k]), then the
-  //      activation rows of this wave's first slice
+  // ---- (0) outlier indices (wave 0: lane l holds idx[256 v + 4 l + k]; they
+  //      become the run table below), then the activation rows of this
+  //      wave's first slice
   int32_t oidx[IV > 0 ? IV : 1][4];
   if constexpr (OUT) {
 #pragma unroll
     for (int v = 0; v < IV; ++v) {
-      const u4v t = ld128(irs, (uint32_t)(256 * v + 4 * lane) * 4u);
+      const u4v t = ld128(w == 0 ? irs : nul, (uint32_t)(256 * v + 4 * lane) * 4u);
       oidx[v][0] = (int32_t)t.x;
       oidx[v][1] = (int32_t)t.y;
       oidx[v][2] = (int32_t)t.z;
@@ -712,19 +722,13 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   x_load(w, xpre);
   asm volatile("" ::: "memory");   // these loads stay ahead of the weight stream
 
+  // slice ks's run of the sorted indices: positions j_lo .. j_lo + nin - 1
   auto jrange = [&](int ks, int& j_lo, int& nin) {
     j_lo = 0;
     nin = 0;
     if constexpr (OUT) {
-      const int lo = ks * kSliceChB, hi = lo + kSliceChB;
-#pragma unroll
-      for (int v = 0; v < IV; ++v)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int c = oidx[v][k];
-          j_lo += __builtin_popcountll(__ballot(c < lo));
-          nin += __builtin_popcountll(__ballot(c >= lo && c < hi));
-        }
+      j_lo = (int)s_runs[ks];
+      nin = (int)s_runs[ks + 1] - j_lo;
     }
   };
 
@@ -786,14 +790,49 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     }
   }
   if constexpr (OUT) {
+    // the run table, built once per workgroup by wave 0: counts per slice,
+    // then their prefix sums (the indices are sorted, so slice ks's run starts
+    // at the number of indices below 128 QG ks); and the indices into LDS
+    if (w == 0) {
+      for (int t = lane; t <= a.nks; t += kWave) s_runs[t] = 0u;
+      wave_lds_sync();
 #pragma unroll
-    for (int v = 0; v < IV; ++v)
+      for (int v = 0; v < IV; ++v) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        asm volatile("" : "+v"(oidx[v][k])::"memory");
-        const uint32_t j = (uint32_t)(256 * v + 4 * lane + k);
-        if (j >= (uint32_t)n_out) oidx[v][k] = 0x7FFFFFFF;
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t j = (uint32_t)(256 * v + 4 * lane + k);
+          const int c = oidx[v][k];
+          if (j < (uint32_t)n_out && c >= 0 && c < a.K) atomicAdd(&s_runs[c / kSliceChB + 1], 1u);
+        }
+        reinterpret_cast<u4v*>(smem + L.idx)[64 * v + lane] =
+            (u4v){(uint32_t)oidx[v][0], (uint32_t)oidx[v][1], (uint32_t)oidx[v][2],
+                  (uint32_t)oidx[v][3]};
       }
+      wave_lds_sync();
+      // inclusive prefix sums over runs[0 .. nks] (at most 257 words): lane l
+      // takes words 5l .. 5l + 4, then the lanes' totals are scanned
+      uint32_t v5[5], tot = 0u;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int t = 5 * lane + i;
+        v5[i] = t <= a.nks ? s_runs[t] : 0u;
+        tot += v5[i];
+        v5[i] = tot;
+      }
+      uint32_t incl = tot;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t u = __shfl_up(incl, d);
+        if (lane >= d) incl += u;
+      }
+      const uint32_t before = incl - tot;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int t = 5 * lane + i;
+        if (t <= a.nks) s_runs[t] = before + v5[i];
+      }
+    }
+    lds_barrier();   // the run table and the index copy, visible to every wave
   }
   {
     int s2 = 0, r2 = 0;
@@ -818,17 +857,14 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
       const int lo = ks * kSliceChB;
       if (lane < 4 * QG) mask[lane] = 0u;
       for (int j = lane; j < 32; j += kWave) list[j] = -1;   // first run step padded
-#pragma unroll
-      for (int v = 0; v < IV; ++v)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int c = oidx[v][k] - lo;
-          if (c >= 0 && c < kSliceChB) {
-            __hip_atomic_fetch_or(&mask[c >> 5], 1u << (c & 31), __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_WORKGROUP);
-            list[256 * v + 4 * lane + k - j_lo] = c;
-          }
+      for (int j = lane; j < nin; j += kWave) {
+        const int c = s_idx[j_lo + j] - lo;   // in [0, slice) for sorted indices
+        if ((unsigned)c < (unsigned)kSliceChB) {
+          __hip_atomic_fetch_or(&mask[c >> 5], 1u << (c & 31), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_WORKGROUP);
+          list[j] = c;
         }
+      }
       // outlier activations of the first 32 columns of the run: X[m][lo + c]
       const int4 l0 = *reinterpret_cast<const int4*>(list + 8 * q);
       const int4 l1 = *reinterpret_cast<const int4*>(list + 8 * q + 4);
@@ -1055,7 +1091,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         for (int e = 0; e < 8; ++e) {
           const int j = j_lo + c0 + 8 * q + e;
           const bool ok = c0 + 8 * q + e < nin;
-          const int col = ok ? (int)ld32(irs, (uint32_t)j * 4u) : 0;
+          const int col = ok ? s_idx[j] : 0;
           hv[e] = ok ? (uint32_t)ld16(xrs, ((uint32_t)n16 * (uint32_t)a.K + (uint32_t)col) * 2u) : 0u;
         }
         const u4v xv = {hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
@@ -1194,7 +1230,7 @@ static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M)
   p.grid = std::min(p.nrb, cus);
   p.rbl = (p.nrb + p.grid - 1) / p.grid;
   p.iv = n_out == 0 ? 0 : n_out <= 256 ? 1 : n_out <= 512 ? 2 : 4;
-  p.lds = mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg).total;
+  p.lds = mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv).total;
   if (p.lds > kMaxLdsBytes) return p;
   p.depth = 2;
   p.ok = true;

@@ -45,12 +45,6 @@ constexpr int kRefineUnroll = 4;              // columns per slot with loads in 
 constexpr int kRefineRuns = kRefineThreads / kGroup;   // 16 runs of 8 slots in the sum
 constexpr int kFusedMaxSel = 4096;            // selections the fused kernel holds in LDS
 
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
@@ -106,12 +100,12 @@ __device__ __forceinline__ void wave_chunk_topk(__amdgpu_buffer_rsrc_t xrs, int 
     h1[lane + kWave] = 0u;
 #pragma unroll
     for (int i = 0; i < kSelBins2 / kWave; ++i) h2[lane + kWave * i] = 0u;
-    wave_sync();
+    wave_lds_sync();
     if (valid) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) atomicAdd(&h1[m[e] >> 8], 1u);
     }
-    wave_sync();
+    wave_lds_sync();
     {
       // lane l holds bins 2l (lower) and 2l + 1 (higher); exactly one bin holds
       // the kk-th largest (1 <= kk < number of valid channels)
@@ -129,7 +123,7 @@ __device__ __forceinline__ void wave_chunk_topk(__amdgpu_buffer_rsrc_t xrs, int 
         st[1] = rem - above - hi;
       }
     }
-    wave_sync();
+    wave_lds_sync();
     const uint32_t b1 = st[0];
     const uint32_t rem = st[1];
     if (valid) {
@@ -137,7 +131,7 @@ __device__ __forceinline__ void wave_chunk_topk(__amdgpu_buffer_rsrc_t xrs, int 
       for (int e = 0; e < 16; ++e)
         if ((m[e] >> 8) == b1) atomicAdd(&h2[m[e] & 0xFFu], 1u);
     }
-    wave_sync();
+    wave_lds_sync();
     {
       uint32_t hb[4], sum = 0u;
 #pragma unroll
@@ -157,7 +151,7 @@ __device__ __forceinline__ void wave_chunk_topk(__amdgpu_buffer_rsrc_t xrs, int 
         cum += hb[i];
       }
     }
-    wave_sync();
+    wave_lds_sync();
     T = st[2];
     keq = st[3];
   }
