@@ -164,6 +164,19 @@ def traffic_for(label):
     return e.get("hbm_bytes_per_launch")
 
 
+def read_probe_rate(torch, timer, nbytes, steps, warmup):
+    """Attainable streaming-read rate at this many bytes per launch: the plain
+    read kernel over rotated buffers, timed like the GEMV (GB/s)."""
+    import bit_weight_only_gemv_amd as B
+    nb = (nbytes + 15) // 16 * 16
+    ncopy = max(1, -(-ROTATE_BYTES // nb))
+    bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
+    sink = torch.empty(B.wq_read_probe_sink_words(nb), dtype=torch.int32, device="cuda")
+    ms = timer(lambda i: B.wq_read_probe(bufs[i % ncopy], nb, sink), steps, warmup)
+    del bufs
+    return nb / (ms * 1e-3) / 1e9
+
+
 def gemv_workload(a, torch, L, label, timer):
     import bit_weight_only_gemv_amd as B
     from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
@@ -192,6 +205,8 @@ def gemv_workload(a, torch, L, label, timer):
     gbs = nbytes / (ms * 1e-3) / 1e9
     bpt = sweep_bytes_per_token(L.fmt, L.ratio)
     traffic = traffic_for(f"{label}_{layout}")
+    del layers
+    probe = read_probe_rate(torch, timer, nbytes, a.steps, a.warmup)
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -211,6 +226,10 @@ def gemv_workload(a, torch, L, label, timer):
                    "bytes_per_step": nbytes, "rotated_copies": ncopy, "layout": layout,
                    "timing": "eager launches" if a.eager else "hip graph replay"},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "attainable": {"read_probe_GB/s": round(probe, 1),
+                       "pct_of_read_probe": round(100 * gbs / probe, 2),
+                       "about": "a plain streaming read of the same bytes per launch, rotated "
+                                "and graph-replayed in the same run"},
         "eq_tokens_per_s": round(gbs * 1e9 / bpt, 1),
         "eq_tokens_basis_bytes_per_token": bpt,
         "host_pack_s": round(pack_s, 2),
@@ -535,15 +554,29 @@ def cpu_baseline(L, nbytes):
     except Exception:
         blas_threads = 1
     ref = O.quantize_layer(L.fmt, L.W, L.profile, L.ratio)
-    times = []
+    times, t_deq, t_mv = [], [], []
     for _ in range(3):
         t0 = time.perf_counter()
         w_hat = ref.w_hat()
+        t1 = time.perf_counter()
         O.matvec_ref(w_hat, L.x, ref.idx, ref.wout)
-        times.append(time.perf_counter() - t0)
+        t2 = time.perf_counter()
+        times.append(t2 - t0)
+        t_deq.append(t1 - t0)
+        t_mv.append(t2 - t1)
     t = float(np.median(times))
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                       "unknown")
+    except OSError:
+        pass
     return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
             "kind": "oracle",
+            "dequant_s": round(float(np.median(t_deq)), 3),
+            "matvec_s": round(float(np.median(t_mv)), 3),
+            "cpu_model": cpu,
             "sample": (f"the whole {ref.N}x{ref.K} layer: oracle dequantization + float64 product, "
                        f"median of 3 runs ({t:.2f} s each); numpy elementwise work is single-threaded, "
                        f"the BLAS product used {blas_threads} threads of "
