@@ -506,3 +506,60 @@ def test_refine_groups_per_workgroup(gpw, N, K, monkeypatch):
     torch.cuda.synchronize()
     assert np.array_equal(ya.cpu().numpy(), yb.cpu().numpy())
     assert np.array_equal(ya.cpu().numpy(), yc.cpu().numpy())
+
+
+# ------------------------------------------- degenerate values and boundaries
+
+
+def _special_layer(fmt, N, K, seed):
+    """Weights with constant groups (the scale floor flushes to FP16 0), all-zero
+    rows, groups of a huge range next to tiny ones; activations with exact
+    zeros, negative zeros and FP16 subnormals; outlier columns at 0, K - 1 and
+    on both sides of 32-, 256- and 512-channel boundaries."""
+    rng = np.random.default_rng(seed)
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    W[1, :] = 0.0
+    W[2, 64:96] = 0.37                       # one constant group
+    W[3, :] = -1.25                          # constant row
+    W[4, 128:160] *= 1e4                     # a huge-range group
+    W[5, 160:192] *= 1e-6                    # a tiny one
+    x = rng.standard_normal(K).astype(np.float16)
+    x[::7] = 0.0
+    x[3::11] = np.float16(-0.0)
+    x[5::13] = np.float16(2.0 ** -20)        # subnormal
+    x[6::17] = np.float16(-(2.0 ** -24))     # smallest subnormal
+    cols = np.array(sorted({0, 31, 32, 255, 256, 511, 512, 513, K - 1}), np.int64)
+    profile = np.full(K, 1e-9)
+    profile[cols] = 1e9
+    ratio = (len(cols) + 0.5) / K
+    return W, x, profile, ratio, cols
+
+
+@pytest.mark.parametrize("fmt", [4, 2, 5])
+@pytest.mark.parametrize("N,K", [(48, 1024), (160, 4096)])
+def test_special_values_and_boundary_outliers(fmt, N, K, monkeypatch):
+    say(f"special values fmt={fmt} N={N} K={K}")
+    W, x, profile, ratio, cols = _special_layer(fmt, N, K, seed=N + K)
+    ref = O.quantize_layer(fmt, W, profile, ratio)
+    assert np.array_equal(ref.idx, cols)
+    hl = pack_host(fmt, W, profile, ratio)
+    assert np.array_equal(hl.codes, ref.codes) and np.array_equal(hl.idx, ref.idx)
+    dl = DeviceLayer(hl, tiled=True)
+    # bit-exact dequantization, constant and zero groups included
+    out = torch.empty((N, K), dtype=torch.int16, device="cuda")
+    dl.dequant(out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16),
+                          np.asarray(ref.w_hat(), np.float16).view(np.uint16))
+    for mode in ("0", "2"):
+        monkeypatch.setenv("WQ_GEMV_MMA", mode)
+        y, _ = run_gemv(dl, x)
+        check_product(ref, y, x, f"special w{fmt} gemv mode {mode}")
+    check_product(ref, run_gemv_tiled(dl, x), x, f"special w{fmt} tiled")
+    X = np.stack([x, -x, x[::-1].copy()])
+    for mode in ("0", "1"):
+        monkeypatch.setenv("WQ_GEMM_MMA", mode)
+        Y = torch.full((3, N), -1, dtype=torch.int16, device="cuda")
+        dl.gemm(dev_fp16(X), Y)
+        torch.cuda.synchronize()
+        check_product(ref, Y, X, f"special w{fmt} gemm M=3 mode {mode}")
