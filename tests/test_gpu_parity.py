@@ -563,3 +563,20 @@ def test_special_values_and_boundary_outliers(fmt, N, K, monkeypatch):
         dl.gemm(dev_fp16(X), Y)
         torch.cuda.synchronize()
         check_product(ref, Y, X, f"special w{fmt} gemm M=3 mode {mode}")
+
+
+@pytest.mark.parametrize("fmt", [4, 2, 5])
+@pytest.mark.parametrize("lds_path", ["0", "1"])
+@pytest.mark.parametrize("rpw", ["1", "2", "4"])
+@pytest.mark.parametrize("N,K,outl", [(129, 4096, True), (37, 14336, False), (300, 2080, True)])
+def test_gemv_valu_launch_variants(fmt, lds_path, rpw, N, K, outl, monkeypatch):
+    """The VALU M = 1 kernels with x staged in LDS or kept in registers, and
+    1, 2 or 4 rows per wave step."""
+    monkeypatch.setenv("WQ_GEMV_MMA", "0")
+    monkeypatch.setenv("WQ_GEMV_LDS_PATH", lds_path)
+    monkeypatch.setenv("WQ_GEMV_ROWS_PER_WAVE", rpw)
+    say(f"gemv VALU fmt={fmt} lds={lds_path} rows/wave={rpw} N={N} K={K} outliers={outl}")
+    L = synthetic.small_layer(fmt, N, K, with_outliers=outl, seed=N + int(rpw))
+    ref, dl = build(fmt, L.W, L.profile, L.ratio)
+    y, _ = run_gemv(dl, L.x)
+    check_product(ref, y, L.x, f"valu w{fmt} lds={lds_path} rpw={rpw} {N}x{K}")
