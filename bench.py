@@ -59,6 +59,10 @@ def _parse():
     p.add_argument("--bytes", type=int, default=26157628,
                    help="bytes per launch of the read / copy workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--m", type=int, default=0,
+                   help="batched workload: only this M (default: 2, 4, 8 and 16)")
+    p.add_argument("--shape", default="",
+                   help="batched workload: only this NxK (default: 14336x4096 and 4096x14336)")
     p.add_argument("--eager", action="store_true", help="time Python-side launches, no graph")
     p.add_argument("--w4-zeros", default="fp16", choices=["fp16", "packed"],
                    help="zero points of the W4 workloads (w4_4096, sweep, batched): FP16, or "
@@ -339,10 +343,13 @@ def batched_workload(a, torch, timer):
     import synthetic
     from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
     rows = []
-    for (N, K) in ((14336, 4096), (4096, 14336)):
+    shapes = [(14336, 4096), (4096, 14336)]
+    if a.shape:
+        shapes = [tuple(int(v) for v in a.shape.lower().split("x"))]
+    for (N, K) in shapes:
         Lb = synthetic.config4(16, N, K)
         base = DeviceLayer(pack_host(w4_fmt(a), Lb.W))
-        for M in (2, 4, 8, 16):
+        for M in ((a.m,) if a.m else (2, 4, 8, 16)):
             nbytes = base.nbytes(M)
             layers = rotated(DeviceLayer, base, nbytes)
             nc = len(layers)
@@ -360,6 +367,7 @@ def batched_workload(a, torch, timer):
                          "gemm_us": round(ms_gemm * 1e3, 3),
                          "gemm_GB/s": round(nbytes / (ms_gemm * 1e-3) / 1e9, 1),
                          "gemm_TFLOP/s": round(flops / (ms_gemm * 1e-3) / 1e12, 2),
+                         "pct_of_fp16_mfma_peak": round(100 * flops / (ms_gemm * 1e-3) / 2.5e15, 3),
                          "repeated_gemv_us": round(ms_rep * 1e3, 3),
                          "speedup_vs_repeated_gemv": round(ms_rep / ms_gemm, 2)})
     return rows
