@@ -514,12 +514,21 @@ def refine_workload(a, torch, timer):
 
         t_all = timer(chain, st, wu)
         t_fused = timer(lambda i: layers[i % nc].refine_topk(x, ys[i % nc], k, chunk), st, wu)
+        # the same call given a selection buffer (two kernels past 8 chunks)
+        t_call = timer(lambda i: layers[i % nc].refine_topk(x, ys[i % nc], k, chunk, sels[i % nc]),
+                       st, wu)
 
         def chain_fused(i):
             layers[i % nc].gemv_tiled(x, ys[i % nc])
             layers[i % nc].refine_topk(x, ys[i % nc], k, chunk)
 
         t_all_fused = timer(chain_fused, st, wu)
+
+        def chain_call(i):
+            layers[i % nc].gemv_tiled(x, ys[i % nc])
+            layers[i % nc].refine_topk(x, ys[i % nc], k, chunk, sels[i % nc])
+
+        t_all_call = timer(chain_call, st, wu)
         Gn = N // 32
         rbytes = n_sel * (N // 2 + 4 * Gn) + 4 * n_sel + 2 * n_sel + 4 * N
         rows.append({"workload": f"refine_topk{k}_per{chunk}_{label}", "N": N, "K": K,
@@ -530,7 +539,9 @@ def refine_workload(a, torch, timer):
                      "fused_topk_refine_us": round(t_fused * 1e3, 3),
                      "gemv_topk_refine_us": round(t_all * 1e3, 3),
                      "gemv_fused_refine_us": round(t_all_fused * 1e3, 3),
-                     "overhead_pct": round(100 * (t_all_fused - t_gemv) / t_gemv, 1)})
+                     "refine_topk_with_sel_out_us": round(t_call * 1e3, 3),
+                     "gemv_refine_topk_with_sel_out_us": round(t_all_call * 1e3, 3),
+                     "overhead_pct": round(100 * (t_all_call - t_gemv) / t_gemv, 1)})
         del layers
     return rows
 

@@ -445,14 +445,24 @@ extern "C" int wq_refine_topk(const uint8_t* rcodes, const uint16_t* rscales,
   if (k == 0) return wq::ok();
   const int64_t kk = std::min(k, chunk);
   const int64_t n_sel = (K / chunk) * kk + std::min(kk, K % chunk);
-  if (n_sel > kFusedMaxSel)
-    return wq::fail(WQ_ERR_UNSUPPORTED, "%s: %lld selected channels exceed %d (use "
-                    "wq_topk_chunks + wq_refine_add)", who, (long long)n_sel, kFusedMaxSel);
   if (!rcodes || !rscales || !rzeros || !x || !y)
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
   if (!aligned16(x)) return wq::fail(WQ_ERR_INVALID_ARG, "%s: x must be 16-byte aligned", who);
   if ((uint64_t)K * (uint64_t)N / 2 > 0xFFFFE000ull)
     return wq::fail(WQ_ERR_UNSUPPORTED, "%s: refinement larger than 4 GB", who);
+  // Past 8 chunks each of the one-launch kernel's 8 waves selects several
+  // chunks in turn; with a buffer for the selection, the two-kernel path is
+  // faster there (and holds any number of selections), and it sums in the
+  // same order (identical y).
+  const int64_t nch = (K + chunk - 1) / chunk;
+  if (sel_out != nullptr && (nch > kRefineThreads / kWave || n_sel > kFusedMaxSel)) {
+    if (int r = wq_topk_chunks(x, K, chunk, k, sel_out, stream)) return r;
+    return wq_refine_add(rcodes, rscales, rzeros, N, K, sel_out, n_sel, x, y, stream);
+  }
+  if (n_sel > kFusedMaxSel)
+    return wq::fail(WQ_ERR_UNSUPPORTED, "%s: %lld selected channels exceed %d without sel_out "
+                    "(pass sel_out, or call wq_topk_chunks + wq_refine_add)", who,
+                    (long long)n_sel, kFusedMaxSel);
   RefineArgs a{};
   a.rcodes = rcodes;
   a.rscales = rscales;

@@ -245,8 +245,10 @@ int wq_refine_add(const uint8_t* rcodes, const uint16_t* rscales, const uint16_t
  * wq_topk_chunks followed by wq_refine_add (the two give identical y).  Every
  * workgroup selects for itself from x, so the selection never goes through
  * global memory; sel_out (int32, device, wq_topk_count(K, chunk, k) entries)
- * receives S(x) if not NULL.  Holds at most 4096 selected channels (larger
- * selections return WQ_ERR_UNSUPPORTED: use the two calls).  N % 32 == 0,
+ * receives S(x) if not NULL.  With sel_out given and more than 8 chunks (or
+ * more than 4096 selected channels), the call runs wq_topk_chunks then
+ * wq_refine_add instead (faster there; the same y).  Without sel_out, more
+ * than 4096 selected channels return WQ_ERR_UNSUPPORTED.  N % 32 == 0,
  * chunk a multiple of 64 in [64, 1024], x 16-byte aligned; k == 0 does
  * nothing. */
 int wq_refine_topk(const uint8_t* rcodes, const uint16_t* rscales, const uint16_t* rzeros,

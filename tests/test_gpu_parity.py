@@ -480,6 +480,41 @@ def test_refine_topk_limits():
     assert int(y.abs().sum()) == 0
 
 
+@pytest.mark.parametrize("fmt", [4, 2])
+def test_refine_topk_with_selection_buffer(fmt):
+    """Given a selection buffer, the call also takes more than 4096 selected
+    channels (and more than 8 chunks) through the two-kernel path: same y as the
+    two calls, S(x) as the oracle's, the add within the bound."""
+    from bit_weight_only_gemv_amd.layer import refinement_host
+    N, K, chunk, k = 64, 8192, 64, 40
+    say(f"refine_topk with sel_out fmt={fmt} N={N} K={K} chunk={chunk} k={k}")
+    L = synthetic.small_layer(fmt, N, K, with_outliers=True, seed=11)
+    hl = pack_host(fmt, L.W, L.profile, L.ratio)
+    dl = DeviceLayer(hl)
+    dl.set_refinement(refinement_host(L.W, hl))
+    x = L.x.reshape(-1)
+    y1, xd = run_gemv(dl, x)
+    y2 = y1.clone()
+    y_base = host_fp16(y1).astype(np.float64).copy()
+    n = B.wq_topk_count(K, chunk, k)
+    assert n > 4096
+    sel_out = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    dl.refine_topk(xd, y1, k, chunk, sel_out)
+    sel = torch.empty(n, dtype=torch.int32, device="cuda")
+    B.wq_topk_chunks(xd, K, chunk, k, sel)
+    dl.refine(xd, y2, sel, n)
+    torch.cuda.synchronize()
+    S = O.topk_chunks(x, k, chunk)
+    assert np.array_equal(sel_out.cpu().numpy(), S)
+    assert np.array_equal(y1.cpu().numpy(), y2.cpu().numpy())
+    rq, rs, rz = O.refinement_w4(L.W, O.quantize_layer(fmt, L.W, L.profile, L.ratio).w_hat(),
+                                 hl.idx)
+    y_ref, a = O.refine_ref(y_base.astype(np.float16), x, S, O.dequant_w4(rq, rs, rz))
+    ok, worst = O.check_tolerance(host_fp16(y1).astype(np.float64), y_ref, a)
+    say(f"  refine add: worst |err|/bound = {worst:.4f}")
+    assert ok
+
+
 @pytest.mark.parametrize("gpw", ["1", "2", "4"])
 @pytest.mark.parametrize("N,K", [(96, 2048), (14336 // 4, 4096), (4096, 14336 // 2)])
 def test_refine_groups_per_workgroup(gpw, N, K, monkeypatch):
