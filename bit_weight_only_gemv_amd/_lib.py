@@ -65,6 +65,7 @@ SIGNATURES = {
     "wq_tiled_bytes": (_I64, [_INT, _I64, _I64, _I64]),
     "wq_tile_host": (_INT, [_INT, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64]),
     "wq_gemv_tiled": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
+    "wq_gemm_tiled": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _I64, _P, _P]),
     "wq_read_probe": (_INT, [_P, _I64, _P, _P]),
     "wq_read_probe_sink_words": (_I64, [_I64]),
     "wq_copy_probe": (_INT, [_P, _P, _I64, _P]),
@@ -273,6 +274,11 @@ def wq_gemm_wq(fmt, codes, scales, zeros, N, K, X, M, Y, out_idx=None, out_w=Non
     _check(load().wq_gemm_wq(fmt, _dptr(codes), _dptr(scales), _dptr(zeros), N, K,
                              _dptr(out_idx) if n_out else None, _dptr(out_w) if n_out else None,
                              n_out, flags, _dptr(X), M, _dptr(Y), _stream(stream)))
+
+
+def wq_gemm_tiled(fmt, tiled, N, K, X, M, Y, out_idx=None, n_out=0, stream=None):
+    _check(load().wq_gemm_tiled(fmt, _dptr(tiled), N, K, _dptr(out_idx) if n_out else None, n_out,
+                                _dptr(X), M, _dptr(Y), _stream(stream)))
 
 
 def wq_gemv_tiled(fmt, tiled, N, K, x, y, out_idx=None, n_out=0, stream=None):

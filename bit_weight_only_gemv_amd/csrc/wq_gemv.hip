@@ -800,6 +800,33 @@ extern "C" int wq_gemv_w2(const uint8_t* codes, const uint16_t* scales, const ui
                     "wq_gemv_w2");
 }
 
+extern "C" int wq_gemm_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
+                             const int32_t* out_idx, int64_t n_out, const uint16_t* X, int64_t M,
+                             uint16_t* Y, void* stream) {
+  const char* who = "wq_gemm_tiled";
+  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2 && fmt != WQ_FMT_W4P)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2", who);
+  if (int r = wq::check_shape(N, K, who)) return r;
+  if (n_out < 0 || n_out > K)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: n_out must be in [0, K] (got %lld)", who,
+                    (long long)n_out);
+  if (M < 1) return wq::fail(WQ_ERR_INVALID_ARG, "%s: M must be >= 1", who);
+  if (M > 2) return wq::fail(WQ_ERR_UNSUPPORTED, "%s: M must be 1 or 2", who);
+  if (!tiled || !X || !Y || (n_out > 0 && !out_idx))
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (!aligned16(tiled) || !aligned16(X) || !aligned16(Y) || (n_out > 0 && !aligned16(out_idx)))
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: device pointers must be 16-byte aligned", who);
+  bool launched = false;
+  const int r = wqd_mma_rows(fmt, true, tiled, nullptr, nullptr, N, K, out_idx, nullptr, n_out, X,
+                             M, Y, (hipStream_t)stream, who, 2, &launched);
+  if (r != WQ_OK) return r;
+  if (!launched)
+    return wq::fail(WQ_ERR_UNSUPPORTED,
+                    "%s: shape not supported by the tiled kernel (K <= 32768 and at most 32 "
+                    "outlier positions per 512-channel slice)", who);
+  return WQ_OK;
+}
+
 extern "C" int wq_gemv_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
                              const int32_t* out_idx, int64_t n_out, const uint16_t* x,
                              uint16_t* y, void* stream) {

@@ -74,9 +74,10 @@ struct MmaArgs {
   const uint16_t* zeros;
   const int32_t* out_idx;
   const uint16_t* out_w;
-  const uint16_t* x;
-  uint16_t* y;
+  const uint16_t* x;   // [M][K]
+  uint16_t* y;         // [M][N]
   int N, K, n_out;   // n_out = 0 when there are no outlier columns
+  int M;             // activation rows (at most the kernel's MS)
   int nw;            // waves per workgroup
   int nks;           // K-slices
   int nsw;           // K-slices per wave, at most
@@ -85,9 +86,10 @@ struct MmaArgs {
   int nch;           // outlier chunks of 8 slab positions, ceil(n_out / 8)
 };
 
-// Per-wave LDS region: for each of its slices, x (1 KB, masked at the outlier
-// columns), the 16 group sums of x (64 B) and the 32 outlier activations of the
-// slice's share of the slab (64 B, zero past the share).
+// Per-wave LDS region: for each of its slices and each activation row, x
+// (1 KB, masked at the outlier columns), the 16 group sums of x (64 B) and the
+// 32 outlier activations of the slice's share of the slab (64 B, zero past the
+// share).
 constexpr uint32_t kSliceLds = 1024u + 64u + 64u;
 constexpr int kShareMax = 32;   // slab positions per slice, at most
 
@@ -95,15 +97,15 @@ constexpr int kShareMax = 32;   // slab positions per slice, at most
 struct MmaLds {
   uint32_t lut, wave, part, total;
 };
-__host__ __device__ inline MmaLds mma_lds_layout(int fmt, int nw, int nsw, int rbl) {
+__host__ __device__ inline MmaLds mma_lds_layout(int fmt, int nw, int nsw, int rbl, int ms) {
   MmaLds L{};
   uint32_t off = 0;
   L.lut = off;
   if (fmt == 2) off += 256u * kLutRow;
   L.wave = off;
-  off += (uint32_t)nw * (uint32_t)nsw * kSliceLds;
+  off += (uint32_t)nw * (uint32_t)nsw * (uint32_t)ms * kSliceLds;
   L.part = off;
-  off += (uint32_t)rbl * (uint32_t)nw * 64u;
+  off += (uint32_t)rbl * (uint32_t)nw * (uint32_t)ms * 64u;
   L.total = off;
   return L;
 }
@@ -155,13 +157,14 @@ __device__ __forceinline__ float slab_dot(const uint32_t (&od)[5], const uint32_
   return v;
 }
 
-template <int FMT, bool OUT, bool TILED, int NSW>
+template <int FMT, bool OUT, bool TILED, int NSW, int MS>
 __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   typedef MmaFmt<FMT> F;
   constexpr int DEPTH = 2;
+  static_assert(MS == 1 || MS == 2, "one or two activation rows");
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_out = OUT ? a.n_out : 0;
-  const MmaLds L = mma_lds_layout(FMT, a.nw, a.nsw, a.rbl);
+  const MmaLds L = mma_lds_layout(FMT, a.nw, a.nsw, a.rbl, MS);
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int lane = tid & 63;
@@ -173,11 +176,13 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   const int nrb_wg = (a.nrb - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const int ns_w = (a.nks - w + a.nw - 1) / a.nw;   // 1 .. NSW (nw <= nks)
   const int T = ns_w * nrb_wg;                       // items of this wave
-  const uint32_t wave_bytes = (uint32_t)a.nsw * kSliceLds;
+  const uint32_t wave_bytes = (uint32_t)a.nsw * MS * kSliceLds;
   const uint32_t wreg = L.wave + (uint32_t)w * wave_bytes;
-  auto slice_x = [&](int s) { return wreg + (uint32_t)s * kSliceLds; };   // 1 KB of x
-  auto slice_sx = [&](int s) { return wreg + (uint32_t)s * kSliceLds + 1024u; };
-  auto slice_xo = [&](int s) { return wreg + (uint32_t)s * kSliceLds + 1088u; };
+  // slice s, activation row m: 1 KB of x, then the group sums and the outlier
+  // activations
+  auto slice_x = [&](int s, int m) { return wreg + (uint32_t)(s * MS + m) * kSliceLds; };
+  auto slice_sx = [&](int s, int m) { return slice_x(s, m) + 1024u; };
+  auto slice_xo = [&](int s, int m) { return slice_x(s, m) + 1088u; };
   // first outlier chunk of slice ks (ks nch < 2^31: the plan bounds both),
   // and the slice's share of slab positions, 8 C(ks) .. min(8 C(ks + 1), n_out)
   auto chunk_lo = [&](int ks) { return (uint32_t)(ks * a.nch) / (uint32_t)a.nks; };
@@ -202,19 +207,26 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
       a.out_w, clamp_bytes(TILED ? (uint64_t)a.nrb * a.nch * 256
                                  : ((uint64_t)a.N * n_out * 2 + 3) & ~(uint64_t)3));
   const __amdgpu_buffer_rsrc_t irs = make_rsrc(a.out_idx, (uint32_t)n_out * 4u);
-  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x, (uint32_t)a.K * 2u);
+  const __amdgpu_buffer_rsrc_t xrs =
+      make_rsrc(a.x, (MS == 1 ? 1u : (uint32_t)a.M) * (uint32_t)a.K * 2u);
 
   // ---- (0) x of every slice of this wave and the outlier indices of its
   //      slices' shares (lane l: slice 2p + l / 32, position l % 32 of the
   //      share), issued before the weight stream so that waiting for them
   //      never waits for weights
-  u4v xr[NSW];
+  u4v xr[MS][NSW];
   const __amdgpu_buffer_rsrc_t xnul = make_rsrc(a.x, 0u);
 #pragma unroll
-  for (int s = 0; s < NSW; ++s) {   // lane l: channels 512 ks + 8 l .. + 8 (past K: 0)
-    const uint32_t c = (uint32_t)((w + a.nw * s) * kSliceCh + 8 * lane);
-    xr[s] = ld128(s < ns_w ? xrs : xnul, c * 2u);
-  }
+  for (int m = 0; m < MS; ++m)
+#pragma unroll
+    for (int s = 0; s < NSW; ++s) {   // lane l: channels 512 ks + 8 l .. + 8 (past K: 0)
+      const uint32_t c = (uint32_t)((w + a.nw * s) * kSliceCh + 8 * lane);
+      // with two rows, row 0's channels past K would read row 1: send them past
+      // the buffer (the row-major codes there belong to the next weight row)
+      const uint32_t off = MS == 1 ? c * 2u
+                           : c < (uint32_t)a.K ? ((uint32_t)m * (uint32_t)a.K + c) * 2u : kOob;
+      xr[m][s] = ld128(s < ns_w ? xrs : xnul, off);
+    }
   constexpr int NIP = OUT ? (NSW + 1) / 2 : 1;
   uint32_t oi[NIP];
   bool oval[NIP];
@@ -316,8 +328,10 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   //      2^-24 like the code values)
   auto setup = [&]() {
 #pragma unroll
-    for (int s = 0; s < NSW; ++s)
-      if (s < ns_w) reinterpret_cast<u4v*>(smem + slice_x(s))[lane] = xr[s];
+    for (int m = 0; m < MS; ++m)
+#pragma unroll
+      for (int s = 0; s < NSW; ++s)
+        if (s < ns_w) reinterpret_cast<u4v*>(smem + slice_x(s, m))[lane] = xr[m][s];
     lds_barrier();   // x of every wave, and the W2 table, visible
     if constexpr (OUT) {
 #pragma unroll
@@ -325,36 +339,43 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
         const int s = 2 * p + (lane >> 5);
         const uint32_t c = oi[p];
         const bool v = oval[p] && c < (uint32_t)a.K;
-        uint16_t xv = 0;
-        if (v) {   // column c: slice c / 512, held by wave (c / 512) % nw as its slice (c / 512) / nw
-          const uint32_t kc = c >> 9;
-          const uint32_t wc = kc % (uint32_t)a.nw, sc = kc / (uint32_t)a.nw;
-          uint16_t* xp = reinterpret_cast<uint16_t*>(smem + L.wave + wc * wave_bytes +
-                                                     sc * kSliceLds + (c & 511u) * 2u);
-          xv = *xp;
-          *xp = 0;
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+          uint16_t xv = 0;
+          if (v) {   // column c: slice c / 512, held by wave (c / 512) % nw as its slice (c / 512) / nw
+            const uint32_t kc = c >> 9;
+            const uint32_t wc = kc % (uint32_t)a.nw, sc = kc / (uint32_t)a.nw;
+            uint16_t* xp = reinterpret_cast<uint16_t*>(
+                smem + L.wave + wc * wave_bytes + (sc * MS + (uint32_t)m) * kSliceLds +
+                (c & 511u) * 2u);
+            xv = *xp;
+            *xp = 0;
+          }
+          if (s < ns_w) reinterpret_cast<uint16_t*>(smem + slice_xo(s, m))[lane & 31] = xv;
         }
-        if (s < ns_w) reinterpret_cast<uint16_t*>(smem + slice_xo(s))[lane & 31] = xv;
       }
       lds_barrier();   // every outlier column of x zeroed
     }
 #pragma unroll
-    for (int s = 0; s < NSW; ++s) {
-      if (s < ns_w && lane < kSliceGroups) {
-        float sum = 0.f;
-        const u4v* src = reinterpret_cast<const u4v*>(smem + slice_x(s) + (uint32_t)lane * 64u);
+    for (int m = 0; m < MS; ++m)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const u4v t = src[v];
-          const uint32_t tw[4] = {t.x, t.y, t.z, t.w};
+      for (int s = 0; s < NSW; ++s) {
+        if (s < ns_w && lane < kSliceGroups) {
+          float sum = 0.f;
+          const u4v* src =
+              reinterpret_cast<const u4v*>(smem + slice_x(s, m) + (uint32_t)lane * 64u);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sum = __builtin_amdgcn_fdot2(as_h2(tw[i]), as_h2(0x3C003C00u), sum, false);
+          for (int v = 0; v < 4; ++v) {
+            const u4v t = src[v];
+            const uint32_t tw[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sum = __builtin_amdgcn_fdot2(as_h2(tw[i]), as_h2(0x3C003C00u), sum, false);
+          }
+          reinterpret_cast<float*>(smem + slice_sx(s, m))[lane] =
+              FMT != 2 ? sum * 5.9604644775390625e-8f : sum;
         }
-        reinterpret_cast<float*>(smem + slice_sx(s))[lane] =
-            FMT != 2 ? sum * 5.9604644775390625e-8f : sum;
       }
-    }
   };
 
   // ---- (3) the prologue: the first row block's loads go out, the table is
@@ -373,79 +394,104 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     advance(ls, lr);
   }
 
-  // ---- A fragments, group sums and outlier activations of slice s
+  // ---- A fragments, group sums and outlier activations of slice s.  The 16
+  //      A rows are group slots: with one activation row, slot g carries group
+  //      g; with two, the slice is taken in two windows of 8 groups, and slot
+  //      8 m + g' carries group 8 w + g' of row m in window w.
   h8 afr[16];
-  f4 sx4 = {0.f, 0.f, 0.f, 0.f};
-  uint32_t xo0[4] = {0u, 0u, 0u, 0u};
+  f4 sxw[MS];
+  uint32_t xo0[MS][4];
   uint32_t keep[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int m = 0; m < MS; ++m) {
+    sxw[m] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xo0[m][i] = 0u;
+  }
   auto enter_slice = [&](int s) {
     const int ks = w + a.nw * s;
     if constexpr (OUT) {
       // valid positions of the lane's chunk (row-major slab: the values past
       // them are other positions or rows, and are masked off)
       const int cnt = (int)share_end(ks) - (int)(8u * (chunk_lo(ks) + (uint32_t)r));
-      const u4v v = *reinterpret_cast<const u4v*>(smem + slice_xo(s) + (uint32_t)r * 16u);
-      xo0[0] = v.x;
-      xo0[1] = v.y;
-      xo0[2] = v.z;
-      xo0[3] = v.w;
+#pragma unroll
+      for (int m = 0; m < MS; ++m) {
+        const u4v v = *reinterpret_cast<const u4v*>(smem + slice_xo(s, m) + (uint32_t)r * 16u);
+        xo0[m][0] = v.x;
+        xo0[m][1] = v.y;
+        xo0[m][2] = v.z;
+        xo0[m][3] = v.w;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         keep[i] = 2 * i + 1 < cnt ? 0xFFFFFFFFu : 2 * i < cnt ? 0x0000FFFFu : 0u;
     }
-    sx4 = *reinterpret_cast<const f4*>(smem + slice_sx(s) + (uint32_t)r * 16u);
-    // A: the lane of slot m = lane % 16 whose k-quarter holds group m carries
-    // that group's 32 activations in the 4 steps of the group; all else is 0
-    const int m = n16;
-    bool act;
-    int u_m, t0;
-    if constexpr (FMT == 2) {   // group m: load m / 8, quarter (m / 2) % 4, half m % 2
-      act = r == ((m >> 1) & 3);
-      u_m = m >> 3;
-      t0 = 4 * (m & 1);
-    } else {                    // group m: load m / 4, quarter m % 4
-      act = r == (m & 3);
-      u_m = m >> 2;
-      t0 = 0;
-    }
-    uint32_t gv[16];
-    {
-      const u4v* src = reinterpret_cast<const u4v*>(smem + slice_x(s) + (uint32_t)m * 64u);
+    // group sums of this lane's output slots in each window: C rows 4r .. 4r + 3
+    // are the groups 4r + j (one row), or 8 w + 4 (r % 2) + j of row r / 2 (two)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const u4v t = src[v];
-        gv[4 * v + 0] = act ? t.x : 0u;
-        gv[4 * v + 1] = act ? t.y : 0u;
-        gv[4 * v + 2] = act ? t.z : 0u;
-        gv[4 * v + 3] = act ? t.w : 0u;
+    for (int wdw = 0; wdw < MS; ++wdw) {
+      const int mc = MS == 1 ? 0 : (r >> 1);
+      const int gb = MS == 1 ? 4 * r : 8 * wdw + 4 * (r & 1);
+      sxw[wdw] = *reinterpret_cast<const f4*>(smem + slice_sx(s, mc) + (uint32_t)gb * 4u);
+    }
+    // A: the lane of a slot whose k-quarter holds the slot's group carries that
+    // group's 32 activations in the 4 steps of the group; all else is 0
+#pragma unroll
+    for (int wdw = 0; wdw < MS; ++wdw) {
+      const int R = n16;
+      const int mi = MS == 1 ? 0 : (R >> 3);
+      const int g = MS == 1 ? R : 8 * wdw + (R & 7);
+      bool act;
+      int u_m, t0;
+      if constexpr (FMT == 2) {   // group g: load g / 8, quarter (g / 2) % 4, half g % 2
+        act = r == ((g >> 1) & 3);
+        u_m = g >> 3;
+        t0 = 4 * (g & 1);
+      } else {                    // group g: load g / 4, quarter g % 4
+        act = r == (g & 3);
+        u_m = g >> 2;
+        t0 = 0;
       }
-    }
-    uint32_t fr[4][4];   // the group's 4 fragments (W4: in decode order)
-    if constexpr (FMT == 2) {
+      uint32_t gv[16];
+      {
+        const u4v* src = reinterpret_cast<const u4v*>(smem + slice_x(s, mi) + (uint32_t)g * 64u);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fr[t][i] = gv[4 * t + i];
-    } else {
-      // step t, word i: codes k0 = 16 (t & 1) + 4 i + (t >> 1) and k0 + 2
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int k0 = 16 * (t & 1) + 4 * i;
-          fr[t][i] = __builtin_amdgcn_perm(gv[k0 / 2 + 1], gv[k0 / 2],
-                                           (t >> 1) ? 0x07060302u : 0x05040100u);
+        for (int v = 0; v < 4; ++v) {
+          const u4v t = src[v];
+          gv[4 * v + 0] = act ? t.x : 0u;
+          gv[4 * v + 1] = act ? t.y : 0u;
+          gv[4 * v + 2] = act ? t.z : 0u;
+          gv[4 * v + 3] = act ? t.w : 0u;
         }
-    }
+      }
+      uint32_t fr[4][4];   // the group's 4 fragments (W4: in decode order)
+      if constexpr (FMT == 2) {
 #pragma unroll
-    for (int f = 0; f < 16; ++f) {
-      const int u = FMT == 2 ? (f >> 3) : (f >> 2);
-      const int t = FMT == 2 ? (f & 7) : (f & 3);
-      const int tt = FMT == 2 ? (t & 3) : t;
-      const bool on = u == u_m && (FMT == 2 ? (t & 4) == t0 : true);
-      const u4v v = on ? (u4v){fr[tt][0], fr[tt][1], fr[tt][2], fr[tt][3]}
-                       : (u4v){0u, 0u, 0u, 0u};
-      afr[f] = __builtin_bit_cast(h8, v);
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) fr[t][i] = gv[4 * t + i];
+      } else {
+        // step t, word i: codes k0 = 16 (t & 1) + 4 i + (t >> 1) and k0 + 2
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int k0 = 16 * (t & 1) + 4 * i;
+            fr[t][i] = __builtin_amdgcn_perm(gv[k0 / 2 + 1], gv[k0 / 2],
+                                             (t >> 1) ? 0x07060302u : 0x05040100u);
+          }
+      }
+      // the window's fragments: 16 / MS of the 16 steps
+#pragma unroll
+      for (int f = wdw * (16 / MS); f < (wdw + 1) * (16 / MS); ++f) {
+        const int u = FMT == 2 ? (f >> 3) : (f >> 2);
+        const int t = FMT == 2 ? (f & 7) : (f & 3);
+        const int tt = FMT == 2 ? (t & 3) : t;
+        const bool on = u == u_m && (FMT == 2 ? (t & 4) == t0 : true);
+        const u4v v = on ? (u4v){fr[tt][0], fr[tt][1], fr[tt][2], fr[tt][3]}
+                         : (u4v){0u, 0u, 0u, 0u};
+        afr[f] = __builtin_bit_cast(h8, v);
+      }
     }
   };
 
@@ -455,94 +501,120 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   const uint32_t lut_lane = (uint32_t)(lane & 31) * 8u;
   auto compute = [&](const Item<FMT, OUT>& it, int ri, int si) {
     const int row = (int)(blockIdx.x + (unsigned)ri * gridDim.x) * 16 + n16;
-    f4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (FMT != 2) {
-      // c0: low-nibble steps (values q 2^-24), c1: high-nibble steps (16 q 2^-24)
+    float v = 0.f;   // this lane's slots: row 0 (one row) or row r / 2 (two)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t d[4] = {it.cw[u].x, it.cw[u].y, it.cw[u].z, it.cw[u].w};
-        uint32_t d8[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) d8[i] = d[i] >> 8;
-        const u4v b0 = {d[0] & 0x000F000Fu, d[1] & 0x000F000Fu, d[2] & 0x000F000Fu,
-                        d[3] & 0x000F000Fu};
-        const u4v b1 = {d[0] & 0x00F000F0u, d[1] & 0x00F000F0u, d[2] & 0x00F000F0u,
-                        d[3] & 0x00F000F0u};
-        const u4v b2 = {d8[0] & 0x000F000Fu, d8[1] & 0x000F000Fu, d8[2] & 0x000F000Fu,
-                        d8[3] & 0x000F000Fu};
-        const u4v b3 = {d8[0] & 0x00F000F0u, d8[1] & 0x00F000F0u, d8[2] & 0x00F000F0u,
-                        d8[3] & 0x00F000F0u};
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[4 * u + 0], __builtin_bit_cast(h8, b0), c0,
-                                                    0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[4 * u + 1], __builtin_bit_cast(h8, b1), c1,
-                                                    0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[4 * u + 2], __builtin_bit_cast(h8, b2), c0,
-                                                    0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[4 * u + 3], __builtin_bit_cast(h8, b3), c1,
-                                                    0, 0, 0);
-      }
-    } else {
-      // byte b of a code word -> LDS address (b << 8) | 8 (lane % 32); the 16
-      // table reads of a load are issued before its 8 products
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint32_t d[4] = {it.cw[u].x, it.cw[u].y, it.cw[u].z, it.cw[u].w};
-        u2 lv[16];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const uint32_t word = d[t >> 1];
-          const uint32_t bsel = (uint32_t)(2 * (t & 1));
-          lv[2 * t] =
-              lds_ld64(L.lut + __builtin_amdgcn_perm(word, lut_lane, 0x0C0C0400u + (bsel << 8)));
-          lv[2 * t + 1] =
-              lds_ld64(L.lut + __builtin_amdgcn_perm(word, lut_lane, 0x0C0C0500u + (bsel << 8)));
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const u4v bv = {lv[2 * t].x, lv[2 * t].y, lv[2 * t + 1].x, lv[2 * t + 1].y};
-          if (t & 1)
-            c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[8 * u + t], __builtin_bit_cast(h8, bv),
-                                                        c1, 0, 0, 0);
-          else
-            c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[8 * u + t], __builtin_bit_cast(h8, bv),
-                                                        c0, 0, 0, 0);
-        }
-      }
-    }
-    // slots 4r + j = groups ks*16 + 4r + j of row n16
-    const uint32_t sw[2] = {it.sv.x, it.sv.y};
-    const uint32_t zw[2] = {it.zv.x, it.zv.y};
-    float v = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float s = h2f((uint16_t)(sw[j >> 1] >> (16 * (j & 1))));
-      const float z = FMT == 5 ? (float)((zw[0] >> (4 * j)) & 0x0Fu)
-                               : h2f((uint16_t)(zw[j >> 1] >> (16 * (j & 1))));
+    for (int wdw = 0; wdw < MS; ++wdw) {
+      f4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
       if constexpr (FMT != 2) {
-        float t = __builtin_fmaf(c1[j], 0.0625f, c0[j]);
-        t = __builtin_fmaf(-z, sx4[j], t);
-        v = __builtin_fmaf(s, t, v);
+        // c0: low-nibble steps (values q 2^-24), c1: high-nibble steps (16 q 2^-24)
+#pragma unroll
+        for (int u = wdw * (4 / MS); u < (wdw + 1) * (4 / MS); ++u) {
+          const uint32_t d[4] = {it.cw[u].x, it.cw[u].y, it.cw[u].z, it.cw[u].w};
+          uint32_t d8[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) d8[i] = d[i] >> 8;
+          const u4v b0 = {d[0] & 0x000F000Fu, d[1] & 0x000F000Fu, d[2] & 0x000F000Fu,
+                          d[3] & 0x000F000Fu};
+          const u4v b1 = {d[0] & 0x00F000F0u, d[1] & 0x00F000F0u, d[2] & 0x00F000F0u,
+                          d[3] & 0x00F000F0u};
+          const u4v b2 = {d8[0] & 0x000F000Fu, d8[1] & 0x000F000Fu, d8[2] & 0x000F000Fu,
+                          d8[3] & 0x000F000Fu};
+          const u4v b3 = {d8[0] & 0x00F000F0u, d8[1] & 0x00F000F0u, d8[2] & 0x00F000F0u,
+                          d8[3] & 0x00F000F0u};
+          c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[4 * u + 0], __builtin_bit_cast(h8, b0),
+                                                      c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[4 * u + 1], __builtin_bit_cast(h8, b1),
+                                                      c1, 0, 0, 0);
+          c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[4 * u + 2], __builtin_bit_cast(h8, b2),
+                                                      c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[4 * u + 3], __builtin_bit_cast(h8, b3),
+                                                      c1, 0, 0, 0);
+        }
       } else {
-        v = __builtin_fmaf(s, c0[j] + c1[j], v);
-        v = __builtin_fmaf(z, sx4[j], v);
+        // byte b of a code word -> LDS address (b << 8) | 8 (lane % 32); the 16
+        // table reads of a load are issued before its 8 products
+#pragma unroll
+        for (int u = wdw * (2 / MS); u < (wdw + 1) * (2 / MS); ++u) {
+          const uint32_t d[4] = {it.cw[u].x, it.cw[u].y, it.cw[u].z, it.cw[u].w};
+          u2 lv[16];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const uint32_t word = d[t >> 1];
+            const uint32_t bsel = (uint32_t)(2 * (t & 1));
+            lv[2 * t] =
+                lds_ld64(L.lut + __builtin_amdgcn_perm(word, lut_lane, 0x0C0C0400u + (bsel << 8)));
+            lv[2 * t + 1] =
+                lds_ld64(L.lut + __builtin_amdgcn_perm(word, lut_lane, 0x0C0C0500u + (bsel << 8)));
+          }
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const u4v bv = {lv[2 * t].x, lv[2 * t].y, lv[2 * t + 1].x, lv[2 * t + 1].y};
+            if (t & 1)
+              c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[8 * u + t],
+                                                          __builtin_bit_cast(h8, bv), c1, 0, 0, 0);
+            else
+              c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[8 * u + t],
+                                                          __builtin_bit_cast(h8, bv), c0, 0, 0, 0);
+          }
+        }
+      }
+      // slots 4r + j: groups ks*16 + 4r + j (one row); with two rows, groups
+      // 8 w + 4 (r % 2) + j, whose scales and zeros the quarter 2 w + r % 2 of
+      // the same row holds (this lane's, or the one 32 lanes away)
+      uint32_t sw[2] = {it.sv.x, it.sv.y};
+      uint32_t zw[2] = {it.zv.x, it.zv.y};
+      if constexpr (MS == 2) {
+        const bool own = (r >> 1) == wdw;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t os = (uint32_t)__shfl_xor((int)sw[i], 32);
+          const uint32_t oz = (uint32_t)__shfl_xor((int)zw[i], 32);
+          sw[i] = own ? sw[i] : os;
+          zw[i] = own ? zw[i] : oz;
+        }
+      }
+      const f4 sx4 = sxw[wdw];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float s = h2f((uint16_t)(sw[j >> 1] >> (16 * (j & 1))));
+        const float z = FMT == 5 ? (float)((zw[0] >> (4 * j)) & 0x0Fu)
+                                 : h2f((uint16_t)(zw[j >> 1] >> (16 * (j & 1))));
+        if constexpr (FMT != 2) {
+          float t = __builtin_fmaf(c1[j], 0.0625f, c0[j]);
+          t = __builtin_fmaf(-z, sx4[j], t);
+          v = __builtin_fmaf(s, t, v);
+        } else {
+          v = __builtin_fmaf(s, c0[j] + c1[j], v);
+          v = __builtin_fmaf(z, sx4[j], v);
+        }
       }
     }
     if constexpr (FMT != 2) v *= 16777216.0f;
-    if constexpr (OUT) {
-      if constexpr (TILED) {   // zero-padded chunks: no alignment, no mask
+    float vv[MS];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v = __builtin_amdgcn_fdot2(as_h2(it.od[i]), as_h2(xo0[i]), v, false);
-      } else {
-        const uint32_t sh = (((uint32_t)row * (uint32_t)n_out) & 1u) * 16u;
-        v = slab_dot(it.od, xo0, keep, sh, v);
+    for (int m = 0; m < MS; ++m) {
+      vv[m] = (MS == 1 || m == (r >> 1)) ? v : 0.f;
+      if constexpr (OUT) {
+        if constexpr (TILED) {   // zero-padded chunks: no alignment, no mask
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vv[m] = __builtin_amdgcn_fdot2(as_h2(it.od[i]), as_h2(xo0[m][i]), vv[m], false);
+        } else {
+          const uint32_t sh = (((uint32_t)row * (uint32_t)n_out) & 1u) * 16u;
+          vv[m] = slab_dot(it.od, xo0[m], keep, sh, vv[m]);
+        }
       }
+      // the four lane quarters hold parts of the same row's sum: add them
+      vv[m] += __shfl_xor(vv[m], 16);
+      vv[m] += __shfl_xor(vv[m], 32);
     }
-    // the four lane quarters hold the same row: add them
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
     if (r == 0) {
-      float* p = s_part + ((uint32_t)ri * (uint32_t)a.nw + (uint32_t)w) * 16u + (uint32_t)n16;
-      *p = si == 0 ? v : *p + v;
+#pragma unroll
+      for (int m = 0; m < MS; ++m) {
+        float* p = s_part + (((uint32_t)ri * (uint32_t)a.nw + (uint32_t)w) * MS + (uint32_t)m) * 16u +
+                   (uint32_t)n16;
+        *p = si == 0 ? vv[m] : *p + vv[m];
+      }
     }
   };
 
@@ -564,13 +636,25 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
 
   // ---- (5) fixed-order sum of the waves' row sums
   __syncthreads();
-  for (int t = tid; t < nrb_wg * 16; t += nthr) {
-    const int ri2 = t >> 4, n = t & 15;
-    const int row = (int)(blockIdx.x + (unsigned)ri2 * gridDim.x) * 16 + n;
-    if (row >= a.N) continue;
-    float s = 0.f;
-    for (int k = 0; k < a.nw; ++k) s += s_part[((uint32_t)ri2 * a.nw + k) * 16u + n];
-    a.y[row] = f2h(s);
+  if constexpr (MS == 1) {
+    for (int t = tid; t < nrb_wg * 16; t += nthr) {
+      const int ri2 = t >> 4, n = t & 15;
+      const int row = (int)(blockIdx.x + (unsigned)ri2 * gridDim.x) * 16 + n;
+      if (row >= a.N) continue;
+      float s = 0.f;
+      for (int k = 0; k < a.nw; ++k) s += s_part[((uint32_t)ri2 * a.nw + k) * 16u + n];
+      a.y[row] = f2h(s);
+    }
+  } else {
+    for (int t = tid; t < nrb_wg * 16 * MS; t += nthr) {
+      const int n = t & 15, m = (t >> 4) % MS, ri2 = (t >> 4) / MS;
+      const int row = (int)(blockIdx.x + (unsigned)ri2 * gridDim.x) * 16 + n;
+      if (row >= a.N || m >= a.M) continue;
+      float s = 0.f;
+      for (int k = 0; k < a.nw; ++k)
+        s += s_part[(((uint32_t)ri2 * a.nw + k) * MS + (uint32_t)m) * 16u + (uint32_t)n];
+      a.y[(size_t)m * a.N + row] = f2h(s);
+    }
   }
 }
 
@@ -1137,7 +1221,7 @@ struct MmaPlan {
   size_t lds;
 };
 
-static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_out) {
+static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_out, int ms) {
   MmaPlan p{};
   // the row-major layout reads whole 128-channel quarters of a slice from
   // each row; the tiled one is padded to whole slices
@@ -1177,7 +1261,7 @@ static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_ou
   if (cus <= 0) return p;
   p.grid = std::min(p.nrb, cus);
   p.rbl = (p.nrb + p.grid - 1) / p.grid;
-  const MmaLds L = mma_lds_layout(fmt, p.nw, p.nsw, p.rbl);
+  const MmaLds L = mma_lds_layout(fmt, p.nw, p.nsw, p.rbl, ms);
   p.lds = L.total;
   if (p.lds > kMaxLdsBytes) return p;
   p.ok = true;
@@ -1245,9 +1329,18 @@ int wqd_gemv_mma(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scal
                  const uint16_t* zeros, int64_t N, int64_t K, const int32_t* out_idx,
                  const uint16_t* out_w, int64_t n_out, const uint16_t* x, uint16_t* y,
                  hipStream_t stream, const char* who, int mode, bool* launched) {
+  return wqd_mma_rows(fmt, tiled, codes, scales, zeros, N, K, out_idx, out_w, n_out, x, 1, y,
+                      stream, who, mode, launched);
+}
+
+int wqd_mma_rows(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scales,
+                 const uint16_t* zeros, int64_t N, int64_t K, const int32_t* out_idx,
+                 const uint16_t* out_w, int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y,
+                 hipStream_t stream, const char* who, int mode, bool* launched) {
   *launched = false;
-  if (mode == 0) return WQ_OK;
-  const MmaPlan p = plan_mma1(fmt, tiled, N, K, n_out);
+  if (mode == 0 || M < 1 || M > 2) return WQ_OK;
+  const int ms = (int)M;
+  const MmaPlan p = plan_mma1(fmt, tiled, N, K, n_out, ms);
   if (!p.ok || (mode == 1 && !p.preferred)) return WQ_OK;
   MmaArgs a{};
   if (tiled) {
@@ -1263,11 +1356,12 @@ int wqd_gemv_mma(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scal
     a.out_w = out_w;
   }
   a.out_idx = out_idx;
-  a.x = x;
-  a.y = y;
+  a.x = X;
+  a.y = Y;
   a.N = (int)N;
   a.K = (int)K;
   a.n_out = (int)n_out;
+  a.M = (int)M;
   a.nw = p.nw;
   a.nks = p.nks;
   a.nsw = p.nsw;
@@ -1275,14 +1369,15 @@ int wqd_gemv_mma(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scal
   a.rbl = p.rbl;
   a.nch = p.nch;
   const dim3 grid(p.grid), block(p.nw * kWave);
-#define WQ_MMA_LAUNCH(F_, O_, T_, S_)                                                        \
-  if (fmt == F_ && (n_out > 0) == O_ && tiled == T_ && p.nswt == S_) {                       \
-    if (!allow_lds(reinterpret_cast<const void*>(&mma1d_kernel<F_, O_, T_, S_>), p.lds))    \
+#define WQ_MMA_LAUNCH_R(F_, O_, T_, S_, R_)                                                  \
+  if (fmt == F_ && (n_out > 0) == O_ && tiled == T_ && p.nswt == S_ && ms == R_) {           \
+    if (!allow_lds(reinterpret_cast<const void*>(&mma1d_kernel<F_, O_, T_, S_, R_>), p.lds)) \
       return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds); \
-    hipLaunchKernelGGL((mma1d_kernel<F_, O_, T_, S_>), grid, block, p.lds, stream, a);       \
+    hipLaunchKernelGGL((mma1d_kernel<F_, O_, T_, S_, R_>), grid, block, p.lds, stream, a);    \
     *launched = true;                                                                        \
     return check_launch(who);                                                                \
   }
+#define WQ_MMA_LAUNCH(F_, O_, T_, S_) WQ_MMA_LAUNCH_R(F_, O_, T_, S_, 1) WQ_MMA_LAUNCH_R(F_, O_, T_, S_, 2)
 #define WQ_MMA_SLICES(F_, O_, T_) \
   WQ_MMA_LAUNCH(F_, O_, T_, 1) WQ_MMA_LAUNCH(F_, O_, T_, 2) WQ_MMA_LAUNCH(F_, O_, T_, 4) \
   WQ_MMA_LAUNCH(F_, O_, T_, 8)
@@ -1292,6 +1387,7 @@ int wqd_gemv_mma(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scal
 #undef WQ_MMA_SLICES
 #undef WQ_MMA_LAYOUTS
 #undef WQ_MMA_LAUNCH
+#undef WQ_MMA_LAUNCH_R
   return WQ_OK;
 }
 

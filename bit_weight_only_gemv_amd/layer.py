@@ -134,6 +134,13 @@ class DeviceLayer:
             raise ValueError("layer built without tiled=True")
         L.wq_gemv_tiled(self.fmt, self.tiled, self.N, self.K, x, y, self.idx, self.n_out, stream)
 
+    def gemm_tiled(self, X, Y, stream=None):
+        """Y [M][N] from X [M][K], M = 1 or 2, on the tiled layout."""
+        if self.tiled is None:
+            raise ValueError("layer built without tiled=True")
+        L.wq_gemm_tiled(self.fmt, self.tiled, self.N, self.K, X, X.shape[0], Y, self.idx,
+                        self.n_out, stream)
+
     def gemm(self, X, Y, flags=L.WQ_FUSE_OUTLIERS, stream=None):
         L.wq_gemm_wq(self.fmt, self.codes, self.scales, self.zeros, self.N, self.K, X, X.shape[0],
                      Y, self.idx, self.wout, self.n_out, flags, stream)

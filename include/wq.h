@@ -309,6 +309,16 @@ int wq_tile_host(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
 int wq_gemv_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K, const int32_t* out_idx,
                   int64_t n_out, const uint16_t* x, uint16_t* y, void* stream);
 
+/* The tiled layer against M = 1 or 2 activation rows: Y [M][N] = X [M][K] times
+ * the layer (outlier pass fused), the batched product of SPECTRA section 4.2 at
+ * its smallest M.  Two rows share the matrix-core kernel's 16 group slots (the
+ * 512-channel slice taken in two windows of 8 groups), so the codes are decoded
+ * once for both rows.  M = 1 is wq_gemv_tiled.  Same shape limits as
+ * wq_gemv_tiled; M above 2 returns WQ_ERR_UNSUPPORTED (use wq_gemm_wq on the
+ * row-major arrays). */
+int wq_gemm_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K, const int32_t* out_idx,
+                  int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y, void* stream);
+
 /* -------------------------------------------------- measurement support
  * Not part of the method: kernels of known traffic that calibrate bandwidth
  * figures and hardware byte counters. */
