@@ -261,10 +261,11 @@ extern "C" int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales,
     int mode = 1;
     if (const char* e = getenv("WQ_GEMM_MMA")) mode = atoi(e);
     bool launched = false;
-    // two rows: the M = 1 matrix-core kernel with its group slots shared by the
-    // two rows (its decode needs no FP16 weights); WQ_GEMM_ROWS=0 skips it
+    // up to four rows (two for W2): the M = 1 matrix-core kernel with its group
+    // slots shared by the rows (its decode needs no FP16 weights);
+    // WQ_GEMM_ROWS=0 skips it
     const char* er = getenv("WQ_GEMM_ROWS");
-    if (M == 2 && mode != 0 && !(er && atoi(er) == 0)) {
+    if (M <= 4 && mode != 0 && !(er && atoi(er) == 0)) {
       const int r = wqd_mma_rows(fmt, false, codes, scales, zeros, N, K, out_idx, out_w,
                                  a.fuse ? n_out : 0, X, M, Y, s, who, 2, &launched);
       if (r != WQ_OK || launched) return r;

@@ -811,7 +811,8 @@ extern "C" int wq_gemm_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: n_out must be in [0, K] (got %lld)", who,
                     (long long)n_out);
   if (M < 1) return wq::fail(WQ_ERR_INVALID_ARG, "%s: M must be >= 1", who);
-  if (M > 2) return wq::fail(WQ_ERR_UNSUPPORTED, "%s: M must be 1 or 2", who);
+  if (M > 4 || (M > 2 && fmt == WQ_FMT_W2))
+    return wq::fail(WQ_ERR_UNSUPPORTED, "%s: M must be at most 4 (W2: 2)", who);
   if (!tiled || !X || !Y || (n_out > 0 && !out_idx))
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
   if (!aligned16(tiled) || !aligned16(X) || !aligned16(Y) || (n_out > 0 && !aligned16(out_idx)))
@@ -822,8 +823,9 @@ extern "C" int wq_gemm_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K
   if (r != WQ_OK) return r;
   if (!launched)
     return wq::fail(WQ_ERR_UNSUPPORTED,
-                    "%s: shape not supported by the tiled kernel (K <= 32768 and at most 32 "
-                    "outlier positions per 512-channel slice)", who);
+                    "%s: shape not supported by the tiled kernel at M = %lld (K <= 32768, at most "
+                    "32 outlier positions per 512-channel slice; more rows need more LDS and, at "
+                    "3 or 4 rows, at most 4 slices per wave)", who, (long long)M);
   return WQ_OK;
 }
 

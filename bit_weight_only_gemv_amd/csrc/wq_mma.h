@@ -15,9 +15,10 @@ int wqd_gemv_mma(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scal
                  const uint16_t* out_w, int64_t n_out, const uint16_t* x, uint16_t* y,
                  hipStream_t stream, const char* who, int mode, bool* launched);
 
-// The same matrix-core kernel for M = 1 or 2 activation rows X [M][K] -> Y [M][N]
-// (two rows share the 16 A-row slots, the slice taken in two windows of 8
-// groups); same contract and `mode` values as wqd_gemv_mma.
+// The same matrix-core kernel for M = 1 to 4 activation rows (W2: 1 or 2),
+// X [M][K] -> Y [M][N]: the rows share the 16 A-row slots, each slice taken in
+// M windows of 16 / M groups (3 rows run as 4); same contract and `mode` values
+// as wqd_gemv_mma.
 int wqd_mma_rows(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scales,
                  const uint16_t* zeros, int64_t N, int64_t K, const int32_t* out_idx,
                  const uint16_t* out_w, int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y,

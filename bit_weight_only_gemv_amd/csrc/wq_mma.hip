@@ -161,7 +161,8 @@ template <int FMT, bool OUT, bool TILED, int NSW, int MS>
 __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   typedef MmaFmt<FMT> F;
   constexpr int DEPTH = 2;
-  static_assert(MS == 1 || MS == 2, "one or two activation rows");
+  static_assert(MS == 1 || MS == 2 || (MS == 4 && FMT != 2), "1, 2 or (W4) 4 activation rows");
+  constexpr int WG = 16 / MS;   // groups per window: each slice is taken in MS windows
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_out = OUT ? a.n_out : 0;
   const MmaLds L = mma_lds_layout(FMT, a.nw, a.nsw, a.rbl, MS);
@@ -396,8 +397,8 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
 
   // ---- A fragments, group sums and outlier activations of slice s.  The 16
   //      A rows are group slots: with one activation row, slot g carries group
-  //      g; with two, the slice is taken in two windows of 8 groups, and slot
-  //      8 m + g' carries group 8 w + g' of row m in window w.
+  //      g; with MS rows the slice is taken in MS windows of WG = 16 / MS
+  //      groups, and slot WG m + g' carries group WG w + g' of row m in window w.
   h8 afr[16];
   f4 sxw[MS];
   uint32_t xo0[MS][4];
@@ -427,11 +428,11 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
         keep[i] = 2 * i + 1 < cnt ? 0xFFFFFFFFu : 2 * i < cnt ? 0x0000FFFFu : 0u;
     }
     // group sums of this lane's output slots in each window: C rows 4r .. 4r + 3
-    // are the groups 4r + j (one row), or 8 w + 4 (r % 2) + j of row r / 2 (two)
+    // are the groups WG w + 4 (r % (WG / 4)) + j of row r / (WG / 4)
 #pragma unroll
     for (int wdw = 0; wdw < MS; ++wdw) {
-      const int mc = MS == 1 ? 0 : (r >> 1);
-      const int gb = MS == 1 ? 4 * r : 8 * wdw + 4 * (r & 1);
+      const int mc = r / (WG / 4);
+      const int gb = WG * wdw + 4 * (r % (WG / 4));
       sxw[wdw] = *reinterpret_cast<const f4*>(smem + slice_sx(s, mc) + (uint32_t)gb * 4u);
     }
     // A: the lane of a slot whose k-quarter holds the slot's group carries that
@@ -439,8 +440,8 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
 #pragma unroll
     for (int wdw = 0; wdw < MS; ++wdw) {
       const int R = n16;
-      const int mi = MS == 1 ? 0 : (R >> 3);
-      const int g = MS == 1 ? R : 8 * wdw + (R & 7);
+      const int mi = R / WG;
+      const int g = WG * wdw + R % WG;
       bool act;
       int u_m, t0;
       if constexpr (FMT == 2) {   // group g: load g / 8, quarter (g / 2) % 4, half g % 2
@@ -501,7 +502,7 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   const uint32_t lut_lane = (uint32_t)(lane & 31) * 8u;
   auto compute = [&](const Item<FMT, OUT>& it, int ri, int si) {
     const int row = (int)(blockIdx.x + (unsigned)ri * gridDim.x) * 16 + n16;
-    float v = 0.f;   // this lane's slots: row 0 (one row) or row r / 2 (two)
+    float v = 0.f;   // this lane's slots: row r / (WG / 4)
 #pragma unroll
     for (int wdw = 0; wdw < MS; ++wdw) {
       f4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
@@ -558,9 +559,9 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
           }
         }
       }
-      // slots 4r + j: groups ks*16 + 4r + j (one row); with two rows, groups
-      // 8 w + 4 (r % 2) + j, whose scales and zeros the quarter 2 w + r % 2 of
-      // the same row holds (this lane's, or the one 32 lanes away)
+      // slots 4r + j: groups ks*16 + WG w + 4 (r % (WG / 4)) + j, whose scales and
+      // zeros the lane quarter w (WG / 4) + r % (WG / 4) of the same weight row
+      // loaded (one row: this lane; two: this one or the one 32 lanes away)
       uint32_t sw[2] = {it.sv.x, it.sv.y};
       uint32_t zw[2] = {it.zv.x, it.zv.y};
       if constexpr (MS == 2) {
@@ -571,6 +572,13 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
           const uint32_t oz = (uint32_t)__shfl_xor((int)zw[i], 32);
           sw[i] = own ? sw[i] : os;
           zw[i] = own ? zw[i] : oz;
+        }
+      } else if constexpr (MS == 4) {
+        const int src = n16 + 16 * wdw;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          sw[i] = (uint32_t)__shfl((int)sw[i], src);
+          zw[i] = (uint32_t)__shfl((int)zw[i], src);
         }
       }
       const f4 sx4 = sxw[wdw];
@@ -593,7 +601,7 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
     float vv[MS];
 #pragma unroll
     for (int m = 0; m < MS; ++m) {
-      vv[m] = (MS == 1 || m == (r >> 1)) ? v : 0.f;
+      vv[m] = (MS == 1 || m == r / (WG / 4)) ? v : 0.f;
       if constexpr (OUT) {
         if constexpr (TILED) {   // zero-padded chunks: no alignment, no mask
 #pragma unroll
@@ -1338,9 +1346,10 @@ int wqd_mma_rows(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scal
                  const uint16_t* out_w, int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y,
                  hipStream_t stream, const char* who, int mode, bool* launched) {
   *launched = false;
-  if (mode == 0 || M < 1 || M > 2) return WQ_OK;
-  const int ms = (int)M;
+  if (mode == 0 || M < 1 || M > 4 || (M > 2 && fmt == 2)) return WQ_OK;
+  const int ms = M <= 2 ? (int)M : 4;   // three rows run as four, the last one empty
   const MmaPlan p = plan_mma1(fmt, tiled, N, K, n_out, ms);
+  if (ms == 4 && p.nswt > 4) return WQ_OK;   // registers: four rows of x per slice
   if (!p.ok || (mode == 1 && !p.preferred)) return WQ_OK;
   MmaArgs a{};
   if (tiled) {
@@ -1378,16 +1387,24 @@ int wqd_mma_rows(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scal
     return check_launch(who);                                                                \
   }
 #define WQ_MMA_LAUNCH(F_, O_, T_, S_) WQ_MMA_LAUNCH_R(F_, O_, T_, S_, 1) WQ_MMA_LAUNCH_R(F_, O_, T_, S_, 2)
+// four rows: W4 and W4P, at most 4 slices per wave
+#define WQ_MMA_SLICES4(F_, O_, T_) \
+  WQ_MMA_LAUNCH_R(F_, O_, T_, 1, 4) WQ_MMA_LAUNCH_R(F_, O_, T_, 2, 4) WQ_MMA_LAUNCH_R(F_, O_, T_, 4, 4)
+#define WQ_MMA_LAYOUTS4(F_, O_) WQ_MMA_SLICES4(F_, O_, false) WQ_MMA_SLICES4(F_, O_, true)
 #define WQ_MMA_SLICES(F_, O_, T_) \
   WQ_MMA_LAUNCH(F_, O_, T_, 1) WQ_MMA_LAUNCH(F_, O_, T_, 2) WQ_MMA_LAUNCH(F_, O_, T_, 4) \
   WQ_MMA_LAUNCH(F_, O_, T_, 8)
 #define WQ_MMA_LAYOUTS(F_, O_) WQ_MMA_SLICES(F_, O_, false) WQ_MMA_SLICES(F_, O_, true)
   WQ_MMA_LAYOUTS(4, false) WQ_MMA_LAYOUTS(4, true) WQ_MMA_LAYOUTS(2, false) WQ_MMA_LAYOUTS(2, true)
   WQ_MMA_LAYOUTS(5, false) WQ_MMA_LAYOUTS(5, true)
+  WQ_MMA_LAYOUTS4(4, false) WQ_MMA_LAYOUTS4(4, true) WQ_MMA_LAYOUTS4(5, false)
+  WQ_MMA_LAYOUTS4(5, true)
 #undef WQ_MMA_SLICES
 #undef WQ_MMA_LAYOUTS
 #undef WQ_MMA_LAUNCH
 #undef WQ_MMA_LAUNCH_R
+#undef WQ_MMA_SLICES4
+#undef WQ_MMA_LAYOUTS4
   return WQ_OK;
 }
 

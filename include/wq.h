@@ -309,13 +309,15 @@ int wq_tile_host(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
 int wq_gemv_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K, const int32_t* out_idx,
                   int64_t n_out, const uint16_t* x, uint16_t* y, void* stream);
 
-/* The tiled layer against M = 1 or 2 activation rows: Y [M][N] = X [M][K] times
- * the layer (outlier pass fused), the batched product of SPECTRA section 4.2 at
- * its smallest M.  Two rows share the matrix-core kernel's 16 group slots (the
- * 512-channel slice taken in two windows of 8 groups), so the codes are decoded
- * once for both rows.  M = 1 is wq_gemv_tiled.  Same shape limits as
- * wq_gemv_tiled; M above 2 returns WQ_ERR_UNSUPPORTED (use wq_gemm_wq on the
- * row-major arrays). */
+/* The tiled layer against M = 1 to 4 activation rows (W2: 1 or 2): Y [M][N] =
+ * X [M][K] times the layer (outlier pass fused), the batched product of SPECTRA
+ * section 4.2 at its smallest M.  The rows share the matrix-core kernel's 16
+ * group slots (each 512-channel slice taken in M windows of 16 / M groups; 3
+ * rows run as 4), so the codes are decoded once for all rows.  M = 1 is
+ * wq_gemv_tiled.  Same shape limits as wq_gemv_tiled, and with more rows more
+ * LDS per slice (at 3 or 4 rows also at most 4 slices per wave, K <= 16384);
+ * shapes outside them return WQ_ERR_UNSUPPORTED (wq_gemm_wq on the row-major
+ * arrays takes every M up to 16). */
 int wq_gemm_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K, const int32_t* out_idx,
                   int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y, void* stream);
 

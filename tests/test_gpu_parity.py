@@ -181,42 +181,46 @@ def test_gemv_tiled(fmt, N, K, outl, monkeypatch):
 @pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("N,K", TILED_SHAPES)
 @pytest.mark.parametrize("outl", [False, True])
-def test_gemm_tiled_two_rows(fmt, N, K, outl):
-    """Two activation rows sharing the tiled kernel's group slots: both rows
-    within the bound; M = 1 through the same entry equals the tiled GEMV."""
-    say(f"gemm tiled M=2 fmt={fmt} N={N} K={K} outliers={outl}")
-    L = synthetic.small_layer(fmt, N, K, M=2, with_outliers=outl, seed=N % 13)
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_gemm_tiled_rows(fmt, N, K, outl, M):
+    """Up to four activation rows sharing the tiled kernel's group slots: every
+    row within the bound; M = 1 through the same entry equals the tiled GEMV."""
+    say(f"gemm tiled M={M} fmt={fmt} N={N} K={K} outliers={outl}")
+    L = synthetic.small_layer(fmt, N, K, M=M, with_outliers=outl, seed=N % 13 + M)
     ref, dl = build_tiled(fmt, L.W, L.profile, L.ratio)
     X = dev_fp16(L.x)
-    Y = torch.full((2, N), -1, dtype=torch.int16, device="cuda")
+    Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
     try:
         dl.gemm_tiled(X, Y)
-    except B.WQError as e:   # two rows' LDS does not fit at the longest rows
-        assert e.status == -2 and K >= 16384, (e.status, K)
+    except B.WQError as e:   # W2 above two rows; more rows' LDS at the longest rows
+        assert e.status == -2 and ((fmt == 2 and M > 2) or K >= 16384), (e.status, fmt, M, K)
         return
     torch.cuda.synchronize()
-    check_product(ref, Y, L.x, f"tiled M=2 w{fmt} {N}x{K} n_out={ref.n_out}")
-    Y1 = torch.full((1, N), -1, dtype=torch.int16, device="cuda")
-    dl.gemm_tiled(dev_fp16(L.x[:1]), Y1)
-    y = run_gemv_tiled(dl, L.x[0])
-    assert torch.equal(Y1[0], y)
+    check_product(ref, Y, L.x, f"tiled M={M} w{fmt} {N}x{K} n_out={ref.n_out}")
+    if M == 2:
+        Y1 = torch.full((1, N), -1, dtype=torch.int16, device="cuda")
+        dl.gemm_tiled(dev_fp16(L.x[:1]), Y1)
+        y = run_gemv_tiled(dl, L.x[0])
+        assert torch.equal(Y1[0], y)
 
 
 @pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("N,K,outl", [(129, 4096, True), (5000, 4224, True), (300, 14336, False)])
-def test_gemm_two_rows_paths(fmt, N, K, outl, monkeypatch):
-    """M = 2 on the row-major arrays: the two-row matrix-core kernel (the
-    default) and the batched kernel (WQ_GEMM_ROWS=0) both within the bound."""
-    L = synthetic.small_layer(fmt, N, K, M=2, with_outliers=outl, seed=K % 11)
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_gemm_rows_paths(fmt, N, K, outl, M, monkeypatch):
+    """M = 2..4 on the row-major arrays: the shared-slot matrix-core kernel (the
+    default where it applies) and the batched kernel (WQ_GEMM_ROWS=0) both
+    within the bound."""
+    L = synthetic.small_layer(fmt, N, K, M=M, with_outliers=outl, seed=K % 11 + M)
     ref, dl = build(fmt, L.W, L.profile, L.ratio)
     X = dev_fp16(L.x)
     for rows in ("1", "0"):
         monkeypatch.setenv("WQ_GEMM_ROWS", rows)
-        say(f"gemm M=2 fmt={fmt} {N}x{K} two-row kernel={rows}")
-        Y = torch.full((2, N), -1, dtype=torch.int16, device="cuda")
+        say(f"gemm M={M} fmt={fmt} {N}x{K} shared-slot kernel={rows}")
+        Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
         dl.gemm(X, Y)
         torch.cuda.synchronize()
-        check_product(ref, Y, L.x, f"M=2 w{fmt} {N}x{K} rows={rows}")
+        check_product(ref, Y, L.x, f"M={M} w{fmt} {N}x{K} rows={rows}")
 
 
 @pytest.mark.parametrize("fmt", [4, 2, 5])

@@ -173,7 +173,8 @@ def test_error_codes():
     assert lib.wq_refine_topk(None, None, None, 64, 64, 64, 0, None, None, None, None) == 0
     assert lib.wq_refine_topk(fake, fake, fake, 64, 64, 64, 1, None, fake, None, None) == -1
     # two-row tiled product
-    assert lib.wq_gemm_tiled(4, fake, 64, 512, None, 0, fake, 3, fake, None) == -2
+    assert lib.wq_gemm_tiled(4, fake, 64, 512, None, 0, fake, 5, fake, None) == -2
+    assert lib.wq_gemm_tiled(2, fake, 64, 512, None, 0, fake, 3, fake, None) == -2
     assert lib.wq_gemm_tiled(4, fake, 64, 512, None, 0, fake, 0, fake, None) == -1
     assert lib.wq_gemm_tiled(4, None, 64, 512, None, 0, fake, 2, fake, None) == -1
     assert lib.wq_gemm_tiled(3, fake, 64, 512, None, 0, fake, 2, fake, None) == -1
