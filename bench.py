@@ -35,6 +35,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -75,10 +76,17 @@ def _parse():
 
 
 def kernel_source_hash() -> str:
+    """Hash of the M = 1 kernels' code with comments and layout removed, so
+    that counters stay attached to the code they were taken on and survive
+    edits of comments only."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "bit_weight_only_gemv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "bit_weight_only_gemv_amd", "csrc", f), encoding="utf-8") as fh:
+            t = fh.read()
+        t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+        t = re.sub(r"//[^\n]*", " ", t)
+        h.update(" ".join(t.split()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

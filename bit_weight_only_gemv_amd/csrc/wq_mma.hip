@@ -1,4 +1,4 @@
-// M = 1 dequantize-and-multiply on the matrix cores of gfx950
+// M = 1 .. 4 dequantize-and-multiply on the matrix cores of gfx950
 // (v_mfma_f32_16x16x32_f16), persistent over row blocks.
 //
 // What is computed is the same as the VALU kernels of wq_gemv.hip (SPECTRA
@@ -47,6 +47,16 @@
 //  * Per row block each wave reduces its 4 lane quarters and adds its row
 //    sums into an LDS slot of its own; the slots are summed in a fixed order
 //    at the end (deterministic, no atomics).
+//  * Several activation rows (MS = 2 or 4) share the 16 slots: each slice is
+//    taken in MS windows of 16 / MS groups, and slot R stands for row R / WG,
+//    group WG w + R % WG of window w (WG = 16 / MS).  Window w is multiplied
+//    in the 16 / MS steps whose B fragments hold its groups, so a row block
+//    still takes 16 MFMAs and one pass over the weights whatever MS is: the
+//    slots a single row leaves empty in a step carry the other rows.  The
+//    lane that holds a slot's sum is not the lane that loaded its scale and
+//    zero; they come from the loading lane quarter by a cross-lane move.  W2
+//    stops at MS = 2: its loads put two groups of different windows into the
+//    same MFMA step.
 
 #include "wq_common.cuh"
 #include "wq_device.h"

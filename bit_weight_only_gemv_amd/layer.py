@@ -135,7 +135,7 @@ class DeviceLayer:
         L.wq_gemv_tiled(self.fmt, self.tiled, self.N, self.K, x, y, self.idx, self.n_out, stream)
 
     def gemm_tiled(self, X, Y, stream=None):
-        """Y [M][N] from X [M][K], M = 1 or 2, on the tiled layout."""
+        """Y [M][N] from X [M][K] on the tiled layout, M = 1 .. 4 (W2: 1 or 2)."""
         if self.tiled is None:
             raise ValueError("layer built without tiled=True")
         L.wq_gemm_tiled(self.fmt, self.tiled, self.N, self.K, X, X.shape[0], Y, self.idx,
