@@ -46,7 +46,8 @@ METRIC = "M=1 dequant-GEMV effective HBM GB/s (% of MI355X peak); eq. tokens/s"
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["wq_gemv.hip", "wq_mma.hip", "wq_mma.h", "wq_common.cuh", "wq_device.h"]
+KERNEL_SOURCES = ["wq_gemv.hip", "wq_mma.hip", "wq_mma.h", "wq_common.cuh", "wq_device.h",
+                  "wq_select.cuh"]
 
 
 def _parse():
@@ -479,7 +480,8 @@ def refine_workload(a, torch, timer):
     """Runtime top-k refinement (StrataFlux section 3.2.1, Eq. 2) after the tiled
     GEMV: per 1024-channel chunk the k = 32 largest |x_i| are selected on the GPU
     and their 4-bit residual columns added to y.  Each launch times the
-    selection, the add, the GEMV, and the three in sequence; the layer and its
+    selection, the add, the GEMV, the three in sequence, and the GEMV with the
+    selection and the add in the same launch; the layer and its
     refinement columns are rotated like the GEMV's.  Refinement bytes = the
     selected columns' codes, scales and zeros, the indices and x entries read,
     and y read and written."""
@@ -537,6 +539,8 @@ def refine_workload(a, torch, timer):
             layers[i % nc].refine_topk(x, ys[i % nc], k, chunk, sels[i % nc])
 
         t_all_call = timer(chain_call, st, wu)
+        # the product with the selection and the add in the same launch
+        t_one = timer(lambda i: layers[i % nc].gemv_tiled_refine(x, ys[i % nc], k, chunk), st, wu)
         Gn = N // 32
         rbytes = n_sel * (N // 2 + 4 * Gn) + 4 * n_sel + 2 * n_sel + 4 * N
         rows.append({"workload": f"refine_topk{k}_per{chunk}_{label}", "N": N, "K": K,
@@ -549,7 +553,9 @@ def refine_workload(a, torch, timer):
                      "gemv_fused_refine_us": round(t_all_fused * 1e3, 3),
                      "refine_topk_with_sel_out_us": round(t_call * 1e3, 3),
                      "gemv_refine_topk_with_sel_out_us": round(t_all_call * 1e3, 3),
-                     "overhead_pct": round(100 * (t_all_call - t_gemv) / t_gemv, 1)})
+                     "two_launch_overhead_pct": round(100 * (t_all_call - t_gemv) / t_gemv, 1),
+                     "gemv_refine_one_launch_us": round(t_one * 1e3, 3),
+                     "one_launch_overhead_pct": round(100 * (t_one - t_gemv) / t_gemv, 1)})
         del layers
     return rows
 

@@ -17,6 +17,6 @@ from ._lib import (  # noqa: F401
     wq_dequant_host, wq_dequant_device, wq_gemv_w4, wq_gemv_w2, wq_gemv_w4p, wq_gemm_wq,
     wq_outlier_add, wq_embed_gather, wq_topk_count, wq_topk_chunks, wq_refine_add,
     wq_refine_topk,
-    wq_tiled_bytes, wq_tile_host, wq_gemv_tiled, wq_gemm_tiled,
+    wq_tiled_bytes, wq_tile_host, wq_gemv_tiled, wq_gemm_tiled, wq_gemv_tiled_refine,
     wq_read_probe, wq_read_probe_sink_words, wq_copy_probe,
 )

@@ -66,6 +66,8 @@ SIGNATURES = {
     "wq_tile_host": (_INT, [_INT, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64]),
     "wq_gemv_tiled": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
     "wq_gemm_tiled": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _I64, _P, _P]),
+    "wq_gemv_tiled_refine": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64,
+                                    _P, _P]),
     "wq_read_probe": (_INT, [_P, _I64, _P, _P]),
     "wq_read_probe_sink_words": (_I64, [_I64]),
     "wq_copy_probe": (_INT, [_P, _P, _I64, _P]),
@@ -284,6 +286,15 @@ def wq_gemm_tiled(fmt, tiled, N, K, X, M, Y, out_idx=None, n_out=0, stream=None)
 def wq_gemv_tiled(fmt, tiled, N, K, x, y, out_idx=None, n_out=0, stream=None):
     _check(load().wq_gemv_tiled(fmt, _dptr(tiled), N, K, _dptr(out_idx) if n_out else None, n_out,
                                 _dptr(x), _dptr(y), _stream(stream)))
+
+
+def wq_gemv_tiled_refine(fmt, tiled, N, K, x, y, rcodes, rscales, rzeros, chunk, k, out_idx=None,
+                         n_out=0, sel_out=None, stream=None):
+    _check(load().wq_gemv_tiled_refine(fmt, _dptr(tiled), N, K, _dptr(out_idx) if n_out else None,
+                                       n_out, _dptr(x), _dptr(y), _dptr(rcodes), _dptr(rscales),
+                                       _dptr(rzeros), chunk, k,
+                                       _dptr(sel_out) if sel_out is not None else None,
+                                       _stream(stream)))
 
 
 def wq_embed_gather(fmt, codes, scales, zeros, V, K, ids, n_ids, out, stream=None):

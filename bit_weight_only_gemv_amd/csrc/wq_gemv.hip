@@ -853,3 +853,40 @@ extern "C" int wq_gemv_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K
                     "outlier positions per 512-channel slice)", who);
   return WQ_OK;
 }
+
+extern "C" int wq_gemv_tiled_refine(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
+                                    const int32_t* out_idx, int64_t n_out, const uint16_t* x,
+                                    uint16_t* y, const uint8_t* rcodes, const uint16_t* rscales,
+                                    const uint16_t* rzeros, int64_t chunk, int64_t k,
+                                    int32_t* sel_out, void* stream) {
+  const char* who = "wq_gemv_tiled_refine";
+  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2 && fmt != WQ_FMT_W4P)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2", who);
+  if (int r = wq::check_shape(N, K, who)) return r;
+  if (n_out < 0 || n_out > K)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: n_out must be in [0, K] (got %lld)", who,
+                    (long long)n_out);
+  if (N % 32) return wq::fail(WQ_ERR_UNSUPPORTED, "%s: N must be a multiple of 32", who);
+  if (chunk < 64 || chunk > 1024 || chunk % 64)
+    return wq::fail(WQ_ERR_UNSUPPORTED, "%s: chunk must be a multiple of 64 in [64, 1024]", who);
+  if (k < 0) return wq::fail(WQ_ERR_INVALID_ARG, "%s: k must be >= 0", who);
+  if (k == 0) return wq_gemv_tiled(fmt, tiled, N, K, out_idx, n_out, x, y, stream);
+  if (!tiled || !x || !y || (n_out > 0 && !out_idx) || !rcodes || !rscales || !rzeros)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (!aligned16(tiled) || !aligned16(x) || !aligned16(y) || (n_out > 0 && !aligned16(out_idx)) ||
+      !aligned16(rcodes))
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: device pointers must be 16-byte aligned", who);
+  if ((uint64_t)K * (uint64_t)N / 2 > 0xFFFFE000ull)
+    return wq::fail(WQ_ERR_UNSUPPORTED, "%s: refinement larger than 4 GB", who);
+  const char* e = getenv("WQ_REFINE_FUSE");
+  if (e == nullptr || atoi(e) != 0) {
+    bool launched = false;
+    const int r = wqd_gemv_refine_mma(fmt, tiled, N, K, out_idx, n_out, x, y, rcodes, rscales,
+                                      rzeros, chunk, k, sel_out, (hipStream_t)stream, who,
+                                      &launched);
+    if (r != WQ_OK || launched) return r;
+  }
+  // two launches: the product (rounded to FP16), then the selection and the add
+  if (int r = wq_gemv_tiled(fmt, tiled, N, K, out_idx, n_out, x, y, stream)) return r;
+  return wq_refine_topk(rcodes, rscales, rzeros, N, K, chunk, k, x, y, sel_out, stream);
+}

@@ -30,3 +30,18 @@ int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
                  int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
                  int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream,
                  const char* who, int mode, bool* launched);
+
+// The tiled M = 1 kernel with the runtime top-k refinement fused in: y =
+// FP16(layer x + sum over the k largest |x_i| of each chunk of x_i C[:, i]),
+// C in the W4 format along N ([K][N / 2] codes, [K][N / 32] scales and zeros).
+// The selection and the add run on helper waves added to the workgroup (up to
+// 12 waves in all) while the others stream the weights.  Launches when the
+// shape suits it (at most 4 refinement units of (chunk, 32 picks, row block)
+// per helper lane, LDS within the limit) and sets *launched;
+// otherwise returns WQ_OK with *launched = false.  sel_out, when not NULL,
+// receives the selection (chunk c's picks at c min(k, chunk)).
+int wqd_gemv_refine_mma(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
+                        const int32_t* out_idx, int64_t n_out, const uint16_t* x, uint16_t* y,
+                        const uint8_t* rcodes, const uint16_t* rscales, const uint16_t* rzeros,
+                        int64_t chunk, int64_t k, int32_t* sel_out, hipStream_t stream,
+                        const char* who, bool* launched);

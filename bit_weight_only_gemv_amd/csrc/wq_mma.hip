@@ -61,6 +61,7 @@
 #include "wq_common.cuh"
 #include "wq_device.h"
 #include "wq_mma.h"
+#include "wq_select.cuh"
 
 #include <stdlib.h>
 
@@ -94,7 +95,24 @@ struct MmaArgs {
   int nrb;           // row blocks (16 rows)
   int rbl;           // row blocks per workgroup, at most
   int nch;           // outlier chunks of 8 slab positions, ceil(n_out / 8)
+  // Runtime top-k refinement (kernels with REF only): the refinement columns
+  // in the W4 format along N ([K][N / 2] codes, [K][N / 32] scales and zeros),
+  // the selection (optional copy, written by workgroup 0), chunk size, picks
+  // per chunk (at most the chunk), chunks, helper waves, and the helpers'
+  // shares: chunks per helper, 32-pick groups per chunk, row blocks per lane
+  // half.
+  const uint8_t* rcodes;
+  const uint16_t* rscales;
+  const uint16_t* rzeros;
+  int32_t* sel_out;
+  int rchunk, rk, rnch, nh;
+  int rc, rp, rh;
 };
+
+// Refinement units (chunk, 32-pick group, row block) one helper lane holds, at
+// most, and the workgroup size with the helper waves.
+constexpr int kRefUnits = 4;
+constexpr int kRefMaxThreads = 768;
 
 // Per-wave LDS region: for each of its slices and each activation row, x
 // (1 KB, masked at the outlier columns), the 16 group sums of x (64 B) and the
@@ -104,10 +122,14 @@ constexpr uint32_t kSliceLds = 1024u + 64u + 64u;
 constexpr int kShareMax = 32;   // slab positions per slice, at most
 
 // LDS layout (byte offsets), identical on host and device.
+// With the refinement also: per helper wave the selection histograms, the
+// picks of every chunk (rnch x rk channel indices and their FP16
+// activations), and the refinement's row sums [row blocks][helpers][16].
 struct MmaLds {
-  uint32_t lut, wave, part, total;
+  uint32_t lut, wave, part, hist, sel, selx, rpart, total;
 };
-__host__ __device__ inline MmaLds mma_lds_layout(int fmt, int nw, int nsw, int rbl, int ms) {
+__host__ __device__ inline MmaLds mma_lds_layout(int fmt, int nw, int nsw, int rbl, int ms,
+                                                 int rnch = 0, int rk = 0, int nh = 0) {
   MmaLds L{};
   uint32_t off = 0;
   L.lut = off;
@@ -116,6 +138,16 @@ __host__ __device__ inline MmaLds mma_lds_layout(int fmt, int nw, int nsw, int r
   off += (uint32_t)nw * (uint32_t)nsw * (uint32_t)ms * kSliceLds;
   L.part = off;
   off += (uint32_t)rbl * (uint32_t)nw * (uint32_t)ms * 64u;
+  L.hist = L.sel = L.selx = L.rpart = off;
+  if (rnch > 0) {
+    off += (uint32_t)nh * (uint32_t)kSelWords * 4u;
+    L.sel = off;
+    off += ((uint32_t)rnch * (uint32_t)rk * 4u + 15u) & ~15u;
+    L.selx = off;
+    off += ((uint32_t)rnch * (uint32_t)rk * 2u + 15u) & ~15u;
+    L.rpart = off;
+    off += (uint32_t)rbl * (uint32_t)nh * 64u;
+  }
   L.total = off;
   return L;
 }
@@ -167,15 +199,17 @@ __device__ __forceinline__ float slab_dot(const uint32_t (&od)[5], const uint32_
   return v;
 }
 
-template <int FMT, bool OUT, bool TILED, int NSW, int MS>
-__global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
+template <int FMT, bool OUT, bool TILED, int NSW, int MS, bool REF>
+__global__ void __launch_bounds__(REF ? kRefMaxThreads : 512) mma1d_kernel(MmaArgs a) {
   typedef MmaFmt<FMT> F;
   constexpr int DEPTH = 2;
   static_assert(MS == 1 || MS == 2 || (MS == 4 && FMT != 2), "1, 2 or (W4) 4 activation rows");
+  static_assert(!REF || MS == 1, "the refinement runs with one activation row");
   constexpr int WG = 16 / MS;   // groups per window: each slice is taken in MS windows
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_out = OUT ? a.n_out : 0;
-  const MmaLds L = mma_lds_layout(FMT, a.nw, a.nsw, a.rbl, MS);
+  const MmaLds L =
+      mma_lds_layout(FMT, a.nw, a.nsw, a.rbl, MS, REF ? a.rnch : 0, REF ? a.rk : 0, REF ? a.nh : 0);
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int lane = tid & 63;
@@ -185,7 +219,11 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   const int G = a.K >> 5;
   const uint32_t row_bytes = (uint32_t)a.K / F::kRowBytesDiv;
   const int nrb_wg = (a.nrb - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int ns_w = (a.nks - w + a.nw - 1) / a.nw;   // 1 .. NSW (nw <= nks)
+  // With the refinement, waves nw .. nw + nh - 1 are helpers: they take part
+  // in the workgroup's set-up and barriers but own no slices (no items).
+  const bool helper = REF && w >= a.nw;
+  const int hw = w - a.nw;                           // helper index
+  const int ns_w = helper ? 0 : (a.nks - w + a.nw - 1) / a.nw;   // 1 .. NSW (nw <= nks)
   const int T = ns_w * nrb_wg;                       // items of this wave
   const uint32_t wave_bytes = (uint32_t)a.nsw * MS * kSliceLds;
   const uint32_t wreg = L.wave + (uint32_t)w * wave_bytes;
@@ -403,6 +441,126 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
   for (int d = 1; d < DEPTH; ++d) {
     load_item(buf[d], d < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
     advance(ls, lr);
+  }
+
+  // ---- (3b) refinement (StrataFlux page, section 3.2.1 and Eq. 2), on the
+  //      helper waves while the others stream the weights: helper hw selects
+  //      the k largest |x| of its chunks (hw, hw + nh, ...) into LDS, then
+  //      loads, for each of its units, the 16 code bytes of one picked column
+  //      over the 32-row group of one of the workgroup's row blocks, with the
+  //      group's scale and zero.  Lane l takes pick 32 p + l % 32 of the unit's
+  //      chunk and row block (l / 32) rh + h.
+  const int nselh = REF ? min(a.nh, a.rnch) : 0;   // helpers with one chunk or more
+  const int nunits = REF ? a.rc * a.rp * a.rh : 0;
+  u4v rcw[REF ? kRefUnits : 1];
+  uint16_t rsv[REF ? kRefUnits : 1], rzv[REF ? kRefUnits : 1];   // FP16 scale, zero
+  uint32_t rxv[REF ? kRefUnits : 1];   // the pick's FP16 activation; 0 when the unit is empty
+  // The products of the units: per unit, pick x (q - z) s for the 16 rows of
+  // its row block (the row block's half of the group: low nibbles for an even
+  // one, high for an odd one), summed over the 32 picks of the lane half by a
+  // butterfly that leaves row ((l % 32) >> 1) on lane l; units of the same row
+  // block are added in unit order, and lane pairs store their row's sum.
+  float* s_rpart = reinterpret_cast<float*>(smem + L.rpart);
+  auto refine_units = [&]() {
+    if constexpr (REF) {
+      float red[kRefUnits];
+#pragma unroll
+      for (int hh = 0; hh < kRefUnits; ++hh) red[hh] = 0.f;
+#pragma unroll
+      for (int u = 0; u < kRefUnits; ++u) {
+        if (u < nunits) {
+          const int h = u % a.rh;
+          const int ri = (lane >> 5) * a.rh + h;
+          // an empty unit holds zeros everywhere and adds 0
+          const float xs = h2f((uint16_t)rxv[u]) * h2f(rsv[u]);
+          const float z = h2f(rzv[u]);
+          const uint32_t sh = 4u * ((blockIdx.x + (uint32_t)ri * gridDim.x) & 1u);
+          const uint32_t dw[4] = {rcw[u].x, rcw[u].y, rcw[u].z, rcw[u].w};
+          float v[16];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float q = (float)((dw[i] >> (8 * j + sh)) & 0x0Fu);
+              v[4 * i + j] = (q - z) * xs;
+            }
+          // reduce-scatter over the 32 lanes of the half: rows by lane bits 4..1
+#pragma unroll
+          for (int st = 8; st >= 1; st >>= 1) {
+            const bool upper = (lane & (2 * st)) != 0;
+#pragma unroll
+            for (int j = 0; j < st; ++j) {
+              const float send = upper ? v[j] : v[j + st];
+              const float keep = upper ? v[j + st] : v[j];
+              v[j] = keep + __shfl_xor(send, 2 * st);
+            }
+          }
+          v[0] += __shfl_xor(v[0], 1);
+#pragma unroll
+          for (int hh = 0; hh < kRefUnits; ++hh) red[hh] += hh == h ? v[0] : 0.f;
+        }
+      }
+      if ((lane & 1) == 0) {
+#pragma unroll
+        for (int hh = 0; hh < kRefUnits; ++hh) {
+          const int ri = (lane >> 5) * a.rh + hh;
+          if (hh < a.rh && ri < nrb_wg)
+            s_rpart[((uint32_t)ri * (uint32_t)a.nh + (uint32_t)hw) * 16u +
+                    (uint32_t)((lane & 31) >> 1)] = red[hh];
+        }
+      }
+    }
+  };
+  if (REF && helper && hw < nselh) {
+    // the helper's work is short and latency-bound: it issues ahead of the
+    // waves that stream the weights
+    __builtin_amdgcn_s_setprio(3);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + L.hist) + hw * kSelWords;
+    int32_t* s_sel = reinterpret_cast<int32_t*>(smem + L.sel);
+    uint16_t* s_selx = reinterpret_cast<uint16_t*>(smem + L.selx);
+    // chunks hw, hw + nh, ...: lane l holds channels 16 l .. 16 l + 15 (a
+    // helper has no other loads in flight)
+    for (int cw = 0; cw < a.rc; ++cw) {
+      const int cc = hw + a.nh * cw;
+      if (cc < a.rnch) {
+        const int c0 = cc * a.rchunk;
+        const int csize = min(a.rchunk, a.K - c0);
+        const int kk = min(a.rk, csize);
+        const uint32_t off = 16 * lane < csize ? (uint32_t)(c0 + 16 * lane) * 2u : kOob;
+        const u4v t0 = ld128(xrs, off), t1 = ld128(xrs, off + 16u);
+        const uint32_t xsel[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+        wave_topk_regs<true>(xsel, c0, csize, kk, hist, s_sel + cc * a.rk, s_selx + cc * a.rk,
+                             lane);
+        if (a.sel_out != nullptr && blockIdx.x == 0) {
+          wave_lds_sync();
+          for (int j = lane; j < kk; j += kWave) a.sel_out[cc * a.rk + j] = s_sel[cc * a.rk + j];
+        }
+      }
+    }
+    wave_lds_sync();
+    const __amdgpu_buffer_rsrc_t rcrs =
+        make_rsrc(a.rcodes, clamp_bytes((uint64_t)a.K * (uint64_t)(a.N / 2)));
+    const uint64_t rmeta = (uint64_t)a.K * (uint64_t)(a.N / 32) * 2u;
+    const __amdgpu_buffer_rsrc_t rsrs = make_rsrc(a.rscales, clamp_bytes(rmeta));
+    const __amdgpu_buffer_rsrc_t rzrs = make_rsrc(a.rzeros, clamp_bytes(rmeta));
+#pragma unroll
+    for (int u = 0; u < kRefUnits; ++u) {
+      const int h = u % a.rh, pg = (u / a.rh) % a.rp, cw = u / (a.rh * a.rp);
+      const int cc = hw + a.nh * cw;
+      const int ri = (lane >> 5) * a.rh + h;
+      const int pos = 32 * pg + (lane & 31);
+      const int kk = cc < a.rnch ? min(a.rk, a.K - cc * a.rchunk) : 0;
+      const bool on = u < nunits && cc < a.rnch && pos < kk && ri < nrb_wg;
+      const uint32_t ch = on ? (uint32_t)s_sel[cc * a.rk + pos] : 0u;
+      const uint32_t grp = (blockIdx.x + (uint32_t)ri * gridDim.x) >> 1;   // 32-row group
+      rcw[u] = ld128(rcrs, on ? ch * (uint32_t)(a.N / 2) + grp * 16u : kOob);
+      const uint32_t mo = on ? (ch * (uint32_t)(a.N / 32) + grp) * 2u : kOob;
+      rsv[u] = ld16(rsrs, mo);
+      rzv[u] = ld16(rzrs, mo);
+      rxv[u] = on ? (uint32_t)s_selx[cc * a.rk + pos] : 0u;
+    }
+    refine_units();
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // ---- A fragments, group sums and outlier activations of slice s.  The 16
@@ -661,6 +819,8 @@ __global__ void __launch_bounds__(512) mma1d_kernel(MmaArgs a) {
       if (row >= a.N) continue;
       float s = 0.f;
       for (int k = 0; k < a.nw; ++k) s += s_part[((uint32_t)ri2 * a.nw + k) * 16u + n];
+      if constexpr (REF)
+        for (int k = 0; k < nselh; ++k) s += s_rpart[((uint32_t)ri2 * a.nh + k) * 16u + n];
       a.y[row] = f2h(s);
     }
   } else {
@@ -1351,16 +1511,12 @@ int wqd_gemv_mma(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scal
                       stream, who, mode, launched);
 }
 
-int wqd_mma_rows(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scales,
-                 const uint16_t* zeros, int64_t N, int64_t K, const int32_t* out_idx,
-                 const uint16_t* out_w, int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y,
-                 hipStream_t stream, const char* who, int mode, bool* launched) {
-  *launched = false;
-  if (mode == 0 || M < 1 || M > 4 || (M > 2 && fmt == 2)) return WQ_OK;
-  const int ms = M <= 2 ? (int)M : 4;   // three rows run as four, the last one empty
-  const MmaPlan p = plan_mma1(fmt, tiled, N, K, n_out, ms);
-  if (ms == 4 && p.nswt > 4) return WQ_OK;   // registers: four rows of x per slice
-  if (!p.ok || (mode == 1 && !p.preferred)) return WQ_OK;
+// Kernel arguments of a plan (the tiled layout's three arrays sit at the
+// offsets of its geometry inside one buffer).
+static MmaArgs mma_args(const MmaPlan& p, int fmt, bool tiled, const uint8_t* codes,
+                        const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K,
+                        const int32_t* out_idx, const uint16_t* out_w, int64_t n_out,
+                        const uint16_t* X, int64_t M, uint16_t* Y) {
   MmaArgs a{};
   if (tiled) {
     const wq::TiledGeometry g = wq::tiled_geometry(fmt, N, K, n_out);
@@ -1387,14 +1543,30 @@ int wqd_mma_rows(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scal
   a.nrb = p.nrb;
   a.rbl = p.rbl;
   a.nch = p.nch;
+  return a;
+}
+
+int wqd_mma_rows(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scales,
+                 const uint16_t* zeros, int64_t N, int64_t K, const int32_t* out_idx,
+                 const uint16_t* out_w, int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y,
+                 hipStream_t stream, const char* who, int mode, bool* launched) {
+  *launched = false;
+  if (mode == 0 || M < 1 || M > 4 || (M > 2 && fmt == 2)) return WQ_OK;
+  const int ms = M <= 2 ? (int)M : 4;   // three rows run as four, the last one empty
+  const MmaPlan p = plan_mma1(fmt, tiled, N, K, n_out, ms);
+  if (ms == 4 && p.nswt > 4) return WQ_OK;   // registers: four rows of x per slice
+  if (!p.ok || (mode == 1 && !p.preferred)) return WQ_OK;
+  const MmaArgs a = mma_args(p, fmt, tiled, codes, scales, zeros, N, K, out_idx, out_w, n_out, X,
+                             M, Y);
   const dim3 grid(p.grid), block(p.nw * kWave);
-#define WQ_MMA_LAUNCH_R(F_, O_, T_, S_, R_)                                                  \
-  if (fmt == F_ && (n_out > 0) == O_ && tiled == T_ && p.nswt == S_ && ms == R_) {           \
-    if (!allow_lds(reinterpret_cast<const void*>(&mma1d_kernel<F_, O_, T_, S_, R_>), p.lds)) \
-      return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds); \
-    hipLaunchKernelGGL((mma1d_kernel<F_, O_, T_, S_, R_>), grid, block, p.lds, stream, a);    \
-    *launched = true;                                                                        \
-    return check_launch(who);                                                                \
+#define WQ_MMA_LAUNCH_R(F_, O_, T_, S_, R_)                                                   \
+  if (fmt == F_ && (n_out > 0) == O_ && tiled == T_ && p.nswt == S_ && ms == R_) {            \
+    if (!allow_lds(reinterpret_cast<const void*>(&mma1d_kernel<F_, O_, T_, S_, R_, false>),   \
+                   p.lds))                                                                    \
+      return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds);  \
+    hipLaunchKernelGGL((mma1d_kernel<F_, O_, T_, S_, R_, false>), grid, block, p.lds, stream, a); \
+    *launched = true;                                                                         \
+    return check_launch(who);                                                                 \
   }
 #define WQ_MMA_LAUNCH(F_, O_, T_, S_) WQ_MMA_LAUNCH_R(F_, O_, T_, S_, 1) WQ_MMA_LAUNCH_R(F_, O_, T_, S_, 2)
 // four rows: W4 and W4P, at most 4 slices per wave
@@ -1415,6 +1587,58 @@ int wqd_mma_rows(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scal
 #undef WQ_MMA_LAUNCH_R
 #undef WQ_MMA_SLICES4
 #undef WQ_MMA_LAYOUTS4
+  return WQ_OK;
+}
+
+int wqd_gemv_refine_mma(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
+                        const int32_t* out_idx, int64_t n_out, const uint16_t* x, uint16_t* y,
+                        const uint8_t* rcodes, const uint16_t* rscales, const uint16_t* rzeros,
+                        int64_t chunk, int64_t k, int32_t* sel_out, hipStream_t stream,
+                        const char* who, bool* launched) {
+  *launched = false;
+  MmaPlan p = plan_mma1(fmt, true, N, K, n_out, 1);
+  if (!p.ok || chunk < 1 || k < 1) return WQ_OK;
+  const int rk = (int)std::min(k, chunk);
+  const int rnch = (int)((K + chunk - 1) / chunk);
+  // helper waves: up to the workgroup size, at most one per chunk
+  const int nh = std::min(rnch, kRefMaxThreads / kWave - p.nw);
+  if (nh < 1) return WQ_OK;
+  const int rc = (rnch + nh - 1) / nh;
+  const int rp = (rk + 31) / 32;
+  const int rh = (p.rbl + 1) / 2;
+  if ((int64_t)rc * rp * rh > kRefUnits) return WQ_OK;   // registers: at most 4 units per lane
+  const MmaLds L = mma_lds_layout(fmt, p.nw, p.nsw, p.rbl, 1, rnch, rk, nh);
+  if (L.total > kMaxLdsBytes) return WQ_OK;
+  p.lds = L.total;
+  MmaArgs a = mma_args(p, fmt, true, tiled, nullptr, nullptr, N, K, out_idx, nullptr, n_out, x,
+                       1, y);
+  a.rcodes = rcodes;
+  a.rscales = rscales;
+  a.rzeros = rzeros;
+  a.sel_out = sel_out;
+  a.rchunk = (int)chunk;
+  a.rk = rk;
+  a.rnch = rnch;
+  a.nh = nh;
+  a.rc = rc;
+  a.rp = rp;
+  a.rh = rh;
+  const dim3 grid(p.grid), block((p.nw + nh) * kWave);
+#define WQ_MMA_REF(F_, O_, S_)                                                                \
+  if (fmt == F_ && (n_out > 0) == O_ && p.nswt == S_) {                                        \
+    if (!allow_lds(reinterpret_cast<const void*>(&mma1d_kernel<F_, O_, true, S_, 1, true>),    \
+                   p.lds))                                                                     \
+      return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds);   \
+    hipLaunchKernelGGL((mma1d_kernel<F_, O_, true, S_, 1, true>), grid, block, p.lds, stream, a); \
+    *launched = true;                                                                          \
+    return check_launch(who);                                                                  \
+  }
+#define WQ_MMA_REF_S(F_, O_) WQ_MMA_REF(F_, O_, 1) WQ_MMA_REF(F_, O_, 2) WQ_MMA_REF(F_, O_, 4) \
+  WQ_MMA_REF(F_, O_, 8)
+  WQ_MMA_REF_S(2, true) WQ_MMA_REF_S(2, false) WQ_MMA_REF_S(4, true) WQ_MMA_REF_S(4, false)
+  WQ_MMA_REF_S(5, true) WQ_MMA_REF_S(5, false)
+#undef WQ_MMA_REF_S
+#undef WQ_MMA_REF
   return WQ_OK;
 }
 

@@ -9,13 +9,9 @@
 // stored per input channel (C transposed, [K][N]) in the W4 format along N
 // (groups of 32 output rows, FP16 scale and zero, in-group nibble interleave).
 //
-// Selection (wave_chunk_topk): one wave per chunk, lane l holding channels
-// 16l .. 16l + 15.  The k-th largest FP16 magnitude T comes from two histogram
-// passes in the wave's own LDS (the top 7 bits of the 15-bit magnitude, then
-// the low 8 bits inside the chosen bin); every channel above T is kept, and of
-// those equal to T the lowest-indexed ones, counted by a wave prefix sum, fill
-// the rest.  The picks are written in index order.  No block barrier is
-// needed.
+// Selection (wave_chunk_topk, wq_select.cuh): one wave per chunk, lane l
+// holding channels 16l .. 16l + 15; the k-th largest FP16 magnitude comes from
+// two histogram passes in the wave's own LDS.  No block barrier is needed.
 //
 // Refinement add (refine_groups): a workgroup of 512 threads owns GPW groups of
 // 32 output rows and splits the selected columns over 128 slots of 4 threads;
@@ -32,155 +28,16 @@
 
 #include "wq_common.cuh"
 #include "wq_device.h"
+#include "wq_select.cuh"
 
 namespace wqd {
 
 constexpr uint32_t kOobR = 0xFFFFF000u;       // past every buffer: loads return 0
-constexpr int kSelBins1 = 128;                // magnitude bits 14..8
-constexpr int kSelBins2 = 256;                // magnitude bits 7..0
-constexpr int kSelWords = kSelBins1 + kSelBins2 + 4;   // per wave: both histograms + state
 constexpr int kRefineThreads = 512;
 constexpr int kRefineSlots = kRefineThreads / 4;       // column slots per workgroup
 constexpr int kRefineUnroll = 4;              // columns per slot with loads in flight
 constexpr int kRefineRuns = kRefineThreads / kGroup;   // 16 runs of 8 slots in the sum
 constexpr int kFusedMaxSel = 4096;            // selections the fused kernel holds in LDS
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
-}
-
-// Per wave (all 64 lanes active): the sum of v over the lanes below this one,
-// and over all lanes in `total`.  Inclusive scan with DPP: shifts by 1, 2, 4, 8
-// inside each row of 16 lanes, then the row broadcasts of lanes 15 and 31.
-__device__ __forceinline__ uint32_t wave_excl_sum(uint32_t v, uint32_t& total) {
-  const int lane = (int)__lane_id();
-  const int rl = lane & 15;
-  uint32_t r = v, t;
-  t = dpp_mov<0x111>(r);   // row_shr:1
-  if (rl >= 1) r += t;
-  t = dpp_mov<0x112>(r);   // row_shr:2
-  if (rl >= 2) r += t;
-  t = dpp_mov<0x114>(r);   // row_shr:4
-  if (rl >= 4) r += t;
-  t = dpp_mov<0x118>(r);   // row_shr:8
-  if (rl >= 8) r += t;
-  t = dpp_mov<0x142>(r);   // row_bcast:15
-  if ((lane & 31) >= 16) r += t;
-  t = dpp_mov<0x143>(r);   // row_bcast:31
-  if (lane >= 32) r += t;
-  total = (uint32_t)__builtin_amdgcn_readlane((int)r, 63);
-  return r - v;
-}
-
-// One wave: of the csize channels c0 .. c0 + csize - 1 (csize a multiple of 32,
-// at most 1024), the kk of largest |x| with ties to the lower index, written
-// ascending to out[0 .. kk).  hist: this wave's kSelWords words of LDS.
-__device__ __forceinline__ void wave_chunk_topk(__amdgpu_buffer_rsrc_t xrs, int c0, int csize, int kk,
-                                uint32_t* hist, int32_t* out, int lane) {
-  const bool valid = 16 * lane < csize;
-  uint32_t m[16];
-  {
-    const uint32_t off = valid ? (uint32_t)(c0 + 16 * lane) * 2u : kOobR;
-    const u4v a = ld128(xrs, off), b = ld128(xrs, off + 16u);
-    const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      m[2 * i] = wv[i] & 0x7FFFu;
-      m[2 * i + 1] = (wv[i] >> 16) & 0x7FFFu;
-    }
-  }
-  const bool all = kk >= csize;
-  uint32_t T = 0u, keq = 0u;   // keep |x| > T, and the first keq channels with |x| == T
-  if (!all && kk > 0) {
-    uint32_t* h1 = hist;
-    uint32_t* h2 = hist + kSelBins1;
-    uint32_t* st = hist + kSelBins1 + kSelBins2;
-    h1[lane] = 0u;
-    h1[lane + kWave] = 0u;
-#pragma unroll
-    for (int i = 0; i < kSelBins2 / kWave; ++i) h2[lane + kWave * i] = 0u;
-    wave_lds_sync();
-    if (valid) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) atomicAdd(&h1[m[e] >> 8], 1u);
-    }
-    wave_lds_sync();
-    {
-      // lane l holds bins 2l (lower) and 2l + 1 (higher); exactly one bin holds
-      // the kk-th largest (1 <= kk < number of valid channels)
-      const uint32_t rem = (uint32_t)kk;
-      const uint32_t lo = h1[2 * lane], hi = h1[2 * lane + 1];
-      uint32_t tot;
-      const uint32_t below = wave_excl_sum(lo + hi, tot);
-      const uint32_t suf = tot - below;                     // bins >= 2l
-      const uint32_t above = suf - lo - hi;                 // bins >= 2l + 2
-      if (above < rem && rem <= above + hi) {
-        st[0] = 2u * lane + 1u;
-        st[1] = rem - above;
-      } else if (above + hi < rem && rem <= suf) {
-        st[0] = 2u * lane;
-        st[1] = rem - above - hi;
-      }
-    }
-    wave_lds_sync();
-    const uint32_t b1 = st[0];
-    const uint32_t rem = st[1];
-    if (valid) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if ((m[e] >> 8) == b1) atomicAdd(&h2[m[e] & 0xFFu], 1u);
-    }
-    wave_lds_sync();
-    {
-      uint32_t hb[4], sum = 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hb[i] = h2[4 * lane + i];
-        sum += hb[i];
-      }
-      uint32_t tot;
-      const uint32_t below = wave_excl_sum(sum, tot);
-      uint32_t cum = tot - below - sum;                     // bins >= 4l + 4
-#pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        if (cum < rem && rem <= cum + hb[i]) {
-          st[2] = (b1 << 8) | (uint32_t)(4 * lane + i);
-          st[3] = rem - cum;
-        }
-        cum += hb[i];
-      }
-    }
-    wave_lds_sync();
-    T = st[2];
-    keq = st[3];
-  }
-  uint32_t gt = 0u, eq = 0u;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const bool g = valid && (all || (kk > 0 && m[e] > T));
-    const bool q = valid && !all && kk > 0 && m[e] == T;
-    gt |= (uint32_t)g << e;
-    eq |= (uint32_t)q << e;
-  }
-  const uint32_t neq = (uint32_t)__builtin_popcount(eq);
-  uint32_t tot;
-  const uint32_t eq_before = wave_excl_sum(neq, tot);
-  uint32_t keep = gt;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const uint32_t rank = eq_before + (uint32_t)__builtin_popcount(eq & ((1u << e) - 1u));
-    if (((eq >> e) & 1u) && rank < keq) keep |= 1u << e;
-  }
-  const uint32_t cnt = (uint32_t)__builtin_popcount(keep);
-  uint32_t pos = wave_excl_sum(cnt, tot);
-#pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if ((keep >> e) & 1u) {
-      if (pos < (uint32_t)kk) out[pos] = c0 + 16 * lane + e;   // never past the chunk's picks
-      ++pos;
-    }
-}
 
 // One chunk per workgroup of one wave.
 __global__ void __launch_bounds__(kWave) topk_kernel(const uint16_t* __restrict__ x, int K,

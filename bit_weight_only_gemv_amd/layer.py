@@ -173,6 +173,15 @@ class DeviceLayer:
         L.wq_refine_topk(self.r_codes, self.r_scales, self.r_zeros, self.N, self.K, chunk, k, x, y,
                          sel_out, stream)
 
+    def gemv_tiled_refine(self, x, y, k, chunk=1024, sel_out=None, stream=None):
+        """The tiled product with the selection and add of StrataFlux Eq. 2 in
+        the same launch (one FP16 rounding)."""
+        if self.tiled is None:
+            raise ValueError("layer built without tiled=True")
+        L.wq_gemv_tiled_refine(self.fmt, self.tiled, self.N, self.K, x, y, self.r_codes,
+                               self.r_scales, self.r_zeros, chunk, k, self.idx, self.n_out, sel_out,
+                               stream)
+
     def dequant(self, W_hat, stream=None):
         L.wq_dequant_device(self.fmt, self.codes, self.scales, self.zeros, self.N, self.K, W_hat,
                             stream)

@@ -321,6 +321,29 @@ int wq_gemv_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K, const int
 int wq_gemm_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K, const int32_t* out_idx,
                   int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y, void* stream);
 
+/* The tiled M = 1 product with the runtime top-k refinement of StrataFlux
+ * (section 3.2.1, Eq. 2) in the same launch:
+ *   y[n] = FP16( sum_k w_hat[n][k] x[k] (outlier pass fused)
+ *                + sum_{i in S(x)} x_i C[n][i] ),   FP32 accumulation,
+ * with S(x) exactly as wq_topk_chunks makes it and C the W4 refinement columns
+ * of wq_refine_add (rcodes [K][N/2], rscales / rzeros [K][N/32]).  Every
+ * workgroup selects for itself while its first weights are in flight, loads
+ * the picked columns for its own row blocks behind them, and adds their
+ * products before the one rounding to FP16.  sel_out (int32, device,
+ * wq_topk_count(K, chunk, k) entries) receives S(x) if not NULL.  Where the
+ * one-launch kernel does not fit (more than 4 units of one chunk, 32 picks
+ * and one row block per lane, i.e. large k, many chunks per wave or many row
+ * blocks per workgroup; or LDS), the call runs wq_gemv_tiled and then
+ * wq_refine_topk: the same selection, and y within the same bound, but with
+ * the product rounded to FP16 before the add.  The environment variable
+ * WQ_REFINE_FUSE=0 forces that path (for comparisons).  Limits: those of
+ * wq_gemv_tiled, plus N % 32 == 0, chunk a multiple of 64 in [64, 1024], and
+ * rcodes, x, y 16-byte aligned; k == 0 is wq_gemv_tiled alone. */
+int wq_gemv_tiled_refine(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
+                         const int32_t* out_idx, int64_t n_out, const uint16_t* x, uint16_t* y,
+                         const uint8_t* rcodes, const uint16_t* rscales, const uint16_t* rzeros,
+                         int64_t chunk, int64_t k, int32_t* sel_out, void* stream);
+
 /* -------------------------------------------------- measurement support
  * Not part of the method: kernels of known traffic that calibrate bandwidth
  * figures and hardware byte counters. */

@@ -560,6 +560,82 @@ def test_refine_topk_with_selection_buffer(fmt):
     assert ok
 
 
+# (fmt, N, K, chunk, k, outliers, fused): whether the one-launch kernel takes the
+# shape (at most 4 units of chunk x 32 picks x row block per helper lane) or the
+# call runs the product and then the selection and add
+TILED_REFINE_CASES = [
+    (2, 14336, 4096, 1024, 32, True, True),     # the default W2 layer: 2 row blocks per lane half
+    (4, 4096, 14336, 1024, 32, True, True),     # 14 chunks on 5 helper waves
+    (5, 3584, 4096, 1024, 32, True, True),      # fewer row blocks than compute units
+    (4, 7168, 4096, 512, 48, False, True),      # two 32-pick groups per chunk
+    (4, 28672, 1024, 1024, 16, True, True),     # 7 row blocks per workgroup: 4 per lane half
+    (2, 512, 2048, 1024, 8, True, True),
+    (4, 96, 1088, 1024, 100, True, True),       # k above a short last chunk (64 channels)
+    (2, 64, 1024, 64, 64, True, True),          # 16 chunks on 10 helper waves
+    (4, 40960, 1024, 1024, 16, True, False),    # 10 row blocks per workgroup: two launches
+    (4, 128, 4096, 1024, 1024, False, False),   # every channel picked: two launches
+]
+
+
+@pytest.mark.parametrize("fmt,N,K,chunk,k,outl,fused", TILED_REFINE_CASES)
+def test_gemv_tiled_refine(fmt, N, K, chunk, k, outl, fused, monkeypatch):
+    """The tiled product with the refinement in the same launch: S(x) equal to the
+    oracle's, y within the bound of the refined product, and the same
+    selection and bound on the two-launch path (WQ_REFINE_FUSE=0), which must be
+    bit-identical to wq_gemv_tiled followed by wq_refine_topk.  Where the fused
+    kernel runs, y is rounded once and differs from the two-launch y."""
+    from bit_weight_only_gemv_amd.layer import refinement_host
+    say(f"tiled gemv + refinement fmt={fmt} N={N} K={K} chunk={chunk} k={k} outliers={outl}")
+    L = synthetic.small_layer(fmt, N, K, with_outliers=outl, seed=k + 3)
+    ref, dl = build_tiled(fmt, L.W, L.profile, L.ratio)
+    hl = pack_host(fmt, L.W, L.profile, L.ratio)
+    dl.set_refinement(refinement_host(L.W, hl))
+    x = L.x.reshape(-1)
+    xd = dev_fp16(x)
+    n = B.wq_topk_count(K, chunk, k)
+    S = O.topk_chunks(x, k, chunk)
+    rq, rs, rz = O.refinement_w4(L.W, ref.w_hat(), ref.idx)
+    c_hat = O.dequant_w4(rq, rs, rz)
+    y0, a0 = O.matvec_ref(ref.w_hat(), x, ref.idx, ref.wout)
+    terms = x.astype(np.float64)[S][:, None] * c_hat.astype(np.float64)[S]
+    outs = {}
+    for mode in ("1", "0"):
+        monkeypatch.setenv("WQ_REFINE_FUSE", mode)
+        y = torch.full((N,), -1, dtype=torch.int16, device="cuda")
+        sel = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+        dl.gemv_tiled_refine(xd, y, k, chunk, sel)
+        torch.cuda.synchronize()
+        assert np.array_equal(sel.cpu().numpy(), S)
+        ok, worst = O.check_tolerance(host_fp16(y).astype(np.float64), y0[0] + terms.sum(0),
+                                      a0[0] + np.abs(terms).sum(0))
+        say(f"  WQ_REFINE_FUSE={mode}: worst |err|/bound = {worst:.4f}")
+        assert ok
+        outs[mode] = y.cpu().numpy()
+    # the two-launch path is exactly the product followed by the fused selection + add
+    y2 = torch.full((N,), -1, dtype=torch.int16, device="cuda")
+    dl.gemv_tiled(xd, y2)
+    dl.refine_topk(xd, y2, k, chunk)
+    torch.cuda.synchronize()
+    assert np.array_equal(outs["0"], y2.cpu().numpy())
+    if not fused:
+        assert np.array_equal(outs["1"], outs["0"])
+    elif N >= 2048:
+        assert not np.array_equal(outs["1"], outs["0"])
+    # refinement moves the product toward the unquantized layer wherever it does
+    # so clearly in float64 (a few picks among thousands of channels, or picks
+    # that are all outlier columns with zero refinement, barely move it)
+    exact = L.W.astype(np.float64) @ x.astype(np.float64)
+    y_ref = outs["1"].view(np.float16).astype(np.float64)
+    base = torch.full((N,), -1, dtype=torch.int16, device="cuda")
+    dl.gemv_tiled(xd, base)
+    torch.cuda.synchronize()
+    y_base = host_fp16(base).astype(np.float64)
+    gain = np.abs(y0[0] + terms.sum(0) - exact).mean() / np.abs(y0[0] - exact).mean()
+    say(f"  float64 refined / base mean error = {gain:.4f}")
+    if gain < 0.98:
+        assert np.abs(y_ref - exact).mean() < np.abs(y_base - exact).mean()
+
+
 @pytest.mark.parametrize("gpw", ["1", "2", "4"])
 @pytest.mark.parametrize("N,K", [(96, 2048), (14336 // 4, 4096), (4096, 14336 // 2)])
 def test_refine_groups_per_workgroup(gpw, N, K, monkeypatch):

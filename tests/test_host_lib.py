@@ -178,6 +178,16 @@ def test_error_codes():
     assert lib.wq_gemm_tiled(4, fake, 64, 512, None, 0, fake, 0, fake, None) == -1
     assert lib.wq_gemm_tiled(4, None, 64, 512, None, 0, fake, 2, fake, None) == -1
     assert lib.wq_gemm_tiled(3, fake, 64, 512, None, 0, fake, 2, fake, None) == -1
+    # tiled product with the refinement fused in
+    R = lib.wq_gemv_tiled_refine
+    assert R(3, fake, 64, 512, None, 0, fake, fake, fake, fake, fake, 1024, 8, None, None) == -1
+    assert R(4, fake, 48, 512, None, 0, fake, fake, fake, fake, fake, 1024, 8, None, None) == -2
+    assert R(4, fake, 64, 512, None, 0, fake, fake, fake, fake, fake, 32, 8, None, None) == -2
+    assert R(4, fake, 64, 512, None, 0, fake, fake, fake, fake, fake, 2048, 8, None, None) == -2
+    assert R(4, fake, 64, 512, None, 0, fake, fake, fake, fake, fake, 1024, -1, None, None) == -1
+    assert R(4, fake, 64, 512, None, -1, fake, fake, fake, fake, fake, 1024, 8, None, None) == -1
+    assert R(4, fake, 64, 512, None, 0, fake, fake, None, fake, fake, 1024, 8, None, None) == -1
+    assert R(4, fake, 64, 512, None, 0, None, fake, fake, fake, fake, 1024, 0, None, None) == -1
 
 
 # ------------------------------------------------- W4P packed zero points
