@@ -572,6 +572,8 @@ TILED_REFINE_CASES = [
     (2, 512, 2048, 1024, 8, True, True),
     (4, 96, 1088, 1024, 100, True, True),       # k above a short last chunk (64 channels)
     (2, 64, 1024, 64, 64, True, True),          # 16 chunks on 10 helper waves
+    (5, 96, 1088, 64, 1, True, True),           # 17 chunks of 64, one pick each
+    (2, 32, 512, 64, 7, False, True),           # one 512-channel slice, smallest N
     (4, 40960, 1024, 1024, 16, True, False),    # 10 row blocks per workgroup: two launches
     (4, 128, 4096, 1024, 1024, False, False),   # every channel picked: two launches
 ]
@@ -634,6 +636,39 @@ def test_gemv_tiled_refine(fmt, N, K, chunk, k, outl, fused, monkeypatch):
     say(f"  float64 refined / base mean error = {gain:.4f}")
     if gain < 0.98:
         assert np.abs(y_ref - exact).mean() < np.abs(y_base - exact).mean()
+
+
+@pytest.mark.parametrize("fmt", [4, 2])
+def test_gemv_tiled_refine_zero_chunk(fmt):
+    """A chunk of x that is all zeros (and one of all-equal magnitudes): the
+    picks are its lowest indices (ties go to the lower index), and their
+    refinement adds nothing (zero activations) or exactly the oracle's terms."""
+    from bit_weight_only_gemv_amd.layer import refinement_host
+    N, K, chunk, k = 256, 3072, 1024, 16
+    say(f"tiled gemv + refinement with a zero chunk fmt={fmt}")
+    L = synthetic.small_layer(fmt, N, K, with_outliers=True, seed=5)
+    ref, dl = build_tiled(fmt, L.W, L.profile, L.ratio)
+    hl = pack_host(fmt, L.W, L.profile, L.ratio)
+    dl.set_refinement(refinement_host(L.W, hl))
+    x = L.x.reshape(-1).copy()
+    x[:chunk] = 0.0
+    x[chunk:2 * chunk] = np.where(np.arange(chunk) % 2, 0.5, -0.5).astype(np.float16)
+    n = B.wq_topk_count(K, chunk, k)
+    S = O.topk_chunks(x, k, chunk)
+    assert np.array_equal(S[:k], np.arange(k)) and np.array_equal(S[k:2 * k], chunk + np.arange(k))
+    y = torch.full((N,), -1, dtype=torch.int16, device="cuda")
+    sel = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    dl.gemv_tiled_refine(dev_fp16(x), y, k, chunk, sel)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), S)
+    rq, rs, rz = O.refinement_w4(L.W, ref.w_hat(), ref.idx)
+    c_hat = O.dequant_w4(rq, rs, rz)
+    y0, a0 = O.matvec_ref(ref.w_hat(), x, ref.idx, ref.wout)
+    terms = x.astype(np.float64)[S][:, None] * c_hat.astype(np.float64)[S]
+    ok, worst = O.check_tolerance(host_fp16(y).astype(np.float64), y0[0] + terms.sum(0),
+                                  a0[0] + np.abs(terms).sum(0))
+    say(f"  worst |err|/bound = {worst:.4f}")
+    assert ok
 
 
 @pytest.mark.parametrize("gpw", ["1", "2", "4"])
