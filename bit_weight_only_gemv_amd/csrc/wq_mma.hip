@@ -886,12 +886,15 @@ struct MmbArgs {
 // 4 rows (rows M..Mp-1 stay unread).
 __host__ __device__ constexpr uint32_t mmb_wave_area(int qg) { return 16u * qg + 512u * qg; }
 struct MmbLds {
-  uint32_t lut, wave, runs, idx, part, total;
+  uint32_t lut, wave, runs, idx, part, xt, total;
 };
+// Transpose area of the activation rows (XT kernels): per wave Mp rows of one
+// slice, each padded by 16 bytes against bank conflicts.
+__host__ __device__ constexpr uint32_t mmb_xt_stride(int qg) { return 256u * qg + 16u; }
 // With outliers also: the run table (slice ks's run of the sorted indices
 // starts at runs[ks], nks + 1 words) and a copy of the indices (256 iv words).
 __host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl, int qg, int nks,
-                                                 int iv) {
+                                                 int iv, bool xt = false) {
   MmbLds L{};
   uint32_t off = 0;
   L.lut = off;
@@ -904,6 +907,8 @@ __host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl
   off += (uint32_t)iv * 1024u;
   L.part = off;
   off += (uint32_t)rbl * (uint32_t)nw * (uint32_t)((M + 3) & ~3) * 64u;
+  L.xt = off;
+  if (xt) off += (uint32_t)nw * (uint32_t)((M + 3) & ~3) * mmb_xt_stride(qg);
   L.total = off;
   return L;
 }
@@ -918,7 +923,7 @@ struct ItemB {
 __device__ __forceinline__ uint32_t splat_lo(uint32_t v) { return __builtin_amdgcn_perm(v, v, 0x01000100u); }
 __device__ __forceinline__ uint32_t splat_hi(uint32_t v) { return __builtin_amdgcn_perm(v, v, 0x03020302u); }
 
-template <int FMT, int IV, int DEPTH, int QG>
+template <int FMT, int IV, int DEPTH, int QG, bool XT>
 __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   typedef MmbFmt<FMT, QG> F;
   constexpr int kSliceChB = F::kSliceCh;
@@ -928,7 +933,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   constexpr bool OUT = IV > 0;
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_out = OUT ? a.n_out : 0;
-  const MmbLds L = mmb_lds_layout(FMT, a.M, a.nw, a.rbl, QG, a.nks, IV);
+  const MmbLds L = mmb_lds_layout(FMT, a.M, a.nw, a.rbl, QG, a.nks, IV, XT);
   uint32_t* s_runs = reinterpret_cast<uint32_t*>(smem + L.runs);
   const int32_t* s_idx = reinterpret_cast<const int32_t*>(smem + L.idx);
   const int tid = threadIdx.x;
@@ -972,12 +977,27 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   // lane (m, q) of slice ks: channels 128 QG ks + 32 QG q + 8 t (t < 4 QG),
   // i.e. the QG groups 4 QG ks + QG q + u, 32 channels each; past K they read
   // 0 (fixed up when the fragments are built)
+  // XT: load t covers whole rows instead (4 / QG rows of the slice, lane l
+  // at row t (4 / QG) + l / (16 QG), channels 8 (l % (16 QG)) .. + 7), so each
+  // load is contiguous; the rows reach the lane layout above through LDS when
+  // the slice is entered.
+  constexpr int kXLanesPerRow = 16 * QG;
+  constexpr int kXRowsPerLoad = kWave / kXLanesPerRow;
   auto x_load = [&](int ks, u4v (&xv)[XS]) {
-    const uint32_t rowoff = (uint32_t)n16 * (uint32_t)a.K;
+    if constexpr (XT) {
+      const uint32_t c = (uint32_t)(ks * kSliceChB + 8 * (lane % kXLanesPerRow));
 #pragma unroll
-    for (int t = 0; t < XS; ++t) {
-      const uint32_t c = (uint32_t)(ks * kSliceChB + 32 * QG * q + 8 * t);
-      xv[t] = ld128(xrs, (rowoff + c) * 2u);
+      for (int t = 0; t < XS; ++t) {
+        const uint32_t row = (uint32_t)(t * kXRowsPerLoad + lane / kXLanesPerRow);
+        xv[t] = ld128(xrs, (row * (uint32_t)a.K + c) * 2u);
+      }
+    } else {
+      const uint32_t rowoff = (uint32_t)n16 * (uint32_t)a.K;
+#pragma unroll
+      for (int t = 0; t < XS; ++t) {
+        const uint32_t c = (uint32_t)(ks * kSliceChB + 32 * QG * q + 8 * t);
+        xv[t] = ld128(xrs, (rowoff + c) * 2u);
+      }
     }
   };
   u4v xpre[XS];
@@ -1152,6 +1172,27 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   auto enter_slice = [&](int s) {
     const int ks = w + a.nw * s;
     const int p = s & 1;
+    if constexpr (XT) {
+      // the slice's rows, loaded whole, into this wave's LDS area and back in
+      // the lane layout of the fragments (lane (m, q): channels 32 QG q + 8 t
+      // of row m); rows past M are zero
+      const uint32_t mpx = (uint32_t)((a.M + 3) & ~3);
+      const uint32_t xbase = L.xt + (uint32_t)w * mpx * mmb_xt_stride(QG);
+#pragma unroll
+      for (int t = 0; t < XS; ++t) {
+        const uint32_t row = (uint32_t)(t * kXRowsPerLoad + lane / kXLanesPerRow);
+        if (row < mpx)
+          *reinterpret_cast<u4v*>(smem + xbase + row * mmb_xt_stride(QG) +
+                                  16u * (uint32_t)(lane % kXLanesPerRow)) = xpre[t];
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int t = 0; t < XS; ++t)
+        xpre[t] = (uint32_t)n16 < mpx
+                      ? *reinterpret_cast<const u4v*>(smem + xbase + (uint32_t)n16 * mmb_xt_stride(QG) +
+                                                       (uint32_t)(32 * QG * q + 8 * t) * 2u)
+                      : (u4v){0u, 0u, 0u, 0u};
+    }
     // fragments of this slice from the prefetched rows (channels past K: 0)
     uint32_t fr[XS][4];
     if constexpr (FMT == 2) {
@@ -1315,9 +1356,15 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     if constexpr (OUT) {
       const uint32_t row = (uint32_t)(((int)blockIdx.x + ri * (int)gridDim.x) * 16 + n16);
       const uint32_t sh = ((row * (uint32_t)n_out + (uint32_t)cur_jlo) & 1u) * 16u;
+      // the slab values past the run belong to other positions or rows (or
+      // lie past the array): cleared, so that an infinite one never meets a
+      // zero activation
+      const int cnt = cur_nin - 8 * q;
       uint32_t bw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bw[i] = __builtin_amdgcn_alignbit(it.od[i + 1], it.od[i], sh);
+      for (int i = 0; i < 4; ++i)
+        bw[i] = __builtin_amdgcn_alignbit(it.od[i + 1], it.od[i], sh) &
+                (2 * i + 1 < cnt ? 0xFFFFFFFFu : 2 * i < cnt ? 0x0000FFFFu : 0u);
       c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
           __builtin_bit_cast(h8, (u4v){xo[0], xo[1], xo[2], xo[3]}),
           __builtin_bit_cast(h8, (u4v){bw[0], bw[1], bw[2], bw[3]}), c, 0, 0, 0);
@@ -1365,9 +1412,12 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
           uint32_t od[5];
 #pragma unroll
           for (int i = 0; i < 5; ++i) od[i] = ld32(ors, b0 + 4u * i);
+          const int cnt = nin - c0 - 8 * q;   // as in the run's first 32 positions
           uint32_t bw[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) bw[i] = __builtin_amdgcn_alignbit(od[i + 1], od[i], (e0 & 1u) * 16u);
+          for (int i = 0; i < 4; ++i)
+            bw[i] = __builtin_amdgcn_alignbit(od[i + 1], od[i], (e0 & 1u) * 16u) &
+                    (2 * i + 1 < cnt ? 0xFFFFFFFFu : 2 * i < cnt ? 0x0000FFFFu : 0u);
           f4 c = {0.f, 0.f, 0.f, 0.f};
           c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
               __builtin_bit_cast(h8, xv), __builtin_bit_cast(h8, (u4v){bw[0], bw[1], bw[2], bw[3]}), c,
@@ -1453,7 +1503,7 @@ static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_ou
 
 
 struct MmbPlan {
-  bool ok;
+  bool ok, xt;
   int nw, nks, nrb, grid, rbl, iv, depth, qg;
   size_t lds;
 };
@@ -1466,10 +1516,12 @@ static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M)
       N * n_out * 2 > 0xFFFFFFF0ll || M * K * 2 > 0xFFFFFFF0ll)
     return p;
   // 512-channel slices (QG = 4) halve the items and slice changes of layers up
-  // to K = 8192 without outliers (measured faster there); longer rows, and the
-  // outlier variants (whose registers would spill at QG = 4), keep 256.
-  // WQ_MMB_QG=2|4 overrides the choice for the variants without outliers.
-  p.qg = n_out == 0 && K <= 8192 ? 4 : 2;
+  // to K = 8192 without outliers (measured faster there up to M = 8); longer
+  // rows, the outlier variants (whose registers would spill at QG = 4) and
+  // more rows keep 256, whose activation rows load whole (measured at M = 16
+  // on 14336 x 4096: 14.6 us against 15.8).  WQ_MMB_QG=2|4 overrides the
+  // choice for the variants without outliers.
+  p.qg = n_out == 0 && K <= 8192 && M <= 8 ? 4 : 2;
   if (const char* e = getenv("WQ_MMB_QG"))
     if (n_out == 0) p.qg = atoi(e) == 4 ? 4 : 2;
   const int slice_ch = 128 * p.qg;
@@ -1494,6 +1546,12 @@ static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M)
   p.iv = n_out == 0 ? 0 : n_out <= 256 ? 1 : n_out <= 512 ? 2 : 4;
   p.lds = mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv).total;
   if (p.lds > kMaxLdsBytes) return p;
+  // 256-channel slices load the activation rows whole and transpose them in
+  // LDS where it fits (WQ_MMB_XT=0|1 overrides, for tests and measurements)
+  const size_t lds_xt = mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv, true).total;
+  p.xt = p.qg == 2 && lds_xt <= kMaxLdsBytes;
+  if (const char* e = getenv("WQ_MMB_XT")) p.xt = p.qg == 2 && lds_xt <= kMaxLdsBytes && atoi(e) != 0;
+  if (p.xt) p.lds = lds_xt;
   p.depth = 2;
   p.ok = true;
   return p;
@@ -1667,20 +1725,20 @@ int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
   a.nrb = p.nrb;
   a.rbl = p.rbl;
   const dim3 grid(p.grid), block(p.nw * kWave);
-#define WQ_MMB_LAUNCH_Q(F_, IV_, Q_)                                                         \
-  if (fmt == F_ && p.iv == IV_ && p.qg == Q_) {                                              \
-    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, Q_>), p.lds))      \
+#define WQ_MMB_LAUNCH_X(F_, IV_, Q_, X_)                                                     \
+  if (fmt == F_ && p.iv == IV_ && p.qg == Q_ && p.xt == X_) {                                \
+    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, Q_, X_>), p.lds))  \
       return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds); \
-    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, Q_>), grid, block, p.lds, stream, a);         \
+    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, Q_, X_>), grid, block, p.lds, stream, a);     \
     *launched = true;                                                                        \
     return check_launch(who);                                                                \
   }
-#define WQ_MMB_LAUNCH(F_, IV_) WQ_MMB_LAUNCH_Q(F_, IV_, 2)
-  WQ_MMB_LAUNCH_Q(4, 0, 4) WQ_MMB_LAUNCH_Q(2, 0, 4) WQ_MMB_LAUNCH_Q(5, 0, 4)
+#define WQ_MMB_LAUNCH(F_, IV_) WQ_MMB_LAUNCH_X(F_, IV_, 2, false) WQ_MMB_LAUNCH_X(F_, IV_, 2, true)
+  WQ_MMB_LAUNCH_X(4, 0, 4, false) WQ_MMB_LAUNCH_X(2, 0, 4, false) WQ_MMB_LAUNCH_X(5, 0, 4, false)
   WQ_MMB_LAUNCH(4, 0) WQ_MMB_LAUNCH(4, 1) WQ_MMB_LAUNCH(4, 2) WQ_MMB_LAUNCH(4, 4)
   WQ_MMB_LAUNCH(2, 0) WQ_MMB_LAUNCH(2, 1) WQ_MMB_LAUNCH(2, 2) WQ_MMB_LAUNCH(2, 4)
   WQ_MMB_LAUNCH(5, 0) WQ_MMB_LAUNCH(5, 1) WQ_MMB_LAUNCH(5, 2) WQ_MMB_LAUNCH(5, 4)
-#undef WQ_MMB_LAUNCH_Q
+#undef WQ_MMB_LAUNCH_X
 #undef WQ_MMB_LAUNCH
   return WQ_OK;
 }
