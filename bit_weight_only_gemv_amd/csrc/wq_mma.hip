@@ -1000,8 +1000,16 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
       }
     }
   };
+  // XT with outliers: two slices of rows in flight (even slices in xpre, odd
+  // ones in xpre2), as the weights are two items ahead (measured: the W2
+  // 8192 x 28672 layer at M = 8 gains 8%; without outliers the registers cost
+  // more than the earlier loads gain)
+  constexpr bool X2 = XT && OUT;
   u4v xpre[XS];
+  u4v xpre2[X2 ? XS : 1];
   x_load(w, xpre);
+  if constexpr (X2)
+    if (1 < ns_w) x_load(w + a.nw, xpre2);
   asm volatile("" ::: "memory");   // these loads stay ahead of the weight stream
 
   // slice ks's run of the sorted indices: positions j_lo .. j_lo + nin - 1
@@ -1148,20 +1156,23 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         }
       }
       // outlier activations of the first 32 columns of the run: X[m][lo + c]
-      const int4 l0 = *reinterpret_cast<const int4*>(list + 8 * q);
-      const int4 l1 = *reinterpret_cast<const int4*>(list + 8 * q + 4);
-      const int cl[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-      uint32_t hv[8];
+      // (XT: read from the slice's rows in LDS when the slice is entered)
+      if constexpr (!XT) {
+        const int4 l0 = *reinterpret_cast<const int4*>(list + 8 * q);
+        const int4 l1 = *reinterpret_cast<const int4*>(list + 8 * q + 4);
+        const int cl[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        uint32_t hv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {   // every lane loads (a valid column when idle)
-        const bool ok = 8 * q + e < nin && cl[e] >= 0;
-        const uint32_t col =
-            (uint32_t)(lo + __builtin_amdgcn_ubfe(ok ? cl[e] : 0, 0, QG == 4 ? 9 : 8));
-        const uint32_t v = ld16(xrs, ((uint32_t)n16 * (uint32_t)a.K + col) * 2u);
-        hv[e] = ok ? v : 0u;
+        for (int e = 0; e < 8; ++e) {   // every lane loads (a valid column when idle)
+          const bool ok = 8 * q + e < nin && cl[e] >= 0;
+          const uint32_t col =
+              (uint32_t)(lo + __builtin_amdgcn_ubfe(ok ? cl[e] : 0, 0, QG == 4 ? 9 : 8));
+          const uint32_t v = ld16(xrs, ((uint32_t)n16 * (uint32_t)a.K + col) * 2u);
+          hv[e] = ok ? v : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xopre[i] = hv[2 * i] | (hv[2 * i + 1] << 16);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xopre[i] = hv[2 * i] | (hv[2 * i + 1] << 16);
     }
   };
   prep_slice(w, 0);
@@ -1169,7 +1180,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   h8 afr[XS];
   uint32_t xo[4] = {0u, 0u, 0u, 0u};
   int cur_jlo = 0, cur_nin = 0;
-  auto enter_slice = [&](int s) {
+  auto enter_slice_rows = [&](int s, auto& xbuf) {
     const int ks = w + a.nw * s;
     const int p = s & 1;
     if constexpr (XT) {
@@ -1183,15 +1194,36 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         const uint32_t row = (uint32_t)(t * kXRowsPerLoad + lane / kXLanesPerRow);
         if (row < mpx)
           *reinterpret_cast<u4v*>(smem + xbase + row * mmb_xt_stride(QG) +
-                                  16u * (uint32_t)(lane % kXLanesPerRow)) = xpre[t];
+                                  16u * (uint32_t)(lane % kXLanesPerRow)) = xbuf[t];
       }
       wave_lds_sync();
 #pragma unroll
       for (int t = 0; t < XS; ++t)
-        xpre[t] = (uint32_t)n16 < mpx
+        xbuf[t] = (uint32_t)n16 < mpx
                       ? *reinterpret_cast<const u4v*>(smem + xbase + (uint32_t)n16 * mmb_xt_stride(QG) +
                                                        (uint32_t)(32 * QG * q + 8 * t) * 2u)
                       : (u4v){0u, 0u, 0u, 0u};
+      if constexpr (OUT) {
+        // the run's first 32 outlier activations from the same rows (the
+        // slice's column list was written when the previous slice was entered)
+        const int32_t* list =
+            reinterpret_cast<const int32_t*>(smem + warea0 + (uint32_t)p * kMmbWaveArea + 16u * QG);
+        int j_lo, nin;
+        jrange(ks, j_lo, nin);
+        const int4 l0 = *reinterpret_cast<const int4*>(list + 8 * q);
+        const int4 l1 = *reinterpret_cast<const int4*>(list + 8 * q + 4);
+        const int cl[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        uint32_t hv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool ok = 8 * q + e < nin && cl[e] >= 0 && cl[e] < kSliceChB && (uint32_t)n16 < mpx;
+          hv[e] = ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(
+                           smem + xbase + (uint32_t)n16 * mmb_xt_stride(QG) + (uint32_t)cl[e] * 2u)
+                     : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xopre[i] = hv[2 * i] | (hv[2 * i + 1] << 16);
+      }
     }
     // fragments of this slice from the prefetched rows (channels past K: 0)
     uint32_t fr[XS][4];
@@ -1199,10 +1231,10 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
 #pragma unroll
       for (int t = 0; t < XS; ++t) {
         const bool ok = ks * kSliceChB + 32 * QG * q + 8 * t < a.K;
-        fr[t][0] = ok ? xpre[t].x : 0u;
-        fr[t][1] = ok ? xpre[t].y : 0u;
-        fr[t][2] = ok ? xpre[t].z : 0u;
-        fr[t][3] = ok ? xpre[t].w : 0u;
+        fr[t][0] = ok ? xbuf[t].x : 0u;
+        fr[t][1] = ok ? xbuf[t].y : 0u;
+        fr[t][2] = ok ? xbuf[t].z : 0u;
+        fr[t][3] = ok ? xbuf[t].w : 0u;
       }
       if constexpr (OUT) {
         // zero the outlier columns: bits 2i, 2i + 1 of step t's byte
@@ -1229,7 +1261,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         uint32_t gv[16];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const u4v t = xpre[4 * u + v];
+          const u4v t = xbuf[4 * u + v];
           gv[4 * v + 0] = ok ? t.x : 0u;
           gv[4 * v + 1] = ok ? t.y : 0u;
           gv[4 * v + 2] = ok ? t.z : 0u;
@@ -1252,10 +1284,24 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) xo[i] = xopre[i];
     jrange(ks, cur_jlo, cur_nin);
-    // the next slice's rows and outlier activations, one slice ahead
-    if (s + 1 < ns_w) {
-      x_load(ks + a.nw, xpre);
-      prep_slice(ks + a.nw, p ^ 1);
+    // the next rows into the buffer just read (X2: two slices ahead, the
+    // buffers alternate; else the next slice) and the next slice's outlier
+    // activations
+    if constexpr (X2) {
+      if (s + 2 < ns_w) x_load(ks + 2 * a.nw, xbuf);
+    } else {
+      if (s + 1 < ns_w) x_load(ks + a.nw, xbuf);
+    }
+    if (s + 1 < ns_w) prep_slice(ks + a.nw, p ^ 1);
+  };
+  auto enter_slice = [&](int s) {
+    if constexpr (X2) {
+      if (s & 1)
+        enter_slice_rows(s, xpre2);
+      else
+        enter_slice_rows(s, xpre);
+    } else {
+      enter_slice_rows(s, xpre);
     }
   };
 
