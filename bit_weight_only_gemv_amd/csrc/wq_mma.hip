@@ -1595,8 +1595,8 @@ static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M)
   // 256-channel slices load the activation rows whole and transpose them in
   // LDS where it fits (WQ_MMB_XT=0|1 overrides, for tests and measurements)
   const size_t lds_xt = mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv, true).total;
-  p.xt = p.qg == 2 && lds_xt <= kMaxLdsBytes;
-  if (const char* e = getenv("WQ_MMB_XT")) p.xt = p.qg == 2 && lds_xt <= kMaxLdsBytes && atoi(e) != 0;
+  p.xt = lds_xt <= kMaxLdsBytes;
+  if (const char* e = getenv("WQ_MMB_XT")) p.xt = lds_xt <= kMaxLdsBytes && atoi(e) != 0;
   if (p.xt) p.lds = lds_xt;
   p.depth = 2;
   p.ok = true;
@@ -1781,6 +1781,7 @@ int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
   }
 #define WQ_MMB_LAUNCH(F_, IV_) WQ_MMB_LAUNCH_X(F_, IV_, 2, false) WQ_MMB_LAUNCH_X(F_, IV_, 2, true)
   WQ_MMB_LAUNCH_X(4, 0, 4, false) WQ_MMB_LAUNCH_X(2, 0, 4, false) WQ_MMB_LAUNCH_X(5, 0, 4, false)
+  WQ_MMB_LAUNCH_X(4, 0, 4, true) WQ_MMB_LAUNCH_X(2, 0, 4, true) WQ_MMB_LAUNCH_X(5, 0, 4, true)
   WQ_MMB_LAUNCH(4, 0) WQ_MMB_LAUNCH(4, 1) WQ_MMB_LAUNCH(4, 2) WQ_MMB_LAUNCH(4, 4)
   WQ_MMB_LAUNCH(2, 0) WQ_MMB_LAUNCH(2, 1) WQ_MMB_LAUNCH(2, 2) WQ_MMB_LAUNCH(2, 4)
   WQ_MMB_LAUNCH(5, 0) WQ_MMB_LAUNCH(5, 1) WQ_MMB_LAUNCH(5, 2) WQ_MMB_LAUNCH(5, 4)

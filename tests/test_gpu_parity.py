@@ -324,19 +324,21 @@ def test_gemm_slice_widths(fmt, M, N, K, qg, monkeypatch):
     check_product(ref, Y, L.x, f"gemm w{fmt} M={M} {N}x{K} slices {128 * int(qg)}")
 
 
+@pytest.mark.parametrize("qg", ["2", "4"])
 @pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("M", [2, 5, 8, 16])
 @pytest.mark.parametrize("N,K,outl", [(129, 4096, True), (300, 8320, False), (64, 2176, True),
                                       (1000, 10240, False), (96, 384, False)])
-def test_gemm_row_transpose(fmt, M, N, K, outl, monkeypatch):
-    """The batched kernel with 256-channel slices, its activation rows loaded
-    whole and transposed in LDS (WQ_MMB_XT=1) or loaded in the lane layout
+def test_gemm_row_transpose(fmt, M, N, K, outl, qg, monkeypatch):
+    """The batched kernel with its activation rows loaded whole and transposed
+    in LDS (WQ_MMB_XT=1, where the LDS fits) or loaded in the lane layout
     directly (WQ_MMB_XT=0): the same fragments, so bit-identical Y, within the
-    bound; short last slices and rows past M included."""
+    bound; 256- and 512-channel slices (outlier layers always take 256), short
+    last slices and rows past M included."""
     monkeypatch.setenv("WQ_GEMM_MMA", "2")
     monkeypatch.setenv("WQ_GEMM_ROWS", "0")
-    monkeypatch.setenv("WQ_MMB_QG", "2")
-    say(f"gemm row transpose fmt={fmt} M={M} N={N} K={K} outliers={outl}")
+    monkeypatch.setenv("WQ_MMB_QG", qg)
+    say(f"gemm row transpose fmt={fmt} M={M} N={N} K={K} outliers={outl} slices={128 * int(qg)}")
     L = synthetic.small_layer(fmt, N, K, M=M, with_outliers=outl, seed=M + N + 1)
     ref, dl = build(fmt, L.W, L.profile, L.ratio) if outl else build(fmt, L.W)
     X = dev_fp16(L.x)
