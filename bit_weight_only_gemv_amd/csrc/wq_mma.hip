@@ -518,17 +518,27 @@ __global__ void __launch_bounds__(REF ? kRefMaxThreads : 512) mma1d_kernel(MmaAr
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + L.hist) + hw * kSelWords;
     int32_t* s_sel = reinterpret_cast<int32_t*>(smem + L.sel);
     uint16_t* s_selx = reinterpret_cast<uint16_t*>(smem + L.selx);
-    // chunks hw, hw + nh, ...: lane l holds channels 16 l .. 16 l + 15 (a
-    // helper has no other loads in flight)
-    for (int cw = 0; cw < a.rc; ++cw) {
+    // chunks hw, hw + nh, ...: lane l holds channels 16 l .. 16 l + 15; the
+    // next chunk's activations are in flight while this one is selected
+    auto chunk_x = [&](int cw, u4v& t0, u4v& t1) {
       const int cc = hw + a.nh * cw;
-      if (cc < a.rnch) {
+      const int c0 = cc * a.rchunk;
+      const bool on = cw < a.rc && cc < a.rnch && 16 * lane < min(a.rchunk, a.K - c0);
+      const uint32_t off = on ? (uint32_t)(c0 + 16 * lane) * 2u : kOob;
+      t0 = ld128(xrs, off);
+      t1 = ld128(xrs, off + 16u);
+    };
+    u4v xc0, xc1;
+    chunk_x(0, xc0, xc1);
+#pragma unroll
+    for (int cw = 0; cw < kRefUnits; ++cw) {
+      const int cc = hw + a.nh * cw;
+      if (cw < a.rc && cc < a.rnch) {
         const int c0 = cc * a.rchunk;
         const int csize = min(a.rchunk, a.K - c0);
         const int kk = min(a.rk, csize);
-        const uint32_t off = 16 * lane < csize ? (uint32_t)(c0 + 16 * lane) * 2u : kOob;
-        const u4v t0 = ld128(xrs, off), t1 = ld128(xrs, off + 16u);
-        const uint32_t xsel[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+        const uint32_t xsel[8] = {xc0.x, xc0.y, xc0.z, xc0.w, xc1.x, xc1.y, xc1.z, xc1.w};
+        if (cw + 1 < kRefUnits) chunk_x(cw + 1, xc0, xc1);
         wave_topk_regs<true>(xsel, c0, csize, kk, hist, s_sel + cc * a.rk, s_selx + cc * a.rk,
                              lane);
         if (a.sel_out != nullptr && blockIdx.x == 0) {

@@ -7,7 +7,10 @@
 // bits of the 15-bit magnitude, then the low 8 bits inside the chosen bin);
 // every channel above T is kept, and of those equal to T the lowest-indexed
 // ones, counted by a wave prefix sum, fill the rest.  The picks are written in
-// index order.  Only wave-level LDS ordering is used, no block barrier.
+// index order.  Only wave-level LDS ordering is used, no block barrier; the
+// bin each pass finds is passed to the other lanes by ballot and readlane, not
+// through LDS, and the histograms are cleared before the chunk's values are
+// waited for.
 #pragma once
 
 #include "wq_common.cuh"
@@ -17,7 +20,7 @@ namespace wqd {
 constexpr uint32_t kSelOob = 0xFFFFF000u;     // past every buffer: loads return 0
 constexpr int kSelBins1 = 128;                // magnitude bits 14..8
 constexpr int kSelBins2 = 256;                // magnitude bits 7..0
-constexpr int kSelWords = kSelBins1 + kSelBins2 + 4;   // per wave: both histograms + state
+constexpr int kSelWords = kSelBins1 + kSelBins2;       // per wave: both histograms
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
@@ -58,48 +61,51 @@ __device__ __forceinline__ void wave_topk_regs(const uint32_t (&wv)[8], int c0, 
                                                uint32_t* hist, int32_t* out, uint16_t* outx,
                                                int lane) {
   const bool valid = 16 * lane < csize;
+  const bool all = kk >= csize;
+  const bool part = !all && kk > 0;
+  uint32_t* h1 = hist;
+  uint32_t* h2 = hist + kSelBins1;
+  if (part) {
+    h1[lane] = 0u;
+    h1[lane + kWave] = 0u;
+#pragma unroll
+    for (int i = 0; i < kSelBins2 / kWave; ++i) h2[lane + kWave * i] = 0u;
+  }
+  // the clearing stays ahead of the first use of wv (and of its wait)
+  __builtin_amdgcn_sched_barrier(0);
   uint32_t m[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     m[2 * i] = wv[i] & 0x7FFFu;
     m[2 * i + 1] = (wv[i] >> 16) & 0x7FFFu;
   }
-  const bool all = kk >= csize;
   uint32_t T = 0u, keq = 0u;   // keep |x| > T, and the first keq channels with |x| == T
-  if (!all && kk > 0) {
-    uint32_t* h1 = hist;
-    uint32_t* h2 = hist + kSelBins1;
-    uint32_t* st = hist + kSelBins1 + kSelBins2;
-    h1[lane] = 0u;
-    h1[lane + kWave] = 0u;
-#pragma unroll
-    for (int i = 0; i < kSelBins2 / kWave; ++i) h2[lane + kWave * i] = 0u;
+  if (part) {
     wave_lds_sync();
     if (valid) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) atomicAdd(&h1[m[e] >> 8], 1u);
     }
     wave_lds_sync();
+    uint32_t b1, rem;
     {
       // lane l holds bins 2l (lower) and 2l + 1 (higher); exactly one bin holds
-      // the kk-th largest (1 <= kk < number of valid channels)
-      const uint32_t rem = (uint32_t)kk;
+      // the kk-th largest (1 <= kk < number of valid channels), and the one
+      // lane that holds it passes the bin and the rank inside it on
+      const uint32_t rk = (uint32_t)kk;
       const uint32_t lo = h1[2 * lane], hi = h1[2 * lane + 1];
       uint32_t tot;
       const uint32_t below = wave_excl_sum(lo + hi, tot);
       const uint32_t suf = tot - below;                     // bins >= 2l
       const uint32_t above = suf - lo - hi;                 // bins >= 2l + 2
-      if (above < rem && rem <= above + hi) {
-        st[0] = 2u * lane + 1u;
-        st[1] = rem - above;
-      } else if (above + hi < rem && rem <= suf) {
-        st[0] = 2u * lane;
-        st[1] = rem - above - hi;
-      }
+      const bool in_hi = above < rk && rk <= above + hi;
+      const bool in_lo = above + hi < rk && rk <= suf;
+      const uint32_t bin = in_hi ? 2u * lane + 1u : 2u * lane;
+      const uint32_t r1 = in_hi ? rk - above : rk - above - hi;
+      const int src = (int)__builtin_ctzll(__ballot(in_hi || in_lo) | (1ull << 63));
+      b1 = (uint32_t)__builtin_amdgcn_readlane((int)bin, src);
+      rem = (uint32_t)__builtin_amdgcn_readlane((int)r1, src);
     }
-    wave_lds_sync();
-    const uint32_t b1 = st[0];
-    const uint32_t rem = st[1];
     if (valid) {
 #pragma unroll
       for (int e = 0; e < 16; ++e)
@@ -116,18 +122,21 @@ __device__ __forceinline__ void wave_topk_regs(const uint32_t (&wv)[8], int c0, 
       uint32_t tot;
       const uint32_t below = wave_excl_sum(sum, tot);
       uint32_t cum = tot - below - sum;                     // bins >= 4l + 4
+      uint32_t tv = 0u, qv = 0u;
+      bool found = false;
 #pragma unroll
       for (int i = 3; i >= 0; --i) {
         if (cum < rem && rem <= cum + hb[i]) {
-          st[2] = (b1 << 8) | (uint32_t)(4 * lane + i);
-          st[3] = rem - cum;
+          tv = (b1 << 8) | (uint32_t)(4 * lane + i);
+          qv = rem - cum;
+          found = true;
         }
         cum += hb[i];
       }
+      const int src = (int)__builtin_ctzll(__ballot(found) | (1ull << 63));
+      T = (uint32_t)__builtin_amdgcn_readlane((int)tv, src);
+      keq = (uint32_t)__builtin_amdgcn_readlane((int)qv, src);
     }
-    wave_lds_sync();
-    T = st[2];
-    keq = st[3];
   }
   uint32_t gt = 0u, eq = 0u;
 #pragma unroll
