@@ -432,6 +432,21 @@ __global__ void __launch_bounds__(REF ? kRefMaxThreads : 512) mma1d_kernel(MmaAr
   //      is the rest of the ring issued (measured on MI355X: issuing the
   //      whole ring at entry delays the first row block behind the others
   //      and costs more than the overlap gains)
+  // A helper's chunks of x (refinement only): chunk hw + nh cw, lane l holds
+  // channels 16 l .. 16 l + 15.  The first is requested here, beside the
+  // first row block, so that it does not queue behind the ring.
+  u4v xc0, xc1;
+  auto chunk_x = [&](int cw, u4v& t0, u4v& t1) {
+    const int cc = hw + a.nh * cw;
+    const int c0 = cc * a.rchunk;
+    const bool on = cw < a.rc && cc < a.rnch && 16 * lane < min(a.rchunk, a.K - c0);
+    const uint32_t off = on ? (uint32_t)(c0 + 16 * lane) * 2u : kOob;
+    t0 = ld128(xrs, off);
+    t1 = ld128(xrs, off + 16u);
+  };
+  if constexpr (REF) {
+    if (helper && hw < min(a.nh, a.rnch)) chunk_x(0, xc0, xc1);
+  }
   Item<FMT, OUT> buf[DEPTH];
   load_item(buf[0], 0 < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
   advance(ls, lr);
@@ -518,18 +533,8 @@ __global__ void __launch_bounds__(REF ? kRefMaxThreads : 512) mma1d_kernel(MmaAr
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + L.hist) + hw * kSelWords;
     int32_t* s_sel = reinterpret_cast<int32_t*>(smem + L.sel);
     uint16_t* s_selx = reinterpret_cast<uint16_t*>(smem + L.selx);
-    // chunks hw, hw + nh, ...: lane l holds channels 16 l .. 16 l + 15; the
-    // next chunk's activations are in flight while this one is selected
-    auto chunk_x = [&](int cw, u4v& t0, u4v& t1) {
-      const int cc = hw + a.nh * cw;
-      const int c0 = cc * a.rchunk;
-      const bool on = cw < a.rc && cc < a.rnch && 16 * lane < min(a.rchunk, a.K - c0);
-      const uint32_t off = on ? (uint32_t)(c0 + 16 * lane) * 2u : kOob;
-      t0 = ld128(xrs, off);
-      t1 = ld128(xrs, off + 16u);
-    };
-    u4v xc0, xc1;
-    chunk_x(0, xc0, xc1);
+    // chunks hw, hw + nh, ...: the first was requested at entry, and the next
+    // chunk's activations are in flight while this one is selected
 #pragma unroll
     for (int cw = 0; cw < kRefUnits; ++cw) {
       const int cc = hw + a.nh * cw;
