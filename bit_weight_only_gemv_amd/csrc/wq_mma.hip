@@ -113,6 +113,8 @@ struct MmaArgs {
 // most, and the workgroup size with the helper waves.
 constexpr int kRefUnits = 4;
 constexpr int kRefMaxThreads = 768;
+// The W4 / W4P kernels without outliers fit 128 VGPRs, and so 16 waves.
+constexpr int kRefWideThreads = 1024;
 
 // Per-wave LDS region: for each of its slices and each activation row, x
 // (1 KB, masked at the outlier columns), the 16 group sums of x (64 B) and the
@@ -199,8 +201,9 @@ __device__ __forceinline__ float slab_dot(const uint32_t (&od)[5], const uint32_
   return v;
 }
 
-template <int FMT, bool OUT, bool TILED, int NSW, int MS, bool REF>
-__global__ void __launch_bounds__(REF ? kRefMaxThreads : 512) mma1d_kernel(MmaArgs a) {
+template <int FMT, bool OUT, bool TILED, int NSW, int MS, bool REF, bool WIDE = false>
+__global__ void __launch_bounds__(WIDE ? kRefWideThreads : REF ? kRefMaxThreads : 512)
+    mma1d_kernel(MmaArgs a) {
   typedef MmaFmt<FMT> F;
   constexpr int DEPTH = 2;
   static_assert(MS == 1 || MS == 2 || (MS == 4 && FMT != 2), "1, 2 or (W4) 4 activation rows");
@@ -1720,8 +1723,19 @@ int wqd_gemv_refine_mma(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
   const int rk = (int)std::min(k, chunk);
   const int rnch = (int)((K + chunk - 1) / chunk);
   // helper waves: up to the workgroup size, at most one per chunk
-  const int nh = std::min(rnch, kRefMaxThreads / kWave - p.nw);
+  int nh = std::min(rnch, kRefMaxThreads / kWave - p.nw);
   if (nh < 1) return WQ_OK;
+  // 16 waves where the kernel fits them and the extra helpers take a chunk
+  // off every helper's share
+  bool wide = false;
+  if (fmt != 2 && n_out == 0) {
+    const char* e = getenv("WQ_REFINE_WIDE");
+    const int nhw = std::min(rnch, kRefWideThreads / kWave - p.nw);
+    if (!(e != nullptr && e[0] == '0') && (rnch + nhw - 1) / nhw < (rnch + nh - 1) / nh) {
+      nh = nhw;
+      wide = true;
+    }
+  }
   const int rc = (rnch + nh - 1) / nh;
   const int rp = (rk + 31) / 32;
   const int rh = (p.rbl + 1) / 2;
@@ -1743,6 +1757,20 @@ int wqd_gemv_refine_mma(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
   a.rp = rp;
   a.rh = rh;
   const dim3 grid(p.grid), block((p.nw + nh) * kWave);
+#define WQ_MMA_REF_WIDE(F_, S_)                                                               \
+  if (wide && fmt == F_ && p.nswt == S_) {                                                     \
+    if (!allow_lds(reinterpret_cast<const void*>(&mma1d_kernel<F_, false, true, S_, 1, true, true>), \
+                   p.lds))                                                                     \
+      return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds);   \
+    hipLaunchKernelGGL((mma1d_kernel<F_, false, true, S_, 1, true, true>), grid, block, p.lds,   \
+                       stream, a);                                                             \
+    *launched = true;                                                                          \
+    return check_launch(who);                                                                  \
+  }
+  WQ_MMA_REF_WIDE(4, 1) WQ_MMA_REF_WIDE(4, 2) WQ_MMA_REF_WIDE(4, 4) WQ_MMA_REF_WIDE(4, 8)
+  WQ_MMA_REF_WIDE(5, 1) WQ_MMA_REF_WIDE(5, 2) WQ_MMA_REF_WIDE(5, 4) WQ_MMA_REF_WIDE(5, 8)
+#undef WQ_MMA_REF_WIDE
+  if (wide) return WQ_OK;
 #define WQ_MMA_REF(F_, O_, S_)                                                                \
   if (fmt == F_ && (n_out > 0) == O_ && p.nswt == S_) {                                        \
     if (!allow_lds(reinterpret_cast<const void*>(&mma1d_kernel<F_, O_, true, S_, 1, true>),    \

@@ -603,6 +603,8 @@ TILED_REFINE_CASES = [
     (2, 64, 1024, 64, 64, True, True),          # 16 chunks on 10 helper waves
     (5, 96, 1088, 64, 1, True, True),           # 17 chunks of 64, one pick each
     (2, 32, 512, 64, 7, False, True),           # one 512-channel slice, smallest N
+    (4, 256, 8192, 1024, 32, False, True),      # W4 without outliers: 16 waves, 8 helpers
+    (5, 4096, 14336, 1024, 32, False, True),    # 14 chunks on 9 helpers of a 16-wave workgroup
     (4, 40960, 1024, 1024, 16, True, False),    # 10 row blocks per workgroup: two launches
     (4, 128, 4096, 1024, 1024, False, False),   # every channel picked: two launches
 ]
@@ -630,8 +632,11 @@ def test_gemv_tiled_refine(fmt, N, K, chunk, k, outl, fused, monkeypatch):
     y0, a0 = O.matvec_ref(ref.w_hat(), x, ref.idx, ref.wout)
     terms = x.astype(np.float64)[S][:, None] * c_hat.astype(np.float64)[S]
     outs = {}
-    for mode in ("1", "0"):
-        monkeypatch.setenv("WQ_REFINE_FUSE", mode)
+    # W4 / W4P layers without outliers also run their 12-wave kernel (WQ_REFINE_WIDE=0)
+    modes = ("1", "1w0", "0") if fmt != 2 and not outl else ("1", "0")
+    for mode in modes:
+        monkeypatch.setenv("WQ_REFINE_FUSE", mode[0])
+        monkeypatch.setenv("WQ_REFINE_WIDE", "0" if mode == "1w0" else "1")
         y = torch.full((N,), -1, dtype=torch.int16, device="cuda")
         sel = torch.full((n,), -7, dtype=torch.int32, device="cuda")
         dl.gemv_tiled_refine(xd, y, k, chunk, sel)
@@ -639,7 +644,7 @@ def test_gemv_tiled_refine(fmt, N, K, chunk, k, outl, fused, monkeypatch):
         assert np.array_equal(sel.cpu().numpy(), S)
         ok, worst = O.check_tolerance(host_fp16(y).astype(np.float64), y0[0] + terms.sum(0),
                                       a0[0] + np.abs(terms).sum(0))
-        say(f"  WQ_REFINE_FUSE={mode}: worst |err|/bound = {worst:.4f}")
+        say(f"  mode {mode}: worst |err|/bound = {worst:.4f}")
         assert ok
         outs[mode] = y.cpu().numpy()
     # the two-launch path is exactly the product followed by the fused selection + add
