@@ -57,9 +57,11 @@ def _parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="w2_14336",
                    choices=["w2_14336", "w4_4096", "sweep", "batched", "w2_70b", "embed",
-                            "kurtosis", "refine", "read", "copy"])
+                            "kurtosis", "refine", "read", "copy", "probe_sweep"])
     p.add_argument("--bytes", type=int, default=26157628,
                    help="bytes per launch of the read / copy workloads")
+    p.add_argument("--probe-sizes", default="",
+                   help="probe_sweep workload: comma-separated byte counts")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--m", type=int, default=0,
                    help="batched workload: only this M (default: 2, 4, 8 and 16)")
@@ -106,45 +108,93 @@ def sweep_bytes_per_token(fmt: int, ratio: float) -> int:
 
 
 class Timer:
-    """Times `steps` calls of fn(i): captured once into a HIP graph and replayed
-    (or launched eagerly), bracketed by events on the launching stream."""
+    """Times exactly `steps` calls of fn(i) after `warmup` untimed ones.  The
+    steps are captured into a HIP graph of `per` launches (the library is
+    called through its C ABI during capture), a whole multiple of `period` (the
+    number of rotated buffer copies, so that every replay walks all of them),
+    replayed R times with an event on the launching stream between replays; a
+    second graph holds the steps - R per left over.  One synchronization ends
+    the timed region.  Returns a Timing: the time per step (median over the
+    replays, their 10th and 90th percentiles, and the mean over all steps)."""
+
+    REPLAYS = 20
+    LEAD_CYCLES = 250_000
 
     def __init__(self, torch, eager=False):
         self.torch, self.eager = torch, eager
 
-    def __call__(self, fn, steps, warmup, reps=3):
+    def _capture(self, fn, n):
         torch = self.torch
+        graph = torch.cuda.CUDAGraph()
+        stream = torch.cuda.current_stream()
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                for i in range(n):
+                    fn(i)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        return graph
+
+    def __call__(self, fn, steps, warmup, period=1):
+        torch = self.torch
+        steps = max(1, int(steps))
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
+        period = max(1, int(period))
+        per = -(-max(1, steps // self.REPLAYS) // period) * period
+        per = min(per, steps)
+        reps = steps // per
+        rest = steps - reps * per
         stream = torch.cuda.current_stream()
-        graph = None
+        g_main = g_rest = None
         if not self.eager:
-            graph = torch.cuda.CUDAGraph()
-            s = torch.cuda.Stream()
-            s.wait_stream(stream)
-            with torch.cuda.stream(s):
-                with torch.cuda.graph(graph, stream=s):
-                    for i in range(steps):
-                        fn(i)
-            torch.cuda.synchronize()
-            graph.replay()
-            torch.cuda.synchronize()
-        best = None
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            if graph is not None:
-                graph.replay()
+            g_main = self._capture(fn, per)
+            if rest:
+                g_rest = self._capture(fn, rest)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
+        torch.cuda.synchronize()
+        # a bounded spin on the stream first (about 0.1 ms), so that the
+        # launches below are queued on the GPU before the first event fires:
+        # the timed region then holds the kernels, not the host's latency to
+        # submit the first of them
+        torch.cuda._sleep(self.LEAD_CYCLES)
+        ev[0].record(stream)
+        for r in range(reps):
+            if g_main is not None:
+                g_main.replay()
             else:
-                for i in range(steps):
-                    fn(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / steps
-            best = ms if best is None else min(best, ms)
-        return best
+                for i in range(per):
+                    fn(r * per + i)
+            ev[r + 1].record(stream)
+        if rest:
+            if g_rest is not None:
+                g_rest.replay()
+            else:
+                for i in range(rest):
+                    fn(reps * per + i)
+        ev[reps + 1].record(stream)
+        torch.cuda.synchronize()
+        t = np.array([ev[r].elapsed_time(ev[r + 1]) / per for r in range(reps)])
+        mean = ev[0].elapsed_time(ev[reps + 1]) / steps
+        return Timing(float(np.median(t)), float(np.percentile(t, 10)),
+                      float(np.percentile(t, 90)), float(mean), steps)
+
+
+class Timing(float):
+    """Milliseconds per step (the median over replays) with the spread."""
+
+    def __new__(cls, median, p10, p90, mean, steps):
+        o = super().__new__(cls, median)
+        o.p10, o.p90, o.mean, o.steps = p10, p90, mean, steps
+        return o
+
+    def us(self):
+        return {"median": round(self * 1e3, 3), "p10": round(self.p10 * 1e3, 3),
+                "p90": round(self.p90 * 1e3, 3), "mean": round(self.mean * 1e3, 3)}
 
 
 def clone_layer(DeviceLayer, base):
@@ -185,7 +235,7 @@ def read_probe_rate(torch, timer, nbytes, steps, warmup):
     ncopy = max(1, -(-ROTATE_BYTES // nb))
     bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
     sink = torch.empty(B.wq_read_probe_sink_words(nb), dtype=torch.int32, device="cuda")
-    ms = timer(lambda i: B.wq_read_probe(bufs[i % ncopy], nb, sink), steps, warmup)
+    ms = timer(lambda i: B.wq_read_probe(bufs[i % ncopy], nb, sink), steps, warmup, ncopy)
     del bufs
     return nb / (ms * 1e-3) / 1e9
 
@@ -211,7 +261,7 @@ def gemv_workload(a, torch, L, label, timer):
         layers[i % ncopy].gemv_tiled(x, ys[i % ncopy])
 
     steps = {"rowmajor": step_rowmajor, "tiled": step_tiled}
-    times = {k: timer(fn, a.steps, a.warmup) for k, fn in steps.items()}
+    times = {k: timer(fn, a.steps, a.warmup, ncopy) for k, fn in steps.items()}
     layout = min(times, key=times.get) if a.layout == "best" else a.layout
     other = "rowmajor" if layout == "tiled" else "tiled"
     ms, ms_other = times[layout], times[other]
@@ -349,6 +399,10 @@ def sweep_workload(a, torch, timer):
 
 
 def batched_workload(a, torch, timer):
+    """Small-M products (SPECTRA section 4.2) on the W4 14336 x 4096 and
+    4096 x 14336 layers: the tiled layout's batched kernel (the same buffer as
+    the M = 1 kernel), the row-major arrays' batched kernel, M repeated GEMVs,
+    and the tiled M = 1 GEMV of the same layer in the same run."""
     import synthetic
     from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
     rows = []
@@ -357,7 +411,14 @@ def batched_workload(a, torch, timer):
         shapes = [tuple(int(v) for v in a.shape.lower().split("x"))]
     for (N, K) in shapes:
         Lb = synthetic.config4(16, N, K)
-        base = DeviceLayer(pack_host(w4_fmt(a), Lb.W))
+        base = DeviceLayer(pack_host(w4_fmt(a), Lb.W), tiled=True)
+        n1 = base.nbytes(1)
+        l1 = rotated(DeviceLayer, base, n1)
+        x1 = torch.from_numpy(np.ascontiguousarray(Lb.x[0]).view(np.int16)).cuda()
+        y1 = [torch.empty(N, dtype=torch.int16, device="cuda") for _ in range(len(l1))]
+        ms_m1 = timer(lambda i: l1[i % len(l1)].gemv_tiled(x1, y1[i % len(l1)]), a.steps // 4,
+                      a.warmup // 4, len(l1))
+        del l1
         for M in ((a.m,) if a.m else (2, 4, 8, 16)):
             nbytes = base.nbytes(M)
             layers = rotated(DeviceLayer, base, nbytes)
@@ -365,20 +426,26 @@ def batched_workload(a, torch, timer):
             X = torch.from_numpy(np.ascontiguousarray(Lb.x[:M]).view(np.int16)).cuda()
             Y = [torch.empty((M, N), dtype=torch.int16, device="cuda") for _ in range(nc)]
             xrow = [X[m].contiguous() for m in range(M)]
-            ms_gemm = timer(lambda i: layers[i % nc].gemm(X, Y[i % nc]), a.steps // 4, a.warmup // 4)
+            ms_tiled = timer(lambda i: layers[i % nc].gemm_tiled(X, Y[i % nc]), a.steps // 4,
+                             a.warmup // 4, nc)
+            ms_gemm = timer(lambda i: layers[i % nc].gemm(X, Y[i % nc]), a.steps // 4, a.warmup // 4, nc)
 
             def rep(i):
                 for m in range(M):
                     layers[i % nc].gemv(xrow[m], Y[i % nc][m])
-            ms_rep = timer(rep, max(1, a.steps // (4 * M)), max(1, a.warmup // (4 * M)))
+            ms_rep = timer(rep, max(1, a.steps // (4 * M)), max(1, a.warmup // (4 * M)), nc)
             flops = 2.0 * M * N * K
-            rows.append({"workload": f"w4_{N}x{K}_m{M}", "bytes": nbytes,
-                         "gemm_us": round(ms_gemm * 1e3, 3),
-                         "gemm_GB/s": round(nbytes / (ms_gemm * 1e-3) / 1e9, 1),
-                         "gemm_TFLOP/s": round(flops / (ms_gemm * 1e-3) / 1e12, 2),
-                         "pct_of_fp16_mfma_peak": round(100 * flops / (ms_gemm * 1e-3) / 2.5e15, 3),
-                         "repeated_gemv_us": round(ms_rep * 1e3, 3),
-                         "speedup_vs_repeated_gemv": round(ms_rep / ms_gemm, 2)})
+            rows.append({"workload": f"w{'4p' if w4_fmt(a) == 5 else '4'}_{N}x{K}_m{M}",
+                         "bytes": nbytes,
+                         "tiled_us": round(ms_tiled * 1e3, 3),
+                         "tiled_GB/s": round(nbytes / (ms_tiled * 1e-3) / 1e9, 1),
+                         "tiled_over_m1": round(ms_tiled / ms_m1, 3),
+                         "m1_tiled_us": round(ms_m1 * 1e3, 3),
+                         "rowmajor_us": round(ms_gemm * 1e3, 3),
+                         "rowmajor_GB/s": round(nbytes / (ms_gemm * 1e-3) / 1e9, 1),
+                         "TFLOP/s": round(flops / (min(ms_tiled, ms_gemm) * 1e-3) / 1e12, 2),
+                         "repeated_gemv_us": round(ms_rep * 1e3, 3)})
+            del layers
     return rows
 
 
@@ -389,7 +456,7 @@ def w2_70b_workload(a, torch, timer):
     for (N, K) in ((28672, 8192), (8192, 28672)):
         L8 = synthetic.config5(N, K, 8)
         base = DeviceLayer(pack_host(2, L8.W, L8.profile, L8.ratio), tiled=True)
-        for M, layout in ((1, "rowmajor"), (1, "tiled"), (8, "rowmajor")):
+        for M, layout in ((1, "rowmajor"), (1, "tiled"), (8, "rowmajor"), (8, "tiled")):
             nbytes = base.nbytes(M)
             layers = rotated(DeviceLayer, base, nbytes)
             nc = len(layers)
@@ -399,9 +466,11 @@ def w2_70b_workload(a, torch, timer):
                 fn = lambda i: layers[i % nc].gemv_tiled(X[0], Y[i % nc][0])  # noqa: E731
             elif M == 1:
                 fn = lambda i: layers[i % nc].gemv(X[0], Y[i % nc][0])  # noqa: E731
+            elif layout == "tiled":
+                fn = lambda i: layers[i % nc].gemm_tiled(X, Y[i % nc])  # noqa: E731
             else:
                 fn = lambda i: layers[i % nc].gemm(X, Y[i % nc])  # noqa: E731
-            ms = timer(fn, a.steps // 4, a.warmup // 4)
+            ms = timer(fn, a.steps // 4, a.warmup // 4, nc)
             rows.append({"workload": f"w2_{N}x{K}_outliers{base.n_out}_m{M}", "layout": layout,
                          "bytes": nbytes, "us": round(ms * 1e3, 3),
                          "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
@@ -433,7 +502,7 @@ def embed_workload(a, torch, timer):
                for _ in range(nsets)]
         outs = [torch.empty((n_ids, K), dtype=torch.int16, device="cuda") for _ in range(4)]
         fn = lambda i: dl.embed(ids[i % nsets], outs[i % 4])  # noqa: E731
-        ms = timer(fn, a.steps // 4, a.warmup // 4)
+        ms = timer(fn, a.steps // 4, a.warmup // 4, nsets)
         nbytes = n_ids * (K // 2 + 2 * G + zrow + 4) + n_ids * K * 2
         rows.append({"workload": f"embed_gather_{V}x{K}_w{'4p' if fmt == 5 else '4'}_ids{n_ids}",
                      "bytes": nbytes, "us": round(ms * 1e3, 3),
@@ -468,7 +537,7 @@ def kurtosis_workload(a, torch, timer):
             x = torch.from_numpy(L.x[:1].reshape(-1).view(np.int16)).cuda()
             ys = [torch.empty(base.N, dtype=torch.int16, device="cuda") for _ in range(nc)]
             ms = timer(lambda i: layers[i % nc].gemv_tiled(x, ys[i % nc]), a.steps // 4,
-                       a.warmup // 4)
+                       a.warmup // 4, nc)
             row[pol] = {"n_out": base.n_out, "bytes": nbytes, "us": round(ms * 1e3, 3),
                         "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
             del layers
@@ -512,9 +581,9 @@ def refine_workload(a, torch, timer):
             B.wq_topk_chunks(x, K, chunk, k, sels[i])
         st = a.steps // 4
         wu = a.warmup // 4
-        t_topk = timer(lambda i: B.wq_topk_chunks(x, K, chunk, k, sels[i % nc]), st, wu)
-        t_ref = timer(lambda i: layers[i % nc].refine(x, ys[i % nc], sels[i % nc], n_sel), st, wu)
-        t_gemv = timer(lambda i: layers[i % nc].gemv_tiled(x, ys[i % nc]), st, wu)
+        t_topk = timer(lambda i: B.wq_topk_chunks(x, K, chunk, k, sels[i % nc]), st, wu, nc)
+        t_ref = timer(lambda i: layers[i % nc].refine(x, ys[i % nc], sels[i % nc], n_sel), st, wu, nc)
+        t_gemv = timer(lambda i: layers[i % nc].gemv_tiled(x, ys[i % nc]), st, wu, nc)
 
         def chain(i):
             lay, y, sel = layers[i % nc], ys[i % nc], sels[i % nc]
@@ -522,25 +591,25 @@ def refine_workload(a, torch, timer):
             B.wq_topk_chunks(x, K, chunk, k, sel)
             lay.refine(x, y, sel, n_sel)
 
-        t_all = timer(chain, st, wu)
-        t_fused = timer(lambda i: layers[i % nc].refine_topk(x, ys[i % nc], k, chunk), st, wu)
+        t_all = timer(chain, st, wu, nc)
+        t_fused = timer(lambda i: layers[i % nc].refine_topk(x, ys[i % nc], k, chunk), st, wu, nc)
         # the same call given a selection buffer (two kernels past 8 chunks)
         t_call = timer(lambda i: layers[i % nc].refine_topk(x, ys[i % nc], k, chunk, sels[i % nc]),
-                       st, wu)
+                       st, wu, nc)
 
         def chain_fused(i):
             layers[i % nc].gemv_tiled(x, ys[i % nc])
             layers[i % nc].refine_topk(x, ys[i % nc], k, chunk)
 
-        t_all_fused = timer(chain_fused, st, wu)
+        t_all_fused = timer(chain_fused, st, wu, nc)
 
         def chain_call(i):
             layers[i % nc].gemv_tiled(x, ys[i % nc])
             layers[i % nc].refine_topk(x, ys[i % nc], k, chunk, sels[i % nc])
 
-        t_all_call = timer(chain_call, st, wu)
+        t_all_call = timer(chain_call, st, wu, nc)
         # the product with the selection and the add in the same launch
-        t_one = timer(lambda i: layers[i % nc].gemv_tiled_refine(x, ys[i % nc], k, chunk), st, wu)
+        t_one = timer(lambda i: layers[i % nc].gemv_tiled_refine(x, ys[i % nc], k, chunk), st, wu, nc)
         Gn = N // 32
         rbytes = n_sel * (N // 2 + 4 * Gn) + 4 * n_sel + 2 * n_sel + 4 * N
         rows.append({"workload": f"refine_topk{k}_per{chunk}_{label}", "N": N, "K": K,
@@ -571,10 +640,52 @@ def stream_workload(a, torch, timer, copy):
     else:
         sink = torch.empty(B.wq_read_probe_sink_words(nb), dtype=torch.int32, device="cuda")
         fn = lambda i: B.wq_read_probe(bufs[i % ncopy], nb, sink)  # noqa: E731
-    ms = timer(fn, a.steps, a.warmup)
+    ms = timer(fn, a.steps, a.warmup, ncopy)
     moved = nb * (2 if copy else 1)
     return {"workload": "copy_probe" if copy else "read_probe", "bytes": nb, "copies": ncopy,
             "us": round(ms * 1e3, 3), "GB/s": round(moved / (ms * 1e-3) / 1e9, 1)}
+
+
+def probe_sweep_workload(a, torch, timer):
+    """The attainable streaming-read rate per launch at the layers' sizes: the
+    geometry-swept read kernel (workgroups x threads x loads in flight per
+    lane; each wave reads one contiguous run) over rotated buffers, every
+    geometry timed like the GEMV.  One line per size, with the best geometry
+    and the whole table."""
+    import bit_weight_only_gemv_amd as B
+    rows = []
+    sizes = [int(v) for v in a.probe_sizes.split(",")] if a.probe_sizes else \
+        [26157628, 10502144, 104555640, 37289984]
+    for nbytes in sizes:
+        nb = (nbytes + 15) // 16 * 16
+        ncopy = max(1, -(-ROTATE_BYTES // nb))
+        bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
+        sink = torch.empty(65536, dtype=torch.int32, device="cuda")
+        table = []
+        for blocks in (256, 512, 768, 1024, 2048, 4096):
+            for threads in (256, 512, 1024):
+                waves = blocks * threads // 64
+                span_kb = -(-nb // 1024 // waves)
+                for ring in (1, 2, 4, 8, 16):
+                    if ring > 2 * max(1, span_kb):
+                        continue
+                    ms = timer(lambda i: B.wq_read_probe_geom(bufs[i % ncopy], nb, sink, blocks,
+                                                               threads, ring),
+                               max(ncopy, a.steps // 10), max(ncopy, a.warmup // 10), ncopy)
+                    table.append({"blocks": blocks, "threads": threads, "ring": ring,
+                                  "span_kb": span_kb, "us": round(ms * 1e3, 3),
+                                  "GB/s": round(nb / (ms * 1e-3) / 1e9, 1)})
+        ms = timer(lambda i: B.wq_read_probe(bufs[i % ncopy], nb, sink[:B.wq_read_probe_sink_words(nb)]),
+                   max(ncopy, a.steps // 10), max(ncopy, a.warmup // 10), ncopy)
+        best = min(table, key=lambda r: r["us"])
+        rows.append({"workload": f"read_probe_sweep_{nb}B", "bytes": nb, "copies": ncopy,
+                     "best": best, "pct_of_hbm_peak": round(best["GB/s"] / HBM_PEAK_GBS * 100, 2),
+                     "grid_stride_probe": {"us": round(ms * 1e3, 3),
+                                           "GB/s": round(nb / (ms * 1e-3) / 1e9, 1)},
+                     "table": sorted(table, key=lambda r: r["us"])[:25]})
+        del bufs
+        torch.cuda.synchronize()
+    return rows
 
 
 def cpu_baseline(L, nbytes):
@@ -649,6 +760,8 @@ def main():
         out = kurtosis_workload(a, torch, timer)
     elif a.workload == "refine":
         out = refine_workload(a, torch, timer)
+    elif a.workload == "probe_sweep":
+        out = probe_sweep_workload(a, torch, timer)
     else:
         out = stream_workload(a, torch, timer, copy=(a.workload == "copy"))
     for o in (out if isinstance(out, list) else [out]):

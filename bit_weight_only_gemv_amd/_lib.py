@@ -68,10 +68,46 @@ SIGNATURES = {
     "wq_gemm_tiled": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _I64, _P, _P]),
     "wq_gemv_tiled_refine": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _I64, _I64,
                                     _P, _P]),
+    "wq_gemv_v": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _P, _P, _P]),
+    "wq_gemm_wq_v": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _I64, _P, _P,
+                            _P]),
+    "wq_gemm_tiled_v": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _P]),
+    "wq_refine_add_v": (_INT, [_P, _P, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P]),
+    "wq_refine_topk_v": (_INT, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "wq_gemv_tiled_refine_v": (_INT, [_INT, _P, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _I64,
+                                      _I64, _P, _P, _P]),
     "wq_read_probe": (_INT, [_P, _I64, _P, _P]),
     "wq_read_probe_sink_words": (_I64, [_I64]),
+    "wq_read_probe_geom": (_INT, [_P, _I64, _P, _INT, _INT, _INT, _P]),
     "wq_copy_probe": (_INT, [_P, _P, _I64, _P]),
 }
+
+
+# Fields of wq_variant (include/wq.h, "kernel-variant selection"), in order.
+VARIANT_FIELDS = ("gemv_kernel", "gemv_rows_per_wave", "gemv_lds_x", "gemm_kernel", "gemm_rows",
+                  "batch_slice_groups", "batch_row_transpose", "refine_groups", "refine_fuse",
+                  "refine_wide")
+
+
+class Variant(ctypes.Structure):
+    """wq_variant: an explicit kernel choice for one call (tests and
+    measurements; not part of the method).  A field < 0 keeps the library's
+    choice."""
+    _fields_ = [(f, ctypes.c_int32) for f in VARIANT_FIELDS]
+
+
+def variant(**fields) -> Variant:
+    """A wq_variant with the given fields set and every other field -1."""
+    v = Variant(*([-1] * len(VARIANT_FIELDS)))
+    for k, val in fields.items():
+        if k not in VARIANT_FIELDS:
+            raise ValueError(f"unknown wq_variant field {k!r}")
+        setattr(v, k, int(val))
+    return v
+
+
+def _vptr(v):
+    return ctypes.addressof(v) if v is not None else None
 
 
 class WQError(RuntimeError):
@@ -249,38 +285,53 @@ def wq_dequant_device(fmt, codes, scales, zeros, N, K, W_hat, stream=None):
                                     _dptr(W_hat), _stream(stream)))
 
 
-def _gemv(fn, codes, scales, zeros, N, K, x, y, out_idx, out_w, n_out, flags, stream):
-    _check(fn(_dptr(codes), _dptr(scales), _dptr(zeros), N, K,
-              _dptr(out_idx) if n_out else None, _dptr(out_w) if n_out else None, n_out, flags,
-              _dptr(x), _dptr(y), _stream(stream)))
+def _gemv(fmt, fn, codes, scales, zeros, N, K, x, y, out_idx, out_w, n_out, flags, stream,
+          variant):
+    args = (_dptr(codes), _dptr(scales), _dptr(zeros), N, K,
+            _dptr(out_idx) if n_out else None, _dptr(out_w) if n_out else None, n_out, flags,
+            _dptr(x), _dptr(y))
+    if variant is None:
+        _check(fn(*args, _stream(stream)))
+    else:
+        _check(load().wq_gemv_v(fmt, *args, _vptr(variant), _stream(stream)))
 
 
 def wq_gemv_w4(codes, scales, zeros, N, K, x, y, out_idx=None, out_w=None, n_out=0,
-               flags=WQ_FUSE_OUTLIERS, stream=None):
-    _gemv(load().wq_gemv_w4, codes, scales, zeros, N, K, x, y, out_idx, out_w, n_out, flags, stream)
+               flags=WQ_FUSE_OUTLIERS, stream=None, variant=None):
+    _gemv(WQ_FMT_W4, load().wq_gemv_w4, codes, scales, zeros, N, K, x, y, out_idx, out_w, n_out,
+          flags, stream, variant)
 
 
 def wq_gemv_w2(codes, scales, zeros, N, K, x, y, out_idx=None, out_w=None, n_out=0,
-               flags=WQ_FUSE_OUTLIERS, stream=None):
-    _gemv(load().wq_gemv_w2, codes, scales, zeros, N, K, x, y, out_idx, out_w, n_out, flags, stream)
+               flags=WQ_FUSE_OUTLIERS, stream=None, variant=None):
+    _gemv(WQ_FMT_W2, load().wq_gemv_w2, codes, scales, zeros, N, K, x, y, out_idx, out_w, n_out,
+          flags, stream, variant)
 
 
 def wq_gemv_w4p(codes, scales, zeros_packed, N, K, x, y, out_idx=None, out_w=None, n_out=0,
-                flags=WQ_FUSE_OUTLIERS, stream=None):
-    _gemv(load().wq_gemv_w4p, codes, scales, zeros_packed, N, K, x, y, out_idx, out_w, n_out, flags,
-          stream)
+                flags=WQ_FUSE_OUTLIERS, stream=None, variant=None):
+    _gemv(WQ_FMT_W4P, load().wq_gemv_w4p, codes, scales, zeros_packed, N, K, x, y, out_idx, out_w,
+          n_out, flags, stream, variant)
 
 
 def wq_gemm_wq(fmt, codes, scales, zeros, N, K, X, M, Y, out_idx=None, out_w=None, n_out=0,
-               flags=WQ_FUSE_OUTLIERS, stream=None):
-    _check(load().wq_gemm_wq(fmt, _dptr(codes), _dptr(scales), _dptr(zeros), N, K,
-                             _dptr(out_idx) if n_out else None, _dptr(out_w) if n_out else None,
-                             n_out, flags, _dptr(X), M, _dptr(Y), _stream(stream)))
+               flags=WQ_FUSE_OUTLIERS, stream=None, variant=None):
+    args = (fmt, _dptr(codes), _dptr(scales), _dptr(zeros), N, K,
+            _dptr(out_idx) if n_out else None, _dptr(out_w) if n_out else None,
+            n_out, flags, _dptr(X), M, _dptr(Y))
+    if variant is None:
+        _check(load().wq_gemm_wq(*args, _stream(stream)))
+    else:
+        _check(load().wq_gemm_wq_v(*args, _vptr(variant), _stream(stream)))
 
 
-def wq_gemm_tiled(fmt, tiled, N, K, X, M, Y, out_idx=None, n_out=0, stream=None):
-    _check(load().wq_gemm_tiled(fmt, _dptr(tiled), N, K, _dptr(out_idx) if n_out else None, n_out,
-                                _dptr(X), M, _dptr(Y), _stream(stream)))
+def wq_gemm_tiled(fmt, tiled, N, K, X, M, Y, out_idx=None, n_out=0, stream=None, variant=None):
+    args = (fmt, _dptr(tiled), N, K, _dptr(out_idx) if n_out else None, n_out, _dptr(X), M,
+            _dptr(Y))
+    if variant is None:
+        _check(load().wq_gemm_tiled(*args, _stream(stream)))
+    else:
+        _check(load().wq_gemm_tiled_v(*args, _vptr(variant), _stream(stream)))
 
 
 def wq_gemv_tiled(fmt, tiled, N, K, x, y, out_idx=None, n_out=0, stream=None):
@@ -289,12 +340,14 @@ def wq_gemv_tiled(fmt, tiled, N, K, x, y, out_idx=None, n_out=0, stream=None):
 
 
 def wq_gemv_tiled_refine(fmt, tiled, N, K, x, y, rcodes, rscales, rzeros, chunk, k, out_idx=None,
-                         n_out=0, sel_out=None, stream=None):
-    _check(load().wq_gemv_tiled_refine(fmt, _dptr(tiled), N, K, _dptr(out_idx) if n_out else None,
-                                       n_out, _dptr(x), _dptr(y), _dptr(rcodes), _dptr(rscales),
-                                       _dptr(rzeros), chunk, k,
-                                       _dptr(sel_out) if sel_out is not None else None,
-                                       _stream(stream)))
+                         n_out=0, sel_out=None, stream=None, variant=None):
+    args = (fmt, _dptr(tiled), N, K, _dptr(out_idx) if n_out else None, n_out, _dptr(x), _dptr(y),
+            _dptr(rcodes), _dptr(rscales), _dptr(rzeros), chunk, k,
+            _dptr(sel_out) if sel_out is not None else None)
+    if variant is None:
+        _check(load().wq_gemv_tiled_refine(*args, _stream(stream)))
+    else:
+        _check(load().wq_gemv_tiled_refine_v(*args, _vptr(variant), _stream(stream)))
 
 
 def wq_embed_gather(fmt, codes, scales, zeros, V, K, ids, n_ids, out, stream=None):
@@ -315,16 +368,23 @@ def wq_topk_chunks(x, K, chunk, k, sel, stream=None):
                                  _stream(stream)))
 
 
-def wq_refine_add(rcodes, rscales, rzeros, N, K, sel, n_sel, x, y, stream=None):
-    _check(load().wq_refine_add(_dptr(rcodes), _dptr(rscales), _dptr(rzeros), N, K,
-                                _dptr(sel) if n_sel else None, n_sel, _dptr(x), _dptr(y),
-                                _stream(stream)))
+def wq_refine_add(rcodes, rscales, rzeros, N, K, sel, n_sel, x, y, stream=None, variant=None):
+    args = (_dptr(rcodes), _dptr(rscales), _dptr(rzeros), N, K, _dptr(sel) if n_sel else None,
+            n_sel, _dptr(x), _dptr(y))
+    if variant is None:
+        _check(load().wq_refine_add(*args, _stream(stream)))
+    else:
+        _check(load().wq_refine_add_v(*args, _vptr(variant), _stream(stream)))
 
 
-def wq_refine_topk(rcodes, rscales, rzeros, N, K, chunk, k, x, y, sel_out=None, stream=None):
-    _check(load().wq_refine_topk(_dptr(rcodes), _dptr(rscales), _dptr(rzeros), N, K, chunk, k,
-                                 _dptr(x), _dptr(y), _dptr(sel_out) if sel_out is not None else None,
-                                 _stream(stream)))
+def wq_refine_topk(rcodes, rscales, rzeros, N, K, chunk, k, x, y, sel_out=None, stream=None,
+                   variant=None):
+    args = (_dptr(rcodes), _dptr(rscales), _dptr(rzeros), N, K, chunk, k, _dptr(x), _dptr(y),
+            _dptr(sel_out) if sel_out is not None else None)
+    if variant is None:
+        _check(load().wq_refine_topk(*args, _stream(stream)))
+    else:
+        _check(load().wq_refine_topk_v(*args, _vptr(variant), _stream(stream)))
 
 
 def wq_outlier_add(idx, out_w, n_out, N, X, M, K, Y, stream=None):
@@ -338,6 +398,11 @@ def wq_read_probe_sink_words(nbytes: int) -> int:
 
 def wq_read_probe(src, nbytes, sink, stream=None):
     _check(load().wq_read_probe(_dptr(src), nbytes, _dptr(sink), _stream(stream)))
+
+
+def wq_read_probe_geom(src, nbytes, sink, blocks, threads, ring, stream=None):
+    _check(load().wq_read_probe_geom(_dptr(src), nbytes, _dptr(sink), blocks, threads, ring,
+                                     _stream(stream)))
 
 
 def wq_copy_probe(src, dst, nbytes, stream=None):

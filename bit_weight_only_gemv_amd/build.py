@@ -57,7 +57,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         objs.append(obj)
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        cmds.append([hipcc, *common, f"--offload-arch={ARCH}", "-munsafe-fp-atomics",
+        cmds.append([hipcc, *common, f"--offload-arch={ARCH}",
                      "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                      "-Wno-unused-command-line-argument",
                      "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj])

@@ -37,6 +37,12 @@ inline int device_cus() {
   return cached[dev];
 }
 
+// A field of an explicit kernel-variant choice (wq.h, wq_variant), or `def`
+// when there is none (v NULL or the field negative).
+inline int variant_or(const wq_variant* v, int32_t wq_variant::*f, int def) {
+  return (v != nullptr && v->*f >= 0) ? (int)(v->*f) : def;
+}
+
 // Turns a failed launch into WQ_ERR_HIP with the runtime's message.
 inline int check_launch(const char* who) {
   const hipError_t e = hipGetLastError();

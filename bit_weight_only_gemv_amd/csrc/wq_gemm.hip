@@ -23,7 +23,6 @@
 #include "wq_device.h"
 #include "wq_mma.h"
 
-#include <stdlib.h>
 
 namespace wqd {
 
@@ -223,10 +222,11 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs a) {
 
 using namespace wqd;
 
-extern "C" int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales,
-                          const uint16_t* zeros, int64_t N, int64_t K, const int32_t* out_idx,
-                          const uint16_t* out_w, int64_t n_out, uint32_t flags, const uint16_t* X,
-                          int64_t M, uint16_t* Y, void* stream) {
+extern "C" int wq_gemm_wq_v(int fmt, const uint8_t* codes, const uint16_t* scales,
+                            const uint16_t* zeros, int64_t N, int64_t K, const int32_t* out_idx,
+                            const uint16_t* out_w, int64_t n_out, uint32_t flags,
+                            const uint16_t* X, int64_t M, uint16_t* Y, const wq_variant* v,
+                            void* stream) {
   const char* who = "wq_gemm_wq";
   if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2 && fmt != WQ_FMT_W4P)
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2", who);
@@ -248,30 +248,21 @@ extern "C" int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales,
   // M = 1 is the GEMV; 2 <= M <= 16 goes to the persistent matrix-core kernel
   // when its plan fits (it fuses the outlier pass; an unfused call with
   // outlier columns stays here)
-  if (M == 1) {
-    if (fmt == WQ_FMT_W4P)
-      return wq_gemv_w4p(codes, scales, reinterpret_cast<const uint8_t*>(zeros), N, K, out_idx,
-                         out_w, n_out, flags, X, Y, stream);
-    return fmt == WQ_FMT_W4 ? wq_gemv_w4(codes, scales, zeros, N, K, out_idx, out_w, n_out, flags,
-                                         X, Y, stream)
-                            : wq_gemv_w2(codes, scales, zeros, N, K, out_idx, out_w, n_out, flags,
-                                         X, Y, stream);
-  }
+  if (M == 1)
+    return wq_gemv_v(fmt, codes, scales, zeros, N, K, out_idx, out_w, n_out, flags, X, Y, v,
+                     stream);
   if (a.fuse || n_out == 0) {
-    int mode = 1;
-    if (const char* e = getenv("WQ_GEMM_MMA")) mode = atoi(e);
+    const int mode = variant_or(v, &wq_variant::gemm_kernel, 1);
     bool launched = false;
     // up to four rows (two for W2): the M = 1 matrix-core kernel with its group
-    // slots shared by the rows (its decode needs no FP16 weights);
-    // WQ_GEMM_ROWS=0 skips it
-    const char* er = getenv("WQ_GEMM_ROWS");
-    if (M <= 4 && mode != 0 && !(er && atoi(er) == 0)) {
+    // slots shared by the rows (its decode needs no FP16 weights)
+    if (M <= 4 && mode != 0 && variant_or(v, &wq_variant::gemm_rows, 1) != 0) {
       const int r = wqd_mma_rows(fmt, false, codes, scales, zeros, N, K, out_idx, out_w,
                                  a.fuse ? n_out : 0, X, M, Y, s, who, 2, &launched);
       if (r != WQ_OK || launched) return r;
     }
     const int r = wqd_gemm_mma(fmt, codes, scales, zeros, N, K, out_idx, out_w, a.fuse ? n_out : 0,
-                               X, M, Y, s, who, mode, &launched);
+                               X, M, Y, v, s, who, mode, &launched);
     if (r != WQ_OK || launched) return r;
   }
   const int G = (int)(K / kGroup);
@@ -292,4 +283,12 @@ extern "C" int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales,
   else
     hipLaunchKernelGGL(gemm_kernel<2>, grid, block, lds, s, a);
   return check_launch(who);
+}
+
+extern "C" int wq_gemm_wq(int fmt, const uint8_t* codes, const uint16_t* scales,
+                          const uint16_t* zeros, int64_t N, int64_t K, const int32_t* out_idx,
+                          const uint16_t* out_w, int64_t n_out, uint32_t flags, const uint16_t* X,
+                          int64_t M, uint16_t* Y, void* stream) {
+  return wq_gemm_wq_v(fmt, codes, scales, zeros, N, K, out_idx, out_w, n_out, flags, X, M, Y,
+                      nullptr, stream);
 }

@@ -32,7 +32,6 @@
 #include "wq_device.h"
 #include "wq_mma.h"
 
-#include <stdlib.h>
 
 #include <algorithm>
 
@@ -659,7 +658,7 @@ struct GemvPlan {
   bool lds_path;   // gemv_lds_kernel (x and the W2 table in LDS) or gemv_reg_kernel
 };
 
-static GemvPlan plan_gemv(int fmt, int64_t N, int64_t K, int64_t n_out) {
+static GemvPlan plan_gemv(int fmt, int64_t N, int64_t K, int64_t n_out, const wq_variant* v) {
   const int G = (int)(K / kGroup);
   GemvPlan p{};
   // Fewest idle lanes, at most 8 K-waves; on a tie prefer 2 groups per lane,
@@ -677,10 +676,8 @@ static GemvPlan plan_gemv(int fmt, int64_t N, int64_t K, int64_t n_out) {
   }
   p.wr = p.wk >= 4 ? 1 : 4 / p.wk;
   p.rpw = kRowsPerStep;
-  if (const char* e = getenv("WQ_GEMV_ROWS_PER_WAVE")) {
-    const int v = atoi(e);
-    if (v >= 1 && v <= kRowsPerStep) p.rpw = v;
-  }
+  const int rpw = variant_or(v, &wq_variant::gemv_rows_per_wave, kRowsPerStep);
+  if (rpw >= 1 && rpw <= kRowsPerStep) p.rpw = rpw;
   p.rt = p.wr * p.rpw;
   p.blocks = (int)((N + p.rt - 1) / p.rt);
   const size_t part = (size_t)16 * p.rt * p.wk;
@@ -688,7 +685,7 @@ static GemvPlan plan_gemv(int fmt, int64_t N, int64_t K, int64_t n_out) {
   p.lds_path = p.lds <= kMaxLdsBytes;
   // the W2 pairing of consecutive groups needs an even group count
   if (fmt == 2 && p.gpl % 2 == 0 && G % 2 != 0) p.lds_path = false;
-  if (const char* e = getenv("WQ_GEMV_LDS_PATH")) p.lds_path = p.lds_path && atoi(e) != 0;
+  p.lds_path = p.lds_path && variant_or(v, &wq_variant::gemv_lds_x, 1) != 0;
   if (!p.lds_path) p.lds = std::max((size_t)4 * G, part);
   // 16-byte chunks of x per thread, loaded before the weights
   const int nthr = p.wk * p.wr * kWave;
@@ -698,9 +695,10 @@ static GemvPlan plan_gemv(int fmt, int64_t N, int64_t K, int64_t n_out) {
 }
 
 template <int FMT>
-static int launch_gemv(const GemvArgs& a0, hipStream_t stream, const char* who) {
+static int launch_gemv(const GemvArgs& a0, hipStream_t stream, const char* who,
+                       const wq_variant* v) {
   GemvArgs a = a0;
-  const GemvPlan p = plan_gemv(FMT, a.N, a.K, a.n_out);
+  const GemvPlan p = plan_gemv(FMT, a.N, a.K, a.n_out, v);
   if (p.gpl == 0) return wq::fail(WQ_ERR_UNSUPPORTED, "%s: K=%d not supported", who, a.K);
   if (p.lds > kMaxLdsBytes)
     return wq::fail(WQ_ERR_UNSUPPORTED, "%s: %zu bytes of LDS needed", who, p.lds);
@@ -741,7 +739,7 @@ using namespace wqd;
 static int gemv_entry(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
                       int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
                       int64_t n_out, uint32_t flags, const uint16_t* x, uint16_t* y,
-                      void* stream, const char* who) {
+                      const wq_variant* v, void* stream, const char* who) {
   if (int r = wq::check_shape(N, K, who)) return r;
   if (int r = wq::check_outlier_args(out_idx, out_w, n_out, K, who)) return r;
   if (!codes || !scales || !zeros || !x || !y)
@@ -765,23 +763,32 @@ static int gemv_entry(int fmt, const uint8_t* codes, const uint16_t* scales, con
   // the matrix-core kernel fuses the outlier pass; an unfused call with
   // outlier columns stays on the VALU kernels
   if (a.fuse || n_out == 0) {
-    int mode = 1;
-    if (const char* e = getenv("WQ_GEMV_MMA")) mode = atoi(e);
+    const int mode = variant_or(v, &wq_variant::gemv_kernel, 1);
     bool launched = false;
     const int r = wqd_gemv_mma(fmt, false, codes, scales, zeros, N, K, out_idx, out_w,
                                a.fuse ? n_out : 0, x, y, s, who, mode, &launched);
     if (r != WQ_OK || launched) return r;
   }
-  return fmt == 4 ? launch_gemv<4>(a, s, who)
-                  : fmt == 5 ? launch_gemv<5>(a, s, who) : launch_gemv<2>(a, s, who);
+  return fmt == 4 ? launch_gemv<4>(a, s, who, v)
+                  : fmt == 5 ? launch_gemv<5>(a, s, who, v) : launch_gemv<2>(a, s, who, v);
+}
+
+extern "C" int wq_gemv_v(int fmt, const uint8_t* codes, const uint16_t* scales,
+                         const uint16_t* zeros, int64_t N, int64_t K, const int32_t* out_idx,
+                         const uint16_t* out_w, int64_t n_out, uint32_t flags, const uint16_t* x,
+                         uint16_t* y, const wq_variant* variant, void* stream) {
+  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2 && fmt != WQ_FMT_W4P)
+    return wq::fail(WQ_ERR_INVALID_ARG, "wq_gemv_v: fmt must be WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2");
+  return gemv_entry(fmt, codes, scales, zeros, N, K, out_idx, out_w, n_out, flags, x, y, variant,
+                    stream, "wq_gemv_v");
 }
 
 extern "C" int wq_gemv_w4(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
                           int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
                           int64_t n_out, uint32_t flags, const uint16_t* x, uint16_t* y,
                           void* stream) {
-  return gemv_entry(4, codes, scales, zeros, N, K, out_idx, out_w, n_out, flags, x, y, stream,
-                    "wq_gemv_w4");
+  return gemv_entry(4, codes, scales, zeros, N, K, out_idx, out_w, n_out, flags, x, y, nullptr,
+                    stream, "wq_gemv_w4");
 }
 
 extern "C" int wq_gemv_w4p(const uint8_t* codes, const uint16_t* scales,
@@ -789,20 +796,20 @@ extern "C" int wq_gemv_w4p(const uint8_t* codes, const uint16_t* scales,
                            const int32_t* out_idx, const uint16_t* out_w, int64_t n_out,
                            uint32_t flags, const uint16_t* x, uint16_t* y, void* stream) {
   return gemv_entry(5, codes, scales, reinterpret_cast<const uint16_t*>(zeros_packed), N, K,
-                    out_idx, out_w, n_out, flags, x, y, stream, "wq_gemv_w4p");
+                    out_idx, out_w, n_out, flags, x, y, nullptr, stream, "wq_gemv_w4p");
 }
 
 extern "C" int wq_gemv_w2(const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
                           int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
                           int64_t n_out, uint32_t flags, const uint16_t* x, uint16_t* y,
                           void* stream) {
-  return gemv_entry(2, codes, scales, zeros, N, K, out_idx, out_w, n_out, flags, x, y, stream,
-                    "wq_gemv_w2");
+  return gemv_entry(2, codes, scales, zeros, N, K, out_idx, out_w, n_out, flags, x, y, nullptr,
+                    stream, "wq_gemv_w2");
 }
 
-extern "C" int wq_gemm_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
-                             const int32_t* out_idx, int64_t n_out, const uint16_t* X, int64_t M,
-                             uint16_t* Y, void* stream) {
+extern "C" int wq_gemm_tiled_v(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
+                               const int32_t* out_idx, int64_t n_out, const uint16_t* X, int64_t M,
+                               uint16_t* Y, const wq_variant* variant, void* stream) {
   const char* who = "wq_gemm_tiled";
   if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2 && fmt != WQ_FMT_W4P)
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2", who);
@@ -811,22 +818,35 @@ extern "C" int wq_gemm_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: n_out must be in [0, K] (got %lld)", who,
                     (long long)n_out);
   if (M < 1) return wq::fail(WQ_ERR_INVALID_ARG, "%s: M must be >= 1", who);
-  if (M > 4 || (M > 2 && fmt == WQ_FMT_W2))
-    return wq::fail(WQ_ERR_UNSUPPORTED, "%s: M must be at most 4 (W2: 2)", who);
+  if (M > WQ_GEMM_MAX_M)
+    return wq::fail(WQ_ERR_UNSUPPORTED, "%s: M above %d is not supported", who, WQ_GEMM_MAX_M);
   if (!tiled || !X || !Y || (n_out > 0 && !out_idx))
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
   if (!aligned16(tiled) || !aligned16(X) || !aligned16(Y) || (n_out > 0 && !aligned16(out_idx)))
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: device pointers must be 16-byte aligned", who);
   bool launched = false;
-  const int r = wqd_mma_rows(fmt, true, tiled, nullptr, nullptr, N, K, out_idx, nullptr, n_out, X,
-                             M, Y, (hipStream_t)stream, who, 2, &launched);
-  if (r != WQ_OK) return r;
-  if (!launched)
-    return wq::fail(WQ_ERR_UNSUPPORTED,
-                    "%s: shape not supported by the tiled kernel at M = %lld (K <= 32768, at most "
-                    "32 outlier positions per 512-channel slice; more rows need more LDS and, at "
-                    "3 or 4 rows, at most 4 slices per wave)", who, (long long)M);
-  return WQ_OK;
+  // up to four rows (W2: two): the M = 1 kernel with its group slots shared
+  // by the rows; else the batched kernel on the same tiles
+  if (M == 1 || variant_or(variant, &wq_variant::gemm_rows, 1) != 0) {
+    const int r = wqd_mma_rows(fmt, true, tiled, nullptr, nullptr, N, K, out_idx, nullptr, n_out,
+                               X, M, Y, (hipStream_t)stream, who, 2, &launched);
+    if (r != WQ_OK || launched) return r;
+  }
+  if (M >= 2) {
+    const int r = wqd_gemm_mma_tiled(fmt, tiled, N, K, out_idx, n_out, X, M, Y, variant,
+                                     (hipStream_t)stream, who, &launched);
+    if (r != WQ_OK || launched) return r;
+  }
+  return wq::fail(WQ_ERR_UNSUPPORTED,
+                  "%s: shape not supported by the tiled kernels at M = %lld (K <= 32768, at most "
+                  "32 outlier positions per 512-channel slice, at most 1024 outlier columns for "
+                  "M > 1, partial sums within the LDS)", who, (long long)M);
+}
+
+extern "C" int wq_gemm_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
+                             const int32_t* out_idx, int64_t n_out, const uint16_t* X, int64_t M,
+                             uint16_t* Y, void* stream) {
+  return wq_gemm_tiled_v(fmt, tiled, N, K, out_idx, n_out, X, M, Y, nullptr, stream);
 }
 
 extern "C" int wq_gemv_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
@@ -854,11 +874,11 @@ extern "C" int wq_gemv_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K
   return WQ_OK;
 }
 
-extern "C" int wq_gemv_tiled_refine(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
-                                    const int32_t* out_idx, int64_t n_out, const uint16_t* x,
-                                    uint16_t* y, const uint8_t* rcodes, const uint16_t* rscales,
-                                    const uint16_t* rzeros, int64_t chunk, int64_t k,
-                                    int32_t* sel_out, void* stream) {
+extern "C" int wq_gemv_tiled_refine_v(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
+                                      const int32_t* out_idx, int64_t n_out, const uint16_t* x,
+                                      uint16_t* y, const uint8_t* rcodes, const uint16_t* rscales,
+                                      const uint16_t* rzeros, int64_t chunk, int64_t k,
+                                      int32_t* sel_out, const wq_variant* variant, void* stream) {
   const char* who = "wq_gemv_tiled_refine";
   if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2 && fmt != WQ_FMT_W4P)
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2", who);
@@ -878,15 +898,23 @@ extern "C" int wq_gemv_tiled_refine(int fmt, const uint8_t* tiled, int64_t N, in
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: device pointers must be 16-byte aligned", who);
   if ((uint64_t)K * (uint64_t)N / 2 > 0xFFFFE000ull)
     return wq::fail(WQ_ERR_UNSUPPORTED, "%s: refinement larger than 4 GB", who);
-  const char* e = getenv("WQ_REFINE_FUSE");
-  if (e == nullptr || atoi(e) != 0) {
+  if (variant_or(variant, &wq_variant::refine_fuse, 1) != 0) {
     bool launched = false;
     const int r = wqd_gemv_refine_mma(fmt, tiled, N, K, out_idx, n_out, x, y, rcodes, rscales,
-                                      rzeros, chunk, k, sel_out, (hipStream_t)stream, who,
+                                      rzeros, chunk, k, sel_out, variant, (hipStream_t)stream, who,
                                       &launched);
     if (r != WQ_OK || launched) return r;
   }
   // two launches: the product (rounded to FP16), then the selection and the add
   if (int r = wq_gemv_tiled(fmt, tiled, N, K, out_idx, n_out, x, y, stream)) return r;
-  return wq_refine_topk(rcodes, rscales, rzeros, N, K, chunk, k, x, y, sel_out, stream);
+  return wq_refine_topk_v(rcodes, rscales, rzeros, N, K, chunk, k, x, y, sel_out, variant, stream);
+}
+
+extern "C" int wq_gemv_tiled_refine(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
+                                    const int32_t* out_idx, int64_t n_out, const uint16_t* x,
+                                    uint16_t* y, const uint8_t* rcodes, const uint16_t* rscales,
+                                    const uint16_t* rzeros, int64_t chunk, int64_t k,
+                                    int32_t* sel_out, void* stream) {
+  return wq_gemv_tiled_refine_v(fmt, tiled, N, K, out_idx, n_out, x, y, rcodes, rscales, rzeros,
+                                chunk, k, sel_out, nullptr, stream);
 }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "wq.h"
+
 // Launches the matrix-core M = 1 kernel when the shape suits it and sets
 // *launched; otherwise returns WQ_OK with *launched = false and the caller
 // uses the VALU kernels.  `mode`: 0 = never, 1 = when the plan prefers it,
@@ -28,8 +30,16 @@ int wqd_mma_rows(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scal
 // it (same contract and `mode` values as wqd_gemv_mma).
 int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
                  int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
-                 int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream,
-                 const char* who, int mode, bool* launched);
+                 int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y, const wq_variant* v,
+                 hipStream_t stream, const char* who, int mode, bool* launched);
+
+// The batched kernel (2 <= M <= 16) on the tiled layout of the M = 1 kernel
+// (the same buffer): each wave load is four contiguous 256-byte runs of a
+// tile.  Launches when the shape suits it and sets *launched.
+int wqd_gemm_mma_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
+                       const int32_t* out_idx, int64_t n_out, const uint16_t* X, int64_t M,
+                       uint16_t* Y, const wq_variant* v, hipStream_t stream, const char* who,
+                       bool* launched);
 
 // The tiled M = 1 kernel with the runtime top-k refinement fused in: y =
 // FP16(layer x + sum over the k largest |x_i| of each chunk of x_i C[:, i]),
@@ -43,5 +53,5 @@ int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
 int wqd_gemv_refine_mma(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
                         const int32_t* out_idx, int64_t n_out, const uint16_t* x, uint16_t* y,
                         const uint8_t* rcodes, const uint16_t* rscales, const uint16_t* rzeros,
-                        int64_t chunk, int64_t k, int32_t* sel_out, hipStream_t stream,
-                        const char* who, bool* launched);
+                        int64_t chunk, int64_t k, int32_t* sel_out, const wq_variant* v,
+                        hipStream_t stream, const char* who, bool* launched);

@@ -63,7 +63,6 @@
 #include "wq_mma.h"
 #include "wq_select.cuh"
 
-#include <stdlib.h>
 
 #include <algorithm>
 
@@ -896,13 +895,17 @@ struct MmbArgs {
   uint16_t* Y;
   int N, K, M, n_out;
   int nw, nks, nrb, rbl;
+  int nch;   // tiled layout: outlier chunks of 8 slab positions, ceil(n_out / 8)
 };
 
-// LDS: W2 table; per wave two slice areas (outlier-column mask, one bit per
-// channel of the slice, and the run's column offsets, up to one per channel);
-// partial tiles [rbl][nw][Mp][16] with Mp = M rounded up to the lane quarter's
-// 4 rows (rows M..Mp-1 stay unread).
-__host__ __device__ constexpr uint32_t mmb_wave_area(int qg) { return 16u * qg + 512u * qg; }
+// LDS: W2 table; with outliers per wave two slice areas (outlier-column mask,
+// one bit per channel of the slice, and, on the row-major layout, the run's
+// column offsets, up to one per channel); partial tiles [rbl][nw][Mp][16]
+// with Mp = M rounded up to the lane quarter's 4 rows (rows M..Mp-1 stay
+// unread).
+__host__ __device__ constexpr uint32_t mmb_wave_area(int qg, bool tiled) {
+  return tiled ? 16u * qg : 16u * qg + 512u * qg;
+}
 struct MmbLds {
   uint32_t lut, wave, runs, idx, part, xt, total;
 };
@@ -912,13 +915,13 @@ __host__ __device__ constexpr uint32_t mmb_xt_stride(int qg) { return 256u * qg 
 // With outliers also: the run table (slice ks's run of the sorted indices
 // starts at runs[ks], nks + 1 words) and a copy of the indices (256 iv words).
 __host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl, int qg, int nks,
-                                                 int iv, bool xt = false) {
+                                                 int iv, bool xt = false, bool tiled = false) {
   MmbLds L{};
   uint32_t off = 0;
   L.lut = off;
   if (fmt == 2) off += 256u * kLutRow;
   L.wave = off;
-  off += (uint32_t)nw * 2u * mmb_wave_area(qg);
+  if (iv > 0) off += (uint32_t)nw * 2u * mmb_wave_area(qg, tiled);
   L.runs = off;
   if (iv > 0) off += ((uint32_t)(nks + 1) * 4u + 15u) & ~15u;
   L.idx = off;
@@ -941,17 +944,26 @@ struct ItemB {
 __device__ __forceinline__ uint32_t splat_lo(uint32_t v) { return __builtin_amdgcn_perm(v, v, 0x01000100u); }
 __device__ __forceinline__ uint32_t splat_hi(uint32_t v) { return __builtin_amdgcn_perm(v, v, 0x03020302u); }
 
-template <int FMT, int IV, int DEPTH, int QG, bool XT>
+// TILED: the layer in the tiled layout of the M = 1 kernel (512-channel slices,
+// QG = 4).  Lane (n, q) reads its groups 4q .. 4q + 3 of a tile as 256-byte
+// runs: each load of a wave is 4 contiguous runs instead of 64 row segments.
+// The scale/zero tile gives lane (n, q) exactly those groups' scales and zeros.
+// The outlier slab is split by position, as in the M = 1 kernel: slice ks owns
+// chunks C(ks) .. C(ks + 1) - 1 of 8 positions (at most 4), lane quarter q
+// takes chunk C(ks) + q, and its activations are gathered per slice through
+// the index copy in LDS; the chunks are zero-padded, so no alignment or mask.
+template <int FMT, int IV, int DEPTH, int QG, bool XT, bool TILED = false>
 __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   typedef MmbFmt<FMT, QG> F;
+  static_assert(!TILED || QG == 4, "the tiled layout has 512-channel slices");
   constexpr int kSliceChB = F::kSliceCh;
   constexpr int kSliceGroupsB = F::kSliceGroups;
   constexpr int XS = F::kSteps;
-  constexpr uint32_t kMmbWaveArea = mmb_wave_area(QG);
+  constexpr uint32_t kMmbWaveArea = mmb_wave_area(QG, TILED);
   constexpr bool OUT = IV > 0;
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_out = OUT ? a.n_out : 0;
-  const MmbLds L = mmb_lds_layout(FMT, a.M, a.nw, a.rbl, QG, a.nks, IV, XT);
+  const MmbLds L = mmb_lds_layout(FMT, a.M, a.nw, a.rbl, QG, a.nks, IV, XT, TILED);
   uint32_t* s_runs = reinterpret_cast<uint32_t*>(smem + L.runs);
   const int32_t* s_idx = reinterpret_cast<const int32_t*>(smem + L.idx);
   const int tid = threadIdx.x;
@@ -966,14 +978,20 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   const int ns_w = (a.nks - w + a.nw - 1) / a.nw;
   const int T = ns_w * nrb_wg;
 
-  const __amdgpu_buffer_rsrc_t crs = make_rsrc(a.codes, clamp_bytes((uint64_t)a.N * row_bytes));
-  const uint64_t meta = (uint64_t)a.N * G * 2;
+  const uint64_t tiles = (uint64_t)a.nrb * a.nks;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(
+      a.codes, clamp_bytes(TILED ? tiles * 16 * F::kSliceBytes : (uint64_t)a.N * row_bytes));
+  const uint64_t meta = TILED ? tiles * (FMT == 5 ? 640 : 1024) : (uint64_t)a.N * G * 2;
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.scales, clamp_bytes(meta));
   // W4P: zero points packed two per byte, (G / 2) bytes per row (G is even here)
   const __amdgpu_buffer_rsrc_t zrs =
-      make_rsrc(a.zeros, clamp_bytes(FMT == 5 ? (uint64_t)a.N * (G / 2) : meta));
-  const __amdgpu_buffer_rsrc_t ors =
-      make_rsrc(a.out_w, clamp_bytes(((uint64_t)a.N * n_out * 2 + 3) & ~(uint64_t)3));
+      make_rsrc(TILED ? a.scales : a.zeros,
+                clamp_bytes(TILED ? meta : FMT == 5 ? (uint64_t)a.N * (G / 2) : meta));
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(
+      a.out_w, clamp_bytes(TILED ? (uint64_t)a.nrb * a.nch * 256
+                                 : ((uint64_t)a.N * n_out * 2 + 3) & ~(uint64_t)3));
+  // tiled slab: slice ks owns chunks chunk_lo(ks) .. chunk_lo(ks + 1) - 1
+  auto chunk_lo = [&](int ks) { return (uint32_t)(ks * a.nch) / (uint32_t)a.nks; };
   const __amdgpu_buffer_rsrc_t irs = make_rsrc(a.out_idx, ((uint32_t)n_out * 4u + 15u) & ~15u);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.X, clamp_bytes((uint64_t)a.M * a.K * 2));
   const __amdgpu_buffer_rsrc_t nul = make_rsrc(a.codes, 0u);
@@ -1022,7 +1040,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   // ones in xpre2), as the weights are two items ahead (measured: the W2
   // 8192 x 28672 layer at M = 8 gains 8%; without outliers the registers cost
   // more than the earlier loads gain)
-  constexpr bool X2 = XT && OUT;
+  constexpr bool X2 = XT && OUT && !TILED;
   u4v xpre[XS];
   u4v xpre2[X2 ? XS : 1];
   x_load(w, xpre);
@@ -1046,6 +1064,25 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     const __amdgpu_buffer_rsrc_t s_ = valid ? srs : nul;
     const __amdgpu_buffer_rsrc_t z_ = valid ? zrs : nul;
     const uint32_t row = (uint32_t)(rb * 16 + n16);
+    if constexpr (TILED) {
+      // tile (rb, ks); lane (n, q): W4 load u = group 4q + u, at 1024 q + 16 (n + 16 u);
+      // W2 load v = groups 4q + 2v, + 1, at 1024 (q / 2) + 16 (n + 16 (2 (q % 2) + v))
+      const uint32_t tile = (uint32_t)(rb * a.nks + ks);
+      const uint32_t cb = tile * (16u * F::kSliceBytes) +
+                          (FMT == 2 ? 1024u * (uint32_t)(q >> 1) + 16u * (uint32_t)(n16 + 32 * (q & 1))
+                                    : 1024u * (uint32_t)q + 16u * (uint32_t)n16);
+#pragma unroll
+      for (int u = 0; u < F::kLoads; ++u) it.cw[u] = ld128(c_, cb + 256u * u);
+      if constexpr (FMT == 5) {   // 640-byte tile: 4 scales per lane, then 4 packed zeros
+        it.sv = ld64(s_, tile * 640u + 8u * (uint32_t)lane);
+        it.zv = (u2){(uint32_t)ld16(s_, tile * 640u + 512u + 2u * (uint32_t)lane), 0u};
+      } else {
+        const u4v m = ld128(s_, tile * 1024u + 16u * (uint32_t)lane);
+        it.sv = (u2){m.x, m.y};
+        it.zv = (u2){m.z, m.w};
+      }
+      return;
+    }
     const uint32_t rbase = row * row_bytes + (uint32_t)(ks * F::kSliceBytes + 16 * F::kLoads * q);
 #pragma unroll
     for (int u = 0; u < F::kLoads; ++u) it.cw[u] = ld128(c_, rbase + 16u * u);
@@ -1064,7 +1101,16 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     }
   };
   auto load_slab = [&](ItemB<FMT, OUT, QG>& it, bool valid, int ks, int rb) {
-    if constexpr (OUT) {
+    if constexpr (OUT && TILED) {
+      const uint32_t c0 = chunk_lo(ks);
+      const bool on = valid && (uint32_t)q < chunk_lo(ks + 1) - c0;
+      const uint32_t off = ((uint32_t)rb * (uint32_t)a.nch + c0) * 256u + 16u * (uint32_t)lane;
+      const u4v t = ld128(ors, on ? off : kOob);
+      it.od[0] = t.x;
+      it.od[1] = t.y;
+      it.od[2] = t.z;
+      it.od[3] = t.w;
+    } else if constexpr (OUT) {
       int j_lo, nin;
       jrange(ks, j_lo, nin);
       const __amdgpu_buffer_rsrc_t o_ = valid ? ors : nul;
@@ -1158,24 +1204,44 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   auto prep_slice = [&](int ks, int p) {
     if constexpr (OUT) {
       uint32_t* mask = reinterpret_cast<uint32_t*>(smem + warea0 + (uint32_t)p * kMmbWaveArea);
+      // (the tiled layout keeps no run list: its slab is split by position)
       int32_t* list =
           reinterpret_cast<int32_t*>(smem + warea0 + (uint32_t)p * kMmbWaveArea + 16u * QG);
       int j_lo, nin;
       jrange(ks, j_lo, nin);
       const int lo = ks * kSliceChB;
       if (lane < 4 * QG) mask[lane] = 0u;
-      for (int j = lane; j < 32; j += kWave) list[j] = -1;   // first run step padded
+      if constexpr (!TILED)
+        for (int j = lane; j < 32; j += kWave) list[j] = -1;   // first run step padded
+      wave_lds_sync();
       for (int j = lane; j < nin; j += kWave) {
         const int c = s_idx[j_lo + j] - lo;   // in [0, slice) for sorted indices
         if ((unsigned)c < (unsigned)kSliceChB) {
           __hip_atomic_fetch_or(&mask[c >> 5], 1u << (c & 31), __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_WORKGROUP);
-          list[j] = c;
+          if constexpr (!TILED) list[j] = c;
         }
+      }
+      // tiled: the activations of the slice's share of slab positions, lane
+      // quarter q: positions 8 (C(ks) + q) .. + 7 (past the share: 0)
+      if constexpr (TILED) {
+        const uint32_t c0 = chunk_lo(ks);
+        const uint32_t send = min(8u * chunk_lo(ks + 1), (uint32_t)n_out);
+        uint32_t hv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t j = 8u * (c0 + (uint32_t)q) + (uint32_t)e;
+          const bool ok = j < send;
+          const uint32_t col = ok ? (uint32_t)s_idx[j] : 0u;
+          const uint32_t v = ld16(xrs, ((uint32_t)n16 * (uint32_t)a.K + col) * 2u);
+          hv[e] = ok ? v : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xopre[i] = hv[2 * i] | (hv[2 * i + 1] << 16);
       }
       // outlier activations of the first 32 columns of the run: X[m][lo + c]
       // (XT: read from the slice's rows in LDS when the slice is entered)
-      if constexpr (!XT) {
+      if constexpr (!XT && !TILED) {
         const int4 l0 = *reinterpret_cast<const int4*>(list + 8 * q);
         const int4 l1 = *reinterpret_cast<const int4*>(list + 8 * q + 4);
         const int cl[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
@@ -1221,7 +1287,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
                       ? *reinterpret_cast<const u4v*>(smem + xbase + (uint32_t)n16 * mmb_xt_stride(QG) +
                                                        (uint32_t)(32 * QG * q + 8 * t) * 2u)
                       : (u4v){0u, 0u, 0u, 0u};
-      if constexpr (OUT) {
+      if constexpr (OUT && !TILED) {
         // the run's first 32 outlier activations from the same rows (the
         // slice's column list was written when the previous slice was entered)
         const int32_t* list =
@@ -1417,7 +1483,11 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         }
       }
     }
-    if constexpr (OUT) {
+    if constexpr (OUT && TILED) {   // zero-padded chunks: no alignment, no mask
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          __builtin_bit_cast(h8, (u4v){xo[0], xo[1], xo[2], xo[3]}),
+          __builtin_bit_cast(h8, (u4v){it.od[0], it.od[1], it.od[2], it.od[3]}), c, 0, 0, 0);
+    } else if constexpr (OUT) {
       const uint32_t row = (uint32_t)(((int)blockIdx.x + ri * (int)gridDim.x) * 16 + n16);
       const uint32_t sh = ((row * (uint32_t)n_out + (uint32_t)cur_jlo) & 1u) * 16u;
       // the slab values past the run belong to other positions or rows (or
@@ -1451,8 +1521,9 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     }
   }
 
-  // ---- outlier runs longer than 32 columns, after the weight stream
-  if constexpr (OUT) {
+  // ---- outlier runs longer than 32 columns, after the weight stream (the
+  //      tiled layout splits positions, at most 32 per slice)
+  if constexpr (OUT && !TILED) {
     for (int s = 0; s < ns_w; ++s) {
       const int ks = w + a.nw * s;
       int j_lo, nin;
@@ -1572,22 +1643,35 @@ struct MmbPlan {
   size_t lds;
 };
 
-static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M) {
+static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M,
+                        const wq_variant* v, bool tiled = false) {
   MmbPlan p{};
-  if (K % 128 != 0 || K > 65536 || n_out > 1024 || M < 2 || M > 16) return p;
+  if (K % (tiled ? 32 : 128) != 0 || K > 65536 || n_out > 1024 || M < 2 || M > 16) return p;
   const int64_t row_bytes = fmt == 2 ? K / 4 : K / 2;
-  if (N * row_bytes > 0xFFFFFFF0ll || N * (K / 32) * 2 > 0xFFFFFFF0ll ||
-      N * n_out * 2 > 0xFFFFFFF0ll || M * K * 2 > 0xFFFFFFF0ll)
+  if (tiled) {
+    const wq::TiledGeometry g = wq::tiled_geometry(fmt, N, K, n_out);
+    if (g.meta_off > kMaxArrayBytes || g.slab_off - g.meta_off > kMaxArrayBytes ||
+        g.total - g.slab_off > kMaxArrayBytes || M * K * 2 > 0xFFFFFFF0ll)
+      return p;
+    // every slice's share of the slab fits the four lane quarters
+    if (g.nch > 4 * g.nks) return p;
+  } else if (N * row_bytes > 0xFFFFFFF0ll || N * (K / 32) * 2 > 0xFFFFFFF0ll ||
+             N * n_out * 2 > 0xFFFFFFF0ll || M * K * 2 > 0xFFFFFFF0ll) {
     return p;
+  }
   // 512-channel slices (QG = 4) halve the items and slice changes of layers up
   // to K = 8192 without outliers (measured faster there up to M = 8); longer
   // rows, the outlier variants (whose registers would spill at QG = 4) and
   // more rows keep 256, whose activation rows load whole (measured at M = 16
-  // on 14336 x 4096: 14.6 us against 15.8).  WQ_MMB_QG=2|4 overrides the
-  // choice for the variants without outliers.
+  // on 14336 x 4096: 14.6 us against 15.8).  An explicit variant may choose
+  // either for the kernels without outliers.
   p.qg = n_out == 0 && K <= 8192 && M <= 8 ? 4 : 2;
-  if (const char* e = getenv("WQ_MMB_QG"))
-    if (n_out == 0) p.qg = atoi(e) == 4 ? 4 : 2;
+  if (tiled) {
+    p.qg = 4;
+  } else if (n_out == 0) {
+    const int qg = variant_or(v, &wq_variant::batch_slice_groups, p.qg);
+    if (qg == 2 || qg == 4) p.qg = qg;
+  }
   const int slice_ch = 128 * p.qg;
   p.nks = (int)((K + slice_ch - 1) / slice_ch);
   if (p.nks <= kMaxWaves) {
@@ -1608,13 +1692,16 @@ static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M)
   p.grid = std::min(p.nrb, cus);
   p.rbl = (p.nrb + p.grid - 1) / p.grid;
   p.iv = n_out == 0 ? 0 : n_out <= 256 ? 1 : n_out <= 512 ? 2 : 4;
-  p.lds = mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv).total;
+  p.lds = mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv, false, tiled).total;
   if (p.lds > kMaxLdsBytes) return p;
-  // 256-channel slices load the activation rows whole and transpose them in
-  // LDS where it fits (WQ_MMB_XT=0|1 overrides, for tests and measurements)
-  const size_t lds_xt = mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv, true).total;
-  p.xt = lds_xt <= kMaxLdsBytes;
-  if (const char* e = getenv("WQ_MMB_XT")) p.xt = lds_xt <= kMaxLdsBytes && atoi(e) != 0;
+  // The activation rows are loaded whole and transposed in LDS where it fits
+  // (an explicit variant may turn it off).  (Measured on MI355X: taking fewer
+  // waves per workgroup so that the transpose fits is slower than loading the
+  // rows in the fragment layout at 8 waves.)
+  const bool want_xt = variant_or(v, &wq_variant::batch_row_transpose, 1) != 0;
+  const size_t lds_xt =
+      mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv, true, tiled).total;
+  p.xt = lds_xt <= kMaxLdsBytes && want_xt;
   if (p.xt) p.lds = lds_xt;
   p.depth = 2;
   p.ok = true;
@@ -1715,34 +1802,47 @@ int wqd_mma_rows(int fmt, bool tiled, const uint8_t* codes, const uint16_t* scal
 int wqd_gemv_refine_mma(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
                         const int32_t* out_idx, int64_t n_out, const uint16_t* x, uint16_t* y,
                         const uint8_t* rcodes, const uint16_t* rscales, const uint16_t* rzeros,
-                        int64_t chunk, int64_t k, int32_t* sel_out, hipStream_t stream,
-                        const char* who, bool* launched) {
+                        int64_t chunk, int64_t k, int32_t* sel_out, const wq_variant* v,
+                        hipStream_t stream, const char* who, bool* launched) {
   *launched = false;
   MmaPlan p = plan_mma1(fmt, true, N, K, n_out, 1);
   if (!p.ok || chunk < 1 || k < 1) return WQ_OK;
   const int rk = (int)std::min(k, chunk);
   const int rnch = (int)((K + chunk - 1) / chunk);
-  // helper waves: up to the workgroup size, at most one per chunk
-  int nh = std::min(rnch, kRefMaxThreads / kWave - p.nw);
-  if (nh < 1) return WQ_OK;
-  // 16 waves where the kernel fits them and the extra helpers take a chunk
-  // off every helper's share
-  bool wide = false;
-  if (fmt != 2 && n_out == 0) {
-    const char* e = getenv("WQ_REFINE_WIDE");
-    const int nhw = std::min(rnch, kRefWideThreads / kWave - p.nw);
-    if (!(e != nullptr && e[0] == '0') && (rnch + nhw - 1) / nhw < (rnch + nh - 1) / nh) {
-      nh = nhw;
-      wide = true;
-    }
-  }
-  const int rc = (rnch + nh - 1) / nh;
   const int rp = (rk + 31) / 32;
   const int rh = (p.rbl + 1) / 2;
-  if ((int64_t)rc * rp * rh > kRefUnits) return WQ_OK;   // registers: at most 4 units per lane
-  const MmaLds L = mma_lds_layout(fmt, p.nw, p.nsw, p.rbl, 1, rnch, rk, nh);
-  if (L.total > kMaxLdsBytes) return WQ_OK;
-  p.lds = L.total;
+  // Helper waves, at most one per chunk: a 12-wave workgroup, or 16 waves for
+  // the W4 / W4P kernels without outliers (they fit 128 VGPRs) where the extra
+  // helpers take a chunk off every helper's share.  The wider plan is tried
+  // first; if its units or LDS do not fit, the 12-wave plan is tried.
+  const int nh12 = std::min(rnch, kRefMaxThreads / kWave - p.nw);
+  int cand_nh[2] = {0, 0};
+  bool cand_wide[2] = {false, false};
+  int ncand = 0;
+  if (fmt != 2 && n_out == 0 && variant_or(v, &wq_variant::refine_wide, 1) != 0) {
+    const int nhw = std::min(rnch, kRefWideThreads / kWave - p.nw);
+    if (nhw >= 1 && (nh12 < 1 || (rnch + nhw - 1) / nhw < (rnch + nh12 - 1) / nh12)) {
+      cand_nh[ncand] = nhw;
+      cand_wide[ncand++] = true;
+    }
+  }
+  if (nh12 >= 1) {
+    cand_nh[ncand] = nh12;
+    cand_wide[ncand++] = false;
+  }
+  int nh = 0, rc = 0;
+  bool wide = false;
+  for (int c = 0; c < ncand && nh == 0; ++c) {
+    const int rcc = (rnch + cand_nh[c] - 1) / cand_nh[c];
+    if ((int64_t)rcc * rp * rh > kRefUnits) continue;   // registers: at most 4 units per lane
+    const MmaLds Lc = mma_lds_layout(fmt, p.nw, p.nsw, p.rbl, 1, rnch, rk, cand_nh[c]);
+    if (Lc.total > kMaxLdsBytes) continue;
+    nh = cand_nh[c];
+    rc = rcc;
+    wide = cand_wide[c];
+    p.lds = Lc.total;
+  }
+  if (nh == 0) return WQ_OK;
   MmaArgs a = mma_args(p, fmt, true, tiled, nullptr, nullptr, N, K, out_idx, nullptr, n_out, x,
                        1, y);
   a.rcodes = rcodes;
@@ -1791,11 +1891,11 @@ int wqd_gemv_refine_mma(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
 
 int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
                  int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
-                 int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y, hipStream_t stream,
-                 const char* who, int mode, bool* launched) {
+                 int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y, const wq_variant* v,
+                 hipStream_t stream, const char* who, int mode, bool* launched) {
   *launched = false;
   if (mode == 0) return WQ_OK;
-  const MmbPlan p = plan_mmb(fmt, N, K, n_out, M);
+  const MmbPlan p = plan_mmb(fmt, N, K, n_out, M, v);
   if (!p.ok) return WQ_OK;
   MmbArgs a{};
   a.codes = codes;
@@ -1830,5 +1930,48 @@ int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
   WQ_MMB_LAUNCH(5, 0) WQ_MMB_LAUNCH(5, 1) WQ_MMB_LAUNCH(5, 2) WQ_MMB_LAUNCH(5, 4)
 #undef WQ_MMB_LAUNCH_X
 #undef WQ_MMB_LAUNCH
+  return WQ_OK;
+}
+
+int wqd_gemm_mma_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
+                       const int32_t* out_idx, int64_t n_out, const uint16_t* X, int64_t M,
+                       uint16_t* Y, const wq_variant* v, hipStream_t stream, const char* who,
+                       bool* launched) {
+  *launched = false;
+  const MmbPlan p = plan_mmb(fmt, N, K, n_out, M, v, true);
+  if (!p.ok) return WQ_OK;
+  const wq::TiledGeometry g = wq::tiled_geometry(fmt, N, K, n_out);
+  MmbArgs a{};
+  a.codes = tiled + g.codes_off;
+  a.scales = reinterpret_cast<const uint16_t*>(tiled + g.meta_off);
+  a.zeros = a.scales;
+  a.out_w = reinterpret_cast<const uint16_t*>(tiled + g.slab_off);
+  a.out_idx = out_idx;
+  a.X = X;
+  a.Y = Y;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.M = (int)M;
+  a.n_out = (int)n_out;
+  a.nw = p.nw;
+  a.nks = p.nks;
+  a.nrb = p.nrb;
+  a.rbl = p.rbl;
+  a.nch = (int)g.nch;
+  const dim3 grid(p.grid), block(p.nw * kWave);
+#define WQ_MMT_LAUNCH_X(F_, IV_, X_)                                                          \
+  if (fmt == F_ && p.iv == IV_ && p.xt == X_) {                                               \
+    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, 4, X_, true>), p.lds)) \
+      return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds);  \
+    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, 4, X_, true>), grid, block, p.lds, stream, a);  \
+    *launched = true;                                                                         \
+    return check_launch(who);                                                                 \
+  }
+#define WQ_MMT_LAUNCH(F_, IV_) WQ_MMT_LAUNCH_X(F_, IV_, false) WQ_MMT_LAUNCH_X(F_, IV_, true)
+  WQ_MMT_LAUNCH(4, 0) WQ_MMT_LAUNCH(4, 1) WQ_MMT_LAUNCH(4, 2) WQ_MMT_LAUNCH(4, 4)
+  WQ_MMT_LAUNCH(2, 0) WQ_MMT_LAUNCH(2, 1) WQ_MMT_LAUNCH(2, 2) WQ_MMT_LAUNCH(2, 4)
+  WQ_MMT_LAUNCH(5, 0) WQ_MMT_LAUNCH(5, 1) WQ_MMT_LAUNCH(5, 2) WQ_MMT_LAUNCH(5, 4)
+#undef WQ_MMT_LAUNCH_X
+#undef WQ_MMT_LAUNCH
   return WQ_OK;
 }

@@ -214,16 +214,15 @@ __global__ void __launch_bounds__(kRefineThreads) topk_refine_kernel(RefineArgs 
 // Groups per workgroup: enough workgroups to spread the loads, few enough that
 // the fused kernel's per-workgroup selection is not repeated far beyond one
 // workgroup per compute unit.
-static int refine_gpw(int Gn, bool fused) {
+// An explicit variant may choose 1, 2 or 4 groups per workgroup instead.
+static int refine_gpw(int Gn, bool fused, const wq_variant* v) {
   int gpw = 1;
   if (fused) {
     const int cus = device_cus() > 0 ? device_cus() : 256;
     while (gpw < 4 && (Gn + gpw - 1) / gpw > cus) gpw *= 2;
   }
-  if (const char* e = getenv("WQ_REFINE_GPW")) {
-    const int v = atoi(e);
-    if (v == 1 || v == 2 || v == 4) gpw = v;
-  }
+  const int e = variant_or(v, &wq_variant::refine_groups, gpw);
+  if (e == 1 || e == 2 || e == 4) gpw = e;
   return gpw;
 }
 
@@ -256,9 +255,10 @@ extern "C" int wq_topk_chunks(const uint16_t* x, int64_t K, int64_t chunk, int64
   return check_launch(who);
 }
 
-extern "C" int wq_refine_add(const uint8_t* rcodes, const uint16_t* rscales,
-                             const uint16_t* rzeros, int64_t N, int64_t K, const int32_t* sel,
-                             int64_t n_sel, const uint16_t* x, uint16_t* y, void* stream) {
+extern "C" int wq_refine_add_v(const uint8_t* rcodes, const uint16_t* rscales,
+                               const uint16_t* rzeros, int64_t N, int64_t K, const int32_t* sel,
+                               int64_t n_sel, const uint16_t* x, uint16_t* y,
+                               const wq_variant* variant, void* stream) {
   const char* who = "wq_refine_add";
   if (int r = wq::check_shape(N, K, who)) return r;
   if (N % 32) return wq::fail(WQ_ERR_UNSUPPORTED, "%s: N must be a multiple of 32", who);
@@ -278,7 +278,7 @@ extern "C" int wq_refine_add(const uint8_t* rcodes, const uint16_t* rscales,
   a.N = (int)N;
   a.K = (int)K;
   a.n_sel = (int)n_sel;
-  const int Gn = (int)(N / kGroup), gpw = refine_gpw(Gn, false);
+  const int Gn = (int)(N / kGroup), gpw = refine_gpw(Gn, false, variant);
   const dim3 grid((unsigned)((Gn + gpw - 1) / gpw)), block(kRefineThreads);
   if (gpw == 1)
     hipLaunchKernelGGL(refine_kernel<1>, grid, block, 0, (hipStream_t)stream, a);
@@ -289,10 +289,10 @@ extern "C" int wq_refine_add(const uint8_t* rcodes, const uint16_t* rscales,
   return check_launch(who);
 }
 
-extern "C" int wq_refine_topk(const uint8_t* rcodes, const uint16_t* rscales,
-                              const uint16_t* rzeros, int64_t N, int64_t K, int64_t chunk,
-                              int64_t k, const uint16_t* x, uint16_t* y, int32_t* sel_out,
-                              void* stream) {
+extern "C" int wq_refine_topk_v(const uint8_t* rcodes, const uint16_t* rscales,
+                                const uint16_t* rzeros, int64_t N, int64_t K, int64_t chunk,
+                                int64_t k, const uint16_t* x, uint16_t* y, int32_t* sel_out,
+                                const wq_variant* variant, void* stream) {
   const char* who = "wq_refine_topk";
   if (int r = wq::check_shape(N, K, who)) return r;
   if (N % 32) return wq::fail(WQ_ERR_UNSUPPORTED, "%s: N must be a multiple of 32", who);
@@ -314,7 +314,7 @@ extern "C" int wq_refine_topk(const uint8_t* rcodes, const uint16_t* rscales,
   const int64_t nch = (K + chunk - 1) / chunk;
   if (sel_out != nullptr && (nch > kRefineThreads / kWave || n_sel > kFusedMaxSel)) {
     if (int r = wq_topk_chunks(x, K, chunk, k, sel_out, stream)) return r;
-    return wq_refine_add(rcodes, rscales, rzeros, N, K, sel_out, n_sel, x, y, stream);
+    return wq_refine_add_v(rcodes, rscales, rzeros, N, K, sel_out, n_sel, x, y, variant, stream);
   }
   if (n_sel > kFusedMaxSel)
     return wq::fail(WQ_ERR_UNSUPPORTED, "%s: %lld selected channels exceed %d without sel_out "
@@ -332,7 +332,7 @@ extern "C" int wq_refine_topk(const uint8_t* rcodes, const uint16_t* rscales,
   a.n_sel = (int)n_sel;
   a.chunk = (int)chunk;
   a.k = (int)kk;
-  const int Gn = (int)(N / kGroup), gpw = refine_gpw(Gn, true);
+  const int Gn = (int)(N / kGroup), gpw = refine_gpw(Gn, true, variant);
   const dim3 grid((unsigned)((Gn + gpw - 1) / gpw)), block(kRefineThreads);
   if (gpw == 1)
     hipLaunchKernelGGL(topk_refine_kernel<1>, grid, block, 0, (hipStream_t)stream, a);
@@ -341,4 +341,17 @@ extern "C" int wq_refine_topk(const uint8_t* rcodes, const uint16_t* rscales,
   else
     hipLaunchKernelGGL(topk_refine_kernel<4>, grid, block, 0, (hipStream_t)stream, a);
   return check_launch(who);
+}
+
+extern "C" int wq_refine_add(const uint8_t* rcodes, const uint16_t* rscales,
+                             const uint16_t* rzeros, int64_t N, int64_t K, const int32_t* sel,
+                             int64_t n_sel, const uint16_t* x, uint16_t* y, void* stream) {
+  return wq_refine_add_v(rcodes, rscales, rzeros, N, K, sel, n_sel, x, y, nullptr, stream);
+}
+
+extern "C" int wq_refine_topk(const uint8_t* rcodes, const uint16_t* rscales,
+                              const uint16_t* rzeros, int64_t N, int64_t K, int64_t chunk,
+                              int64_t k, const uint16_t* x, uint16_t* y, int32_t* sel_out,
+                              void* stream) {
+  return wq_refine_topk_v(rcodes, rscales, rzeros, N, K, chunk, k, x, y, sel_out, nullptr, stream);
 }

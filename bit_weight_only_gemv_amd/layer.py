@@ -123,27 +123,27 @@ class DeviceLayer:
         b += 2 * self.N * self.n_out + 4 * self.n_out
         return b + 2 * M * self.K + 2 * M * self.N
 
-    def gemv(self, x, y, flags=L.WQ_FUSE_OUTLIERS, stream=None):
+    def gemv(self, x, y, flags=L.WQ_FUSE_OUTLIERS, stream=None, variant=None):
         fn = {L.WQ_FMT_W4: L.wq_gemv_w4, L.WQ_FMT_W2: L.wq_gemv_w2,
               L.WQ_FMT_W4P: L.wq_gemv_w4p}[self.fmt]
         fn(self.codes, self.scales, self.zeros, self.N, self.K, x, y, self.idx, self.wout,
-           self.n_out, flags, stream)
+           self.n_out, flags, stream, variant)
 
     def gemv_tiled(self, x, y, stream=None):
         if self.tiled is None:
             raise ValueError("layer built without tiled=True")
         L.wq_gemv_tiled(self.fmt, self.tiled, self.N, self.K, x, y, self.idx, self.n_out, stream)
 
-    def gemm_tiled(self, X, Y, stream=None):
-        """Y [M][N] from X [M][K] on the tiled layout, M = 1 .. 4 (W2: 1 or 2)."""
+    def gemm_tiled(self, X, Y, stream=None, variant=None):
+        """Y [M][N] from X [M][K] on the tiled layout, M = 1 .. 16."""
         if self.tiled is None:
             raise ValueError("layer built without tiled=True")
         L.wq_gemm_tiled(self.fmt, self.tiled, self.N, self.K, X, X.shape[0], Y, self.idx,
-                        self.n_out, stream)
+                        self.n_out, stream, variant)
 
-    def gemm(self, X, Y, flags=L.WQ_FUSE_OUTLIERS, stream=None):
+    def gemm(self, X, Y, flags=L.WQ_FUSE_OUTLIERS, stream=None, variant=None):
         L.wq_gemm_wq(self.fmt, self.codes, self.scales, self.zeros, self.N, self.K, X, X.shape[0],
-                     Y, self.idx, self.wout, self.n_out, flags, stream)
+                     Y, self.idx, self.wout, self.n_out, flags, stream, variant)
 
     def outlier_add(self, X, Y, stream=None):
         L.wq_outlier_add(self.idx, self.wout, self.n_out, self.N, X, X.shape[0], self.K, Y, stream)
@@ -163,24 +163,24 @@ class DeviceLayer:
         self.r_scales = up(ref.scales.view(np.int16), np.int16)
         self.r_zeros = up(ref.zeros.view(np.int16), np.int16)
 
-    def refine(self, x, y, sel, n_sel, stream=None):
+    def refine(self, x, y, sel, n_sel, stream=None, variant=None):
         """y += sum over the selected channels of x_i C[:, i] (StrataFlux Eq. 2)."""
         L.wq_refine_add(self.r_codes, self.r_scales, self.r_zeros, self.N, self.K, sel, n_sel,
-                        x, y, stream)
+                        x, y, stream, variant)
 
-    def refine_topk(self, x, y, k, chunk=1024, sel_out=None, stream=None):
+    def refine_topk(self, x, y, k, chunk=1024, sel_out=None, stream=None, variant=None):
         """Selection and add of StrataFlux Eq. 2 in one launch."""
         L.wq_refine_topk(self.r_codes, self.r_scales, self.r_zeros, self.N, self.K, chunk, k, x, y,
-                         sel_out, stream)
+                         sel_out, stream, variant)
 
-    def gemv_tiled_refine(self, x, y, k, chunk=1024, sel_out=None, stream=None):
+    def gemv_tiled_refine(self, x, y, k, chunk=1024, sel_out=None, stream=None, variant=None):
         """The tiled product with the selection and add of StrataFlux Eq. 2 in
         the same launch (one FP16 rounding)."""
         if self.tiled is None:
             raise ValueError("layer built without tiled=True")
         L.wq_gemv_tiled_refine(self.fmt, self.tiled, self.N, self.K, x, y, self.r_codes,
                                self.r_scales, self.r_zeros, chunk, k, self.idx, self.n_out, sel_out,
-                               stream)
+                               stream, variant)
 
     def dequant(self, W_hat, stream=None):
         L.wq_dequant_device(self.fmt, self.codes, self.scales, self.zeros, self.N, self.K, W_hat,

@@ -309,15 +309,18 @@ int wq_tile_host(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
 int wq_gemv_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K, const int32_t* out_idx,
                   int64_t n_out, const uint16_t* x, uint16_t* y, void* stream);
 
-/* The tiled layer against M = 1 to 4 activation rows (W2: 1 or 2): Y [M][N] =
- * X [M][K] times the layer (outlier pass fused), the batched product of SPECTRA
- * section 4.2 at its smallest M.  The rows share the matrix-core kernel's 16
- * group slots (each 512-channel slice taken in M windows of 16 / M groups; 3
- * rows run as 4), so the codes are decoded once for all rows.  M = 1 is
- * wq_gemv_tiled.  Same shape limits as wq_gemv_tiled, and with more rows more
- * LDS per slice (at 3 or 4 rows also at most 4 slices per wave, K <= 16384);
- * shapes outside them return WQ_ERR_UNSUPPORTED (wq_gemm_wq on the row-major
- * arrays takes every M up to 16). */
+/* The tiled layer against M = 1 to WQ_GEMM_MAX_M activation rows: Y [M][N] =
+ * X [M][K] times the layer (outlier pass fused), the batched product of
+ * SPECTRA section 4.2 (M a runtime argument).  Up to 4 rows (W2: 2) share the
+ * matrix-core kernel's 16 group slots (each 512-channel slice taken in M
+ * windows of 16 / M groups; 3 rows run as 4), so the codes are decoded once
+ * for all rows; past that, or where the slot kernel does not fit, the batched
+ * kernel reads the same tiles (each wave load four contiguous 256-byte runs),
+ * dequantizes them to FP16 and multiplies them with the M rows on the matrix
+ * cores.  M = 1 is wq_gemv_tiled.  Limits: those of wq_gemv_tiled, and for
+ * M > 1 on the batched kernel at most 1024 outlier columns and its partial
+ * sums within the LDS; other shapes return WQ_ERR_UNSUPPORTED (wq_gemm_wq on
+ * the row-major arrays takes every M up to 16). */
 int wq_gemm_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K, const int32_t* out_idx,
                   int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y, void* stream);
 
@@ -335,14 +338,72 @@ int wq_gemm_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K, const int
  * and one row block per lane, i.e. large k, many chunks per wave or many row
  * blocks per workgroup; or LDS), the call runs wq_gemv_tiled and then
  * wq_refine_topk: the same selection, and y within the same bound, but with
- * the product rounded to FP16 before the add.  The environment variable
- * WQ_REFINE_FUSE=0 forces that path (for comparisons).  Limits: those of
+ * the product rounded to FP16 before the add.  Limits: those of
  * wq_gemv_tiled, plus N % 32 == 0, chunk a multiple of 64 in [64, 1024], and
  * rcodes, x, y 16-byte aligned; k == 0 is wq_gemv_tiled alone. */
 int wq_gemv_tiled_refine(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
                          const int32_t* out_idx, int64_t n_out, const uint16_t* x, uint16_t* y,
                          const uint8_t* rcodes, const uint16_t* rscales, const uint16_t* rzeros,
                          int64_t chunk, int64_t k, int32_t* sel_out, void* stream);
+
+/* ------------------------------------------------ kernel-variant selection
+ * Not part of the method: for tests and measurements that run a call on each
+ * of the kernels the library could choose for it.  Each *_v entry point is
+ * the entry point of the same name without the suffix, with an explicit
+ * choice of kernel; NULL (or a field < 0) keeps the library's own choice,
+ * which is what the plain entry points use.  Every variant meets the same
+ * result contract (bit-identical results where the plain entry point's
+ * comment says so, else within the same bound).  Nothing is remembered
+ * between calls. */
+typedef struct wq_variant {
+  /* M = 1 GEMV on the row-major arrays: 0 the VALU kernels, 1 the library's
+   * rule, 2 the matrix-core kernel wherever it takes the shape */
+  int32_t gemv_kernel;
+  /* VALU GEMV: rows per wave step (1..4), and 0 / 1 to keep x in registers /
+   * stage it in LDS (where the LDS fits) */
+  int32_t gemv_rows_per_wave;
+  int32_t gemv_lds_x;
+  /* wq_gemm_wq at 2 <= M: 0 the per-group tile kernel only, 1 the rule, 2 the
+   * persistent matrix-core kernels wherever they take the shape; gemm_rows 0
+   * skips the shared-slot kernel of M <= 4 (wq_gemm_wq and wq_gemm_tiled) */
+  int32_t gemm_kernel;
+  int32_t gemm_rows;
+  /* persistent batched kernel: groups per lane quarter of a slice (2 or 4;
+   * layers without outliers), and 0 / 1 to load the activation rows in the
+   * lane layout / whole through an LDS transpose (where the LDS fits) */
+  int32_t batch_slice_groups;
+  int32_t batch_row_transpose;
+  /* refinement add: 1, 2 or 4 groups of 32 output rows per workgroup */
+  int32_t refine_groups;
+  /* wq_gemv_tiled_refine: 0 runs the product and then wq_refine_topk (two
+   * launches); refine_wide 0 keeps the one-launch kernel at 12 waves where
+   * the library would take 16 */
+  int32_t refine_fuse;
+  int32_t refine_wide;
+} wq_variant;
+
+int wq_gemv_v(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+              int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w, int64_t n_out,
+              uint32_t flags, const uint16_t* x, uint16_t* y, const wq_variant* variant,
+              void* stream);
+int wq_gemm_wq_v(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                 int64_t N, int64_t K, const int32_t* out_idx, const uint16_t* out_w,
+                 int64_t n_out, uint32_t flags, const uint16_t* X, int64_t M, uint16_t* Y,
+                 const wq_variant* variant, void* stream);
+int wq_gemm_tiled_v(int fmt, const uint8_t* tiled, int64_t N, int64_t K, const int32_t* out_idx,
+                    int64_t n_out, const uint16_t* X, int64_t M, uint16_t* Y,
+                    const wq_variant* variant, void* stream);
+int wq_refine_add_v(const uint8_t* rcodes, const uint16_t* rscales, const uint16_t* rzeros,
+                    int64_t N, int64_t K, const int32_t* sel, int64_t n_sel, const uint16_t* x,
+                    uint16_t* y, const wq_variant* variant, void* stream);
+int wq_refine_topk_v(const uint8_t* rcodes, const uint16_t* rscales, const uint16_t* rzeros,
+                     int64_t N, int64_t K, int64_t chunk, int64_t k, const uint16_t* x,
+                     uint16_t* y, int32_t* sel_out, const wq_variant* variant, void* stream);
+int wq_gemv_tiled_refine_v(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
+                           const int32_t* out_idx, int64_t n_out, const uint16_t* x, uint16_t* y,
+                           const uint8_t* rcodes, const uint16_t* rscales, const uint16_t* rzeros,
+                           int64_t chunk, int64_t k, int32_t* sel_out, const wq_variant* variant,
+                           void* stream);
 
 /* -------------------------------------------------- measurement support
  * Not part of the method: kernels of known traffic that calibrate bandwidth
@@ -352,6 +413,15 @@ int wq_gemv_tiled_refine(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
  * workgroup to `sink` (sink must hold wq_read_probe_sink_words(bytes) words). */
 int wq_read_probe(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 int64_t wq_read_probe_sink_words(int64_t bytes);
+
+/* The same streaming read with a chosen launch geometry, for finding the
+ * attainable rate at a given size: `blocks` workgroups of `threads` threads
+ * (a multiple of 64, at most 1024); wave v reads its own run of
+ * ceil(bytes / 1 KB / waves) consecutive 1 KB blocks (one 16-byte load per
+ * lane each) through a ring of `ring` loads in flight per lane (1, 2, 4, 8 or
+ * 16).  sink holds `blocks` uint32 words.  bytes < 4 GB. */
+int wq_read_probe_geom(const void* src, int64_t bytes, uint32_t* sink, int blocks, int threads,
+                       int ring, void* stream);
 
 /* Copies `bytes` (multiple of 16) from src to dst with 16-byte vector loads
  * and stores. */

@@ -64,10 +64,10 @@ def check_product(ref, y, x, label):
     return worst
 
 
-def run_gemv(dl, x, flags=B.WQ_FUSE_OUTLIERS):
+def run_gemv(dl, x, flags=B.WQ_FUSE_OUTLIERS, variant=None):
     xd = dev_fp16(x.reshape(-1))
     y = torch.full((dl.N,), -1, dtype=torch.int16, device="cuda")
-    dl.gemv(xd, y, flags)
+    dl.gemv(xd, y, flags, variant=variant)
     torch.cuda.synchronize()
     return y, xd
 
@@ -94,13 +94,21 @@ SHAPES = [(1, 32), (7, 96), (129, 4096), (300, 14336), (77, 28672), (64, 8192), 
           (1000, 1024), (17, 65536), (5000, 4224)]
 
 
+class Path(str):
+    """A named kernel choice: the variant passed with each call."""
+
+    def __new__(cls, name, variant):
+        o = super().__new__(cls, name)
+        o.variant = variant
+        return o
+
+
 @pytest.fixture(params=["valu", "mfma"])
-def gemv_path(request, monkeypatch):
+def gemv_path(request):
     """Runs a GEMV test on the VALU kernels and again with the matrix-core
-    kernel forced wherever it supports the shape (K % 128 == 0 and its LDS
+    kernel chosen wherever it supports the shape (K % 128 == 0 and its LDS
     fits); the library otherwise picks it only for large N."""
-    monkeypatch.setenv("WQ_GEMV_MMA", "0" if request.param == "valu" else "2")
-    return request.param
+    return Path(request.param, B.variant(gemv_kernel=0 if request.param == "valu" else 2))
 
 
 @pytest.mark.parametrize("fmt", [4, 2, 5])
@@ -110,7 +118,7 @@ def test_gemv_small(fmt, N, K, outl, gemv_path):
     say(f"gemv fmt={fmt} N={N} K={K} outliers={outl} path={gemv_path}")
     L = synthetic.small_layer(fmt, N, K, with_outliers=outl, seed=N % 17)
     ref, dl = build(fmt, L.W, L.profile, L.ratio)
-    y, _ = run_gemv(dl, L.x)
+    y, _ = run_gemv(dl, L.x, variant=gemv_path.variant)
     check_product(ref, y, L.x, f"w{fmt} {N}x{K} n_out={ref.n_out}")
 
 
@@ -123,7 +131,7 @@ def test_gemv_outlier_counts(fmt, n_out, gemv_path):
                               ratio=(n_out + 0.5) / K)
     ref, dl = build(fmt, L.W, L.profile, L.ratio)
     assert ref.n_out == n_out
-    y, _ = run_gemv(dl, L.x)
+    y, _ = run_gemv(dl, L.x, variant=gemv_path.variant)
     check_product(ref, y, L.x, f"w{fmt} n_out={n_out}")
 
 
@@ -164,7 +172,7 @@ def run_gemv_tiled(dl, x):
 @pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("N,K", TILED_SHAPES)
 @pytest.mark.parametrize("outl", [False, True])
-def test_gemv_tiled(fmt, N, K, outl, monkeypatch):
+def test_gemv_tiled(fmt, N, K, outl):
     say(f"gemv tiled fmt={fmt} N={N} K={K} outliers={outl}")
     L = synthetic.small_layer(fmt, N, K, with_outliers=outl, seed=N % 17)
     ref, dl = build_tiled(fmt, L.W, L.profile, L.ratio)
@@ -173,30 +181,34 @@ def test_gemv_tiled(fmt, N, K, outl, monkeypatch):
     if K % 128 == 0:
         # the row-major matrix-core kernel performs the same operations in the
         # same order on the same values: identical bits
-        monkeypatch.setenv("WQ_GEMV_MMA", "2")
-        y2, _ = run_gemv(dl, L.x)
+        y2, _ = run_gemv(dl, L.x, variant=B.variant(gemv_kernel=2))
         assert torch.equal(y, y2)
 
 
 @pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("N,K", TILED_SHAPES)
 @pytest.mark.parametrize("outl", [False, True])
-@pytest.mark.parametrize("M", [2, 3, 4])
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 8, 13, 16])
 def test_gemm_tiled_rows(fmt, N, K, outl, M):
-    """Up to four activation rows sharing the tiled kernel's group slots: every
-    row within the bound; M = 1 through the same entry equals the tiled GEMV."""
+    """Up to 16 activation rows on the tiled layer: every row within the
+    bound, on the kernel the library picks (the shared-slot kernel up to 4
+    rows where it fits, else the batched kernel on the same tiles) and, up to
+    4 rows, on the batched kernel too; M = 1 through the same entry equals the
+    tiled GEMV."""
     say(f"gemm tiled M={M} fmt={fmt} N={N} K={K} outliers={outl}")
     L = synthetic.small_layer(fmt, N, K, M=M, with_outliers=outl, seed=N % 13 + M)
     ref, dl = build_tiled(fmt, L.W, L.profile, L.ratio)
     X = dev_fp16(L.x)
-    Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
-    try:
-        dl.gemm_tiled(X, Y)
-    except B.WQError as e:   # W2 above two rows; more rows' LDS at the longest rows
-        assert e.status == -2 and ((fmt == 2 and M > 2) or K >= 16384), (e.status, fmt, M, K)
-        return
-    torch.cuda.synchronize()
-    check_product(ref, Y, L.x, f"tiled M={M} w{fmt} {N}x{K} n_out={ref.n_out}")
+    paths = [("default", None)] + ([("batched", B.variant(gemm_rows=0))] if M <= 4 else [])
+    for name, var in paths:
+        Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
+        try:
+            dl.gemm_tiled(X, Y, variant=var)
+        except B.WQError as e:   # the batched kernel takes at most 1024 outlier columns
+            assert e.status == -2 and ref.n_out > 1024, (e.status, fmt, M, K, ref.n_out)
+            continue
+        torch.cuda.synchronize()
+        check_product(ref, Y, L.x, f"tiled M={M} w{fmt} {N}x{K} n_out={ref.n_out} {name}")
     if M == 2:
         Y1 = torch.full((1, N), -1, dtype=torch.int16, device="cuda")
         dl.gemm_tiled(dev_fp16(L.x[:1]), Y1)
@@ -207,18 +219,17 @@ def test_gemm_tiled_rows(fmt, N, K, outl, M):
 @pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("N,K,outl", [(129, 4096, True), (5000, 4224, True), (300, 14336, False)])
 @pytest.mark.parametrize("M", [2, 3, 4])
-def test_gemm_rows_paths(fmt, N, K, outl, M, monkeypatch):
+def test_gemm_rows_paths(fmt, N, K, outl, M):
     """M = 2..4 on the row-major arrays: the shared-slot matrix-core kernel (the
-    default where it applies) and the batched kernel (WQ_GEMM_ROWS=0) both
+    default where it applies) and the batched kernel (gemm_rows 0) both
     within the bound."""
     L = synthetic.small_layer(fmt, N, K, M=M, with_outliers=outl, seed=K % 11 + M)
     ref, dl = build(fmt, L.W, L.profile, L.ratio)
     X = dev_fp16(L.x)
-    for rows in ("1", "0"):
-        monkeypatch.setenv("WQ_GEMM_ROWS", rows)
+    for rows in (1, 0):
         say(f"gemm M={M} fmt={fmt} {N}x{K} shared-slot kernel={rows}")
         Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
-        dl.gemm(X, Y)
+        dl.gemm(X, Y, variant=B.variant(gemm_rows=rows))
         torch.cuda.synchronize()
         check_product(ref, Y, L.x, f"M={M} w{fmt} {N}x{K} rows={rows}")
 
@@ -255,8 +266,8 @@ def test_gemv_tiled_unsupported_shapes():
 def test_gemv_deterministic(gemv_path):
     L = synthetic.small_layer(2, 1500, 4096, with_outliers=True, seed=9)
     ref, dl = build(2, L.W, L.profile, L.ratio)
-    y1, _ = run_gemv(dl, L.x)
-    y2, _ = run_gemv(dl, L.x)
+    y1, _ = run_gemv(dl, L.x, variant=gemv_path.variant)
+    y2, _ = run_gemv(dl, L.x, variant=gemv_path.variant)
     assert torch.equal(y1, y2)
 
 
@@ -281,12 +292,11 @@ def test_outlier_add_standalone():
 
 
 @pytest.fixture(params=["tile", "mfma"])
-def gemm_path(request, monkeypatch):
+def gemm_path(request):
     """Runs a batched test on the per-group tile kernel and on the persistent
     matrix-core kernel (the library's choice wherever the latter supports the
     shape: K % 128 == 0, fused outliers, its LDS fits)."""
-    monkeypatch.setenv("WQ_GEMM_MMA", "0" if request.param == "tile" else "1")
-    return request.param
+    return Path(request.param, B.variant(gemm_kernel=0 if request.param == "tile" else 1))
 
 
 @pytest.mark.parametrize("fmt", [4, 2, 5])
@@ -299,7 +309,7 @@ def test_gemm_small(fmt, M, N, K, outl, gemm_path):
     ref, dl = build(fmt, L.W, L.profile, L.ratio)
     X = dev_fp16(L.x)
     Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
-    dl.gemm(X, Y)
+    dl.gemm(X, Y, variant=gemm_path.variant)
     torch.cuda.synchronize()
     check_product(ref, Y, L.x, f"gemm w{fmt} M={M} {N}x{K} n_out={ref.n_out}")
 
@@ -308,18 +318,16 @@ def test_gemm_small(fmt, M, N, K, outl, gemm_path):
 @pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("M", [2, 5, 16])
 @pytest.mark.parametrize("N,K", [(129, 4096), (300, 8192), (5000, 4224), (64, 2176), (48, 384)])
-def test_gemm_slice_widths(fmt, M, N, K, qg, monkeypatch):
+def test_gemm_slice_widths(fmt, M, N, K, qg):
     """The matrix-core batched kernel with 256- and 512-channel slices (no
     outliers), including a short last slice (K % 512 = 128) and K below one
     slice."""
-    monkeypatch.setenv("WQ_GEMM_MMA", "1")
-    monkeypatch.setenv("WQ_MMB_QG", qg)
     say(f"gemm slices of {128 * int(qg)} fmt={fmt} M={M} N={N} K={K}")
     L = synthetic.small_layer(fmt, N, K, M=M, seed=M + N)
     ref, dl = build(fmt, L.W)
     X = dev_fp16(L.x)
     Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
-    dl.gemm(X, Y)
+    dl.gemm(X, Y, variant=B.variant(gemm_kernel=1, batch_slice_groups=int(qg)))
     torch.cuda.synchronize()
     check_product(ref, Y, L.x, f"gemm w{fmt} M={M} {N}x{K} slices {128 * int(qg)}")
 
@@ -329,24 +337,21 @@ def test_gemm_slice_widths(fmt, M, N, K, qg, monkeypatch):
 @pytest.mark.parametrize("M", [2, 5, 8, 16])
 @pytest.mark.parametrize("N,K,outl", [(129, 4096, True), (300, 8320, False), (64, 2176, True),
                                       (1000, 10240, False), (96, 384, False)])
-def test_gemm_row_transpose(fmt, M, N, K, outl, qg, monkeypatch):
+def test_gemm_row_transpose(fmt, M, N, K, outl, qg):
     """The batched kernel with its activation rows loaded whole and transposed
-    in LDS (WQ_MMB_XT=1, where the LDS fits) or loaded in the lane layout
-    directly (WQ_MMB_XT=0): the same fragments, so bit-identical Y, within the
+    in LDS (batch_row_transpose 1, where the LDS fits) or loaded in the lane
+    layout directly (0): the same fragments, so bit-identical Y, within the
     bound; 256- and 512-channel slices (outlier layers always take 256), short
     last slices and rows past M included."""
-    monkeypatch.setenv("WQ_GEMM_MMA", "2")
-    monkeypatch.setenv("WQ_GEMM_ROWS", "0")
-    monkeypatch.setenv("WQ_MMB_QG", qg)
     say(f"gemm row transpose fmt={fmt} M={M} N={N} K={K} outliers={outl} slices={128 * int(qg)}")
     L = synthetic.small_layer(fmt, N, K, M=M, with_outliers=outl, seed=M + N + 1)
     ref, dl = build(fmt, L.W, L.profile, L.ratio) if outl else build(fmt, L.W)
     X = dev_fp16(L.x)
     ys = []
-    for xt in ("1", "0"):
-        monkeypatch.setenv("WQ_MMB_XT", xt)
+    for xt in (1, 0):
         Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
-        dl.gemm(X, Y)
+        dl.gemm(X, Y, variant=B.variant(gemm_kernel=2, gemm_rows=0, batch_slice_groups=int(qg),
+                                        batch_row_transpose=xt))
         torch.cuda.synchronize()
         ys.append(Y.cpu().numpy())
     assert np.array_equal(ys[0], ys[1])
@@ -611,10 +616,10 @@ TILED_REFINE_CASES = [
 
 
 @pytest.mark.parametrize("fmt,N,K,chunk,k,outl,fused", TILED_REFINE_CASES)
-def test_gemv_tiled_refine(fmt, N, K, chunk, k, outl, fused, monkeypatch):
+def test_gemv_tiled_refine(fmt, N, K, chunk, k, outl, fused):
     """The tiled product with the refinement in the same launch: S(x) equal to the
     oracle's, y within the bound of the refined product, and the same
-    selection and bound on the two-launch path (WQ_REFINE_FUSE=0), which must be
+    selection and bound on the two-launch path (refine_fuse 0), which must be
     bit-identical to wq_gemv_tiled followed by wq_refine_topk.  Where the fused
     kernel runs, y is rounded once and differs from the two-launch y."""
     from bit_weight_only_gemv_amd.layer import refinement_host
@@ -632,14 +637,13 @@ def test_gemv_tiled_refine(fmt, N, K, chunk, k, outl, fused, monkeypatch):
     y0, a0 = O.matvec_ref(ref.w_hat(), x, ref.idx, ref.wout)
     terms = x.astype(np.float64)[S][:, None] * c_hat.astype(np.float64)[S]
     outs = {}
-    # W4 / W4P layers without outliers also run their 12-wave kernel (WQ_REFINE_WIDE=0)
+    # W4 / W4P layers without outliers also run their 12-wave kernel (refine_wide 0)
     modes = ("1", "1w0", "0") if fmt != 2 and not outl else ("1", "0")
     for mode in modes:
-        monkeypatch.setenv("WQ_REFINE_FUSE", mode[0])
-        monkeypatch.setenv("WQ_REFINE_WIDE", "0" if mode == "1w0" else "1")
+        var = B.variant(refine_fuse=int(mode[0]), refine_wide=0 if mode == "1w0" else 1)
         y = torch.full((N,), -1, dtype=torch.int16, device="cuda")
         sel = torch.full((n,), -7, dtype=torch.int32, device="cuda")
-        dl.gemv_tiled_refine(xd, y, k, chunk, sel)
+        dl.gemv_tiled_refine(xd, y, k, chunk, sel, variant=var)
         torch.cuda.synchronize()
         assert np.array_equal(sel.cpu().numpy(), S)
         ok, worst = O.check_tolerance(host_fp16(y).astype(np.float64), y0[0] + terms.sum(0),
@@ -707,7 +711,7 @@ def test_gemv_tiled_refine_zero_chunk(fmt):
 
 @pytest.mark.parametrize("gpw", ["1", "2", "4"])
 @pytest.mark.parametrize("N,K", [(96, 2048), (14336 // 4, 4096), (4096, 14336 // 2)])
-def test_refine_groups_per_workgroup(gpw, N, K, monkeypatch):
+def test_refine_groups_per_workgroup(gpw, N, K):
     """Workgroups of 1, 2 or 4 row groups (a ragged last workgroup included) sum
     every group in the same order: the fused and two-call paths stay
     bit-identical to each other and to the one-group default."""
@@ -724,10 +728,10 @@ def test_refine_groups_per_workgroup(gpw, N, K, monkeypatch):
     B.wq_topk_chunks(xd, K, 1024, 32, sel)
     ya = y0.clone()
     dl.refine(xd, ya, sel, n)                  # default grouping
-    monkeypatch.setenv("WQ_REFINE_GPW", gpw)
+    var = B.variant(refine_groups=int(gpw))
     yb, yc = y0.clone(), y0.clone()
-    dl.refine(xd, yb, sel, n)
-    dl.refine_topk(xd, yc, 32)
+    dl.refine(xd, yb, sel, n, variant=var)
+    dl.refine_topk(xd, yc, 32, variant=var)
     torch.cuda.synchronize()
     assert np.array_equal(ya.cpu().numpy(), yb.cpu().numpy())
     assert np.array_equal(ya.cpu().numpy(), yc.cpu().numpy())
@@ -762,7 +766,7 @@ def _special_layer(fmt, N, K, seed):
 
 @pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("N,K", [(48, 1024), (160, 4096)])
-def test_special_values_and_boundary_outliers(fmt, N, K, monkeypatch):
+def test_special_values_and_boundary_outliers(fmt, N, K):
     say(f"special values fmt={fmt} N={N} K={K}")
     W, x, profile, ratio, cols = _special_layer(fmt, N, K, seed=N + K)
     ref = O.quantize_layer(fmt, W, profile, ratio)
@@ -776,16 +780,14 @@ def test_special_values_and_boundary_outliers(fmt, N, K, monkeypatch):
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(np.uint16),
                           np.asarray(ref.w_hat(), np.float16).view(np.uint16))
-    for mode in ("0", "2"):
-        monkeypatch.setenv("WQ_GEMV_MMA", mode)
-        y, _ = run_gemv(dl, x)
+    for mode in (0, 2):
+        y, _ = run_gemv(dl, x, variant=B.variant(gemv_kernel=mode))
         check_product(ref, y, x, f"special w{fmt} gemv mode {mode}")
     check_product(ref, run_gemv_tiled(dl, x), x, f"special w{fmt} tiled")
     X = np.stack([x, -x, x[::-1].copy()])
-    for mode in ("0", "1"):
-        monkeypatch.setenv("WQ_GEMM_MMA", mode)
+    for mode in (0, 1):
         Y = torch.full((3, N), -1, dtype=torch.int16, device="cuda")
-        dl.gemm(dev_fp16(X), Y)
+        dl.gemm(dev_fp16(X), Y, variant=B.variant(gemm_kernel=mode))
         torch.cuda.synchronize()
         check_product(ref, Y, X, f"special w{fmt} gemm M=3 mode {mode}")
 
@@ -794,14 +796,12 @@ def test_special_values_and_boundary_outliers(fmt, N, K, monkeypatch):
 @pytest.mark.parametrize("lds_path", ["0", "1"])
 @pytest.mark.parametrize("rpw", ["1", "2", "4"])
 @pytest.mark.parametrize("N,K,outl", [(129, 4096, True), (37, 14336, False), (300, 2080, True)])
-def test_gemv_valu_launch_variants(fmt, lds_path, rpw, N, K, outl, monkeypatch):
+def test_gemv_valu_launch_variants(fmt, lds_path, rpw, N, K, outl):
     """The VALU M = 1 kernels with x staged in LDS or kept in registers, and
     1, 2 or 4 rows per wave step."""
-    monkeypatch.setenv("WQ_GEMV_MMA", "0")
-    monkeypatch.setenv("WQ_GEMV_LDS_PATH", lds_path)
-    monkeypatch.setenv("WQ_GEMV_ROWS_PER_WAVE", rpw)
+    var = B.variant(gemv_kernel=0, gemv_lds_x=int(lds_path), gemv_rows_per_wave=int(rpw))
     say(f"gemv VALU fmt={fmt} lds={lds_path} rows/wave={rpw} N={N} K={K} outliers={outl}")
     L = synthetic.small_layer(fmt, N, K, with_outliers=outl, seed=N + int(rpw))
     ref, dl = build(fmt, L.W, L.profile, L.ratio)
-    y, _ = run_gemv(dl, L.x)
+    y, _ = run_gemv(dl, L.x, variant=var)
     check_product(ref, y, L.x, f"valu w{fmt} lds={lds_path} rpw={rpw} {N}x{K}")

@@ -77,3 +77,70 @@ def test_refine_ref_exact_rationals():
                                              for i in sel)
         assert abs(Fraction(y[n]) - exact) <= Fraction(1, 10**12) * (1 + abs(exact))
         assert a[n] >= abs(float(exact)) * (1 - 1e-12)
+
+
+def _hand_layer():
+    """A 32 x 64 layer whose residual the W4 grid holds exactly: with w_hat = 0
+    the residual is W itself, W[n, c] = ((n + c) mod 16) / 8.  Each refinement
+    group (32 output rows of one input channel) then spans 0 .. 15/8, so
+    s = (15/8) / 15 = 1/8 exactly, z = 0 and q = (n + c) mod 16: the dequantized
+    refinement equals W^T bit for bit."""
+    n = np.arange(32)[:, None]
+    c = np.arange(64)[None, :]
+    W = (((n + c) % 16) / 8.0).astype(np.float32)
+    return W, np.zeros((32, 64), np.float16)
+
+
+def _refined_rows(fn, W, w_hat, idx):
+    q, s, z = fn(W, w_hat, idx)
+    return O.dequant_w4(q, s, z).astype(np.float64)
+
+
+def _idx_branch_holds(fn):
+    """StrataFlux section 3.2.1 with the resident layer's outlier columns Omega
+    (held exactly in FP16): their residual is 0.  Omega lies below N = 32, so
+    that applying it to the output rows instead is a valid (wrong) index.  Per input channel c of R^T:
+    c in Omega -> the dequantized refinement row is exactly 0; every other
+    channel's row equals the one computed without Omega (refinement groups run
+    along N inside one channel, so zeroing one channel cannot move another)."""
+    W, w_hat = _hand_layer()
+    idx = np.array([3, 17, 29], np.int32)
+    with_idx = _refined_rows(fn, W, w_hat, idx)
+    without = _refined_rows(fn, W, w_hat, None)
+    others = np.setdiff1d(np.arange(64), idx)
+    return (with_idx.shape == (64, 32)
+            and np.all(with_idx[idx] == 0.0)
+            and np.array_equal(with_idx[others], without[others])
+            and np.array_equal(without, W.T.astype(np.float64)))
+
+
+def test_refinement_outlier_columns_hand_worked():
+    W, w_hat = _hand_layer()
+    idx = np.array([3, 17, 29], np.int32)
+    c_hat = _refined_rows(O.refinement_w4, W, w_hat, idx)
+    expect = W.T.astype(np.float64).copy()
+    expect[idx] = 0.0
+    assert np.array_equal(c_hat, expect)
+    # the zeroed channels encode as an all-zero group: codes 0, zero point 0,
+    # and the 1e-8 scale floor, which FP16 rounds to 0
+    q, s, z = O.refinement_w4(W, w_hat, idx)
+    assert np.all(q[idx] == 0) and np.all(z[idx] == 0) and np.all(s[idx] == 0)
+    assert _idx_branch_holds(O.refinement_w4)
+
+
+def test_refinement_outlier_branch_catches_rows_for_columns():
+    # a planted mistake in the oracle's branch: the outlier set applied to the
+    # output rows of R (R[idx, :]) instead of its input channels
+    def rows_instead(W, w_hat, idx=None):
+        R = np.asarray(W, np.float32) - np.asarray(w_hat, np.float16).astype(np.float32)
+        if idx is not None and len(idx):
+            R[np.asarray(idx, np.int64), :] = 0.0
+        q, sc, ze, _ = O.quantize_w4(np.ascontiguousarray(R.T))
+        return q, sc, ze
+
+    # and one that forgets the branch altogether
+    def no_branch(W, w_hat, idx=None):
+        return O.refinement_w4(W, w_hat, None)
+
+    assert not _idx_branch_holds(rows_instead)
+    assert not _idx_branch_holds(no_branch)
