@@ -14,7 +14,7 @@ from ._lib import (  # noqa: F401
     WQ_GEMM_MAX_M, SIGNATURES, VARIANT_FIELDS, Variant, variant,
     wq_quantize_w4, wq_quantize_w2, wq_pack_zeros_w4, wq_select_outliers,
     wq_select_outliers_kurtosis, wq_split_outliers,
-    wq_dequant_host, wq_dequant_device, wq_gemv_w4, wq_gemv_w2, wq_gemv_w4p, wq_gemm_wq,
+    wq_dequant_host, wq_refinement_w4, wq_dequant_device, wq_gemv_w4, wq_gemv_w2, wq_gemv_w4p, wq_gemm_wq,
     wq_outlier_add, wq_embed_gather, wq_topk_count, wq_topk_chunks, wq_refine_add,
     wq_refine_topk,
     wq_tiled_bytes, wq_tile_host, wq_gemv_tiled, wq_gemm_tiled, wq_gemv_tiled_refine,

@@ -51,6 +51,7 @@ SIGNATURES = {
                                            _P, _P]),
     "wq_split_outliers": (_INT, [_P, _I64, _I64, _P, _I64, _P, _P]),
     "wq_dequant_host": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P]),
+    "wq_refinement_w4": (_INT, [_INT, _P, _P, _P, _P, _I64, _I64, _P, _I64, _P, _P, _P]),
     "wq_dequant_device": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _P]),
     "wq_gemv_w4": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _P, _P]),
     "wq_gemv_w2": (_INT, [_P, _P, _P, _I64, _I64, _P, _P, _I64, _U32, _P, _P, _P]),
@@ -239,6 +240,24 @@ def wq_dequant_host(fmt: int, codes, scales, zeros, N: int, K: int) -> np.ndarra
     out = np.empty((N, K), np.uint16)
     _check(load().wq_dequant_host(fmt, _np_ptr(codes), _np_ptr(sc), _np_ptr(ze), N, K, _np_ptr(out)))
     return out.view(np.float16)
+
+
+def wq_refinement_w4(fmt: int, W: np.ndarray, codes, scales, zeros, idx=None):
+    """Refinement columns of a packed layer (W float32 [N, K] before the outlier
+    split) -> (rcodes uint8 [K, N/2], rscales fp16 [K, N/32], rzeros fp16 [K, N/32])."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    codes = _c(codes, np.uint8)
+    sc = _c(np.asarray(scales).view(np.uint16), np.uint16)
+    ze = _zeros_arg(fmt, zeros)
+    idx = _c(idx if idx is not None else np.zeros(0, np.int32), np.int32)
+    rc = np.empty((K, N // 2), np.uint8)
+    rs = np.empty((K, N // WQ_GROUP), np.uint16)
+    rz = np.empty((K, N // WQ_GROUP), np.uint16)
+    _check(load().wq_refinement_w4(fmt, _np_ptr(W), _np_ptr(codes), _np_ptr(sc), _np_ptr(ze), N, K,
+                                   _np_ptr(idx) if len(idx) else None, len(idx), _np_ptr(rc),
+                                   _np_ptr(rs), _np_ptr(rz)))
+    return rc, rs.view(np.float16), rz.view(np.float16)
 
 
 def wq_tiled_bytes(fmt: int, N: int, K: int, n_out: int) -> int:

@@ -163,6 +163,39 @@ const char* wq_last_error(void) { return g_last_error.c_str(); }
 
 const char* wq_version(void) { return "wq 0.1 gfx950"; }
 
+}  // extern "C"
+
+namespace {
+
+// One W4 group of 32 float32 weights (SPECTRA section 3.4, Appendix A): the 16
+// code bytes (in-group nibble interleave), the FP16 scale and the FP16 zero.
+void quantize_w4_group(const float* w, uint8_t* c, uint16_t* scale, uint16_t* zero) {
+  float wmin = w[0], wmax = w[0];
+  for (int k = 1; k < WQ_GROUP; ++k) {
+    wmin = std::min(wmin, w[k]);
+    wmax = std::max(wmax, w[k]);
+  }
+  float s = (wmax - wmin) / 15.0f;
+  if (!(s > 1e-8f)) s = 1e-8f;
+  float z = round_half_even(-wmin / s);
+  z = std::min(std::max(z, 0.0f), 15.0f);
+  uint8_t q[WQ_GROUP];
+  for (int k = 0; k < WQ_GROUP; ++k) {
+    float t = w[k] / s;
+    t = t + z;
+    t = round_half_even(t);
+    t = std::min(std::max(t, 0.0f), 15.0f);
+    q[k] = (uint8_t)t;
+  }
+  for (int k = 0; k < 16; ++k) c[k] = (uint8_t)((q[k] & 0x0F) | ((q[k + 16] & 0x0F) << 4));
+  *scale = f32_to_f16(s);
+  *zero = f32_to_f16(z);
+}
+
+}  // namespace
+
+extern "C" {
+
 int wq_quantize_w4(const float* W, int64_t N, int64_t K, int32_t group, uint8_t* codes,
                    uint16_t* scales, uint16_t* zeros) {
   if (group != WQ_GROUP) return fail(WQ_ERR_UNSUPPORTED, "wq_quantize_w4: group must be 32");
@@ -170,32 +203,10 @@ int wq_quantize_w4(const float* W, int64_t N, int64_t K, int32_t group, uint8_t*
   if (!W || !codes || !scales || !zeros)
     return fail(WQ_ERR_INVALID_ARG, "wq_quantize_w4: NULL pointer");
   const int64_t G = K / WQ_GROUP;
-  for (int64_t n = 0; n < N; ++n) {
-    for (int64_t g = 0; g < G; ++g) {
-      const float* w = W + n * K + g * WQ_GROUP;
-      float wmin = w[0], wmax = w[0];
-      for (int k = 1; k < WQ_GROUP; ++k) {
-        wmin = std::min(wmin, w[k]);
-        wmax = std::max(wmax, w[k]);
-      }
-      float s = (wmax - wmin) / 15.0f;
-      if (!(s > 1e-8f)) s = 1e-8f;
-      float z = round_half_even(-wmin / s);
-      z = std::min(std::max(z, 0.0f), 15.0f);
-      uint8_t q[WQ_GROUP];
-      for (int k = 0; k < WQ_GROUP; ++k) {
-        float t = w[k] / s;
-        t = t + z;
-        t = round_half_even(t);
-        t = std::min(std::max(t, 0.0f), 15.0f);
-        q[k] = (uint8_t)t;
-      }
-      uint8_t* c = codes + n * (K / 2) + g * 16;
-      for (int k = 0; k < 16; ++k) c[k] = (uint8_t)((q[k] & 0x0F) | ((q[k + 16] & 0x0F) << 4));
-      scales[n * G + g] = f32_to_f16(s);
-      zeros[n * G + g] = f32_to_f16(z);
-    }
-  }
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t g = 0; g < G; ++g)
+      quantize_w4_group(W + n * K + g * WQ_GROUP, codes + n * (K / 2) + g * 16,
+                        scales + n * G + g, zeros + n * G + g);
   return wq::ok();
 }
 
@@ -499,6 +510,51 @@ int wq_tile_host(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
         }
       }
     }
+  }
+  return wq::ok();
+}
+
+int wq_refinement_w4(int fmt, const float* W, const uint8_t* codes, const uint16_t* scales,
+                     const uint16_t* zeros, int64_t N, int64_t K, const int32_t* out_idx,
+                     int64_t n_out, uint8_t* rcodes, uint16_t* rscales, uint16_t* rzeros) {
+  const char* who = "wq_refinement_w4";
+  if (fmt != WQ_FMT_W4 && fmt != WQ_FMT_W2 && fmt != WQ_FMT_W4P)
+    return fail(WQ_ERR_INVALID_ARG, "%s: fmt must be WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2", who);
+  if (int r = wq::check_shape(N, K, who)) return r;
+  if (N % WQ_GROUP != 0 || N > WQ_MAX_K)
+    return fail(WQ_ERR_UNSUPPORTED, "%s: N must be a multiple of 32 up to %d", who, WQ_MAX_K);
+  if (n_out < 0 || n_out > K)
+    return fail(WQ_ERR_INVALID_ARG, "%s: n_out must be in [0, K] (got %lld)", who,
+                (long long)n_out);
+  if (!W || !codes || !scales || !zeros || !rcodes || !rscales || !rzeros ||
+      (n_out > 0 && !out_idx))
+    return fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  for (int64_t j = 0; j < n_out; ++j)
+    if (out_idx[j] < 0 || out_idx[j] >= K || (j > 0 && out_idx[j] <= out_idx[j - 1]))
+      return fail(WQ_ERR_INVALID_ARG, "%s: out_idx must be strictly increasing in [0, K)", who);
+  const int64_t G = K / WQ_GROUP, Gn = N / WQ_GROUP;
+  const int64_t row_bytes = fmt == WQ_FMT_W2 ? K / 4 : K / 2;
+  const int64_t zrow = fmt == WQ_FMT_W4P ? (G + 1) / 2 : 2 * G;   // bytes of zero points per row
+  std::vector<uint8_t> outlier(K, 0);
+  for (int64_t j = 0; j < n_out; ++j) outlier[out_idx[j]] = 1;
+  // 32 output rows at a time: their dequantized weights, then R^T of the block
+  // ([K][32]: one refinement group per input channel), quantized group by group
+  std::vector<uint16_t> what((size_t)WQ_GROUP * K);
+  std::vector<float> rt((size_t)K * WQ_GROUP);
+  for (int64_t gn = 0; gn < Gn; ++gn) {
+    const int64_t n0 = gn * WQ_GROUP;
+    const uint16_t* zrows =
+        reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(zeros) + n0 * zrow);
+    if (int r = wq_dequant_host(fmt, codes + n0 * row_bytes, scales + n0 * G, zrows, WQ_GROUP, K,
+                                what.data()))
+      return r;
+    for (int64_t r = 0; r < WQ_GROUP; ++r)
+      for (int64_t k = 0; k < K; ++k)
+        rt[k * WQ_GROUP + r] =
+            outlier[k] ? 0.0f : W[(n0 + r) * K + k] - f16_to_f32(what[r * K + k]);
+    for (int64_t k = 0; k < K; ++k)
+      quantize_w4_group(&rt[k * WQ_GROUP], rcodes + k * (N / 2) + gn * 16, rscales + k * Gn + gn,
+                        rzeros + k * Gn + gn);
   }
   return wq::ok();
 }

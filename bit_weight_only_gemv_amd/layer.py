@@ -74,16 +74,13 @@ class HostRefinement:
 
 
 def refinement_host(W: np.ndarray, host: "HostLayer") -> HostRefinement:
-    """The residual of the packed layer, R = W_dense - w_hat (outlier columns 0:
-    they are exact already), transposed and packed with the library's W4
-    encoder (StrataFlux section 3.2.1, DecDEC's 4-bit residual encoding)."""
+    """The refinement columns of the packed layer (StrataFlux section 3.2.1):
+    the library's host encoder forms the residual of the resident layer, zeroes
+    the outlier columns and W4-encodes it transposed (wq_refinement_w4)."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     N, K = W.shape
-    w_hat = L.wq_dequant_host(host.fmt, host.codes, host.scales, host.zeros, N, K)
-    R = W - w_hat.astype(np.float32)
-    if host.n_out:
-        R[:, host.idx] = 0.0
-    codes, sc, ze = L.wq_quantize_w4(np.ascontiguousarray(R.T))
+    codes, sc, ze = L.wq_refinement_w4(host.fmt, W, host.codes, host.scales, host.zeros,
+                                       host.idx if host.n_out else None)
     return HostRefinement(N, K, codes, sc, ze)
 
 

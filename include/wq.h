@@ -158,6 +158,24 @@ int wq_split_outliers(const float* W, int64_t N, int64_t K, const int32_t* idx,
 int wq_dequant_host(int fmt, const uint8_t* codes, const uint16_t* scales,
                     const uint16_t* zeros, int64_t N, int64_t K, uint16_t* W_hat);
 
+/* Refinement columns of a packed layer (StrataFlux page, section 3.2.1: the
+ * weight residual, stored as 4-bit integers with their own scale factors):
+ *   R = W - w_hat  in float32 (w_hat the FP16 dequantized layer, as
+ *       wq_dequant_host makes it), with R[:, c] = 0 for every outlier column c
+ *       in out_idx (the resident layer holds those exactly in FP16);
+ *   R^T [K][N] quantized in the W4 format along N (wq_quantize_w4 of R^T:
+ *       groups of 32 output rows): rcodes [K][N/2], rscales, rzeros [K][N/32].
+ * W is the float32 layer [N][K] before the outlier split; codes / scales /
+ * zeros its packed form in fmt (WQ_FMT_W4, WQ_FMT_W4P or WQ_FMT_W2); out_idx
+ * int32 [n_out] strictly increasing in [0, K) (NULL when n_out == 0).  These
+ * are the columns wq_refine_add, wq_refine_topk and wq_gemv_tiled_refine add.
+ * Works on 32 output rows at a time (host memory of about 200 K bytes).
+ * Errors: WQ_ERR_UNSUPPORTED unless N % 32 == 0 and N <= 65536;
+ * WQ_ERR_INVALID_ARG for NULL pointers, bad shapes or indices. */
+int wq_refinement_w4(int fmt, const float* W, const uint8_t* codes, const uint16_t* scales,
+                     const uint16_t* zeros, int64_t N, int64_t K, const int32_t* out_idx,
+                     int64_t n_out, uint8_t* rcodes, uint16_t* rscales, uint16_t* rzeros);
+
 /* ------------------------------------------------------------- device (HIP)
  * All device pointers; `stream` is a hipStream_t (NULL = null stream).
  */

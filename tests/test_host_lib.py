@@ -265,3 +265,44 @@ def test_kurtosis_policy_errors():
                                            0.01, idx.ctypes.data_as(ctypes.c_void_p), 4,
                                            ctypes.byref(n), None, None) == -1
     assert p is not None
+
+
+# ------------------------------------------------ refinement columns (C ABI)
+
+
+@pytest.mark.parametrize("fmt", [4, 5, 2])
+@pytest.mark.parametrize("N,K,outl", [(32, 64, False), (96, 1088, True), (256, 4096, True),
+                                      (64, 2080, False)])
+def test_refinement_columns_match_oracle(fmt, N, K, outl):
+    """wq_refinement_w4 (StrataFlux section 3.2.1): the residual of the packed
+    layer with the outlier columns zeroed, W4-encoded transposed, byte for byte
+    the oracle's refinement_w4."""
+    from bit_weight_only_gemv_amd.layer import pack_host, refinement_host
+    L = synthetic.small_layer(fmt, N, K, with_outliers=outl, seed=N + K)
+    hl = pack_host(fmt, L.W, L.profile, L.ratio)
+    ref = O.quantize_layer(fmt, L.W, L.profile, L.ratio)
+    assert (ref.n_out > 0) == outl
+    rq, rs, rz = O.refinement_w4(L.W, ref.w_hat(), ref.idx if outl else None)
+    rf = refinement_host(L.W, hl)
+    assert np.array_equal(rf.codes, O.pack_w4(rq))
+    assert np.array_equal(_bits(rf.scales), _bits(rs))
+    assert np.array_equal(_bits(rf.zeros), _bits(rz))
+    if outl:   # the outlier channels' refinement rows decode to exactly 0
+        c_hat = O.dequant_w4(O.unpack_w4(rf.codes), rf.scales, rf.zeros)
+        assert np.all(c_hat[hl.idx] == 0)
+
+
+def test_refinement_columns_errors():
+    W = np.zeros((48, 64), np.float32)
+    codes, sc, ze = B.wq_quantize_w4(W)
+    with pytest.raises(B.WQError) as e:            # N not a multiple of 32
+        B.wq_refinement_w4(4, W, codes, sc, ze)
+    assert e.value.status == B._lib.WQ_ERR_UNSUPPORTED
+    W = np.zeros((32, 64), np.float32)
+    codes, sc, ze = B.wq_quantize_w4(W)
+    for bad in ([5, 5], [70], [-1], [9, 3]):       # not strictly increasing in [0, K)
+        with pytest.raises(B.WQError) as e:
+            B.wq_refinement_w4(4, W, codes, sc, ze, np.array(bad, np.int32))
+        assert e.value.status == B._lib.WQ_ERR_INVALID_ARG
+    with pytest.raises(B.WQError):
+        B.wq_refinement_w4(3, W, codes, sc, ze)
