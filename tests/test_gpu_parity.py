@@ -387,12 +387,16 @@ def test_full_w2_14336x4096_outliers_m1():
 def test_full_w4_batched(N, K, M):
     say(f"full W4 batched {N}x{K} M={M}")
     L = synthetic.config4(M, N, K)
-    ref, dl = build(4, L.W)
+    ref = O.quantize_layer(4, L.W)
+    dl = DeviceLayer(pack_host(4, L.W), tiled=True)
     X = dev_fp16(L.x)
     Y = torch.empty((M, N), dtype=torch.int16, device="cuda")
     dl.gemm(X, Y)
+    Yt = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    dl.gemm_tiled(X, Yt)
     torch.cuda.synchronize()
     check_product(ref, Y, L.x, f"W4 {N}x{K} M={M}")
+    check_product(ref, Yt, L.x, f"W4 {N}x{K} M={M} tiled")
     # M repeated GEMVs agree with the oracle too
     for m in range(M):
         y, _ = run_gemv(dl, L.x[m])

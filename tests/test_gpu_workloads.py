@@ -1,16 +1,17 @@
 """GPU parity at the full sizes of the larger workloads, in the launch
-configuration the benchmark times, on outputs the oracle computes row by row:
+configuration the benchmark times, on every output element:
 
-* 70B-class W2 + outlier layers (28672 x 8192 and 8192 x 28672, M = 1 on both
-  layouts and M = 8):
-  the oracle selects the outlier columns from the whole matrix, then splits,
-  quantizes and multiplies only a sample of rows (the encoding of a row does
-  not depend on other rows once the outlier columns are fixed);
+* 70B-class W2 + outlier layers (28672 x 8192 and 8192 x 28672; M = 1 and
+  M = 8, each on the row-major and the tiled layout): the oracle selects the
+  outlier columns from the whole matrix, then splits, quantizes and multiplies
+  the rows in chunks of 4096 (the encoding of a row does not depend on other
+  rows once the outlier columns are fixed), covering every row;
 * the Llama-3-8B-shaped W4 decode sweep (225 GEMVs) captured in one HIP
   graph: every replay (with eager work in between) equals the eager result
-  bit for bit, and sampled GEMVs match the oracle;
+  bit for bit, and every distinct projection of the first layer and the
+  whole LM head (128256 rows) match the oracle;
 * the stacked projections the fused sweep runs (q|k|v 6144 x 4096, gate|up
-  28672 x 4096), on both layouts, on rows sampled from every part.
+  28672 x 4096), on both layouts, on every row.
 """
 
 import sys
@@ -34,35 +35,38 @@ def say(*a):
     print(*a, flush=True, file=sys.stderr)
 
 
-def oracle_rows(fmt, W, profile, ratio, rows):
-    """The oracle's quantized rows: outlier columns from the whole matrix, then
-    split / quantize / dequantize of the sampled rows only."""
-    if profile is not None:
-        idx = O.select_outliers(W, profile, ratio)
-    else:
-        idx = np.zeros(0, np.int32)
-    dense, wout = O.split_outliers(W[rows], idx)
-    if fmt == 4:
-        q, s, z, _ = O.quantize_w4(dense)
-        w_hat = O.dequant_w4(q, s, z)
-    else:
-        q, s, z = O.quantize_w2(dense)
-        w_hat = O.dequant_w2(q, s, z)
-    return w_hat, idx, wout
+CHUNK = 4096
 
 
-def check_rows(y_gpu, rows, w_hat, x, idx, wout, label):
-    y_ref, a = O.matvec_ref(w_hat, x, idx if len(idx) else None, wout if len(idx) else None)
-    got = y_gpu[:, rows].astype(np.float64)
-    ok, worst = O.check_tolerance(got, y_ref, a)
-    say(f"  {label}: {len(rows)} sampled rows, worst |err|/bound = {worst:.4f}")
-    assert ok, f"{label}: worst {worst}"
+def row_chunks(N, chunk=CHUNK):
+    """Every row, in consecutive chunks of at most `chunk` rows."""
+    return [np.arange(r0, min(N, r0 + chunk), dtype=np.int64) for r0 in range(0, N, chunk)]
 
 
-def sample_rows(N, n=192, seed=0):
-    rng = np.random.default_rng(seed)
-    r = np.unique(np.concatenate([[0, 1, N - 2, N - 1], rng.choice(N, n, replace=False)]))
-    return r.astype(np.int64)
+def check_all_rows(outputs, fmt, W, profile, ratio, X):
+    """Each GPU output (a label and its [M, N] FP16 array) against the oracle on
+    every row, chunk by chunk."""
+    N = W.shape[0]
+    idx = O.select_outliers(W, profile, ratio) if profile is not None else np.zeros(0, np.int32)
+    worst = {label: 0.0 for label, _ in outputs}
+    for rows in row_chunks(N):
+        dense, wout = O.split_outliers(W[rows], idx)
+        if fmt == 4:
+            q, s, z, _ = O.quantize_w4(dense)
+            w_hat = O.dequant_w4(q, s, z)
+        else:
+            q, s, z = O.quantize_w2(dense)
+            w_hat = O.dequant_w2(q, s, z)
+        for label, y in outputs:
+            Xm = X[:y.shape[0]]
+            y_ref, a = O.matvec_ref(w_hat, Xm, idx if len(idx) else None,
+                                    wout if len(idx) else None)
+            ok, wr = O.check_tolerance(y[:, rows].astype(np.float64), y_ref, a)
+            assert ok, f"{label}: rows {rows[0]}..{rows[-1]}: worst |err|/bound = {wr}"
+            worst[label] = max(worst[label], wr)
+    for label, wr in worst.items():
+        say(f"  {label}: all {N} rows, worst |err|/bound = {wr:.4f}")
+    return idx
 
 
 @pytest.mark.parametrize("N,K", [(28672, 8192), (8192, 28672)])
@@ -71,12 +75,6 @@ def test_w2_70b_class_outliers(N, K):
     L = synthetic.config5(N, K, 8)
     dl = DeviceLayer(pack_host(2, L.W, L.profile, L.ratio), tiled=True)
     assert dl.n_out == int(np.floor(0.035 * K))
-    rows = sample_rows(N)
-    w_hat, idx, wout = oracle_rows(2, L.W, L.profile, L.ratio, rows)
-    # spiked channels carry |N(0,1)| x 300 in the profile: all but the ones whose
-    # draw was tiny land among the top 3.5% of scores
-    hit = len(set(L.spikes.tolist()) & set(idx.tolist()))
-    assert hit >= 0.95 * len(L.spikes)
     X = torch.from_numpy(np.ascontiguousarray(L.x).view(np.int16)).cuda()
     y1 = torch.empty(N, dtype=torch.int16, device="cuda")
     dl.gemv(X[0].contiguous(), y1)
@@ -84,15 +82,22 @@ def test_w2_70b_class_outliers(N, K):
     dl.gemv_tiled(X[0].contiguous(), yt)
     Y8 = torch.empty((8, N), dtype=torch.int16, device="cuda")
     dl.gemm(X, Y8)
+    Y8t = torch.empty((8, N), dtype=torch.int16, device="cuda")
+    dl.gemm_tiled(X, Y8t)
     torch.cuda.synchronize()
-    check_rows(y1.cpu().numpy().view(np.float16)[None, :], rows, w_hat, L.x[:1], idx, wout,
-               f"M=1 {N}x{K}")
-    check_rows(yt.cpu().numpy().view(np.float16)[None, :], rows, w_hat, L.x[:1], idx, wout,
-               f"M=1 tiled {N}x{K}")
-    check_rows(Y8.cpu().numpy().view(np.float16), rows, w_hat, L.x, idx, wout, f"M=8 {N}x{K}")
+
+    def h(t):
+        return t.cpu().numpy().view(np.float16).reshape(-1, N)
+    idx = check_all_rows([(f"M=1 {N}x{K}", h(y1)), (f"M=1 tiled {N}x{K}", h(yt)),
+                          (f"M=8 {N}x{K}", h(Y8)), (f"M=8 tiled {N}x{K}", h(Y8t))],
+                         2, L.W, L.profile, L.ratio, L.x)
+    # spiked channels carry |N(0,1)| x 300 in the profile: all but the ones whose
+    # draw was tiny land among the top 3.5% of scores
+    hit = len(set(L.spikes.tolist()) & set(idx.tolist()))
+    assert hit >= 0.95 * len(L.spikes)
 
 
-def test_llama_sweep_graph_replay_and_samples():
+def test_llama_sweep_graph_replay_and_oracle():
     shapes = synthetic.config3_shapes()
     assert len(shapes) == 225
     key = {"q": "sq", "o": "sq", "k": "kv", "v": "kv", "gate": "mlp", "up": "mlp",
@@ -137,14 +142,14 @@ def test_llama_sweep_graph_replay_and_samples():
         for i, (y, e) in enumerate(zip(ys, eager)):
             assert torch.equal(y, e), f"replay {rep}: GEMV {i} differs from the eager run"
     say("  225-GEMV graph: 3 replays equal the eager run")
-    # sampled GEMVs against the oracle
-    for i in (0, 4, 6, 7 * 17 + 1, 224):
+    # every distinct projection of the first layer (q, k, v, o, gate, up, down)
+    # and the LM head against the oracle, on every row
+    for i in list(range(7)) + [224]:
         layer, proj, name, N, K = shapes[i]
-        W = Ws[key[name]]
-        rows = sample_rows(N, 128, seed=i) if N > 20000 else np.arange(N)
-        w_hat, idx, wout = oracle_rows(4, W, None, 0.0, rows)
-        check_rows(eager[i].cpu().numpy().view(np.float16)[None, :], rows, w_hat, xs[i], idx, wout,
-                   f"sweep GEMV {i} ({name} {N}x{K})")
+        W = Ws[key[name]]   # the graph runs each shape class on one prototype layer
+        check_all_rows([(f"sweep GEMV {i} ({name} {N}x{K})",
+                         eager[i].cpu().numpy().view(np.float16)[None, :])],
+                       4, W, None, 0.0, xs[i])
 
 
 @pytest.mark.parametrize("names", [("q", "k", "v"), ("gate", "up")])
@@ -162,12 +167,6 @@ def test_stacked_projections_both_layouts(names):
     dl.gemv(xd, y1)
     dl.gemv_tiled(xd, y2)
     torch.cuda.synchronize()
-    # rows from every stacked part, including each part's first and last row
-    edges = np.cumsum([0] + [w.shape[0] for w in Ws])
-    rows = np.unique(np.concatenate([sample_rows(N, 160, seed=len(names)), edges[1:-1] - 1,
-                                     edges[1:-1]])).astype(np.int64)
-    w_hat, idx, wout = oracle_rows(4, W, None, 0.0, rows)
-    check_rows(y1.cpu().numpy().view(np.float16)[None, :], rows, w_hat, x, idx, wout,
-               f"stacked {N}x{K} row-major")
-    check_rows(y2.cpu().numpy().view(np.float16)[None, :], rows, w_hat, x, idx, wout,
-               f"stacked {N}x{K} tiled")
+    check_all_rows([(f"stacked {N}x{K} row-major", y1.cpu().numpy().view(np.float16)[None, :]),
+                    (f"stacked {N}x{K} tiled", y2.cpu().numpy().view(np.float16)[None, :])],
+                   4, W, None, 0.0, x)

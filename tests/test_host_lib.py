@@ -113,6 +113,55 @@ def test_encoder_matches_oracle_w2_14336x4096_outliers():
     assert ref.n_out == 143 and set(L.spikes.tolist()) <= set(ref.idx.tolist())
 
 
+def _same_layer_chunked(fmt, W, profile=None, ratio=0.0, chunk=4096):
+    """Byte equality of the library's encoding of the whole layer with the
+    oracle's, the oracle taking the rows in chunks (outlier columns chosen from
+    the whole matrix; a row's encoding depends on nothing else)."""
+    from bit_weight_only_gemv_amd.layer import pack_host
+    lib = pack_host(fmt, W, profile, ratio)
+    idx = O.select_outliers(W, profile, ratio) if profile is not None else np.zeros(0, np.int32)
+    assert np.array_equal(lib.idx, idx)
+    for r0 in range(0, W.shape[0], chunk):
+        rows = slice(r0, min(W.shape[0], r0 + chunk))
+        dense, wout = O.split_outliers(W[rows], idx)
+        if fmt == 4:
+            q, sc, ze, _ = O.quantize_w4(dense)
+            codes = O.pack_w4(q)
+        else:
+            q, sc, ze = O.quantize_w2(dense)
+            codes = O.pack_w2(q)
+        assert np.array_equal(lib.codes[rows], codes), f"codes, rows {r0}.."
+        assert np.array_equal(_bits(lib.scales[rows]), _bits(sc)), f"scales, rows {r0}.."
+        assert np.array_equal(_bits(lib.zeros[rows]), _bits(ze)), f"zeros, rows {r0}.."
+        if len(idx):
+            assert np.array_equal(_bits(lib.wout[rows]), _bits(wout)), f"slab, rows {r0}.."
+    return lib
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("N,K", [(14336, 4096), (4096, 14336)])
+def test_encoder_matches_oracle_config4_full(N, K):
+    _same_layer_chunked(4, synthetic.config4(2, N, K).W)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("N,K", [(28672, 8192), (8192, 28672)])
+def test_encoder_matches_oracle_config5_full(N, K):
+    L = synthetic.config5(N, K, 1)
+    lib = _same_layer_chunked(2, L.W, L.profile, L.ratio)
+    assert lib.n_out == int(np.floor(0.035 * K))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["q", "k", "gate", "down", "lm_head"])
+def test_encoder_matches_oracle_config3_shapes(name):
+    """One layer of each distinct shape of the Llama-3-8B-shaped sweep
+    (q and o 4096 x 4096, k and v 1024 x 4096, gate and up 14336 x 4096, down
+    4096 x 14336, the LM head 128256 x 4096)."""
+    layer, proj, nm, N, K = next(s for s in synthetic.config3_shapes() if s[2] == name)
+    _same_layer_chunked(4, synthetic.config3_layer(layer, proj, N, K, nm).W)
+
+
 # ------------------------------------------------------------- error codes
 
 
