@@ -11,22 +11,26 @@ Measurement:
 * weights are rotated through >= 512 MB of distinct device copies so neither
   the 256 MB Infinity Cache nor the L2s serve repeats; inputs sit in HBM
   before the timed region;
-* the timed launches are captured once into a HIP graph (the kernels are
-  launched through the library's C ABI during capture) and replayed; hipEvents
-  on the replay stream bracket exactly --steps launches, with device
-  synchronization on both sides (--eager times Python-side launches instead,
-  which measures the interpreter, not the GPU);
+* exactly --steps launches are timed: captured into HIP graphs (the kernels
+  are launched through the library's C ABI during capture) and replayed, with
+  hipEvents on the replay stream between replays (median and 10th / 90th
+  percentiles over the replays); --eager times Python-side launches instead;
 * value = algorithmic bytes per step (codes + FP16 scales + FP16 zeros + FP16
-  outlier slab + int32 indices + x + y) / time per step.
+  outlier slab + int32 indices + x + y) / median time per step;
+* every line carries `roofline` (achieved rate against MI355X's published
+  peak, plus HBM bytes per launch from rocprofv3 counters where they were taken
+  on the current kernel sources) and `cpu_baseline` (the CPU oracle timed on
+  the host on the same layer, or a stated sample of it).
 
 Other workloads (--workload): w4_4096 (W4 4096x4096), sweep (Llama-3-8B-shaped
 decode in one graph -> tokens/s: 225 separate W4 GEMVs per token, and 129 with
-q|k|v and gate|up stacked along N), batched (W4 small-M
-matrix-core path vs M repeated GEMVs), w2_70b (W2 + outliers at 28672x8192 and
+q|k|v and gate|up stacked along N), batched (W4 small-M products on both
+layouts vs M repeated GEMVs), w2_70b (W2 + outliers at 28672x8192 and
 8192x28672, M = 1 and 8), embed (row gather from a 131072 x 4096 W4 table),
-kurtosis (the kurtosis-adaptive outlier policy on the W2 layers),
-read / copy (plain streaming kernels: the attainable
-HBM rate and the byte-counter calibration).
+kurtosis (the kurtosis-adaptive outlier policy on the W2 layers), refine
+(runtime top-k refinement), read / copy (plain streaming kernels: the
+attainable HBM rate and the byte-counter calibration), probe_sweep (the read
+probe's launch geometries at the layers' sizes).
 """
 
 from __future__ import annotations
@@ -43,11 +47,13 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "M=1 dequant-GEMV effective HBM GB/s (% of MI355X peak); eq. tokens/s"
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 matrix cores, published
 ROTATE_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["wq_gemv.hip", "wq_mma.hip", "wq_mma.h", "wq_common.cuh", "wq_device.h",
                   "wq_select.cuh"]
+DATA = "synthetic (seeded Gaussian weights and activations; no checkpoint)"
 
 
 def _parse():
@@ -79,9 +85,9 @@ def _parse():
 
 
 def kernel_source_hash() -> str:
-    """Hash of the M = 1 kernels' code with comments and layout removed, so
-    that counters stay attached to the code they were taken on and survive
-    edits of comments only."""
+    """Hash of the kernels' code with comments and layout removed, so that
+    counters stay attached to the code they were taken on and survive edits of
+    comments only."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "bit_weight_only_gemv_amd", "csrc", f), encoding="utf-8") as fh:
@@ -107,15 +113,30 @@ def sweep_bytes_per_token(fmt: int, ratio: float) -> int:
     return tot
 
 
+class Timing(float):
+    """Milliseconds per step (the median over replays) with the spread."""
+
+    def __new__(cls, median, p10, p90, mean, steps):
+        o = super().__new__(cls, median)
+        o.p10, o.p90, o.mean, o.steps = p10, p90, mean, steps
+        return o
+
+    def us(self):
+        return {"median": round(self * 1e3, 3), "p10": round(self.p10 * 1e3, 3),
+                "p90": round(self.p90 * 1e3, 3), "mean": round(self.mean * 1e3, 3)}
+
+
 class Timer:
     """Times exactly `steps` calls of fn(i) after `warmup` untimed ones.  The
     steps are captured into a HIP graph of `per` launches (the library is
     called through its C ABI during capture), a whole multiple of `period` (the
     number of rotated buffer copies, so that every replay walks all of them),
     replayed R times with an event on the launching stream between replays; a
-    second graph holds the steps - R per left over.  One synchronization ends
-    the timed region.  Returns a Timing: the time per step (median over the
-    replays, their 10th and 90th percentiles, and the mean over all steps)."""
+    second graph holds the steps - R per left over.  A bounded spin on the
+    stream (about 0.1 ms) comes first, so that the launches are queued on the
+    GPU before the first event fires and the timed region holds the kernels,
+    not the host's latency to submit the first of them.  One synchronization
+    ends the timed region.  Returns a Timing."""
 
     REPLAYS = 20
     LEAD_CYCLES = 250_000
@@ -157,10 +178,6 @@ class Timer:
                 g_rest = self._capture(fn, rest)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
         torch.cuda.synchronize()
-        # a bounded spin on the stream first (about 0.1 ms), so that the
-        # launches below are queued on the GPU before the first event fires:
-        # the timed region then holds the kernels, not the host's latency to
-        # submit the first of them
         torch.cuda._sleep(self.LEAD_CYCLES)
         ev[0].record(stream)
         for r in range(reps):
@@ -182,19 +199,6 @@ class Timer:
         mean = ev[0].elapsed_time(ev[reps + 1]) / steps
         return Timing(float(np.median(t)), float(np.percentile(t, 10)),
                       float(np.percentile(t, 90)), float(mean), steps)
-
-
-class Timing(float):
-    """Milliseconds per step (the median over replays) with the spread."""
-
-    def __new__(cls, median, p10, p90, mean, steps):
-        o = super().__new__(cls, median)
-        o.p10, o.p90, o.mean, o.steps = p10, p90, mean, steps
-        return o
-
-    def us(self):
-        return {"median": round(self * 1e3, 3), "p10": round(self.p10 * 1e3, 3),
-                "p90": round(self.p90 * 1e3, 3), "mean": round(self.mean * 1e3, 3)}
 
 
 def clone_layer(DeviceLayer, base):
@@ -227,21 +231,124 @@ def traffic_for(label):
     return e.get("hbm_bytes_per_launch")
 
 
-def read_probe_rate(torch, timer, nbytes, steps, warmup):
-    """Attainable streaming-read rate at this many bytes per launch: the plain
-    read kernel over rotated buffers, timed like the GEMV (GB/s)."""
+def gbs(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def roofline_hbm(nbytes, ms, traffic=None):
+    g = gbs(nbytes, ms)
+    return {"bound": "hbm", "achieved": round(g, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(g / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+def line(metric, value, unit, a, ms, config, roofline, **extra):
+    """One JSON record in the shape every workload line shares."""
+    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps,
+           "warmup": a.warmup, "ms_per_step": float(ms), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": DATA,
+           "config": config}
+    if isinstance(ms, Timing):
+        out["timing_us"] = ms.us()
+    out["roofline"] = roofline
+    out.update(extra)
+    return out
+
+
+ATTAINABLE_GEOMETRIES = ((0, 256, 1), (0, 256, 2), (0, 256, 4))
+
+
+def attainable_read(torch, timer, nbytes, steps, warmup):
+    """The attainable streaming-read rate at this many bytes per launch: the
+    one-shot grid-stride read kernel at the geometries that measured fastest
+    at the layers' sizes (256-thread workgroups, 1, 2 or 4 loads in flight per
+    lane), over rotated buffers, timed like the GEMV; the best one (GB/s)."""
     import bit_weight_only_gemv_amd as B
     nb = (nbytes + 15) // 16 * 16
     ncopy = max(1, -(-ROTATE_BYTES // nb))
     bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
-    sink = torch.empty(B.wq_read_probe_sink_words(nb), dtype=torch.int32, device="cuda")
-    ms = timer(lambda i: B.wq_read_probe(bufs[i % ncopy], nb, sink), steps, warmup, ncopy)
+    sink = torch.empty(65536, dtype=torch.int32, device="cuda")
+    best = None
+    for blocks, threads, ring in ATTAINABLE_GEOMETRIES:
+        ms = timer(lambda i: B.wq_read_probe_geom(bufs[i % ncopy], nb, sink, blocks, threads, ring),
+                   max(steps, ncopy), max(warmup, ncopy), ncopy)
+        rate = gbs(nb, ms)
+        if best is None or rate > best[0]:
+            best = (rate, {"blocks": "one-shot", "threads": threads, "loads_in_flight": ring})
     del bufs
-    return nb / (ms * 1e-3) / 1e9
+    return best
+
+
+# ------------------------------------------------------------ CPU baseline
+
+
+def host_info():
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                       "unknown")
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    return {"cores": len(os.sched_getaffinity(0)), "blas_threads": int(blas), "cpu_model": cpu}
+
+
+def oracle_times(ref, X, runs, min_s=0.0):
+    """Wall times of the oracle's dequantization and float64 product of one
+    packed layer against X (median of `runs`, or of as many runs as fill
+    `min_s` seconds)."""
+    import oracle as O
+    t_deq, t_mv = [], []
+    t_start = time.perf_counter()
+    while len(t_deq) < runs or time.perf_counter() - t_start < min_s:
+        t0 = time.perf_counter()
+        w_hat = ref.w_hat()
+        t1 = time.perf_counter()
+        O.matvec_ref(w_hat, X, ref.idx, ref.wout)
+        t2 = time.perf_counter()
+        t_deq.append(t1 - t0)
+        t_mv.append(t2 - t1)
+    return float(np.median(t_deq)), float(np.median(t_mv))
+
+
+def cpu_baseline_rate(value, unit, t_deq, t_mv, sample, **extra):
+    info = host_info()
+    out = {"value": value, "unit": unit, "cores": info["cores"], "kind": "oracle",
+           "blas_threads": info["blas_threads"], "dequant_s": round(t_deq, 3),
+           "matvec_s": round(t_mv, 3), "cpu_model": info["cpu_model"],
+           "sample": sample + (f"; numpy elementwise work is single-threaded, the BLAS product "
+                               f"used {info['blas_threads']} threads of {info['cores']} host cores")}
+    out.update(extra)
+    return out
+
+
+def cpu_baseline_layer(ref, X, nbytes, runs=3, what="the whole layer"):
+    """The oracle, as it stands, on the same packed layer and activations:
+    dequantization followed by the float64 product; rate in the same
+    algorithmic bytes as the GPU line."""
+    t_deq, t_mv = oracle_times(ref, X, runs)
+    t = t_deq + t_mv
+    return cpu_baseline_rate(round(nbytes / t / 1e9, 4), "GB/s", t_deq, t_mv,
+                             f"{what} ({ref.N}x{ref.K}, M={np.atleast_2d(X).shape[0]}): oracle "
+                             f"dequantization + float64 product, median of {runs} runs "
+                             f"({t:.2f} s each)")
+
+
+# ---------------------------------------------------------------- workloads
+
+
+FMT_NAME = {4: "W4", 2: "W2", 5: "W4P (packed zero points)"}
 
 
 def gemv_workload(a, torch, L, label, timer):
-    import bit_weight_only_gemv_amd as B
+    """The M = 1 fused GEMV of one layer on both layouts (tiled and row-major);
+    `value` is the faster one unless --layout says which."""
+    import bit_weight_only_gemv_amd as B  # noqa: F401
+    import oracle as O
     from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
     t0 = time.time()
     hl = pack_host(L.fmt, L.W, L.profile, L.ratio)
@@ -265,45 +372,31 @@ def gemv_workload(a, torch, L, label, timer):
     layout = min(times, key=times.get) if a.layout == "best" else a.layout
     other = "rowmajor" if layout == "tiled" else "tiled"
     ms, ms_other = times[layout], times[other]
-    gbs = nbytes / (ms * 1e-3) / 1e9
+    g = gbs(nbytes, ms)
     bpt = sweep_bytes_per_token(L.fmt, L.ratio)
-    traffic = traffic_for(f"{label}_{layout}")
     del layers
-    probe = read_probe_rate(torch, timer, nbytes, a.steps, a.warmup)
-    out = {
-        "metric": METRIC,
-        "value": round(gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic (seeded Gaussian weights and activations; no checkpoint)",
-        "config": {"workload": label, "N": base.N, "K": base.K, "M": 1, "n_out": base.n_out,
-                   "format": {4: "W4", 2: "W2", 5: "W4P (packed zero points)"}[L.fmt] + " group-32",
-                   "accumulate": "f32",
-                   "bytes_per_step": nbytes, "rotated_copies": ncopy, "layout": layout,
-                   "timing": "eager launches" if a.eager else "hip graph replay"},
-        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "attainable": {"read_probe_GB/s": round(probe, 1),
-                       "pct_of_read_probe": round(100 * gbs / probe, 2),
-                       "about": "a plain streaming read of the same bytes per launch, rotated "
-                                "and graph-replayed in the same run"},
-        "eq_tokens_per_s": round(gbs * 1e9 / bpt, 1),
-        "eq_tokens_basis_bytes_per_token": bpt,
-        "host_pack_s": round(pack_s, 2),
-        f"{other}_layout": {"us": round(ms_other * 1e3, 3),
-                            "GB/s": round(nbytes / (ms_other * 1e-3) / 1e9, 2)},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
-    }
+    probe, geom = attainable_read(torch, timer, nbytes, max(a.steps // 4, 1), max(a.warmup // 4, 1))
+    out = line(METRIC, round(g, 2), "GB/s", a, ms,
+               {"workload": label, "N": base.N, "K": base.K, "M": 1, "n_out": base.n_out,
+                "format": FMT_NAME[L.fmt] + " group-32", "accumulate": "f32",
+                "bytes_per_step": nbytes, "rotated_copies": ncopy, "layout": layout,
+                "timing": "eager launches" if a.eager else "hip graph replay"},
+               roofline_hbm(nbytes, ms, traffic_for(f"{label}_{layout}")),
+               pct_of_hbm_peak=round(100 * g / HBM_PEAK_GBS, 2),
+               attainable={"read_probe_GB/s": round(probe, 1),
+                           "pct_of_read_probe": round(100 * g / probe, 2),
+                           "read_probe_geometry": geom,
+                           "about": "the best of the one-shot grid-stride read kernels over the "
+                                    "same bytes per launch, rotated and graph-replayed in the "
+                                    "same run"},
+               eq_tokens_per_s=round(g * 1e9 / bpt, 1),
+               eq_tokens_basis_bytes_per_token=bpt,
+               host_pack_s=round(pack_s, 2))
+    out[f"{other}_layout"] = {"us": round(ms_other * 1e3, 3), "GB/s": round(gbs(nbytes, ms_other), 2),
+                              "timing_us": ms_other.us()}
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(L, nbytes)
+        ref = O.quantize_layer(L.fmt, L.W, L.profile, L.ratio)
+        out["cpu_baseline"] = cpu_baseline_layer(ref, L.x, nbytes)
     return out
 
 
@@ -325,12 +418,38 @@ def w4_fmt(a) -> int:
     return 5 if a.w4_zeros == "packed" else 4
 
 
+def sweep_cpu_baseline(fmt, bytes_per_token):
+    """The oracle on a bounded sample of the decode step: the 7 GEMVs of the
+    first layer (their own weights and activations), dequantization + float64
+    product, scaled to tokens/s by bytes."""
+    import oracle as O
+    import synthetic
+    shapes = [s for s in synthetic.config3_shapes() if s[0] == 0]
+    t_deq = t_mv = 0.0
+    nb = 0
+    for (layer, p, name, N, K) in shapes:
+        L = synthetic.config3_layer(layer, p, N, K, name)
+        ref = O.quantize_layer(fmt, L.W)
+        d, m = oracle_times(ref, L.x, 1)
+        t_deq += d
+        t_mv += m
+        G = K // 32
+        nb += N * K // 2 + 2 * N * G + (N * ((G + 1) // 2) if fmt == 5 else 2 * N * G) + 2 * K + 2 * N
+    t = t_deq + t_mv
+    tps = (nb / t) / bytes_per_token
+    return cpu_baseline_rate(round(tps, 4), "tokens/s", t_deq, t_mv,
+                             f"the 7 GEMVs of the first layer ({nb / 1e6:.0f} MB of the "
+                             f"{bytes_per_token / 1e9:.2f} GB per token), oracle dequantization "
+                             f"+ float64 product in {t:.2f} s, scaled to a whole token by bytes",
+                             GB_per_s=round(nb / t / 1e9, 4))
+
+
 def sweep_workload(a, torch, timer):
     """One Llama-3-8B-shaped W4 decode step per graph replay, two ways:
     225 separate GEMVs, and 129 GEMVs with q|k|v and gate|up stacked along N
     (same weights, same bytes, fewer launches).  Each group of GEMVs runs on
     the layout (row-major or tiled) measured faster for it over its 32 layers;
-    tokens_per_s is the fused step's rate."""
+    `value` is the stacked step's rate in tokens/s."""
     import synthetic
     from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
     shapes = synthetic.config3_shapes()
@@ -350,8 +469,7 @@ def sweep_workload(a, torch, timer):
     head_layer = DeviceLayer(pack_host(w4_fmt(a), hL.W), tiled=True)
     torch.cuda.synchronize()
     steps = max(1, min(a.steps, 50))
-    out = {"workload": "w4_llama3_8b_decode_step" + ("_w4p" if w4_fmt(a) == 5 else ""),
-           "steps": steps}
+    res = {}
     for label, groups in SWEEP_GROUPS.items():
         layers = {g: [protos[g]] + [clone_layer(DeviceLayer, protos[g]) for _ in range(nlayers - 1)]
                   for g in groups}
@@ -385,39 +503,54 @@ def sweep_workload(a, torch, timer):
                 fn(x, y)
 
         ms = timer(step, steps, min(a.warmup, 5))
-        out[label] = {"gemvs_per_token": len(calls), "ms_per_token": round(ms, 4),
+        res[label] = {"gemvs_per_token": len(calls), "ms_per_token": round(ms, 4),
                       "tokens_per_s": round(1e3 / ms, 1), "bytes_per_token": total,
-                      "GB/s": round(total / (ms * 1e-3) / 1e9, 1),
+                      "GB/s": round(gbs(total, ms), 1), "timing_us": ms.us(), "ms": ms,
                       "layouts": {("|".join(g) if g != "head" else g): pick[g] for g in pick}}
         del layers, calls
         torch.cuda.synchronize()
-    best = out["fused"]
-    out.update({"ms_per_token": best["ms_per_token"], "tokens_per_s": best["tokens_per_s"],
-                "pct_of_hbm_peak": round(100 * best["GB/s"] / HBM_PEAK_GBS, 2),
-                "roofline_tokens_per_s": round(HBM_PEAK_GBS * 1e9 / best["bytes_per_token"], 1)})
+    best = res["fused"]
+    ms = best.pop("ms")
+    res["unfused"].pop("ms")
+    roof_tps = HBM_PEAK_GBS * 1e9 / best["bytes_per_token"]
+    tps = 1e3 / ms
+    out = line("decode step tokens/s (Llama-3-8B-shaped W4 sweep, M=1)", round(tps, 1), "tokens/s",
+               a, ms,
+               {"workload": "w4_llama3_8b_decode_step" + ("_w4p" if w4_fmt(a) == 5 else ""),
+                "gemvs_per_token": best["gemvs_per_token"], "bytes_per_token": best["bytes_per_token"],
+                "format": FMT_NAME[w4_fmt(a)] + " group-32"},
+               {"bound": "hbm", "achieved": round(tps, 1), "peak": round(roof_tps, 1),
+                "unit": "tokens/s", "frac": round(tps / roof_tps, 4),
+                "achieved_GB/s": best["GB/s"], "peak_GB/s": HBM_PEAK_GBS, "traffic": None},
+               steps_timed=steps, fused=best, unfused=res["unfused"],
+               pct_of_hbm_peak=round(100 * best["GB/s"] / HBM_PEAK_GBS, 2))
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = sweep_cpu_baseline(w4_fmt(a), best["bytes_per_token"])
     return out
 
 
 def batched_workload(a, torch, timer):
     """Small-M products (SPECTRA section 4.2) on the W4 14336 x 4096 and
-    4096 x 14336 layers: the tiled layout's batched kernel (the same buffer as
-    the M = 1 kernel), the row-major arrays' batched kernel, M repeated GEMVs,
+    4096 x 14336 layers: the tiled layout's kernels (the same buffer as the
+    M = 1 kernel), the row-major arrays' batched kernel, M repeated GEMVs,
     and the tiled M = 1 GEMV of the same layer in the same run."""
+    import oracle as O
     import synthetic
     from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
     rows = []
     shapes = [(14336, 4096), (4096, 14336)]
     if a.shape:
         shapes = [tuple(int(v) for v in a.shape.lower().split("x"))]
+    st, wu = max(1, a.steps // 4), max(1, a.warmup // 4)
     for (N, K) in shapes:
         Lb = synthetic.config4(16, N, K)
         base = DeviceLayer(pack_host(w4_fmt(a), Lb.W), tiled=True)
+        ref = None if a.no_cpu_baseline else O.quantize_layer(w4_fmt(a), Lb.W)
         n1 = base.nbytes(1)
         l1 = rotated(DeviceLayer, base, n1)
         x1 = torch.from_numpy(np.ascontiguousarray(Lb.x[0]).view(np.int16)).cuda()
         y1 = [torch.empty(N, dtype=torch.int16, device="cuda") for _ in range(len(l1))]
-        ms_m1 = timer(lambda i: l1[i % len(l1)].gemv_tiled(x1, y1[i % len(l1)]), a.steps // 4,
-                      a.warmup // 4, len(l1))
+        ms_m1 = timer(lambda i: l1[i % len(l1)].gemv_tiled(x1, y1[i % len(l1)]), st, wu, len(l1))
         del l1
         for M in ((a.m,) if a.m else (2, 4, 8, 16)):
             nbytes = base.nbytes(M)
@@ -426,36 +559,50 @@ def batched_workload(a, torch, timer):
             X = torch.from_numpy(np.ascontiguousarray(Lb.x[:M]).view(np.int16)).cuda()
             Y = [torch.empty((M, N), dtype=torch.int16, device="cuda") for _ in range(nc)]
             xrow = [X[m].contiguous() for m in range(M)]
-            ms_tiled = timer(lambda i: layers[i % nc].gemm_tiled(X, Y[i % nc]), a.steps // 4,
-                             a.warmup // 4, nc)
-            ms_gemm = timer(lambda i: layers[i % nc].gemm(X, Y[i % nc]), a.steps // 4, a.warmup // 4, nc)
+            ms_tiled = timer(lambda i: layers[i % nc].gemm_tiled(X, Y[i % nc]), st, wu, nc)
+            ms_gemm = timer(lambda i: layers[i % nc].gemm(X, Y[i % nc]), st, wu, nc)
 
             def rep(i):
                 for m in range(M):
                     layers[i % nc].gemv(xrow[m], Y[i % nc][m])
-            ms_rep = timer(rep, max(1, a.steps // (4 * M)), max(1, a.warmup // (4 * M)), nc)
+            ms_rep = timer(rep, max(1, st // M), max(1, wu // M), nc)
+            ms = min(ms_tiled, ms_gemm)
             flops = 2.0 * M * N * K
-            rows.append({"workload": f"w{'4p' if w4_fmt(a) == 5 else '4'}_{N}x{K}_m{M}",
-                         "bytes": nbytes,
-                         "tiled_us": round(ms_tiled * 1e3, 3),
-                         "tiled_GB/s": round(nbytes / (ms_tiled * 1e-3) / 1e9, 1),
-                         "tiled_over_m1": round(ms_tiled / ms_m1, 3),
-                         "m1_tiled_us": round(ms_m1 * 1e3, 3),
-                         "rowmajor_us": round(ms_gemm * 1e3, 3),
-                         "rowmajor_GB/s": round(nbytes / (ms_gemm * 1e-3) / 1e9, 1),
-                         "TFLOP/s": round(flops / (min(ms_tiled, ms_gemm) * 1e-3) / 1e12, 2),
-                         "repeated_gemv_us": round(ms_rep * 1e3, 3)})
+            tfl = flops / (ms * 1e-3) / 1e12
+            roof = roofline_hbm(nbytes, ms)
+            roof["mfma"] = {"achieved": round(tfl, 2), "peak": MFMA_FP16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(tfl / MFMA_FP16_PEAK_TFLOPS, 5)}
+            out = line(f"batched M={M} W4A16 product effective HBM GB/s", round(gbs(nbytes, ms), 2),
+                       "GB/s", a, ms,
+                       {"workload": f"w{'4p' if w4_fmt(a) == 5 else '4'}_{N}x{K}_m{M}", "N": N,
+                        "K": K, "M": M, "format": FMT_NAME[w4_fmt(a)] + " group-32",
+                        "bytes_per_step": nbytes, "rotated_copies": nc,
+                        "layout": "tiled" if ms_tiled <= ms_gemm else "rowmajor"},
+                       roof,
+                       tiled={"us": round(ms_tiled * 1e3, 3), "GB/s": round(gbs(nbytes, ms_tiled), 1),
+                              "over_m1": round(ms_tiled / ms_m1, 3)},
+                       rowmajor={"us": round(ms_gemm * 1e3, 3), "GB/s": round(gbs(nbytes, ms_gemm), 1)},
+                       m1_tiled_us=round(ms_m1 * 1e3, 3),
+                       repeated_gemv_us=round(ms_rep * 1e3, 3),
+                       speedup_vs_repeated_gemv=round(ms_rep / ms, 2))
+            if ref is not None:
+                out["cpu_baseline"] = cpu_baseline_layer(ref, Lb.x[:M], nbytes, runs=1)
+            rows.append(out)
             del layers
     return rows
 
 
 def w2_70b_workload(a, torch, timer):
+    """70B-class W2 layers with 3.5% FP16 outlier columns (28672 x 8192 and
+    8192 x 28672) at M = 1 and M = 8, on both layouts."""
     import synthetic
     from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
     rows = []
+    st, wu = max(1, a.steps // 4), max(1, a.warmup // 4)
     for (N, K) in ((28672, 8192), (8192, 28672)):
         L8 = synthetic.config5(N, K, 8)
         base = DeviceLayer(pack_host(2, L8.W, L8.profile, L8.ratio), tiled=True)
+        cpu = {}
         for M, layout in ((1, "rowmajor"), (1, "tiled"), (8, "rowmajor"), (8, "tiled")):
             nbytes = base.nbytes(M)
             layers = rotated(DeviceLayer, base, nbytes)
@@ -470,13 +617,62 @@ def w2_70b_workload(a, torch, timer):
                 fn = lambda i: layers[i % nc].gemm_tiled(X, Y[i % nc])  # noqa: E731
             else:
                 fn = lambda i: layers[i % nc].gemm(X, Y[i % nc])  # noqa: E731
-            ms = timer(fn, a.steps // 4, a.warmup // 4, nc)
-            rows.append({"workload": f"w2_{N}x{K}_outliers{base.n_out}_m{M}", "layout": layout,
-                         "bytes": nbytes, "us": round(ms * 1e3, 3),
-                         "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                         "pct_of_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)})
+            ms = timer(fn, st, wu, nc)
+            g = gbs(nbytes, ms)
+            out = line("M=%d W2 + outliers effective HBM GB/s" % M, round(g, 2), "GB/s", a, ms,
+                       {"workload": f"w2_{N}x{K}_outliers{base.n_out}_m{M}", "N": N, "K": K, "M": M,
+                        "n_out": base.n_out, "format": "W2 group-32", "layout": layout,
+                        "bytes_per_step": nbytes, "rotated_copies": nc},
+                       roofline_hbm(nbytes, ms, traffic_for(f"w2_{N}x{K}_m{M}_{layout}")),
+                       pct_of_hbm_peak=round(100 * g / HBM_PEAK_GBS, 2))
+            if not a.no_cpu_baseline:
+                if M not in cpu:
+                    cpu[M] = cpu_baseline_rows(2, L8.W, L8.profile, L8.ratio, L8.x[:M], 2048,
+                                               f"the {N}x{K} W2 layer")
+                out["cpu_baseline"] = cpu[M]
+            rows.append(out)
             del layers
     return rows
+
+
+def cpu_baseline_rows(fmt, W, profile, ratio, X, rows, what):
+    """The oracle on a bounded sample of a large layer: its first `rows`
+    output rows, quantized by the oracle beforehand (untimed), then the timed
+    dequantization + float64 product; GB/s in the sample's algorithmic bytes
+    (codes, scales, zeros, outlier slab and indices, X and the sample's Y)."""
+    import oracle as O
+    X = np.atleast_2d(X)
+    ref = O.quantize_layer(fmt, W[:rows], profile, ratio)
+    M, K = X.shape
+    G = K // 32
+    zb = rows * ((G + 1) // 2) if fmt == 5 else 2 * rows * G
+    nb = ref.codes.nbytes + 2 * rows * G + zb + 2 * rows * ref.n_out + 4 * ref.n_out + 2 * M * K \
+        + 2 * M * rows
+    t_deq, t_mv = oracle_times(ref, X, 1, min_s=5.0)
+    t = t_deq + t_mv
+    return cpu_baseline_rate(round(nb / t / 1e9, 4), "GB/s", t_deq, t_mv,
+                             f"{what}: the first {rows} of {W.shape[0]} output rows "
+                             f"({rows}x{K}, M={M}), oracle dequantization + float64 product, "
+                             f"median over at least 5 s of runs ({t:.2f} s each)")
+
+
+def host_read_baseline(nbytes):
+    """Host-side reference for the plain streaming kernels (which have no
+    oracle): numpy's sum over a buffer of the same size, as uint64 words."""
+    buf = np.ones(nbytes // 8, np.uint64)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        int(buf.sum())
+        reps += 1
+        if time.perf_counter() - t0 > 1.0:
+            break
+    t = (time.perf_counter() - t0) / reps
+    info = host_info()
+    return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "numpy read",
+            "cpu_model": info["cpu_model"],
+            "sample": f"numpy sum over {nbytes} bytes of uint64 words, {reps} passes in "
+                      f"{t * reps:.2f} s, one thread of {info['cores']} host cores"}
 
 
 def embed_workload(a, torch, timer):
@@ -485,12 +681,15 @@ def embed_workload(a, torch, timer):
     ids per launch, a fresh id set each launch (rotated), rows dequantized
     straight into FP16 output rows.  Bytes = the gathered rows' codes, scales,
     zeros and ids read plus the FP16 rows written."""
+    import oracle as O
     import synthetic
     from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
     V, K = 131072, 4096
     fmt = w4_fmt(a)
     W = synthetic.gaussian_weights(V, K, 0.02, 6, 0, fmt)
     dl = DeviceLayer(pack_host(fmt, W))
+    # the oracle's table for the CPU baseline: the first 8192 rows (quantized untimed)
+    ref = None if a.no_cpu_baseline else O.quantize_layer(fmt, W[:8192])
     del W
     G = K // 32
     zrow = (G + 1) // 2 if fmt == 5 else 2 * G
@@ -502,12 +701,32 @@ def embed_workload(a, torch, timer):
                for _ in range(nsets)]
         outs = [torch.empty((n_ids, K), dtype=torch.int16, device="cuda") for _ in range(4)]
         fn = lambda i: dl.embed(ids[i % nsets], outs[i % 4])  # noqa: E731
-        ms = timer(fn, a.steps // 4, a.warmup // 4, nsets)
+        ms = timer(fn, max(1, a.steps // 4), max(1, a.warmup // 4), nsets)
         nbytes = n_ids * (K // 2 + 2 * G + zrow + 4) + n_ids * K * 2
-        rows.append({"workload": f"embed_gather_{V}x{K}_w{'4p' if fmt == 5 else '4'}_ids{n_ids}",
-                     "bytes": nbytes, "us": round(ms * 1e3, 3),
-                     "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                     "pct_of_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)})
+        g = gbs(nbytes, ms)
+        out = line(f"embedding gather ({n_ids} ids) effective HBM GB/s", round(g, 2), "GB/s", a, ms,
+                   {"workload": f"embed_gather_{V}x{K}_w{'4p' if fmt == 5 else '4'}_ids{n_ids}",
+                    "V": V, "K": K, "n_ids": n_ids, "bytes_per_step": nbytes,
+                    "id_sets": nsets},
+                   roofline_hbm(nbytes, ms), pct_of_hbm_peak=round(100 * g / HBM_PEAK_GBS, 2))
+        if ref is not None:
+            rid = np.random.default_rng(7 + n_ids).integers(0, 8192, n_ids)
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                q = O.unpack_w4(ref.codes[rid])
+                O.dequant_w4(q, ref.scale[rid], ref.zero[rid])
+                reps += 1
+                if time.perf_counter() - t0 > 2.0:
+                    break
+            t = (time.perf_counter() - t0) / reps
+            info = host_info()
+            out["cpu_baseline"] = {
+                "value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": info["cores"],
+                "kind": "oracle", "cpu_model": info["cpu_model"],
+                "sample": f"{n_ids} ids drawn from the first 8192 rows of the table (the oracle's "
+                          f"packed codes, scales and zeros): code unpacking + dequantization of the "
+                          f"gathered rows, {reps} runs in {t * reps:.2f} s, numpy single-threaded"}
+        rows.append(out)
     return rows
 
 
@@ -515,7 +734,7 @@ def kurtosis_workload(a, torch, timer):
     """The kurtosis-adaptive outlier policy (SPECTRA sections 3.1-3.3) on the W2
     layers of the other workloads: kappa, the ratio and n_out it picks (host
     time), and the tiled W2 GEMV with those outliers next to the profile-guided
-    3.5% of the default workloads."""
+    3.5% of the default workloads; `value` is the kurtosis-picked layer's rate."""
     import synthetic
     from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host
     import bit_weight_only_gemv_amd as B
@@ -525,8 +744,7 @@ def kurtosis_workload(a, torch, timer):
         t0 = time.time()
         idx, r, kappa = B.wq_select_outliers_kurtosis(L.W)
         t_sel = time.time() - t0
-        row = {"workload": f"kurtosis_policy_{label}", "kappa": round(kappa, 4), "ratio": round(r, 5),
-               "n_out": int(len(idx)), "host_select_s": round(t_sel, 3)}
+        res = {}
         for pol in ("kurtosis", "profile_3.5pct"):
             hl = pack_host(2, L.W, kurtosis=True) if pol == "kurtosis" else \
                 pack_host(2, L.W, L.profile, L.ratio)
@@ -536,24 +754,55 @@ def kurtosis_workload(a, torch, timer):
             nc = len(layers)
             x = torch.from_numpy(L.x[:1].reshape(-1).view(np.int16)).cuda()
             ys = [torch.empty(base.N, dtype=torch.int16, device="cuda") for _ in range(nc)]
-            ms = timer(lambda i: layers[i % nc].gemv_tiled(x, ys[i % nc]), a.steps // 4,
-                       a.warmup // 4, nc)
-            row[pol] = {"n_out": base.n_out, "bytes": nbytes, "us": round(ms * 1e3, 3),
-                        "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+            ms = timer(lambda i: layers[i % nc].gemv_tiled(x, ys[i % nc]), max(1, a.steps // 4),
+                       max(1, a.warmup // 4), nc)
+            res[pol] = {"n_out": base.n_out, "bytes": nbytes, "us": round(ms * 1e3, 3),
+                        "GB/s": round(gbs(nbytes, ms), 2), "timing_us": ms.us(), "ms": ms}
             del layers
-        rows.append(row)
+        k = res["kurtosis"]
+        ms = k.pop("ms")
+        res["profile_3.5pct"].pop("ms")
+        out = line("M=1 W2 GEMV with kurtosis-picked outliers, effective HBM GB/s", k["GB/s"], "GB/s",
+                   a, ms,
+                   {"workload": f"kurtosis_policy_{label}", "N": L.W.shape[0], "K": L.W.shape[1],
+                    "M": 1, "n_out": k["n_out"], "format": "W2 group-32", "layout": "tiled",
+                    "bytes_per_step": k["bytes"]},
+                   roofline_hbm(k["bytes"], ms),
+                   kappa=round(kappa, 4), ratio=round(r, 5), host_select_s=round(t_sel, 3),
+                   kurtosis=k, profile_3_5pct=res["profile_3.5pct"])
+        if not a.no_cpu_baseline:
+            out["cpu_baseline"] = _kurtosis_cpu(L, idx)
+        rows.append(out)
     return rows
+
+
+def _kurtosis_cpu(L, idx):
+    """The oracle on the kurtosis-picked layer: its first 2048 output rows with
+    the same outlier columns, dequantization + float64 product."""
+    import oracle as O
+    rows = 2048
+    ref = O.quantize_layer(2, L.W[:rows], idx=idx)
+    K = L.W.shape[1]
+    G = K // 32
+    nb = ref.codes.nbytes + 4 * rows * G + 2 * rows * ref.n_out + 4 * ref.n_out + 2 * K + 2 * rows
+    t_deq, t_mv = oracle_times(ref, L.x[:1], 1, min_s=5.0)
+    t = t_deq + t_mv
+    return cpu_baseline_rate(round(nb / t / 1e9, 4), "GB/s", t_deq, t_mv,
+                             f"the first {rows} of {L.W.shape[0]} output rows with the "
+                             f"{len(idx)} kurtosis-picked outlier columns, oracle dequantization + "
+                             f"float64 product, median over at least 5 s of runs ({t:.2f} s each)")
 
 
 def refine_workload(a, torch, timer):
     """Runtime top-k refinement (StrataFlux section 3.2.1, Eq. 2) after the tiled
     GEMV: per 1024-channel chunk the k = 32 largest |x_i| are selected on the GPU
-    and their 4-bit residual columns added to y.  Each launch times the
-    selection, the add, the GEMV, the three in sequence, and the GEMV with the
-    selection and the add in the same launch; the layer and its
-    refinement columns are rotated like the GEMV's.  Refinement bytes = the
-    selected columns' codes, scales and zeros, the indices and x entries read,
-    and y read and written."""
+    and their 4-bit residual columns added to y.  Times the selection, the add,
+    the GEMV, the three in sequence, and the GEMV with the selection and the add
+    in the same launch (`value`, in the layer's and the refinement's bytes); the
+    layer and its refinement columns are rotated like the GEMV's.  Refinement
+    bytes = the selected columns' codes, scales and zeros, the indices and x
+    entries read, and y read and written."""
+    import oracle as O
     import synthetic
     import bit_weight_only_gemv_amd as B
     from bit_weight_only_gemv_amd.layer import DeviceLayer, pack_host, refinement_host
@@ -579,8 +828,8 @@ def refine_workload(a, torch, timer):
         sels = [torch.empty(n_sel, dtype=torch.int32, device="cuda") for _ in range(nc)]
         for i in range(nc):
             B.wq_topk_chunks(x, K, chunk, k, sels[i])
-        st = a.steps // 4
-        wu = a.warmup // 4
+        st = max(1, a.steps // 4)
+        wu = max(1, a.warmup // 4)
         t_topk = timer(lambda i: B.wq_topk_chunks(x, K, chunk, k, sels[i % nc]), st, wu, nc)
         t_ref = timer(lambda i: layers[i % nc].refine(x, ys[i % nc], sels[i % nc], n_sel), st, wu, nc)
         t_gemv = timer(lambda i: layers[i % nc].gemv_tiled(x, ys[i % nc]), st, wu, nc)
@@ -593,43 +842,55 @@ def refine_workload(a, torch, timer):
 
         t_all = timer(chain, st, wu, nc)
         t_fused = timer(lambda i: layers[i % nc].refine_topk(x, ys[i % nc], k, chunk), st, wu, nc)
-        # the same call given a selection buffer (two kernels past 8 chunks)
-        t_call = timer(lambda i: layers[i % nc].refine_topk(x, ys[i % nc], k, chunk, sels[i % nc]),
-                       st, wu, nc)
 
         def chain_fused(i):
             layers[i % nc].gemv_tiled(x, ys[i % nc])
             layers[i % nc].refine_topk(x, ys[i % nc], k, chunk)
 
         t_all_fused = timer(chain_fused, st, wu, nc)
-
-        def chain_call(i):
-            layers[i % nc].gemv_tiled(x, ys[i % nc])
-            layers[i % nc].refine_topk(x, ys[i % nc], k, chunk, sels[i % nc])
-
-        t_all_call = timer(chain_call, st, wu, nc)
-        # the product with the selection and the add in the same launch
         t_one = timer(lambda i: layers[i % nc].gemv_tiled_refine(x, ys[i % nc], k, chunk), st, wu, nc)
         Gn = N // 32
         rbytes = n_sel * (N // 2 + 4 * Gn) + 4 * n_sel + 2 * n_sel + 4 * N
-        rows.append({"workload": f"refine_topk{k}_per{chunk}_{label}", "N": N, "K": K,
-                     "n_sel": n_sel, "topk_us": round(t_topk * 1e3, 3),
-                     "refine_us": round(t_ref * 1e3, 3), "refine_bytes": rbytes,
-                     "refine_GB/s": round(rbytes / (t_ref * 1e-3) / 1e9, 1),
-                     "gemv_us": round(t_gemv * 1e3, 3),
-                     "fused_topk_refine_us": round(t_fused * 1e3, 3),
-                     "gemv_topk_refine_us": round(t_all * 1e3, 3),
-                     "gemv_fused_refine_us": round(t_all_fused * 1e3, 3),
-                     "refine_topk_with_sel_out_us": round(t_call * 1e3, 3),
-                     "gemv_refine_topk_with_sel_out_us": round(t_all_call * 1e3, 3),
-                     "two_launch_overhead_pct": round(100 * (t_all_call - t_gemv) / t_gemv, 1),
-                     "gemv_refine_one_launch_us": round(t_one * 1e3, 3),
-                     "one_launch_overhead_pct": round(100 * (t_one - t_gemv) / t_gemv, 1)})
+        total = nbytes + rbytes - 4 * N + 2 * N     # y is written once in the one-launch form
+        g = gbs(total, t_one)
+        out = line("M=1 GEMV + top-k refinement in one launch, effective HBM GB/s", round(g, 2),
+                   "GB/s", a, t_one,
+                   {"workload": f"refine_topk{k}_per{chunk}_{label}", "N": N, "K": K, "M": 1,
+                    "n_sel": n_sel, "bytes_per_step": total, "layer_bytes": nbytes,
+                    "refine_bytes": rbytes, "layout": "tiled"},
+                   roofline_hbm(total, t_one),
+                   topk_us=round(t_topk * 1e3, 3), refine_us=round(t_ref * 1e3, 3),
+                   refine_GB_per_s=round(gbs(rbytes, t_ref), 1),
+                   gemv_us=round(t_gemv * 1e3, 3),
+                   fused_topk_refine_us=round(t_fused * 1e3, 3),
+                   gemv_topk_refine_us=round(t_all * 1e3, 3),
+                   gemv_fused_refine_us=round(t_all_fused * 1e3, 3),
+                   two_launch_overhead_pct=round(100 * (t_all_fused - t_gemv) / t_gemv, 1),
+                   one_launch_overhead_pct=round(100 * (t_one - t_gemv) / t_gemv, 1))
+        if not a.no_cpu_baseline:
+            ref = O.quantize_layer(L.fmt, L.W, L.profile, L.ratio)
+            rq = O.refinement_w4(L.W, ref.w_hat(), ref.idx)
+            c_hat = O.dequant_w4(*rq)
+            t0 = time.perf_counter()
+            w_hat = ref.w_hat()
+            y0, _ = O.matvec_ref(w_hat, L.x[:1], ref.idx, ref.wout)
+            t1 = time.perf_counter()
+            sel = O.topk_chunks(L.x[0], k, chunk)
+            O.refine_ref(y0[0], L.x[0], sel, c_hat)
+            t2 = time.perf_counter()
+            out["cpu_baseline"] = cpu_baseline_rate(
+                round(total / (t2 - t0) / 1e9, 4), "GB/s", t1 - t0, t2 - t1,
+                f"the whole {N}x{K} layer: oracle dequantization + float64 product, then the "
+                f"oracle's top-k selection and refinement add over the dequantized residual "
+                f"columns ({t2 - t0:.2f} s; the refinement's time is in matvec_s)")
+        rows.append(out)
         del layers
     return rows
 
 
 def stream_workload(a, torch, timer, copy):
+    """Plain streaming kernels: the attainable read rate (read) and the
+    byte-counter calibration (copy)."""
     import bit_weight_only_gemv_amd as B
     nb = (a.bytes + 15) // 16 * 16
     ncopy = max(1, -(-ROTATE_BYTES // nb))
@@ -642,89 +903,65 @@ def stream_workload(a, torch, timer, copy):
         fn = lambda i: B.wq_read_probe(bufs[i % ncopy], nb, sink)  # noqa: E731
     ms = timer(fn, a.steps, a.warmup, ncopy)
     moved = nb * (2 if copy else 1)
-    return {"workload": "copy_probe" if copy else "read_probe", "bytes": nb, "copies": ncopy,
-            "us": round(ms * 1e3, 3), "GB/s": round(moved / (ms * 1e-3) / 1e9, 1)}
+    out = line(("copy" if copy else "read") + " probe HBM GB/s", round(gbs(moved, ms), 2), "GB/s", a,
+               ms, {"workload": "copy_probe" if copy else "read_probe", "bytes_per_step": moved,
+                    "rotated_copies": ncopy},
+               roofline_hbm(moved, ms))
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = host_read_baseline(nb)
+    return out
+
+
+PROBE_SIZES = [26157628, 10502144, 104555640, 37289984, 147849216, 265056256]
 
 
 def probe_sweep_workload(a, torch, timer):
     """The attainable streaming-read rate per launch at the layers' sizes: the
-    geometry-swept read kernel (workgroups x threads x loads in flight per
-    lane; each wave reads one contiguous run) over rotated buffers, every
-    geometry timed like the GEMV.  One line per size, with the best geometry
-    and the whole table."""
+    grid-stride read kernel over a table of launch geometries (workgroups x
+    threads x loads in flight per lane, blocks 0 = one-shot) over rotated
+    buffers, every geometry timed like the GEMV.  One line per size, with the
+    best geometry and the fastest rows of the table."""
     import bit_weight_only_gemv_amd as B
     rows = []
-    sizes = [int(v) for v in a.probe_sizes.split(",")] if a.probe_sizes else \
-        [26157628, 10502144, 104555640, 37289984]
+    sizes = [int(v) for v in a.probe_sizes.split(",")] if a.probe_sizes else PROBE_SIZES
     for nbytes in sizes:
         nb = (nbytes + 15) // 16 * 16
         ncopy = max(1, -(-ROTATE_BYTES // nb))
         bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(ncopy)]
         sink = torch.empty(65536, dtype=torch.int32, device="cuda")
         table = []
-        for blocks in (256, 512, 768, 1024, 2048, 4096):
+        for blocks in (0, 256, 512, 1024, 2048, 4096):
             for threads in (256, 512, 1024):
-                waves = blocks * threads // 64
-                span_kb = -(-nb // 1024 // waves)
-                for ring in (1, 2, 4, 8, 16):
-                    if ring > 2 * max(1, span_kb):
+                for ring in (1, 2, 4, 8):
+                    per_block = threads * 16 * ring
+                    nblk = blocks if blocks else -(-nb // per_block)
+                    if nblk > 65536 or nblk * per_block > 0x80000000:
                         continue
+                    if blocks and blocks * per_block >= nb:
+                        continue       # the same single round as the one-shot launch
                     ms = timer(lambda i: B.wq_read_probe_geom(bufs[i % ncopy], nb, sink, blocks,
                                                                threads, ring),
                                max(ncopy, a.steps // 10), max(ncopy, a.warmup // 10), ncopy)
-                    table.append({"blocks": blocks, "threads": threads, "ring": ring,
-                                  "span_kb": span_kb, "us": round(ms * 1e3, 3),
-                                  "GB/s": round(nb / (ms * 1e-3) / 1e9, 1)})
-        ms = timer(lambda i: B.wq_read_probe(bufs[i % ncopy], nb, sink[:B.wq_read_probe_sink_words(nb)]),
-                   max(ncopy, a.steps // 10), max(ncopy, a.warmup // 10), ncopy)
+                    table.append({"blocks": blocks or f"one-shot ({nblk})", "threads": threads,
+                                  "ring": ring, "us": round(ms * 1e3, 3),
+                                  "GB/s": round(gbs(nb, ms), 1)})
+        ms_gs = timer(lambda i: B.wq_read_probe(bufs[i % ncopy], nb,
+                                                 sink[:B.wq_read_probe_sink_words(nb)]),
+                      max(ncopy, a.steps // 10), max(ncopy, a.warmup // 10), ncopy)
         best = min(table, key=lambda r: r["us"])
-        rows.append({"workload": f"read_probe_sweep_{nb}B", "bytes": nb, "copies": ncopy,
-                     "best": best, "pct_of_hbm_peak": round(best["GB/s"] / HBM_PEAK_GBS * 100, 2),
-                     "grid_stride_probe": {"us": round(ms * 1e3, 3),
-                                           "GB/s": round(nb / (ms * 1e-3) / 1e9, 1)},
-                     "table": sorted(table, key=lambda r: r["us"])[:25]})
+        ms = best["us"] * 1e-3
+        out = line("attainable streaming read (best launch geometry) HBM GB/s", best["GB/s"], "GB/s",
+                   a, ms, {"workload": f"read_probe_sweep_{nb}B", "bytes_per_step": nb,
+                           "rotated_copies": ncopy},
+                   roofline_hbm(nb, ms), best=best,
+                   library_read_probe={"us": round(ms_gs * 1e3, 3), "GB/s": round(gbs(nb, ms_gs), 1)},
+                   table=sorted(table, key=lambda r: r["us"])[:25])
+        if not a.no_cpu_baseline:
+            out["cpu_baseline"] = host_read_baseline(min(nb, 64 << 20))
+        rows.append(out)
         del bufs
         torch.cuda.synchronize()
     return rows
-
-
-def cpu_baseline(L, nbytes):
-    """The oracle, as it stands, on the same layer: dequantization of the packed
-    weights followed by the float64 product (median of 3)."""
-    import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = 1
-    ref = O.quantize_layer(L.fmt, L.W, L.profile, L.ratio)
-    times, t_deq, t_mv = [], [], []
-    for _ in range(3):
-        t0 = time.perf_counter()
-        w_hat = ref.w_hat()
-        t1 = time.perf_counter()
-        O.matvec_ref(w_hat, L.x, ref.idx, ref.wout)
-        t2 = time.perf_counter()
-        times.append(t2 - t0)
-        t_deq.append(t1 - t0)
-        t_mv.append(t2 - t1)
-    t = float(np.median(times))
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
-                       "unknown")
-    except OSError:
-        pass
-    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
-            "kind": "oracle",
-            "dequant_s": round(float(np.median(t_deq)), 3),
-            "matvec_s": round(float(np.median(t_mv)), 3),
-            "cpu_model": cpu,
-            "sample": (f"the whole {ref.N}x{ref.K} layer: oracle dequantization + float64 product, "
-                       f"median of 3 runs ({t:.2f} s each); numpy elementwise work is single-threaded, "
-                       f"the BLAS product used {blas_threads} threads of "
-                       f"{len(os.sched_getaffinity(0))} host cores")}
 
 
 def main():

@@ -185,41 +185,33 @@ __global__ void __launch_bounds__(kProbeThreads) read_probe_kernel(const u4v* __
   }
 }
 
-// Geometry-swept read: wave v of the grid (blockIdx.x * waves + wave) owns
-// `span` consecutive 1 KB blocks starting at v * span KB; a 1 KB block is one
-// 64-lane load of 16 bytes per lane.  The blocks stream through a ring of RING
-// register buffers (RING loads in flight per lane; the compiler's vmcnt waits
-// keep exactly RING - 1 behind the one consumed).  Loads past `bytes` return 0
-// through the buffer descriptor and move no data.
+// Geometry-swept read: a grid-stride sweep in which every thread issues RING
+// 16-byte loads per round (piece t, t + P, ..., t + (RING - 1) P of the
+// buffer, P = threads in the grid), so that at any time the whole grid reads
+// one contiguous front of the buffer.  With enough blocks for one round the
+// launch is one-shot.  Loads past `bytes` return 0 through the buffer
+// descriptor and move no data.
 template <int RING>
 __global__ void __launch_bounds__(1024) read_probe_ring_kernel(const u4v* __restrict__ src,
-                                                               uint32_t bytes, uint32_t span,
+                                                               uint32_t bytes,
                                                                uint32_t* __restrict__ sink) {
-  __shared__ uint32_t red[16];
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, bytes);
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t wv = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const uint32_t base = wv * span * 1024u + 16u * lane;
+  const uint32_t stride = gridDim.x * blockDim.x * 16u;
   uint32_t acc = 0;
-  u4v buf[RING];
-#pragma unroll
-  for (int u = 0; u < RING; ++u) buf[u] = ld128(rs, (uint32_t)u < span ? base + 1024u * u : 0xFFFFF000u);
-  for (uint32_t b = 0; b < span; b += RING) {
+  for (uint32_t off = (blockIdx.x * blockDim.x + threadIdx.x) * 16u; off < bytes;
+       off += RING * stride) {
+    u4v v[RING];
 #pragma unroll
     for (int u = 0; u < RING; ++u) {
-      acc ^= buf[u].x ^ buf[u].y ^ buf[u].z ^ buf[u].w;
-      const uint32_t nb = b + RING + (uint32_t)u;
-      buf[u] = ld128(rs, nb < span ? base + 1024u * nb : 0xFFFFF000u);
+      const uint32_t o = off + (uint32_t)u * stride;
+      v[u] = ld128(rs, o < bytes ? o : 0xFFFFF000u);
     }
+#pragma unroll
+    for (int u = 0; u < RING; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
-  if (lane == 0) red[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = 0;
-    for (uint32_t w = 0; w < (blockDim.x >> 6); ++w) r ^= red[w];
-    sink[blockIdx.x] = r;
-  }
+  // one word per workgroup, written only when the data could not have been
+  // anything else (keeps the loads live without a reduction)
+  if (acc == 0x5A5A5A5Au) sink[blockIdx.x] = acc;
 }
 
 __global__ void __launch_bounds__(kProbeThreads) copy_probe_kernel(const u4v* __restrict__ src,
@@ -319,26 +311,30 @@ extern "C" int wq_read_probe(const void* src, int64_t bytes, uint32_t* sink, voi
 extern "C" int wq_read_probe_geom(const void* src, int64_t bytes, uint32_t* sink, int blocks,
                                   int threads, int ring, void* stream) {
   const char* who = "wq_read_probe_geom";
-  if (!src || !sink || bytes <= 0 || bytes % 16 || bytes > 0xFFFFE000ll)
-    return wq::fail(WQ_ERR_INVALID_ARG, "%s: bytes must be a positive multiple of 16 below 4 GB", who);
+  if (!src || !sink || bytes <= 0 || bytes % 16 || bytes > 0xFFFFE000ll / 2)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: bytes must be a positive multiple of 16 below 2 GB", who);
   if (!aligned16(src)) return wq::fail(WQ_ERR_INVALID_ARG, "%s: src not 16-byte aligned", who);
-  if (blocks < 1 || blocks > 65536 || threads < 64 || threads > 1024 || threads % 64)
-    return wq::fail(WQ_ERR_INVALID_ARG, "%s: blocks in [1, 65536], threads a multiple of 64 up to 1024",
+  if (threads < 64 || threads > 1024 || threads % 64 || blocks < 0 || blocks > 65536)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: threads a multiple of 64 up to 1024, blocks in [0, 65536]",
                     who);
-  const int64_t waves = (int64_t)blocks * (threads / 64);
-  const int64_t kb = (bytes + 1023) / 1024;
-  const int64_t span = (kb + waves - 1) / waves;
-  if (span * waves * 1024 > 0xFFFFF000ll)
-    return wq::fail(WQ_ERR_INVALID_ARG, "%s: grid too large for the buffer offsets", who);
+  if (ring != 1 && ring != 2 && ring != 4 && ring != 8 && ring != 16)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: ring must be 1, 2, 4, 8 or 16", who);
+  // blocks == 0: one round (one-shot)
+  const int64_t per_block = (int64_t)threads * 16 * ring;
+  int64_t nb = blocks > 0 ? blocks : (bytes + per_block - 1) / per_block;
+  if (nb > 65536) return wq::fail(WQ_ERR_INVALID_ARG, "%s: more than 65536 blocks", who);
+  // every load offset (at most bytes + one round's span) stays below 2^32
+  if (nb * per_block > 0x80000000ll)
+    return wq::fail(WQ_ERR_INVALID_ARG, "%s: one round of the grid spans more than 2 GB", who);
   hipStream_t s = (hipStream_t)stream;
-  const dim3 g((unsigned)blocks), b((unsigned)threads);
+  const dim3 g((unsigned)nb), b((unsigned)threads);
+  const uint32_t n = (uint32_t)bytes;
   switch (ring) {
-    case 1: hipLaunchKernelGGL(read_probe_ring_kernel<1>, g, b, 0, s, (const u4v*)src, (uint32_t)bytes, (uint32_t)span, sink); break;
-    case 2: hipLaunchKernelGGL(read_probe_ring_kernel<2>, g, b, 0, s, (const u4v*)src, (uint32_t)bytes, (uint32_t)span, sink); break;
-    case 4: hipLaunchKernelGGL(read_probe_ring_kernel<4>, g, b, 0, s, (const u4v*)src, (uint32_t)bytes, (uint32_t)span, sink); break;
-    case 8: hipLaunchKernelGGL(read_probe_ring_kernel<8>, g, b, 0, s, (const u4v*)src, (uint32_t)bytes, (uint32_t)span, sink); break;
-    case 16: hipLaunchKernelGGL(read_probe_ring_kernel<16>, g, b, 0, s, (const u4v*)src, (uint32_t)bytes, (uint32_t)span, sink); break;
-    default: return wq::fail(WQ_ERR_INVALID_ARG, "%s: ring must be 1, 2, 4, 8 or 16", who);
+    case 1: hipLaunchKernelGGL(read_probe_ring_kernel<1>, g, b, 0, s, (const u4v*)src, n, sink); break;
+    case 2: hipLaunchKernelGGL(read_probe_ring_kernel<2>, g, b, 0, s, (const u4v*)src, n, sink); break;
+    case 4: hipLaunchKernelGGL(read_probe_ring_kernel<4>, g, b, 0, s, (const u4v*)src, n, sink); break;
+    case 8: hipLaunchKernelGGL(read_probe_ring_kernel<8>, g, b, 0, s, (const u4v*)src, n, sink); break;
+    default: hipLaunchKernelGGL(read_probe_ring_kernel<16>, g, b, 0, s, (const u4v*)src, n, sink); break;
   }
   return check_launch(who);
 }

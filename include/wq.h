@@ -433,11 +433,11 @@ int wq_read_probe(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 int64_t wq_read_probe_sink_words(int64_t bytes);
 
 /* The same streaming read with a chosen launch geometry, for finding the
- * attainable rate at a given size: `blocks` workgroups of `threads` threads
- * (a multiple of 64, at most 1024); wave v reads its own run of
- * ceil(bytes / 1 KB / waves) consecutive 1 KB blocks (one 16-byte load per
- * lane each) through a ring of `ring` loads in flight per lane (1, 2, 4, 8 or
- * 16).  sink holds `blocks` uint32 words.  bytes < 4 GB. */
+ * attainable rate at a given size: a grid-stride sweep by `blocks` workgroups
+ * of `threads` threads (a multiple of 64, at most 1024), each thread with
+ * `ring` 16-byte loads in flight per round (1, 2, 4, 8 or 16); blocks == 0
+ * takes enough workgroups for one round (one-shot).  sink holds as many
+ * uint32 words as workgroups (at most 65536).  bytes < 2 GB. */
 int wq_read_probe_geom(const void* src, int64_t bytes, uint32_t* sink, int blocks, int threads,
                        int ring, void* stream);
 

@@ -809,3 +809,19 @@ def test_gemv_valu_launch_variants(fmt, lds_path, rpw, N, K, outl):
     ref, dl = build(fmt, L.W, L.profile, L.ratio)
     y, _ = run_gemv(dl, L.x, variant=var)
     check_product(ref, y, L.x, f"valu w{fmt} lds={lds_path} rpw={rpw} {N}x{K}")
+
+
+@pytest.mark.parametrize("nbytes", [4096, 26157632, 104555648])
+def test_read_probe_geometries(nbytes):
+    """The streaming-read probes the benchmark times against: every geometry it
+    uses launches, returns, and leaves the sink as it was (the probe writes a
+    word only for data that a buffer of ones cannot hold)."""
+    say(f"read probe {nbytes} B")
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(65536, dtype=torch.int32, device="cuda")
+    for blocks, threads, ring in [(0, 256, 1), (0, 256, 2), (0, 256, 4), (0, 1024, 8),
+                                  (256, 256, 1), (512, 512, 16), (4096, 64, 2)]:
+        B.wq_read_probe_geom(buf, nbytes, sink, blocks, threads, ring)
+    B.wq_read_probe(buf, nbytes, sink[:B.wq_read_probe_sink_words(nbytes)])
+    torch.cuda.synchronize()
+    assert int(sink[B.wq_read_probe_sink_words(nbytes):].abs().sum()) == 0

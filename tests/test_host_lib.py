@@ -198,6 +198,14 @@ def test_error_codes():
     assert lib.wq_gemm_wq(3, fake, fake, fake, 8, 64, None, None, 0, 1, fake, 2, fake, None) == -1
     assert lib.wq_gemv_w4(fake, fake, fake, 8, 65536 + 32, None, None, 0, 1, fake, fake, None) == -2
     assert lib.wq_read_probe(fake, 15, fake, None) == -1
+    # the geometry probe: bad thread counts, ring, sizes and grids fail before any launch
+    assert lib.wq_read_probe_geom(fake, 4096, fake, 0, 96, 1, None) == -1
+    assert lib.wq_read_probe_geom(fake, 4096, fake, 0, 256, 3, None) == -1
+    assert lib.wq_read_probe_geom(fake, 4100, fake, 0, 256, 1, None) == -1
+    assert lib.wq_read_probe_geom(fake, 1 << 31, fake, 0, 256, 1, None) == -1
+    assert lib.wq_read_probe_geom(fake, 4096, fake, -1, 256, 1, None) == -1
+    assert lib.wq_read_probe_geom(fake, (1 << 31) - 4096, fake, 0, 64, 1, None) == -1
+    assert lib.wq_read_probe_geom(fake, 4096, fake, 65536, 1024, 16, None) == -1
     assert lib.wq_embed_gather(3, fake, fake, fake, 8, 64, fake, 1, fake, None) == -1
     assert lib.wq_embed_gather(4, fake, fake, fake, 8, 40, fake, 1, fake, None) == -2
     assert lib.wq_embed_gather(4, fake, fake, fake, 8, 64, fake, -1, fake, None) == -1
