@@ -569,15 +569,16 @@ def batched_workload(a, torch, timer):
             ms = min(ms_tiled, ms_gemm)
             flops = 2.0 * M * N * K
             tfl = flops / (ms * 1e-3) / 1e12
-            roof = roofline_hbm(nbytes, ms)
+            layout = "tiled" if ms_tiled <= ms_gemm else "rowmajor"
+            roof = roofline_hbm(nbytes, ms, traffic_for(f"w4_{N}x{K}_m{M}_{layout}")
+                                if w4_fmt(a) == 4 else None)
             roof["mfma"] = {"achieved": round(tfl, 2), "peak": MFMA_FP16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(tfl / MFMA_FP16_PEAK_TFLOPS, 5)}
             out = line(f"batched M={M} W4A16 product effective HBM GB/s", round(gbs(nbytes, ms), 2),
                        "GB/s", a, ms,
                        {"workload": f"w{'4p' if w4_fmt(a) == 5 else '4'}_{N}x{K}_m{M}", "N": N,
                         "K": K, "M": M, "format": FMT_NAME[w4_fmt(a)] + " group-32",
-                        "bytes_per_step": nbytes, "rotated_copies": nc,
-                        "layout": "tiled" if ms_tiled <= ms_gemm else "rowmajor"},
+                        "bytes_per_step": nbytes, "rotated_copies": nc, "layout": layout},
                        roof,
                        tiled={"us": round(ms_tiled * 1e3, 3), "GB/s": round(gbs(nbytes, ms_tiled), 1),
                               "over_m1": round(ms_tiled / ms_m1, 3)},
