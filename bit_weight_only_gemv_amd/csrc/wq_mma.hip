@@ -1210,16 +1210,23 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
       int j_lo, nin;
       jrange(ks, j_lo, nin);
       const int lo = ks * kSliceChB;
-      if (lane < 4 * QG) mask[lane] = 0u;
-      if constexpr (!TILED)
-        for (int j = lane; j < 32; j += kWave) list[j] = -1;   // first run step padded
-      wave_lds_sync();
-      for (int j = lane; j < nin; j += kWave) {
-        const int c = s_idx[j_lo + j] - lo;   // in [0, slice) for sorted indices
-        if ((unsigned)c < (unsigned)kSliceChB) {
-          __hip_atomic_fetch_or(&mask[c >> 5], 1u << (c & 31), __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_WORKGROUP);
-          if constexpr (!TILED) list[j] = c;
+      // the bit mask serves W2 fragments loaded in the lane layout only: W4
+      // needs none (its zeroed columns reconstruct to 0), and rows staged
+      // through LDS have their outlier columns zeroed there
+      constexpr bool kMaskBits = FMT == 2 && !XT;
+      if constexpr (kMaskBits || !TILED) {
+        if (kMaskBits && lane < 4 * QG) mask[lane] = 0u;
+        if constexpr (!TILED)
+          for (int j = lane; j < 32; j += kWave) list[j] = -1;   // first run step padded
+        wave_lds_sync();
+        for (int j = lane; j < nin; j += kWave) {
+          const int c = s_idx[j_lo + j] - lo;   // in [0, slice) for sorted indices
+          if ((unsigned)c < (unsigned)kSliceChB) {
+            if constexpr (kMaskBits)
+              __hip_atomic_fetch_or(&mask[c >> 5], 1u << (c & 31), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+            if constexpr (!TILED) list[j] = c;
+          }
         }
       }
       // tiled: the activations of the slice's share of slab positions, lane
@@ -1281,12 +1288,6 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
                                   16u * (uint32_t)(lane % kXLanesPerRow)) = xbuf[t];
       }
       wave_lds_sync();
-#pragma unroll
-      for (int t = 0; t < XS; ++t)
-        xbuf[t] = (uint32_t)n16 < mpx
-                      ? *reinterpret_cast<const u4v*>(smem + xbase + (uint32_t)n16 * mmb_xt_stride(QG) +
-                                                       (uint32_t)(32 * QG * q + 8 * t) * 2u)
-                      : (u4v){0u, 0u, 0u, 0u};
       if constexpr (OUT && !TILED) {
         // the run's first 32 outlier activations from the same rows (the
         // slice's column list was written when the previous slice was entered)
@@ -1308,6 +1309,27 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) xopre[i] = hv[2 * i] | (hv[2 * i + 1] << 16);
       }
+      if constexpr (FMT == 2 && OUT) {
+        // W2 outlier columns of the slice: zero in every staged row (after the
+        // run's activations above were read from them)
+        int j_lo, nin;
+        jrange(ks, j_lo, nin);
+        const int lo = ks * kSliceChB;
+        wave_lds_sync();
+        for (int j = lane; j < nin; j += kWave) {
+          const int c = s_idx[j_lo + j] - lo;
+          if ((unsigned)c < (unsigned)kSliceChB)
+            for (uint32_t m = 0; m < mpx; ++m)
+              *reinterpret_cast<uint16_t*>(smem + xbase + m * mmb_xt_stride(QG) + (uint32_t)c * 2u) = 0;
+        }
+        wave_lds_sync();
+      }
+#pragma unroll
+      for (int t = 0; t < XS; ++t)
+        xbuf[t] = (uint32_t)n16 < mpx
+                      ? *reinterpret_cast<const u4v*>(smem + xbase + (uint32_t)n16 * mmb_xt_stride(QG) +
+                                                       (uint32_t)(32 * QG * q + 8 * t) * 2u)
+                      : (u4v){0u, 0u, 0u, 0u};
     }
     // fragments of this slice from the prefetched rows (channels past K: 0)
     uint32_t fr[XS][4];
@@ -1320,7 +1342,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         fr[t][2] = ok ? xbuf[t].z : 0u;
         fr[t][3] = ok ? xbuf[t].w : 0u;
       }
-      if constexpr (OUT) {
+      if constexpr (OUT && !XT) {
         // zero the outlier columns: bits 2i, 2i + 1 of step t's byte
         const uint32_t* mask =
             reinterpret_cast<const uint32_t*>(smem + warea0 + (uint32_t)p * kMmbWaveArea);
