@@ -132,7 +132,9 @@ class Timer:
     called through its C ABI during capture), a whole multiple of `period` (the
     number of rotated buffer copies, so that every replay walks all of them),
     replayed R times with an event on the launching stream between replays; a
-    second graph holds the steps - R per left over.  A bounded spin on the
+    second graph holds the steps - R per left over.  Before the timed replays
+    the first graph is replayed back to back for WARM_S seconds (the clocks
+    ramp down while the host prepares a workload).  A bounded spin on the
     stream (about 0.1 ms) comes first, so that the launches are queued on the
     GPU before the first event fires and the timed region holds the kernels,
     not the host's latency to submit the first of them.  One synchronization
@@ -140,6 +142,7 @@ class Timer:
 
     REPLAYS = 20
     LEAD_CYCLES = 250_000
+    WARM_S = 0.05     # graph replays before the timed ones, at least this long
 
     def __init__(self, torch, eager=False):
         self.torch, self.eager = torch, eager
@@ -176,6 +179,14 @@ class Timer:
             g_main = self._capture(fn, per)
             if rest:
                 g_rest = self._capture(fn, rest)
+            # the GPU's clocks drop while the host prepares a workload: replay
+            # the graph back to back for WARM_S first, so that the timed
+            # replays do not include the ramp
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < self.WARM_S:
+                for _ in range(4):
+                    g_main.replay()
+                torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
         torch.cuda.synchronize()
         torch.cuda._sleep(self.LEAD_CYCLES)
