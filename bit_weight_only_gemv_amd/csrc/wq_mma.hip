@@ -1333,14 +1333,27 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     }
     // fragments of this slice from the prefetched rows (channels past K: 0)
     uint32_t fr[XS][4];
+    // a slice inside K needs no selects (uniform: every lane's channels lie
+    // below (ks + 1) * slice)
+    const bool inside = (ks + 1) * kSliceChB <= a.K;
     if constexpr (FMT == 2) {
+      if (inside) {
 #pragma unroll
-      for (int t = 0; t < XS; ++t) {
-        const bool ok = ks * kSliceChB + 32 * QG * q + 8 * t < a.K;
-        fr[t][0] = ok ? xbuf[t].x : 0u;
-        fr[t][1] = ok ? xbuf[t].y : 0u;
-        fr[t][2] = ok ? xbuf[t].z : 0u;
-        fr[t][3] = ok ? xbuf[t].w : 0u;
+        for (int t = 0; t < XS; ++t) {
+          fr[t][0] = xbuf[t].x;
+          fr[t][1] = xbuf[t].y;
+          fr[t][2] = xbuf[t].z;
+          fr[t][3] = xbuf[t].w;
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < XS; ++t) {
+          const bool ok = ks * kSliceChB + 32 * QG * q + 8 * t < a.K;
+          fr[t][0] = ok ? xbuf[t].x : 0u;
+          fr[t][1] = ok ? xbuf[t].y : 0u;
+          fr[t][2] = ok ? xbuf[t].z : 0u;
+          fr[t][3] = ok ? xbuf[t].w : 0u;
+        }
       }
       if constexpr (OUT && !XT) {
         // zero the outlier columns: bits 2i, 2i + 1 of step t's byte
@@ -1363,7 +1376,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     } else {
 #pragma unroll
       for (int u = 0; u < QG; ++u) {
-        const bool ok = ks * kSliceGroupsB + QG * q + u < G;
+        const bool ok = inside || ks * kSliceGroupsB + QG * q + u < G;
         uint32_t gv[16];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -1443,14 +1456,18 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
 #pragma unroll
       for (int u = 0; u < QG; ++u) {
         const uint32_t sp = (u & 1) ? splat_hi(svw[u >> 1]) : splat_lo(svw[u >> 1]);
-        // -(1024 + z) in both halves: the zero is an exact small integer
-        uint32_t nz;
-        if constexpr (FMT == 5) {   // FP16 -(1024 + z) = 0xE400 | z for z in 0..15
-          nz = splat_lo(0xE400u | ((zvw[0] >> (4 * u)) & 0x0Fu));
+        // -(1024 + z) and -(64 + z) in both halves: exact in FP16
+        uint32_t nz, nz64;
+        if constexpr (FMT == 5) {   // FP16 -(1024 + z) = 0xE400 | z, -(64 + z) = 0xD400 | 16 z
+          const uint32_t z = (zvw[0] >> (4 * u)) & 0x0Fu;
+          nz = splat_lo(0xE400u | z);
+          nz64 = splat_lo(0xD400u | (z << 4));
         } else {
           const _Float16 zf = __builtin_bit_cast(_Float16, (uint16_t)(zvw[u >> 1] >> (16 * (u & 1))));
           nz = splat_lo((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(-1024.0f16 - zf)));
+          nz64 = splat_lo((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(-64.0f16 - zf)));
         }
+        const h2 sixteenth = {0.0625f16, 0.0625f16};
         const uint32_t d[4] = {it.cw[u].x, it.cw[u].y, it.cw[u].z, it.cw[u].w};
         uint32_t b[4][4];
         // the FP16 exponent of 1024 held in a register, so that mask and OR
@@ -1459,15 +1476,22 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         asm volatile("" : "+v"(magic));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          // low nibbles: 1024 + q; high nibbles masked in place: 1024 + 16 q
+          // (exact below 2048), which saves their shifts
+          const uint32_t d8 = d[i] >> 8;
           const uint32_t v0 = (d[i] & 0x000F000Fu) | magic;
-          const uint32_t v1 = ((d[i] >> 4) & 0x000F000Fu) | magic;
-          const uint32_t v2 = ((d[i] >> 8) & 0x000F000Fu) | magic;
-          const uint32_t v3 = ((d[i] >> 12) & 0x000F000Fu) | magic;
+          const uint32_t v1 = (d[i] & 0x00F000F0u) | magic;
+          const uint32_t v2 = (d8 & 0x000F000Fu) | magic;
+          const uint32_t v3 = (d8 & 0x00F000F0u) | magic;
           const uint32_t vv[4] = {v0, v1, v2, v3};
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const h2 qz = as_h2(vv[t]) + as_h2(nz);   // exact q - z
-            b[t][i] = as_u32(qz * as_h2(sp));         // one rounding: w_hat
+            // exact q - z: (1024 + q) - (1024 + z), or for the high nibbles
+            // (1024 + 16 q) / 16 - (64 + z) in one fused step (the product is
+            // exact, and so is the sum); then one rounding: w_hat
+            const h2 qz = (t & 1) ? __builtin_elementwise_fma(as_h2(vv[t]), sixteenth, as_h2(nz64))
+                                  : as_h2(vv[t]) + as_h2(nz);
+            b[t][i] = as_u32(qz * as_h2(sp));
           }
         }
 #pragma unroll
