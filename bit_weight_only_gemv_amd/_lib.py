@@ -87,7 +87,7 @@ SIGNATURES = {
 # Fields of wq_variant (include/wq.h, "kernel-variant selection"), in order.
 VARIANT_FIELDS = ("gemv_kernel", "gemv_rows_per_wave", "gemv_lds_x", "gemm_kernel", "gemm_rows",
                   "batch_slice_groups", "batch_row_transpose", "refine_groups", "refine_fuse",
-                  "refine_wide")
+                  "refine_wide", "batch_register_partials")
 
 
 class Variant(ctypes.Structure):

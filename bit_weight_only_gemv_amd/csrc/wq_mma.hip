@@ -914,8 +914,12 @@ struct MmbLds {
 __host__ __device__ constexpr uint32_t mmb_xt_stride(int qg) { return 256u * qg + 16u; }
 // With outliers also: the run table (slice ks's run of the sorted indices
 // starts at runs[ks], nks + 1 words) and a copy of the indices (256 iv words).
+// preg: the partial tiles are kept in registers while the weights stream and
+// written at the end into the staged-rows area (free by then), so the layout
+// has no separate region for them.
 __host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl, int qg, int nks,
-                                                 int iv, bool xt = false, bool tiled = false) {
+                                                 int iv, bool xt = false, bool tiled = false,
+                                                 bool preg = false) {
   MmbLds L{};
   uint32_t off = 0;
   L.lut = off;
@@ -927,9 +931,10 @@ __host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl
   L.idx = off;
   off += (uint32_t)iv * 1024u;
   L.part = off;
-  off += (uint32_t)rbl * (uint32_t)nw * (uint32_t)((M + 3) & ~3) * 64u;
+  if (!preg) off += (uint32_t)rbl * (uint32_t)nw * (uint32_t)((M + 3) & ~3) * 64u;
   L.xt = off;
   if (xt) off += (uint32_t)nw * (uint32_t)((M + 3) & ~3) * mmb_xt_stride(qg);
+  if (preg) L.part = L.xt;
   L.total = off;
   return L;
 }
@@ -952,10 +957,15 @@ __device__ __forceinline__ uint32_t splat_hi(uint32_t v) { return __builtin_amdg
 // chunks C(ks) .. C(ks + 1) - 1 of 8 positions (at most 4), lane quarter q
 // takes chunk C(ks) + q, and its activations are gathered per slice through
 // the index copy in LDS; the chunks are zero-padded, so no alignment or mask.
-template <int FMT, int IV, int DEPTH, int QG, bool XT, bool TILED = false>
+// PREG: each wave's partial tiles in registers (at most kPregMax row blocks
+// per workgroup), added in the same order as the LDS tiles would be, so the
+// results are the same bits; they reach LDS once, at the end.
+constexpr int kPregMax = 8;
+template <int FMT, int IV, int DEPTH, int QG, bool XT, bool TILED = false, bool PREG = false>
 __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   typedef MmbFmt<FMT, QG> F;
   static_assert(!TILED || QG == 4, "the tiled layout has 512-channel slices");
+  static_assert(!PREG || XT, "register partials reuse the staged-rows area at the end");
   constexpr int kSliceChB = F::kSliceCh;
   constexpr int kSliceGroupsB = F::kSliceGroups;
   constexpr int XS = F::kSteps;
@@ -963,7 +973,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   constexpr bool OUT = IV > 0;
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_out = OUT ? a.n_out : 0;
-  const MmbLds L = mmb_lds_layout(FMT, a.M, a.nw, a.rbl, QG, a.nks, IV, XT, TILED);
+  const MmbLds L = mmb_lds_layout(FMT, a.M, a.nw, a.rbl, QG, a.nks, IV, XT, TILED, PREG);
   uint32_t* s_runs = reinterpret_cast<uint32_t*>(smem + L.runs);
   const int32_t* s_idx = reinterpret_cast<const int32_t*>(smem + L.idx);
   const int tid = threadIdx.x;
@@ -1435,13 +1445,23 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     return s_part + (((uint32_t)ri * (uint32_t)a.nw + (uint32_t)w) * Mp + (uint32_t)(4 * q + jj)) *
                         16u + (uint32_t)n16;
   };
-  if (qrows)
+  f4 pacc[PREG ? kPregMax : 1];
+#pragma unroll
+  for (int r = 0; r < (PREG ? kPregMax : 1); ++r) pacc[r] = (f4){0.f, 0.f, 0.f, 0.f};
+  if (!PREG && qrows)
     for (int ri = 0; ri < nrb_wg; ++ri)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) *part_at(ri, jj) = 0.f;
   auto add_tile = [&](const f4& c, int ri, int si) {
     (void)si;
-    if (qrows) {
+    if constexpr (PREG) {   // ri is wave-uniform: one of these adds runs
+#pragma unroll
+      for (int r = 0; r < kPregMax; ++r)
+        if (r == ri) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) pacc[r][jj] += c[jj];
+        }
+    } else if (qrows) {
       float old[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) old[jj] = *part_at(ri, jj);
@@ -1609,7 +1629,19 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     }
   }
 
-  // ---- fixed-order sum of the waves' tiles
+  // ---- fixed-order sum of the waves' tiles (register partials: written
+  //      into the staged-rows area once every wave is done with it)
+  if constexpr (PREG) {
+    __syncthreads();
+    if (qrows) {
+#pragma unroll
+      for (int r = 0; r < kPregMax; ++r)
+        if (r < nrb_wg) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) *part_at(r, jj) = pacc[r][jj];
+        }
+    }
+  }
   __syncthreads();
   for (int t = tid; t < nrb_wg * a.M * 16; t += nthr) {
     const int n = t & 15, m = (t >> 4) % a.M, ri2 = (t >> 4) / a.M;
@@ -1684,7 +1716,7 @@ static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_ou
 
 
 struct MmbPlan {
-  bool ok, xt;
+  bool ok, xt, preg;
   int nw, nks, nrb, grid, rbl, iv, depth, qg;
   size_t lds;
 };
@@ -1749,6 +1781,20 @@ static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M,
       mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv, true, tiled).total;
   p.xt = lds_xt <= kMaxLdsBytes && want_xt;
   if (p.xt) p.lds = lds_xt;
+  // Partial tiles in registers (a workgroup with at most kPregMax row blocks)
+  // leave room for the staged rows where the LDS tiles would not.  Measured on
+  // MI355X, the library takes them only then: W2 28672 x 8192 at M = 8 33.2 ->
+  // 27.4 us, W4 14336 x 4096 at M = 16 14.1 -> 13.6 us; where the rows fit
+  // anyway the per-item register select is slower (W4 14336 x 4096 at M = 8,
+  // 11.8 -> 12.7 us).  An explicit variant may ask for them wherever they fit.
+  const int preg = variant_or(v, &wq_variant::batch_register_partials, -1);
+  const size_t lds_preg =
+      mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv, true, tiled, true).total;
+  if (want_xt && preg != 0 && (preg == 1 || !p.xt) && p.rbl <= kPregMax &&
+      lds_preg <= kMaxLdsBytes) {
+    p.xt = p.preg = true;
+    p.lds = lds_preg;
+  }
   p.depth = 2;
   p.ok = true;
   return p;
@@ -1960,14 +2006,16 @@ int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
   a.nrb = p.nrb;
   a.rbl = p.rbl;
   const dim3 grid(p.grid), block(p.nw * kWave);
-#define WQ_MMB_LAUNCH_X(F_, IV_, Q_, X_)                                                     \
-  if (fmt == F_ && p.iv == IV_ && p.qg == Q_ && p.xt == X_) {                                \
-    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, Q_, X_>), p.lds))  \
+#define WQ_MMB_LAUNCH_XP(F_, IV_, Q_, X_, P_)                                                 \
+  if (fmt == F_ && p.iv == IV_ && p.qg == Q_ && p.xt == X_ && p.preg == P_) {               \
+    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, Q_, X_, false, P_>), \
+                   p.lds))                                                                    \
       return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds); \
-    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, Q_, X_>), grid, block, p.lds, stream, a);     \
+    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, Q_, X_, false, P_>), grid, block, p.lds, stream, a); \
     *launched = true;                                                                        \
     return check_launch(who);                                                                \
   }
+#define WQ_MMB_LAUNCH_X(F_, IV_, Q_, X_) WQ_MMB_LAUNCH_XP(F_, IV_, Q_, X_, false) WQ_MMB_LAUNCH_XP(F_, IV_, Q_, X_, X_)
 #define WQ_MMB_LAUNCH(F_, IV_) WQ_MMB_LAUNCH_X(F_, IV_, 2, false) WQ_MMB_LAUNCH_X(F_, IV_, 2, true)
   WQ_MMB_LAUNCH_X(4, 0, 4, false) WQ_MMB_LAUNCH_X(2, 0, 4, false) WQ_MMB_LAUNCH_X(5, 0, 4, false)
   WQ_MMB_LAUNCH_X(4, 0, 4, true) WQ_MMB_LAUNCH_X(2, 0, 4, true) WQ_MMB_LAUNCH_X(5, 0, 4, true)
@@ -1975,6 +2023,7 @@ int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
   WQ_MMB_LAUNCH(2, 0) WQ_MMB_LAUNCH(2, 1) WQ_MMB_LAUNCH(2, 2) WQ_MMB_LAUNCH(2, 4)
   WQ_MMB_LAUNCH(5, 0) WQ_MMB_LAUNCH(5, 1) WQ_MMB_LAUNCH(5, 2) WQ_MMB_LAUNCH(5, 4)
 #undef WQ_MMB_LAUNCH_X
+#undef WQ_MMB_LAUNCH_XP
 #undef WQ_MMB_LAUNCH
   return WQ_OK;
 }
@@ -2005,19 +2054,21 @@ int wqd_gemm_mma_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
   a.rbl = p.rbl;
   a.nch = (int)g.nch;
   const dim3 grid(p.grid), block(p.nw * kWave);
-#define WQ_MMT_LAUNCH_X(F_, IV_, X_)                                                          \
-  if (fmt == F_ && p.iv == IV_ && p.xt == X_) {                                               \
-    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, 4, X_, true>), p.lds)) \
+#define WQ_MMT_LAUNCH_XP(F_, IV_, X_, P_)                                                      \
+  if (fmt == F_ && p.iv == IV_ && p.xt == X_ && p.preg == P_) {                               \
+    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, 4, X_, true, P_>), p.lds)) \
       return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds);  \
-    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, 4, X_, true>), grid, block, p.lds, stream, a);  \
+    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, 4, X_, true, P_>), grid, block, p.lds, stream, a);  \
     *launched = true;                                                                         \
     return check_launch(who);                                                                 \
   }
+#define WQ_MMT_LAUNCH_X(F_, IV_, X_) WQ_MMT_LAUNCH_XP(F_, IV_, X_, false) WQ_MMT_LAUNCH_XP(F_, IV_, X_, X_)
 #define WQ_MMT_LAUNCH(F_, IV_) WQ_MMT_LAUNCH_X(F_, IV_, false) WQ_MMT_LAUNCH_X(F_, IV_, true)
   WQ_MMT_LAUNCH(4, 0) WQ_MMT_LAUNCH(4, 1) WQ_MMT_LAUNCH(4, 2) WQ_MMT_LAUNCH(4, 4)
   WQ_MMT_LAUNCH(2, 0) WQ_MMT_LAUNCH(2, 1) WQ_MMT_LAUNCH(2, 2) WQ_MMT_LAUNCH(2, 4)
   WQ_MMT_LAUNCH(5, 0) WQ_MMT_LAUNCH(5, 1) WQ_MMT_LAUNCH(5, 2) WQ_MMT_LAUNCH(5, 4)
 #undef WQ_MMT_LAUNCH_X
+#undef WQ_MMT_LAUNCH_XP
 #undef WQ_MMT_LAUNCH
   return WQ_OK;
 }

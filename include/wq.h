@@ -398,6 +398,11 @@ typedef struct wq_variant {
    * the library would take 16 */
   int32_t refine_fuse;
   int32_t refine_wide;
+  /* persistent batched kernel: 0 keeps each wave's partial tiles in LDS, 1
+   * in registers wherever a workgroup has at most 8 row blocks (the same
+   * bits); the library's choice takes registers only where that leaves room
+   * for the staged activation rows */
+  int32_t batch_register_partials;
 } wq_variant;
 
 int wq_gemv_v(int fmt, const uint8_t* codes, const uint16_t* scales, const uint16_t* zeros,

@@ -358,6 +358,38 @@ def test_gemm_row_transpose(fmt, M, N, K, outl, qg):
     check_product(ref, torch.from_numpy(ys[0]), L.x, f"gemm w{fmt} M={M} {N}x{K} row transpose")
 
 
+@pytest.mark.parametrize("fmt", [4, 2, 5])
+@pytest.mark.parametrize("M", [3, 8, 16])
+@pytest.mark.parametrize("N,K,outl", [(129, 4096, True), (5000, 2048, False), (20000, 512, True),
+                                      (33000, 256, False)])
+def test_gemm_register_partials(fmt, M, N, K, outl):
+    """The batched kernel with each wave's partial tiles in registers
+    (batch_register_partials 1, where a workgroup has at most 8 row blocks)
+    or in LDS (0): the same additions in the same order, so bit-identical Y
+    on both layouts, within the bound; 1, 2, 5 and 9 row blocks per
+    workgroup (the last keeps the LDS tiles)."""
+    say(f"gemm register partials fmt={fmt} M={M} N={N} K={K} outliers={outl}")
+    L = synthetic.small_layer(fmt, N, K, M=M, with_outliers=outl, seed=M + N + 2)
+    ref = O.quantize_layer(fmt, L.W, L.profile if outl else None, L.ratio if outl else 0.0)
+    dl = DeviceLayer(pack_host(fmt, L.W, L.profile if outl else None, L.ratio if outl else 0.0),
+                     tiled=True)
+    X = dev_fp16(L.x)
+    for layout in ("rowmajor", "tiled"):
+        ys = []
+        for pr in (1, 0):
+            Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
+            v = B.variant(gemm_kernel=2, gemm_rows=0, batch_register_partials=pr)
+            if layout == "tiled":
+                dl.gemm_tiled(X, Y, variant=v)
+            else:
+                dl.gemm(X, Y, variant=v)
+            torch.cuda.synchronize()
+            ys.append(Y.cpu().numpy())
+        assert np.array_equal(ys[0], ys[1]), layout
+        check_product(ref, torch.from_numpy(ys[0]), L.x,
+                      f"gemm w{fmt} M={M} {N}x{K} register partials {layout}")
+
+
 # ------------------------------------------------------- full-size layers
 
 
