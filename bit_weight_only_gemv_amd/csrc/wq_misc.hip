@@ -90,29 +90,74 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict_
 
 // --------------------------------------------------- embedding row gather
 // SPECTRA section 4.3: only the rows of the token ids in the batch are read
-// and dequantized, straight into the FP16 output rows; the same per-group
-// arithmetic as the dequantization above, so the rows are bit-identical to
-// it.  One thread per (token, group); an id outside [0, V) gives a zero row.
+// and dequantized, straight into the FP16 output rows, with the per-element
+// arithmetic of the dequantization above (the same expressions, so the rows
+// are bit-identical to it).  One thread per (token, group, quarter): lane l
+// of a wave writes the 16 bytes that follow lane l - 1's, so every store
+// instruction covers one contiguous kilobyte of output (one thread per group,
+// four 16-byte stores 64 bytes apart per lane, was 5% slower).  Quarter u holds the
+// group's channels 8u .. 8u + 7:
+//   W4: the low nibbles (u < 2) or high nibbles (u >= 2) of the group's bytes
+//       8 (u % 2) .. + 7 (byte i holds channel i low, channel i + 16 high);
+//   W2: the group's bytes 2u and 2u + 1 (byte i holds channels 4i .. 4i + 3,
+//       two bits each from bit 0).
+// An id outside [0, V) gives a zero row.
+template <int FMT>
+__device__ __forceinline__ u4v dequant_quarter(const uint8_t* __restrict__ codes,
+                                               const uint16_t* __restrict__ scales,
+                                               const uint16_t* __restrict__ zeros, int64_t n,
+                                               int64_t g, int u, int64_t K) {
+  const int64_t G = K / kGroup;
+  const float s = h2f(scales[n * G + g]);
+  float z;
+  if constexpr (FMT == 5) {
+    const uint8_t* zp = reinterpret_cast<const uint8_t*>(zeros) + n * ((G + 1) / 2);
+    z = (float)((zp[g >> 1] >> (4 * (g & 1))) & 0x0Fu);
+  } else {
+    z = h2f(zeros[n * G + g]);
+  }
+  uint16_t w[8];
+  if constexpr (FMT == 4 || FMT == 5) {
+    const u2 c = *reinterpret_cast<const u2*>(codes + n * (K / 2) + g * 16 + 8 * (u & 1));
+    const bool hi = u >= 2;
+    const float zlo = 1024.0f + z, zhi = 1024.0f + 16.0f * z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t byte = ((i < 4 ? c.x : c.y) >> (8 * (i & 3))) & 0xFFu;
+      // the decoder's FP16 value: 1024 + q (low nibble) or 1024 + 16 q (high)
+      if (hi)
+        w[i] = f2h(((float)(1024u + (byte & 0xF0u)) - zhi) * 0.0625f * s);
+      else
+        w[i] = f2h(((float)(1024u + (byte & 0x0Fu)) - zlo) * s);
+    }
+  } else {
+    const uint32_t c = *reinterpret_cast<const uint16_t*>(codes + n * (K / 4) + g * 8 + 2 * u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const h2 cp = as_h2(w2_centroid_pair((c >> (2 * i)) & 3u));
+      w[i] = f2h(__builtin_fmaf(s, (float)cp[0], z));
+    }
+  }
+  return (u4v){pack2(w[0], w[1]), pack2(w[2], w[3]), pack2(w[4], w[5]), pack2(w[6], w[7])};
+}
+
 template <int FMT>
 __global__ void __launch_bounds__(256) embed_kernel(const uint8_t* __restrict__ codes,
                                                     const uint16_t* __restrict__ scales,
                                                     const uint16_t* __restrict__ zeros, int64_t V,
                                                     int64_t K, const int32_t* __restrict__ ids,
                                                     int64_t n_ids, uint16_t* __restrict__ out) {
-  const int64_t G = K / kGroup;
-  const int64_t items = n_ids * G;
+  const int64_t Q = K / 8;   // quarters of groups per row
+  const int64_t items = n_ids * Q;
   for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items;
        it += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t t = it / G, g = it % G;
+    const int64_t t = it / Q, e = it % Q;
     const int64_t n = ids[t];
-    uint16_t* row = out + t * K;
-    if (n >= 0 && n < V) {
-      dequant_group<FMT>(codes, scales, zeros, n, g, K, row);
-    } else {
-      u4v* dst = reinterpret_cast<u4v*>(row + g * 32);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) dst[v] = (u4v){0u, 0u, 0u, 0u};
-    }
+    u4v v = {0u, 0u, 0u, 0u};
+    if (n >= 0 && n < V) v = dequant_quarter<FMT>(codes, scales, zeros, n, e >> 2, (int)(e & 3), K);
+    // streaming store: the output rows are not read again by this kernel
+    // (measured on MI355X: 4096 rows of 4096, 15.1 -> 13.8 us)
+    __builtin_nontemporal_store(v, reinterpret_cast<u4v*>(out + t * K + 8 * e));
   }
 }
 
@@ -266,7 +311,7 @@ extern "C" int wq_embed_gather(int fmt, const uint8_t* codes, const uint16_t* sc
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: NULL pointer", who);
   if (!aligned16(codes) || !aligned16(out))
     return wq::fail(WQ_ERR_INVALID_ARG, "%s: device pointers must be 16-byte aligned", who);
-  const int64_t items = n_ids * (K / kGroup);
+  const int64_t items = n_ids * (K / 8);
   int64_t blocks = (items + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipStream_t s = (hipStream_t)stream;
