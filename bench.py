@@ -502,11 +502,14 @@ def sweep_workload(a, torch, timer):
                 t[lay] = timer(run, 5, 2)
             pick[g] = min(t, key=t.get)
         calls = []
+        reads = []   # the buffer each GEMV streams (its tiled copy: codes and metadata)
         for li in range(nlayers):
             for g in groups:
                 d = layers[g][li]
                 calls.append((d.gemv_tiled if pick[g] == "tiled" else d.gemv, xs[g], ys[g]))
+                reads.append(d.tiled)
         calls.append((head_layer.gemv_tiled if pick["head"] == "tiled" else head_layer.gemv, xh, yh))
+        reads.append(head_layer.tiled)
         total = sum(layers[g][0].nbytes(1) for g in groups) * nlayers + head_layer.nbytes(1)
 
         def step(i, calls=calls):
@@ -518,7 +521,31 @@ def sweep_workload(a, torch, timer):
                       "tokens_per_s": round(1e3 / ms, 1), "bytes_per_token": total,
                       "GB/s": round(gbs(total, ms), 1), "timing_us": ms.us(), "ms": ms,
                       "layouts": {("|".join(g) if g != "head" else g): pick[g] for g in pick}}
-        del layers, calls
+        if label == "fused":
+            # The same launch sequence with each GEMV replaced by the one-shot
+            # read kernel over that GEMV's weight buffer: the rate a step of
+            # these launches reaches when it only streams the bytes.
+            import bit_weight_only_gemv_amd as B
+            sink = torch.empty(65536, dtype=torch.int32, device="cuda")
+            blocks, threads, ring = ATTAINABLE_GEOMETRIES[0]
+
+            def read_step(i, reads=reads):
+                for buf in reads:
+                    nb = buf.numel() // 16 * 16
+                    # one-shot up to 65536 workgroups (268 MB); past that the
+                    # same kernel strides over the buffer with 65536
+                    bl = blocks if nb <= 65536 * threads * 16 * ring else 65536
+                    B.wq_read_probe_geom(buf, nb, sink, bl, threads, ring)
+
+            ms_r = timer(read_step, steps, min(a.warmup, 5))
+            rbytes = sum(buf.numel() // 16 * 16 for buf in reads)
+            res[label]["read_step"] = {
+                "ms_per_token": round(ms_r, 4), "tokens_per_s": round(1e3 / ms_r, 1),
+                "bytes_per_token": rbytes, "GB/s": round(gbs(rbytes, ms_r), 1),
+                "about": "the same launch sequence, each GEMV replaced by the one-shot read kernel "
+                         "over its tiled weight buffer (256-thread workgroups, one load in flight "
+                         "per lane; the 328 MB LM head strided over 65536 workgroups)"}
+        del layers, calls, reads
         torch.cuda.synchronize()
     best = res["fused"]
     ms = best.pop("ms")
@@ -534,7 +561,10 @@ def sweep_workload(a, torch, timer):
                 "unit": "tokens/s", "frac": round(tps / roof_tps, 4),
                 "achieved_GB/s": best["GB/s"], "peak_GB/s": HBM_PEAK_GBS, "traffic": None},
                steps_timed=steps, fused=best, unfused=res["unfused"],
-               pct_of_hbm_peak=round(100 * best["GB/s"] / HBM_PEAK_GBS, 2))
+               pct_of_hbm_peak=round(100 * best["GB/s"] / HBM_PEAK_GBS, 2),
+               attainable={"read_step_tokens_per_s": best["read_step"]["tokens_per_s"],
+                           "pct_of_read_step": round(100 * tps / best["read_step"]["tokens_per_s"], 2),
+                           "about": best["read_step"]["about"]})
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = sweep_cpu_baseline(w4_fmt(a), best["bytes_per_token"])
     return out
