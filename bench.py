@@ -645,6 +645,7 @@ def w2_70b_workload(a, torch, timer):
         L8 = synthetic.config5(N, K, 8)
         base = DeviceLayer(pack_host(2, L8.W, L8.profile, L8.ratio), tiled=True)
         cpu = {}
+        att = attainable_read(torch, timer, base.nbytes(1), st, wu)
         for M, layout in ((1, "rowmajor"), (1, "tiled"), (8, "rowmajor"), (8, "tiled")):
             nbytes = base.nbytes(M)
             layers = rotated(DeviceLayer, base, nbytes)
@@ -666,7 +667,13 @@ def w2_70b_workload(a, torch, timer):
                         "n_out": base.n_out, "format": "W2 group-32", "layout": layout,
                         "bytes_per_step": nbytes, "rotated_copies": nc},
                        roofline_hbm(nbytes, ms, traffic_for(f"w2_{N}x{K}_m{M}_{layout}")),
-                       pct_of_hbm_peak=round(100 * g / HBM_PEAK_GBS, 2))
+                       pct_of_hbm_peak=round(100 * g / HBM_PEAK_GBS, 2),
+                       attainable={"read_probe_GB/s": round(att[0], 1),
+                                   "pct_of_read_probe": round(100 * g / att[0], 2),
+                                   "read_probe_geometry": att[1],
+                                   "about": "the best of the one-shot read kernels over the layer's "
+                                            "M = 1 bytes per launch, rotated and graph-replayed in "
+                                            "the same run"})
             if not a.no_cpu_baseline:
                 if M not in cpu:
                     cpu[M] = cpu_baseline_rows(2, L8.W, L8.profile, L8.ratio, L8.x[:M], 2048,
