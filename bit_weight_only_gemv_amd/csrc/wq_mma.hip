@@ -966,12 +966,16 @@ __device__ __forceinline__ uint32_t splat_hi(uint32_t v) { return __builtin_amdg
 // PREG: each wave's partial tiles in registers (at most kPregMax row blocks
 // per workgroup), added in the same order as the LDS tiles would be, so the
 // results are the same bits; they reach LDS once, at the end.
+// R8 (with XT): at most 8 activation rows, so the loads of staged rows 8..15
+// are not issued (they would read zeros).
 constexpr int kPregMax = 8;
-template <int FMT, int IV, int DEPTH, int QG, bool XT, bool TILED = false, bool PREG = false>
+template <int FMT, int IV, int DEPTH, int QG, bool XT, bool TILED = false, bool PREG = false,
+          bool R8 = false>
 __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   typedef MmbFmt<FMT, QG> F;
   static_assert(!TILED || QG == 4, "the tiled layout has 512-channel slices");
   static_assert(!PREG || XT, "register partials reuse the staged-rows area at the end");
+  static_assert(!R8 || XT, "R8 limits the staged rows");
   constexpr int kSliceChB = F::kSliceCh;
   constexpr int kSliceGroupsB = F::kSliceGroups;
   constexpr int XS = F::kSteps;
@@ -1041,7 +1045,10 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
 #pragma unroll
       for (int t = 0; t < XS; ++t) {
         const uint32_t row = (uint32_t)(t * kXRowsPerLoad + lane / kXLanesPerRow);
-        xv[t] = ld128(xrs, (row * (uint32_t)a.K + c) * 2u);
+        if (R8 && t * kXRowsPerLoad >= 8)   // a constant once unrolled: not issued
+          xv[t] = (u4v){0u, 0u, 0u, 0u};
+        else
+          xv[t] = ld128(xrs, (row * (uint32_t)a.K + c) * 2u);
       }
     } else {
       const uint32_t rowoff = (uint32_t)n16 * (uint32_t)a.K;
@@ -2012,15 +2019,21 @@ int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
   a.nrb = p.nrb;
   a.rbl = p.rbl;
   const dim3 grid(p.grid), block(p.nw * kWave);
-#define WQ_MMB_LAUNCH_XP(F_, IV_, Q_, X_, P_)                                                 \
-  if (fmt == F_ && p.iv == IV_ && p.qg == Q_ && p.xt == X_ && p.preg == P_) {               \
-    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, Q_, X_, false, P_>), \
-                   p.lds))                                                                    \
-      return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds); \
-    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, Q_, X_, false, P_>), grid, block, p.lds, stream, a); \
-    *launched = true;                                                                        \
-    return check_launch(who);                                                                \
+  // staged rows: at most 8 for M <= 8 (W4 / W4P; measured on MI355X: the W2
+  // kernels on the row-major arrays are no faster with it)
+  const bool r8 = p.xt && M <= 8 && fmt != 2;
+#define WQ_MMB_LAUNCH_XPR(F_, IV_, Q_, X_, P_, R_)                                               \
+  if (fmt == F_ && p.iv == IV_ && p.qg == Q_ && p.xt == X_ && p.preg == P_ && r8 == R_) {     \
+    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, Q_, X_, false, P_, R_>), \
+                   p.lds))                                                                       \
+      return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds);    \
+    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, Q_, X_, false, P_, R_>), grid, block, p.lds, stream, \
+                       a);                                                                       \
+    *launched = true;                                                                           \
+    return check_launch(who);                                                                   \
   }
+#define WQ_MMB_LAUNCH_XP(F_, IV_, Q_, X_, P_) \
+  WQ_MMB_LAUNCH_XPR(F_, IV_, Q_, X_, P_, false) WQ_MMB_LAUNCH_XPR(F_, IV_, Q_, X_, P_, (X_ && F_ != 2))
 #define WQ_MMB_LAUNCH_X(F_, IV_, Q_, X_) WQ_MMB_LAUNCH_XP(F_, IV_, Q_, X_, false) WQ_MMB_LAUNCH_XP(F_, IV_, Q_, X_, X_)
 #define WQ_MMB_LAUNCH(F_, IV_) WQ_MMB_LAUNCH_X(F_, IV_, 2, false) WQ_MMB_LAUNCH_X(F_, IV_, 2, true)
   WQ_MMB_LAUNCH_X(4, 0, 4, false) WQ_MMB_LAUNCH_X(2, 0, 4, false) WQ_MMB_LAUNCH_X(5, 0, 4, false)
@@ -2030,6 +2043,7 @@ int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
   WQ_MMB_LAUNCH(5, 0) WQ_MMB_LAUNCH(5, 1) WQ_MMB_LAUNCH(5, 2) WQ_MMB_LAUNCH(5, 4)
 #undef WQ_MMB_LAUNCH_X
 #undef WQ_MMB_LAUNCH_XP
+#undef WQ_MMB_LAUNCH_XPR
 #undef WQ_MMB_LAUNCH
   return WQ_OK;
 }
@@ -2060,14 +2074,22 @@ int wqd_gemm_mma_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
   a.rbl = p.rbl;
   a.nch = (int)g.nch;
   const dim3 grid(p.grid), block(p.nw * kWave);
-#define WQ_MMT_LAUNCH_XP(F_, IV_, X_, P_)                                                      \
-  if (fmt == F_ && p.iv == IV_ && p.xt == X_ && p.preg == P_) {                               \
-    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, 4, X_, true, P_>), p.lds)) \
-      return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds);  \
-    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, 4, X_, true, P_>), grid, block, p.lds, stream, a);  \
-    *launched = true;                                                                         \
-    return check_launch(who);                                                                 \
+  // staged rows: at most 8 for M <= 8 (measured on MI355X: W2 8192 x 28672 +
+  // 1003 outliers at M = 8 38.0 -> 36.1 us, W4 14336 x 4096 11.86 -> 11.46 us;
+  // not with the W2 register partials, whose registers would spill)
+  const bool r8 = p.xt && M <= 8 && (fmt != 2 || !p.preg);
+#define WQ_MMT_LAUNCH_XPR(F_, IV_, X_, P_, R_)                                                    \
+  if (fmt == F_ && p.iv == IV_ && p.xt == X_ && p.preg == P_ && r8 == R_) {                      \
+    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, 4, X_, true, P_, R_>),  \
+                   p.lds))                                                                       \
+      return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds);    \
+    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, 4, X_, true, P_, R_>), grid, block, p.lds, stream, \
+                       a);                                                                       \
+    *launched = true;                                                                           \
+    return check_launch(who);                                                                   \
   }
+#define WQ_MMT_LAUNCH_XP(F_, IV_, X_, P_) \
+  WQ_MMT_LAUNCH_XPR(F_, IV_, X_, P_, false) WQ_MMT_LAUNCH_XPR(F_, IV_, X_, P_, (X_ && (F_ != 2 || !P_)))
 #define WQ_MMT_LAUNCH_X(F_, IV_, X_) WQ_MMT_LAUNCH_XP(F_, IV_, X_, false) WQ_MMT_LAUNCH_XP(F_, IV_, X_, X_)
 #define WQ_MMT_LAUNCH(F_, IV_) WQ_MMT_LAUNCH_X(F_, IV_, false) WQ_MMT_LAUNCH_X(F_, IV_, true)
   WQ_MMT_LAUNCH(4, 0) WQ_MMT_LAUNCH(4, 1) WQ_MMT_LAUNCH(4, 2) WQ_MMT_LAUNCH(4, 4)
@@ -2075,6 +2097,7 @@ int wqd_gemm_mma_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
   WQ_MMT_LAUNCH(5, 0) WQ_MMT_LAUNCH(5, 1) WQ_MMT_LAUNCH(5, 2) WQ_MMT_LAUNCH(5, 4)
 #undef WQ_MMT_LAUNCH_X
 #undef WQ_MMT_LAUNCH_XP
+#undef WQ_MMT_LAUNCH_XPR
 #undef WQ_MMT_LAUNCH
   return WQ_OK;
 }
