@@ -1223,7 +1223,15 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   // ---- per-slice activation work: outlier-column mask and run list in this
   //      wave's LDS area (parity p), then the run's outlier activations
   const uint32_t warea0 = L.wave + (uint32_t)w * 2u * kMmbWaveArea;
-  uint32_t xopre[4] = {0u, 0u, 0u, 0u};
+  // The next slice's outlier activations: per position the aligned 4-byte
+  // word that holds the FP16 value, and in bit e of xhalf which half of word
+  // e it is.  A global gather is issued when the previous slice is entered
+  // and its words are first read when their slice is entered: as whole
+  // loaded registers (no 16-bit zero extension, no copy into the loop's
+  // registers) they make the wave wait neither for them nor, as loads
+  // complete in order, for every load issued before them.
+  uint32_t xopre[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  uint32_t xhalf = 0u;
   auto prep_slice = [&](int ks, int p) {
     if constexpr (OUT) {
       uint32_t* mask = reinterpret_cast<uint32_t*>(smem + warea0 + (uint32_t)p * kMmbWaveArea);
@@ -1257,17 +1265,17 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
       if constexpr (TILED) {
         const uint32_t c0 = chunk_lo(ks);
         const uint32_t send = min(8u * chunk_lo(ks + 1), (uint32_t)n_out);
-        uint32_t hv[8];
+        const uint32_t jmax = (uint32_t)IV * 256u - 1u;   // the LDS copy's last entry
+        xhalf = 0u;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 8; ++e) {   // past the share: read at kOob, which gives 0
           const uint32_t j = 8u * (c0 + (uint32_t)q) + (uint32_t)e;
           const bool ok = j < send;
-          const uint32_t col = ok ? (uint32_t)s_idx[j] : 0u;
-          const uint32_t v = ld16(xrs, ((uint32_t)n16 * (uint32_t)a.K + col) * 2u);
-          hv[e] = ok ? v : 0u;
+          const uint32_t col = (uint32_t)s_idx[min(j, jmax)];
+          const uint32_t off = ((uint32_t)n16 * (uint32_t)a.K + col) * 2u;
+          xopre[e] = ld32(xrs, ok ? (off & ~3u) : kOob);
+          xhalf |= ((off >> 1) & 1u) << e;
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xopre[i] = hv[2 * i] | (hv[2 * i + 1] << 16);
       }
       // outlier activations of the first 32 columns of the run: X[m][lo + c]
       // (XT: read from the slice's rows in LDS when the slice is entered)
@@ -1275,17 +1283,16 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         const int4 l0 = *reinterpret_cast<const int4*>(list + 8 * q);
         const int4 l1 = *reinterpret_cast<const int4*>(list + 8 * q + 4);
         const int cl[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        uint32_t hv[8];
+        xhalf = 0u;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {   // every lane loads (a valid column when idle)
+        for (int e = 0; e < 8; ++e) {   // an idle position reads at kOob, which gives 0
           const bool ok = 8 * q + e < nin && cl[e] >= 0;
           const uint32_t col =
               (uint32_t)(lo + __builtin_amdgcn_ubfe(ok ? cl[e] : 0, 0, QG == 4 ? 9 : 8));
-          const uint32_t v = ld16(xrs, ((uint32_t)n16 * (uint32_t)a.K + col) * 2u);
-          hv[e] = ok ? v : 0u;
+          const uint32_t off = ((uint32_t)n16 * (uint32_t)a.K + col) * 2u;
+          xopre[e] = ld32(xrs, ok ? (off & ~3u) : kOob);
+          xhalf |= ((off >> 1) & 1u) << e;
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xopre[i] = hv[2 * i] | (hv[2 * i + 1] << 16);
       }
     }
   };
@@ -1321,16 +1328,14 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         const int4 l0 = *reinterpret_cast<const int4*>(list + 8 * q);
         const int4 l1 = *reinterpret_cast<const int4*>(list + 8 * q + 4);
         const int cl[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        uint32_t hv[8];
+        xhalf = 0u;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const bool ok = 8 * q + e < nin && cl[e] >= 0 && cl[e] < kSliceChB && (uint32_t)n16 < mpx;
-          hv[e] = ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(
-                           smem + xbase + (uint32_t)n16 * mmb_xt_stride(QG) + (uint32_t)cl[e] * 2u)
-                     : 0u;
+          xopre[e] = ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(
+                              smem + xbase + (uint32_t)n16 * mmb_xt_stride(QG) + (uint32_t)cl[e] * 2u)
+                        : 0u;
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xopre[i] = hv[2 * i] | (hv[2 * i + 1] << 16);
       }
       if constexpr (FMT == 2 && OUT) {
         // W2 outlier columns of the slice: zero in every staged row (after the
@@ -1424,7 +1429,16 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     for (int f = 0; f < XS; ++f)
       afr[f] = __builtin_bit_cast(h8, (u4v){fr[f][0], fr[f][1], fr[f][2], fr[f][3]});
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xo[i] = xopre[i];
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (xhalf >> (2 * i)) & 1u ? xopre[2 * i] >> 16 : xopre[2 * i] & 0xFFFFu;
+      const uint32_t hi =
+          (xhalf >> (2 * i + 1)) & 1u ? xopre[2 * i + 1] >> 16 : xopre[2 * i + 1] & 0xFFFFu;
+      xo[i] = lo | (hi << 16);
+    }
+    // the words are consumed here, before the next slice's gather reuses
+    // their registers (without this point the combine sinks below the new
+    // loads, the old and new words overlap, and the loaded values are copied)
+    asm volatile("" : "+v"(xo[0]), "+v"(xo[1]), "+v"(xo[2]), "+v"(xo[3])::"memory");
     jrange(ks, cur_jlo, cur_nin);
     // the next rows into the buffer just read (X2: two slices ahead, the
     // buffers alternate; else the next slice) and the next slice's outlier
