@@ -829,6 +829,34 @@ def test_special_values_and_boundary_outliers(fmt, N, K):
 
 
 @pytest.mark.parametrize("fmt", [4, 2, 5])
+@pytest.mark.parametrize("N,K", [(48, 1024), (160, 4096), (37, 14336)])
+@pytest.mark.parametrize("M", [5, 8, 16])
+def test_batched_boundary_outliers(fmt, N, K, M):
+    """The batched kernels (both layouts, rows staged or not) on the special
+    layer: outlier columns at 0 and K - 1, odd and even, on both sides of the
+    32-, 256- and 512-channel boundaries, so each gathered activation comes
+    from either half of its aligned 4-byte word."""
+    say(f"batched boundary outliers fmt={fmt} N={N} K={K} M={M}")
+    W, x, profile, ratio, cols = _special_layer(fmt, N, K, seed=N + K + M)
+    ref = O.quantize_layer(fmt, W, profile, ratio)
+    dl = DeviceLayer(pack_host(fmt, W, profile, ratio), tiled=True)
+    rng = np.random.default_rng(M)
+    X = np.stack([x] + [(x * np.float16(rng.uniform(-2, 2))).astype(np.float16)
+                        for _ in range(M - 1)])
+    Xd = dev_fp16(X)
+    for layout in ("tiled", "rowmajor"):
+        for xt in (0, 1):
+            var = B.variant(gemm_rows=0, batch_row_transpose=xt)
+            Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
+            if layout == "tiled":
+                dl.gemm_tiled(Xd, Y, variant=var)
+            else:
+                dl.gemm(Xd, Y, variant=var)
+            torch.cuda.synchronize()
+            check_product(ref, Y, X, f"boundary w{fmt} M={M} {layout} xt={xt}")
+
+
+@pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("lds_path", ["0", "1"])
 @pytest.mark.parametrize("rpw", ["1", "2", "4"])
 @pytest.mark.parametrize("N,K,outl", [(129, 4096, True), (37, 14336, False), (300, 2080, True)])
