@@ -966,8 +966,8 @@ __device__ __forceinline__ uint32_t splat_hi(uint32_t v) { return __builtin_amdg
 // PREG: each wave's partial tiles in registers (at most kPregMax row blocks
 // per workgroup), added in the same order as the LDS tiles would be, so the
 // results are the same bits; they reach LDS once, at the end.
-// R8 (with XT): at most 8 activation rows, so the loads of staged rows 8..15
-// are not issued (they would read zeros).
+// R8 (with XT): at most 8 activation rows, so staged rows 8..15 are neither
+// loaded nor held in registers (they would be zeros).
 constexpr int kPregMax = 8;
 template <int FMT, int IV, int DEPTH, int QG, bool XT, bool TILED = false, bool PREG = false,
           bool R8 = false>
@@ -1039,16 +1039,15 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   // the slice is entered.
   constexpr int kXLanesPerRow = 16 * QG;
   constexpr int kXRowsPerLoad = kWave / kXLanesPerRow;
-  auto x_load = [&](int ks, u4v (&xv)[XS]) {
+  // loads (and registers) of a slice's activation rows: R8 stages rows 0..7
+  constexpr int XL = (XT && R8) ? 8 / kXRowsPerLoad : XS;
+  auto x_load = [&](int ks, u4v (&xv)[XL]) {
     if constexpr (XT) {
       const uint32_t c = (uint32_t)(ks * kSliceChB + 8 * (lane % kXLanesPerRow));
 #pragma unroll
-      for (int t = 0; t < XS; ++t) {
+      for (int t = 0; t < XL; ++t) {
         const uint32_t row = (uint32_t)(t * kXRowsPerLoad + lane / kXLanesPerRow);
-        if (R8 && t * kXRowsPerLoad >= 8)   // a constant once unrolled: not issued
-          xv[t] = (u4v){0u, 0u, 0u, 0u};
-        else
-          xv[t] = ld128(xrs, (row * (uint32_t)a.K + c) * 2u);
+        xv[t] = ld128(xrs, (row * (uint32_t)a.K + c) * 2u);
       }
     } else {
       const uint32_t rowoff = (uint32_t)n16 * (uint32_t)a.K;
@@ -1062,10 +1061,11 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   // XT with outliers: two slices of rows in flight (even slices in xpre, odd
   // ones in xpre2), as the weights are two items ahead (measured: the W2
   // 8192 x 28672 layer at M = 8 gains 8%; without outliers the registers cost
-  // more than the earlier loads gain)
+  // more than the earlier loads gain, and on the tiled layout, even with R8's
+  // eight rows, that layer at M = 8 goes from 33.3 to 36.7 us)
   constexpr bool X2 = XT && OUT && !TILED;
-  u4v xpre[XS];
-  u4v xpre2[X2 ? XS : 1];
+  u4v xpre[XL];
+  u4v xpre2[X2 ? XL : 1];
   x_load(w, xpre);
   if constexpr (X2)
     if (1 < ns_w) x_load(w + a.nw, xpre2);
@@ -1304,6 +1304,15 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   auto enter_slice_rows = [&](int s, auto& xbuf) {
     const int ks = w + a.nw * s;
     const int p = s & 1;
+    // the slice's activations in the lane layout of the fragments: read back
+    // from LDS when the rows were loaded whole, else the loaded registers
+    u4v fv[XT ? XS : 1];
+    auto xf = [&](int t) -> u4v {
+      if constexpr (XT)
+        return fv[t];
+      else
+        return xbuf[t];
+    };
     if constexpr (XT) {
       // the slice's rows, loaded whole, into this wave's LDS area and back in
       // the lane layout of the fragments (lane (m, q): channels 32 QG q + 8 t
@@ -1311,7 +1320,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
       const uint32_t mpx = (uint32_t)((a.M + 3) & ~3);
       const uint32_t xbase = L.xt + (uint32_t)w * mpx * mmb_xt_stride(QG);
 #pragma unroll
-      for (int t = 0; t < XS; ++t) {
+      for (int t = 0; t < XL; ++t) {
         const uint32_t row = (uint32_t)(t * kXRowsPerLoad + lane / kXLanesPerRow);
         if (row < mpx)
           *reinterpret_cast<u4v*>(smem + xbase + row * mmb_xt_stride(QG) +
@@ -1354,10 +1363,10 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
       }
 #pragma unroll
       for (int t = 0; t < XS; ++t)
-        xbuf[t] = (uint32_t)n16 < mpx
-                      ? *reinterpret_cast<const u4v*>(smem + xbase + (uint32_t)n16 * mmb_xt_stride(QG) +
-                                                       (uint32_t)(32 * QG * q + 8 * t) * 2u)
-                      : (u4v){0u, 0u, 0u, 0u};
+        fv[t] = (uint32_t)n16 < mpx
+                    ? *reinterpret_cast<const u4v*>(smem + xbase + (uint32_t)n16 * mmb_xt_stride(QG) +
+                                                     (uint32_t)(32 * QG * q + 8 * t) * 2u)
+                    : (u4v){0u, 0u, 0u, 0u};
     }
     // fragments of this slice from the prefetched rows (channels past K: 0)
     uint32_t fr[XS][4];
@@ -1368,19 +1377,19 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
       if (inside) {
 #pragma unroll
         for (int t = 0; t < XS; ++t) {
-          fr[t][0] = xbuf[t].x;
-          fr[t][1] = xbuf[t].y;
-          fr[t][2] = xbuf[t].z;
-          fr[t][3] = xbuf[t].w;
+          fr[t][0] = xf(t).x;
+          fr[t][1] = xf(t).y;
+          fr[t][2] = xf(t).z;
+          fr[t][3] = xf(t).w;
         }
       } else {
 #pragma unroll
         for (int t = 0; t < XS; ++t) {
           const bool ok = ks * kSliceChB + 32 * QG * q + 8 * t < a.K;
-          fr[t][0] = ok ? xbuf[t].x : 0u;
-          fr[t][1] = ok ? xbuf[t].y : 0u;
-          fr[t][2] = ok ? xbuf[t].z : 0u;
-          fr[t][3] = ok ? xbuf[t].w : 0u;
+          fr[t][0] = ok ? xf(t).x : 0u;
+          fr[t][1] = ok ? xf(t).y : 0u;
+          fr[t][2] = ok ? xf(t).z : 0u;
+          fr[t][3] = ok ? xf(t).w : 0u;
         }
       }
       if constexpr (OUT && !XT) {
@@ -1408,7 +1417,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         uint32_t gv[16];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const u4v t = xbuf[4 * u + v];
+          const u4v t = xf(4 * u + v);
           gv[4 * v + 0] = ok ? t.x : 0u;
           gv[4 * v + 1] = ok ? t.y : 0u;
           gv[4 * v + 2] = ok ? t.z : 0u;
@@ -2033,9 +2042,8 @@ int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
   a.nrb = p.nrb;
   a.rbl = p.rbl;
   const dim3 grid(p.grid), block(p.nw * kWave);
-  // staged rows: at most 8 for M <= 8 (W4 / W4P; measured on MI355X: the W2
-  // kernels on the row-major arrays are no faster with it)
-  const bool r8 = p.xt && M <= 8 && fmt != 2;
+  // staged rows: at most 8 for M <= 8
+  const bool r8 = p.xt && M <= 8;
 #define WQ_MMB_LAUNCH_XPR(F_, IV_, Q_, X_, P_, R_)                                               \
   if (fmt == F_ && p.iv == IV_ && p.qg == Q_ && p.xt == X_ && p.preg == P_ && r8 == R_) {     \
     if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, Q_, X_, false, P_, R_>), \
@@ -2047,7 +2055,7 @@ int wqd_gemm_mma(int fmt, const uint8_t* codes, const uint16_t* scales, const ui
     return check_launch(who);                                                                   \
   }
 #define WQ_MMB_LAUNCH_XP(F_, IV_, Q_, X_, P_) \
-  WQ_MMB_LAUNCH_XPR(F_, IV_, Q_, X_, P_, false) WQ_MMB_LAUNCH_XPR(F_, IV_, Q_, X_, P_, (X_ && F_ != 2))
+  WQ_MMB_LAUNCH_XPR(F_, IV_, Q_, X_, P_, false) WQ_MMB_LAUNCH_XPR(F_, IV_, Q_, X_, P_, X_)
 #define WQ_MMB_LAUNCH_X(F_, IV_, Q_, X_) WQ_MMB_LAUNCH_XP(F_, IV_, Q_, X_, false) WQ_MMB_LAUNCH_XP(F_, IV_, Q_, X_, X_)
 #define WQ_MMB_LAUNCH(F_, IV_) WQ_MMB_LAUNCH_X(F_, IV_, 2, false) WQ_MMB_LAUNCH_X(F_, IV_, 2, true)
   WQ_MMB_LAUNCH_X(4, 0, 4, false) WQ_MMB_LAUNCH_X(2, 0, 4, false) WQ_MMB_LAUNCH_X(5, 0, 4, false)
@@ -2090,8 +2098,9 @@ int wqd_gemm_mma_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
   const dim3 grid(p.grid), block(p.nw * kWave);
   // staged rows: at most 8 for M <= 8 (measured on MI355X: W2 8192 x 28672 +
   // 1003 outliers at M = 8 38.0 -> 36.1 us, W4 14336 x 4096 11.86 -> 11.46 us;
-  // not with the W2 register partials, whose registers would spill)
-  const bool r8 = p.xt && M <= 8 && (fmt != 2 || !p.preg);
+  // with only those rows' registers held, 35.2 -> 33.3 us and W4 4096 x 14336
+  // 15.2 -> 14.45 us)
+  const bool r8 = p.xt && M <= 8;
 #define WQ_MMT_LAUNCH_XPR(F_, IV_, X_, P_, R_)                                                    \
   if (fmt == F_ && p.iv == IV_ && p.xt == X_ && p.preg == P_ && r8 == R_) {                      \
     if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, 4, X_, true, P_, R_>),  \
@@ -2103,7 +2112,7 @@ int wqd_gemm_mma_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
     return check_launch(who);                                                                   \
   }
 #define WQ_MMT_LAUNCH_XP(F_, IV_, X_, P_) \
-  WQ_MMT_LAUNCH_XPR(F_, IV_, X_, P_, false) WQ_MMT_LAUNCH_XPR(F_, IV_, X_, P_, (X_ && (F_ != 2 || !P_)))
+  WQ_MMT_LAUNCH_XPR(F_, IV_, X_, P_, false) WQ_MMT_LAUNCH_XPR(F_, IV_, X_, P_, X_)
 #define WQ_MMT_LAUNCH_X(F_, IV_, X_) WQ_MMT_LAUNCH_XP(F_, IV_, X_, false) WQ_MMT_LAUNCH_XP(F_, IV_, X_, X_)
 #define WQ_MMT_LAUNCH(F_, IV_) WQ_MMT_LAUNCH_X(F_, IV_, false) WQ_MMT_LAUNCH_X(F_, IV_, true)
   WQ_MMT_LAUNCH(4, 0) WQ_MMT_LAUNCH(4, 1) WQ_MMT_LAUNCH(4, 2) WQ_MMT_LAUNCH(4, 4)
