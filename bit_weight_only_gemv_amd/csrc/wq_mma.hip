@@ -916,8 +916,14 @@ struct MmbLds {
   uint32_t lut, wave, runs, idx, part, xt, total;
 };
 // Transpose area of the activation rows (XT kernels): per wave Mp rows of one
-// slice, each padded by 16 bytes against bank conflicts.
+// slice, each padded by 16 bytes against bank conflicts.  W2 on the tiled
+// layout at M > 8 passes its rows through an area of 8 rows, in two rounds:
+// beside the 64 KB centroid table 8 waves x 16 rows x 1 KB would not fit.
 __host__ __device__ constexpr uint32_t mmb_xt_stride(int qg) { return 256u * qg + 16u; }
+__host__ __device__ constexpr bool mmb_xt_halves(int fmt, bool tiled) { return fmt == 2 && tiled; }
+__host__ __device__ constexpr uint32_t mmb_xt_rows(int fmt, int M, bool tiled) {
+  return mmb_xt_halves(fmt, tiled) && M > 8 ? 8u : (uint32_t)((M + 3) & ~3);
+}
 // With outliers also: the run table (slice ks's run of the sorted indices
 // starts at runs[ks], nks + 1 words) and a copy of the indices (256 iv words).
 // preg: the partial tiles are kept in registers while the weights stream and
@@ -939,7 +945,14 @@ __host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl
   L.part = off;
   if (!preg) off += (uint32_t)rbl * (uint32_t)nw * (uint32_t)((M + 3) & ~3) * 64u;
   L.xt = off;
-  if (xt) off += (uint32_t)nw * (uint32_t)((M + 3) & ~3) * mmb_xt_stride(qg);
+  if (xt) {
+    uint32_t area = (uint32_t)nw * mmb_xt_rows(fmt, M, tiled) * mmb_xt_stride(qg);
+    if (preg) {   // the partial tiles land here at the end
+      const uint32_t tiles = (uint32_t)rbl * (uint32_t)nw * (uint32_t)((M + 3) & ~3) * 64u;
+      area = area > tiles ? area : tiles;
+    }
+    off += area;
+  }
   if (preg) L.part = L.xt;
   L.total = off;
   return L;
@@ -1041,6 +1054,10 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   constexpr int kXRowsPerLoad = kWave / kXLanesPerRow;
   // loads (and registers) of a slice's activation rows: R8 stages rows 0..7
   constexpr int XL = (XT && R8) ? 8 / kXRowsPerLoad : XS;
+  // more than 8 rows through the 8-row area, rows 0..7 and then 8..15 (one
+  // row per load at 512-channel slices)
+  constexpr bool XH = XT && !R8 && mmb_xt_halves(FMT, TILED);
+  static_assert(!XH || kXRowsPerLoad == 1, "two rounds of whole rows");
   auto x_load = [&](int ks, u4v (&xv)[XL]) {
     if constexpr (XT) {
       const uint32_t c = (uint32_t)(ks * kSliceChB + 8 * (lane % kXLanesPerRow));
@@ -1318,12 +1335,18 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
       // the lane layout of the fragments (lane (m, q): channels 32 QG q + 8 t
       // of row m); rows past M are zero
       const uint32_t mpx = (uint32_t)((a.M + 3) & ~3);
-      const uint32_t xbase = L.xt + (uint32_t)w * mpx * mmb_xt_stride(QG);
+      const uint32_t arows = XH ? 8u : mpx;
+      const uint32_t xbase = L.xt + (uint32_t)w * arows * mmb_xt_stride(QG);
+#pragma unroll
+      for (int r = 0; r < (XH ? 2 : 1); ++r) {
+      const uint32_t r0 = 8u * (uint32_t)r;   // the round's first row
+      if (r > 0) wave_lds_sync();             // after the first round's reads
 #pragma unroll
       for (int t = 0; t < XL; ++t) {
+        if (XH && t / 8 != r) continue;       // a constant once unrolled
         const uint32_t row = (uint32_t)(t * kXRowsPerLoad + lane / kXLanesPerRow);
         if (row < mpx)
-          *reinterpret_cast<u4v*>(smem + xbase + row * mmb_xt_stride(QG) +
+          *reinterpret_cast<u4v*>(smem + xbase + (row - r0) * mmb_xt_stride(QG) +
                                   16u * (uint32_t)(lane % kXLanesPerRow)) = xbuf[t];
       }
       wave_lds_sync();
@@ -1353,20 +1376,24 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         jrange(ks, j_lo, nin);
         const int lo = ks * kSliceChB;
         wave_lds_sync();
+        const uint32_t mr = mpx - r0 < arows ? mpx - r0 : arows;
         for (int j = lane; j < nin; j += kWave) {
           const int c = s_idx[j_lo + j] - lo;
           if ((unsigned)c < (unsigned)kSliceChB)
-            for (uint32_t m = 0; m < mpx; ++m)
+            for (uint32_t m = 0; m < mr; ++m)
               *reinterpret_cast<uint16_t*>(smem + xbase + m * mmb_xt_stride(QG) + (uint32_t)c * 2u) = 0;
         }
         wave_lds_sync();
       }
+      if (!XH || (uint32_t)n16 / 8u == (uint32_t)r) {
 #pragma unroll
-      for (int t = 0; t < XS; ++t)
-        fv[t] = (uint32_t)n16 < mpx
-                    ? *reinterpret_cast<const u4v*>(smem + xbase + (uint32_t)n16 * mmb_xt_stride(QG) +
-                                                     (uint32_t)(32 * QG * q + 8 * t) * 2u)
-                    : (u4v){0u, 0u, 0u, 0u};
+        for (int t = 0; t < XS; ++t)
+          fv[t] = (uint32_t)n16 < mpx
+                      ? *reinterpret_cast<const u4v*>(smem + xbase + ((uint32_t)n16 - r0) * mmb_xt_stride(QG) +
+                                                       (uint32_t)(32 * QG * q + 8 * t) * 2u)
+                      : (u4v){0u, 0u, 0u, 0u};
+      }
+      }
     }
     // fragments of this slice from the prefetched rows (channels past K: 0)
     uint32_t fr[XS][4];

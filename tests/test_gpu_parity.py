@@ -830,7 +830,7 @@ def test_special_values_and_boundary_outliers(fmt, N, K):
 
 @pytest.mark.parametrize("fmt", [4, 2, 5])
 @pytest.mark.parametrize("N,K", [(48, 1024), (160, 4096), (37, 14336)])
-@pytest.mark.parametrize("M", [5, 8, 16])
+@pytest.mark.parametrize("M", [5, 8, 10, 16])
 def test_batched_boundary_outliers(fmt, N, K, M):
     """The batched kernels (both layouts, rows staged or not) on the special
     layer: outlier columns at 0 and K - 1, odd and even, on both sides of the
