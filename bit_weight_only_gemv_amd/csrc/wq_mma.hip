@@ -916,13 +916,13 @@ struct MmbLds {
   uint32_t lut, wave, runs, idx, part, xt, total;
 };
 // Transpose area of the activation rows (XT kernels): per wave Mp rows of one
-// slice, each padded by 16 bytes against bank conflicts.  W2 on the tiled
-// layout at M > 8 passes its rows through an area of 8 rows, in two rounds:
-// beside the 64 KB centroid table 8 waves x 16 rows x 1 KB would not fit.
+// slice, each padded by 16 bytes against bank conflicts.  xh (the tiled layout
+// at M > 8): an area of 8 rows that the rows pass through in two rounds, where
+// 16 rows would not fit (beside the W2 centroid table, or the LDS partial
+// tiles of several row blocks).
 __host__ __device__ constexpr uint32_t mmb_xt_stride(int qg) { return 256u * qg + 16u; }
-__host__ __device__ constexpr bool mmb_xt_halves(int fmt, bool tiled) { return fmt == 2 && tiled; }
-__host__ __device__ constexpr uint32_t mmb_xt_rows(int fmt, int M, bool tiled) {
-  return mmb_xt_halves(fmt, tiled) && M > 8 ? 8u : (uint32_t)((M + 3) & ~3);
+__host__ __device__ constexpr uint32_t mmb_xt_rows(int M, bool xh) {
+  return xh ? 8u : (uint32_t)((M + 3) & ~3);
 }
 // With outliers also: the run table (slice ks's run of the sorted indices
 // starts at runs[ks], nks + 1 words) and a copy of the indices (256 iv words).
@@ -931,7 +931,7 @@ __host__ __device__ constexpr uint32_t mmb_xt_rows(int fmt, int M, bool tiled) {
 // has no separate region for them.
 __host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl, int qg, int nks,
                                                  int iv, bool xt = false, bool tiled = false,
-                                                 bool preg = false) {
+                                                 bool preg = false, bool xh = false) {
   MmbLds L{};
   uint32_t off = 0;
   L.lut = off;
@@ -946,7 +946,7 @@ __host__ __device__ inline MmbLds mmb_lds_layout(int fmt, int M, int nw, int rbl
   if (!preg) off += (uint32_t)rbl * (uint32_t)nw * (uint32_t)((M + 3) & ~3) * 64u;
   L.xt = off;
   if (xt) {
-    uint32_t area = (uint32_t)nw * mmb_xt_rows(fmt, M, tiled) * mmb_xt_stride(qg);
+    uint32_t area = (uint32_t)nw * mmb_xt_rows(M, xh) * mmb_xt_stride(qg);
     if (preg) {   // the partial tiles land here at the end
       const uint32_t tiles = (uint32_t)rbl * (uint32_t)nw * (uint32_t)((M + 3) & ~3) * 64u;
       area = area > tiles ? area : tiles;
@@ -981,9 +981,11 @@ __device__ __forceinline__ uint32_t splat_hi(uint32_t v) { return __builtin_amdg
 // results are the same bits; they reach LDS once, at the end.
 // R8 (with XT): at most 8 activation rows, so staged rows 8..15 are neither
 // loaded nor held in registers (they would be zeros).
+// XH (tiled, with XT, M > 8): the rows pass through an 8-row LDS area in two
+// rounds, rows 0..7 and then 8..15, where 16 rows would not fit.
 constexpr int kPregMax = 8;
 template <int FMT, int IV, int DEPTH, int QG, bool XT, bool TILED = false, bool PREG = false,
-          bool R8 = false>
+          bool R8 = false, bool XH = false>
 __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   typedef MmbFmt<FMT, QG> F;
   static_assert(!TILED || QG == 4, "the tiled layout has 512-channel slices");
@@ -996,7 +998,8 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   constexpr bool OUT = IV > 0;
   extern __shared__ __align__(16) unsigned char smem[];
   const int n_out = OUT ? a.n_out : 0;
-  const MmbLds L = mmb_lds_layout(FMT, a.M, a.nw, a.rbl, QG, a.nks, IV, XT, TILED, PREG);
+  static_assert(!XH || (XT && !R8 && TILED), "two rounds: whole rows of 512-channel slices, M > 8");
+  const MmbLds L = mmb_lds_layout(FMT, a.M, a.nw, a.rbl, QG, a.nks, IV, XT, TILED, PREG, XH);
   uint32_t* s_runs = reinterpret_cast<uint32_t*>(smem + L.runs);
   const int32_t* s_idx = reinterpret_cast<const int32_t*>(smem + L.idx);
   const int tid = threadIdx.x;
@@ -1054,9 +1057,6 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
   constexpr int kXRowsPerLoad = kWave / kXLanesPerRow;
   // loads (and registers) of a slice's activation rows: R8 stages rows 0..7
   constexpr int XL = (XT && R8) ? 8 / kXRowsPerLoad : XS;
-  // more than 8 rows through the 8-row area, rows 0..7 and then 8..15 (one
-  // row per load at 512-channel slices)
-  constexpr bool XH = XT && !R8 && mmb_xt_halves(FMT, TILED);
   static_assert(!XH || kXRowsPerLoad == 1, "two rounds of whole rows");
   auto x_load = [&](int ks, u4v (&xv)[XL]) {
     if constexpr (XT) {
@@ -1333,66 +1333,71 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     if constexpr (XT) {
       // the slice's rows, loaded whole, into this wave's LDS area and back in
       // the lane layout of the fragments (lane (m, q): channels 32 QG q + 8 t
-      // of row m); rows past M are zero
+      // of row m); rows past M are zero.  NR = 2 (XH): through the 8-row
+      // area, rows 0..7 and then 8..15
       const uint32_t mpx = (uint32_t)((a.M + 3) & ~3);
-      const uint32_t arows = XH ? 8u : mpx;
-      const uint32_t xbase = L.xt + (uint32_t)w * arows * mmb_xt_stride(QG);
+      {
+        constexpr int NR = XH ? 2 : 1;
+        const uint32_t arows = NR == 2 ? 8u : mpx;
+        const uint32_t xbase = L.xt + (uint32_t)w * arows * mmb_xt_stride(QG);
 #pragma unroll
-      for (int r = 0; r < (XH ? 2 : 1); ++r) {
-      const uint32_t r0 = 8u * (uint32_t)r;   // the round's first row
-      if (r > 0) wave_lds_sync();             // after the first round's reads
+        for (int r = 0; r < NR; ++r) {
+          const uint32_t r0 = 8u * (uint32_t)r;   // the round's first row
+          if (r > 0) wave_lds_sync();             // after the first round's reads
 #pragma unroll
-      for (int t = 0; t < XL; ++t) {
-        if (XH && t / 8 != r) continue;       // a constant once unrolled
-        const uint32_t row = (uint32_t)(t * kXRowsPerLoad + lane / kXLanesPerRow);
-        if (row < mpx)
-          *reinterpret_cast<u4v*>(smem + xbase + (row - r0) * mmb_xt_stride(QG) +
-                                  16u * (uint32_t)(lane % kXLanesPerRow)) = xbuf[t];
-      }
-      wave_lds_sync();
-      if constexpr (OUT && !TILED) {
-        // the run's first 32 outlier activations from the same rows (the
-        // slice's column list was written when the previous slice was entered)
-        const int32_t* list =
-            reinterpret_cast<const int32_t*>(smem + warea0 + (uint32_t)p * kMmbWaveArea + 16u * QG);
-        int j_lo, nin;
-        jrange(ks, j_lo, nin);
-        const int4 l0 = *reinterpret_cast<const int4*>(list + 8 * q);
-        const int4 l1 = *reinterpret_cast<const int4*>(list + 8 * q + 4);
-        const int cl[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        xhalf = 0u;
+          for (int t = 0; t < XL; ++t) {
+            if (NR == 2 && t / 8 != r) continue;   // a constant once unrolled
+            const uint32_t row = (uint32_t)(t * kXRowsPerLoad + lane / kXLanesPerRow);
+            if (row < mpx)
+              *reinterpret_cast<u4v*>(smem + xbase + (row - r0) * mmb_xt_stride(QG) +
+                                      16u * (uint32_t)(lane % kXLanesPerRow)) = xbuf[t];
+          }
+          wave_lds_sync();
+          if constexpr (OUT && !TILED) {
+            // the run's first 32 outlier activations from the same rows (the
+            // slice's column list was written when the previous slice was entered)
+            const int32_t* list = reinterpret_cast<const int32_t*>(
+                smem + warea0 + (uint32_t)p * kMmbWaveArea + 16u * QG);
+            int j_lo, nin;
+            jrange(ks, j_lo, nin);
+            const int4 l0 = *reinterpret_cast<const int4*>(list + 8 * q);
+            const int4 l1 = *reinterpret_cast<const int4*>(list + 8 * q + 4);
+            const int cl[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+            xhalf = 0u;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool ok = 8 * q + e < nin && cl[e] >= 0 && cl[e] < kSliceChB && (uint32_t)n16 < mpx;
-          xopre[e] = ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(
-                              smem + xbase + (uint32_t)n16 * mmb_xt_stride(QG) + (uint32_t)cl[e] * 2u)
-                        : 0u;
+            for (int e = 0; e < 8; ++e) {
+              const bool ok =
+                  8 * q + e < nin && cl[e] >= 0 && cl[e] < kSliceChB && (uint32_t)n16 < mpx;
+              xopre[e] = ok ? (uint32_t)*reinterpret_cast<const uint16_t*>(
+                                  smem + xbase + (uint32_t)n16 * mmb_xt_stride(QG) + (uint32_t)cl[e] * 2u)
+                            : 0u;
+            }
+          }
+          if constexpr (FMT == 2 && OUT) {
+            // W2 outlier columns of the slice: zero in every staged row (after
+            // the run's activations above were read from them)
+            int j_lo, nin;
+            jrange(ks, j_lo, nin);
+            const int lo = ks * kSliceChB;
+            wave_lds_sync();
+            const uint32_t mr = mpx - r0 < arows ? mpx - r0 : arows;
+            for (int j = lane; j < nin; j += kWave) {
+              const int c = s_idx[j_lo + j] - lo;
+              if ((unsigned)c < (unsigned)kSliceChB)
+                for (uint32_t m = 0; m < mr; ++m)
+                  *reinterpret_cast<uint16_t*>(smem + xbase + m * mmb_xt_stride(QG) + (uint32_t)c * 2u) = 0;
+            }
+            wave_lds_sync();
+          }
+          if (NR == 1 || (uint32_t)n16 / 8u == (uint32_t)r) {
+#pragma unroll
+            for (int t = 0; t < XS; ++t)
+              fv[t] = (uint32_t)n16 < mpx
+                          ? *reinterpret_cast<const u4v*>(smem + xbase + ((uint32_t)n16 - r0) * mmb_xt_stride(QG) +
+                                                           (uint32_t)(32 * QG * q + 8 * t) * 2u)
+                          : (u4v){0u, 0u, 0u, 0u};
+          }
         }
-      }
-      if constexpr (FMT == 2 && OUT) {
-        // W2 outlier columns of the slice: zero in every staged row (after the
-        // run's activations above were read from them)
-        int j_lo, nin;
-        jrange(ks, j_lo, nin);
-        const int lo = ks * kSliceChB;
-        wave_lds_sync();
-        const uint32_t mr = mpx - r0 < arows ? mpx - r0 : arows;
-        for (int j = lane; j < nin; j += kWave) {
-          const int c = s_idx[j_lo + j] - lo;
-          if ((unsigned)c < (unsigned)kSliceChB)
-            for (uint32_t m = 0; m < mr; ++m)
-              *reinterpret_cast<uint16_t*>(smem + xbase + m * mmb_xt_stride(QG) + (uint32_t)c * 2u) = 0;
-        }
-        wave_lds_sync();
-      }
-      if (!XH || (uint32_t)n16 / 8u == (uint32_t)r) {
-#pragma unroll
-        for (int t = 0; t < XS; ++t)
-          fv[t] = (uint32_t)n16 < mpx
-                      ? *reinterpret_cast<const u4v*>(smem + xbase + ((uint32_t)n16 - r0) * mmb_xt_stride(QG) +
-                                                       (uint32_t)(32 * QG * q + 8 * t) * 2u)
-                      : (u4v){0u, 0u, 0u, 0u};
-      }
       }
     }
     // fragments of this slice from the prefetched rows (channels past K: 0)
@@ -1779,7 +1784,7 @@ static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_ou
 
 
 struct MmbPlan {
-  bool ok, xt, preg;
+  bool ok, xt, preg, xh;
   int nw, nks, nrb, grid, rbl, iv, depth, qg;
   size_t lds;
 };
@@ -1844,6 +1849,21 @@ static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M,
       mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv, true, tiled).total;
   p.xt = lds_xt <= kMaxLdsBytes && want_xt;
   if (p.xt) p.lds = lds_xt;
+  // On the tiled layout at M > 8 the rows may pass through an 8-row area in
+  // two rounds where all of them do not fit.  Measured on MI355X: W2 8192 x
+  // 28672 + 1003 outliers at M = 16 70.4 -> 46.0 us (rows in the lane layout
+  // before), W4 14336 x 4096 at M = 16 14.1 -> 13.2 us (register partials
+  // before); where 16 rows fit, two rounds per slice are slower (W4 4096 x
+  // 14336 at M = 16 16.9 -> 17.7 us), so only then.
+  const bool can_xh = tiled && M > 8;
+  if (want_xt && !p.xt && can_xh) {
+    const size_t lds_xh =
+        mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv, true, tiled, false, true).total;
+    if (lds_xh <= kMaxLdsBytes) {
+      p.xt = p.xh = true;
+      p.lds = lds_xh;
+    }
+  }
   // Partial tiles in registers (a workgroup with at most kPregMax row blocks)
   // leave room for the staged rows where the LDS tiles would not.  Measured on
   // MI355X, the library takes them only then: W2 28672 x 8192 at M = 8 33.2 ->
@@ -1851,12 +1871,21 @@ static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M,
   // anyway the per-item register select is slower (W4 14336 x 4096 at M = 8,
   // 11.8 -> 12.7 us).  An explicit variant may ask for them wherever they fit.
   const int preg = variant_or(v, &wq_variant::batch_register_partials, -1);
-  const size_t lds_preg =
-      mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv, true, tiled, true).total;
-  if (want_xt && preg != 0 && (preg == 1 || !p.xt) && p.rbl <= kPregMax &&
-      lds_preg <= kMaxLdsBytes) {
-    p.xt = p.preg = true;
-    p.lds = lds_preg;
+  if (want_xt && preg != 0 && (preg == 1 || !p.xt) && p.rbl <= kPregMax) {
+    // the staging area chosen above, else 16 rows, else (tiled, M > 8) 8
+    bool xh = p.xt && p.xh;
+    size_t lds_preg =
+        mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv, true, tiled, true, xh).total;
+    if (lds_preg > kMaxLdsBytes && !xh && can_xh) {
+      xh = true;
+      lds_preg =
+          mmb_lds_layout(fmt, (int)M, p.nw, p.rbl, p.qg, p.nks, p.iv, true, tiled, true, true).total;
+    }
+    if (lds_preg <= kMaxLdsBytes) {
+      p.xt = p.preg = true;
+      p.xh = xh;
+      p.lds = lds_preg;
+    }
   }
   p.depth = 2;
   p.ok = true;
@@ -2128,16 +2157,18 @@ int wqd_gemm_mma_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
   // with only those rows' registers held, 35.2 -> 33.3 us and W4 4096 x 14336
   // 15.2 -> 14.45 us)
   const bool r8 = p.xt && M <= 8;
-#define WQ_MMT_LAUNCH_XPR(F_, IV_, X_, P_, R_)                                                    \
-  if (fmt == F_ && p.iv == IV_ && p.xt == X_ && p.preg == P_ && r8 == R_) {                      \
-    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, 4, X_, true, P_, R_>),  \
+#define WQ_MMT_LAUNCH_XPRH(F_, IV_, X_, P_, R_, H_)                                               \
+  if (fmt == F_ && p.iv == IV_ && p.xt == X_ && p.preg == P_ && r8 == R_ && p.xh == H_) {        \
+    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, 4, X_, true, P_, R_, H_>), \
                    p.lds))                                                                       \
       return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds);    \
-    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, 4, X_, true, P_, R_>), grid, block, p.lds, stream, \
-                       a);                                                                       \
+    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, 4, X_, true, P_, R_, H_>), grid, block, p.lds,     \
+                       stream, a);                                                               \
     *launched = true;                                                                           \
     return check_launch(who);                                                                   \
   }
+#define WQ_MMT_LAUNCH_XPR(F_, IV_, X_, P_, R_) \
+  WQ_MMT_LAUNCH_XPRH(F_, IV_, X_, P_, R_, false) WQ_MMT_LAUNCH_XPRH(F_, IV_, X_, P_, R_, (X_ && !R_))
 #define WQ_MMT_LAUNCH_XP(F_, IV_, X_, P_) \
   WQ_MMT_LAUNCH_XPR(F_, IV_, X_, P_, false) WQ_MMT_LAUNCH_XPR(F_, IV_, X_, P_, X_)
 #define WQ_MMT_LAUNCH_X(F_, IV_, X_) WQ_MMT_LAUNCH_XP(F_, IV_, X_, false) WQ_MMT_LAUNCH_XP(F_, IV_, X_, X_)
@@ -2148,6 +2179,7 @@ int wqd_gemm_mma_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
 #undef WQ_MMT_LAUNCH_X
 #undef WQ_MMT_LAUNCH_XP
 #undef WQ_MMT_LAUNCH_XPR
+#undef WQ_MMT_LAUNCH_XPRH
 #undef WQ_MMT_LAUNCH
   return WQ_OK;
 }
