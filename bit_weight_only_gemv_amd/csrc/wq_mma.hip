@@ -1174,11 +1174,13 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
     load_main(buf[d], d < T, w + a.nw * ls, blockIdx.x + lr * gridDim.x);
     advance(ls, lr);
     if (d == 0 && FMT == 2) {   // W2 centroid table (as in the M = 1 kernel)
-      u2* lut = reinterpret_cast<u2*>(smem + L.lut);
-      for (int sl = tid; sl < 256 * 32; sl += nthr) {
-        const uint32_t e = (uint32_t)sl >> 5;
-        lut[sl] = (u2){w2_centroid_pair((e & 3u) | (((e >> 2) & 3u) << 16)),
-                       w2_centroid_pair(((e >> 4) & 3u) | ((e >> 6) << 16))};
+      // 16-byte chunk ch: copies 2 (ch % 16) and 2 (ch % 16) + 1 of entry ch / 16
+      u4v* lut = reinterpret_cast<u4v*>(smem + L.lut);
+      for (int ch = tid; ch < 256 * 16; ch += nthr) {
+        const uint32_t e = (uint32_t)ch >> 4;
+        const uint32_t lo = w2_centroid_pair((e & 3u) | (((e >> 2) & 3u) << 16));
+        const uint32_t hi = w2_centroid_pair(((e >> 4) & 3u) | ((e >> 6) << 16));
+        lut[ch] = (u4v){lo, hi, lo, hi};
       }
       lds_barrier();
     }
