@@ -1182,7 +1182,9 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         const uint32_t hi = w2_centroid_pair(((e >> 4) & 3u) | ((e >> 6) << 16));
         lut[ch] = (u4v){lo, hi, lo, hi};
       }
-      lds_barrier();
+      // with outliers the run table's barrier below covers the table too
+      // (one wait for the slowest wave instead of two)
+      if constexpr (!OUT) lds_barrier();
     }
   }
   if constexpr (OUT) {
@@ -1228,7 +1230,7 @@ __global__ void __launch_bounds__(512) mmb_kernel(MmbArgs a) {
         if (t <= a.nks) s_runs[t] = before + v5[i];
       }
     }
-    lds_barrier();   // the run table and the index copy, visible to every wave
+    lds_barrier();   // the run table, the index copy and the W2 table, visible to every wave
   }
   {
     int s2 = 0, r2 = 0;
