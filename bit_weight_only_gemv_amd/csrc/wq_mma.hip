@@ -1734,6 +1734,18 @@ struct MmaPlan {
   size_t lds;
 };
 
+// Waves per workgroup for nks slices: one per slice up to 8, else 8 with the
+// leftover slices on waves 0, 1, ...  The first wave on each SIMD (waves 0..3)
+// gets its first data well before the second, so a split that gives the early
+// waves more slices evens out the finish.  Measured on MI355X (per-wave
+// timestamps): W4 4096 x 14336 (28 slices) at M = 8 on 7 waves of 4 slices,
+// waves 4..6 entered their first slice 1.8 us after waves 0..3 and finished
+// 2.5 us after them.  With 8 waves (4, 4, 4, 4, 3, 3, 3, 3): that layer at
+// M = 1 / 4 / 8 / 16 9.69 / 13.03 / 14.35 / 16.35 -> 9.45 / 12.39 / 13.65 /
+// 15.60 us; W4 4096 x 6144 (12 slices, 6 waves before) 6.60 / 9.31 ->
+// 6.13 / 8.35 us at M = 1 / 8; W2 4096 x 14336 + outliers 9.49 -> 8.69 us.
+static int mma_waves(int nks) { return nks <= kMaxWaves ? nks : kMaxWaves; }
+
 static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_out, int ms) {
   MmaPlan p{};
   // the row-major layout reads whole 128-channel quarters of a slice from
@@ -1755,18 +1767,7 @@ static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_ou
         N * n_out * 2 > kMaxArrayBytes)
       return p;
   }
-  if (p.nks <= kMaxWaves) {
-    p.nw = p.nks;
-  } else {
-    int best = -1;
-    for (int nw = kMaxWaves; nw >= 4; --nw) {
-      const int waste = ((p.nks + nw - 1) / nw) * nw - p.nks;
-      if (best < 0 || waste < best) {
-        best = waste;
-        p.nw = nw;
-      }
-    }
-  }
+  p.nw = mma_waves(p.nks);
   p.nsw = (p.nks + p.nw - 1) / p.nw;
   if (p.nsw > 8) return p;
   p.nswt = p.nsw <= 1 ? 1 : p.nsw <= 2 ? 2 : p.nsw <= 4 ? 4 : 8;
@@ -1824,18 +1825,7 @@ static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M,
   }
   const int slice_ch = 128 * p.qg;
   p.nks = (int)((K + slice_ch - 1) / slice_ch);
-  if (p.nks <= kMaxWaves) {
-    p.nw = p.nks;
-  } else {
-    int best = -1;
-    for (int nw = kMaxWaves; nw >= 4; --nw) {
-      const int waste = ((p.nks + nw - 1) / nw) * nw - p.nks;
-      if (best < 0 || waste < best) {
-        best = waste;
-        p.nw = nw;
-      }
-    }
-  }
+  p.nw = mma_waves(p.nks);
   p.nrb = (int)((N + 15) / 16);
   const int cus = device_cus();
   if (cus <= 0) return p;
