@@ -1745,8 +1745,24 @@ struct MmaPlan {
 // 15.60 us; W4 4096 x 6144 (12 slices, 6 waves before) 6.60 / 9.31 ->
 // 6.13 / 8.35 us at M = 1 / 8; W2 4096 x 14336 + outliers 9.49 -> 8.69 us.
 static int mma_waves(int nks) { return nks <= kMaxWaves ? nks : kMaxWaves; }
+// The fused refinement's streaming waves: the fewest wasted slices (28 slices:
+// 7 waves), which leaves one more wave for the helpers (W4 4096 x 14336: 9
+// helpers, 14.8 us; 8 streaming waves and 8 helpers, 15.1 us).
+static int mma_waves_even(int nks) {
+  if (nks <= kMaxWaves) return nks;
+  int best = -1, nw_best = kMaxWaves;
+  for (int nw = kMaxWaves; nw >= 4; --nw) {
+    const int waste = ((nks + nw - 1) / nw) * nw - nks;
+    if (best < 0 || waste < best) {
+      best = waste;
+      nw_best = nw;
+    }
+  }
+  return nw_best;
+}
 
-static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_out, int ms) {
+static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_out, int ms,
+                         bool refine = false) {
   MmaPlan p{};
   // the row-major layout reads whole 128-channel quarters of a slice from
   // each row; the tiled one is padded to whole slices
@@ -1767,7 +1783,7 @@ static MmaPlan plan_mma1(int fmt, bool tiled, int64_t N, int64_t K, int64_t n_ou
         N * n_out * 2 > kMaxArrayBytes)
       return p;
   }
-  p.nw = mma_waves(p.nks);
+  p.nw = refine ? mma_waves_even(p.nks) : mma_waves(p.nks);
   p.nsw = (p.nks + p.nw - 1) / p.nw;
   if (p.nsw > 8) return p;
   p.nswt = p.nsw <= 1 ? 1 : p.nsw <= 2 ? 2 : p.nsw <= 4 ? 4 : 8;
@@ -1983,7 +1999,7 @@ int wqd_gemv_refine_mma(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
                         int64_t chunk, int64_t k, int32_t* sel_out, const wq_variant* v,
                         hipStream_t stream, const char* who, bool* launched) {
   *launched = false;
-  MmaPlan p = plan_mma1(fmt, true, N, K, n_out, 1);
+  MmaPlan p = plan_mma1(fmt, true, N, K, n_out, 1, true);
   if (!p.ok || chunk < 1 || k < 1) return WQ_OK;
   const int rk = (int)std::min(k, chunk);
   const int rnch = (int)((K + chunk - 1) / chunk);
