@@ -435,6 +435,31 @@ def test_full_w4_batched(N, K, M):
         check_product(ref, y, L.x[m:m + 1], f"W4 {N}x{K} gemv row {m}")
 
 
+@pytest.mark.parametrize("fmt", [4, 5])
+@pytest.mark.parametrize("N", [12300, 16400])
+@pytest.mark.parametrize("M", [5, 8, 13])
+def test_batched_several_row_blocks(fmt, N, M):
+    """K = 4096 (8 slices on 8 waves) with 3 or 4 row blocks per workgroup
+    and a ragged last one: every row within the bound on both layouts, with
+    the rows staged in one round or in two (M = 13 on the tiled layout), and
+    with the partial tiles in LDS or in registers."""
+    K = 4096
+    say(f"batched several row blocks fmt={fmt} {N}x{K} M={M}")
+    L = synthetic.small_layer(fmt, N, K, M=M, with_outliers=False, seed=N % 97 + M)
+    ref, dl = build_tiled(fmt, L.W, L.profile, L.ratio)
+    X = dev_fp16(L.x)
+    for name, var in (("default", B.variant(gemm_rows=0)),
+                      ("register partials", B.variant(gemm_rows=0, batch_register_partials=1))):
+        for layout in ("tiled", "rowmajor"):
+            Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
+            if layout == "tiled":
+                dl.gemm_tiled(X, Y, variant=var)
+            else:
+                dl.gemm(X, Y, variant=var)
+            torch.cuda.synchronize()
+            check_product(ref, Y, L.x, f"row blocks w{fmt} {N}x{K} M={M} {layout} {name}")
+
+
 # ------------------------------------------------------ embedding row gather
 
 
