@@ -1897,7 +1897,13 @@ static MmbPlan plan_mmb(int fmt, int64_t N, int64_t K, int64_t n_out, int64_t M,
       p.lds = lds_preg;
     }
   }
-  p.depth = 2;
+  // Items in flight per wave: 2, or 1 on the tiled layout without outliers
+  // where a workgroup has one row block (every item then starts a new slice).
+  // Measured on MI355X (same bits): W4 4096 x 14336 at M = 5 / 8 / 16
+  // 13.24 / 13.59 / 15.55 -> 12.02 / 12.63 / 14.68 us; with 3 or more row
+  // blocks one item is slower (W4 14336 x 4096 at M = 8 11.1 -> 11.6 us, W2
+  // 28672 x 8192 + 286 24.1 -> 26.4 us), and so are 3 items everywhere.
+  p.depth = tiled && n_out == 0 && p.rbl == 1 ? 1 : 2;
   p.ok = true;
   return p;
 }
@@ -2167,16 +2173,19 @@ int wqd_gemm_mma_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
   // with only those rows' registers held, 35.2 -> 33.3 us and W4 4096 x 14336
   // 15.2 -> 14.45 us)
   const bool r8 = p.xt && M <= 8;
-#define WQ_MMT_LAUNCH_XPRH(F_, IV_, X_, P_, R_, H_)                                               \
-  if (fmt == F_ && p.iv == IV_ && p.xt == X_ && p.preg == P_ && r8 == R_ && p.xh == H_) {        \
-    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, 2, 4, X_, true, P_, R_, H_>), \
+#define WQ_MMT_LAUNCH_XPRHD(F_, IV_, X_, P_, R_, H_, D_)                                          \
+  if (fmt == F_ && p.iv == IV_ && p.xt == X_ && p.preg == P_ && r8 == R_ && p.xh == H_ &&        \
+      p.depth == D_) {                                                                           \
+    if (!allow_lds(reinterpret_cast<const void*>(&mmb_kernel<F_, IV_, D_, 4, X_, true, P_, R_, H_>), \
                    p.lds))                                                                       \
       return wq::fail(WQ_ERR_HIP, "%s: cannot raise the LDS limit to %zu bytes", who, p.lds);    \
-    hipLaunchKernelGGL((mmb_kernel<F_, IV_, 2, 4, X_, true, P_, R_, H_>), grid, block, p.lds,     \
+    hipLaunchKernelGGL((mmb_kernel<F_, IV_, D_, 4, X_, true, P_, R_, H_>), grid, block, p.lds,    \
                        stream, a);                                                               \
     *launched = true;                                                                           \
     return check_launch(who);                                                                   \
   }
+#define WQ_MMT_LAUNCH_XPRH(F_, IV_, X_, P_, R_, H_) \
+  WQ_MMT_LAUNCH_XPRHD(F_, IV_, X_, P_, R_, H_, 2) WQ_MMT_LAUNCH_XPRHD(F_, IV_, X_, P_, R_, H_, (IV_ == 0 ? 1 : 2))
 #define WQ_MMT_LAUNCH_XPR(F_, IV_, X_, P_, R_) \
   WQ_MMT_LAUNCH_XPRH(F_, IV_, X_, P_, R_, false) WQ_MMT_LAUNCH_XPRH(F_, IV_, X_, P_, R_, (X_ && !R_))
 #define WQ_MMT_LAUNCH_XP(F_, IV_, X_, P_) \
@@ -2190,6 +2199,7 @@ int wqd_gemm_mma_tiled(int fmt, const uint8_t* tiled, int64_t N, int64_t K,
 #undef WQ_MMT_LAUNCH_XP
 #undef WQ_MMT_LAUNCH_XPR
 #undef WQ_MMT_LAUNCH_XPRH
+#undef WQ_MMT_LAUNCH_XPRHD
 #undef WQ_MMT_LAUNCH
   return WQ_OK;
 }
